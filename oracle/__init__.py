@@ -1,0 +1,16 @@
+"""CPU reference decoder.  TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the bench's CPU-baseline leg may
+import this package.  It shares no code with the HIP library or its binding.
+
+Parity pins (all CPU tests): every function here is pinned by at least one
+closed form, invariant, special case or brute-force check; none is "parity
+unpinned".
+"""
+from .decoder import (f64, f16_round, rmsnorm, rope, rope_angles, silu, softmax,
+                      attend, greedy, top2_margin, Weights, OracleDecoder,
+                      prefill_matrix, greedy_decode)
+
+__all__ = ["f64", "f16_round", "rmsnorm", "rope", "rope_angles", "silu", "softmax",
+           "attend", "greedy", "top2_margin", "Weights", "OracleDecoder",
+           "prefill_matrix", "greedy_decode"]

@@ -1,0 +1,120 @@
+"""Seeded weight and prompt generators.
+
+Every matrix is drawn as float32 standard normals times 0.02 and rounded once
+to fp16 (round to nearest even); norm gains are 1.0.  Each tensor has its own
+generator, seeded with (seed, tensor index), so tensors can be drawn one at a
+time and a lane's tensors are row/column slices of the full model's.
+
+Canonical tensor order (also the order of the C ABI's host tensor list):
+  E [vocab, d]
+  per layer: g_attn [d], Wq [H*hd, d], Wk [H*hd, d], Wv [H*hd, d],
+             Wo [d, H*hd], g_ffn [d], Wg [F, d], Wu [F, d], Wd [d, F]
+  g_final [d], W_lm [lm_vocab, d]
+All matrices are stored [out, in], row-major.
+"""
+import numpy as np
+
+from .shapes import ModelShape, Workload, DENSE_2B
+
+LAYER_TENSORS = ("g_attn", "Wq", "Wk", "Wv", "Wo", "g_ffn", "Wg", "Wu", "Wd")
+N_TENSORS_PER_LAYER = len(LAYER_TENSORS)
+
+
+def tensor_names(shape: ModelShape):
+    names = ["E"]
+    for l in range(shape.n_layers):
+        names += [f"{t}.{l}" for t in LAYER_TENSORS]
+    names += ["g_final", "W_lm"]
+    return names
+
+
+def tensor_shapes(shape: ModelShape):
+    d, q, f = shape.d_model, shape.qkv_width, shape.d_ffn
+    per = {"g_attn": (d,), "Wq": (q, d), "Wk": (q, d), "Wv": (q, d), "Wo": (d, q),
+           "g_ffn": (d,), "Wg": (f, d), "Wu": (f, d), "Wd": (d, f)}
+    shapes = [(shape.vocab, d)]
+    for _ in range(shape.n_layers):
+        shapes += [per[t] for t in LAYER_TENSORS]
+    shapes += [(d,), (shape.lm_vocab, d)]
+    return shapes
+
+
+def _draw(shp, seed, index, scale=0.02):
+    rng = np.random.default_rng([seed, index])
+    a = rng.standard_normal(shp, dtype=np.float32)
+    a *= np.float32(scale)
+    return a.astype(np.float16)
+
+
+def make_weights(shape: ModelShape, seed: int = 0, gain_jitter: float = 0.0):
+    """List of fp16 arrays in canonical order.
+
+    gain_jitter > 0 draws every gain as 1 + N(0, gain_jitter) (rounded to
+    fp16) instead of 1.0, so that a consumer that ignores gains is caught.
+    """
+    out = []
+    for idx, (name, shp) in enumerate(zip(tensor_names(shape), tensor_shapes(shape))):
+        if name.startswith("g_"):
+            if gain_jitter > 0.0:
+                rng = np.random.default_rng([seed, idx, 7])
+                g = 1.0 + gain_jitter * rng.standard_normal(shp)
+                out.append(g.astype(np.float16))
+            else:
+                out.append(np.ones(shp, dtype=np.float16))
+        else:
+            out.append(_draw(shp, seed, idx))
+    return out
+
+
+def lane_slice_weights(lane_shape: ModelShape, full_shape: ModelShape = DENSE_2B, seed: int = 0):
+    """Lane 0's tensors: the first heads, FFN columns and LM rows of the full model.
+
+    Heads 0..n_heads-1 are Q/K/V rows [0, n_heads*hd) and Wo columns
+    [0, n_heads*hd); FFN columns [0, d_ffn) are rows of Wg/Wu and columns of
+    Wd; the LM head keeps rows [0, lm_vocab); the embedding is whole.
+    """
+    q, f = lane_shape.qkv_width, lane_shape.d_ffn
+    names = tensor_names(full_shape)
+    shapes = tensor_shapes(full_shape)
+    out = []
+    for idx, (name, shp) in enumerate(zip(names, shapes)):
+        base = name.split(".")[0]
+        if base.startswith("g_"):
+            out.append(np.ones(shp, dtype=np.float16))
+            continue
+        if base == "E":
+            out.append(_draw(shp, seed, idx))
+            continue
+        if base == "W_lm":
+            # only the first lm_vocab rows are needed; rows are drawn row-major so
+            # drawing the full table and slicing keeps the lane a true slice.
+            full = _draw(shp, seed, idx)
+            out.append(np.ascontiguousarray(full[:lane_shape.lm_vocab]))
+            del full
+            continue
+        full = _draw(shp, seed, idx)
+        if base in ("Wq", "Wk", "Wv"):
+            out.append(np.ascontiguousarray(full[:q]))
+        elif base == "Wo":
+            out.append(np.ascontiguousarray(full[:, :q]))
+        elif base in ("Wg", "Wu"):
+            out.append(np.ascontiguousarray(full[:f]))
+        elif base == "Wd":
+            out.append(np.ascontiguousarray(full[:, :f]))
+        else:
+            raise AssertionError(name)
+        del full
+    assert len(out) == len(names)
+    return out
+
+
+def make_prompt(vocab: int, n: int, batch: int = 1, seed: int = 1):
+    """Uniform random token ids, int32, shape [batch, n]."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, vocab, size=(batch, n)).astype(np.int32)
+
+
+def workload_weights(w: Workload):
+    if w.lane:
+        return lane_slice_weights(w.shape, DENSE_2B, seed=w.weight_seed)
+    return make_weights(w.shape, seed=w.weight_seed)
