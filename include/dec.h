@@ -1,0 +1,268 @@
+/*
+ * dec.h -- C ABI of libdecmono.so: batch-1 (and small-batch) greedy decode of
+ * a dense decoder-only transformer with fp16 weights on one AMD MI355X
+ * (gfx950).
+ *
+ * What the library computes.  At batch size 1 each generated token is a
+ * chain of matrix-vector products that reads every active weight once, so a
+ * decode step is bound by memory bandwidth, not arithmetic
+ * (hakusoku.com/story/7519, section GPU推論の速度制限要因：メモリ帯域幅).  The
+ * whole step -- matrix products, attention, normalisation and sampling -- runs
+ * as one resident GPU program with grid-wide phase barriers instead of one
+ * kernel launch per operation (same page, sections
+ * 標準推論スタックのボトルネックとKogの工夫 and
+ * Kog Inference Engineの特徴とイノベーション).  Weights and the KV cache are
+ * fp16 with no quantisation, pruning or cache compression (aether-echoes.com
+ * operator view, section どう出したか).  The per-layer math (pre-norm RMSNorm,
+ * rotary embedding on adjacent pairs, multi-head attention, SwiGLU MLP,
+ * untied LM head, greedy argmax with the lowest index winning ties) is fixed
+ * by the model description below.
+ *
+ * Conventions
+ *  - Every function returns a dec_status (0 = OK, negative = error) unless
+ *    stated; on error dec_last_error() describes it.
+ *  - Pointers named host_* or out_* and token/logit arrays are HOST memory.
+ *    The library never retains caller pointers past the call, except the
+ *    optional device arena and stream passed to dec_init.
+ *  - A handle is not thread-safe; distinct handles are independent.
+ *  - All calls that run GPU work are synchronous with respect to the handle's
+ *    stream unless stated (dec_step with out_tok == NULL is asynchronous).
+ */
+#ifndef DECMONO_DEC_H
+#define DECMONO_DEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DEC_ABI_VERSION 1
+
+typedef enum dec_status {
+  DEC_OK = 0,
+  DEC_ERR_INVALID_ARG = -1,   /* NULL handle/pointer, negative count, ...          */
+  DEC_ERR_BAD_DESC = -2,      /* model description violates the rules below         */
+  DEC_ERR_WEIGHTS = -3,       /* weight file or tensor list missing/short/mismatched */
+  DEC_ERR_NO_DEVICE = -4,     /* no usable gfx950 device                             */
+  DEC_ERR_OOM = -5,           /* device or pinned-host allocation failed / arena small */
+  DEC_ERR_CONTEXT_FULL = -6,  /* position would pass max_ctx                         */
+  DEC_ERR_STATE = -7,         /* call not valid in the handle's state                */
+  DEC_ERR_TOKEN_RANGE = -8,   /* token id outside [0, vocab)                         */
+  DEC_ERR_DEVICE = -9,        /* a HIP runtime call failed                           */
+  DEC_ERR_TIMEOUT = -10,      /* an in-kernel barrier wait passed the watchdog bound */
+  DEC_ERR_UNSUPPORTED = -11   /* valid request this build does not implement         */
+} dec_status;
+
+/*
+ * Model description.  Rules (DEC_ERR_BAD_DESC otherwise):
+ *   n_layers >= 1; d_model >= 8, a multiple of 8 and even;
+ *   n_kv_heads == n_heads >= 1 (multi-head attention);
+ *   head_dim in {8, 16, 32, 64, 128};
+ *   n_heads*head_dim may differ from d_model and must be a multiple of 8;
+ *   d_ffn >= 8, a multiple of 8;
+ *   1 <= lm_vocab <= vocab, lm_vocab even;
+ *   1 <= max_ctx <= 65536; batch == 1 (batch > 1: DEC_ERR_UNSUPPORTED in this
+ *   build); rms_eps > 0; rope_base > 1; flags == 0.
+ * Shapes of the weight tensors follow from it (see dec_weights_src).
+ */
+typedef struct dec_model_desc {
+  int32_t n_layers;
+  int32_t d_model;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t d_ffn;
+  int32_t vocab;      /* rows of the embedding table                  */
+  int32_t lm_vocab;   /* rows of the LM head (a vocabulary shard if < vocab) */
+  int32_t max_ctx;    /* KV-cache positions per sequence               */
+  int32_t batch;      /* sequences decoded together                    */
+  float rms_eps;
+  float rope_base;
+  uint32_t flags;     /* reserved, must be 0 */
+} dec_model_desc;
+
+/*
+ * Weight source: exactly one of `path` or `host_tensors` is non-NULL.
+ *
+ * host_tensors: n_tensors pointers to fp16 bit patterns (IEEE binary16,
+ * little-endian), matrices [out, in] row-major, in canonical order
+ *   E [vocab, d]
+ *   for each layer: g_attn [d], Wq [H*hd, d], Wk [H*hd, d], Wv [H*hd, d],
+ *                   Wo [d, H*hd], g_ffn [d], Wg [F, d], Wu [F, d], Wd [d, F]
+ *   g_final [d], W_lm [lm_vocab, d]
+ * so n_tensors == 1 + 9*n_layers + 2.  The caller owns the buffers; they are
+ * read during dec_init only.
+ *
+ * path: a DECW weight file (format below).  Its description must equal the
+ * one passed to dec_init in every shape field.
+ *
+ * DECW file, little-endian:
+ *   0   char[4]  "DECW"
+ *   4   uint32   version (1)
+ *   8   uint32   n_tensors
+ *   12  uint32   reserved (0)
+ *   16  int32[10] n_layers d_model n_heads n_kv_heads head_dim d_ffn vocab
+ *                lm_vocab max_ctx batch; float32 rms_eps, rope_base;
+ *                uint32 flags; 4 bytes padding   (56 bytes, ends at 72)
+ *   72  n_tensors entries of 40 bytes:
+ *         uint32 index (== position in the canonical order)
+ *         uint32 dtype (1 = fp16)
+ *         uint32 ndim (1 or 2), uint32 reserved
+ *         uint32 dim0, uint32 dim1 (dim1 = 1 when ndim == 1)
+ *         uint64 offset (from file start, multiple of 256)
+ *         uint64 nbytes (== 2*dim0*dim1)
+ *   payload: each tensor at its offset, row-major fp16.
+ */
+typedef struct dec_weights_src {
+  const char* path;
+  const uint16_t* const* host_tensors;
+  int32_t n_tensors;
+} dec_weights_src;
+
+/* debug_flags */
+#define DEC_DEBUG_MULTILAUNCH 0x1u  /* one kernel launch per phase instead of one
+                                       resident kernel with grid barriers (the
+                                       "one launch per op" stack, for comparison) */
+
+/*
+ * Init options (NULL = all defaults).
+ *   device:      HIP device ordinal.
+ *   stream:      hipStream_t to run on (e.g. torch.cuda.Stream().cuda_stream);
+ *                NULL: the library creates and owns a stream.  A caller stream
+ *                must outlive the handle.
+ *   arena, arena_bytes: optional caller-owned device memory that holds every
+ *                device buffer of the handle (weights, KV cache, activations,
+ *                barrier words); must be 256-byte aligned, at least
+ *                dec_arena_bytes() long and outlive the handle.  NULL: the
+ *                library allocates with hipMalloc.
+ *   debug_flags: DEC_DEBUG_*.
+ *   watchdog_us: bound on every in-kernel barrier wait; on expiry the kernel
+ *                exits and the call returns DEC_ERR_TIMEOUT.  0 = 2,000,000.
+ *   grid:        workgroups of the resident kernel; 0 = one per compute unit.
+ */
+typedef struct dec_init_opts {
+  int32_t device;
+  int32_t grid;
+  void* stream;
+  void* arena;
+  size_t arena_bytes;
+  uint32_t debug_flags;
+  int32_t watchdog_us;
+  int32_t reserved[6];
+} dec_init_opts;
+
+typedef struct dec_handle dec_handle;
+
+/* ABI version of the loaded library (DEC_ABI_VERSION it was built with). */
+int32_t dec_abi_version(void);
+
+/*
+ * Bytes of device memory a handle for `desc` needs (weights, KV cache,
+ * activations and control words), for a caller-provided arena.  Host only;
+ * needs no GPU.  grid = workgroups the kernel will use (0 = 256).
+ */
+int dec_arena_bytes(const dec_model_desc* desc, int32_t grid, size_t* out_bytes);
+
+/*
+ * Validate `desc` without touching any device.  DEC_OK or DEC_ERR_BAD_DESC /
+ * DEC_ERR_UNSUPPORTED with the reason in dec_last_error(NULL).
+ */
+int dec_check_desc(const dec_model_desc* desc);
+
+/*
+ * Read and validate the header and tensor table of a DECW file against the
+ * rules above (magic, version, count, dtypes, shapes, offsets, file size).
+ * Fills *out_desc from the header.  Host only.  DEC_ERR_WEIGHTS on any defect.
+ */
+int dec_weights_file_check(const char* path, dec_model_desc* out_desc);
+
+/*
+ * Create a handle: validate, read/pack the weights on the host, upload them,
+ * allocate the KV cache for batch x max_ctx positions and build the rotary
+ * table (cos/sin of p * rope_base^(-2i/head_dim), computed in double on the
+ * host, stored as fp32).  Position starts at 0.  On failure *out is NULL and
+ * dec_last_error(NULL) holds the reason.
+ */
+int dec_init(const dec_model_desc* desc, const dec_weights_src* weights,
+             const dec_init_opts* opts, dec_handle** out);
+
+/*
+ * Prefill: requires position 0 (fresh or after dec_reset), else
+ * DEC_ERR_STATE.  tokens: host int32 [batch * n] (sequence-major), 1 <= n <=
+ * max_ctx.  Runs positions 0..n-1 (keys/values of every position enter the
+ * cache) and returns the greedy next token of each sequence in out_tok
+ * [batch] (host, required) and, if out_logits != NULL, the last position's
+ * logits [batch * lm_vocab] (host, fp32).  Position becomes n.
+ */
+int dec_prefill(dec_handle* h, const int32_t* tokens, int32_t n,
+                int32_t* out_tok, float* out_logits);
+
+/*
+ * One decode step at the current position p.  Input token: force_tok[batch]
+ * (host) if non-NULL (teacher forcing), else the previous greedy output kept
+ * on the device.  Appends the keys/values of position p, advances to p+1 and
+ * produces the greedy token.  out_tok [batch] (host) and out_logits
+ * [batch * lm_vocab] (host) are optional; with both NULL the call only
+ * enqueues work on the stream and returns without waiting (use dec_sync).
+ * DEC_ERR_CONTEXT_FULL if p == max_ctx; DEC_ERR_STATE before any prefill.
+ */
+int dec_step(dec_handle* h, const int32_t* force_tok, int32_t* out_tok, float* out_logits);
+
+/*
+ * n_steps greedy steps inside one kernel launch, each step fed the previous
+ * step's token on the device.  Same result as n_steps dec_step calls with
+ * force_tok == NULL.  out_toks: host int32 [n_steps * batch] (step-major).
+ */
+int dec_generate(dec_handle* h, int32_t n_steps, int32_t* out_toks);
+
+/* Wait for all work enqueued on the handle's stream; reports deferred errors. */
+int dec_sync(dec_handle* h);
+
+/* Position -> 0.  The cache is logically empty (overwritten, not cleared). */
+int dec_reset(dec_handle* h);
+
+/* Current position (number of cached positions), or -1 for a NULL handle. */
+int32_t dec_position(const dec_handle* h);
+
+/*
+ * Copy cached keys and values of positions [0, n_pos) of one layer and one
+ * sequence to host memory as fp16 bits, each [n_heads, n_pos, head_dim].
+ * Either output may be NULL.  For tests and inspection; synchronous.
+ */
+int dec_read_kv(dec_handle* h, int32_t layer, int32_t seq, int32_t n_pos,
+                uint16_t* host_k, uint16_t* host_v);
+
+/* Release every resource of the handle (not a caller arena or stream). */
+void dec_free(dec_handle* h);
+
+/*
+ * Last error text of the handle, or of the calling thread's last failed
+ * handle-less call (dec_init, dec_check_desc, ...) when h == NULL.  Never NULL.
+ */
+const char* dec_last_error(const dec_handle* h);
+
+/*
+ * Host packer, exposed for inspection and tests (no GPU needed).
+ * dec_packed_bytes: size of the packed fp16 weight image for desc.
+ * dec_pack: write that image to host memory dst (dst_bytes >= the size) from
+ * the canonical tensor list (see dec_weights_src).  Layout of the image, in
+ * fp16 elements, each region 128-element aligned:
+ *   for each layer l:
+ *     Wqkv[l]  [3*H*hd, d]   rows: Wq rows, then Wk rows, then Wv rows
+ *     Wo[l]    [d, H*hd]
+ *     Wgu[l]   [2*F, d]      row 2f = Wg row f, row 2f+1 = Wu row f
+ *     Wd[l]    [d, F]
+ *   E        [vocab, d]
+ *   W_lm     [lm_vocab, d]
+ * Gains are not part of the image (they are uploaded as fp32).
+ */
+int dec_packed_bytes(const dec_model_desc* desc, size_t* out_bytes);
+int dec_pack(const dec_model_desc* desc, const uint16_t* const* host_tensors,
+             int32_t n_tensors, void* dst, size_t dst_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DECMONO_DEC_H */

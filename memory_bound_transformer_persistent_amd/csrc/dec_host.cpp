@@ -1,0 +1,741 @@
+// Host runtime behind include/dec.h: model-description checks, DECW weight
+// file ingest, the host packer, the device arena, and the launches of the
+// resident decode kernel (dec_kernels.hip).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/dec.h"
+#include "dec_internal.h"
+
+using namespace decmono;
+
+namespace {
+
+thread_local std::string g_err;   // last error of a handle-less call on this thread
+
+int fail(std::string* where, int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  (where ? *where : g_err) = buf;
+  return code;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t n, size_t a = kAlign) { return (n + a - 1) / a * a; }
+
+int n_tensors_for(const dec_model_desc& d) { return 1 + 9 * d.n_layers + 2; }
+
+int check_desc_impl(const dec_model_desc* d, std::string* err) {
+  if (!d) return fail(err, DEC_ERR_INVALID_ARG, "model description is NULL");
+  if (d->n_layers < 1) return fail(err, DEC_ERR_BAD_DESC, "n_layers must be >= 1 (got %d)", d->n_layers);
+  if (d->d_model < 8 || d->d_model % 8) return fail(err, DEC_ERR_BAD_DESC, "d_model must be a positive multiple of 8 (got %d)", d->d_model);
+  if (d->n_heads < 1) return fail(err, DEC_ERR_BAD_DESC, "n_heads must be >= 1 (got %d)", d->n_heads);
+  if (d->n_kv_heads != d->n_heads) return fail(err, DEC_ERR_BAD_DESC, "n_kv_heads must equal n_heads (multi-head attention)");
+  const int hd = d->head_dim;
+  if (hd != 8 && hd != 16 && hd != 32 && hd != 64 && hd != 128)
+    return fail(err, DEC_ERR_BAD_DESC, "head_dim must be one of 8,16,32,64,128 (got %d)", hd);
+  if (d->d_ffn < 8 || d->d_ffn % 8) return fail(err, DEC_ERR_BAD_DESC, "d_ffn must be a positive multiple of 8 (got %d)", d->d_ffn);
+  if (d->vocab < 1) return fail(err, DEC_ERR_BAD_DESC, "vocab must be >= 1");
+  if (d->lm_vocab < 2 || d->lm_vocab > d->vocab || d->lm_vocab % 2)
+    return fail(err, DEC_ERR_BAD_DESC, "lm_vocab must be even and in [2, vocab] (got %d)", d->lm_vocab);
+  if (d->max_ctx < 1 || d->max_ctx > 65536) return fail(err, DEC_ERR_BAD_DESC, "max_ctx must be in [1, 65536] (got %d)", d->max_ctx);
+  if (!(d->rms_eps > 0.f) || !std::isfinite(d->rms_eps)) return fail(err, DEC_ERR_BAD_DESC, "rms_eps must be > 0");
+  if (!(d->rope_base > 1.f) || !std::isfinite(d->rope_base)) return fail(err, DEC_ERR_BAD_DESC, "rope_base must be > 1");
+  if (d->flags != 0) return fail(err, DEC_ERR_BAD_DESC, "flags must be 0");
+  if (d->batch < 1) return fail(err, DEC_ERR_BAD_DESC, "batch must be >= 1");
+  const long long q = (long long)d->n_heads * hd;
+  if (q % 8) return fail(err, DEC_ERR_BAD_DESC, "n_heads*head_dim must be a multiple of 8");
+  if (d->batch != 1) return fail(err, DEC_ERR_UNSUPPORTED, "batch > 1 is not implemented in this build");
+  if (d->d_model > kMaxK || q > kMaxK || d->d_ffn > kMaxK)
+    return fail(err, DEC_ERR_UNSUPPORTED, "d_model, n_heads*head_dim and d_ffn must be <= %d", kMaxK);
+  // largest matrix must be addressable with 32-bit byte offsets
+  const long long lm_bytes = 2LL * d->lm_vocab * d->d_model;
+  const long long big = std::max({lm_bytes, 2LL * 3 * q * d->d_model, 2LL * 2 * d->d_ffn * d->d_model});
+  if (big >= (1LL << 31)) return fail(err, DEC_ERR_UNSUPPORTED, "a weight matrix is 2 GiB or larger");
+  if (2LL * d->max_ctx * hd >= (1LL << 31)) return fail(err, DEC_ERR_UNSUPPORTED, "KV cache of one head is 2 GiB or larger");
+  if ((long long)d->n_heads * max_attn_chunks(d->max_ctx, d->n_heads, 1024) > 4096)
+    return fail(err, DEC_ERR_UNSUPPORTED, "too many attention partials (n_heads x chunks > 4096)");
+  return DEC_OK;
+}
+
+// ---------------------------------------------------------------------------
+// packed image layout (elements)
+// ---------------------------------------------------------------------------
+struct Image {
+  size_t off_qkv, off_o, off_gu, off_d, layer_stride, off_E, off_lm, total;
+};
+
+size_t al128(size_t n) { return (n + 127) / 128 * 128; }
+
+Image image_layout(const dec_model_desc& d) {
+  Image im;
+  const size_t D = d.d_model, q = (size_t)d.n_heads * d.head_dim, F = d.d_ffn;
+  im.off_qkv = 0;
+  im.off_o = al128(im.off_qkv + 3 * q * D);
+  im.off_gu = al128(im.off_o + D * q);
+  im.off_d = al128(im.off_gu + 2 * F * D);
+  im.layer_stride = al128(im.off_d + D * F);
+  im.off_E = im.layer_stride * d.n_layers;
+  im.off_lm = al128(im.off_E + (size_t)d.vocab * D);
+  im.total = al128(im.off_lm + (size_t)d.lm_vocab * D);
+  return im;
+}
+
+// shape of canonical tensor `idx`
+void tensor_shape(const dec_model_desc& d, int idx, size_t* r, size_t* c) {
+  const size_t D = d.d_model, q = (size_t)d.n_heads * d.head_dim, F = d.d_ffn;
+  const int last = n_tensors_for(d) - 1;
+  if (idx == 0) { *r = d.vocab; *c = D; return; }
+  if (idx == last) { *r = d.lm_vocab; *c = D; return; }
+  if (idx == last - 1) { *r = D; *c = 1; return; }
+  switch ((idx - 1) % 9) {
+    case 0: case 5: *r = D; *c = 1; return;            // gains
+    case 1: case 2: case 3: *r = q; *c = D; return;     // Wq, Wk, Wv
+    case 4: *r = D; *c = q; return;                     // Wo
+    case 6: case 7: *r = F; *c = D; return;             // Wg, Wu
+    default: *r = D; *c = F; return;                   // Wd
+  }
+}
+
+// Place canonical tensor idx (fp16 bits, row-major) into the packed image;
+// gains go to gains_out (fp32) instead.  Rows may be passed in slices.
+void place_tensor(const dec_model_desc& d, const Image& im, int idx, const uint16_t* src,
+                  size_t row0, size_t nrows, uint16_t* image, float* gains_out) {
+  size_t R, C;
+  tensor_shape(d, idx, &R, &C);
+  const size_t D = d.d_model, q = (size_t)d.n_heads * d.head_dim;
+  const int last = n_tensors_for(d) - 1;
+  auto half_to_float = [](uint16_t h) {
+    const uint32_t s = (uint32_t)(h >> 15) << 31;
+    const uint32_t e = (h >> 10) & 0x1f, m = h & 0x3ff;
+    uint32_t bits;
+    if (e == 0) {
+      if (m == 0) bits = s;
+      else {  // subnormal: value m * 2^-24, exact in fp32
+        float f = (float)m * 5.9604644775390625e-08f;
+        std::memcpy(&bits, &f, 4);
+        bits |= s;
+      }
+    } else if (e == 31) bits = s | 0x7f800000u | (m << 13);
+    else bits = s | ((e + 112) << 23) | (m << 13);
+    float f;
+    std::memcpy(&f, &bits, 4);
+    return f;
+  };
+  if (idx == 0) {
+    std::memcpy(image + im.off_E + row0 * C, src, nrows * C * 2);
+    return;
+  }
+  if (idx == last) {
+    std::memcpy(image + im.off_lm + row0 * C, src, nrows * C * 2);
+    return;
+  }
+  if (idx == last - 1) {
+    for (size_t i = 0; i < nrows; ++i) gains_out[(size_t)d.n_layers * 2 * D + row0 + i] = half_to_float(src[i]);
+    return;
+  }
+  const int l = (idx - 1) / 9, kind = (idx - 1) % 9;
+  uint16_t* lay = image + (size_t)l * im.layer_stride;
+  switch (kind) {
+    case 0:
+    case 5:
+      for (size_t i = 0; i < nrows; ++i)
+        gains_out[((size_t)l * 2 + (kind == 5)) * D + row0 + i] = half_to_float(src[i]);
+      return;
+    case 1: case 2: case 3:  // Wq, Wk, Wv stacked into Wqkv
+      std::memcpy(lay + im.off_qkv + ((kind - 1) * q + row0) * C, src, nrows * C * 2);
+      return;
+    case 4:
+      std::memcpy(lay + im.off_o + row0 * C, src, nrows * C * 2);
+      return;
+    case 6: case 7:          // Wg -> even rows, Wu -> odd rows of Wgu
+      for (size_t i = 0; i < nrows; ++i)
+        std::memcpy(lay + im.off_gu + (2 * (row0 + i) + (kind == 7)) * C, src + i * C, C * 2);
+      return;
+    default:
+      std::memcpy(lay + im.off_d + row0 * C, src, nrows * C * 2);
+      return;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// DECW weight file
+// ---------------------------------------------------------------------------
+constexpr size_t kHdrBytes = 72, kEntryBytes = 40;
+
+struct FileEntry { uint32_t index, dtype, ndim, dim0, dim1; uint64_t offset, nbytes; };
+
+template <class T> T rd(const unsigned char* p) { T v; std::memcpy(&v, p, sizeof v); return v; }
+
+int read_file_header(FILE* f, dec_model_desc* out, std::vector<FileEntry>* entries, std::string* err) {
+  unsigned char h[kHdrBytes];
+  if (fseek(f, 0, SEEK_END) != 0) return fail(err, DEC_ERR_WEIGHTS, "cannot seek weight file");
+  const long long fsize = ftell(f);
+  fseek(f, 0, SEEK_SET);
+  if (fsize < (long long)kHdrBytes || fread(h, 1, kHdrBytes, f) != kHdrBytes)
+    return fail(err, DEC_ERR_WEIGHTS, "weight file shorter than its header");
+  if (std::memcmp(h, "DECW", 4) != 0) return fail(err, DEC_ERR_WEIGHTS, "bad magic (not a DECW file)");
+  if (rd<uint32_t>(h + 4) != 1) return fail(err, DEC_ERR_WEIGHTS, "unsupported DECW version %u", rd<uint32_t>(h + 4));
+  const uint32_t n = rd<uint32_t>(h + 8);
+  dec_model_desc d;
+  std::memset(&d, 0, sizeof d);
+  int32_t* ints = &d.n_layers;
+  for (int i = 0; i < 10; ++i) ints[i] = rd<int32_t>(h + 16 + 4 * i);
+  d.rms_eps = rd<float>(h + 56);
+  d.rope_base = rd<float>(h + 60);
+  d.flags = rd<uint32_t>(h + 64);
+  int rc = check_desc_impl(&d, err);
+  if (rc == DEC_ERR_BAD_DESC) return fail(err, DEC_ERR_WEIGHTS, "weight file description invalid: %s", err ? err->c_str() : g_err.c_str());
+  if ((int)n != n_tensors_for(d)) return fail(err, DEC_ERR_WEIGHTS, "weight file has %u tensors, description needs %d", n, n_tensors_for(d));
+  if (fsize < (long long)(kHdrBytes + n * kEntryBytes)) return fail(err, DEC_ERR_WEIGHTS, "weight file truncated in its tensor table");
+  std::vector<unsigned char> tab(n * kEntryBytes);
+  if (fread(tab.data(), 1, tab.size(), f) != tab.size()) return fail(err, DEC_ERR_WEIGHTS, "cannot read tensor table");
+  entries->resize(n);
+  for (uint32_t i = 0; i < n; ++i) {
+    const unsigned char* e = tab.data() + i * kEntryBytes;
+    FileEntry fe{rd<uint32_t>(e), rd<uint32_t>(e + 4), rd<uint32_t>(e + 8), rd<uint32_t>(e + 16), rd<uint32_t>(e + 20),
+                 rd<uint64_t>(e + 24), rd<uint64_t>(e + 32)};
+    size_t R, C;
+    tensor_shape(d, (int)i, &R, &C);
+    if (fe.index != i) return fail(err, DEC_ERR_WEIGHTS, "tensor %u: index field %u out of order", i, fe.index);
+    if (fe.dtype != 1) return fail(err, DEC_ERR_WEIGHTS, "tensor %u: dtype %u is not fp16", i, fe.dtype);
+    const bool vec = (C == 1);
+    if (vec ? !(fe.ndim == 1 && fe.dim0 == R && fe.dim1 == 1) : !(fe.ndim == 2 && fe.dim0 == R && fe.dim1 == C))
+      return fail(err, DEC_ERR_WEIGHTS, "tensor %u: shape (%u,%u) does not match the description (%zu,%zu)", i, fe.dim0, fe.dim1, R, C);
+    if (fe.nbytes != 2ull * R * C) return fail(err, DEC_ERR_WEIGHTS, "tensor %u: nbytes %llu != %llu", i, (unsigned long long)fe.nbytes, 2ull * R * C);
+    if (fe.offset % 256) return fail(err, DEC_ERR_WEIGHTS, "tensor %u: offset not 256-byte aligned", i);
+    if (fe.offset < kHdrBytes + n * kEntryBytes || fe.offset + fe.nbytes > (uint64_t)fsize)
+      return fail(err, DEC_ERR_WEIGHTS, "tensor %u: payload [%llu, %llu) outside the file (size %lld)", i,
+                  (unsigned long long)fe.offset, (unsigned long long)(fe.offset + fe.nbytes), fsize);
+    (*entries)[i] = fe;
+  }
+  *out = d;
+  return DEC_OK;
+}
+
+bool same_shape(const dec_model_desc& a, const dec_model_desc& b) {
+  return a.n_layers == b.n_layers && a.d_model == b.d_model && a.n_heads == b.n_heads && a.n_kv_heads == b.n_kv_heads &&
+         a.head_dim == b.head_dim && a.d_ffn == b.d_ffn && a.vocab == b.vocab && a.lm_vocab == b.lm_vocab;
+}
+
+// ---------------------------------------------------------------------------
+// device arena layout (bytes)
+// ---------------------------------------------------------------------------
+struct Arena {
+  size_t w, gains, rope, kv, x, qkv, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out, prompt, ctl, params, total;
+};
+
+Arena arena_layout(const dec_model_desc& d, int G) {
+  Arena a;
+  const Image im = image_layout(d);
+  const size_t D = d.d_model, q = (size_t)d.n_heads * d.head_dim;
+  const int mc = max_attn_chunks(d.max_ctx, d.n_heads, G);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  a.w = take(im.total * 2);
+  a.gains = take(((size_t)d.n_layers * 2 + 1) * D * 4);
+  a.rope = take((size_t)d.max_ctx * (d.head_dim / 2) * 2 * 4);
+  a.kv = take((size_t)d.n_layers * 2 * d.n_heads * d.max_ctx * d.head_dim * 2);
+  a.x = take(D * 4);
+  a.qkv = take(3 * q * 4);
+  a.part = take((size_t)d.n_heads * mc * d.head_dim * 4);
+  a.pml = take((size_t)d.n_heads * mc * 2 * 4);
+  a.act = take((size_t)d.d_ffn * 4);
+  a.logits = take((size_t)d.lm_vocab * 4);
+  a.amax_v = take((size_t)G * 4);
+  a.amax_i = take((size_t)G * 4);
+  a.tok_cur = take(4);
+  a.tok_out = take((size_t)d.max_ctx * 4);
+  a.prompt = take((size_t)d.max_ctx * 4);
+  a.ctl = take(kCtlWords * 4);
+  a.params = take(sizeof(Params));
+  a.total = o;
+  return a;
+}
+
+}  // namespace
+
+struct dec_handle {
+  dec_model_desc desc;
+  std::string err;
+  int device = 0;
+  int grid = 0;
+  hipStream_t stream = nullptr;
+  bool own_stream = false;
+  void* base = nullptr;
+  bool own_arena = false;
+  Arena ar;
+  Image im;
+  Params P;               // host copy
+  Params* dP = nullptr;   // device copy read by the kernel
+  uint32_t debug = 0;
+  uint32_t bar_done = 0;   // barriers completed by resident launches (wrapping)
+  int pos = 0;
+  bool broken = false;     // a launch failed; only dec_reset/dec_free are allowed
+  bool has_prev_tok = false;
+};
+
+namespace {
+
+int hip_fail(dec_handle* h, std::string* err, hipError_t e, const char* what) {
+  if (h) h->broken = true;
+  return fail(err, DEC_ERR_DEVICE, "%s failed: %s", what, hipGetErrorString(e));
+}
+#define HIPCHK(h, err, call) do { hipError_t e_ = (call); if (e_ != hipSuccess) return hip_fail(h, err, e_, #call); } while (0)
+
+int launch(dec_handle* h, int pos0, int n_tok, int tok_src, int lm_last_only, int write_logits) {
+  Launch A;
+  A.pos0 = pos0;
+  A.n_tok = n_tok;
+  A.tok_src = tok_src;
+  A.lm_last_only = lm_last_only;
+  A.write_logits = write_logits;
+  A.fenced = 0;
+  A.phase_begin = 0;
+  A.phase_end = 0x7fffffff;
+  if (h->debug & DEC_DEBUG_MULTILAUNCH) {
+    // one ordinary launch per phase: the kernel boundary is the barrier
+    const int ppt = phases_per_token(h->desc.n_layers);
+    A.bar_base = h->bar_done;
+    for (int i = 0; i < n_tok; ++i) {
+      const bool lm = !lm_last_only || i == n_tok - 1;
+      const int nph = kPhasesPerLayer * h->desc.n_layers + (lm ? 2 : 0);
+      for (int k = 0; k < nph; ++k) {
+        A.phase_begin = i * ppt + k;
+        A.phase_end = A.phase_begin + 1;
+        HIPCHK(h, &h->err, (hipError_t)kernel_launch_plain(h->dP, A, h->grid, h->stream));
+      }
+    }
+    return DEC_OK;
+  }
+  A.bar_base = h->bar_done;
+  HIPCHK(h, &h->err, (hipError_t)kernel_launch_resident(h->dP, A, h->grid, h->stream));
+  h->bar_done += launch_barriers(h->desc.n_layers, n_tok, lm_last_only);
+  return DEC_OK;
+}
+
+int check_device_error(dec_handle* h) {
+  uint32_t e = 0;
+  HIPCHK(h, &h->err, hipMemcpyAsync(&e, h->P.ctl + kCtlErr, 4, hipMemcpyDeviceToHost, h->stream));
+  HIPCHK(h, &h->err, hipStreamSynchronize(h->stream));
+  if (e != 0) {
+    h->broken = true;
+    if ((int)e == kDevErrTimeout)
+      return fail(&h->err, DEC_ERR_TIMEOUT, "a grid barrier wait passed the watchdog bound; call dec_reset");
+    return fail(&h->err, DEC_ERR_DEVICE, "device raised error %d; call dec_reset", (int)e);
+  }
+  return DEC_OK;
+}
+
+int finish(dec_handle* h, int32_t* out_tok, int n_tok_out, float* out_logits) {
+  int rc = check_device_error(h);
+  if (rc) return rc;
+  if (out_tok) HIPCHK(h, &h->err, hipMemcpy(out_tok, h->P.tok_out, (size_t)n_tok_out * 4, hipMemcpyDeviceToHost));
+  if (out_logits)
+    HIPCHK(h, &h->err, hipMemcpy(out_logits, h->P.logits, (size_t)h->desc.lm_vocab * 4, hipMemcpyDeviceToHost));
+  return DEC_OK;
+}
+
+int upload_weights(dec_handle* h, const dec_weights_src* src) {
+  const dec_model_desc& d = h->desc;
+  const int nt = n_tensors_for(d);
+  std::vector<float> gains(((size_t)d.n_layers * 2 + 1) * d.d_model, 0.f);
+  // Pack one layer (or the embedding / LM head) at a time into a host
+  // staging image and copy it to its place in the device image.
+  const size_t chunk_elems = std::max(h->im.layer_stride, (size_t)1);
+  std::vector<uint16_t> stage;
+  uint16_t* dev_w = reinterpret_cast<uint16_t*>(static_cast<char*>(h->base) + h->ar.w);
+  std::vector<FileEntry> entries;
+  FILE* f = nullptr;
+  if (src->path) {
+    f = std::fopen(src->path, "rb");
+    if (!f) return fail(&h->err, DEC_ERR_WEIGHTS, "cannot open weight file '%s'", src->path);
+    dec_model_desc fd;
+    int rc = read_file_header(f, &fd, &entries, &h->err);
+    if (rc) { std::fclose(f); return rc; }
+    if (!same_shape(fd, d)) {
+      std::fclose(f);
+      return fail(&h->err, DEC_ERR_WEIGHTS, "weight file shapes differ from the model description");
+    }
+  }
+  std::vector<uint16_t> rowbuf;
+  auto fetch = [&](int idx, std::vector<uint16_t>& tmp) -> const uint16_t* {
+    size_t R, C;
+    tensor_shape(d, idx, &R, &C);
+    if (!f) return src->host_tensors[idx];
+    tmp.resize(R * C);
+    if (fseeko(f, (off_t)entries[idx].offset, SEEK_SET) != 0 || std::fread(tmp.data(), 2, R * C, f) != R * C) return nullptr;
+    return tmp.data();
+  };
+  int rc = DEC_OK;
+  const Image local = h->im;
+  // layers: a one-layer description has the same per-layer offsets and stride
+  dec_model_desc one = d;
+  one.n_layers = 1;
+  const Image im1 = image_layout(one);
+  std::vector<float> g1(3 * (size_t)d.d_model);
+  for (int l = 0; l < d.n_layers && rc == DEC_OK; ++l) {
+    stage.assign(chunk_elems, 0);
+    for (int kind = 0; kind < 9; ++kind) {
+      const int idx = 1 + 9 * l + kind;
+      const uint16_t* t = fetch(idx, rowbuf);
+      if (!t) { rc = fail(&h->err, DEC_ERR_WEIGHTS, "cannot read tensor %d from the weight file", idx); break; }
+      size_t R, C;
+      tensor_shape(d, idx, &R, &C);
+      place_tensor(one, im1, 1 + kind, t, 0, R, stage.data(), g1.data());
+    }
+    if (rc != DEC_OK) break;
+    std::memcpy(gains.data() + (size_t)l * 2 * d.d_model, g1.data(), 2 * (size_t)d.d_model * 4);
+    hipError_t e = hipMemcpy(dev_w + (size_t)l * local.layer_stride, stage.data(), local.layer_stride * 2, hipMemcpyHostToDevice);
+    if (e != hipSuccess) rc = hip_fail(h, &h->err, e, "hipMemcpy(weights)");
+  }
+  // embedding, final gain, LM head: already row-major, copied as they are
+  const int last = nt - 1;
+  for (int idx : {0, last - 1, last}) {
+    if (rc != DEC_OK) break;
+    const uint16_t* t = fetch(idx, rowbuf);
+    if (!t) { rc = fail(&h->err, DEC_ERR_WEIGHTS, "cannot read tensor %d from the weight file", idx); break; }
+    size_t R, C;
+    tensor_shape(d, idx, &R, &C);
+    if (idx == last - 1) {
+      place_tensor(d, local, idx, t, 0, R, nullptr, gains.data());
+      continue;
+    }
+    const size_t off = idx == 0 ? local.off_E : local.off_lm;
+    hipError_t e = hipMemcpy(dev_w + off, t, R * C * 2, hipMemcpyHostToDevice);
+    if (e != hipSuccess) rc = hip_fail(h, &h->err, e, "hipMemcpy(embedding/LM head)");
+  }
+  if (f) std::fclose(f);
+  if (rc) return rc;
+  HIPCHK(h, &h->err, hipMemcpy(static_cast<char*>(h->base) + h->ar.gains, gains.data(), gains.size() * 4, hipMemcpyHostToDevice));
+  return DEC_OK;
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+int32_t dec_abi_version(void) { return DEC_ABI_VERSION; }
+
+int dec_check_desc(const dec_model_desc* desc) { return check_desc_impl(desc, nullptr); }
+
+int dec_arena_bytes(const dec_model_desc* desc, int32_t grid, size_t* out_bytes) {
+  if (!out_bytes) return fail(nullptr, DEC_ERR_INVALID_ARG, "out_bytes is NULL");
+  int rc = check_desc_impl(desc, nullptr);
+  if (rc) return rc;
+  if (grid < 0 || grid > 1024) return fail(nullptr, DEC_ERR_INVALID_ARG, "grid must be in [0, 1024]");
+  *out_bytes = arena_layout(*desc, grid ? grid : 256).total;
+  return DEC_OK;
+}
+
+int dec_packed_bytes(const dec_model_desc* desc, size_t* out_bytes) {
+  if (!out_bytes) return fail(nullptr, DEC_ERR_INVALID_ARG, "out_bytes is NULL");
+  int rc = check_desc_impl(desc, nullptr);
+  if (rc) return rc;
+  *out_bytes = image_layout(*desc).total * 2;
+  return DEC_OK;
+}
+
+int dec_pack(const dec_model_desc* desc, const uint16_t* const* host_tensors, int32_t n_tensors, void* dst, size_t dst_bytes) {
+  int rc = check_desc_impl(desc, nullptr);
+  if (rc) return rc;
+  if (!host_tensors || !dst) return fail(nullptr, DEC_ERR_INVALID_ARG, "NULL tensor list or destination");
+  if (n_tensors != n_tensors_for(*desc))
+    return fail(nullptr, DEC_ERR_WEIGHTS, "expected %d tensors, got %d", n_tensors_for(*desc), n_tensors);
+  const Image im = image_layout(*desc);
+  if (dst_bytes < im.total * 2) return fail(nullptr, DEC_ERR_INVALID_ARG, "destination smaller than %zu bytes", im.total * 2);
+  std::memset(dst, 0, im.total * 2);
+  std::vector<float> gains(((size_t)desc->n_layers * 2 + 1) * desc->d_model);
+  for (int i = 0; i < n_tensors; ++i) {
+    if (!host_tensors[i]) return fail(nullptr, DEC_ERR_WEIGHTS, "tensor %d is NULL", i);
+    size_t R, C;
+    tensor_shape(*desc, i, &R, &C);
+    place_tensor(*desc, im, i, host_tensors[i], 0, R, static_cast<uint16_t*>(dst), gains.data());
+  }
+  return DEC_OK;
+}
+
+int dec_weights_file_check(const char* path, dec_model_desc* out_desc) {
+  if (!path || !out_desc) return fail(nullptr, DEC_ERR_INVALID_ARG, "NULL path or output");
+  FILE* f = std::fopen(path, "rb");
+  if (!f) return fail(nullptr, DEC_ERR_WEIGHTS, "cannot open weight file '%s'", path);
+  std::vector<FileEntry> entries;
+  int rc = read_file_header(f, out_desc, &entries, nullptr);
+  std::fclose(f);
+  return rc;
+}
+
+int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const dec_init_opts* opts, dec_handle** out) {
+  if (!out) return fail(nullptr, DEC_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  int rc = check_desc_impl(desc, nullptr);
+  if (rc) return rc;
+  if (!weights) return fail(nullptr, DEC_ERR_INVALID_ARG, "weights is NULL");
+  if ((weights->path == nullptr) == (weights->host_tensors == nullptr))
+    return fail(nullptr, DEC_ERR_INVALID_ARG, "exactly one of weights->path and weights->host_tensors must be set");
+  if (weights->host_tensors) {
+    if (weights->n_tensors != n_tensors_for(*desc))
+      return fail(nullptr, DEC_ERR_WEIGHTS, "expected %d tensors, got %d", n_tensors_for(*desc), weights->n_tensors);
+    for (int i = 0; i < weights->n_tensors; ++i)
+      if (!weights->host_tensors[i]) return fail(nullptr, DEC_ERR_WEIGHTS, "tensor %d is NULL", i);
+  } else {
+    FILE* f = std::fopen(weights->path, "rb");
+    if (!f) return fail(nullptr, DEC_ERR_WEIGHTS, "cannot open weight file '%s'", weights->path);
+    dec_model_desc fd;
+    std::vector<FileEntry> entries;
+    rc = read_file_header(f, &fd, &entries, nullptr);
+    std::fclose(f);
+    if (rc) return rc;
+    if (!same_shape(fd, *desc)) return fail(nullptr, DEC_ERR_WEIGHTS, "weight file shapes differ from the model description");
+  }
+  dec_init_opts o;
+  std::memset(&o, 0, sizeof o);
+  if (opts) o = *opts;
+  if (o.grid < 0 || o.grid > 1024) return fail(nullptr, DEC_ERR_INVALID_ARG, "grid must be in [0, 1024]");
+  if (o.watchdog_us < 0) return fail(nullptr, DEC_ERR_INVALID_ARG, "watchdog_us must be >= 0");
+
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return fail(nullptr, DEC_ERR_NO_DEVICE, "no HIP device visible");
+  if (o.device < 0 || o.device >= ndev) return fail(nullptr, DEC_ERR_NO_DEVICE, "device %d not present (%d visible)", o.device, ndev);
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, o.device) != hipSuccess) return fail(nullptr, DEC_ERR_NO_DEVICE, "cannot query device %d", o.device);
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(nullptr, DEC_ERR_NO_DEVICE, "device %d is %s; this library is built for gfx950", o.device, prop.gcnArchName);
+  if (hipSetDevice(o.device) != hipSuccess) return fail(nullptr, DEC_ERR_NO_DEVICE, "hipSetDevice(%d) failed", o.device);
+
+  dec_handle* h = new (std::nothrow) dec_handle();
+  if (!h) return fail(nullptr, DEC_ERR_OOM, "host allocation failed");
+  h->desc = *desc;
+  h->device = o.device;
+  h->debug = o.debug_flags;
+  const int cus = prop.multiProcessorCount;
+  h->grid = o.grid ? o.grid : cus;
+  auto bail = [&](int code) {
+    g_err = h->err;
+    dec_free(h);
+    return code;
+  };
+  // the resident kernel needs every workgroup co-resident
+  int coop = 0;
+  (void)hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, o.device);
+  if (!coop && !(h->debug & DEC_DEBUG_MULTILAUNCH)) {
+    fail(&h->err, DEC_ERR_UNSUPPORTED, "device lacks cooperative launch");
+    return bail(DEC_ERR_UNSUPPORTED);
+  }
+  hipError_t e = (hipError_t)kernel_prepare();
+  if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipFuncSetAttribute"); return bail(DEC_ERR_DEVICE); }
+  int per_cu = 0;
+  e = (hipError_t)kernel_blocks_per_cu(&per_cu);
+  if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"); return bail(DEC_ERR_DEVICE); }
+  if (per_cu < 1 || h->grid > per_cu * cus) {
+    fail(&h->err, DEC_ERR_UNSUPPORTED, "grid %d exceeds co-resident capacity %d x %d", h->grid, per_cu, cus);
+    return bail(DEC_ERR_UNSUPPORTED);
+  }
+  if (o.stream) {
+    h->stream = static_cast<hipStream_t>(o.stream);
+  } else {
+    e = hipStreamCreateWithFlags(&h->stream, hipStreamNonBlocking);
+    if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipStreamCreate"); return bail(DEC_ERR_DEVICE); }
+    h->own_stream = true;
+  }
+  h->im = image_layout(*desc);
+  h->ar = arena_layout(*desc, h->grid);
+  if (o.arena) {
+    if (reinterpret_cast<uintptr_t>(o.arena) % kAlign) { fail(&h->err, DEC_ERR_INVALID_ARG, "arena is not 256-byte aligned"); return bail(DEC_ERR_INVALID_ARG); }
+    if (o.arena_bytes < h->ar.total) {
+      fail(&h->err, DEC_ERR_OOM, "arena of %zu bytes is smaller than the %zu needed", o.arena_bytes, h->ar.total);
+      return bail(DEC_ERR_OOM);
+    }
+    h->base = o.arena;
+  } else {
+    e = hipMalloc(&h->base, h->ar.total);
+    if (e != hipSuccess) {
+      h->base = nullptr;
+      fail(&h->err, DEC_ERR_OOM, "hipMalloc of %zu bytes failed: %s", h->ar.total, hipGetErrorString(e));
+      return bail(DEC_ERR_OOM);
+    }
+    h->own_arena = true;
+  }
+  char* b = static_cast<char*>(h->base);
+  // zero activations and control words (weights and cache are overwritten)
+  e = hipMemset(b + h->ar.x, 0, h->ar.total - h->ar.x);
+  if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemset"); return bail(DEC_ERR_DEVICE); }
+  rc = upload_weights(h, weights);
+  if (rc) return bail(rc);
+  // rotary table: cos/sin(p * base^(-2i/hd)) in double, stored as fp32
+  {
+    const int half = desc->head_dim / 2;
+    std::vector<float> tab((size_t)desc->max_ctx * half * 2);
+    for (int p = 0; p < desc->max_ctx; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double theta = std::pow((double)desc->rope_base, -2.0 * i / desc->head_dim);
+        const double ang = (double)p * theta;
+        tab[((size_t)p * half + i) * 2] = (float)std::cos(ang);
+        tab[((size_t)p * half + i) * 2 + 1] = (float)std::sin(ang);
+      }
+    e = hipMemcpy(b + h->ar.rope, tab.data(), tab.size() * 4, hipMemcpyHostToDevice);
+    if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemcpy(rope)"); return bail(DEC_ERR_DEVICE); }
+  }
+  int wall_khz = 100000;
+  (void)hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, o.device);
+  if (wall_khz <= 0) wall_khz = 100000;
+  const double wd_us = o.watchdog_us ? (double)o.watchdog_us : 2.0e6;
+  const double ticks = wd_us * wall_khz / 1000.0;
+  Params& P = h->P;
+  P.L = desc->n_layers; P.d = desc->d_model; P.H = desc->n_heads; P.hd = desc->head_dim; P.F = desc->d_ffn;
+  P.V = desc->vocab; P.Vlm = desc->lm_vocab; P.max_ctx = desc->max_ctx; P.q = desc->n_heads * desc->head_dim;
+  P.eps = desc->rms_eps;
+  P.w = reinterpret_cast<const uint16_t*>(b + h->ar.w);
+  P.layer_stride = h->im.layer_stride;
+  P.off_qkv = h->im.off_qkv; P.off_o = h->im.off_o; P.off_gu = h->im.off_gu; P.off_d = h->im.off_d;
+  P.off_E = h->im.off_E; P.off_lm = h->im.off_lm;
+  P.gains = reinterpret_cast<const float*>(b + h->ar.gains);
+  P.rope = reinterpret_cast<const float*>(b + h->ar.rope);
+  P.kv = reinterpret_cast<uint16_t*>(b + h->ar.kv);
+  P.x = reinterpret_cast<float*>(b + h->ar.x);
+  P.qkv = reinterpret_cast<float*>(b + h->ar.qkv);
+  P.part = reinterpret_cast<float*>(b + h->ar.part);
+  P.pml = reinterpret_cast<float*>(b + h->ar.pml);
+  P.act = reinterpret_cast<float*>(b + h->ar.act);
+  P.logits = reinterpret_cast<float*>(b + h->ar.logits);
+  P.amax_v = reinterpret_cast<float*>(b + h->ar.amax_v);
+  P.amax_i = reinterpret_cast<int*>(b + h->ar.amax_i);
+  P.tok_cur = reinterpret_cast<int*>(b + h->ar.tok_cur);
+  P.tok_out = reinterpret_cast<int*>(b + h->ar.tok_out);
+  P.prompt = reinterpret_cast<const int*>(b + h->ar.prompt);
+  P.ctl = reinterpret_cast<uint32_t*>(b + h->ar.ctl);
+  P.max_chunks = max_attn_chunks(desc->max_ctx, desc->n_heads, h->grid);
+  P.watchdog_ticks = (uint32_t)std::min(ticks, 4.0e9);
+  h->dP = reinterpret_cast<Params*>(b + h->ar.params);
+  e = hipMemcpy(h->dP, &P, sizeof(Params), hipMemcpyHostToDevice);
+  if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemcpy(params)"); return bail(DEC_ERR_DEVICE); }
+  if (hipDeviceSynchronize() != hipSuccess) { fail(&h->err, DEC_ERR_DEVICE, "device synchronize failed after upload"); return bail(DEC_ERR_DEVICE); }
+  *out = h;
+  return DEC_OK;
+}
+
+int dec_prefill(dec_handle* h, const int32_t* tokens, int32_t n, int32_t* out_tok, float* out_logits) {
+  if (!h) return fail(nullptr, DEC_ERR_INVALID_ARG, "handle is NULL");
+  if (!tokens || !out_tok) return fail(&h->err, DEC_ERR_INVALID_ARG, "tokens and out_tok are required");
+  if (h->broken) return fail(&h->err, DEC_ERR_STATE, "handle is in an error state; call dec_reset");
+  if (h->pos != 0) return fail(&h->err, DEC_ERR_STATE, "prefill needs position 0 (call dec_reset)");
+  if (n < 1) return fail(&h->err, DEC_ERR_INVALID_ARG, "n must be >= 1");
+  if (n > h->desc.max_ctx) return fail(&h->err, DEC_ERR_CONTEXT_FULL, "prompt of %d tokens exceeds max_ctx %d", n, h->desc.max_ctx);
+  for (int i = 0; i < n; ++i)
+    if (tokens[i] < 0 || tokens[i] >= h->desc.vocab)
+      return fail(&h->err, DEC_ERR_TOKEN_RANGE, "prompt token %d = %d outside [0, %d)", i, tokens[i], h->desc.vocab);
+  HIPCHK(h, &h->err, hipMemcpyAsync(const_cast<int*>(h->P.prompt), tokens, (size_t)n * 4, hipMemcpyHostToDevice, h->stream));
+  int rc = launch(h, 0, n, TOK_PROMPT, 1, out_logits != nullptr);
+  if (rc) return rc;
+  h->pos = n;
+  h->has_prev_tok = true;
+  // the launch computed token index n-1's argmax
+  rc = check_device_error(h);
+  if (rc) return rc;
+  HIPCHK(h, &h->err, hipMemcpy(out_tok, h->P.tok_out + (n - 1), 4, hipMemcpyDeviceToHost));
+  if (out_logits) HIPCHK(h, &h->err, hipMemcpy(out_logits, h->P.logits, (size_t)h->desc.lm_vocab * 4, hipMemcpyDeviceToHost));
+  return DEC_OK;
+}
+
+int dec_step(dec_handle* h, const int32_t* force_tok, int32_t* out_tok, float* out_logits) {
+  if (!h) return fail(nullptr, DEC_ERR_INVALID_ARG, "handle is NULL");
+  if (h->broken) return fail(&h->err, DEC_ERR_STATE, "handle is in an error state; call dec_reset");
+  if (h->pos >= h->desc.max_ctx) return fail(&h->err, DEC_ERR_CONTEXT_FULL, "context is full (%d positions)", h->desc.max_ctx);
+  if (!force_tok && !h->has_prev_tok) return fail(&h->err, DEC_ERR_STATE, "no previous token: prefill first or pass force_tok");
+  if (force_tok) {
+    if (force_tok[0] < 0 || force_tok[0] >= h->desc.vocab)
+      return fail(&h->err, DEC_ERR_TOKEN_RANGE, "token %d outside [0, %d)", force_tok[0], h->desc.vocab);
+    HIPCHK(h, &h->err, hipMemcpyAsync(h->P.tok_cur, force_tok, 4, hipMemcpyHostToDevice, h->stream));
+  }
+  int rc = launch(h, h->pos, 1, TOK_DEVICE, 0, out_logits != nullptr);
+  if (rc) return rc;
+  h->pos += 1;
+  h->has_prev_tok = true;
+  if (!out_tok && !out_logits) return DEC_OK;
+  return finish(h, out_tok, 1, out_logits);
+}
+
+int dec_generate(dec_handle* h, int32_t n_steps, int32_t* out_toks) {
+  if (!h) return fail(nullptr, DEC_ERR_INVALID_ARG, "handle is NULL");
+  if (!out_toks) return fail(&h->err, DEC_ERR_INVALID_ARG, "out_toks is required");
+  if (h->broken) return fail(&h->err, DEC_ERR_STATE, "handle is in an error state; call dec_reset");
+  if (n_steps < 1) return fail(&h->err, DEC_ERR_INVALID_ARG, "n_steps must be >= 1");
+  if (!h->has_prev_tok) return fail(&h->err, DEC_ERR_STATE, "no previous token: prefill first");
+  if ((long long)h->pos + n_steps > h->desc.max_ctx)
+    return fail(&h->err, DEC_ERR_CONTEXT_FULL, "%d steps from position %d pass max_ctx %d", n_steps, h->pos, h->desc.max_ctx);
+  int rc = launch(h, h->pos, n_steps, TOK_DEVICE, 0, 0);
+  if (rc) return rc;
+  h->pos += n_steps;
+  return finish(h, out_toks, n_steps, nullptr);
+}
+
+int dec_sync(dec_handle* h) {
+  if (!h) return fail(nullptr, DEC_ERR_INVALID_ARG, "handle is NULL");
+  if (h->broken) return fail(&h->err, DEC_ERR_STATE, "handle is in an error state; call dec_reset");
+  return check_device_error(h);
+}
+
+int dec_reset(dec_handle* h) {
+  if (!h) return fail(nullptr, DEC_ERR_INVALID_ARG, "handle is NULL");
+  hipError_t e = hipStreamSynchronize(h->stream);
+  if (e != hipSuccess) return fail(&h->err, DEC_ERR_DEVICE, "hipStreamSynchronize failed: %s", hipGetErrorString(e));
+  if (h->broken) {
+    // barrier counters may be mid-epoch after an aborted launch: restart them
+    e = hipMemset(h->P.ctl, 0, kCtlWords * 4);
+    if (e != hipSuccess) return fail(&h->err, DEC_ERR_DEVICE, "hipMemset(control) failed: %s", hipGetErrorString(e));
+    h->bar_done = 0;
+    h->broken = false;
+  }
+  h->pos = 0;
+  h->has_prev_tok = false;
+  return DEC_OK;
+}
+
+int32_t dec_position(const dec_handle* h) { return h ? h->pos : -1; }
+
+int dec_read_kv(dec_handle* h, int32_t layer, int32_t seq, int32_t n_pos, uint16_t* host_k, uint16_t* host_v) {
+  if (!h) return fail(nullptr, DEC_ERR_INVALID_ARG, "handle is NULL");
+  const dec_model_desc& d = h->desc;
+  if (layer < 0 || layer >= d.n_layers || seq < 0 || seq >= d.batch || n_pos < 0 || n_pos > d.max_ctx)
+    return fail(&h->err, DEC_ERR_INVALID_ARG, "layer/seq/n_pos out of range");
+  HIPCHK(h, &h->err, hipStreamSynchronize(h->stream));
+  const size_t head = (size_t)d.max_ctx * d.head_dim;
+  for (int kind = 0; kind < 2; ++kind) {
+    uint16_t* dst = kind ? host_v : host_k;
+    if (!dst) continue;
+    for (int hh = 0; hh < d.n_heads; ++hh) {
+      const uint16_t* src = h->P.kv + (((size_t)layer * 2 + kind) * d.n_heads + hh) * head;
+      HIPCHK(h, &h->err, hipMemcpy(dst + (size_t)hh * n_pos * d.head_dim, src, (size_t)n_pos * d.head_dim * 2, hipMemcpyDeviceToHost));
+    }
+  }
+  return DEC_OK;
+}
+
+void dec_free(dec_handle* h) {
+  if (!h) return;
+  if (h->stream) (void)hipStreamSynchronize(h->stream);
+  if (h->own_arena && h->base) (void)hipFree(h->base);
+  if (h->own_stream && h->stream) (void)hipStreamDestroy(h->stream);
+  delete h;
+}
+
+const char* dec_last_error(const dec_handle* h) {
+  if (h) return h->err.c_str();
+  return g_err.c_str();
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

@@ -1,0 +1,122 @@
+// Internal definitions shared by the host runtime (dec_host.cpp) and the
+// device code (dec_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__HIPCC__) || defined(__HIP__)
+#define DEC_HD __host__ __device__
+#else
+#define DEC_HD
+#endif
+
+namespace decmono {
+
+constexpr int kThreads = 512;               // threads per workgroup (8 wave64)
+constexpr int kWaves = kThreads / 64;
+constexpr int kGroups = 8;                  // barrier groups: workgroup b is in group b % 8
+constexpr int kMaxK = 8192;                 // longest GEMV row supported (16 pieces per lane)
+constexpr int kChunkMin = 32;               // shortest attention chunk (positions)
+constexpr int kChunkMax = 2048;             // longest attention chunk (scores kept in LDS)
+constexpr int kLdsBytes = 100 * 1024;       // dynamic LDS per workgroup; > half a CU's 160 KB,
+                                            // so exactly one workgroup runs per compute unit
+
+// Control words (uint32 index into Params::ctl); each on its own 256-byte line.
+constexpr int kCtlGlobal = 0;               // arrivals of group leaders (cumulative)
+constexpr int kCtlGroup0 = 64;              // group k counter at kCtlGroup0 + 64*k
+constexpr int kCtlErr = 64 * (1 + kGroups); // first error code raised by any workgroup
+constexpr int kCtlWords = 64 * (2 + kGroups);
+
+// Phases of one token.  Per layer: QKV, ATTN, O, GU, DOWN; then LM and ARGMAX
+// when the token's logits are wanted.
+enum Phase : int { PH_QKV = 0, PH_ATTN = 1, PH_O = 2, PH_GU = 3, PH_DOWN = 4 };
+constexpr int kPhasesPerLayer = 5;
+
+enum TokSrc : int { TOK_PROMPT = 0, TOK_DEVICE = 1 };
+
+// Error codes raised on the device (same values as dec_status).
+constexpr int kDevErrTimeout = -10;
+
+struct Params {
+  int L, d, H, hd, F, V, Vlm, max_ctx, q;   // q = H*hd
+  float eps;
+  const uint16_t* w;          // packed weight image (fp16 bits)
+  size_t layer_stride;        // elements between consecutive layers in the image
+  size_t off_qkv, off_o, off_gu, off_d;   // element offsets inside a layer
+  size_t off_E, off_lm;       // element offsets of the embedding and the LM head
+  const float* gains;         // [L][2][d] (attn, ffn) then g_final [d]
+  const float* rope;          // [max_ctx][hd/2][2] (cos, sin)
+  uint16_t* kv;               // [L][2][H][max_ctx][hd] fp16
+  float* x;                   // residual stream [d]
+  float* qkv;                 // [3q]
+  float* part;                // attention partial sums [H][max_chunks][hd]
+  float* pml;                 // attention partial (max, sum) [H][max_chunks][2]
+  float* act;                 // SwiGLU output [F]
+  float* logits;              // [Vlm]
+  float* amax_v;              // per-workgroup best logit [G]
+  int* amax_i;                // per-workgroup best index [G]
+  int* tok_cur;               // token the next step consumes [1]
+  int* tok_out;               // greedy token of each token of a launch [max_ctx]
+  const int* prompt;          // tokens of a prompt launch [max_ctx]
+  uint32_t* ctl;              // control words
+  int max_chunks;
+  uint32_t watchdog_ticks;    // bound on one barrier wait, in wall-clock ticks
+};
+
+struct Launch {
+  int pos0;          // position of the launch's first token
+  int n_tok;         // tokens in this launch
+  int tok_src;       // TOK_PROMPT (prompt[i]) or TOK_DEVICE (*tok_cur, then own argmax)
+  int lm_last_only;  // LM head + argmax only for the last token (prefill)
+  int write_logits;  // store the last token's logits
+  int fenced;        // also issue agent-scope release/acquire fences at barriers
+  uint32_t bar_base; // barriers completed before this launch (wrapping)
+  int phase_begin;   // run only phases with global index in [phase_begin, phase_end)
+  int phase_end;
+};
+
+DEC_HD inline int phases_per_token(int L) { return kPhasesPerLayer * L + 2; }
+
+// Number of attention chunks per head at context length ctx for a grid of G
+// workgroups: as many as keeps every workgroup busy (at most G/H per head),
+// no chunk shorter than kChunkMin or longer than kChunkMax positions.
+DEC_HD inline int attn_chunks(int ctx, int H, int G) {
+  int by_min = (ctx + kChunkMin - 1) / kChunkMin;
+  int by_max = (ctx + kChunkMax - 1) / kChunkMax;
+  int fill = G / H > 0 ? G / H : 1;
+  int c = by_min < fill ? by_min : fill;
+  return c > by_max ? c : by_max;
+}
+
+DEC_HD inline int max_attn_chunks(int max_ctx, int H, int G) {
+  int m = 1;
+  // attn_chunks grows with ctx, so its value at max_ctx bounds every launch
+  m = attn_chunks(max_ctx, H, G);
+  return m < 1 ? 1 : m;
+}
+
+// Grid barriers a resident launch executes: one before every phase except the
+// launch's first and a QKV phase that directly follows this launch's ARGMAX
+// (each workgroup then already holds the token it computed itself).
+inline uint32_t launch_barriers(int L, int n_tok, int lm_last_only) {
+  uint32_t phases = 0, skipped = 0;
+  for (int i = 0; i < n_tok; ++i) {
+    bool lm = !lm_last_only || i == n_tok - 1;
+    phases += kPhasesPerLayer * L + (lm ? 2 : 0);
+    if (i > 0) {
+      bool prev_lm = !lm_last_only || i - 1 == n_tok - 1;
+      if (prev_lm) skipped += 1;
+    }
+  }
+  return phases - 1 - skipped;
+}
+
+// Launch helpers defined next to the kernel (dec_kernels.hip).  P points to a
+// device copy of the parameters; stream is a hipStream_t; each returns a hipError_t value (0 = success).
+int kernel_prepare();                                   // raise the dynamic-LDS limit
+int kernel_blocks_per_cu(int* out);                     // co-resident workgroups per CU
+int kernel_launch_resident(const Params* P, const Launch& A, int grid, void* stream);  // cooperative
+int kernel_launch_plain(const Params* P, const Launch& A, int grid, void* stream);     // ordinary
+
+}  // namespace decmono

@@ -12,9 +12,14 @@ Canonical tensor order (also the order of the C ABI's host tensor list):
   g_final [d], W_lm [lm_vocab, d]
 All matrices are stored [out, in], row-major.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from .shapes import ModelShape, Workload, DENSE_2B
+
+_THREADS = min(16, os.cpu_count() or 1)
 
 LAYER_TENSORS = ("g_attn", "Wq", "Wk", "Wv", "Wo", "g_ffn", "Wg", "Wu", "Wd")
 N_TENSORS_PER_LAYER = len(LAYER_TENSORS)
@@ -52,18 +57,20 @@ def make_weights(shape: ModelShape, seed: int = 0, gain_jitter: float = 0.0):
     gain_jitter > 0 draws every gain as 1 + N(0, gain_jitter) (rounded to
     fp16) instead of 1.0, so that a consumer that ignores gains is caught.
     """
-    out = []
-    for idx, (name, shp) in enumerate(zip(tensor_names(shape), tensor_shapes(shape))):
+    def one(item):
+        idx, (name, shp) = item
         if name.startswith("g_"):
             if gain_jitter > 0.0:
                 rng = np.random.default_rng([seed, idx, 7])
-                g = 1.0 + gain_jitter * rng.standard_normal(shp)
-                out.append(g.astype(np.float16))
-            else:
-                out.append(np.ones(shp, dtype=np.float16))
-        else:
-            out.append(_draw(shp, seed, idx))
-    return out
+                return (1.0 + gain_jitter * rng.standard_normal(shp)).astype(np.float16)
+            return np.ones(shp, dtype=np.float16)
+        return _draw(shp, seed, idx)
+
+    items = list(enumerate(zip(tensor_names(shape), tensor_shapes(shape))))
+    # every tensor has its own generator, so drawing them concurrently
+    # yields exactly the same arrays as drawing them in order
+    with ThreadPoolExecutor(_THREADS) as ex:
+        return list(ex.map(one, items))
 
 
 def lane_slice_weights(lane_shape: ModelShape, full_shape: ModelShape = DENSE_2B, seed: int = 0):
@@ -76,34 +83,31 @@ def lane_slice_weights(lane_shape: ModelShape, full_shape: ModelShape = DENSE_2B
     q, f = lane_shape.qkv_width, lane_shape.d_ffn
     names = tensor_names(full_shape)
     shapes = tensor_shapes(full_shape)
-    out = []
-    for idx, (name, shp) in enumerate(zip(names, shapes)):
+
+    def one(item):
+        idx, (name, shp) = item
         base = name.split(".")[0]
         if base.startswith("g_"):
-            out.append(np.ones(shp, dtype=np.float16))
-            continue
-        if base == "E":
-            out.append(_draw(shp, seed, idx))
-            continue
-        if base == "W_lm":
-            # only the first lm_vocab rows are needed; rows are drawn row-major so
-            # drawing the full table and slicing keeps the lane a true slice.
-            full = _draw(shp, seed, idx)
-            out.append(np.ascontiguousarray(full[:lane_shape.lm_vocab]))
-            del full
-            continue
+            return np.ones(shp, dtype=np.float16)
         full = _draw(shp, seed, idx)
+        if base == "E":
+            return full
+        if base == "W_lm":
+            # rows are drawn row-major, so the first lm_vocab rows of the full
+            # table are exactly the lane's shard
+            return np.ascontiguousarray(full[:lane_shape.lm_vocab])
         if base in ("Wq", "Wk", "Wv"):
-            out.append(np.ascontiguousarray(full[:q]))
-        elif base == "Wo":
-            out.append(np.ascontiguousarray(full[:, :q]))
-        elif base in ("Wg", "Wu"):
-            out.append(np.ascontiguousarray(full[:f]))
-        elif base == "Wd":
-            out.append(np.ascontiguousarray(full[:, :f]))
-        else:
-            raise AssertionError(name)
-        del full
+            return np.ascontiguousarray(full[:q])
+        if base == "Wo":
+            return np.ascontiguousarray(full[:, :q])
+        if base in ("Wg", "Wu"):
+            return np.ascontiguousarray(full[:f])
+        if base == "Wd":
+            return np.ascontiguousarray(full[:, :f])
+        raise AssertionError(name)
+
+    with ThreadPoolExecutor(_THREADS) as ex:
+        out = list(ex.map(one, list(enumerate(zip(names, shapes)))))
     assert len(out) == len(names)
     return out
 

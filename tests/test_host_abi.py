@@ -1,0 +1,196 @@
+"""The C ABI on the CPU: exports, descriptor rules, packer, DECW reader, no-device path.
+
+No compute calls: these run without a GPU.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from memory_bound_transformer_persistent_amd import binding as B
+from memory_bound_transformer_persistent_amd import weights_file as WF
+
+TINY = synth.shape_for("tiny")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def desc(**kw):
+    return B.ModelDesc.from_shape(TINY, **kw)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = B.header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.dec_abi_version() == 1
+    assert set(names) == set(B.SIGNATURES)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("n_layers", 0, B.DEC_ERR_BAD_DESC),
+    ("d_model", 12, B.DEC_ERR_BAD_DESC),
+    ("n_kv_heads", 2, B.DEC_ERR_BAD_DESC),
+    ("head_dim", 48, B.DEC_ERR_BAD_DESC),
+    ("d_ffn", 1001, B.DEC_ERR_BAD_DESC),
+    ("lm_vocab", 4097, B.DEC_ERR_BAD_DESC),
+    ("lm_vocab", 3, B.DEC_ERR_BAD_DESC),
+    ("max_ctx", 0, B.DEC_ERR_BAD_DESC),
+    ("rms_eps", 0.0, B.DEC_ERR_BAD_DESC),
+    ("rope_base", 1.0, B.DEC_ERR_BAD_DESC),
+    ("flags", 1, B.DEC_ERR_BAD_DESC),
+    ("batch", 8, B.DEC_ERR_UNSUPPORTED),
+    ("d_ffn", 8200, B.DEC_ERR_UNSUPPORTED),
+])
+def test_desc_rules(lib, field, value, code):
+    d = desc(**{field: value})
+    assert B.check_desc(d) == code
+    assert B.last_error()  # reason recorded for handle-less calls
+
+
+def test_valid_descs_and_arena(lib):
+    for name in ("tiny", "dense2b", "lane2b"):
+        d = B.ModelDesc.from_shape(synth.shape_for(name))
+        assert B.check_desc(d) == B.DEC_OK, B.last_error()
+    d2 = B.ModelDesc.from_shape(synth.shape_for("dense2b"))
+    n = B.arena_bytes(d2)
+    # weights (with the whole embedding) + a 4096-position fp16 KV cache
+    assert 4.63e9 + 1.04e9 < n < 4.63e9 + 1.04e9 + 64e6
+
+
+def test_packer_layout_round_trip(lib):
+    s = TINY.with_(n_layers=2)
+    t = synth.make_weights(s, seed=3, gain_jitter=0.1)
+    d = B.ModelDesc.from_shape(s)
+    img = B.pack(d, t)
+    assert img.nbytes == B.packed_bytes(d)
+    al = lambda n: (n + 127) // 128 * 128
+    D, q, F = s.d_model, s.qkv_width, s.d_ffn
+    off_o = al(3 * q * D)
+    off_gu = al(off_o + D * q)
+    off_d = al(off_gu + 2 * F * D)
+    stride = al(off_d + D * F)
+    names = synth.tensor_names(s)
+    bits = lambda a: np.ascontiguousarray(a).view(np.uint16)
+    for l in range(s.n_layers):
+        base = l * stride
+        get = lambda n: t[names.index(f"{n}.{l}")]
+        qkv = img[base:base + 3 * q * D].reshape(3 * q, D)
+        np.testing.assert_array_equal(qkv, np.concatenate([bits(get("Wq")), bits(get("Wk")), bits(get("Wv"))]))
+        np.testing.assert_array_equal(img[base + off_o: base + off_o + D * q].reshape(D, q), bits(get("Wo")))
+        gu = img[base + off_gu: base + off_gu + 2 * F * D].reshape(2 * F, D)
+        np.testing.assert_array_equal(gu[0::2], bits(get("Wg")))
+        np.testing.assert_array_equal(gu[1::2], bits(get("Wu")))
+        np.testing.assert_array_equal(img[base + off_d: base + off_d + D * F].reshape(D, F), bits(get("Wd")))
+    off_E = stride * s.n_layers
+    np.testing.assert_array_equal(img[off_E: off_E + s.vocab * D].reshape(s.vocab, D), bits(t[0]))
+    off_lm = al(off_E + s.vocab * D)
+    np.testing.assert_array_equal(img[off_lm: off_lm + s.lm_vocab * D].reshape(s.lm_vocab, D), bits(t[-1]))
+
+
+def test_pack_rejects_wrong_count(lib):
+    d = desc()
+    t = synth.make_weights(TINY)
+    arrs, ptrs = B._tensor_ptrs(t[:-1])
+    out = np.zeros(B.packed_bytes(d) // 2, dtype=np.uint16)
+    assert lib.dec_pack(ctypes.byref(d), ptrs, len(arrs), out.ctypes.data, out.nbytes) == B.DEC_ERR_WEIGHTS
+
+
+@pytest.fixture(scope="module")
+def good_file(tmp_path_factory):
+    p = tmp_path_factory.mktemp("w") / "tiny.decw"
+    WF.write(p, desc(), synth.make_weights(TINY))
+    return p
+
+
+def test_weights_file_round_trip(lib, good_file):
+    rc, d = B.weights_file_check(good_file)
+    assert rc == B.DEC_OK, B.last_error()
+    assert (d.n_layers, d.d_model, d.vocab, d.max_ctx) == (2, 256, 4096, 128)
+    assert abs(d.rms_eps - 1e-5) < 1e-12
+
+
+def _corrupt(src, dst, offset, data):
+    b = bytearray(open(src, "rb").read())
+    b[offset:offset + len(data)] = data
+    open(dst, "wb").write(bytes(b))
+
+
+@pytest.mark.parametrize("what", ["magic", "version", "count", "dtype", "shape", "offset", "nbytes", "truncated", "empty"])
+def test_weights_file_defects(lib, good_file, tmp_path, what):
+    import struct
+    p = tmp_path / f"{what}.decw"
+    if what == "magic":
+        _corrupt(good_file, p, 0, b"XECW")
+    elif what == "version":
+        _corrupt(good_file, p, 4, struct.pack("<I", 2))
+    elif what == "count":
+        _corrupt(good_file, p, 8, struct.pack("<I", 20))
+    elif what == "dtype":
+        _corrupt(good_file, p, 72 + 40 * 3 + 4, struct.pack("<I", 2))
+    elif what == "shape":
+        _corrupt(good_file, p, 72 + 40 * 2 + 16, struct.pack("<I", 255))
+    elif what == "offset":
+        _corrupt(good_file, p, 72 + 40 * 5 + 24, struct.pack("<Q", 1 << 40))
+    elif what == "nbytes":
+        _corrupt(good_file, p, 72 + 40 * 5 + 32, struct.pack("<Q", 12))
+    elif what == "truncated":
+        b = open(good_file, "rb").read()
+        open(p, "wb").write(b[:len(b) - 1000])
+    elif what == "empty":
+        open(p, "wb").write(b"")
+    rc, _ = B.weights_file_check(p)
+    assert rc == B.DEC_ERR_WEIGHTS, what
+    assert B.last_error()
+
+
+def test_init_errors_before_any_device_work(lib, good_file, tmp_path):
+    t = synth.make_weights(TINY)
+    with pytest.raises(B.DecError) as e:
+        B.Decoder(desc(head_dim=48), tensors=t)
+    assert e.value.code == B.DEC_ERR_BAD_DESC
+    with pytest.raises(B.DecError) as e:
+        B.Decoder(desc(), tensors=t[:-1])
+    assert e.value.code == B.DEC_ERR_WEIGHTS
+    with pytest.raises(B.DecError) as e:
+        B.Decoder(desc(), path=tmp_path / "missing.decw")
+    assert e.value.code == B.DEC_ERR_WEIGHTS
+    with pytest.raises(B.DecError) as e:   # file shapes differ from the description
+        B.Decoder(desc(d_ffn=512), path=good_file)
+    assert e.value.code == B.DEC_ERR_WEIGHTS
+
+
+def test_init_without_gpu_reports_no_device(lib, good_file):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    with pytest.raises(B.DecError) as e:
+        B.Decoder(desc(), tensors=synth.make_weights(TINY))
+    assert e.value.code == B.DEC_ERR_NO_DEVICE
+    with pytest.raises(B.DecError) as e:
+        B.Decoder(desc(), path=good_file)
+    assert e.value.code == B.DEC_ERR_NO_DEVICE
+
+
+def test_null_handle_calls(lib):
+    assert lib.dec_step(None, None, None, None) == B.DEC_ERR_INVALID_ARG
+    assert lib.dec_prefill(None, None, 1, None, None) == B.DEC_ERR_INVALID_ARG
+    assert lib.dec_generate(None, 1, None) == B.DEC_ERR_INVALID_ARG
+    assert lib.dec_reset(None) == B.DEC_ERR_INVALID_ARG
+    assert lib.dec_sync(None) == B.DEC_ERR_INVALID_ARG
+    assert lib.dec_position(None) == -1
+    lib.dec_free(None)
+    assert isinstance(lib.dec_last_error(None), bytes)
+
+
+def test_library_missing_fails_loudly(monkeypatch):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/libdecmono.so")
+    with pytest.raises(B.DecLibraryMissing):
+        B.load()
