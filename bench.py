@@ -1,0 +1,196 @@
+"""Decode benchmark: tokens/s per request at batch 1 on one MI355X.
+
+Workload (default "dense2b"): a 25-layer dense decoder, d_model 2560, 20 heads
+x 128, SwiGLU 6912, vocab 65536, fp16 weights drawn N(0, 0.02) from fixed
+seeds; a 128-token random prompt is prefilled, then the timed region is the
+512 greedy decode steps at positions 128..639.  One step = one decode token
+= one pass over every active weight (the whole hot path).
+
+Prints one JSON line.  The roofline object prices the resident decode kernel
+against MI355X's 8 TB/s HBM peak with ALGORITHMIC bytes per launch: every
+weight byte once, one embedding row, the KV-cache rows attention reads at
+that position and the rows it appends.  The cpu_baseline object times the
+CPU oracle (test infrastructure) on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s per request (bs=1) and achieved HBM GB/s vs peak, 1 MI355X"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_dec_resident_dense2b.txt")
+KERNEL_SRC = os.path.join(ROOT, "memory_bound_transformer_persistent_amd", "csrc", "dec_kernels.hip")
+
+
+def kernel_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(n_launch_bytes_unit):
+    """HBM bytes per launch from the committed PMC summary, if it matches this kernel."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    rec = {}
+    for line in open(PROFILE_TRAFFIC):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("kernel_sha") != kernel_hash():
+        return None
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(shape, tensors, prompt_len, n_steps):
+    """The oracle, untouched, on a bounded sample: a short prompt then n_steps decode steps."""
+    import numpy as np
+    import oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the process's CPU count
+        threads = os.cpu_count() or 1
+    prompt = synth.make_prompt(shape.vocab, prompt_len, seed=1)[0]
+    lg, K16, V16, _ = O.prefill_matrix(shape, tensors, prompt)
+    dec = O.OracleDecoder(shape, tensors)
+    dec.load_cache(K16, V16, prompt_len)
+    tok = O.greedy(lg[-1])
+    t0 = time.perf_counter()
+    for _ in range(n_steps):
+        tok = O.greedy(dec.step(tok))
+    dt = time.perf_counter() - t0
+    return {"value": round(n_steps / dt, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_steps} greedy decode steps of the same model after a {prompt_len}-token prompt "
+                      f"(float64 NumPy oracle; prompt prefill untimed); {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="dense2b")
+    ap.add_argument("--mode", choices=["step", "generate"], default="step",
+                    help="step: one dec_step launch per token (token fed back on the device); "
+                         "generate: all timed steps inside one dec_generate launch")
+    ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--multilaunch", action="store_true", help="one kernel launch per phase (comparison)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this decode path runs on one GPU; multi-GPU runs are not part of it "
+                                   "(data-parallel serving would run one independent replica per GPU)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    from memory_bound_transformer_persistent_amd import binding as B
+    from memory_bound_transformer_persistent_amd import roofline as R
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    w = synth.workload(args.workload)
+    s = w.shape
+    if w.prompt_len + max(args.steps, args.warmup) > s.max_ctx:
+        sys.exit("prompt + steps exceed the context cap")
+    t_gen = time.time()
+    tensors = synth.workload_weights(w)
+    prompt = synth.make_prompt(s.vocab, w.prompt_len, seed=w.prompt_seed)[0]
+    print(f"# weights generated in {time.time() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.Stream(device=0)
+    flags = B.DEC_DEBUG_MULTILAUNCH if args.multilaunch else 0
+    dec = B.Decoder(B.ModelDesc.from_shape(s), tensors=tensors, device=0, stream=stream.cuda_stream,
+                    debug_flags=flags)
+
+    # warm-up: prefill + W steps, then rewind so the timed steps are the workload's positions
+    dec.prefill(prompt)
+    for _ in range(args.warmup):
+        dec.step(want_tok=False)
+    dec.sync()
+    dec.reset()
+    first_tok, _ = dec.prefill(prompt)
+    pos0 = dec.position
+
+    K = args.steps
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    if args.mode == "generate":
+        starts[0].record(stream)
+        toks = dec.generate(K)
+        ends[0].record(stream)
+    else:
+        for i in range(K):
+            starts[i].record(stream)
+            dec.step(want_tok=False)
+            ends[i].record(stream)
+    ev1.record(stream)
+    ev1.synchronize()
+    dec.sync()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    region_ms = ev0.elapsed_time(ev1)
+    if args.mode == "generate":
+        launch_ms = [starts[0].elapsed_time(ends[0])]
+        bytes_per_launch = sum(R.step_bytes(s, pos0 + i).total for i in range(K))
+    else:
+        launch_ms = [starts[i].elapsed_time(ends[i]) for i in range(K)]
+        bytes_per_launch = R.mean_step_bytes(s, pos0, K)
+    avg_launch_s = float(np.mean(launch_ms)) / 1e3
+    tok_s = K / (region_ms / 1e3)
+    achieved = bytes_per_launch / avg_launch_s / 1e9
+    peak = R.MI355X_HBM_PEAK / 1e9
+    traffic = read_traffic(bytes_per_launch)
+    roof_tps = R.roofline_tokens_per_s(s, pos0, K)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(region_ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "storage_dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.description}; prompt {w.prompt_len} + {K} greedy decode steps, batch 1",
+                   "positions": [pos0, pos0 + K - 1], "mode": args.mode,
+                   "launch": "one kernel launch per phase" if args.multilaunch else "resident kernel, grid barriers"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s",
+                     "frac": round(achieved / peak, 4),
+                     "traffic": traffic,
+                     "kernel": "dec_resident",
+                     "algorithmic_bytes_per_launch": int(bytes_per_launch),
+                     "avg_launch_ms": round(avg_launch_s * 1e3, 4)},
+        "roofline_tokens_per_s": round(roof_tps, 1),
+        "hbm_GBps_per_step": round(R.mean_step_bytes(s, pos0, K) * tok_s / 1e9, 1),
+        "wall_s": round(wall, 3),
+        "context": {"pages_8xMI300X_tokens_per_s": 3000, "pages_8xH200_tokens_per_s": 2100,
+                    "note": "2B fp16, batch 1, 8 GPUs each: other hardware, context only"},
+    }
+    dec.close()
+    if not args.no_cpu_baseline:
+        print("# running the CPU oracle baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(s, tensors, 16, args.cpu_steps)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

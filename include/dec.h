@@ -125,6 +125,8 @@ typedef struct dec_weights_src {
 #define DEC_DEBUG_MULTILAUNCH 0x1u  /* one kernel launch per phase instead of one
                                        resident kernel with grid barriers (the
                                        "one launch per op" stack, for comparison) */
+#define DEC_DEBUG_TRACE 0x2u        /* record per-phase wall-clock stamps (see
+                                       dec_read_trace) */
 
 /*
  * Init options (NULL = all defaults).
@@ -233,6 +235,17 @@ int32_t dec_position(const dec_handle* h);
  */
 int dec_read_kv(dec_handle* h, int32_t layer, int32_t seq, int32_t n_pos,
                 uint16_t* host_k, uint16_t* host_v);
+
+/*
+ * Phase trace of the most recent launch (handle created with DEC_DEBUG_TRACE).
+ * For each workgroup g the kernel stores, in order, the device wall-clock
+ * time at the start and at the end of every phase it ran: stamps
+ * [g*stride + 2j] and [g*stride + 2j + 1] for the launch's j-th phase
+ * (stamps beyond `stride` are dropped).  *out_grid and *out_stride receive
+ * the grid and the stride; *out_hz the clock rate.  host: uint64
+ * [grid*stride] or NULL to query the sizes only.  Synchronous.
+ */
+int dec_read_trace(dec_handle* h, uint64_t* host, int32_t* out_grid, int32_t* out_stride, double* out_hz);
 
 /* Release every resource of the handle (not a caller arena or stream). */
 void dec_free(dec_handle* h);

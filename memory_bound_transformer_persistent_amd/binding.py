@@ -27,6 +27,7 @@ DEC_ERR_DEVICE = -9
 DEC_ERR_TIMEOUT = -10
 DEC_ERR_UNSUPPORTED = -11
 DEC_DEBUG_MULTILAUNCH = 0x1
+DEC_DEBUG_TRACE = 0x2
 
 ERR_NAMES = {v: k for k, v in globals().items() if k.startswith("DEC_ERR_")}
 
@@ -91,6 +92,7 @@ SIGNATURES = {
     "dec_read_kv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _u16p, _u16p]),
     "dec_free": (None, [ctypes.c_void_p]),
     "dec_last_error": (ctypes.c_char_p, [ctypes.c_void_p]),
+    "dec_read_trace": (ctypes.c_int, [ctypes.c_void_p, _P(ctypes.c_uint64), _i32p, _i32p, _P(ctypes.c_double)]),
     "dec_packed_bytes": (ctypes.c_int, [_P(ModelDesc), _P(ctypes.c_size_t)]),
     "dec_pack": (ctypes.c_int, [_P(ModelDesc), _P(_u16p), ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t]),
 }
@@ -243,6 +245,14 @@ class Decoder:
 
     def reset(self):
         self._rc(self._lib.dec_reset(self._h))
+
+    def read_trace(self):
+        """(stamps [grid, stride] uint64, clock Hz) of the most recent launch."""
+        g, st, hz = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_double()
+        self._rc(self._lib.dec_read_trace(self._h, None, ctypes.byref(g), ctypes.byref(st), ctypes.byref(hz)))
+        out = np.zeros((g.value, st.value), dtype=np.uint64)
+        self._rc(self._lib.dec_read_trace(self._h, out.ctypes.data_as(_P(ctypes.c_uint64)), None, None, None))
+        return out, hz.value
 
     def read_kv(self, layer, n_pos, seq=0):
         H, hd = self.desc.n_heads, self.desc.head_dim

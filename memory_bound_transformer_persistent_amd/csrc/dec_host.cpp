@@ -65,8 +65,8 @@ int check_desc_impl(const dec_model_desc* d, std::string* err) {
   const long long big = std::max({lm_bytes, 2LL * 3 * q * d->d_model, 2LL * 2 * d->d_ffn * d->d_model});
   if (big >= (1LL << 31)) return fail(err, DEC_ERR_UNSUPPORTED, "a weight matrix is 2 GiB or larger");
   if (2LL * d->max_ctx * hd >= (1LL << 31)) return fail(err, DEC_ERR_UNSUPPORTED, "KV cache of one head is 2 GiB or larger");
-  if ((long long)d->n_heads * max_attn_chunks(d->max_ctx, d->n_heads, 1024) > 4096)
-    return fail(err, DEC_ERR_UNSUPPORTED, "too many attention partials (n_heads x chunks > 4096)");
+  if ((long long)d->n_heads * max_attn_chunks(d->max_ctx, d->n_heads, 1024) > 1024)
+    return fail(err, DEC_ERR_UNSUPPORTED, "too many attention partials (n_heads x chunks > 1024)");
   return DEC_OK;
 }
 
@@ -234,7 +234,7 @@ bool same_shape(const dec_model_desc& a, const dec_model_desc& b) {
 // device arena layout (bytes)
 // ---------------------------------------------------------------------------
 struct Arena {
-  size_t w, gains, rope, kv, x, qkv, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out, prompt, ctl, params, total;
+  size_t w, gains, rope, kv, x, qkv, attn_o, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out, prompt, ctl, params, trace, total;
 };
 
 Arena arena_layout(const dec_model_desc& d, int G) {
@@ -250,6 +250,7 @@ Arena arena_layout(const dec_model_desc& d, int G) {
   a.kv = take((size_t)d.n_layers * 2 * d.n_heads * d.max_ctx * d.head_dim * 2);
   a.x = take(D * 4);
   a.qkv = take(3 * q * 4);
+  a.attn_o = take(q * 4);
   a.part = take((size_t)d.n_heads * mc * d.head_dim * 4);
   a.pml = take((size_t)d.n_heads * mc * 2 * 4);
   a.act = take((size_t)d.d_ffn * 4);
@@ -261,6 +262,7 @@ Arena arena_layout(const dec_model_desc& d, int G) {
   a.prompt = take((size_t)d.max_ctx * 4);
   a.ctl = take(kCtlWords * 4);
   a.params = take(sizeof(Params));
+  a.trace = take((size_t)G * kTraceStride * 8);
   a.total = o;
   return a;
 }
@@ -285,6 +287,7 @@ struct dec_handle {
   int pos = 0;
   bool broken = false;     // a launch failed; only dec_reset/dec_free are allowed
   bool has_prev_tok = false;
+  double wall_hz = 1e8;
 };
 
 namespace {
@@ -607,6 +610,7 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
   P.kv = reinterpret_cast<uint16_t*>(b + h->ar.kv);
   P.x = reinterpret_cast<float*>(b + h->ar.x);
   P.qkv = reinterpret_cast<float*>(b + h->ar.qkv);
+  P.attn_o = reinterpret_cast<float*>(b + h->ar.attn_o);
   P.part = reinterpret_cast<float*>(b + h->ar.part);
   P.pml = reinterpret_cast<float*>(b + h->ar.pml);
   P.act = reinterpret_cast<float*>(b + h->ar.act);
@@ -619,6 +623,9 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
   P.ctl = reinterpret_cast<uint32_t*>(b + h->ar.ctl);
   P.max_chunks = max_attn_chunks(desc->max_ctx, desc->n_heads, h->grid);
   P.watchdog_ticks = (uint32_t)std::min(ticks, 4.0e9);
+  P.trace = (h->debug & DEC_DEBUG_TRACE) ? reinterpret_cast<uint64_t*>(b + h->ar.trace) : nullptr;
+  P.trace_stride = kTraceStride;
+  h->wall_hz = (double)wall_khz * 1000.0;
   h->dP = reinterpret_cast<Params*>(b + h->ar.params);
   e = hipMemcpy(h->dP, &P, sizeof(Params), hipMemcpyHostToDevice);
   if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemcpy(params)"); return bail(DEC_ERR_DEVICE); }
@@ -721,6 +728,18 @@ int dec_read_kv(dec_handle* h, int32_t layer, int32_t seq, int32_t n_pos, uint16
       HIPCHK(h, &h->err, hipMemcpy(dst + (size_t)hh * n_pos * d.head_dim, src, (size_t)n_pos * d.head_dim * 2, hipMemcpyDeviceToHost));
     }
   }
+  return DEC_OK;
+}
+
+int dec_read_trace(dec_handle* h, uint64_t* host, int32_t* out_grid, int32_t* out_stride, double* out_hz) {
+  if (!h) return fail(nullptr, DEC_ERR_INVALID_ARG, "handle is NULL");
+  if (out_grid) *out_grid = h->grid;
+  if (out_stride) *out_stride = kTraceStride;
+  if (out_hz) *out_hz = h->wall_hz;
+  if (!host) return DEC_OK;
+  if (!h->P.trace) return fail(&h->err, DEC_ERR_STATE, "handle was created without DEC_DEBUG_TRACE");
+  HIPCHK(h, &h->err, hipStreamSynchronize(h->stream));
+  HIPCHK(h, &h->err, hipMemcpy(host, h->P.trace, (size_t)h->grid * kTraceStride * 8, hipMemcpyDeviceToHost));
   return DEC_OK;
 }
 

@@ -18,19 +18,22 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kGroups = 8;                  // barrier groups: workgroup b is in group b % 8
 constexpr int kMaxK = 8192;                 // longest GEMV row supported (16 pieces per lane)
 constexpr int kChunkMin = 32;               // shortest attention chunk (positions)
-constexpr int kChunkMax = 2048;             // longest attention chunk (scores kept in LDS)
-constexpr int kLdsBytes = 100 * 1024;       // dynamic LDS per workgroup; > half a CU's 160 KB,
+constexpr int kChunkMax = 2048;
+constexpr int kTraceStride = 4096;          // trace stamps kept per workgroup per launch             // longest attention chunk (scores kept in LDS)
+constexpr int kLdsBytes = 144 * 1024;       // dynamic LDS per workgroup; > half a CU's 160 KB,
                                             // so exactly one workgroup runs per compute unit
 
 // Control words (uint32 index into Params::ctl); each on its own 256-byte line.
 constexpr int kCtlGlobal = 0;               // arrivals of group leaders (cumulative)
 constexpr int kCtlGroup0 = 64;              // group k counter at kCtlGroup0 + 64*k
 constexpr int kCtlErr = 64 * (1 + kGroups); // first error code raised by any workgroup
-constexpr int kCtlWords = 64 * (2 + kGroups);
+constexpr int kCtlHead0 = 64 * (2 + kGroups);  // per-head arrival counters of attention chunks
+constexpr int kMaxHeads = 1024;
+constexpr int kCtlWords = kCtlHead0 + kMaxHeads;
 
 // Phases of one token.  Per layer: QKV, ATTN, O, GU, DOWN; then LM and ARGMAX
 // when the token's logits are wanted.
-enum Phase : int { PH_QKV = 0, PH_ATTN = 1, PH_O = 2, PH_GU = 3, PH_DOWN = 4 };
+enum Phase : int { PH_QKV = 0, PH_ATTN = 1, PH_O = 2, PH_GU = 3, PH_DOWN = 4, PH_LM = 5 };
 constexpr int kPhasesPerLayer = 5;
 
 enum TokSrc : int { TOK_PROMPT = 0, TOK_DEVICE = 1 };
@@ -50,6 +53,7 @@ struct Params {
   uint16_t* kv;               // [L][2][H][max_ctx][hd] fp16
   float* x;                   // residual stream [d]
   float* qkv;                 // [3q]
+  float* attn_o;              // merged attention output [q]
   float* part;                // attention partial sums [H][max_chunks][hd]
   float* pml;                 // attention partial (max, sum) [H][max_chunks][2]
   float* act;                 // SwiGLU output [F]
@@ -62,6 +66,8 @@ struct Params {
   uint32_t* ctl;              // control words
   int max_chunks;
   uint32_t watchdog_ticks;    // bound on one barrier wait, in wall-clock ticks
+  uint64_t* trace;            // optional [G][trace_stride] wall-clock stamps (phase start, phase end, ...)
+  int trace_stride;
 };
 
 struct Launch {

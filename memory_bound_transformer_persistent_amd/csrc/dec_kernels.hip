@@ -39,6 +39,16 @@ constexpr int kAuxSc1 = 0x10;  // coherent at device (agent) scope
 constexpr uint32_t kOOB = 0xFFFFFF00u;  // buffer offset past any region: loads read 0
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS map (floats): xs [kMaxK] | red [64] | si [16 ints] | aux [kAuxFloats] | pf [kWaves][kPfFloats]
+constexpr int kPfBlocks = 12;                // 1 KB blocks of weights prefetched per wave
+constexpr int kPfFloats = kPfBlocks * 256;
+constexpr int kAuxFloats = 3072;
+constexpr int kLdsRed = kMaxK, kLdsSi = kMaxK + 64, kLdsAux = kMaxK + 80, kLdsPf = kMaxK + 80 + kAuxFloats;
+static_assert((kLdsPf + kWaves * kPfFloats) * 4 <= kLdsBytes, "LDS map exceeds the allocation");
+static_assert(kLdsPf % 4 == 0, "prefetch buffer must be 16-byte aligned");
+constexpr int kWaitVm0 = 0x0F70;             // s_waitcnt vmcnt(0), expcnt/lgkmcnt untouched
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
@@ -48,6 +58,15 @@ __device__ __forceinline__ u32x4 ld_nt(rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ u32x4 ld_kv(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxNt | kAuxSc1);
+}
+// 16 bytes per lane from a buffer straight into LDS at lds_base + 16*lane (wave-uniform base).
+__device__ __forceinline__ void dma16(rsrc_t r, float* lds_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, off, 0, 0, kAuxNt);
+}
+__device__ __forceinline__ void wait_vm0() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 __device__ __forceinline__ f32x4 ld_coh4(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxSc1));
@@ -134,133 +153,272 @@ __device__ __forceinline__ void split(int n, int g, int G, int& b, int& e) {
 __device__ __forceinline__ int round512(int n) { return (n + 511) & ~511; }
 
 // ---------------------------------------------------------------------------
-// grid barrier
+// weight prefetch into LDS
 // ---------------------------------------------------------------------------
-// epoch: cumulative barrier number (1-based, wrapping).  Returns false when the
-// launch must stop (watchdog expired here or an error was raised elsewhere).
-__device__ __noinline__ bool grid_barrier(const Params* __restrict__ Pp, uint32_t epoch, int fenced, int* s_flag) {
-  const Params& P = *Pp;
-  // This wave's coherent stores must have completed before the workgroup arrives.
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+// A GEMV phase's work for one workgroup: row pairs [p0, p1) of W[rows, K].
+// Wave w consumes pairs p0+w, p0+w+8, ... as a stream of 1 KB blocks, block
+// b = (2*j + r)*NP + k for its j-th pair, row r of the pair, piece-column k.
+struct GemvWork {
+  const uint16_t* W;
+  int rows, K, p0, p1;
+};
+
+// A row pair is streamed in nch column chunks of np pieces per lane (np <= 8,
+// nch*np*512 >= K), so no more than 8 16-byte pieces per row sit in registers.
+__device__ __forceinline__ void gemv_shape(int K, int& np, int& nch) {
+  const int pieces = (K + 511) >> 9;          // 16-byte pieces per lane per row
+  nch = (pieces + 7) >> 3;
+  np = (pieces + nch - 1) / nch;
+}
+// LDS floats of the input vector a GEMV with row length K reads (zero-padded past K).
+__device__ __forceinline__ int gemv_span(int K) {
+  int np, nch;
+  gemv_shape(K, np, nch);
+  return 512 * np * nch;
+}
+
+// Waves [w_first, 8) copy the first kPfBlocks blocks of every wave's stream
+// into pf + w*kPfFloats with LDS-direct buffer loads (pieces past K read 0).
+// Block b of wave w's stream is unit u = b / (2*np) (pair u / nch, column
+// chunk u % nch), row (b / np) & 1 of the pair, piece b % np.  Whoever reads
+// the blocks first waits for the issuing waves (vmcnt) and a workgroup sync.
+__device__ __forceinline__ void prefetch_issue(const GemvWork& g, float* pf, int w_first) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave < w_first || g.W == nullptr) return;
+  const int nis = kWaves - w_first;
+  int np, nch;
+  gemv_shape(g.K, np, nch);
+  const uint32_t row_bytes = (uint32_t)g.K * 2u;
+  const rsrc_t r = make_rsrc(g.W, (uint32_t)g.rows * row_bytes);
+  const int P16 = g.K >> 3;
+  for (int f = wave - w_first; f < kWaves * kPfBlocks; f += nis) {
+    const int tw = f / kPfBlocks, b = f % kPfBlocks;
+    const int u = b / (2 * np), rr = (b / np) & 1, kk = b % np;
+    const int pr = g.p0 + tw + kWaves * (u / nch);
+    if (pr >= g.p1) continue;
+    const int c = lane + 64 * ((u % nch) * np + kk);
+    const uint32_t off = c < P16 ? (uint32_t)(2 * pr + rr) * row_bytes + 16u * c : kOOB;
+    dma16(r, pf + tw * kPfFloats + b * 256, off);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// grid barrier, split in two halves
+// ---------------------------------------------------------------------------
+// Arrive: waves [0, n_store) wait for their coherent stores to complete
+// (vmcnt: waves that only have prefetch loads in flight skip it), the
+// workgroup syncs, and thread 0 adds one to its group's counter (group =
+// blockIdx % 8).  Wait (wave 0): lanes 0..7 poll the eight group counters
+// until each holds group_size * epoch, so a workgroup is released one
+// atomic hop after the last arrival.  epoch is the cumulative barrier number
+// (1-based, wrapping).  The wait returns false if the watchdog expires here
+// or any workgroup raised an error.
+__device__ __forceinline__ void barrier_arrive(const Params& P, uint32_t epoch, int fenced, int n_store) {
+  if ((int)(threadIdx.x >> 6) < n_store) wait_vm0();
   __syncthreads();
   if (threadIdx.x == 0) {
     if (fenced) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint32_t G = gridDim.x;
-    const uint32_t grp = blockIdx.x % kGroups;
-    const uint32_t ngroups = G < (uint32_t)kGroups ? G : (uint32_t)kGroups;
-    const uint32_t gsize = (G - grp + kGroups - 1) / kGroups;
-    uint32_t* gcnt = P.ctl + kCtlGroup0 + 64 * grp;
-    const uint32_t old = __hip_atomic_fetch_add(gcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == gsize * epoch - 1u)
-      __hip_atomic_fetch_add(P.ctl + kCtlGlobal, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t target = ngroups * epoch;
-    int ok = 1;
-    const uint64_t t0 = wall_clock64();
-    while ((int)(ld_coh(P.ctl + kCtlGlobal) - target) < 0) {
-      if (ld_coh(P.ctl + kCtlErr) != 0u) { ok = 0; break; }
-      if (wall_clock64() - t0 > (uint64_t)P.watchdog_ticks) {
+    __hip_atomic_fetch_add(P.ctl + kCtlGroup0 + 64 * (blockIdx.x % kGroups), 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__device__ __forceinline__ bool barrier_wait(const Params& P, uint32_t epoch, int fenced) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t G = gridDim.x;
+  const int ng = G < (uint32_t)kGroups ? (int)G : kGroups;
+  uint32_t target = 0;
+  const uint32_t* cnt = P.ctl + kCtlGroup0 + 64 * (lane < ng ? lane : 0);
+  if (lane < ng) target = ((G - (uint32_t)lane + kGroups - 1) / kGroups) * epoch;
+  const uint64_t t0 = wall_clock64();
+  bool ok = true;
+  while (true) {
+    const bool done = lane >= ng || (int)(ld_coh(cnt) - target) >= 0;
+    if (__all(done)) break;
+    if (ld_coh(P.ctl + kCtlErr) != 0u) { ok = false; break; }
+    if (wall_clock64() - t0 > (uint64_t)P.watchdog_ticks) {
+      if (lane == 0) {
         uint32_t expected = 0u;
         __hip_atomic_compare_exchange_strong(P.ctl + kCtlErr, &expected, (uint32_t)kDevErrTimeout,
                                              __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ok = 0;
-        break;
       }
+      ok = false;
+      break;
     }
-    if (fenced) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    *s_flag = ok;
   }
-  __syncthreads();
-  return *s_flag != 0;
+  if (fenced) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return ok;
 }
 
 // ---------------------------------------------------------------------------
-// GEMV: y = W x over row pairs [p0, p1) of a row-major fp16 matrix W[rows, K].
-// Wave w takes pairs p0+w, p0+w+8, ...; lane l reads 16-byte pieces l, l+64, ...
-// of both rows (NP pieces per lane cover K <= 512*NP).  xs: fp32 x in LDS,
-// zero-padded to 512*NP.  epi(pair, y0, y1, lane) sees the reduced sums.
+// GEMV: y = W x over the row pairs of a GemvWork.  A wave's work is a stream of
+// units (pair, column chunk); lane l reads 16-byte pieces l, l+64, ... of both
+// rows of the unit, and the first kPfBlocks 1 KB blocks of the stream come from
+// the LDS prefetch when pf is set.  While one unit is multiplied the next
+// unit's loads are in flight.  xs: fp32 x in LDS, zero-padded to
+// gemv_span(K).  epi(pair, y0, y1, lane) sees the wave-reduced sums.
 // ---------------------------------------------------------------------------
-template <int NP, class Epi>
-__device__ __forceinline__ void gemv_pairs(const uint16_t* W, int rows, int K, int p0, int p1,
-                                           const float* xs, Epi& epi) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t row_bytes = (uint32_t)K * 2u;
-  const rsrc_t r = make_rsrc(W, (uint32_t)rows * row_bytes);
-  const int P16 = K >> 3;
-  for (int pr = p0 + wave; pr < p1; pr += kWaves) {
-    const uint32_t b0 = (uint32_t)(2 * pr) * row_bytes;
-    u32x4 w0[NP], w1[NP];
+template <int NP>
+__device__ __forceinline__ void gemv_fetch(rsrc_t r, uint32_t row_bytes, int P16, int pr, int u, int ch,
+                                           const float* pfw, int lane, u32x4 (&w0)[NP], u32x4 (&w1)[NP]) {
+  const uint32_t b0 = (uint32_t)(2 * pr) * row_bytes;
 #pragma unroll
-    for (int k = 0; k < NP; ++k) {
-      const int c = lane + 64 * k;
-      const bool in = c < P16;
+  for (int k = 0; k < NP; ++k) {
+    const int c = lane + 64 * (ch * NP + k);
+    const bool in = c < P16;
+    const int blk0 = (2 * u) * NP + k, blk1 = (2 * u + 1) * NP + k;
+    if (pfw != nullptr && blk0 < kPfBlocks)
+      w0[k] = *reinterpret_cast<const u32x4*>(pfw + blk0 * 256 + lane * 4);
+    else
       w0[k] = ld_nt(r, in ? b0 + 16u * c : kOOB);
+    if (pfw != nullptr && blk1 < kPfBlocks)
+      w1[k] = *reinterpret_cast<const u32x4*>(pfw + blk1 * 256 + lane * 4);
+    else
       w1[k] = ld_nt(r, in ? b0 + row_bytes + 16u * c : kOOB);
-    }
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int k = 0; k < NP; ++k) {
-      const f32x4* xp = reinterpret_cast<const f32x4*>(xs + 8 * (lane + 64 * k));
-      const f32x4 xa = xp[0], xb = xp[1];
-      a0 = dot8(w0[k], xa, xb, a0);
-      a1 = dot8(w1[k], xa, xb, a1);
-    }
-    a0 = wave_sum(a0);
-    a1 = wave_sum(a1);
-    epi(pr, a0, a1, lane);
   }
 }
 
-// Pieces per lane of the instantiation gemv() uses for row length K.
-__device__ __forceinline__ int gemv_np(int K) {
-  const int np = (K + 511) >> 9;
-  if (np <= 6) return np < 1 ? 1 : np;
-  if (np <= 8) return 8;
-  if (np <= 10) return 10;
-  if (np <= 12) return 12;
-  if (np <= 14) return 14;
-  return 16;
+template <int NP>
+__device__ __forceinline__ void gemv_accum(const u32x4 (&w0)[NP], const u32x4 (&w1)[NP], const float* xs, int lane,
+                                           int ch, float& a0, float& a1) {
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const f32x4* xp = reinterpret_cast<const f32x4*>(xs + 8 * (lane + 64 * (ch * NP + k)));
+    const f32x4 xa = xp[0], xb = xp[1];
+    a0 = dot8(w0[k], xa, xb, a0);
+    a1 = dot8(w1[k], xa, xb, a1);
+  }
 }
-// LDS floats of the input vector a GEMV with row length K reads (zero-padded past K).
-__device__ __forceinline__ int gemv_span(int K) { return 512 * gemv_np(K); }
+
+template <int NP, class Epi>
+__device__ __forceinline__ void gemv_stream(const GemvWork& g, int nch, const float* xs, const float* pf, Epi& epi) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t row_bytes = (uint32_t)g.K * 2u;
+  const rsrc_t r = make_rsrc(g.W, (uint32_t)g.rows * row_bytes);
+  const int P16 = g.K >> 3;
+  const float* pfw = pf ? pf + wave * kPfFloats : nullptr;
+  const int npairs = g.p1 - g.p0 - wave > 0 ? (g.p1 - g.p0 - wave + kWaves - 1) / kWaves : 0;
+  const int nunits = npairs * nch;
+  if (nunits == 0) return;
+  float a0 = 0.f, a1 = 0.f;
+  u32x4 x0[NP], x1[NP], y0[NP], y1[NP];
+  auto pair_of = [&](int u) { return g.p0 + wave + kWaves * (u / nch); };
+  gemv_fetch<NP>(r, row_bytes, P16, pair_of(0), 0, 0, pfw, lane, x0, x1);
+  auto finish = [&](int u) {
+    if (u % nch == nch - 1) {
+      const float s0 = wave_sum(a0), s1 = wave_sum(a1);
+      epi(pair_of(u), s0, s1, lane);
+      a0 = 0.f;
+      a1 = 0.f;
+    }
+  };
+  for (int u = 0; u < nunits; u += 2) {
+    if (u + 1 < nunits) gemv_fetch<NP>(r, row_bytes, P16, pair_of(u + 1), u + 1, (u + 1) % nch, pfw, lane, y0, y1);
+    gemv_accum<NP>(x0, x1, xs, lane, u % nch, a0, a1);
+    finish(u);
+    if (u + 1 >= nunits) break;
+    if (u + 2 < nunits) gemv_fetch<NP>(r, row_bytes, P16, pair_of(u + 2), u + 2, (u + 2) % nch, pfw, lane, x0, x1);
+    gemv_accum<NP>(y0, y1, xs, lane, (u + 1) % nch, a0, a1);
+    finish(u + 1);
+  }
+}
 
 template <class Epi>
-__device__ void gemv(const uint16_t* W, int rows, int K, int p0, int p1, const float* xs, Epi& epi) {
-  const int np = gemv_np(K);
-  if (np <= 1) gemv_pairs<1>(W, rows, K, p0, p1, xs, epi);
-  else if (np <= 2) gemv_pairs<2>(W, rows, K, p0, p1, xs, epi);
-  else if (np <= 3) gemv_pairs<3>(W, rows, K, p0, p1, xs, epi);
-  else if (np <= 4) gemv_pairs<4>(W, rows, K, p0, p1, xs, epi);
-  else if (np <= 5) gemv_pairs<5>(W, rows, K, p0, p1, xs, epi);
-  else if (np <= 6) gemv_pairs<6>(W, rows, K, p0, p1, xs, epi);
-  else if (np <= 8) gemv_pairs<8>(W, rows, K, p0, p1, xs, epi);
-  else if (np <= 10) gemv_pairs<10>(W, rows, K, p0, p1, xs, epi);
-  else if (np <= 12) gemv_pairs<12>(W, rows, K, p0, p1, xs, epi);
-  else if (np <= 14) gemv_pairs<14>(W, rows, K, p0, p1, xs, epi);
-  else gemv_pairs<16>(W, rows, K, p0, p1, xs, epi);
+__device__ __forceinline__ void gemv(const GemvWork& g, const float* xs, const float* pf, Epi& epi) {
+  int np, nch;
+  gemv_shape(g.K, np, nch);
+  switch (np) {
+    case 1: gemv_stream<1>(g, nch, xs, pf, epi); break;
+    case 2: gemv_stream<2>(g, nch, xs, pf, epi); break;
+    case 3: gemv_stream<3>(g, nch, xs, pf, epi); break;
+    case 4: gemv_stream<4>(g, nch, xs, pf, epi); break;
+    case 5: gemv_stream<5>(g, nch, xs, pf, epi); break;
+    case 6: gemv_stream<6>(g, nch, xs, pf, epi); break;
+    case 7: gemv_stream<7>(g, nch, xs, pf, epi); break;
+    default: gemv_stream<8>(g, nch, xs, pf, epi); break;
+  }
+}
+
+// The GEMV work of each phase for this workgroup (pairs split evenly).
+__device__ __forceinline__ GemvWork work_of(const Params& P, int ph, int l) {
+  GemvWork g{nullptr, 0, 0, 0, 0};
+  int npairs = 0;
+  const uint16_t* lay = P.w + (size_t)l * P.layer_stride;
+  switch (ph) {
+    case PH_QKV: g.W = lay + P.off_qkv; g.rows = 3 * P.q; g.K = P.d; npairs = 3 * P.q / 2; break;
+    case PH_O: g.W = lay + P.off_o; g.rows = P.d; g.K = P.q; npairs = P.d / 2; break;
+    case PH_GU: g.W = lay + P.off_gu; g.rows = 2 * P.F; g.K = P.d; npairs = P.F; break;
+    case PH_DOWN: g.W = lay + P.off_d; g.rows = P.d; g.K = P.F; npairs = P.d / 2; break;
+    case PH_LM: g.W = P.w + P.off_lm; g.rows = P.Vlm; g.K = P.d; npairs = P.Vlm / 2; break;
+    default: return g;
+  }
+  split(npairs, blockIdx.x, gridDim.x, g.p0, g.p1);
+  return g;
 }
 
 // ---------------------------------------------------------------------------
-// prologues
+// prologues: run by wave 0 alone while the other waves' prefetch lands
 // ---------------------------------------------------------------------------
-// xs[0..gemv_span(n)) <- coherent copy of src[0..n), zero beyond n.  n % 4 == 0.
-__device__ __forceinline__ void load_vec(float* xs, const float* src, int n) {
+constexpr int kVecBatch = 16;   // 16-byte loads per lane in flight in a prologue
+
+// xs[0..gemv_span(n)) <- src[0..n) (coherent loads), zero past n; with g set,
+// the RMSNorm of src times g: src / sqrt(mean(src^2) + eps) * g.
+__device__ __forceinline__ void w0_load_vec(float* xs, const float* src, int n, const float* g, float eps) {
+  const int lane = threadIdx.x & 63;
   const rsrc_t r = make_rsrc(src, (uint32_t)n * 4u);
-  const int npad = gemv_span(n);
-  for (int i = threadIdx.x * 4; i < npad; i += kThreads * 4)
-    *reinterpret_cast<f32x4*>(xs + i) = ld_coh4(r, i < n ? (uint32_t)i * 4u : kOOB);
+  const int span = gemv_span(n);
+  float ss = 0.f;
+  for (int i0 = 0; i0 < span; i0 += 256 * kVecBatch) {
+    f32x4 v[kVecBatch], gv[kVecBatch];
+#pragma unroll
+    for (int t = 0; t < kVecBatch; ++t) {
+      const int i = i0 + 256 * t + 4 * lane;
+      v[t] = ld_coh4(r, i < n ? (uint32_t)i * 4u : kOOB);
+      if (g != nullptr) gv[t] = (i < n) ? *reinterpret_cast<const f32x4*>(g + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int t = 0; t < kVecBatch; ++t) {
+      const int i = i0 + 256 * t + 4 * lane;
+      if (i < span) {
+        ss += v[t][0] * v[t][0] + v[t][1] * v[t][1] + v[t][2] * v[t][2] + v[t][3] * v[t][3];
+        *reinterpret_cast<f32x4*>(xs + i) = g != nullptr ? v[t] * gv[t] : v[t];
+      }
+    }
+  }
+  if (g != nullptr) {
+    const float s = 1.0f / sqrtf(wave_sum(ss) / (float)n + eps);
+    for (int i = 4 * lane; i < n; i += 256) *reinterpret_cast<f32x4*>(xs + i) *= s;
+  }
 }
 
-// RMSNorm in place: xs[i] = xs[i] / sqrt(mean(xs^2) + eps) * g[i] for i < n.
-__device__ __forceinline__ void rmsnorm_lds(float* xs, int n, const float* g, float eps, float* red) {
-  __syncthreads();
+// Layer-0 input: x = E[tok] (fp16 -> fp32); this workgroup stores its own rows
+// of x, and xs gets rmsnorm(x) * g.
+__device__ __forceinline__ void w0_embed(const Params& P, int tok, float* xs, const float* g) {
+  const int lane = threadIdx.x & 63, d = P.d;
+  const _Float16* e = reinterpret_cast<const _Float16*>(P.w + P.off_E + (size_t)tok * d);
+  int b, en;
+  split(d / 2, blockIdx.x, gridDim.x, b, en);
+  const int span = gemv_span(d);
   float ss = 0.f;
-  for (int i = threadIdx.x; i < n; i += kThreads) ss += xs[i] * xs[i];
-  ss = block_sum(ss, red);
-  const float s = 1.0f / sqrtf(ss / (float)n + eps);
-  for (int i = threadIdx.x; i < n; i += kThreads) xs[i] = xs[i] * s * g[i];
-  __syncthreads();
+  for (int i = 8 * lane; i < span; i += 512) {
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+    if (i < d) {
+      const f16x8 h = *reinterpret_cast<const f16x8*>(e + i);
+      lo = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+      hi = f32x4{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
+      for (int q = 0; q < 8; ++q)
+        if (i + q >= 2 * b && i + q < 2 * en) st_coh(P.x + i + q, q < 4 ? lo[q] : hi[q - 4]);
+      const f32x4 ga = *reinterpret_cast<const f32x4*>(g + i), gb = *reinterpret_cast<const f32x4*>(g + i + 4);
+      ss += lo[0] * lo[0] + lo[1] * lo[1] + lo[2] * lo[2] + lo[3] * lo[3] +
+            hi[0] * hi[0] + hi[1] * hi[1] + hi[2] * hi[2] + hi[3] * hi[3];
+      lo *= ga;
+      hi *= gb;
+    }
+    *reinterpret_cast<f32x4*>(xs + i) = lo;
+    *reinterpret_cast<f32x4*>(xs + i + 4) = hi;
+  }
+  const float s = 1.0f / sqrtf(wave_sum(ss) / (float)d + P.eps);
+  for (int i = 4 * lane; i < d; i += 256) *reinterpret_cast<f32x4*>(xs + i) *= s;
 }
 
 // ---------------------------------------------------------------------------
@@ -270,54 +428,36 @@ struct Lds {
   float* xs;    // GEMV input vector, kMaxK floats
   float* red;   // 64 floats
   int* si;      // 16 ints
-  float* aux;   // attention / merge scratch
+  float* aux;   // attention / argmax scratch, kAuxFloats
+  float* pf;    // weight prefetch, kWaves x kPfFloats
 };
 
-__device__ __noinline__ void phase_qkv(const Params* __restrict__ Pp, int l, int tok, bool first_layer, const Lds& S) {
-  const Params& P = *Pp;
-  const int d = P.d;
-  if (first_layer) {
-    // x = E[tok]: every workgroup converts the row; each owns rows of x to store.
-    const uint16_t* e = P.w + P.off_E + (size_t)tok * d;
-    const _Float16* eh = reinterpret_cast<const _Float16*>(e);
-    for (int i = threadIdx.x; i < gemv_span(d); i += kThreads) S.xs[i] = i < d ? (float)eh[i] : 0.f;
-    __syncthreads();
-    int b, e_;
-    split(d / 2, blockIdx.x, gridDim.x, b, e_);
-    for (int r = 2 * b + threadIdx.x; r < 2 * e_; r += kThreads) st_coh(P.x + r, S.xs[r]);
-  } else {
-    load_vec(S.xs, P.x, d);
-  }
-  rmsnorm_lds(S.xs, d, P.gains + (size_t)l * 2 * d, P.eps, S.red);
-  int b, e;
-  split(3 * P.q / 2, blockIdx.x, gridDim.x, b, e);
-  float* out = P.qkv;
-  auto epi = [out](int pr, float y0, float y1, int lane) {
-    if (lane == 0) { st_coh(out + 2 * pr, y0); st_coh(out + 2 * pr + 1, y1); }
-  };
-  gemv(P.w + (size_t)l * P.layer_stride + P.off_qkv, 3 * P.q, d, b, e, S.xs, epi);
-}
-
 // Single-query attention of every head over positions 0..pos, split into
-// chunks of positions; each (head, chunk) unit writes an unnormalised partial
-// (running max m, sum of exp l, sum of exp * V) that the O phase merges.
-template <int HD>
-__device__ __noinline__ void phase_attn(const Params* __restrict__ Pp, int l, int pos, const Lds& S) {
-  const Params& P = *Pp;
+// chunks of positions.  AW waves compute; a thread holds K and V of NPASS
+// positions in registers (their loads are issued before the query is read),
+// so a unit costs one memory round trip per group of GRP positions, with an
+// online softmax across groups.  With more than one chunk per head each unit
+// stores an unnormalised partial (max m, sum of exp l, sum of exp * V) and
+// the last unit of a head to finish (per-head counter) merges them; the head's
+// output o goes to P.attn_o.
+template <int HD, int AW>
+__device__ __forceinline__ void phase_attn(const Params& P, int l, int pos, const Lds& S) {
   constexpr int LP = HD / 8;             // lanes per position (16 B of K or V each)
   constexpr int PPW = 64 / LP;           // positions per wave per pass
-  constexpr int PPB = PPW * kWaves;      // positions per workgroup per pass
-  constexpr int NPG = kThreads / LP;     // position groups in the V pass
+  constexpr int PPB = PPW * AW;          // positions per workgroup per pass
+  constexpr int NPASS = 4;
+  constexpr int GRP = PPB * NPASS;       // positions per register group
   float* qs = S.aux;                     // [HD] rotated, scaled query
   float* kn = qs + HD;                   // [HD] new key (fp16-rounded)
   float* vn = kn + HD;                   // [HD] new value (fp16-rounded)
-  float* stat = vn + HD;                 // [4]
-  float* sc = stat + 4;                  // [kChunkMax] scores, then exp weights
-  float* red = sc + kChunkMax;           // [NPG * HD]
+  float* wred = vn + HD;                 // [2 * kWaves]
+  float* ored = wred + 2 * kWaves;       // [AW * HD]
   const int ctx = pos + 1, H = P.H, G = gridDim.x;
   const int C = attn_chunks(ctx, H, G);
   const int CH = (ctx + C - 1) / C;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool cw = wave < AW;
+  const int sub = lane % LP, pidx = lane / LP;
   const float scale = 1.0f / sqrtf((float)HD);
   const size_t head_elems = (size_t)P.max_ctx * HD;
   for (int u = blockIdx.x; u < H * C; u += G) {
@@ -327,195 +467,174 @@ __device__ __noinline__ void phase_attn(const Params* __restrict__ Pp, int l, in
     const bool has_new = j0 < ctx && j1 == ctx;
     uint16_t* kc = P.kv + ((size_t)(l * 2 + 0) * H + h) * head_elems;
     uint16_t* vc = P.kv + ((size_t)(l * 2 + 1) * H + h) * head_elems;
-    if (threadIdx.x < HD / 2) {
-      const int i = threadIdx.x;
-      const float cs = P.rope[((size_t)pos * (HD / 2) + i) * 2];
-      const float sn = P.rope[((size_t)pos * (HD / 2) + i) * 2 + 1];
-      const float* qh = P.qkv + h * HD;
-      const float q0 = ld_coh(qh + 2 * i), q1 = ld_coh(qh + 2 * i + 1);
-      qs[2 * i] = (q0 * cs - q1 * sn) * scale;
-      qs[2 * i + 1] = (q0 * sn + q1 * cs) * scale;
-      if (has_new) {
-        const float* kh = P.qkv + P.q + h * HD;
-        const float* vh = P.qkv + 2 * P.q + h * HD;
-        const float k0 = ld_coh(kh + 2 * i), k1 = ld_coh(kh + 2 * i + 1);
-        const _Float16 kr0 = (_Float16)(k0 * cs - k1 * sn), kr1 = (_Float16)(k0 * sn + k1 * cs);
-        const _Float16 vr0 = (_Float16)ld_coh(vh + 2 * i), vr1 = (_Float16)ld_coh(vh + 2 * i + 1);
-        kn[2 * i] = (float)kr0; kn[2 * i + 1] = (float)kr1;
-        vn[2 * i] = (float)vr0; vn[2 * i + 1] = (float)vr1;
-        const uint32_t kb = (uint32_t)__builtin_bit_cast(uint16_t, kr0) | ((uint32_t)__builtin_bit_cast(uint16_t, kr1) << 16);
-        const uint32_t vb = (uint32_t)__builtin_bit_cast(uint16_t, vr0) | ((uint32_t)__builtin_bit_cast(uint16_t, vr1) << 16);
-        st_coh(reinterpret_cast<uint32_t*>(kc + (size_t)pos * HD + 2 * i), kb);
-        st_coh(reinterpret_cast<uint32_t*>(vc + (size_t)pos * HD + 2 * i), vb);
-      }
-    }
-    __syncthreads();
     const rsrc_t rk = make_rsrc(kc, (uint32_t)(head_elems * 2));
     const rsrc_t rv = make_rsrc(vc, (uint32_t)(head_elems * 2));
-    // scores s_j = q . K_j (q already carries 1/sqrt(hd))
-    {
-      const int sub = lane % LP, pidx = lane / LP;
-      const f32x4 qa = *reinterpret_cast<const f32x4*>(qs + 8 * sub);
-      const f32x4 qb = *reinterpret_cast<const f32x4*>(qs + 8 * sub + 4);
-#pragma unroll 4
-      for (int jb = j0 + wave * PPW; jb < j1; jb += PPB) {
-        const int j = jb + pidx;
-        float s = 0.f;
-        if (j < j1) {
+    float M = -INFINITY, Lsum = 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int g0 = j0; g0 < j1; g0 += GRP) {
+      u32x4 kr[NPASS], vr[NPASS];
+      if (cw) {
+#pragma unroll
+        for (int t = 0; t < NPASS; ++t) {
+          const int j = g0 + t * PPB + wave * PPW + pidx;
+          const uint32_t off = (j < j1 && j != pos) ? (uint32_t)(j * HD + 8 * sub) * 2u : kOOB;
+          kr[t] = ld_kv(rk, off);
+          vr[t] = ld_kv(rv, off);
+        }
+      }
+      if (g0 == j0) {
+        if (threadIdx.x < HD / 2) {
+          const int i = threadIdx.x;
+          const float cs = P.rope[((size_t)pos * (HD / 2) + i) * 2];
+          const float sn = P.rope[((size_t)pos * (HD / 2) + i) * 2 + 1];
+          const float* qh = P.qkv + h * HD;
+          const float q0 = ld_coh(qh + 2 * i), q1 = ld_coh(qh + 2 * i + 1);
+          qs[2 * i] = (q0 * cs - q1 * sn) * scale;
+          qs[2 * i + 1] = (q0 * sn + q1 * cs) * scale;
+          if (has_new) {
+            const float* kh = P.qkv + P.q + h * HD;
+            const float* vh = P.qkv + 2 * P.q + h * HD;
+            const float k0 = ld_coh(kh + 2 * i), k1 = ld_coh(kh + 2 * i + 1);
+            const _Float16 kr0 = (_Float16)(k0 * cs - k1 * sn), kr1 = (_Float16)(k0 * sn + k1 * cs);
+            const _Float16 vr0 = (_Float16)ld_coh(vh + 2 * i), vr1 = (_Float16)ld_coh(vh + 2 * i + 1);
+            kn[2 * i] = (float)kr0; kn[2 * i + 1] = (float)kr1;
+            vn[2 * i] = (float)vr0; vn[2 * i + 1] = (float)vr1;
+            const uint32_t kb = (uint32_t)__builtin_bit_cast(uint16_t, kr0) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, kr1) << 16);
+            const uint32_t vb = (uint32_t)__builtin_bit_cast(uint16_t, vr0) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, vr1) << 16);
+            st_coh(reinterpret_cast<uint32_t*>(kc + (size_t)pos * HD + 2 * i), kb);
+            st_coh(reinterpret_cast<uint32_t*>(vc + (size_t)pos * HD + 2 * i), vb);
+          }
+        }
+        __syncthreads();
+      }
+      float s[NPASS];
+      if (cw) {
+        const f32x4 qa = *reinterpret_cast<const f32x4*>(qs + 8 * sub);
+        const f32x4 qb = *reinterpret_cast<const f32x4*>(qs + 8 * sub + 4);
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < NPASS; ++t) {
+          const int j = g0 + t * PPB + wave * PPW + pidx;
+          float dsum;
           if (j == pos) {
             const f32x4 ka = *reinterpret_cast<const f32x4*>(kn + 8 * sub);
             const f32x4 kb = *reinterpret_cast<const f32x4*>(kn + 8 * sub + 4);
-            s = ka[0] * qa[0] + ka[1] * qa[1] + ka[2] * qa[2] + ka[3] * qa[3] +
-                kb[0] * qb[0] + kb[1] * qb[1] + kb[2] * qb[2] + kb[3] * qb[3];
+            dsum = ka[0] * qa[0] + ka[1] * qa[1] + ka[2] * qa[2] + ka[3] * qa[3] +
+                   kb[0] * qb[0] + kb[1] * qb[1] + kb[2] * qb[2] + kb[3] * qb[3];
           } else {
-            s = dot8(ld_kv(rk, (uint32_t)(j * HD + 8 * sub) * 2u), qa, qb, 0.f);
+            dsum = dot8(kr[t], qa, qb, 0.f);
+          }
+          dsum = group_sum<LP>(dsum);
+          s[t] = j < j1 ? dsum : -INFINITY;
+          mloc = fmaxf(mloc, s[t]);
+        }
+        mloc = wave_max(mloc);
+        if (lane == 0) wred[wave] = mloc;
+      }
+      __syncthreads();
+      float mg = wred[0];
+#pragma unroll
+      for (int w = 1; w < AW; ++w) mg = fmaxf(mg, wred[w]);
+      const float Mn = fmaxf(M, mg);
+      const float alpha = M == -INFINITY ? 0.f : expf(M - Mn);
+      if (cw) {
+        float lloc = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+#pragma unroll
+        for (int t = 0; t < NPASS; ++t) {
+          const int j = g0 + t * PPB + wave * PPW + pidx;
+          const float e = j < j1 ? expf(s[t] - Mn) : 0.f;
+          lloc += e;
+          if (j == pos) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(e, vn[8 * sub + q], acc[q]);
+          } else {
+            const f16x8 v = __builtin_bit_cast(f16x8, vr[t]);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(e, (float)v[q], acc[q]);
           }
         }
-        s = group_sum<LP>(s);
-        if (sub == 0 && j < j1) sc[j - j0] = s;
+        // every lane of a position group holds the same e: count it once
+        lloc = wave_sum(sub == 0 ? lloc : 0.f);
+        if (lane == 0) wred[kWaves + wave] = lloc;
+      }
+      __syncthreads();
+      float lg = 0.f;
+#pragma unroll
+      for (int w = 0; w < AW; ++w) lg += wred[kWaves + w];
+      Lsum = Lsum * alpha + lg;
+      M = Mn;
+      __syncthreads();
+    }
+    // sum acc over the position groups of each wave, then over waves
+    if (cw) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        for (int off = LP; off < 64; off <<= 1) acc[q] += __shfl_xor(acc[q], off, 64);
+      if (pidx == 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ored[wave * HD + 8 * sub + q] = acc[q];
       }
     }
     __syncthreads();
-    const int n = j1 - j0;
-    if (wave == 0) {
-      float m = -INFINITY;
-      for (int t = lane; t < n; t += 64) m = fmaxf(m, sc[t]);
-      m = wave_max(m);
-      float ls = 0.f;
-      for (int t = lane; t < n; t += 64) {
-        const float e = expf(sc[t] - m);
-        sc[t] = e;
-        ls += e;
-      }
-      ls = wave_sum(ls);
-      if (lane == 0) { stat[0] = m; stat[1] = ls; }
-    }
-    __syncthreads();
-    // acc = sum_j exp(s_j - m) V_j
-    {
-      const int dg = threadIdx.x % LP, pg = threadIdx.x / LP;
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int j = j0 + pg; j < j1; j += NPG) {
-        const float wj = sc[j - j0];
-        if (j == pos) {
-#pragma unroll
-          for (int t = 0; t < 8; ++t) acc[t] += wj * vn[8 * dg + t];
-        } else {
-          const f16x8 v = __builtin_bit_cast(f16x8, ld_kv(rv, (uint32_t)(j * HD + 8 * dg) * 2u));
-#pragma unroll
-          for (int t = 0; t < 8; ++t) acc[t] = __builtin_fmaf(wj, (float)v[t], acc[t]);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < 8; ++t) red[pg * HD + 8 * dg + t] = acc[t];
-    }
-    __syncthreads();
+    float o = 0.f;
     if (threadIdx.x < HD) {
-      float s = 0.f;
-      for (int p = 0; p < NPG; ++p) s += red[p * HD + threadIdx.x];
-      st_coh(P.part + ((size_t)h * P.max_chunks + c) * HD + threadIdx.x, s);
+#pragma unroll
+      for (int w = 0; w < AW; ++w) o += ored[w * HD + threadIdx.x];
     }
-    if (threadIdx.x == 0) {
-      st_coh(P.pml + ((size_t)h * P.max_chunks + c) * 2, stat[0]);
-      st_coh(P.pml + ((size_t)h * P.max_chunks + c) * 2 + 1, stat[1]);
+    if (C == 1) {
+      if (threadIdx.x < HD) st_coh(P.attn_o + h * HD + threadIdx.x, o / Lsum);
+    } else {
+      float* pp = P.part + ((size_t)h * P.max_chunks) * HD;
+      float* pm = P.pml + ((size_t)h * P.max_chunks) * 2;
+      if (threadIdx.x < HD) st_coh(pp + (size_t)c * HD + threadIdx.x, o);
+      if (threadIdx.x == 0) { st_coh(pm + 2 * c, M); st_coh(pm + 2 * c + 1, Lsum); }
+      if (cw) wait_vm0();
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        uint32_t* hc = P.ctl + kCtlHead0 + h;
+        const uint32_t old = __hip_atomic_fetch_add(hc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old == (uint32_t)(C - 1);
+        if (last) st_coh(hc, 0u);   // every unit of this head has arrived: re-arm for the next layer
+        S.si[10] = last;
+      }
+      __syncthreads();
+      if (S.si[10] != 0 && threadIdx.x < HD) {
+        // merge the C partials of head h with a running max
+        constexpr int MB = 8;
+        float Mr = -INFINITY, Lr = 0.f, Or = 0.f;
+        for (int c0 = 0; c0 < C; c0 += MB) {
+          float mv[MB], lv[MB], pv[MB];
+#pragma unroll
+          for (int t = 0; t < MB; ++t) {
+            const bool in = c0 + t < C;
+            mv[t] = in ? ld_coh(pm + 2 * (c0 + t)) : -INFINITY;
+            lv[t] = in ? ld_coh(pm + 2 * (c0 + t) + 1) : 0.f;
+            pv[t] = in ? ld_coh(pp + (size_t)(c0 + t) * HD + threadIdx.x) : 0.f;
+          }
+#pragma unroll
+          for (int t = 0; t < MB; ++t) {
+            if (mv[t] == -INFINITY) continue;
+            const float Mn = fmaxf(Mr, mv[t]);
+            const float a = Mr == -INFINITY ? 0.f : expf(Mr - Mn);
+            const float bscale = expf(mv[t] - Mn);
+            Or = Or * a + pv[t] * bscale;
+            Lr = Lr * a + lv[t] * bscale;
+            Mr = Mn;
+          }
+        }
+        st_coh(P.attn_o + h * HD + threadIdx.x, Or / Lr);
+      }
     }
     __syncthreads();
   }
 }
 
-// o = merged attention output of every head -> x += Wo o on this workgroup's rows.
-__device__ __noinline__ void phase_o(const Params* __restrict__ Pp, int l, int pos, const Lds& S) {
-  const Params& P = *Pp;
-  const int ctx = pos + 1, H = P.H, hd = P.hd, q = P.q;
-  const int C = attn_chunks(ctx, H, gridDim.x);
-  float* sf = S.aux;   // [H * C] merge factor of each chunk
-  for (int h = threadIdx.x; h < H; h += kThreads) {
-    const float* pm = P.pml + (size_t)h * P.max_chunks * 2;
-    float M = -INFINITY;
-    for (int c = 0; c < C; ++c) M = fmaxf(M, ld_coh(pm + 2 * c));
-    float sum = 0.f;
-    for (int c = 0; c < C; ++c) {
-      const float m = ld_coh(pm + 2 * c);
-      sum += (m == -INFINITY ? 0.f : expf(m - M)) * ld_coh(pm + 2 * c + 1);
-    }
-    const float inv = 1.0f / sum;
-    for (int c = 0; c < C; ++c) {
-      const float m = ld_coh(pm + 2 * c);
-      sf[h * C + c] = (m == -INFINITY ? 0.f : expf(m - M)) * inv;
-    }
-  }
-  __syncthreads();
-  const rsrc_t rp = make_rsrc(P.part, (uint32_t)((size_t)H * P.max_chunks * hd * 4));
-  for (int i = threadIdx.x * 4; i < gemv_span(q); i += kThreads * 4) {
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    if (i < q) {
-      const int h = i / hd, j = i % hd;
-      for (int c = 0; c < C; ++c)
-        o += sf[h * C + c] * ld_coh4(rp, (uint32_t)(((size_t)h * P.max_chunks + c) * hd + j) * 4u);
-    }
-    *reinterpret_cast<f32x4*>(S.xs + i) = o;
-  }
-  __syncthreads();
-  int b, e;
-  split(P.d / 2, blockIdx.x, gridDim.x, b, e);
-  float* x = P.x;
-  auto epi = [x](int pr, float y0, float y1, int lane) {
-    if (lane == 0) {
-      st_coh(x + 2 * pr, ld_coh(x + 2 * pr) + y0);
-      st_coh(x + 2 * pr + 1, ld_coh(x + 2 * pr + 1) + y1);
-    }
-  };
-  gemv(P.w + (size_t)l * P.layer_stride + P.off_o, P.d, q, b, e, S.xs, epi);
-}
-
-__device__ __noinline__ void phase_gu(const Params* __restrict__ Pp, int l, const Lds& S) {
-  const Params& P = *Pp;
-  const int d = P.d;
-  load_vec(S.xs, P.x, d);
-  rmsnorm_lds(S.xs, d, P.gains + (size_t)l * 2 * d + d, P.eps, S.red);
-  int b, e;
-  split(P.F, blockIdx.x, gridDim.x, b, e);
-  float* act = P.act;
-  auto epi = [act](int pr, float g, float u, int lane) {
-    if (lane == 0) st_coh(act + pr, g / (1.0f + expf(-g)) * u);
-  };
-  gemv(P.w + (size_t)l * P.layer_stride + P.off_gu, 2 * P.F, d, b, e, S.xs, epi);
-}
-
-__device__ __noinline__ void phase_down(const Params* __restrict__ Pp, int l, const Lds& S) {
-  const Params& P = *Pp;
-  load_vec(S.xs, P.act, P.F);
-  __syncthreads();
-  int b, e;
-  split(P.d / 2, blockIdx.x, gridDim.x, b, e);
-  float* x = P.x;
-  auto epi = [x](int pr, float y0, float y1, int lane) {
-    if (lane == 0) {
-      st_coh(x + 2 * pr, ld_coh(x + 2 * pr) + y0);
-      st_coh(x + 2 * pr + 1, ld_coh(x + 2 * pr + 1) + y1);
-    }
-  };
-  gemv(P.w + (size_t)l * P.layer_stride + P.off_d, P.d, P.F, b, e, S.xs, epi);
-}
-
-// logits = W_lm rmsnorm(x, g_final); per-workgroup (max, lowest index).
-__device__ __noinline__ void phase_lm(const Params* __restrict__ Pp, int write_logits, const Lds& S) {
-  const Params& P = *Pp;
-  const int d = P.d;
-  load_vec(S.xs, P.x, d);
-  rmsnorm_lds(S.xs, d, P.gains + (size_t)P.L * 2 * d, P.eps, S.red);
-  int b, e;
-  split(P.Vlm / 2, blockIdx.x, gridDim.x, b, e);
-  float best = -INFINITY;
-  int bidx = 0x7fffffff;
-  float* lg = write_logits ? P.logits : nullptr;
-  auto epi = [&best, &bidx, lg](int pr, float y0, float y1, int lane) {
-    if (y0 > best) { best = y0; bidx = 2 * pr; }
-    if (y1 > best) { best = y1; bidx = 2 * pr + 1; }
-    if (lg != nullptr && lane == 0) { lg[2 * pr] = y0; lg[2 * pr + 1] = y1; }
-  };
-  gemv(P.w + P.off_lm, P.Vlm, d, b, e, S.xs, epi);
+// logits -> per-workgroup (max, lowest index) after phase LM's GEMV.
+__device__ __forceinline__ void lm_finish(const Params& P, float best, int bidx, const Lds& S) {
   float* bv = S.red;
   int* bi = S.si;
   if ((threadIdx.x & 63) == 0) { bv[threadIdx.x >> 6] = best; bi[threadIdx.x >> 6] = bidx; }
@@ -528,14 +647,12 @@ __device__ __noinline__ void phase_lm(const Params* __restrict__ Pp, int write_l
     st_coh(P.amax_v + blockIdx.x, v);
     st_coh(P.amax_i + blockIdx.x, ix);
   }
-  __syncthreads();
 }
 
 // Greedy token = argmax over the workgroups' partials (lowest index on ties).
 // Every workgroup computes it (it is the next token's input); workgroup 0
 // publishes it.
-__device__ __noinline__ int phase_argmax(const Params* __restrict__ Pp, int i, const Lds& S) {
-  const Params& P = *Pp;
+__device__ __forceinline__ int phase_argmax(const Params& P, int i, const Lds& S) {
   float* v = S.aux;
   int* ix = reinterpret_cast<int*>(S.aux + 1024);
   const int G = gridDim.x;
@@ -563,70 +680,152 @@ __device__ __noinline__ int phase_argmax(const Params* __restrict__ Pp, int i, c
 }
 
 template <int HD>
-__device__ __forceinline__ void attn_dispatch(const Params* __restrict__ P, int l, int pos, const Lds& S) {
-  phase_attn<HD>(P, l, pos, S);
+__device__ __forceinline__ void attn_dispatch(const Params& P, int l, int pos, int aw, const Lds& S) {
+  if (aw == 4) phase_attn<HD, 4>(P, l, pos, S);
+  else phase_attn<HD, kWaves>(P, l, pos, S);
 }
+
+// Attention positions per chunk up to which four waves compute it (and the
+// other four prefetch the O projection meanwhile).
+constexpr int kAttnNarrow = 64;
 
 extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident(const Params* __restrict__ Pp, Launch A) {
   const Params& P = *Pp;
   extern __shared__ __attribute__((aligned(16))) float smem[];
   Lds S;
   S.xs = smem;
-  S.red = smem + kMaxK;
-  S.si = reinterpret_cast<int*>(smem + kMaxK + 64);
-  S.aux = smem + kMaxK + 64 + 16;
-  const int L = P.L;
+  S.red = smem + kLdsRed;
+  S.si = reinterpret_cast<int*>(smem + kLdsSi);
+  S.aux = smem + kLdsAux;
+  S.pf = smem + kLdsPf;
+  const int wave = threadIdx.x >> 6;
+  const int L = P.L, d = P.d;
   const int ppt = phases_per_token(L);
+  const int nlayer_ph = kPhasesPerLayer * L;
   const long long total = (long long)A.n_tok * ppt;
-  long long g0 = A.phase_begin < 0 ? 0 : A.phase_begin;
-  long long g1 = (long long)A.phase_end < total ? (long long)A.phase_end : total;
+  const long long g0 = A.phase_begin < 0 ? 0 : A.phase_begin;
+  const long long g1 = (long long)A.phase_end < total ? (long long)A.phase_end : total;
   uint32_t epoch = A.bar_base;
   bool first = true, have_tok = false;
   int tok_local = 0;
+  int n_store = kWaves;    // waves with coherent stores pending from the previous phase
+  long long pf_for = -1;   // global index of the phase whose first weight blocks sit in S.pf
+  uint64_t* trace = P.trace ? P.trace + (size_t)blockIdx.x * P.trace_stride : nullptr;
+  int ev = 0;
+  auto stamp = [&]() {
+    if (trace && threadIdx.x == 0 && ev < P.trace_stride) trace[ev] = wall_clock64();
+    ++ev;
+  };
   for (long long g = g0; g < g1; ++g) {
     const int i = (int)(g / ppt), k = (int)(g % ppt);
     const bool lm = !A.lm_last_only || i == A.n_tok - 1;
-    if (k >= kPhasesPerLayer * L && !lm) continue;
+    if (k >= nlayer_ph && !lm) continue;
     const int pos = A.pos0 + i;
+    const int l = k < nlayer_ph ? k / kPhasesPerLayer : 0;
+    const int ph = k < nlayer_ph ? k % kPhasesPerLayer : (k == nlayer_ph ? (int)PH_LM : -1);
+    const bool is_gemv = ph == PH_QKV || ph == PH_O || ph == PH_GU || ph == PH_DOWN || ph == PH_LM;
     const bool skip_bar = first || (k == 0 && have_tok);
+    bool ok = true;
     if (!skip_bar) {
       ++epoch;
-      if (!grid_barrier(Pp, epoch, A.fenced, S.si)) return;
+      barrier_arrive(P, epoch, A.fenced, n_store);
+      if (is_gemv && pf_for != g) {
+        prefetch_issue(work_of(P, ph, l), S.pf, 1);
+        pf_for = g;
+      }
+      if (wave == 0) ok = barrier_wait(P, epoch, A.fenced);
     }
     first = false;
-    if (k < kPhasesPerLayer * L) {
-      const int l = k / kPhasesPerLayer, ph = k % kPhasesPerLayer;
+    // prologue: wave 0 brings this phase's input vector into LDS
+    int tok = 0;
+    if (ph == PH_QKV && l == 0) {
+      if (A.tok_src == TOK_PROMPT) tok = P.prompt[i];
+      else tok = have_tok ? tok_local : ld_coh(P.tok_cur);
+      have_tok = false;
+      tok = tok < 0 ? 0 : (tok >= P.V ? P.V - 1 : tok);
+    }
+    if (wave == 0) {
       if (ph == PH_QKV) {
-        int tok = 0;
-        if (l == 0) {
-          if (A.tok_src == TOK_PROMPT) tok = P.prompt[i];
-          else tok = have_tok ? tok_local : ld_coh(P.tok_cur);
-          have_tok = false;
-          tok = tok < 0 ? 0 : (tok >= P.V ? P.V - 1 : tok);
-        }
-        phase_qkv(Pp, l, tok, l == 0, S);
-      } else if (ph == PH_ATTN) {
-        switch (P.hd) {
-          case 8: attn_dispatch<8>(Pp, l, pos, S); break;
-          case 16: attn_dispatch<16>(Pp, l, pos, S); break;
-          case 32: attn_dispatch<32>(Pp, l, pos, S); break;
-          case 64: attn_dispatch<64>(Pp, l, pos, S); break;
-          default: attn_dispatch<128>(Pp, l, pos, S); break;
-        }
+        if (l == 0) w0_embed(P, tok, S.xs, P.gains);
+        else w0_load_vec(S.xs, P.x, d, P.gains + (size_t)l * 2 * d, P.eps);
       } else if (ph == PH_O) {
-        phase_o(Pp, l, pos, S);
+        w0_load_vec(S.xs, P.attn_o, P.q, nullptr, 0.f);
       } else if (ph == PH_GU) {
-        phase_gu(Pp, l, S);
-      } else {
-        phase_down(Pp, l, S);
+        w0_load_vec(S.xs, P.x, d, P.gains + (size_t)l * 2 * d + d, P.eps);
+      } else if (ph == PH_DOWN) {
+        w0_load_vec(S.xs, P.act, P.F, nullptr, 0.f);
+      } else if (ph == PH_LM) {
+        w0_load_vec(S.xs, P.x, d, P.gains + (size_t)L * 2 * d, P.eps);
       }
-    } else if (k == kPhasesPerLayer * L) {
-      phase_lm(Pp, A.write_logits && i == A.n_tok - 1, S);
+      if (threadIdx.x == 0) S.si[12] = ok ? 1 : 0;
+    } else if (is_gemv) {
+      wait_vm0();   // this wave's prefetch blocks have landed
+    }
+    __syncthreads();
+    if (S.si[12] == 0) {
+      wait_vm0();
+      return;
+    }
+    stamp();
+    const bool use_pf = pf_for == g;
+    const float* pf = use_pf ? S.pf : nullptr;
+    n_store = kWaves;
+    if (ph == PH_QKV) {
+      float* out = P.qkv;
+      auto epi = [out](int pr, float y0, float y1, int lane) {
+        if (lane == 0) { st_coh(out + 2 * pr, y0); st_coh(out + 2 * pr + 1, y1); }
+      };
+      gemv(work_of(P, PH_QKV, l), S.xs, pf, epi);
+    } else if (ph == PH_ATTN) {
+      const int ctx = pos + 1;
+      const int C = attn_chunks(ctx, P.H, gridDim.x);
+      const int aw = (ctx + C - 1) / C <= kAttnNarrow ? 4 : kWaves;
+      if (aw == 4) {
+        // the other four waves prefetch the O projection meanwhile
+        prefetch_issue(work_of(P, PH_O, l), S.pf, 4);
+        pf_for = g + 1;
+        n_store = 4;
+      }
+      switch (P.hd) {
+        case 8: attn_dispatch<8>(P, l, pos, aw, S); break;
+        case 16: attn_dispatch<16>(P, l, pos, aw, S); break;
+        case 32: attn_dispatch<32>(P, l, pos, aw, S); break;
+        case 64: attn_dispatch<64>(P, l, pos, aw, S); break;
+        default: attn_dispatch<128>(P, l, pos, aw, S); break;
+      }
+    } else if (ph == PH_O || ph == PH_DOWN) {
+      float* x = P.x;
+      auto epi = [x](int pr, float y0, float y1, int lane) {
+        if (lane == 0) {
+          st_coh(x + 2 * pr, ld_coh(x + 2 * pr) + y0);
+          st_coh(x + 2 * pr + 1, ld_coh(x + 2 * pr + 1) + y1);
+        }
+      };
+      gemv(work_of(P, ph, l), S.xs, pf, epi);
+    } else if (ph == PH_GU) {
+      float* act = P.act;
+      auto epi = [act](int pr, float gt, float up, int lane) {
+        if (lane == 0) st_coh(act + pr, gt / (1.0f + expf(-gt)) * up);
+      };
+      gemv(work_of(P, PH_GU, l), S.xs, pf, epi);
+    } else if (ph == PH_LM) {
+      float best = -INFINITY;
+      int bidx = 0x7fffffff;
+      float* lgp = (A.write_logits && i == A.n_tok - 1) ? P.logits : nullptr;
+      auto epi = [&best, &bidx, lgp](int pr, float y0, float y1, int lane) {
+        if (y0 > best) { best = y0; bidx = 2 * pr; }
+        if (y1 > best) { best = y1; bidx = 2 * pr + 1; }
+        if (lgp != nullptr && lane == 0) { lgp[2 * pr] = y0; lgp[2 * pr + 1] = y1; }
+      };
+      gemv(work_of(P, PH_LM, 0), S.xs, pf, epi);
+      lm_finish(P, best, bidx, S);
     } else {
-      tok_local = phase_argmax(Pp, i, S);
+      tok_local = phase_argmax(P, i, S);
       have_tok = true;
     }
+    stamp();
   }
+  wait_vm0();   // no LDS-direct load may outlive the workgroup
 }
 
 int kernel_prepare() {

@@ -155,7 +155,11 @@ def test_kv_cache_after_prefill_matches_oracle(stream):
                 # absolute fp32 error carried in, 2e-5 for O(0.3) values.  Near
                 # zero that is many ulps, so ulps alone are the wrong yardstick.
                 assert np.all(diff <= ulp + 2e-5), f"layer {l} {name}: max {diff.max()}"
-                assert np.mean(diff == 0) > 0.95, f"layer {l} {name}"
+                # layer 0 sees identical inputs, so only fp32-vs-fp64 rounding can
+                # flip an fp16 value; deeper layers also inherit upstream differences
+                same = float(np.mean(diff == 0))
+                print(f"layer {l} {name}: {same:.4f} identical, max diff {diff.max():.2e}")
+                assert same > (0.99 if l == 0 else 0.90), f"layer {l} {name}: {same}"
 
 
 def _idx(shape, name, layer=None):
