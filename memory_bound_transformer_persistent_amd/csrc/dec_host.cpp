@@ -547,6 +547,18 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
     fail(&h->err, DEC_ERR_UNSUPPORTED, "grid %d exceeds co-resident capacity %d x %d", h->grid, per_cu, cus);
     return bail(DEC_ERR_UNSUPPORTED);
   }
+  {
+    // per-workgroup GEMV results and residual rows live in fixed LDS buffers
+    auto per_wg = [&](long long n) { return (n + h->grid - 1) / h->grid; };
+    const long long q = (long long)desc->n_heads * desc->head_dim;
+    const long long need_out = std::max({2 * per_wg(3 * q / 2), 2 * per_wg(desc->d_model / 2), per_wg(desc->d_ffn),
+                                         2 * per_wg(desc->lm_vocab / 2)});
+    if (need_out > kOutFloats || 2 * per_wg(desc->d_model / 2) > kOwnFloats) {
+      fail(&h->err, DEC_ERR_UNSUPPORTED, "grid %d too small for this model (a workgroup would own %lld outputs)",
+           h->grid, need_out);
+      return bail(DEC_ERR_UNSUPPORTED);
+    }
+  }
   if (o.stream) {
     h->stream = static_cast<hipStream_t>(o.stream);
   } else {

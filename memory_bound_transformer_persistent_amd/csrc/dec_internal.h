@@ -19,8 +19,10 @@ constexpr int kGroups = 8;                  // barrier groups: workgroup b is in
 constexpr int kMaxK = 8192;                 // longest GEMV row supported (16 pieces per lane)
 constexpr int kChunkMin = 32;               // shortest attention chunk (positions)
 constexpr int kChunkMax = 2048;
-constexpr int kTraceStride = 4096;          // trace stamps kept per workgroup per launch             // longest attention chunk (scores kept in LDS)
-constexpr int kLdsBytes = 144 * 1024;       // dynamic LDS per workgroup; > half a CU's 160 KB,
+constexpr int kTraceStride = 4096;          // trace stamps kept per workgroup per launch
+constexpr int kOutFloats = 2048;            // LDS: one phase's GEMV results of a workgroup
+constexpr int kOwnFloats = 256;             // LDS: a workgroup's rows of the residual stream             // longest attention chunk (scores kept in LDS)
+constexpr int kLdsBytes = 160 * 1024;       // dynamic LDS per workgroup; > half a CU's 160 KB,
                                             // so exactly one workgroup runs per compute unit
 
 // Control words (uint32 index into Params::ctl); each on its own 256-byte line.

@@ -41,13 +41,18 @@ constexpr uint32_t kOOB = 0xFFFFFF00u;  // buffer offset past any region: loads 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS map (floats): xs [kMaxK] | red [64] | si [16 ints] | aux [kAuxFloats] | pf [kWaves][kPfFloats]
-constexpr int kPfBlocks = 12;                // 1 KB blocks of weights prefetched per wave
-constexpr int kPfFloats = kPfBlocks * 256;
-constexpr int kAuxFloats = 3072;
-constexpr int kLdsRed = kMaxK, kLdsSi = kMaxK + 64, kLdsAux = kMaxK + 80, kLdsPf = kMaxK + 80 + kAuxFloats;
-static_assert((kLdsPf + kWaves * kPfFloats) * 4 <= kLdsBytes, "LDS map exceeds the allocation");
-static_assert(kLdsPf % 4 == 0, "prefetch buffer must be 16-byte aligned");
+// Roles: wave 0 controls (grid barrier, phase input vectors, global stores,
+// attention, argmax); waves 1..7 stream GEMV weights into registers.
+constexpr int kStreamers = kWaves - 1;
+// Units (two 1 KB weight blocks) each streamer keeps in flight: 16-byte loads
+// per lane land in registers, so a wave's LDS reads never queue behind its
+// own weight traffic.
+constexpr int kUnitsInFlight = 6;
+constexpr int kBlocksInFlight = 2 * kUnitsInFlight;
+// LDS map (floats): xs | out | xown | red | si | aux | phase tables
+constexpr int kAuxFloats = 2048;
+constexpr int kLdsOut = kMaxK, kLdsOwn = kLdsOut + kOutFloats, kLdsRed = kLdsOwn + kOwnFloats;
+constexpr int kLdsSi = kLdsRed + 64, kLdsAux = kLdsSi + 16, kLdsTables = kLdsAux + kAuxFloats;
 constexpr int kWaitVm0 = 0x0F70;             // s_waitcnt vmcnt(0), expcnt/lgkmcnt untouched
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -59,15 +64,36 @@ __device__ __forceinline__ u32x4 ld_nt(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ u32x4 ld_kv(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxNt | kAuxSc1);
 }
-// 16 bytes per lane from a buffer straight into LDS at lds_base + 16*lane (wave-uniform base).
-__device__ __forceinline__ void dma16(rsrc_t r, float* lds_base, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, off, 0, 0, kAuxNt);
+// 16 bytes per lane from a buffer straight into LDS at lds_base + 16*lane (wave-uniform
+// base), coherent at device scope (activations written by other workgroups).
+__device__ __forceinline__ void dma16_coh(rsrc_t r, float* lds_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, off, 0, 0, kAuxSc1);
 }
 __device__ __forceinline__ void wait_vm0() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt[3:0] | expcnt 7 | lgkmcnt 15 | vmcnt[5:4] << 14)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ void wait_lgkm0() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt/expcnt untouched
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Plain loads of read-only data through the global address space.
+typedef __attribute__((address_space(1))) const float gfloat;
+typedef __attribute__((address_space(1))) const int gint;
+typedef __attribute__((address_space(1))) const f32x4 gf32x4;
+__device__ __forceinline__ float ldg(const float* p) { return *(gfloat*)p; }
+__device__ __forceinline__ int ldg(const int* p) { return *(gint*)p; }
+__device__ __forceinline__ f32x4 ldg4(const float* p) { return *(gf32x4*)p; }
 __device__ __forceinline__ f32x4 ld_coh4(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxSc1));
 }
@@ -150,80 +176,220 @@ __device__ __forceinline__ void split(int n, int g, int G, int& b, int& e) {
   b = (int)((long long)n * g / G);
   e = (int)((long long)n * (g + 1) / G);
 }
-__device__ __forceinline__ int round512(int n) { return (n + 511) & ~511; }
 
 // ---------------------------------------------------------------------------
 // weight prefetch into LDS
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// GEMV work and block streams
+// ---------------------------------------------------------------------------
 // A GEMV phase's work for one workgroup: row pairs [p0, p1) of W[rows, K].
-// Wave w consumes pairs p0+w, p0+w+8, ... as a stream of 1 KB blocks, block
-// b = (2*j + r)*NP + k for its j-th pair, row r of the pair, piece-column k.
+// A row is NPC = ceil(K/512) piece-columns of 512 elements (64 lanes x 16 B);
+// the workgroup's phase is the list of (pair, piece-column) units, unit
+// n = pair_offset * NPC + column, and streamer s (1..7) takes an equal
+// contiguous range of them.  A unit is two 1 KB blocks (row 0, row 1) that
+// share one piece of x.  Partial row sums meet in LDS (ds_add_f32).
 struct GemvWork {
   const uint16_t* W;
   int rows, K, p0, p1;
 };
 
-// A row pair is streamed in nch column chunks of np pieces per lane (np <= 8,
-// nch*np*512 >= K), so no more than 8 16-byte pieces per row sit in registers.
-__device__ __forceinline__ void gemv_shape(int K, int& np, int& nch) {
-  const int pieces = (K + 511) >> 9;          // 16-byte pieces per lane per row
-  nch = (pieces + 7) >> 3;
-  np = (pieces + nch - 1) / nch;
-}
+__device__ __forceinline__ int gemv_npc(int K) { return (K + 511) >> 9; }
 // LDS floats of the input vector a GEMV with row length K reads (zero-padded past K).
-__device__ __forceinline__ int gemv_span(int K) {
-  int np, nch;
-  gemv_shape(K, np, nch);
-  return 512 * np * nch;
+__device__ __forceinline__ int gemv_span(int K) { return 512 * gemv_npc(K); }
+
+__device__ __forceinline__ GemvWork work_of(const Params& P, int ph, int l) {
+  GemvWork g{nullptr, 0, 0, 0, 0};
+  int npairs = 0;
+  const uint16_t* lay = P.w + (size_t)l * P.layer_stride;
+  switch (ph) {
+    case PH_QKV: g.W = lay + P.off_qkv; g.rows = 3 * P.q; g.K = P.d; npairs = 3 * P.q / 2; break;
+    case PH_O: g.W = lay + P.off_o; g.rows = P.d; g.K = P.q; npairs = P.d / 2; break;
+    case PH_GU: g.W = lay + P.off_gu; g.rows = 2 * P.F; g.K = P.d; npairs = P.F; break;
+    case PH_DOWN: g.W = lay + P.off_d; g.rows = P.d; g.K = P.F; npairs = P.d / 2; break;
+    case PH_LM: g.W = P.w + P.off_lm; g.rows = P.Vlm; g.K = P.d; npairs = P.Vlm / 2; break;
+    default: return g;
+  }
+  split(npairs, blockIdx.x, gridDim.x, g.p0, g.p1);
+  return g;
 }
 
-// Waves [w_first, 8) copy the first kPfBlocks blocks of every wave's stream
-// into pf + w*kPfFloats with LDS-direct buffer loads (pieces past K read 0).
-// Block b of wave w's stream is unit u = b / (2*np) (pair u / nch, column
-// chunk u % nch), row (b / np) & 1 of the pair, piece b % np.  Whoever reads
-// the blocks first waits for the issuing waves (vmcnt) and a workgroup sync.
-__device__ __forceinline__ void prefetch_issue(const GemvWork& g, float* pf, int w_first) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (wave < w_first || g.W == nullptr) return;
-  const int nis = kWaves - w_first;
-  int np, nch;
-  gemv_shape(g.K, np, nch);
-  const uint32_t row_bytes = (uint32_t)g.K * 2u;
-  const rsrc_t r = make_rsrc(g.W, (uint32_t)g.rows * row_bytes);
-  const int P16 = g.K >> 3;
-  for (int f = wave - w_first; f < kWaves * kPfBlocks; f += nis) {
-    const int tw = f / kPfBlocks, b = f % kPfBlocks;
-    const int u = b / (2 * np), rr = (b / np) & 1, kk = b % np;
-    const int pr = g.p0 + tw + kWaves * (u / nch);
-    if (pr >= g.p1) continue;
-    const int c = lane + 64 * ((u % nch) * np + kk);
-    const uint32_t off = c < P16 ? (uint32_t)(2 * pr + rr) * row_bytes + 16u * c : kOOB;
-    dma16(r, pf + tw * kPfFloats + b * 256, off);
+// Streamer s's unit range [u0, u1) of a phase.
+__device__ __forceinline__ void streamer_units(const GemvWork& g, int s, int& u0, int& u1) {
+  const int n = (g.p1 - g.p0) * gemv_npc(g.K);
+  split(n, s - 1, kStreamers, u0, u1);
+}
+
+// Phase g of a launch: token i, layer l, phase type ph (-1: argmax, -2: not
+// run, i.e. the LM head and argmax of a prefill token that wants no logits);
+// k = g mod phases_per_token.  Decoded once per launch, then advanced.
+struct PhaseIt { int g, i, k, l, ph; };
+__device__ __forceinline__ int tail_phase(const Launch& A, int i, int k, int nl) {
+  const bool lm = !A.lm_last_only || i == A.n_tok - 1;
+  return !lm ? -2 : (k == nl ? (int)PH_LM : -1);
+}
+__device__ __forceinline__ PhaseIt phase_at(const Params& P, const Launch& A, int g) {
+  const int ppt = phases_per_token(P.L), nl = kPhasesPerLayer * P.L;
+  PhaseIt it;
+  it.g = g;
+  it.i = g / ppt;
+  it.k = g - it.i * ppt;
+  it.l = it.k < nl ? it.k / kPhasesPerLayer : 0;
+  it.ph = it.k < nl ? it.k - it.l * kPhasesPerLayer : tail_phase(A, it.i, it.k, nl);
+  return it;
+}
+__device__ __forceinline__ void phase_next(const Params& P, const Launch& A, PhaseIt& it) {
+  const int nl = kPhasesPerLayer * P.L;
+  ++it.g;
+  if (++it.k == nl + 2) {
+    it.k = 0; ++it.i; it.l = 0; it.ph = PH_QKV;
+  } else if (it.k < nl) {
+    if (++it.ph == kPhasesPerLayer) { it.ph = 0; ++it.l; }
+  } else {
+    it.l = 0;
+    it.ph = tail_phase(A, it.i, it.k, nl);
+  }
+}
+__device__ __forceinline__ bool is_gemv(int ph) {
+  return ph == PH_QKV || ph == PH_O || ph == PH_GU || ph == PH_DOWN || ph == PH_LM;
+}
+
+// Launch-constant split of every GEMV phase type, computed once per launch
+// into LDS (no divisions on the phase path).  Per type ph: the workgroup's
+// pairs [p0, p1) (kept by wave 0) and, per streamer, its share of units.
+constexpr int kTabStride = 12;   // ints per (streamer, phase type) entry
+enum TabField { T_LEFT, T_OFF, T_COL, T_NPC, T_ROWB, T_WRAP, T_TAIL, T_T0, T_NBYTES, T_PAD };
+constexpr int kLdsTabWg = kLdsTables;                                       // [6][2] ints
+constexpr int kLdsTab = kLdsTabWg + 16;                                     // [7][6][kTabStride] ints
+static_assert((kLdsTab + kStreamers * 6 * kTabStride) * 4 <= kLdsBytes, "LDS map exceeds the allocation");
+
+__device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ void fill_tables(const Params& P, int wave, int* tab_wg, int* tab) {
+  const int lane = threadIdx.x & 63;
+  if (lane >= 6 || lane == PH_ATTN) return;
+  const GemvWork w = work_of(P, lane, 0);
+  if (wave == 0) {
+    tab_wg[2 * lane] = w.p0;
+    tab_wg[2 * lane + 1] = w.p1;
+    return;
+  }
+  int u0, u1;
+  streamer_units(w, wave, u0, u1);
+  const uint32_t npc = (uint32_t)gemv_npc(w.K), rowb = (uint32_t)w.K * 2u;
+  int* e = tab + lane * kTabStride;   // tab: this streamer's entries
+  const int t0 = u0 / (int)npc, col = u0 - t0 * (int)npc;
+  e[T_LEFT] = u1 - u0;
+  e[T_OFF] = (int)((uint32_t)(2 * (w.p0 + t0)) * rowb + 1024u * (uint32_t)col);
+  e[T_COL] = col;
+  e[T_NPC] = (int)npc;
+  e[T_ROWB] = (int)rowb;
+  e[T_WRAP] = (int)(2u * rowb - 1024u * (npc - 1));   // last column -> next pair's column 0
+  e[T_TAIL] = (int)((uint32_t)(w.K >> 3) - 64u * (npc - 1));   // lanes with data in the last column
+  e[T_T0] = t0;
+  e[T_NBYTES] = (int)((uint32_t)w.rows * rowb);
+  // zero-reading units that round the phase up to whole groups of kUnitsInFlight
+  e[T_PAD] = (kUnitsInFlight - (u1 - u0) % kUnitsInFlight) % kUnitsInFlight;
+}
+
+__device__ __forceinline__ const uint16_t* gemv_base(const Params& P, int ph, int l) {
+  const uint16_t* lay = P.w + (size_t)l * P.layer_stride;
+  switch (ph) {
+    case PH_QKV: return lay + P.off_qkv;
+    case PH_O: return lay + P.off_o;
+    case PH_GU: return lay + P.off_gu;
+    case PH_DOWN: return lay + P.off_d;
+    default: return P.w + P.off_lm;
   }
 }
 
+// A streamer's position in its block stream (wave-uniform).  The next unit is
+// column col of the pair whose row 0 starts at byte `off` of phase it's
+// matrix; `left` units of the phase remain, then `pad` zero-reading ones
+// that round the phase to whole groups.  Once the stream has ended every
+// further load is out of range and reads zeros, so the number of loads in
+// flight never changes.
+struct Cursor {
+  PhaseIt it;
+  uint32_t left, pad, off, col, npc, row_bytes, wrap, tail;
+  rsrc_t r;
+};
+
+// Take phase it if this streamer has units in it.
+__device__ __forceinline__ bool cursor_take(const Params& P, const int* tab, Cursor& cu) {
+  if (!is_gemv(cu.it.ph)) return false;
+  const int* e = tab + cu.it.ph * kTabStride;
+  const int left = rfl(e[T_LEFT]);
+  if (left <= 0) return false;
+  cu.left = (uint32_t)left;
+  cu.pad = (uint32_t)rfl(e[T_PAD]);
+  cu.off = (uint32_t)rfl(e[T_OFF]);
+  cu.col = (uint32_t)rfl(e[T_COL]);
+  cu.npc = (uint32_t)rfl(e[T_NPC]);
+  cu.row_bytes = (uint32_t)rfl(e[T_ROWB]);
+  cu.wrap = (uint32_t)rfl(e[T_WRAP]);
+  cu.tail = (uint32_t)rfl(e[T_TAIL]);
+  cu.r = make_rsrc(gemv_base(P, cu.it.ph, cu.it.l), (uint32_t)rfl(e[T_NBYTES]));
+  return true;
+}
+__device__ __forceinline__ void cursor_start(const Params& P, const Launch& A, int g0, int g1, const int* tab,
+                                             Cursor& cu) {
+  cu.left = cu.pad = 0;
+  cu.col = cu.npc = cu.off = cu.row_bytes = cu.wrap = cu.tail = 0;
+  cu.r = make_rsrc(P.w, 0);
+  if (g0 >= g1) { cu.it.g = g1; return; }
+  cu.it = phase_at(P, A, g0);
+  while (!cursor_take(P, tab, cu)) {
+    phase_next(P, A, cu.it);
+    if (cu.it.g >= g1) return;
+  }
+}
+__device__ __forceinline__ void cursor_next(const Params& P, const Launch& A, int g1, const int* tab, Cursor& cu) {
+  do {
+    phase_next(P, A, cu.it);
+    if (cu.it.g >= g1) return;
+  } while (!cursor_take(P, tab, cu));
+}
+
+// Load the cursor's next unit (both rows, 16 B per lane each); advance.
+// Straight-line code: the two loads are the same instructions whatever the
+// cursor's state, so their destination registers never need copying.
+__device__ __forceinline__ void issue_unit(Cursor& cu, uint32_t lane16, u32x4& b0, u32x4& b1) {
+  const bool live = cu.left > 0;
+  const bool last_col = cu.col + 1 == cu.npc;
+  const bool ok = live && (!last_col || (lane16 >> 4) < cu.tail);
+  const uint32_t o0 = ok ? cu.off + lane16 : kOOB;
+  const uint32_t o1 = ok ? cu.off + cu.row_bytes + lane16 : kOOB + 16u;   // distinct: always two loads
+  b0 = ld_nt(cu.r, o0);
+  b1 = ld_nt(cu.r, o1);
+  cu.left -= live ? 1u : 0u;
+  cu.pad -= (!live && cu.pad > 0) ? 1u : 0u;
+  cu.off += live ? (last_col ? cu.wrap : 1024u) : 0u;
+  cu.col = live ? (last_col ? 0u : cu.col + 1u) : cu.col;
+}
+
+__device__ __forceinline__ void lds_add(float* p, float v) {
+  __builtin_amdgcn_ds_faddf((__attribute__((address_space(3))) float*)p, v, 0, 0, false);
+}
+
 // ---------------------------------------------------------------------------
-// grid barrier, split in two halves
+// wave 0: grid barrier
 // ---------------------------------------------------------------------------
-// Arrive: waves [0, n_store) wait for their coherent stores to complete
-// (vmcnt: waves that only have prefetch loads in flight skip it), the
-// workgroup syncs, and thread 0 adds one to its group's counter (group =
-// blockIdx % 8).  Wait (wave 0): lanes 0..7 poll the eight group counters
-// until each holds group_size * epoch, so a workgroup is released one
-// atomic hop after the last arrival.  epoch is the cumulative barrier number
-// (1-based, wrapping).  The wait returns false if the watchdog expires here
-// or any workgroup raised an error.
-__device__ __forceinline__ void barrier_arrive(const Params& P, uint32_t epoch, int fenced, int n_store) {
-  if ((int)(threadIdx.x >> 6) < n_store) wait_vm0();
-  __syncthreads();
-  if (threadIdx.x == 0) {
+// Arrive: wave 0 has issued every coherent store of the phase; it waits for
+// them, then adds one to its group's counter (group = blockIdx % 8).  Wait:
+// lanes 0..7 poll the eight group counters until each holds
+// group_size * epoch (epoch = cumulative barrier number, wrapping).  Returns
+// false if the watchdog expires or any workgroup raised an error.
+__device__ __forceinline__ void w0_arrive(const Params& P, int fenced) {
+  wait_vm0();
+  if ((threadIdx.x & 63) == 0) {
     if (fenced) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __hip_atomic_fetch_add(P.ctl + kCtlGroup0 + 64 * (blockIdx.x % kGroups), 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-__device__ __forceinline__ bool barrier_wait(const Params& P, uint32_t epoch, int fenced) {
+__device__ __forceinline__ bool w0_wait(const Params& P, uint32_t epoch, int fenced) {
   const int lane = threadIdx.x & 63;
   const uint32_t G = gridDim.x;
   const int ng = G < (uint32_t)kGroups ? (int)G : kGroups;
@@ -251,149 +417,48 @@ __device__ __forceinline__ bool barrier_wait(const Params& P, uint32_t epoch, in
 }
 
 // ---------------------------------------------------------------------------
-// GEMV: y = W x over the row pairs of a GemvWork.  A wave's work is a stream of
-// units (pair, column chunk); lane l reads 16-byte pieces l, l+64, ... of both
-// rows of the unit, and the first kPfBlocks 1 KB blocks of the stream come from
-// the LDS prefetch when pf is set.  While one unit is multiplied the next
-// unit's loads are in flight.  xs: fp32 x in LDS, zero-padded to
-// gemv_span(K).  epi(pair, y0, y1, lane) sees the wave-reduced sums.
+// wave 0: phase inputs
 // ---------------------------------------------------------------------------
-template <int NP>
-__device__ __forceinline__ void gemv_fetch(rsrc_t r, uint32_t row_bytes, int P16, int pr, int u, int ch,
-                                           const float* pfw, int lane, u32x4 (&w0)[NP], u32x4 (&w1)[NP]) {
-  const uint32_t b0 = (uint32_t)(2 * pr) * row_bytes;
+constexpr int kGainRegs = 12;   // f32x4 of norm gains held per lane (d <= 3072 in one batch)
+
+// Norm gains g[0..n) for w0_load_vec, loaded early (before the barrier poll).
+__device__ __forceinline__ void w0_gains(const float* g, int n, f32x4 (&gv)[kGainRegs]) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int k = 0; k < NP; ++k) {
-    const int c = lane + 64 * (ch * NP + k);
-    const bool in = c < P16;
-    const int blk0 = (2 * u) * NP + k, blk1 = (2 * u + 1) * NP + k;
-    if (pfw != nullptr && blk0 < kPfBlocks)
-      w0[k] = *reinterpret_cast<const u32x4*>(pfw + blk0 * 256 + lane * 4);
-    else
-      w0[k] = ld_nt(r, in ? b0 + 16u * c : kOOB);
-    if (pfw != nullptr && blk1 < kPfBlocks)
-      w1[k] = *reinterpret_cast<const u32x4*>(pfw + blk1 * 256 + lane * 4);
-    else
-      w1[k] = ld_nt(r, in ? b0 + row_bytes + 16u * c : kOOB);
+  for (int t = 0; t < kGainRegs; ++t) {
+    const int i = 256 * t + 4 * lane;
+    gv[t] = (g != nullptr && i < n) ? ldg4(g + i) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
-template <int NP>
-__device__ __forceinline__ void gemv_accum(const u32x4 (&w0)[NP], const u32x4 (&w1)[NP], const float* xs, int lane,
-                                           int ch, float& a0, float& a1) {
-#pragma unroll
-  for (int k = 0; k < NP; ++k) {
-    const f32x4* xp = reinterpret_cast<const f32x4*>(xs + 8 * (lane + 64 * (ch * NP + k)));
-    const f32x4 xa = xp[0], xb = xp[1];
-    a0 = dot8(w0[k], xa, xb, a0);
-    a1 = dot8(w1[k], xa, xb, a1);
-  }
-}
-
-template <int NP, class Epi>
-__device__ __forceinline__ void gemv_stream(const GemvWork& g, int nch, const float* xs, const float* pf, Epi& epi) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t row_bytes = (uint32_t)g.K * 2u;
-  const rsrc_t r = make_rsrc(g.W, (uint32_t)g.rows * row_bytes);
-  const int P16 = g.K >> 3;
-  const float* pfw = pf ? pf + wave * kPfFloats : nullptr;
-  const int npairs = g.p1 - g.p0 - wave > 0 ? (g.p1 - g.p0 - wave + kWaves - 1) / kWaves : 0;
-  const int nunits = npairs * nch;
-  if (nunits == 0) return;
-  float a0 = 0.f, a1 = 0.f;
-  u32x4 x0[NP], x1[NP], y0[NP], y1[NP];
-  auto pair_of = [&](int u) { return g.p0 + wave + kWaves * (u / nch); };
-  gemv_fetch<NP>(r, row_bytes, P16, pair_of(0), 0, 0, pfw, lane, x0, x1);
-  auto finish = [&](int u) {
-    if (u % nch == nch - 1) {
-      const float s0 = wave_sum(a0), s1 = wave_sum(a1);
-      epi(pair_of(u), s0, s1, lane);
-      a0 = 0.f;
-      a1 = 0.f;
-    }
-  };
-  for (int u = 0; u < nunits; u += 2) {
-    if (u + 1 < nunits) gemv_fetch<NP>(r, row_bytes, P16, pair_of(u + 1), u + 1, (u + 1) % nch, pfw, lane, y0, y1);
-    gemv_accum<NP>(x0, x1, xs, lane, u % nch, a0, a1);
-    finish(u);
-    if (u + 1 >= nunits) break;
-    if (u + 2 < nunits) gemv_fetch<NP>(r, row_bytes, P16, pair_of(u + 2), u + 2, (u + 2) % nch, pfw, lane, x0, x1);
-    gemv_accum<NP>(y0, y1, xs, lane, (u + 1) % nch, a0, a1);
-    finish(u + 1);
-  }
-}
-
-template <class Epi>
-__device__ __forceinline__ void gemv(const GemvWork& g, const float* xs, const float* pf, Epi& epi) {
-  int np, nch;
-  gemv_shape(g.K, np, nch);
-  switch (np) {
-    case 1: gemv_stream<1>(g, nch, xs, pf, epi); break;
-    case 2: gemv_stream<2>(g, nch, xs, pf, epi); break;
-    case 3: gemv_stream<3>(g, nch, xs, pf, epi); break;
-    case 4: gemv_stream<4>(g, nch, xs, pf, epi); break;
-    case 5: gemv_stream<5>(g, nch, xs, pf, epi); break;
-    case 6: gemv_stream<6>(g, nch, xs, pf, epi); break;
-    case 7: gemv_stream<7>(g, nch, xs, pf, epi); break;
-    default: gemv_stream<8>(g, nch, xs, pf, epi); break;
-  }
-}
-
-// The GEMV work of each phase for this workgroup (pairs split evenly).
-__device__ __forceinline__ GemvWork work_of(const Params& P, int ph, int l) {
-  GemvWork g{nullptr, 0, 0, 0, 0};
-  int npairs = 0;
-  const uint16_t* lay = P.w + (size_t)l * P.layer_stride;
-  switch (ph) {
-    case PH_QKV: g.W = lay + P.off_qkv; g.rows = 3 * P.q; g.K = P.d; npairs = 3 * P.q / 2; break;
-    case PH_O: g.W = lay + P.off_o; g.rows = P.d; g.K = P.q; npairs = P.d / 2; break;
-    case PH_GU: g.W = lay + P.off_gu; g.rows = 2 * P.F; g.K = P.d; npairs = P.F; break;
-    case PH_DOWN: g.W = lay + P.off_d; g.rows = P.d; g.K = P.F; npairs = P.d / 2; break;
-    case PH_LM: g.W = P.w + P.off_lm; g.rows = P.Vlm; g.K = P.d; npairs = P.Vlm / 2; break;
-    default: return g;
-  }
-  split(npairs, blockIdx.x, gridDim.x, g.p0, g.p1);
-  return g;
-}
-
-// ---------------------------------------------------------------------------
-// prologues: run by wave 0 alone while the other waves' prefetch lands
-// ---------------------------------------------------------------------------
-constexpr int kVecBatch = 16;   // 16-byte loads per lane in flight in a prologue
-
-// xs[0..gemv_span(n)) <- src[0..n) (coherent loads), zero past n; with g set,
-// the RMSNorm of src times g: src / sqrt(mean(src^2) + eps) * g.
-__device__ __forceinline__ void w0_load_vec(float* xs, const float* src, int n, const float* g, float eps) {
+// xs[0..gemv_span(n)) <- src[0..n) (coherent, zero past n); with g set,
+// xs = src / sqrt(mean(src^2) + eps) * g (gv: g's first kGainRegs*256 values).
+__device__ __forceinline__ void w0_load_vec(float* xs, const float* src, int n, const float* g,
+                                            const f32x4 (&gv)[kGainRegs], float eps) {
   const int lane = threadIdx.x & 63;
   const rsrc_t r = make_rsrc(src, (uint32_t)n * 4u);
   const int span = gemv_span(n);
+  for (int i = 0; i < span; i += 256) dma16_coh(r, xs + i, (uint32_t)(i + 4 * lane) * 4u);
+  wait_vm0();
+  if (g == nullptr) return;
   float ss = 0.f;
-  for (int i0 = 0; i0 < span; i0 += 256 * kVecBatch) {
-    f32x4 v[kVecBatch], gv[kVecBatch];
-#pragma unroll
-    for (int t = 0; t < kVecBatch; ++t) {
-      const int i = i0 + 256 * t + 4 * lane;
-      v[t] = ld_coh4(r, i < n ? (uint32_t)i * 4u : kOOB);
-      if (g != nullptr) gv[t] = (i < n) ? *reinterpret_cast<const f32x4*>(g + i) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int t = 0; t < kVecBatch; ++t) {
-      const int i = i0 + 256 * t + 4 * lane;
-      if (i < span) {
-        ss += v[t][0] * v[t][0] + v[t][1] * v[t][1] + v[t][2] * v[t][2] + v[t][3] * v[t][3];
-        *reinterpret_cast<f32x4*>(xs + i) = g != nullptr ? v[t] * gv[t] : v[t];
-      }
-    }
+  for (int i = 4 * lane; i < n; i += 256) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(xs + i);
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
   }
-  if (g != nullptr) {
-    const float s = 1.0f / sqrtf(wave_sum(ss) / (float)n + eps);
-    for (int i = 4 * lane; i < n; i += 256) *reinterpret_cast<f32x4*>(xs + i) *= s;
+  const float s = 1.0f / sqrtf(wave_sum(ss) / (float)n + eps);
+#pragma unroll
+  for (int t = 0; t < kGainRegs; ++t) {
+    const int i = 256 * t + 4 * lane;
+    if (i < n) *reinterpret_cast<f32x4*>(xs + i) = *reinterpret_cast<const f32x4*>(xs + i) * s * gv[t];
   }
+  for (int i = 256 * kGainRegs + 4 * lane; i < n; i += 256)
+    *reinterpret_cast<f32x4*>(xs + i) = *reinterpret_cast<const f32x4*>(xs + i) * s * ldg4(g + i);
 }
 
-// Layer-0 input: x = E[tok] (fp16 -> fp32); this workgroup stores its own rows
-// of x, and xs gets rmsnorm(x) * g.
-__device__ __forceinline__ void w0_embed(const Params& P, int tok, float* xs, const float* g) {
+// Layer-0 input: x = E[tok] (fp16 -> fp32).  This workgroup's rows of x go to
+// xown and to global x; xs gets rmsnorm(x) * g.
+__device__ __forceinline__ void w0_embed(const Params& P, int tok, float* xs, float* xown, const float* g) {
   const int lane = threadIdx.x & 63, d = P.d;
   const _Float16* e = reinterpret_cast<const _Float16*>(P.w + P.off_E + (size_t)tok * d);
   int b, en;
@@ -403,63 +468,52 @@ __device__ __forceinline__ void w0_embed(const Params& P, int tok, float* xs, co
   for (int i = 8 * lane; i < span; i += 512) {
     f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
     if (i < d) {
-      const f16x8 h = *reinterpret_cast<const f16x8*>(e + i);
+      const f16x8 h = __builtin_bit_cast(f16x8, ldg4(reinterpret_cast<const float*>(e + i)));
       lo = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
       hi = f32x4{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
-      for (int q = 0; q < 8; ++q)
-        if (i + q >= 2 * b && i + q < 2 * en) st_coh(P.x + i + q, q < 4 ? lo[q] : hi[q - 4]);
-      const f32x4 ga = *reinterpret_cast<const f32x4*>(g + i), gb = *reinterpret_cast<const f32x4*>(g + i + 4);
-      ss += lo[0] * lo[0] + lo[1] * lo[1] + lo[2] * lo[2] + lo[3] * lo[3] +
-            hi[0] * hi[0] + hi[1] * hi[1] + hi[2] * hi[2] + hi[3] * hi[3];
-      lo *= ga;
-      hi *= gb;
     }
     *reinterpret_cast<f32x4*>(xs + i) = lo;
     *reinterpret_cast<f32x4*>(xs + i + 4) = hi;
+    ss += lo[0] * lo[0] + lo[1] * lo[1] + lo[2] * lo[2] + lo[3] * lo[3] +
+          hi[0] * hi[0] + hi[1] * hi[1] + hi[2] * hi[2] + hi[3] * hi[3];
+  }
+  for (int r = 2 * b + lane; r < 2 * en; r += 64) {
+    xown[r - 2 * b] = xs[r];
+    st_coh(P.x + r, xs[r]);
   }
   const float s = 1.0f / sqrtf(wave_sum(ss) / (float)d + P.eps);
-  for (int i = 4 * lane; i < d; i += 256) *reinterpret_cast<f32x4*>(xs + i) *= s;
+  for (int i = 4 * lane; i < d; i += 256)
+    *reinterpret_cast<f32x4*>(xs + i) = *reinterpret_cast<const f32x4*>(xs + i) * s * ldg4(g + i);
 }
 
 // ---------------------------------------------------------------------------
-// phases
+// wave 0: attention
 // ---------------------------------------------------------------------------
-struct Lds {
-  float* xs;    // GEMV input vector, kMaxK floats
-  float* red;   // 64 floats
-  int* si;      // 16 ints
-  float* aux;   // attention / argmax scratch, kAuxFloats
-  float* pf;    // weight prefetch, kWaves x kPfFloats
-};
-
 // Single-query attention of every head over positions 0..pos, split into
-// chunks of positions.  AW waves compute; a thread holds K and V of NPASS
-// positions in registers (their loads are issued before the query is read),
-// so a unit costs one memory round trip per group of GRP positions, with an
-// online softmax across groups.  With more than one chunk per head each unit
-// stores an unnormalised partial (max m, sum of exp l, sum of exp * V) and
-// the last unit of a head to finish (per-head counter) merges them; the head's
-// output o goes to P.attn_o.
-template <int HD, int AW>
-__device__ __forceinline__ void phase_attn(const Params& P, int l, int pos, const Lds& S) {
-  constexpr int LP = HD / 8;             // lanes per position (16 B of K or V each)
-  constexpr int PPW = 64 / LP;           // positions per wave per pass
-  constexpr int PPB = PPW * AW;          // positions per workgroup per pass
-  constexpr int NPASS = 4;
-  constexpr int GRP = PPB * NPASS;       // positions per register group
-  float* qs = S.aux;                     // [HD] rotated, scaled query
+// chunks of positions; (head, chunk) units go round-robin over workgroups.
+// A lane group of HD/8 lanes holds one position (16 B of its K and V row per
+// lane); K and V of NPASS*64/(HD/8) positions are loaded together and an
+// online softmax runs across such groups.  The first group's loads are
+// issued before the grid barrier releases (`wait` runs the barrier wait once):
+// cached positions do not depend on this token.  Each unit stores an
+// unnormalised partial (max m, sum of exp l, sum of exp * V) that the O
+// phase merges.
+template <int HD, class Wait>
+__device__ __forceinline__ bool w0_attention(const Params& P, int l, int pos, float* aux, Wait&& wait) {
+  constexpr int LP = HD / 8, PPW = 64 / LP;
+  constexpr int NPASS = 8;
+  constexpr int GRP = PPW * NPASS;       // positions per register group
+  float* qs = aux;                       // [HD] rotated, scaled query
   float* kn = qs + HD;                   // [HD] new key (fp16-rounded)
   float* vn = kn + HD;                   // [HD] new value (fp16-rounded)
-  float* wred = vn + HD;                 // [2 * kWaves]
-  float* ored = wred + 2 * kWaves;       // [AW * HD]
   const int ctx = pos + 1, H = P.H, G = gridDim.x;
   const int C = attn_chunks(ctx, H, G);
   const int CH = (ctx + C - 1) / C;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const bool cw = wave < AW;
+  const int lane = threadIdx.x & 63;
   const int sub = lane % LP, pidx = lane / LP;
   const float scale = 1.0f / sqrtf((float)HD);
   const size_t head_elems = (size_t)P.max_ctx * HD;
+  bool waited = false;
   for (int u = blockIdx.x; u < H * C; u += G) {
     const int h = u / C, c = u % C;
     const int j0 = c * CH;
@@ -473,20 +527,21 @@ __device__ __forceinline__ void phase_attn(const Params& P, int l, int pos, cons
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int g0 = j0; g0 < j1; g0 += GRP) {
       u32x4 kr[NPASS], vr[NPASS];
-      if (cw) {
 #pragma unroll
-        for (int t = 0; t < NPASS; ++t) {
-          const int j = g0 + t * PPB + wave * PPW + pidx;
-          const uint32_t off = (j < j1 && j != pos) ? (uint32_t)(j * HD + 8 * sub) * 2u : kOOB;
-          kr[t] = ld_kv(rk, off);
-          vr[t] = ld_kv(rv, off);
-        }
+      for (int t = 0; t < NPASS; ++t) {
+        const int j = g0 + t * PPW + pidx;
+        const uint32_t off = (j < j1 && j != pos) ? (uint32_t)(j * HD + 8 * sub) * 2u : kOOB;
+        kr[t] = ld_kv(rk, off);
+        vr[t] = ld_kv(rv, off);
+      }
+      if (!waited) {
+        waited = true;
+        if (!wait()) return false;
       }
       if (g0 == j0) {
-        if (threadIdx.x < HD / 2) {
-          const int i = threadIdx.x;
-          const float cs = P.rope[((size_t)pos * (HD / 2) + i) * 2];
-          const float sn = P.rope[((size_t)pos * (HD / 2) + i) * 2 + 1];
+        for (int i = lane; i < HD / 2; i += 64) {
+          const float cs = ldg(P.rope + ((size_t)pos * (HD / 2) + i) * 2);
+          const float sn = ldg(P.rope + ((size_t)pos * (HD / 2) + i) * 2 + 1);
           const float* qh = P.qkv + h * HD;
           const float q0 = ld_coh(qh + 2 * i), q1 = ld_coh(qh + 2 * i + 1);
           qs[2 * i] = (q0 * cs - q1 * sn) * scale;
@@ -507,325 +562,359 @@ __device__ __forceinline__ void phase_attn(const Params& P, int l, int pos, cons
             st_coh(reinterpret_cast<uint32_t*>(vc + (size_t)pos * HD + 2 * i), vb);
           }
         }
-        __syncthreads();
+        wait_lgkm0();   // LDS writes above are visible to this wave's reads below
       }
+      const f32x4 qa = *reinterpret_cast<const f32x4*>(qs + 8 * sub);
+      const f32x4 qb = *reinterpret_cast<const f32x4*>(qs + 8 * sub + 4);
       float s[NPASS];
-      if (cw) {
-        const f32x4 qa = *reinterpret_cast<const f32x4*>(qs + 8 * sub);
-        const f32x4 qb = *reinterpret_cast<const f32x4*>(qs + 8 * sub + 4);
-        float mloc = -INFINITY;
+      float mloc = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < NPASS; ++t) {
-          const int j = g0 + t * PPB + wave * PPW + pidx;
-          float dsum;
-          if (j == pos) {
-            const f32x4 ka = *reinterpret_cast<const f32x4*>(kn + 8 * sub);
-            const f32x4 kb = *reinterpret_cast<const f32x4*>(kn + 8 * sub + 4);
-            dsum = ka[0] * qa[0] + ka[1] * qa[1] + ka[2] * qa[2] + ka[3] * qa[3] +
-                   kb[0] * qb[0] + kb[1] * qb[1] + kb[2] * qb[2] + kb[3] * qb[3];
-          } else {
-            dsum = dot8(kr[t], qa, qb, 0.f);
-          }
-          dsum = group_sum<LP>(dsum);
-          s[t] = j < j1 ? dsum : -INFINITY;
-          mloc = fmaxf(mloc, s[t]);
+      for (int t = 0; t < NPASS; ++t) {
+        const int j = g0 + t * PPW + pidx;
+        float dsum;
+        if (j == pos) {
+          const f32x4 ka = *reinterpret_cast<const f32x4*>(kn + 8 * sub);
+          const f32x4 kb = *reinterpret_cast<const f32x4*>(kn + 8 * sub + 4);
+          dsum = ka[0] * qa[0] + ka[1] * qa[1] + ka[2] * qa[2] + ka[3] * qa[3] +
+                 kb[0] * qb[0] + kb[1] * qb[1] + kb[2] * qb[2] + kb[3] * qb[3];
+        } else {
+          dsum = dot8(kr[t], qa, qb, 0.f);
         }
-        mloc = wave_max(mloc);
-        if (lane == 0) wred[wave] = mloc;
+        dsum = group_sum<LP>(dsum);
+        s[t] = j < j1 ? dsum : -INFINITY;
+        mloc = fmaxf(mloc, s[t]);
       }
-      __syncthreads();
-      float mg = wred[0];
-#pragma unroll
-      for (int w = 1; w < AW; ++w) mg = fmaxf(mg, wred[w]);
-      const float Mn = fmaxf(M, mg);
+      const float Mn = fmaxf(M, wave_max(mloc));
       const float alpha = M == -INFINITY ? 0.f : expf(M - Mn);
-      if (cw) {
-        float lloc = 0.f;
+      float lloc = 0.f;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+      for (int q = 0; q < 8; ++q) acc[q] *= alpha;
 #pragma unroll
-        for (int t = 0; t < NPASS; ++t) {
-          const int j = g0 + t * PPB + wave * PPW + pidx;
-          const float e = j < j1 ? expf(s[t] - Mn) : 0.f;
-          lloc += e;
-          if (j == pos) {
+      for (int t = 0; t < NPASS; ++t) {
+        const int j = g0 + t * PPW + pidx;
+        const float e = j < j1 ? expf(s[t] - Mn) : 0.f;
+        lloc += e;
+        if (j == pos) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(e, vn[8 * sub + q], acc[q]);
-          } else {
-            const f16x8 v = __builtin_bit_cast(f16x8, vr[t]);
+          for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(e, vn[8 * sub + q], acc[q]);
+        } else {
+          const f16x8 v = __builtin_bit_cast(f16x8, vr[t]);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(e, (float)v[q], acc[q]);
-          }
+          for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(e, (float)v[q], acc[q]);
         }
-        // every lane of a position group holds the same e: count it once
-        lloc = wave_sum(sub == 0 ? lloc : 0.f);
-        if (lane == 0) wred[kWaves + wave] = lloc;
       }
-      __syncthreads();
-      float lg = 0.f;
-#pragma unroll
-      for (int w = 0; w < AW; ++w) lg += wred[kWaves + w];
-      Lsum = Lsum * alpha + lg;
+      // every lane of a position group holds the same e: count it once
+      Lsum = Lsum * alpha + wave_sum(sub == 0 ? lloc : 0.f);
       M = Mn;
-      __syncthreads();
     }
-    // sum acc over the position groups of each wave, then over waves
-    if (cw) {
+    // sum over the position groups of the wave: lanes sub, sub+LP, ...
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        for (int off = LP; off < 64; off <<= 1) acc[q] += __shfl_xor(acc[q], off, 64);
-      if (pidx == 0) {
+    for (int q = 0; q < 8; ++q)
+      for (int off = LP; off < 64; off <<= 1) acc[q] += __shfl_xor(acc[q], off, 64);
+    float* pp = P.part + ((size_t)h * P.max_chunks + c) * HD;
+    float* pm = P.pml + ((size_t)h * P.max_chunks + c) * 2;
+    if (pidx == 0) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) ored[wave * HD + 8 * sub + q] = acc[q];
-      }
+      for (int q = 0; q < 8; ++q) st_coh(pp + 8 * sub + q, acc[q]);
     }
-    __syncthreads();
-    float o = 0.f;
-    if (threadIdx.x < HD) {
+    if (lane == 0) { st_coh(pm, M); st_coh(pm + 1, Lsum); }
+  }
+  if (!waited) return wait();
+  return true;
+}
+
+// All waves: xs <- o, the attention output of every head, merged from the
+// per-chunk partials with a running max: o = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c.
+__device__ __forceinline__ void merge_attention(const Params& P, int pos, float* xs) {
+  const int ctx = pos + 1, H = P.H, hd = P.hd, q = P.q;
+  const int C = attn_chunks(ctx, H, gridDim.x);
+  const rsrc_t rp = make_rsrc(P.part, (uint32_t)((size_t)H * P.max_chunks * hd * 4));
+  constexpr int MB = 8;
+  for (int i = threadIdx.x * 4; i < gemv_span(q); i += kThreads * 4) {
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    if (i < q) {
+      const int h = i / hd, jj = i % hd;
+      const float* pm = P.pml + (size_t)h * P.max_chunks * 2;
+      float Mr = -INFINITY, Lr = 0.f;
+      f32x4 Or = {0.f, 0.f, 0.f, 0.f};
+      for (int c0 = 0; c0 < C; c0 += MB) {
+        float mv[MB], lv[MB];
+        f32x4 pv[MB];
 #pragma unroll
-      for (int w = 0; w < AW; ++w) o += ored[w * HD + threadIdx.x];
-    }
-    if (C == 1) {
-      if (threadIdx.x < HD) st_coh(P.attn_o + h * HD + threadIdx.x, o / Lsum);
-    } else {
-      float* pp = P.part + ((size_t)h * P.max_chunks) * HD;
-      float* pm = P.pml + ((size_t)h * P.max_chunks) * 2;
-      if (threadIdx.x < HD) st_coh(pp + (size_t)c * HD + threadIdx.x, o);
-      if (threadIdx.x == 0) { st_coh(pm + 2 * c, M); st_coh(pm + 2 * c + 1, Lsum); }
-      if (cw) wait_vm0();
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        uint32_t* hc = P.ctl + kCtlHead0 + h;
-        const uint32_t old = __hip_atomic_fetch_add(hc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int last = old == (uint32_t)(C - 1);
-        if (last) st_coh(hc, 0u);   // every unit of this head has arrived: re-arm for the next layer
-        S.si[10] = last;
-      }
-      __syncthreads();
-      if (S.si[10] != 0 && threadIdx.x < HD) {
-        // merge the C partials of head h with a running max
-        constexpr int MB = 8;
-        float Mr = -INFINITY, Lr = 0.f, Or = 0.f;
-        for (int c0 = 0; c0 < C; c0 += MB) {
-          float mv[MB], lv[MB], pv[MB];
-#pragma unroll
-          for (int t = 0; t < MB; ++t) {
-            const bool in = c0 + t < C;
-            mv[t] = in ? ld_coh(pm + 2 * (c0 + t)) : -INFINITY;
-            lv[t] = in ? ld_coh(pm + 2 * (c0 + t) + 1) : 0.f;
-            pv[t] = in ? ld_coh(pp + (size_t)(c0 + t) * HD + threadIdx.x) : 0.f;
-          }
-#pragma unroll
-          for (int t = 0; t < MB; ++t) {
-            if (mv[t] == -INFINITY) continue;
-            const float Mn = fmaxf(Mr, mv[t]);
-            const float a = Mr == -INFINITY ? 0.f : expf(Mr - Mn);
-            const float bscale = expf(mv[t] - Mn);
-            Or = Or * a + pv[t] * bscale;
-            Lr = Lr * a + lv[t] * bscale;
-            Mr = Mn;
-          }
+        for (int t = 0; t < MB; ++t) {
+          const bool in = c0 + t < C;
+          mv[t] = in ? ld_coh(pm + 2 * (c0 + t)) : -INFINITY;
+          lv[t] = in ? ld_coh(pm + 2 * (c0 + t) + 1) : 0.f;
+          pv[t] = ld_coh4(rp, in ? (uint32_t)(((size_t)h * P.max_chunks + c0 + t) * hd + jj) * 4u : kOOB);
         }
-        st_coh(P.attn_o + h * HD + threadIdx.x, Or / Lr);
+#pragma unroll
+        for (int t = 0; t < MB; ++t) {
+          if (mv[t] == -INFINITY) continue;
+          const float Mn = fmaxf(Mr, mv[t]);
+          const float a = Mr == -INFINITY ? 0.f : expf(Mr - Mn);
+          const float bs = expf(mv[t] - Mn);
+          Or = Or * a + pv[t] * bs;
+          Lr = Lr * a + lv[t] * bs;
+          Mr = Mn;
+        }
       }
+      o = Or / Lr;
     }
-    __syncthreads();
+    *reinterpret_cast<f32x4*>(xs + i) = o;
   }
 }
 
-// logits -> per-workgroup (max, lowest index) after phase LM's GEMV.
-__device__ __forceinline__ void lm_finish(const Params& P, float best, int bidx, const Lds& S) {
-  float* bv = S.red;
-  int* bi = S.si;
-  if ((threadIdx.x & 63) == 0) { bv[threadIdx.x >> 6] = best; bi[threadIdx.x >> 6] = bidx; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float v = bv[0];
-    int ix = bi[0];
-    for (int w = 1; w < kWaves; ++w)
-      if (bv[w] > v || (bv[w] == v && bi[w] < ix)) { v = bv[w]; ix = bi[w]; }
-    st_coh(P.amax_v + blockIdx.x, v);
-    st_coh(P.amax_i + blockIdx.x, ix);
+// ---------------------------------------------------------------------------
+// wave 0: phase outputs
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, const int* tab_wg, bool want_logits,
+                                                 const float* out, float* xown) {
+  const int lane = threadIdx.x & 63;
+  if (!is_gemv(ph)) return;
+  struct { int p0; } w{rfl(tab_wg[2 * ph])};
+  const int n = rfl(tab_wg[2 * ph + 1]) - w.p0;
+  if (ph == PH_QKV) {
+    for (int t = lane; t < 2 * n; t += 64) st_coh(P.qkv + 2 * w.p0 + t, out[t]);
+  } else if (ph == PH_O || ph == PH_DOWN) {
+    for (int t = lane; t < 2 * n; t += 64) {
+      xown[t] += out[t];
+      st_coh(P.x + 2 * w.p0 + t, xown[t]);
+    }
+  } else if (ph == PH_GU) {
+    for (int t = lane; t < n; t += 64) {
+      const float gt = out[2 * t], up = out[2 * t + 1];
+      st_coh(P.act + w.p0 + t, gt / (1.0f + expf(-gt)) * up);
+    }
+  } else if (ph == PH_LM) {
+    float best = -INFINITY;
+    int bidx = 0x7fffffff;
+    for (int t = lane; t < 2 * n; t += 64) {
+      const float v = out[t];
+      if (v > best) { best = v; bidx = 2 * w.p0 + t; }
+      if (want_logits) P.logits[2 * w.p0 + t] = v;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(best, off, 64);
+      const int oi = __shfl_xor(bidx, off, 64);
+      if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
+    }
+    if (lane == 0) {
+      st_coh(P.amax_v + blockIdx.x, best);
+      st_coh(P.amax_i + blockIdx.x, bidx);
+    }
   }
 }
 
 // Greedy token = argmax over the workgroups' partials (lowest index on ties).
 // Every workgroup computes it (it is the next token's input); workgroup 0
 // publishes it.
-__device__ __forceinline__ int phase_argmax(const Params& P, int i, const Lds& S) {
-  float* v = S.aux;
-  int* ix = reinterpret_cast<int*>(S.aux + 1024);
-  const int G = gridDim.x;
-  for (int t = threadIdx.x; t < G; t += kThreads) { v[t] = ld_coh(P.amax_v + t); ix[t] = ld_coh(P.amax_i + t); }
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    float bvv = -INFINITY;
-    int bii = 0x7fffffff;
-    for (int t = threadIdx.x; t < G; t += 64)
-      if (v[t] > bvv || (v[t] == bvv && ix[t] < bii)) { bvv = v[t]; bii = ix[t]; }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bvv, off, 64);
-      const int oi = __shfl_xor(bii, off, 64);
-      if (ov > bvv || (ov == bvv && oi < bii)) { bvv = ov; bii = oi; }
-    }
-    if (threadIdx.x == 0) {
-      const int tok = (bii == 0x7fffffff) ? 0 : bii;
-      S.si[8] = tok;
-      if (blockIdx.x == 0) { st_coh(P.tok_cur, tok); st_coh(P.tok_out + i, tok); }
-    }
+__device__ __forceinline__ int w0_argmax(const Params& P, int i) {
+  const int lane = threadIdx.x & 63, G = gridDim.x;
+  float bvv = -INFINITY;
+  int bii = 0x7fffffff;
+  for (int t = lane; t < G; t += 64) {
+    const float v = ld_coh(P.amax_v + t);
+    const int ix = ld_coh(P.amax_i + t);
+    if (v > bvv || (v == bvv && ix < bii)) { bvv = v; bii = ix; }
   }
-  __syncthreads();
-  return S.si[8];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bvv, off, 64);
+    const int oi = __shfl_xor(bii, off, 64);
+    if (ov > bvv || (ov == bvv && oi < bii)) { bvv = ov; bii = oi; }
+  }
+  const int tok = (bii == 0x7fffffff) ? 0 : bii;
+  if (blockIdx.x == 0 && lane == 0) { st_coh(P.tok_cur, tok); st_coh(P.tok_out + i, tok); }
+  return tok;
 }
 
-template <int HD>
-__device__ __forceinline__ void attn_dispatch(const Params& P, int l, int pos, int aw, const Lds& S) {
-  if (aw == 4) phase_attn<HD, 4>(P, l, pos, S);
-  else phase_attn<HD, kWaves>(P, l, pos, S);
-}
+// ---------------------------------------------------------------------------
+// the resident kernel
+// ---------------------------------------------------------------------------
+// Both roles walk the same phase sequence and meet at the same workgroup
+// barriers: S1 (phase input in LDS; wave 0 has passed the grid barrier),
+// for O also after the attention merge, and S2 (phase outputs in LDS).
 
-// Attention positions per chunk up to which four waves compute it (and the
-// other four prefetch the O projection meanwhile).
-constexpr int kAttnNarrow = 64;
+// Streamer role (waves 1..7): kBlocksInFlight loads always in flight, in
+// stream order.  Every phase is a whole number of groups of kUnitsInFlight
+// units (zero-reading units pad it), so unit k of each group always sits in
+// register slot k: the steps below are unrolled over the slots and never
+// copy a register that a load is still filling.
+__device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, int g0, int g1, const int* tab,
+                                              float* xs, float* out, const int* si) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t lane16 = (uint32_t)lane * 16u;
+  const float* xl = xs + 8 * lane;
+  Cursor cu;
+  cursor_start(P, A, g0, g1, tab, cu);
+  u32x4 buf[kBlocksInFlight];
+#pragma unroll
+  for (int k = 0; k < kUnitsInFlight; ++k) issue_unit(cu, lane16, buf[2 * k], buf[2 * k + 1]);
+  PhaseIt id = phase_at(P, A, g0);
+  for (; id.g < g1; phase_next(P, A, id)) {
+    if (id.ph == -2) continue;
+    __syncthreads();   // S1
+    if (si[12] == 0) break;
+    if (id.ph == PH_O) {
+      merge_attention(P, A.pos0 + id.i, xs);
+      __syncthreads();
+    }
+    if (is_gemv(id.ph)) {
+      const int* e = tab + id.ph * kTabStride;
+      const int n = rfl(e[T_LEFT]);
+      const int ngroups = (n + rfl(e[T_PAD])) / kUnitsInFlight;
+      const int npc = rfl(e[T_NPC]);
+      int t = rfl(e[T_T0]), col = rfl(e[T_COL]);
+      float a0 = 0.f, a1 = 0.f;
+      int u = 0;
+      for (int grp = 0; grp < ngroups; ++grp) {
+        // the issue side runs one group ahead; phases hold whole groups, so
+        // it can only reach the end of its phase here
+        if (cu.left == 0 && cu.pad == 0 && cu.it.g < g1) cursor_next(P, A, g1, tab, cu);
+#pragma unroll
+        for (int k = 0; k < kUnitsInFlight; ++k) {
+          wait_vm<kBlocksInFlight - 2>();
+          if (u < n) {
+            const f32x4 xa = *reinterpret_cast<const f32x4*>(xl + 512 * col);
+            const f32x4 xb = *reinterpret_cast<const f32x4*>(xl + 512 * col + 4);
+            a0 = dot8(buf[2 * k], xa, xb, a0);
+            a1 = dot8(buf[2 * k + 1], xa, xb, a1);
+            if (col == npc - 1 || u == n - 1) {
+              const float y0 = wave_sum(a0), y1 = wave_sum(a1);
+              if (lane == 0) {
+                lds_add(out + 2 * t, y0);
+                lds_add(out + 2 * t + 1, y1);
+              }
+              a0 = a1 = 0.f;
+              ++t;
+            }
+            if (++col == npc) col = 0;
+          }
+          ++u;
+          issue_unit(cu, lane16, buf[2 * k], buf[2 * k + 1]);
+        }
+      }
+    }
+    __syncthreads();   // S2
+  }
+  wait_vm0();   // the zero-filled loads past the stream's end
+}
 
 extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident(const Params* __restrict__ Pp, Launch A) {
   const Params& P = *Pp;
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  Lds S;
-  S.xs = smem;
-  S.red = smem + kLdsRed;
-  S.si = reinterpret_cast<int*>(smem + kLdsSi);
-  S.aux = smem + kLdsAux;
-  S.pf = smem + kLdsPf;
-  const int wave = threadIdx.x >> 6;
-  const int L = P.L, d = P.d;
-  const int ppt = phases_per_token(L);
-  const int nlayer_ph = kPhasesPerLayer * L;
-  const long long total = (long long)A.n_tok * ppt;
-  const long long g0 = A.phase_begin < 0 ? 0 : A.phase_begin;
-  const long long g1 = (long long)A.phase_end < total ? (long long)A.phase_end : total;
-  uint32_t epoch = A.bar_base;
-  bool first = true, have_tok = false;
-  int tok_local = 0;
-  int n_store = kWaves;    // waves with coherent stores pending from the previous phase
-  long long pf_for = -1;   // global index of the phase whose first weight blocks sit in S.pf
+  float* xs = smem;
+  float* out = smem + kLdsOut;
+  float* xown = smem + kLdsOwn;
+  int* si = reinterpret_cast<int*>(smem + kLdsSi);
+  float* aux = smem + kLdsAux;
+  int* tab_wg = reinterpret_cast<int*>(smem + kLdsTabWg);
+  // wave index through readfirstlane: provably uniform, so the role split
+  // below is a scalar branch and every per-wave value stays in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  int* tab = reinterpret_cast<int*>(smem + kLdsTab) + (wave > 0 ? (wave - 1) * 6 * kTabStride : 0);
+  const int total = A.n_tok * phases_per_token(P.L);
+  const int g0 = A.phase_begin < 0 ? 0 : A.phase_begin;
+  const int g1 = A.phase_end < total ? A.phase_end : total;
+
+  fill_tables(P, wave, tab_wg, tab);
+  wait_lgkm0();
+  if (wave > 0) {
+    streamer_role(P, A, g0, g1, tab, xs, out, si);
+    return;
+  }
+
+  // wave 0: control
   uint64_t* trace = P.trace ? P.trace + (size_t)blockIdx.x * P.trace_stride : nullptr;
   int ev = 0;
   auto stamp = [&]() {
-    if (trace && threadIdx.x == 0 && ev < P.trace_stride) trace[ev] = wall_clock64();
+    if (trace && lane == 0 && ev < P.trace_stride) trace[ev] = wall_clock64();
     ++ev;
   };
-  for (long long g = g0; g < g1; ++g) {
-    const int i = (int)(g / ppt), k = (int)(g % ppt);
-    const bool lm = !A.lm_last_only || i == A.n_tok - 1;
-    if (k >= nlayer_ph && !lm) continue;
-    const int pos = A.pos0 + i;
-    const int l = k < nlayer_ph ? k / kPhasesPerLayer : 0;
-    const int ph = k < nlayer_ph ? k % kPhasesPerLayer : (k == nlayer_ph ? (int)PH_LM : -1);
-    const bool is_gemv = ph == PH_QKV || ph == PH_O || ph == PH_GU || ph == PH_DOWN || ph == PH_LM;
-    const bool skip_bar = first || (k == 0 && have_tok);
-    bool ok = true;
+  {
+    // this workgroup's rows of the residual stream
+    int b, e;
+    split(P.d / 2, blockIdx.x, gridDim.x, b, e);
+    for (int r = 2 * b + lane; r < 2 * e; r += 64) xown[r - 2 * b] = ld_coh(P.x + r);
+  }
+  uint32_t epoch = A.bar_base;
+  bool first = true, have_tok = false;
+  int tok_local = 0;
+  int prev_ph = -3, prev_i = 0;
+  PhaseIt id = phase_at(P, A, g0);
+  for (; id.g < g1; phase_next(P, A, id)) {
+    if (id.ph == -2) continue;
+    const int pos = A.pos0 + id.i;
+    // outputs of the previous phase; this phase's LDS results start at zero
+    if (!first) w0_store_outputs(P, prev_ph, tab_wg, A.write_logits && prev_i == A.n_tok - 1, out, xown);
+    if (is_gemv(id.ph)) {
+      const int np = rfl(tab_wg[2 * id.ph + 1]) - rfl(tab_wg[2 * id.ph]);
+      for (int t = lane; t < 2 * np; t += 64) out[t] = 0.f;
+    }
+    const bool skip_bar = first || (id.ph == PH_QKV && id.l == 0 && have_tok);
     if (!skip_bar) {
       ++epoch;
-      barrier_arrive(P, epoch, A.fenced, n_store);
-      if (is_gemv && pf_for != g) {
-        prefetch_issue(work_of(P, ph, l), S.pf, 1);
-        pf_for = g;
-      }
-      if (wave == 0) ok = barrier_wait(P, epoch, A.fenced);
+      w0_arrive(P, A.fenced);
     }
-    first = false;
-    // prologue: wave 0 brings this phase's input vector into LDS
-    int tok = 0;
-    if (ph == PH_QKV && l == 0) {
-      if (A.tok_src == TOK_PROMPT) tok = P.prompt[i];
+    auto wait = [&]() { return skip_bar ? true : w0_wait(P, epoch, A.fenced); };
+    bool ok = true;
+    if (id.ph == PH_ATTN) {
+      switch (P.hd) {
+        case 8: ok = w0_attention<8>(P, id.l, pos, aux, wait); break;
+        case 16: ok = w0_attention<16>(P, id.l, pos, aux, wait); break;
+        case 32: ok = w0_attention<32>(P, id.l, pos, aux, wait); break;
+        case 64: ok = w0_attention<64>(P, id.l, pos, aux, wait); break;
+        default: ok = w0_attention<128>(P, id.l, pos, aux, wait); break;
+      }
+    } else if (id.ph == PH_QKV && id.l == 0) {
+      int tok;
+      if (A.tok_src == TOK_PROMPT) tok = ldg(P.prompt + id.i);
       else tok = have_tok ? tok_local : ld_coh(P.tok_cur);
       have_tok = false;
       tok = tok < 0 ? 0 : (tok >= P.V ? P.V - 1 : tok);
-    }
-    if (wave == 0) {
-      if (ph == PH_QKV) {
-        if (l == 0) w0_embed(P, tok, S.xs, P.gains);
-        else w0_load_vec(S.xs, P.x, d, P.gains + (size_t)l * 2 * d, P.eps);
-      } else if (ph == PH_O) {
-        w0_load_vec(S.xs, P.attn_o, P.q, nullptr, 0.f);
-      } else if (ph == PH_GU) {
-        w0_load_vec(S.xs, P.x, d, P.gains + (size_t)l * 2 * d + d, P.eps);
-      } else if (ph == PH_DOWN) {
-        w0_load_vec(S.xs, P.act, P.F, nullptr, 0.f);
-      } else if (ph == PH_LM) {
-        w0_load_vec(S.xs, P.x, d, P.gains + (size_t)L * 2 * d, P.eps);
+      ok = wait();
+      if (ok) w0_embed(P, tok, xs, xown, P.gains);
+    } else if (id.ph == PH_QKV || id.ph == PH_GU || id.ph == PH_LM) {
+      const float* gp = P.gains + (id.ph == PH_LM ? (size_t)P.L * 2 * P.d
+                                                  : (size_t)id.l * 2 * P.d + (id.ph == PH_GU ? P.d : 0));
+      f32x4 gv[kGainRegs];
+      w0_gains(gp, P.d, gv);
+      ok = wait();
+      if (ok) w0_load_vec(xs, P.x, P.d, gp, gv, P.eps);
+    } else if (id.ph == PH_DOWN) {
+      f32x4 gv[kGainRegs];
+      w0_gains(nullptr, 0, gv);
+      ok = wait();
+      if (ok) w0_load_vec(xs, P.act, P.F, nullptr, gv, 0.f);
+    } else if (id.ph == PH_O) {
+      ok = wait();
+    } else {
+      ok = wait();
+      if (ok) {
+        tok_local = w0_argmax(P, id.i);
+        have_tok = true;
       }
-      if (threadIdx.x == 0) S.si[12] = ok ? 1 : 0;
-    } else if (is_gemv) {
-      wait_vm0();   // this wave's prefetch blocks have landed
     }
-    __syncthreads();
-    if (S.si[12] == 0) {
+    if (lane == 0) si[12] = ok ? 1 : 0;
+    first = false;
+    __syncthreads();   // S1
+    if (!ok) {
       wait_vm0();
       return;
     }
-    stamp();
-    const bool use_pf = pf_for == g;
-    const float* pf = use_pf ? S.pf : nullptr;
-    n_store = kWaves;
-    if (ph == PH_QKV) {
-      float* out = P.qkv;
-      auto epi = [out](int pr, float y0, float y1, int lane) {
-        if (lane == 0) { st_coh(out + 2 * pr, y0); st_coh(out + 2 * pr + 1, y1); }
-      };
-      gemv(work_of(P, PH_QKV, l), S.xs, pf, epi);
-    } else if (ph == PH_ATTN) {
-      const int ctx = pos + 1;
-      const int C = attn_chunks(ctx, P.H, gridDim.x);
-      const int aw = (ctx + C - 1) / C <= kAttnNarrow ? 4 : kWaves;
-      if (aw == 4) {
-        // the other four waves prefetch the O projection meanwhile
-        prefetch_issue(work_of(P, PH_O, l), S.pf, 4);
-        pf_for = g + 1;
-        n_store = 4;
-      }
-      switch (P.hd) {
-        case 8: attn_dispatch<8>(P, l, pos, aw, S); break;
-        case 16: attn_dispatch<16>(P, l, pos, aw, S); break;
-        case 32: attn_dispatch<32>(P, l, pos, aw, S); break;
-        case 64: attn_dispatch<64>(P, l, pos, aw, S); break;
-        default: attn_dispatch<128>(P, l, pos, aw, S); break;
-      }
-    } else if (ph == PH_O || ph == PH_DOWN) {
-      float* x = P.x;
-      auto epi = [x](int pr, float y0, float y1, int lane) {
-        if (lane == 0) {
-          st_coh(x + 2 * pr, ld_coh(x + 2 * pr) + y0);
-          st_coh(x + 2 * pr + 1, ld_coh(x + 2 * pr + 1) + y1);
-        }
-      };
-      gemv(work_of(P, ph, l), S.xs, pf, epi);
-    } else if (ph == PH_GU) {
-      float* act = P.act;
-      auto epi = [act](int pr, float gt, float up, int lane) {
-        if (lane == 0) st_coh(act + pr, gt / (1.0f + expf(-gt)) * up);
-      };
-      gemv(work_of(P, PH_GU, l), S.xs, pf, epi);
-    } else if (ph == PH_LM) {
-      float best = -INFINITY;
-      int bidx = 0x7fffffff;
-      float* lgp = (A.write_logits && i == A.n_tok - 1) ? P.logits : nullptr;
-      auto epi = [&best, &bidx, lgp](int pr, float y0, float y1, int lane) {
-        if (y0 > best) { best = y0; bidx = 2 * pr; }
-        if (y1 > best) { best = y1; bidx = 2 * pr + 1; }
-        if (lgp != nullptr && lane == 0) { lgp[2 * pr] = y0; lgp[2 * pr + 1] = y1; }
-      };
-      gemv(work_of(P, PH_LM, 0), S.xs, pf, epi);
-      lm_finish(P, best, bidx, S);
-    } else {
-      tok_local = phase_argmax(P, i, S);
-      have_tok = true;
+    if (id.ph == PH_O) {
+      merge_attention(P, pos, xs);
+      __syncthreads();
     }
     stamp();
+    __syncthreads();   // S2
+    stamp();
+    prev_ph = id.ph;
+    prev_i = id.i;
   }
-  wait_vm0();   // no LDS-direct load may outlive the workgroup
+  if (!first) w0_store_outputs(P, prev_ph, tab_wg, A.write_logits && prev_i == A.n_tok - 1, out, xown);
+  wait_vm0();
 }
 
 int kernel_prepare() {
