@@ -84,6 +84,8 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--multilaunch", action="store_true", help="one kernel launch per phase (comparison)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run plain device-to-device copies of BYTES (HBM counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -94,6 +96,17 @@ def main():
     import numpy as np
     import torch
     import synth
+
+    if args.copy_calibration:
+        # a plain copy kernel of known size: reads and writes BYTES once per call
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "calls": 3}), flush=True)
+        return
     from memory_bound_transformer_persistent_amd import binding as B
     from memory_bound_transformer_persistent_amd import roofline as R
 
