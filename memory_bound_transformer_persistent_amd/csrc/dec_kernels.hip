@@ -47,12 +47,13 @@ constexpr int kStreamers = kWaves - 1;
 // Units (two 1 KB weight blocks) each streamer keeps in flight: 16-byte loads
 // per lane land in registers, so a wave's LDS reads never queue behind its
 // own weight traffic.
-constexpr int kUnitsInFlight = 6;
+constexpr int kUnitsInFlight = 4;
 constexpr int kBlocksInFlight = 2 * kUnitsInFlight;
-// LDS map (floats): xs | out | xown | red | si | aux | phase tables
+// LDS map (floats): xs | out | xown | red | si | aux | gains | phase tables
 constexpr int kAuxFloats = 2048;
 constexpr int kLdsOut = kMaxK, kLdsOwn = kLdsOut + kOutFloats, kLdsRed = kLdsOwn + kOwnFloats;
-constexpr int kLdsSi = kLdsRed + 64, kLdsAux = kLdsSi + 16, kLdsTables = kLdsAux + kAuxFloats;
+constexpr int kLdsSi = kLdsRed + 64, kLdsAux = kLdsSi + 16, kLdsGain = kLdsAux + kAuxFloats;
+constexpr int kLdsTables = kLdsGain + kMaxK;
 constexpr int kWaitVm0 = 0x0F70;             // s_waitcnt vmcnt(0), expcnt/lgkmcnt untouched
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -68,6 +69,10 @@ __device__ __forceinline__ u32x4 ld_kv(rsrc_t r, uint32_t off) {
 // base), coherent at device scope (activations written by other workgroups).
 __device__ __forceinline__ void dma16_coh(rsrc_t r, float* lds_base, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, off, 0, 0, kAuxSc1);
+}
+// Same for read-only data.
+__device__ __forceinline__ void dma16_ld(rsrc_t r, float* lds_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, off, 0, 0, 0);
 }
 __device__ __forceinline__ void wait_vm0() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -419,52 +424,44 @@ __device__ __forceinline__ bool w0_wait(const Params& P, uint32_t epoch, int fen
 // ---------------------------------------------------------------------------
 // wave 0: phase inputs
 // ---------------------------------------------------------------------------
-constexpr int kGainRegs = 12;   // f32x4 of norm gains held per lane (d <= 3072 in one batch)
+// RMSNorm is split so that no wave waits on a reduction before the GEMV:
+// wave 0 lands the raw vector in xs and the norm gains in gs (LDS DMA); all
+// waves then form xs = x * g and their shares of sum(x^2); the scalar
+// 1/sqrt(mean(x^2) + eps) multiplies the phase's outputs when wave 0
+// publishes them, since W (x g s) = s W (x g).
 
-// Norm gains g[0..n) for w0_load_vec, loaded early (before the barrier poll).
-__device__ __forceinline__ void w0_gains(const float* g, int n, f32x4 (&gv)[kGainRegs]) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int t = 0; t < kGainRegs; ++t) {
-    const int i = 256 * t + 4 * lane;
-    gv[t] = (g != nullptr && i < n) ? ldg4(g + i) : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-}
-
-// xs[0..gemv_span(n)) <- src[0..n) (coherent, zero past n); with g set,
-// xs = src / sqrt(mean(src^2) + eps) * g (gv: g's first kGainRegs*256 values).
-__device__ __forceinline__ void w0_load_vec(float* xs, const float* src, int n, const float* g,
-                                            const f32x4 (&gv)[kGainRegs], float eps) {
+// dst[0..gemv_span(n)) <- src[0..n) by LDS DMA (coherent when coh; zero past n).
+// Issues only; the caller waits.
+__device__ __forceinline__ void w0_dma_vec(float* dst, const float* src, int n, bool coh) {
   const int lane = threadIdx.x & 63;
   const rsrc_t r = make_rsrc(src, (uint32_t)n * 4u);
   const int span = gemv_span(n);
-  for (int i = 0; i < span; i += 256) dma16_coh(r, xs + i, (uint32_t)(i + 4 * lane) * 4u);
-  wait_vm0();
-  if (g == nullptr) return;
-  float ss = 0.f;
-  for (int i = 4 * lane; i < n; i += 256) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(xs + i);
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  for (int i = 0; i < span; i += 256) {
+    if (coh) dma16_coh(r, dst + i, (uint32_t)(i + 4 * lane) * 4u);
+    else dma16_ld(r, dst + i, (uint32_t)(i + 4 * lane) * 4u);
   }
-  const float s = 1.0f / sqrtf(wave_sum(ss) / (float)n + eps);
-#pragma unroll
-  for (int t = 0; t < kGainRegs; ++t) {
-    const int i = 256 * t + 4 * lane;
-    if (i < n) *reinterpret_cast<f32x4*>(xs + i) = *reinterpret_cast<const f32x4*>(xs + i) * s * gv[t];
-  }
-  for (int i = 256 * kGainRegs + 4 * lane; i < n; i += 256)
-    *reinterpret_cast<f32x4*>(xs + i) = *reinterpret_cast<const f32x4*>(xs + i) * s * ldg4(g + i);
 }
 
-// Layer-0 input: x = E[tok] (fp16 -> fp32).  This workgroup's rows of x go to
-// xown and to global x; xs gets rmsnorm(x) * g.
-__device__ __forceinline__ void w0_embed(const Params& P, int tok, float* xs, float* xown, const float* g) {
+// All waves: xs[0..n) *= gs[0..n); red[wave] <- this wave's share of sum(x^2).
+__device__ __forceinline__ void apply_gains(float* xs, const float* gs, int n, float* red) {
+  float ss = 0.f;
+  for (int i = 4 * (int)threadIdx.x; i < n; i += 4 * kThreads) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(xs + i);
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    *reinterpret_cast<f32x4*>(xs + i) = v * *reinterpret_cast<const f32x4*>(gs + i);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+}
+
+// Layer-0 input: x = E[tok] (fp16 -> fp32) into xs (raw, zero past d).  This
+// workgroup's rows of x go to xown and to global x.
+__device__ __forceinline__ void w0_embed(const Params& P, int tok, float* xs, float* xown) {
   const int lane = threadIdx.x & 63, d = P.d;
   const _Float16* e = reinterpret_cast<const _Float16*>(P.w + P.off_E + (size_t)tok * d);
   int b, en;
   split(d / 2, blockIdx.x, gridDim.x, b, en);
   const int span = gemv_span(d);
-  float ss = 0.f;
   for (int i = 8 * lane; i < span; i += 512) {
     f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
     if (i < d) {
@@ -474,16 +471,12 @@ __device__ __forceinline__ void w0_embed(const Params& P, int tok, float* xs, fl
     }
     *reinterpret_cast<f32x4*>(xs + i) = lo;
     *reinterpret_cast<f32x4*>(xs + i + 4) = hi;
-    ss += lo[0] * lo[0] + lo[1] * lo[1] + lo[2] * lo[2] + lo[3] * lo[3] +
-          hi[0] * hi[0] + hi[1] * hi[1] + hi[2] * hi[2] + hi[3] * hi[3];
   }
+  wait_lgkm0();
   for (int r = 2 * b + lane; r < 2 * en; r += 64) {
     xown[r - 2 * b] = xs[r];
     st_coh(P.x + r, xs[r]);
   }
-  const float s = 1.0f / sqrtf(wave_sum(ss) / (float)d + P.eps);
-  for (int i = 4 * lane; i < d; i += 256)
-    *reinterpret_cast<f32x4*>(xs + i) = *reinterpret_cast<const f32x4*>(xs + i) * s * ldg4(g + i);
 }
 
 // ---------------------------------------------------------------------------
@@ -668,13 +661,13 @@ __device__ __forceinline__ void merge_attention(const Params& P, int pos, float*
 // wave 0: phase outputs
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, const int* tab_wg, bool want_logits,
-                                                 const float* out, float* xown) {
+                                                 float scale, const float* out, float* xown) {
   const int lane = threadIdx.x & 63;
   if (!is_gemv(ph)) return;
   struct { int p0; } w{rfl(tab_wg[2 * ph])};
   const int n = rfl(tab_wg[2 * ph + 1]) - w.p0;
   if (ph == PH_QKV) {
-    for (int t = lane; t < 2 * n; t += 64) st_coh(P.qkv + 2 * w.p0 + t, out[t]);
+    for (int t = lane; t < 2 * n; t += 64) st_coh(P.qkv + 2 * w.p0 + t, out[t] * scale);
   } else if (ph == PH_O || ph == PH_DOWN) {
     for (int t = lane; t < 2 * n; t += 64) {
       xown[t] += out[t];
@@ -682,14 +675,14 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, const 
     }
   } else if (ph == PH_GU) {
     for (int t = lane; t < n; t += 64) {
-      const float gt = out[2 * t], up = out[2 * t + 1];
+      const float gt = out[2 * t] * scale, up = out[2 * t + 1] * scale;
       st_coh(P.act + w.p0 + t, gt / (1.0f + expf(-gt)) * up);
     }
   } else if (ph == PH_LM) {
     float best = -INFINITY;
     int bidx = 0x7fffffff;
     for (int t = lane; t < 2 * n; t += 64) {
-      const float v = out[t];
+      const float v = out[t] * scale;
       if (v > best) { best = v; bidx = 2 * w.p0 + t; }
       if (want_logits) P.logits[2 * w.p0 + t] = v;
     }
@@ -741,8 +734,17 @@ __device__ __forceinline__ int w0_argmax(const Params& P, int i) {
 // units (zero-reading units pad it), so unit k of each group always sits in
 // register slot k: the steps below are unrolled over the slots and never
 // copy a register that a load is still filling.
+// Phases whose input is rmsnorm(x) * g, and their g.
+__device__ __forceinline__ bool norm_phase(const PhaseIt& id) {
+  return id.ph == PH_QKV || id.ph == PH_GU || id.ph == PH_LM;
+}
+__device__ __forceinline__ const float* norm_gains(const Params& P, const PhaseIt& id) {
+  if (id.ph == PH_LM) return P.gains + (size_t)P.L * 2 * P.d;
+  return P.gains + (size_t)id.l * 2 * P.d + (id.ph == PH_GU ? P.d : 0);
+}
+
 __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, int g0, int g1, const int* tab,
-                                              float* xs, float* out, const int* si) {
+                                              float* xs, float* out, const float* gs, float* red, const int* si) {
   const int lane = threadIdx.x & 63;
   const uint32_t lane16 = (uint32_t)lane * 16u;
   const float* xl = xs + 8 * lane;
@@ -754,12 +756,11 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
   PhaseIt id = phase_at(P, A, g0);
   for (; id.g < g1; phase_next(P, A, id)) {
     if (id.ph == -2) continue;
-    __syncthreads();   // S1
+    __syncthreads();   // S1a
     if (si[12] == 0) break;
-    if (id.ph == PH_O) {
-      merge_attention(P, A.pos0 + id.i, xs);
-      __syncthreads();
-    }
+    if (norm_phase(id)) apply_gains(xs, gs, P.d, red);
+    if (id.ph == PH_O) merge_attention(P, A.pos0 + id.i, xs);
+    __syncthreads();   // S1
     if (is_gemv(id.ph)) {
       const int* e = tab + id.ph * kTabStride;
       const int n = rfl(e[T_LEFT]);
@@ -809,6 +810,8 @@ extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident(const Par
   float* xown = smem + kLdsOwn;
   int* si = reinterpret_cast<int*>(smem + kLdsSi);
   float* aux = smem + kLdsAux;
+  float* gs = smem + kLdsGain;
+  float* red = smem + kLdsRed;
   int* tab_wg = reinterpret_cast<int*>(smem + kLdsTabWg);
   // wave index through readfirstlane: provably uniform, so the role split
   // below is a scalar branch and every per-wave value stays in SGPRs
@@ -821,7 +824,7 @@ extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident(const Par
   fill_tables(P, wave, tab_wg, tab);
   wait_lgkm0();
   if (wave > 0) {
-    streamer_role(P, A, g0, g1, tab, xs, out, si);
+    streamer_role(P, A, g0, g1, tab, xs, out, gs, red, si);
     return;
   }
 
@@ -842,12 +845,13 @@ extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident(const Par
   bool first = true, have_tok = false;
   int tok_local = 0;
   int prev_ph = -3, prev_i = 0;
+  float prev_scale = 1.0f;
   PhaseIt id = phase_at(P, A, g0);
   for (; id.g < g1; phase_next(P, A, id)) {
     if (id.ph == -2) continue;
     const int pos = A.pos0 + id.i;
     // outputs of the previous phase; this phase's LDS results start at zero
-    if (!first) w0_store_outputs(P, prev_ph, tab_wg, A.write_logits && prev_i == A.n_tok - 1, out, xown);
+    if (!first) w0_store_outputs(P, prev_ph, tab_wg, A.write_logits && prev_i == A.n_tok - 1, prev_scale, out, xown);
     if (is_gemv(id.ph)) {
       const int np = rfl(tab_wg[2 * id.ph + 1]) - rfl(tab_wg[2 * id.ph]);
       for (int t = lane; t < 2 * np; t += 64) out[t] = 0.f;
@@ -858,6 +862,8 @@ extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident(const Par
       w0_arrive(P, A.fenced);
     }
     auto wait = [&]() { return skip_bar ? true : w0_wait(P, epoch, A.fenced); };
+    // the norm gains do not depend on the barrier: start them first
+    if (norm_phase(id)) w0_dma_vec(gs, norm_gains(P, id), P.d, false);
     bool ok = true;
     if (id.ph == PH_ATTN) {
       switch (P.hd) {
@@ -874,19 +880,13 @@ extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident(const Par
       have_tok = false;
       tok = tok < 0 ? 0 : (tok >= P.V ? P.V - 1 : tok);
       ok = wait();
-      if (ok) w0_embed(P, tok, xs, xown, P.gains);
+      if (ok) w0_embed(P, tok, xs, xown);
     } else if (id.ph == PH_QKV || id.ph == PH_GU || id.ph == PH_LM) {
-      const float* gp = P.gains + (id.ph == PH_LM ? (size_t)P.L * 2 * P.d
-                                                  : (size_t)id.l * 2 * P.d + (id.ph == PH_GU ? P.d : 0));
-      f32x4 gv[kGainRegs];
-      w0_gains(gp, P.d, gv);
       ok = wait();
-      if (ok) w0_load_vec(xs, P.x, P.d, gp, gv, P.eps);
+      if (ok) w0_dma_vec(xs, P.x, P.d, true);
     } else if (id.ph == PH_DOWN) {
-      f32x4 gv[kGainRegs];
-      w0_gains(nullptr, 0, gv);
       ok = wait();
-      if (ok) w0_load_vec(xs, P.act, P.F, nullptr, gv, 0.f);
+      if (ok) w0_dma_vec(xs, P.act, P.F, true);
     } else if (id.ph == PH_O) {
       ok = wait();
     } else {
@@ -896,24 +896,29 @@ extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident(const Par
         have_tok = true;
       }
     }
+    wait_vm0();   // the phase input has landed in LDS
     if (lane == 0) si[12] = ok ? 1 : 0;
     first = false;
+    __syncthreads();   // S1a
+    if (!ok) return;
+    if (norm_phase(id)) apply_gains(xs, gs, P.d, red);
+    if (id.ph == PH_O) merge_attention(P, pos, xs);
     __syncthreads();   // S1
-    if (!ok) {
-      wait_vm0();
-      return;
-    }
-    if (id.ph == PH_O) {
-      merge_attention(P, pos, xs);
-      __syncthreads();
+    float scale = 1.0f;
+    if (norm_phase(id)) {
+      float ss = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) ss += red[w];
+      scale = 1.0f / sqrtf(ss / (float)P.d + P.eps);
     }
     stamp();
     __syncthreads();   // S2
     stamp();
     prev_ph = id.ph;
     prev_i = id.i;
+    prev_scale = scale;
   }
-  if (!first) w0_store_outputs(P, prev_ph, tab_wg, A.write_logits && prev_i == A.n_tok - 1, out, xown);
+  if (!first) w0_store_outputs(P, prev_ph, tab_wg, A.write_logits && prev_i == A.n_tok - 1, prev_scale, out, xown);
   wait_vm0();
 }
 
