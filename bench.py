@@ -31,8 +31,9 @@ def kernel_hash():
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic(n_launch_bytes_unit):
-    """HBM bytes per launch from the committed PMC summary, if it matches this kernel."""
+def read_traffic(workload):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on
+    this kernel source and this workload."""
     if not os.path.exists(PROFILE_TRAFFIC):
         return None
     rec = {}
@@ -40,7 +41,7 @@ def read_traffic(n_launch_bytes_unit):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             rec[k.strip()] = v.strip()
-    if rec.get("kernel_sha") != kernel_hash():
+    if rec.get("kernel_sha") != kernel_hash() or rec.get("workload") != workload:
         return None
     try:
         return float(rec["hbm_bytes_per_launch"])
@@ -166,7 +167,7 @@ def main():
     tok_s = K / (region_ms / 1e3)
     achieved = bytes_per_launch / avg_launch_s / 1e9
     peak = R.MI355X_HBM_PEAK / 1e9
-    traffic = read_traffic(bytes_per_launch)
+    traffic = read_traffic(w.name) if args.mode == "step" and not args.multilaunch else None
     roof_tps = R.roofline_tokens_per_s(s, pos0, K)
 
     out = {

@@ -10,7 +10,7 @@ duration); and, for counter runs, each counter's per-dispatch value.
     python -m memory_bound_transformer_persistent_amd.profsum trace DIR
     python -m memory_bound_transformer_persistent_amd.profsum counters DIR [KERNEL]
     python -m memory_bound_transformer_persistent_amd.profsum traffic FETCH_DIR WRITE_DIR \\
-        COPY_FETCH_DIR COPY_WRITE_DIR COPY_BYTES KERNEL_SOURCE
+        COPY_FETCH_DIR COPY_WRITE_DIR COPY_BYTES KERNEL_SOURCE [WORKLOAD]
 
 The traffic mode turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) into HBM
 bytes per decode launch, scaled by what the same counters read for a plain
@@ -121,7 +121,7 @@ def largest_counter(d, counter):
     return per[k], k[1]
 
 
-def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes, kernel_src):
+def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes, kernel_src, workload="dense2b"):
     f_kib, nf = decode_counter(fetch_dir, "FETCH_SIZE")
     w_kib, nw = decode_counter(write_dir, "WRITE_SIZE")
     cf_kib, cname = largest_counter(cfetch_dir, "FETCH_SIZE")
@@ -132,6 +132,7 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes, kernel_src
     sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
     return "\n".join([
         f"kernel = {DECODE_KERNEL}",
+        f"workload = {workload}",
         f"kernel_sha = {sha}",
         f"decode_dispatches_fetch = {nf}",
         f"decode_dispatches_write = {nw}",
@@ -156,8 +157,8 @@ def main(argv):
             vals = list(v.values())
             s = _stats(vals)
             print(f"{c}: dispatches {s['n']}, median {s['median']:.1f}, min {s['min']:.1f}, max {s['max']:.1f}")
-    elif len(argv) == 7 and argv[0] == "traffic":
-        print(traffic(argv[1], argv[2], argv[3], argv[4], int(argv[5]), argv[6]))
+    elif len(argv) in (7, 8) and argv[0] == "traffic":
+        print(traffic(argv[1], argv[2], argv[3], argv[4], int(argv[5]), argv[6], *argv[7:]))
     else:
         print(__doc__)
         return 2
