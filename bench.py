@@ -4,7 +4,10 @@ Workload (default "dense2b"): a 25-layer dense decoder, d_model 2560, 20 heads
 x 128, SwiGLU 6912, vocab 65536, fp16 weights drawn N(0, 0.02) from fixed
 seeds; a 128-token random prompt is prefilled, then the timed region is the
 512 greedy decode steps at positions 128..639.  One step = one decode token
-= one pass over every active weight (the whole hot path).
+= one pass over every active weight (the whole hot path).  --workload
+dense2b_b8 decodes 8 independent sequences together (256-token prompts):
+`value` is then the whole-job tokens/s (8 per step) and
+tokens_per_s_per_request the rate each sequence sees.
 
 Prints one JSON line.  The roofline object prices the resident decode kernel
 against MI355X's 8 TB/s HBM peak with ALGORITHMIC bytes per launch: every
@@ -118,12 +121,13 @@ def main():
         sys.exit("prompt + steps exceed the context cap")
     t_gen = time.time()
     tensors = synth.workload_weights(w)
-    prompt = synth.make_prompt(s.vocab, w.prompt_len, seed=w.prompt_seed)[0]
+    nb = w.batch
+    prompt = synth.make_prompt(s.vocab, w.prompt_len, batch=nb, seed=w.prompt_seed)   # [batch, n]
     print(f"# weights generated in {time.time() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.Stream(device=0)
     flags = B.DEC_DEBUG_MULTILAUNCH if args.multilaunch else 0
-    dec = B.Decoder(B.ModelDesc.from_shape(s), tensors=tensors, device=0, stream=stream.cuda_stream,
+    dec = B.Decoder(B.ModelDesc.from_shape(s, batch=nb), tensors=tensors, device=0, stream=stream.cuda_stream,
                     debug_flags=flags)
 
     # warm-up: prefill + W steps, then rewind so the timed steps are the workload's positions
@@ -159,16 +163,17 @@ def main():
     region_ms = ev0.elapsed_time(ev1)
     if args.mode == "generate":
         launch_ms = [starts[0].elapsed_time(ends[0])]
-        bytes_per_launch = sum(R.step_bytes(s, pos0 + i).total for i in range(K))
+        bytes_per_launch = sum(R.step_bytes(s, pos0 + i, nb).total for i in range(K))
     else:
         launch_ms = [starts[i].elapsed_time(ends[i]) for i in range(K)]
-        bytes_per_launch = R.mean_step_bytes(s, pos0, K)
+        bytes_per_launch = R.mean_step_bytes(s, pos0, K, nb)
     avg_launch_s = float(np.mean(launch_ms)) / 1e3
-    tok_s = K / (region_ms / 1e3)
+    req_tok_s = K / (region_ms / 1e3)          # tokens/s of each sequence
+    tok_s = req_tok_s * nb                     # whole-job tokens/s
     achieved = bytes_per_launch / avg_launch_s / 1e9
     peak = R.MI355X_HBM_PEAK / 1e9
     traffic = read_traffic(w.name) if args.mode == "step" and not args.multilaunch else None
-    roof_tps = R.roofline_tokens_per_s(s, pos0, K)
+    roof_tps = R.roofline_tokens_per_s(s, pos0, K, nb)   # per request
 
     out = {
         "metric": METRIC,
@@ -184,8 +189,9 @@ def main():
         "dtype": "f32",
         "storage_dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: {w.description}; prompt {w.prompt_len} + {K} greedy decode steps, batch 1",
-                   "positions": [pos0, pos0 + K - 1], "mode": args.mode,
+        "config": {"workload": f"{w.name}: {w.description}; prompt {w.prompt_len} + {K} greedy decode steps, "
+                               f"batch {nb}",
+                   "batch": nb, "positions": [pos0, pos0 + K - 1], "mode": args.mode,
                    "launch": "one kernel launch per phase" if args.multilaunch else "resident kernel, grid barriers"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s",
                      "frac": round(achieved / peak, 4),
@@ -193,8 +199,10 @@ def main():
                      "kernel": "dec_resident",
                      "algorithmic_bytes_per_launch": int(bytes_per_launch),
                      "avg_launch_ms": round(avg_launch_s * 1e3, 4)},
-        "roofline_tokens_per_s": round(roof_tps, 1),
-        "hbm_GBps_per_step": round(R.mean_step_bytes(s, pos0, K) * tok_s / 1e9, 1),
+        "tokens_per_s_per_request": round(req_tok_s, 2),
+        "roofline_tokens_per_s": round(roof_tps * nb, 1),
+        "roofline_tokens_per_s_per_request": round(roof_tps, 1),
+        "hbm_GBps_per_step": round(R.mean_step_bytes(s, pos0, K, nb) * req_tok_s / 1e9, 1),
         "wall_s": round(wall, 3),
         "context": {"pages_8xMI300X_tokens_per_s": 3000, "pages_8xH200_tokens_per_s": 2100,
                     "note": "2B fp16, batch 1, 8 GPUs each: other hardware, context only"},

@@ -63,9 +63,19 @@ typedef enum dec_status {
  *   n_heads*head_dim may differ from d_model and must be a multiple of 8;
  *   d_ffn >= 8, a multiple of 8;
  *   1 <= lm_vocab <= vocab, lm_vocab even;
- *   1 <= max_ctx <= 65536; batch == 1 (batch > 1: DEC_ERR_UNSUPPORTED in this
- *   build); rms_eps > 0; rope_base > 1; flags == 0.
+ *   1 <= max_ctx <= 65536; batch >= 1; rms_eps > 0; rope_base > 1; flags == 0.
+ * Limits of this build (DEC_ERR_UNSUPPORTED): d_model, n_heads*head_dim and
+ * d_ffn <= 8192; batch <= 8; with batch > 1, d_model <= 2560 and d_ffn,
+ * n_heads*head_dim <= 7680 after rounding up to a multiple of 512 (every
+ * sequence's matrix-product input is held on chip, in fp16).
  * Shapes of the weight tensors follow from it (see dec_weights_src).
+ *
+ * Batch.  batch > 1 decodes that many independent sequences in lockstep (same
+ * position, one pass over the weights per step serves all of them); each has
+ * its own KV cache.  Sequence b's tokens and logits are the ones it would get
+ * alone, up to rounding: the batched kernel rounds each matrix product's input
+ * vector (x*g, the attention output, the SwiGLU output) to fp16, where the
+ * batch-1 kernel keeps it in fp32.
  */
 typedef struct dec_model_desc {
   int32_t n_layers;

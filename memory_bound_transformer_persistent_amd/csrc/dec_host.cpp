@@ -57,7 +57,14 @@ int check_desc_impl(const dec_model_desc* d, std::string* err) {
   if (d->batch < 1) return fail(err, DEC_ERR_BAD_DESC, "batch must be >= 1");
   const long long q = (long long)d->n_heads * hd;
   if (q % 8) return fail(err, DEC_ERR_BAD_DESC, "n_heads*head_dim must be a multiple of 8");
-  if (d->batch != 1) return fail(err, DEC_ERR_UNSUPPORTED, "batch > 1 is not implemented in this build");
+  if (d->batch > kMaxBatch) return fail(err, DEC_ERR_UNSUPPORTED, "batch must be <= %d", kMaxBatch);
+  if (d->batch > 1) {
+    auto span = [](long long k) { return (k + 511) / 512 * 512; };
+    if (span(d->d_model) > kBatchSpanD || span(d->d_ffn) > kBatchSpanK || span(q) > kBatchSpanK)
+      return fail(err, DEC_ERR_UNSUPPORTED,
+                  "batch > 1 needs d_model <= %d and d_ffn, n_heads*head_dim <= %d (inputs kept in LDS)",
+                  kBatchSpanD, kBatchSpanK);
+  }
   if (d->d_model > kMaxK || q > kMaxK || d->d_ffn > kMaxK)
     return fail(err, DEC_ERR_UNSUPPORTED, "d_model, n_heads*head_dim and d_ffn must be <= %d", kMaxK);
   // largest matrix must be addressable with 32-bit byte offsets
@@ -65,8 +72,9 @@ int check_desc_impl(const dec_model_desc* d, std::string* err) {
   const long long big = std::max({lm_bytes, 2LL * 3 * q * d->d_model, 2LL * 2 * d->d_ffn * d->d_model});
   if (big >= (1LL << 31)) return fail(err, DEC_ERR_UNSUPPORTED, "a weight matrix is 2 GiB or larger");
   if (2LL * d->max_ctx * hd >= (1LL << 31)) return fail(err, DEC_ERR_UNSUPPORTED, "KV cache of one head is 2 GiB or larger");
-  if ((long long)d->n_heads * max_attn_chunks(d->max_ctx, d->n_heads, 1024) > 1024)
-    return fail(err, DEC_ERR_UNSUPPORTED, "too many attention partials (n_heads x chunks > 1024)");
+  const int hb = d->batch * d->n_heads;
+  if ((long long)hb * max_attn_chunks(d->max_ctx, hb, 1024) > 65536)
+    return fail(err, DEC_ERR_UNSUPPORTED, "too many attention partials (batch x n_heads x chunks > 65536)");
   return DEC_OK;
 }
 
@@ -234,32 +242,32 @@ bool same_shape(const dec_model_desc& a, const dec_model_desc& b) {
 // device arena layout (bytes)
 // ---------------------------------------------------------------------------
 struct Arena {
-  size_t w, gains, rope, kv, x, qkv, attn_o, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out, prompt, ctl, params, trace, total;
+  size_t w, gains, rope, kv, x, qkv, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out, prompt, ctl, params, trace, total;
 };
 
 Arena arena_layout(const dec_model_desc& d, int G) {
   Arena a;
   const Image im = image_layout(d);
-  const size_t D = d.d_model, q = (size_t)d.n_heads * d.head_dim;
-  const int mc = max_attn_chunks(d.max_ctx, d.n_heads, G);
+  const size_t D = d.d_model, q = (size_t)d.n_heads * d.head_dim, B = d.batch;
+  const size_t hb = B * d.n_heads;   // attention heads of all sequences
+  const int mc = max_attn_chunks(d.max_ctx, (int)hb, G);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
   a.w = take(im.total * 2);
   a.gains = take(((size_t)d.n_layers * 2 + 1) * D * 4);
   a.rope = take((size_t)d.max_ctx * (d.head_dim / 2) * 2 * 4);
-  a.kv = take((size_t)d.n_layers * 2 * d.n_heads * d.max_ctx * d.head_dim * 2);
-  a.x = take(D * 4);
-  a.qkv = take(3 * q * 4);
-  a.attn_o = take(q * 4);
-  a.part = take((size_t)d.n_heads * mc * d.head_dim * 4);
-  a.pml = take((size_t)d.n_heads * mc * 2 * 4);
-  a.act = take((size_t)d.d_ffn * 4);
-  a.logits = take((size_t)d.lm_vocab * 4);
-  a.amax_v = take((size_t)G * 4);
-  a.amax_i = take((size_t)G * 4);
-  a.tok_cur = take(4);
-  a.tok_out = take((size_t)d.max_ctx * 4);
-  a.prompt = take((size_t)d.max_ctx * 4);
+  a.kv = take((size_t)d.n_layers * 2 * hb * d.max_ctx * d.head_dim * 2);
+  a.x = take(B * D * 4);
+  a.qkv = take(B * 3 * q * 4);
+  a.part = take(hb * mc * d.head_dim * 4);
+  a.pml = take(hb * mc * 2 * 4);
+  a.act = take(B * d.d_ffn * 4);
+  a.logits = take(B * d.lm_vocab * 4);
+  a.amax_v = take(B * G * 4);
+  a.amax_i = take(B * G * 4);
+  a.tok_cur = take(B * 4);
+  a.tok_out = take((size_t)d.max_ctx * B * 4);
+  a.prompt = take((size_t)d.max_ctx * B * 4);
   a.ctl = take(kCtlWords * 4);
   a.params = take(sizeof(Params));
   a.trace = take((size_t)G * kTraceStride * 8);
@@ -318,13 +326,13 @@ int launch(dec_handle* h, int pos0, int n_tok, int tok_src, int lm_last_only, in
       for (int k = 0; k < nph; ++k) {
         A.phase_begin = i * ppt + k;
         A.phase_end = A.phase_begin + 1;
-        HIPCHK(h, &h->err, (hipError_t)kernel_launch_plain(h->dP, A, h->grid, h->stream));
+        HIPCHK(h, &h->err, (hipError_t)kernel_launch_plain(h->dP, A, h->grid, h->desc.batch, h->stream));
       }
     }
     return DEC_OK;
   }
   A.bar_base = h->bar_done;
-  HIPCHK(h, &h->err, (hipError_t)kernel_launch_resident(h->dP, A, h->grid, h->stream));
+  HIPCHK(h, &h->err, (hipError_t)kernel_launch_resident(h->dP, A, h->grid, h->desc.batch, h->stream));
   h->bar_done += launch_barriers(h->desc.n_layers, n_tok, lm_last_only);
   return DEC_OK;
 }
@@ -345,9 +353,10 @@ int check_device_error(dec_handle* h) {
 int finish(dec_handle* h, int32_t* out_tok, int n_tok_out, float* out_logits) {
   int rc = check_device_error(h);
   if (rc) return rc;
-  if (out_tok) HIPCHK(h, &h->err, hipMemcpy(out_tok, h->P.tok_out, (size_t)n_tok_out * 4, hipMemcpyDeviceToHost));
+  const size_t B = h->desc.batch;
+  if (out_tok) HIPCHK(h, &h->err, hipMemcpy(out_tok, h->P.tok_out, (size_t)n_tok_out * B * 4, hipMemcpyDeviceToHost));
   if (out_logits)
-    HIPCHK(h, &h->err, hipMemcpy(out_logits, h->P.logits, (size_t)h->desc.lm_vocab * 4, hipMemcpyDeviceToHost));
+    HIPCHK(h, &h->err, hipMemcpy(out_logits, h->P.logits, B * h->desc.lm_vocab * 4, hipMemcpyDeviceToHost));
   return DEC_OK;
 }
 
@@ -541,19 +550,21 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
   hipError_t e = (hipError_t)kernel_prepare();
   if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipFuncSetAttribute"); return bail(DEC_ERR_DEVICE); }
   int per_cu = 0;
-  e = (hipError_t)kernel_blocks_per_cu(&per_cu);
+  e = (hipError_t)kernel_blocks_per_cu(desc->batch, &per_cu);
   if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"); return bail(DEC_ERR_DEVICE); }
   if (per_cu < 1 || h->grid > per_cu * cus) {
     fail(&h->err, DEC_ERR_UNSUPPORTED, "grid %d exceeds co-resident capacity %d x %d", h->grid, per_cu, cus);
     return bail(DEC_ERR_UNSUPPORTED);
   }
   {
-    // per-workgroup GEMV results and residual rows live in fixed LDS buffers
+    // per-workgroup GEMV results (every sequence) and residual rows live in
+    // fixed LDS buffers; the batch kernel keeps kMaxBatch sequences' slots
     auto per_wg = [&](long long n) { return (n + h->grid - 1) / h->grid; };
     const long long q = (long long)desc->n_heads * desc->head_dim;
-    const long long need_out = std::max({2 * per_wg(3 * q / 2), 2 * per_wg(desc->d_model / 2), per_wg(desc->d_ffn),
-                                         2 * per_wg(desc->lm_vocab / 2)});
-    if (need_out > kOutFloats || 2 * per_wg(desc->d_model / 2) > kOwnFloats) {
+    const long long mb = desc->batch > 1 ? kMaxBatch : 1;
+    const long long need_out = mb * std::max({2 * per_wg(3 * q / 2), 2 * per_wg(desc->d_model / 2),
+                                              2 * per_wg(desc->d_ffn), 2 * per_wg(desc->lm_vocab / 2)});
+    if (need_out > kOutFloats || mb * 2 * per_wg(desc->d_model / 2) > kOwnFloats) {
       fail(&h->err, DEC_ERR_UNSUPPORTED, "grid %d too small for this model (a workgroup would own %lld outputs)",
            h->grid, need_out);
       return bail(DEC_ERR_UNSUPPORTED);
@@ -619,13 +630,14 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
   P.off_E = h->im.off_E; P.off_lm = h->im.off_lm;
   P.gains = reinterpret_cast<const float*>(b + h->ar.gains);
   P.rope = reinterpret_cast<const float*>(b + h->ar.rope);
+  P.B = desc->batch;
   P.kv = reinterpret_cast<uint16_t*>(b + h->ar.kv);
   P.x = reinterpret_cast<float*>(b + h->ar.x);
   P.qkv = reinterpret_cast<float*>(b + h->ar.qkv);
-  P.attn_o = reinterpret_cast<float*>(b + h->ar.attn_o);
   P.part = reinterpret_cast<float*>(b + h->ar.part);
   P.pml = reinterpret_cast<float*>(b + h->ar.pml);
   P.act = reinterpret_cast<float*>(b + h->ar.act);
+  P.act16 = reinterpret_cast<uint16_t*>(b + h->ar.act);
   P.logits = reinterpret_cast<float*>(b + h->ar.logits);
   P.amax_v = reinterpret_cast<float*>(b + h->ar.amax_v);
   P.amax_i = reinterpret_cast<int*>(b + h->ar.amax_i);
@@ -633,7 +645,7 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
   P.tok_out = reinterpret_cast<int*>(b + h->ar.tok_out);
   P.prompt = reinterpret_cast<const int*>(b + h->ar.prompt);
   P.ctl = reinterpret_cast<uint32_t*>(b + h->ar.ctl);
-  P.max_chunks = max_attn_chunks(desc->max_ctx, desc->n_heads, h->grid);
+  P.max_chunks = max_attn_chunks(desc->max_ctx, desc->batch * desc->n_heads, h->grid);
   P.watchdog_ticks = (uint32_t)std::min(ticks, 4.0e9);
   P.trace = (h->debug & DEC_DEBUG_TRACE) ? reinterpret_cast<uint64_t*>(b + h->ar.trace) : nullptr;
   P.trace_stride = kTraceStride;
@@ -653,10 +665,12 @@ int dec_prefill(dec_handle* h, const int32_t* tokens, int32_t n, int32_t* out_to
   if (h->pos != 0) return fail(&h->err, DEC_ERR_STATE, "prefill needs position 0 (call dec_reset)");
   if (n < 1) return fail(&h->err, DEC_ERR_INVALID_ARG, "n must be >= 1");
   if (n > h->desc.max_ctx) return fail(&h->err, DEC_ERR_CONTEXT_FULL, "prompt of %d tokens exceeds max_ctx %d", n, h->desc.max_ctx);
-  for (int i = 0; i < n; ++i)
+  const int B = h->desc.batch;
+  for (long long i = 0; i < (long long)n * B; ++i)
     if (tokens[i] < 0 || tokens[i] >= h->desc.vocab)
-      return fail(&h->err, DEC_ERR_TOKEN_RANGE, "prompt token %d = %d outside [0, %d)", i, tokens[i], h->desc.vocab);
-  HIPCHK(h, &h->err, hipMemcpyAsync(const_cast<int*>(h->P.prompt), tokens, (size_t)n * 4, hipMemcpyHostToDevice, h->stream));
+      return fail(&h->err, DEC_ERR_TOKEN_RANGE, "prompt token %lld = %d outside [0, %d)", i, tokens[i], h->desc.vocab);
+  HIPCHK(h, &h->err, hipMemcpyAsync(const_cast<int*>(h->P.prompt), tokens, (size_t)n * B * 4, hipMemcpyHostToDevice,
+                                    h->stream));
   int rc = launch(h, 0, n, TOK_PROMPT, 1, out_logits != nullptr);
   if (rc) return rc;
   h->pos = n;
@@ -664,8 +678,9 @@ int dec_prefill(dec_handle* h, const int32_t* tokens, int32_t n, int32_t* out_to
   // the launch computed token index n-1's argmax
   rc = check_device_error(h);
   if (rc) return rc;
-  HIPCHK(h, &h->err, hipMemcpy(out_tok, h->P.tok_out + (n - 1), 4, hipMemcpyDeviceToHost));
-  if (out_logits) HIPCHK(h, &h->err, hipMemcpy(out_logits, h->P.logits, (size_t)h->desc.lm_vocab * 4, hipMemcpyDeviceToHost));
+  HIPCHK(h, &h->err, hipMemcpy(out_tok, h->P.tok_out + (size_t)(n - 1) * B, (size_t)B * 4, hipMemcpyDeviceToHost));
+  if (out_logits)
+    HIPCHK(h, &h->err, hipMemcpy(out_logits, h->P.logits, (size_t)B * h->desc.lm_vocab * 4, hipMemcpyDeviceToHost));
   return DEC_OK;
 }
 
@@ -675,9 +690,12 @@ int dec_step(dec_handle* h, const int32_t* force_tok, int32_t* out_tok, float* o
   if (h->pos >= h->desc.max_ctx) return fail(&h->err, DEC_ERR_CONTEXT_FULL, "context is full (%d positions)", h->desc.max_ctx);
   if (!force_tok && !h->has_prev_tok) return fail(&h->err, DEC_ERR_STATE, "no previous token: prefill first or pass force_tok");
   if (force_tok) {
-    if (force_tok[0] < 0 || force_tok[0] >= h->desc.vocab)
-      return fail(&h->err, DEC_ERR_TOKEN_RANGE, "token %d outside [0, %d)", force_tok[0], h->desc.vocab);
-    HIPCHK(h, &h->err, hipMemcpyAsync(h->P.tok_cur, force_tok, 4, hipMemcpyHostToDevice, h->stream));
+    for (int b = 0; b < h->desc.batch; ++b)
+      if (force_tok[b] < 0 || force_tok[b] >= h->desc.vocab)
+        return fail(&h->err, DEC_ERR_TOKEN_RANGE, "token %d of sequence %d outside [0, %d)", force_tok[b], b,
+                    h->desc.vocab);
+    HIPCHK(h, &h->err, hipMemcpyAsync(h->P.tok_cur, force_tok, (size_t)h->desc.batch * 4, hipMemcpyHostToDevice,
+                                      h->stream));
   }
   int rc = launch(h, h->pos, 1, TOK_DEVICE, 0, out_logits != nullptr);
   if (rc) return rc;
@@ -736,7 +754,7 @@ int dec_read_kv(dec_handle* h, int32_t layer, int32_t seq, int32_t n_pos, uint16
     uint16_t* dst = kind ? host_v : host_k;
     if (!dst) continue;
     for (int hh = 0; hh < d.n_heads; ++hh) {
-      const uint16_t* src = h->P.kv + (((size_t)layer * 2 + kind) * d.n_heads + hh) * head;
+      const uint16_t* src = h->P.kv + ((((size_t)layer * 2 + kind) * d.batch + seq) * d.n_heads + hh) * head;
       HIPCHK(h, &h->err, hipMemcpy(dst + (size_t)hh * n_pos * d.head_dim, src, (size_t)n_pos * d.head_dim * 2, hipMemcpyDeviceToHost));
     }
   }

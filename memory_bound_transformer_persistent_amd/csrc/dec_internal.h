@@ -21,7 +21,13 @@ constexpr int kChunkMin = 32;               // shortest attention chunk (positio
 constexpr int kChunkMax = 2048;
 constexpr int kTraceStride = 4096;          // trace stamps kept per workgroup per launch
 constexpr int kOutFloats = 2048;            // LDS: one phase's GEMV results of a workgroup
-constexpr int kOwnFloats = 256;             // LDS: a workgroup's rows of the residual stream             // longest attention chunk (scores kept in LDS)
+constexpr int kOwnFloats = 256;             // LDS: a workgroup's rows of the residual stream (all sequences)
+// Batched decode (up to kMaxBatch sequences at the same position): the GEMV
+// inputs of every sequence sit in LDS as fp16, side by side, so one pass over
+// the weights serves all of them.  Limits that keep them in LDS:
+constexpr int kMaxBatch = 8;
+constexpr int kBatchSpanD = 2560;           // padded d_model (input of QKV, GU, LM; staged in fp32 too)
+constexpr int kBatchSpanK = 7680;           // padded d_ffn and n_heads*head_dim
 constexpr int kLdsBytes = 160 * 1024;       // dynamic LDS per workgroup; > half a CU's 160 KB,
                                             // so exactly one workgroup runs per compute unit
 
@@ -52,19 +58,20 @@ struct Params {
   size_t off_E, off_lm;       // element offsets of the embedding and the LM head
   const float* gains;         // [L][2][d] (attn, ffn) then g_final [d]
   const float* rope;          // [max_ctx][hd/2][2] (cos, sin)
-  uint16_t* kv;               // [L][2][H][max_ctx][hd] fp16
-  float* x;                   // residual stream [d]
-  float* qkv;                 // [3q]
-  float* attn_o;              // merged attention output [q]
-  float* part;                // attention partial sums [H][max_chunks][hd]
-  float* pml;                 // attention partial (max, sum) [H][max_chunks][2]
-  float* act;                 // SwiGLU output [F]
-  float* logits;              // [Vlm]
-  float* amax_v;              // per-workgroup best logit [G]
-  int* amax_i;                // per-workgroup best index [G]
-  int* tok_cur;               // token the next step consumes [1]
-  int* tok_out;               // greedy token of each token of a launch [max_ctx]
-  const int* prompt;          // tokens of a prompt launch [max_ctx]
+  int B;                      // sequences decoded together (batch)
+  uint16_t* kv;               // [L][2][B][H][max_ctx][hd] fp16
+  float* x;                   // residual stream [B][d]
+  float* qkv;                 // [B][3q]
+  float* part;                // attention partial sums [B*H][max_chunks][hd]
+  float* pml;                 // attention partial (max, sum) [B*H][max_chunks][2]
+  float* act;                 // SwiGLU output [F] (batch 1, fp32)
+  uint16_t* act16;            // SwiGLU output [B][F] (batch > 1, fp16; same memory as act)
+  float* logits;              // [B][Vlm]
+  float* amax_v;              // per-workgroup best logit [B][G]
+  int* amax_i;                // per-workgroup best index [B][G]
+  int* tok_cur;               // token each sequence's next step consumes [B]
+  int* tok_out;               // greedy tokens of a launch [max_ctx][B]
+  const int* prompt;          // tokens of a prompt launch [B][n_tok]
   uint32_t* ctl;              // control words
   int max_chunks;
   uint32_t watchdog_ticks;    // bound on one barrier wait, in wall-clock ticks
@@ -87,7 +94,8 @@ struct Launch {
 DEC_HD inline int phases_per_token(int L) { return kPhasesPerLayer * L + 2; }
 
 // Number of attention chunks per head at context length ctx for a grid of G
-// workgroups: as many as keeps every workgroup busy (at most G/H per head),
+// workgroups and H heads (all sequences' heads in a batch): as many as keeps
+// every workgroup busy (at most G/H per head),
 // no chunk shorter than kChunkMin or longer than kChunkMax positions.
 DEC_HD inline int attn_chunks(int ctx, int H, int G) {
   int by_min = (ctx + kChunkMin - 1) / kChunkMin;
@@ -121,10 +129,12 @@ inline uint32_t launch_barriers(int L, int n_tok, int lm_last_only) {
 }
 
 // Launch helpers defined next to the kernel (dec_kernels.hip).  P points to a
-// device copy of the parameters; stream is a hipStream_t; each returns a hipError_t value (0 = success).
+// device copy of the parameters; stream is a hipStream_t; batch selects the
+// kernel built for one sequence or for up to kMaxBatch; each returns a
+// hipError_t value (0 = success).
 int kernel_prepare();                                   // raise the dynamic-LDS limit
-int kernel_blocks_per_cu(int* out);                     // co-resident workgroups per CU
-int kernel_launch_resident(const Params* P, const Launch& A, int grid, void* stream);  // cooperative
-int kernel_launch_plain(const Params* P, const Launch& A, int grid, void* stream);     // ordinary
+int kernel_blocks_per_cu(int batch, int* out);          // co-resident workgroups per CU
+int kernel_launch_resident(const Params* P, const Launch& A, int grid, int batch, void* stream);  // cooperative
+int kernel_launch_plain(const Params* P, const Launch& A, int grid, int batch, void* stream);     // ordinary
 
 }  // namespace decmono

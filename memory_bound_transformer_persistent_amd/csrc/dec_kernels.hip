@@ -10,19 +10,21 @@
 //
 // Batch-1 decode reads every weight once per token through matrix-vector
 // products, so it is bound by HBM bandwidth (same page, section
-// GPU推論の速度制限要因：メモリ帯域幅).  Every GEMV here streams its rows with
-// 16-byte non-temporal buffer loads (one 1 KB contiguous segment per wave
-// instruction), keeps the activation vector in LDS as fp32, accumulates in
-// fp32 and reduces across the wave with DPP.  No MFMA: at one token per step
-// there is no dense contraction to feed it.
+// GPU推論の速度制限要因：メモリ帯域幅).  Every GEMV streams its rows with 16-byte
+// non-temporal buffer loads into registers (one 1 KB contiguous segment per
+// wave instruction), reads its input vector from LDS, accumulates in fp32 and
+// reduces across the wave with DPP.  No MFMA: at one token per step there is
+// no dense contraction to feed it.  With several sequences at the same
+// position (batch), the same pass over the weights serves all of them: the
+// inputs sit in LDS as fp16 and each weight pair meets every sequence's input
+// through v_dot2_f32_f16.
 //
 // Cross-workgroup data (residual stream, q/k/v, attention partials, SwiGLU
 // output, KV-cache appends, argmax partials) is written with agent-coherent
 // (sc1) stores and read with agent-coherent loads, so a barrier needs no L2
-// write-back or invalidate: it waits for this workgroup's stores to complete,
-// then arrives on a per-group counter whose last arriver bumps the global
-// counter.  Weights are read-only for the whole launch and use plain
-// non-temporal loads.
+// write-back or invalidate: a workgroup waits for its own stores to complete,
+// then adds one to its group's counter; waiters poll the group counters.
+// Weights are read-only for the whole launch and use plain non-temporal loads.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -33,6 +35,8 @@ namespace decmono {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kAuxNt = 0x2;    // non-temporal: streamed once
 constexpr int kAuxSc1 = 0x10;  // coherent at device (agent) scope
@@ -49,11 +53,28 @@ constexpr int kStreamers = kWaves - 1;
 // own weight traffic.
 constexpr int kUnitsInFlight = 4;
 constexpr int kBlocksInFlight = 2 * kUnitsInFlight;
-// LDS map (floats): xs | out | xown | red | si | aux | gains | phase tables
+constexpr int kTabStride = 12;   // ints per (streamer, phase type) entry of the phase tables
 constexpr int kAuxFloats = 2048;
-constexpr int kLdsOut = kMaxK, kLdsOwn = kLdsOut + kOutFloats, kLdsRed = kLdsOwn + kOwnFloats;
-constexpr int kLdsSi = kLdsRed + 64, kLdsAux = kLdsSi + 16, kLdsGain = kLdsAux + kAuxFloats;
-constexpr int kLdsTables = kLdsGain + kMaxK;
+
+// LDS map (floats) for a kernel built for up to MB sequences:
+// input region | out | xown | red | scales | si | aux | gains | phase tables.
+// MB == 1: the input region is the fp32 vector xs.  MB > 1: it holds the fp16
+// inputs of every sequence side by side (stride = the phase's padded row
+// length) and, for the normed phases, the fp32 residual vectors they come
+// from, staged after them.
+template <int MB>
+struct Lds {
+  static constexpr int Region = MB == 1 ? kMaxK : (kMaxBatch * kBatchSpanK) / 2;
+  static constexpr int GainN = MB == 1 ? kMaxK : kBatchSpanD;
+  static constexpr int Out = Region, Own = Out + kOutFloats, Red = Own + kOwnFloats;
+  static constexpr int Scl = Red + kWaves * kMaxBatch, Si = Scl + kMaxBatch, Aux = Si + 16;
+  static constexpr int Gain = Aux + kAuxFloats, TabWg = Gain + GainN, Tab = TabWg + 16;
+  static constexpr int End = Tab + kStreamers * 6 * kTabStride;
+  static_assert(End * 4 <= kLdsBytes, "LDS map exceeds the allocation");
+  static_assert(MB == 1 || 3 * kMaxBatch * kBatchSpanD / 2 <= Region, "staged fp32 inputs do not fit");
+  static_assert(Gain % 4 == 0 && Region % 4 == 0, "16-byte alignment");
+};
+
 constexpr int kWaitVm0 = 0x0F70;             // s_waitcnt vmcnt(0), expcnt/lgkmcnt untouched
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -67,11 +88,11 @@ __device__ __forceinline__ u32x4 ld_kv(rsrc_t r, uint32_t off) {
 }
 // 16 bytes per lane from a buffer straight into LDS at lds_base + 16*lane (wave-uniform
 // base), coherent at device scope (activations written by other workgroups).
-__device__ __forceinline__ void dma16_coh(rsrc_t r, float* lds_base, uint32_t off) {
+__device__ __forceinline__ void dma16_coh(rsrc_t r, void* lds_base, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, off, 0, 0, kAuxSc1);
 }
 // Same for read-only data.
-__device__ __forceinline__ void dma16_ld(rsrc_t r, float* lds_base, uint32_t off) {
+__device__ __forceinline__ void dma16_ld(rsrc_t r, void* lds_base, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, off, 0, 0, 0);
 }
 __device__ __forceinline__ void wait_vm0() {
@@ -120,6 +141,9 @@ __device__ __forceinline__ void st_coh(int* p, int v) {
 __device__ __forceinline__ void st_coh(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_coh(uint16_t* p, uint16_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // ---------------------------------------------------------------------------
 // wave reductions (DPP inside 16-lane rows, readlane across rows)
@@ -152,18 +176,7 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(readlane(v, 0), readlane(v, 16)), fmaxf(readlane(v, 32), readlane(v, 48)));
 }
 
-// Sum over the workgroup; every thread gets the same value.  red: kWaves floats.
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) s += red[w];
-  __syncthreads();
-  return s;
-}
-
+// 8 fp16 weights times 8 fp32 inputs, fp32 accumulate.
 __device__ __forceinline__ float dot8(u32x4 w, f32x4 xa, f32x4 xb, float acc) {
   const f16x8 h = __builtin_bit_cast(f16x8, w);
   acc = __builtin_fmaf((float)h[0], xa[0], acc);
@@ -176,15 +189,23 @@ __device__ __forceinline__ float dot8(u32x4 w, f32x4 xa, f32x4 xb, float acc) {
   acc = __builtin_fmaf((float)h[7], xb[3], acc);
   return acc;
 }
+// 8 fp16 weights times 8 fp16 inputs, fp32 accumulate (v_dot2_f32_f16).  The
+// pairs are taken by value from whole vectors: this compiler's
+// __builtin_bit_cast of a vector element reads element 0.
+__device__ __forceinline__ float dot8h(u32x4 w, u32x4 x, float acc) {
+  const f16x8 a = __builtin_bit_cast(f16x8, w), b = __builtin_bit_cast(f16x8, x);
+  acc = __builtin_amdgcn_fdot2(f16x2{a[0], a[1]}, f16x2{b[0], b[1]}, acc, false);
+  acc = __builtin_amdgcn_fdot2(f16x2{a[2], a[3]}, f16x2{b[2], b[3]}, acc, false);
+  acc = __builtin_amdgcn_fdot2(f16x2{a[4], a[5]}, f16x2{b[4], b[5]}, acc, false);
+  acc = __builtin_amdgcn_fdot2(f16x2{a[6], a[7]}, f16x2{b[6], b[7]}, acc, false);
+  return acc;
+}
 
 __device__ __forceinline__ void split(int n, int g, int G, int& b, int& e) {
   b = (int)((long long)n * g / G);
   e = (int)((long long)n * (g + 1) / G);
 }
 
-// ---------------------------------------------------------------------------
-// weight prefetch into LDS
-// ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
 // GEMV work and block streams
 // ---------------------------------------------------------------------------
@@ -200,7 +221,7 @@ struct GemvWork {
 };
 
 __device__ __forceinline__ int gemv_npc(int K) { return (K + 511) >> 9; }
-// LDS floats of the input vector a GEMV with row length K reads (zero-padded past K).
+// Elements of the input vector a GEMV with row length K reads (zero-padded past K).
 __device__ __forceinline__ int gemv_span(int K) { return 512 * gemv_npc(K); }
 
 __device__ __forceinline__ GemvWork work_of(const Params& P, int ph, int l) {
@@ -258,15 +279,23 @@ __device__ __forceinline__ void phase_next(const Params& P, const Launch& A, Pha
 __device__ __forceinline__ bool is_gemv(int ph) {
   return ph == PH_QKV || ph == PH_O || ph == PH_GU || ph == PH_DOWN || ph == PH_LM;
 }
+// Phases whose input is rmsnorm(x) * g, and their g.
+__device__ __forceinline__ bool norm_phase(const PhaseIt& id) {
+  return id.ph == PH_QKV || id.ph == PH_GU || id.ph == PH_LM;
+}
+__device__ __forceinline__ const float* norm_gains(const Params& P, const PhaseIt& id) {
+  if (id.ph == PH_LM) return P.gains + (size_t)P.L * 2 * P.d;
+  return P.gains + (size_t)id.l * 2 * P.d + (id.ph == PH_GU ? P.d : 0);
+}
+// Row length of the GEMV of phase ph (its input's length).
+__device__ __forceinline__ int phase_k(const Params& P, int ph) {
+  return ph == PH_O ? P.q : (ph == PH_DOWN ? P.F : P.d);
+}
 
 // Launch-constant split of every GEMV phase type, computed once per launch
 // into LDS (no divisions on the phase path).  Per type ph: the workgroup's
 // pairs [p0, p1) (kept by wave 0) and, per streamer, its share of units.
-constexpr int kTabStride = 12;   // ints per (streamer, phase type) entry
 enum TabField { T_LEFT, T_OFF, T_COL, T_NPC, T_ROWB, T_WRAP, T_TAIL, T_T0, T_NBYTES, T_PAD };
-constexpr int kLdsTabWg = kLdsTables;                                       // [6][2] ints
-constexpr int kLdsTab = kLdsTabWg + 16;                                     // [7][6][kTabStride] ints
-static_assert((kLdsTab + kStreamers * 6 * kTabStride) * 4 <= kLdsBytes, "LDS map exceeds the allocation");
 
 __device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -422,27 +451,28 @@ __device__ __forceinline__ bool w0_wait(const Params& P, uint32_t epoch, int fen
 }
 
 // ---------------------------------------------------------------------------
-// wave 0: phase inputs
+// phase inputs
 // ---------------------------------------------------------------------------
 // RMSNorm is split so that no wave waits on a reduction before the GEMV:
-// wave 0 lands the raw vector in xs and the norm gains in gs (LDS DMA); all
-// waves then form xs = x * g and their shares of sum(x^2); the scalar
+// wave 0 lands the raw vector(s) and the norm gains in LDS (LDS DMA); all
+// waves then form x * g and their shares of sum(x^2); the scalar
 // 1/sqrt(mean(x^2) + eps) multiplies the phase's outputs when wave 0
 // publishes them, since W (x g s) = s W (x g).
 
-// dst[0..gemv_span(n)) <- src[0..n) by LDS DMA (coherent when coh; zero past n).
-// Issues only; the caller waits.
-__device__ __forceinline__ void w0_dma_vec(float* dst, const float* src, int n, bool coh) {
+// dst[0..gemv_span(n) elements of esize bytes) <- src[0..n) by LDS DMA
+// (coherent when coh; zero past n).  Issues only; the caller waits.
+__device__ __forceinline__ void w0_dma_vec(void* dst, const void* src, int n, int esize, bool coh) {
   const int lane = threadIdx.x & 63;
-  const rsrc_t r = make_rsrc(src, (uint32_t)n * 4u);
-  const int span = gemv_span(n);
-  for (int i = 0; i < span; i += 256) {
-    if (coh) dma16_coh(r, dst + i, (uint32_t)(i + 4 * lane) * 4u);
-    else dma16_ld(r, dst + i, (uint32_t)(i + 4 * lane) * 4u);
+  const rsrc_t r = make_rsrc(src, (uint32_t)(n * esize));
+  const int span_bytes = gemv_span(n) * esize;
+  for (int o = 0; o < span_bytes; o += 1024) {
+    void* base = static_cast<char*>(dst) + o;
+    if (coh) dma16_coh(r, base, (uint32_t)(o + 16 * lane));
+    else dma16_ld(r, base, (uint32_t)(o + 16 * lane));
   }
 }
 
-// All waves: xs[0..n) *= gs[0..n); red[wave] <- this wave's share of sum(x^2).
+// MB == 1, all waves: xs[0..n) *= gs[0..n); red[wave] <- this wave's share of sum(x^2).
 __device__ __forceinline__ void apply_gains(float* xs, const float* gs, int n, float* red) {
   float ss = 0.f;
   for (int i = 4 * (int)threadIdx.x; i < n; i += 4 * kThreads) {
@@ -454,13 +484,33 @@ __device__ __forceinline__ void apply_gains(float* xs, const float* gs, int n, f
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
 }
 
-// Layer-0 input: x = E[tok] (fp16 -> fp32) into xs (raw, zero past d).  This
-// workgroup's rows of x go to xown and to global x.
-__device__ __forceinline__ void w0_embed(const Params& P, int tok, float* xs, float* xown) {
+// MB > 1, all waves: for each sequence b, xh[b][0..span) <- fp16(st[b] * gs)
+// (st: the staged fp32 vectors, zero past n) and red[b*kWaves + wave] <- this
+// wave's share of sum(st[b]^2).
+__device__ __forceinline__ void apply_gains_batch(_Float16* xh, const float* st, const float* gs, int n, int B,
+                                                  float* red) {
+  const int span = gemv_span(n);
+  for (int b = 0; b < B; ++b) {
+    float ss = 0.f;
+    for (int i = 4 * (int)threadIdx.x; i < span; i += 4 * kThreads) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(st + (size_t)b * span + i);
+      ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+      const f32x4 y = v * *reinterpret_cast<const f32x4*>(gs + i);
+      *reinterpret_cast<f16x4*>(xh + (size_t)b * span + i) = f16x4{(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[b * kWaves + (threadIdx.x >> 6)] = ss;
+  }
+}
+
+// Layer-0 input of sequence b: x = E[tok] (fp16 -> fp32) into dst (raw, zero
+// past d).  This workgroup's rows of x go to xown (own floats per sequence)
+// and to global x.
+__device__ __forceinline__ void w0_embed(const Params& P, int b, int tok, float* dst, float* xown, int own) {
   const int lane = threadIdx.x & 63, d = P.d;
   const _Float16* e = reinterpret_cast<const _Float16*>(P.w + P.off_E + (size_t)tok * d);
-  int b, en;
-  split(d / 2, blockIdx.x, gridDim.x, b, en);
+  int r0, r1;
+  split(d / 2, blockIdx.x, gridDim.x, r0, r1);
   const int span = gemv_span(d);
   for (int i = 8 * lane; i < span; i += 512) {
     f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
@@ -469,28 +519,28 @@ __device__ __forceinline__ void w0_embed(const Params& P, int tok, float* xs, fl
       lo = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
       hi = f32x4{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
     }
-    *reinterpret_cast<f32x4*>(xs + i) = lo;
-    *reinterpret_cast<f32x4*>(xs + i + 4) = hi;
+    *reinterpret_cast<f32x4*>(dst + i) = lo;
+    *reinterpret_cast<f32x4*>(dst + i + 4) = hi;
   }
   wait_lgkm0();
-  for (int r = 2 * b + lane; r < 2 * en; r += 64) {
-    xown[r - 2 * b] = xs[r];
-    st_coh(P.x + r, xs[r]);
+  for (int r = 2 * r0 + lane; r < 2 * r1; r += 64) {
+    xown[b * own + r - 2 * r0] = dst[r];
+    st_coh(P.x + (size_t)b * d + r, dst[r]);
   }
 }
 
 // ---------------------------------------------------------------------------
 // wave 0: attention
 // ---------------------------------------------------------------------------
-// Single-query attention of every head over positions 0..pos, split into
-// chunks of positions; (head, chunk) units go round-robin over workgroups.
-// A lane group of HD/8 lanes holds one position (16 B of its K and V row per
-// lane); K and V of NPASS*64/(HD/8) positions are loaded together and an
-// online softmax runs across such groups.  The first group's loads are
-// issued before the grid barrier releases (`wait` runs the barrier wait once):
-// cached positions do not depend on this token.  Each unit stores an
-// unnormalised partial (max m, sum of exp l, sum of exp * V) that the O
-// phase merges.
+// Single-query attention of every head of every sequence over positions
+// 0..pos, split into chunks of positions; (sequence-head, chunk) units go
+// round-robin over workgroups.  A lane group of HD/8 lanes holds one
+// position (16 B of its K and V row per lane); K and V of NPASS*64/(HD/8)
+// positions are loaded together and an online softmax runs across such
+// groups.  The first group's loads are issued before the grid barrier
+// releases (`wait` runs the barrier wait once): cached positions do not
+// depend on this token.  Each unit stores an unnormalised partial (max m, sum
+// of exp l, sum of exp * V) that the O phase merges.
 template <int HD, class Wait>
 __device__ __forceinline__ bool w0_attention(const Params& P, int l, int pos, float* aux, Wait&& wait) {
   constexpr int LP = HD / 8, PPW = 64 / LP;
@@ -499,23 +549,25 @@ __device__ __forceinline__ bool w0_attention(const Params& P, int l, int pos, fl
   float* qs = aux;                       // [HD] rotated, scaled query
   float* kn = qs + HD;                   // [HD] new key (fp16-rounded)
   float* vn = kn + HD;                   // [HD] new value (fp16-rounded)
-  const int ctx = pos + 1, H = P.H, G = gridDim.x;
-  const int C = attn_chunks(ctx, H, G);
+  const int ctx = pos + 1, H = P.H, HB = P.B * P.H, G = gridDim.x;
+  const int C = attn_chunks(ctx, HB, G);
   const int CH = (ctx + C - 1) / C;
   const int lane = threadIdx.x & 63;
   const int sub = lane % LP, pidx = lane / LP;
   const float scale = 1.0f / sqrtf((float)HD);
   const size_t head_elems = (size_t)P.max_ctx * HD;
   bool waited = false;
-  for (int u = blockIdx.x; u < H * C; u += G) {
-    const int h = u / C, c = u % C;
+  for (int u = blockIdx.x; u < HB * C; u += G) {
+    const int hb = u / C, c = u % C;             // hb = sequence * H + head
+    const int seq = hb / H, h = hb - seq * H;
     const int j0 = c * CH;
     const int j1 = min(ctx, j0 + CH);
     const bool has_new = j0 < ctx && j1 == ctx;
-    uint16_t* kc = P.kv + ((size_t)(l * 2 + 0) * H + h) * head_elems;
-    uint16_t* vc = P.kv + ((size_t)(l * 2 + 1) * H + h) * head_elems;
+    uint16_t* kc = P.kv + ((size_t)(l * 2 + 0) * HB + hb) * head_elems;
+    uint16_t* vc = P.kv + ((size_t)(l * 2 + 1) * HB + hb) * head_elems;
     const rsrc_t rk = make_rsrc(kc, (uint32_t)(head_elems * 2));
     const rsrc_t rv = make_rsrc(vc, (uint32_t)(head_elems * 2));
+    const float* qkv = P.qkv + (size_t)seq * 3 * P.q;
     float M = -INFINITY, Lsum = 0.f;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int g0 = j0; g0 < j1; g0 += GRP) {
@@ -535,13 +587,13 @@ __device__ __forceinline__ bool w0_attention(const Params& P, int l, int pos, fl
         for (int i = lane; i < HD / 2; i += 64) {
           const float cs = ldg(P.rope + ((size_t)pos * (HD / 2) + i) * 2);
           const float sn = ldg(P.rope + ((size_t)pos * (HD / 2) + i) * 2 + 1);
-          const float* qh = P.qkv + h * HD;
+          const float* qh = qkv + h * HD;
           const float q0 = ld_coh(qh + 2 * i), q1 = ld_coh(qh + 2 * i + 1);
           qs[2 * i] = (q0 * cs - q1 * sn) * scale;
           qs[2 * i + 1] = (q0 * sn + q1 * cs) * scale;
           if (has_new) {
-            const float* kh = P.qkv + P.q + h * HD;
-            const float* vh = P.qkv + 2 * P.q + h * HD;
+            const float* kh = qkv + P.q + h * HD;
+            const float* vh = qkv + 2 * P.q + h * HD;
             const float k0 = ld_coh(kh + 2 * i), k1 = ld_coh(kh + 2 * i + 1);
             const _Float16 kr0 = (_Float16)(k0 * cs - k1 * sn), kr1 = (_Float16)(k0 * sn + k1 * cs);
             const _Float16 vr0 = (_Float16)ld_coh(vh + 2 * i), vr1 = (_Float16)ld_coh(vh + 2 * i + 1);
@@ -604,8 +656,8 @@ __device__ __forceinline__ bool w0_attention(const Params& P, int l, int pos, fl
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       for (int off = LP; off < 64; off <<= 1) acc[q] += __shfl_xor(acc[q], off, 64);
-    float* pp = P.part + ((size_t)h * P.max_chunks + c) * HD;
-    float* pm = P.pml + ((size_t)h * P.max_chunks + c) * 2;
+    float* pp = P.part + ((size_t)hb * P.max_chunks + c) * HD;
+    float* pm = P.pml + ((size_t)hb * P.max_chunks + c) * 2;
     if (pidx == 0) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) st_coh(pp + 8 * sub + q, acc[q]);
@@ -616,32 +668,37 @@ __device__ __forceinline__ bool w0_attention(const Params& P, int l, int pos, fl
   return true;
 }
 
-// All waves: xs <- o, the attention output of every head, merged from the
-// per-chunk partials with a running max: o = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c.
+// All waves: the attention output o of every head of every sequence, merged
+// from the per-chunk partials with a running max:
+// o = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c.  MB == 1: into xs
+// (fp32); MB > 1: into xh[b][0..span(q)) (fp16).
+template <int MB>
 __device__ __forceinline__ void merge_attention(const Params& P, int pos, float* xs) {
-  const int ctx = pos + 1, H = P.H, hd = P.hd, q = P.q;
-  const int C = attn_chunks(ctx, H, gridDim.x);
-  const rsrc_t rp = make_rsrc(P.part, (uint32_t)((size_t)H * P.max_chunks * hd * 4));
-  constexpr int MB = 8;
-  for (int i = threadIdx.x * 4; i < gemv_span(q); i += kThreads * 4) {
+  const int ctx = pos + 1, H = P.H, hd = P.hd, q = P.q, HB = P.B * P.H;
+  const int C = attn_chunks(ctx, HB, gridDim.x);
+  const int span = gemv_span(q);
+  const rsrc_t rp = make_rsrc(P.part, (uint32_t)((size_t)HB * P.max_chunks * hd * 4));
+  constexpr int CB = 8;
+  for (int e4 = threadIdx.x * 4; e4 < P.B * span; e4 += kThreads * 4) {
+    const int b = e4 / span, i = e4 - b * span;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
     if (i < q) {
-      const int h = i / hd, jj = i % hd;
-      const float* pm = P.pml + (size_t)h * P.max_chunks * 2;
+      const int hb = b * H + i / hd, jj = i % hd;
+      const float* pm = P.pml + (size_t)hb * P.max_chunks * 2;
       float Mr = -INFINITY, Lr = 0.f;
       f32x4 Or = {0.f, 0.f, 0.f, 0.f};
-      for (int c0 = 0; c0 < C; c0 += MB) {
-        float mv[MB], lv[MB];
-        f32x4 pv[MB];
+      for (int c0 = 0; c0 < C; c0 += CB) {
+        float mv[CB], lv[CB];
+        f32x4 pv[CB];
 #pragma unroll
-        for (int t = 0; t < MB; ++t) {
+        for (int t = 0; t < CB; ++t) {
           const bool in = c0 + t < C;
           mv[t] = in ? ld_coh(pm + 2 * (c0 + t)) : -INFINITY;
           lv[t] = in ? ld_coh(pm + 2 * (c0 + t) + 1) : 0.f;
-          pv[t] = ld_coh4(rp, in ? (uint32_t)(((size_t)h * P.max_chunks + c0 + t) * hd + jj) * 4u : kOOB);
+          pv[t] = ld_coh4(rp, in ? (uint32_t)(((size_t)hb * P.max_chunks + c0 + t) * hd + jj) * 4u : kOOB);
         }
 #pragma unroll
-        for (int t = 0; t < MB; ++t) {
+        for (int t = 0; t < CB; ++t) {
           if (mv[t] == -INFINITY) continue;
           const float Mn = fmaxf(Mr, mv[t]);
           const float a = Mr == -INFINITY ? 0.f : expf(Mr - Mn);
@@ -653,62 +710,85 @@ __device__ __forceinline__ void merge_attention(const Params& P, int pos, float*
       }
       o = Or / Lr;
     }
-    *reinterpret_cast<f32x4*>(xs + i) = o;
+    if constexpr (MB == 1) {
+      *reinterpret_cast<f32x4*>(xs + i) = o;
+    } else {
+      _Float16* xh = reinterpret_cast<_Float16*>(xs);
+      *reinterpret_cast<f16x4*>(xh + (size_t)b * span + i) = f16x4{(_Float16)o[0], (_Float16)o[1], (_Float16)o[2], (_Float16)o[3]};
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // wave 0: phase outputs
 // ---------------------------------------------------------------------------
+// out holds the phase's row sums, row-major over sequences: out[row * MB + b].
+// scl[b] is sequence b's norm scale for the phase (1 where there is no norm).
+template <int MB>
 __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, const int* tab_wg, bool want_logits,
-                                                 float scale, const float* out, float* xown) {
-  const int lane = threadIdx.x & 63;
+                                                 const float* scl, const float* out, float* xown) {
+  const int lane = threadIdx.x & 63, B = P.B;
   if (!is_gemv(ph)) return;
-  struct { int p0; } w{rfl(tab_wg[2 * ph])};
-  const int n = rfl(tab_wg[2 * ph + 1]) - w.p0;
+  const int p0 = rfl(tab_wg[2 * ph]);
+  const int n = rfl(tab_wg[2 * ph + 1]) - p0;
+  const int own = kOwnFloats / MB;
   if (ph == PH_QKV) {
-    for (int t = lane; t < 2 * n; t += 64) st_coh(P.qkv + 2 * w.p0 + t, out[t] * scale);
+    for (int e = lane; e < 2 * n * MB; e += 64) {
+      const int t = e / MB, b = e - t * MB;
+      if (b < B) st_coh(P.qkv + (size_t)b * 3 * P.q + 2 * p0 + t, out[e] * scl[b]);
+    }
   } else if (ph == PH_O || ph == PH_DOWN) {
-    for (int t = lane; t < 2 * n; t += 64) {
-      xown[t] += out[t];
-      st_coh(P.x + 2 * w.p0 + t, xown[t]);
+    for (int e = lane; e < 2 * n * MB; e += 64) {
+      const int t = e / MB, b = e - t * MB;
+      if (b < B) {
+        const float v = xown[b * own + t] + out[e];
+        xown[b * own + t] = v;
+        st_coh(P.x + (size_t)b * P.d + 2 * p0 + t, v);
+      }
     }
   } else if (ph == PH_GU) {
-    for (int t = lane; t < n; t += 64) {
-      const float gt = out[2 * t] * scale, up = out[2 * t + 1] * scale;
-      st_coh(P.act + w.p0 + t, gt / (1.0f + expf(-gt)) * up);
+    for (int e = lane; e < n * MB; e += 64) {
+      const int t = e / MB, b = e - t * MB;
+      if (b < B) {
+        const float gt = out[2 * t * MB + b] * scl[b], up = out[(2 * t + 1) * MB + b] * scl[b];
+        const float a = gt / (1.0f + expf(-gt)) * up;
+        if constexpr (MB == 1) st_coh(P.act + p0 + t, a);
+        else st_coh(P.act16 + (size_t)b * P.F + p0 + t, __builtin_bit_cast(uint16_t, (_Float16)a));
+      }
     }
   } else if (ph == PH_LM) {
-    float best = -INFINITY;
-    int bidx = 0x7fffffff;
-    for (int t = lane; t < 2 * n; t += 64) {
-      const float v = out[t] * scale;
-      if (v > best) { best = v; bidx = 2 * w.p0 + t; }
-      if (want_logits) P.logits[2 * w.p0 + t] = v;
-    }
+    for (int b = 0; b < B; ++b) {
+      float best = -INFINITY;
+      int bidx = 0x7fffffff;
+      for (int t = lane; t < 2 * n; t += 64) {
+        const float v = out[t * MB + b] * scl[b];
+        if (v > best) { best = v; bidx = 2 * p0 + t; }
+        if (want_logits) P.logits[(size_t)b * P.Vlm + 2 * p0 + t] = v;
+      }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(best, off, 64);
-      const int oi = __shfl_xor(bidx, off, 64);
-      if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
-    }
-    if (lane == 0) {
-      st_coh(P.amax_v + blockIdx.x, best);
-      st_coh(P.amax_i + blockIdx.x, bidx);
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(best, off, 64);
+        const int oi = __shfl_xor(bidx, off, 64);
+        if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
+      }
+      if (lane == 0) {
+        st_coh(P.amax_v + (size_t)b * gridDim.x + blockIdx.x, best);
+        st_coh(P.amax_i + (size_t)b * gridDim.x + blockIdx.x, bidx);
+      }
     }
   }
 }
 
-// Greedy token = argmax over the workgroups' partials (lowest index on ties).
-// Every workgroup computes it (it is the next token's input); workgroup 0
-// publishes it.
-__device__ __forceinline__ int w0_argmax(const Params& P, int i) {
+// Greedy token of sequence b = argmax over the workgroups' partials (lowest
+// index on ties).  Every workgroup computes it (it is the next token's
+// input); workgroup 0 publishes it.
+__device__ __forceinline__ int w0_argmax(const Params& P, int i, int b) {
   const int lane = threadIdx.x & 63, G = gridDim.x;
   float bvv = -INFINITY;
   int bii = 0x7fffffff;
   for (int t = lane; t < G; t += 64) {
-    const float v = ld_coh(P.amax_v + t);
-    const int ix = ld_coh(P.amax_i + t);
+    const float v = ld_coh(P.amax_v + (size_t)b * G + t);
+    const int ix = ld_coh(P.amax_i + (size_t)b * G + t);
     if (v > bvv || (v == bvv && ix < bii)) { bvv = v; bii = ix; }
   }
 #pragma unroll
@@ -718,7 +798,7 @@ __device__ __forceinline__ int w0_argmax(const Params& P, int i) {
     if (ov > bvv || (ov == bvv && oi < bii)) { bvv = ov; bii = oi; }
   }
   const int tok = (bii == 0x7fffffff) ? 0 : bii;
-  if (blockIdx.x == 0 && lane == 0) { st_coh(P.tok_cur, tok); st_coh(P.tok_out + i, tok); }
+  if (blockIdx.x == 0 && lane == 0) { st_coh(P.tok_cur + b, tok); st_coh(P.tok_out + (size_t)i * P.B + b, tok); }
   return tok;
 }
 
@@ -726,28 +806,20 @@ __device__ __forceinline__ int w0_argmax(const Params& P, int i) {
 // the resident kernel
 // ---------------------------------------------------------------------------
 // Both roles walk the same phase sequence and meet at the same workgroup
-// barriers: S1 (phase input in LDS; wave 0 has passed the grid barrier),
-// for O also after the attention merge, and S2 (phase outputs in LDS).
+// barriers: S1a (raw phase input in LDS; wave 0 has passed the grid
+// barrier), S1 (input ready: gains applied or attention merged) and S2
+// (phase outputs in LDS).
 
 // Streamer role (waves 1..7): kBlocksInFlight loads always in flight, in
 // stream order.  Every phase is a whole number of groups of kUnitsInFlight
 // units (zero-reading units pad it), so unit k of each group always sits in
 // register slot k: the steps below are unrolled over the slots and never
 // copy a register that a load is still filling.
-// Phases whose input is rmsnorm(x) * g, and their g.
-__device__ __forceinline__ bool norm_phase(const PhaseIt& id) {
-  return id.ph == PH_QKV || id.ph == PH_GU || id.ph == PH_LM;
-}
-__device__ __forceinline__ const float* norm_gains(const Params& P, const PhaseIt& id) {
-  if (id.ph == PH_LM) return P.gains + (size_t)P.L * 2 * P.d;
-  return P.gains + (size_t)id.l * 2 * P.d + (id.ph == PH_GU ? P.d : 0);
-}
-
+template <int MB>
 __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, int g0, int g1, const int* tab,
                                               float* xs, float* out, const float* gs, float* red, const int* si) {
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, B = P.B;
   const uint32_t lane16 = (uint32_t)lane * 16u;
-  const float* xl = xs + 8 * lane;
   Cursor cu;
   cursor_start(P, A, g0, g1, tab, cu);
   u32x4 buf[kBlocksInFlight];
@@ -758,8 +830,11 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
     if (id.ph == -2) continue;
     __syncthreads();   // S1a
     if (si[12] == 0) break;
-    if (norm_phase(id)) apply_gains(xs, gs, P.d, red);
-    if (id.ph == PH_O) merge_attention(P, A.pos0 + id.i, xs);
+    if (norm_phase(id)) {
+      if constexpr (MB == 1) apply_gains(xs, gs, P.d, red);
+      else apply_gains_batch(reinterpret_cast<_Float16*>(xs), xs + kMaxBatch * gemv_span(P.d) / 2, gs, P.d, B, red);
+    }
+    if (id.ph == PH_O) merge_attention<MB>(P, A.pos0 + id.i, xs);
     __syncthreads();   // S1
     if (is_gemv(id.ph)) {
       const int* e = tab + id.ph * kTabStride;
@@ -767,7 +842,9 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
       const int ngroups = (n + rfl(e[T_PAD])) / kUnitsInFlight;
       const int npc = rfl(e[T_NPC]);
       int t = rfl(e[T_T0]), col = rfl(e[T_COL]);
-      float a0 = 0.f, a1 = 0.f;
+      float a0[MB], a1[MB];
+#pragma unroll
+      for (int b = 0; b < MB; ++b) a0[b] = a1[b] = 0.f;
       int u = 0;
       for (int grp = 0; grp < ngroups; ++grp) {
         // the issue side runs one group ahead; phases hold whole groups, so
@@ -777,17 +854,36 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
         for (int k = 0; k < kUnitsInFlight; ++k) {
           wait_vm<kBlocksInFlight - 2>();
           if (u < n) {
-            const f32x4 xa = *reinterpret_cast<const f32x4*>(xl + 512 * col);
-            const f32x4 xb = *reinterpret_cast<const f32x4*>(xl + 512 * col + 4);
-            a0 = dot8(buf[2 * k], xa, xb, a0);
-            a1 = dot8(buf[2 * k + 1], xa, xb, a1);
-            if (col == npc - 1 || u == n - 1) {
-              const float y0 = wave_sum(a0), y1 = wave_sum(a1);
-              if (lane == 0) {
-                lds_add(out + 2 * t, y0);
-                lds_add(out + 2 * t + 1, y1);
+            if constexpr (MB == 1) {
+              const float* xl = xs + 8 * lane + 512 * col;
+              const f32x4 xa = *reinterpret_cast<const f32x4*>(xl);
+              const f32x4 xb = *reinterpret_cast<const f32x4*>(xl + 4);
+              a0[0] = dot8(buf[2 * k], xa, xb, a0[0]);
+              a1[0] = dot8(buf[2 * k + 1], xa, xb, a1[0]);
+            } else {
+              const int span = 512 * npc;
+              const _Float16* xl = reinterpret_cast<const _Float16*>(xs) + 8 * lane + 512 * col;
+#pragma unroll
+              for (int b = 0; b < MB; ++b) {
+                if (b < B) {
+                  const u32x4 xv = *reinterpret_cast<const u32x4*>(xl + (size_t)b * span);
+                  a0[b] = dot8h(buf[2 * k], xv, a0[b]);
+                  a1[b] = dot8h(buf[2 * k + 1], xv, a1[b]);
+                }
               }
-              a0 = a1 = 0.f;
+            }
+            if (col == npc - 1 || u == n - 1) {
+#pragma unroll
+              for (int b = 0; b < MB; ++b) {
+                if (b < B) {
+                  const float y0 = wave_sum(a0[b]), y1 = wave_sum(a1[b]);
+                  if (lane == 0) {
+                    lds_add(out + (2 * t) * MB + b, y0);
+                    lds_add(out + (2 * t + 1) * MB + b, y1);
+                  }
+                  a0[b] = a1[b] = 0.f;
+                }
+              }
               ++t;
             }
             if (++col == npc) col = 0;
@@ -802,29 +898,34 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
   wait_vm0();   // the zero-filled loads past the stream's end
 }
 
-extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident(const Params* __restrict__ Pp, Launch A) {
-  const Params& P = *Pp;
+template <int MB>
+__device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
+  using M = Lds<MB>;
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  float* xs = smem;
-  float* out = smem + kLdsOut;
-  float* xown = smem + kLdsOwn;
-  int* si = reinterpret_cast<int*>(smem + kLdsSi);
-  float* aux = smem + kLdsAux;
-  float* gs = smem + kLdsGain;
-  float* red = smem + kLdsRed;
-  int* tab_wg = reinterpret_cast<int*>(smem + kLdsTabWg);
+  float* xs = smem;                                   // input region (see Lds)
+  float* out = smem + M::Out;
+  float* xown = smem + M::Own;
+  float* red = smem + M::Red;
+  float* scl = smem + M::Scl;
+  int* si = reinterpret_cast<int*>(smem + M::Si);
+  float* aux = smem + M::Aux;
+  float* gs = smem + M::Gain;
+  int* tab_wg = reinterpret_cast<int*>(smem + M::TabWg);
   // wave index through readfirstlane: provably uniform, so the role split
   // below is a scalar branch and every per-wave value stays in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  int* tab = reinterpret_cast<int*>(smem + kLdsTab) + (wave > 0 ? (wave - 1) * 6 * kTabStride : 0);
+  int* tab = reinterpret_cast<int*>(smem + M::Tab) + (wave > 0 ? (wave - 1) * 6 * kTabStride : 0);
   const int total = A.n_tok * phases_per_token(P.L);
   const int g0 = A.phase_begin < 0 ? 0 : A.phase_begin;
   const int g1 = A.phase_end < total ? A.phase_end : total;
+  const int B = P.B;
+  // MB > 1: where the normed phases' fp32 inputs are staged (after the fp16 ones)
+  float* stage = xs + kMaxBatch * gemv_span(P.d) / 2;
 
   fill_tables(P, wave, tab_wg, tab);
   wait_lgkm0();
   if (wave > 0) {
-    streamer_role(P, A, g0, g1, tab, xs, out, gs, red, si);
+    streamer_role<MB>(P, A, g0, g1, tab, xs, out, gs, red, si);
     return;
   }
 
@@ -835,26 +936,30 @@ extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident(const Par
     if (trace && lane == 0 && ev < P.trace_stride) trace[ev] = wall_clock64();
     ++ev;
   };
+  const int own = kOwnFloats / MB;   // xown floats per sequence
   {
-    // this workgroup's rows of the residual stream
-    int b, e;
-    split(P.d / 2, blockIdx.x, gridDim.x, b, e);
-    for (int r = 2 * b + lane; r < 2 * e; r += 64) xown[r - 2 * b] = ld_coh(P.x + r);
+    // this workgroup's rows of each sequence's residual stream
+    int r0, r1;
+    split(P.d / 2, blockIdx.x, gridDim.x, r0, r1);
+    for (int b = 0; b < B; ++b)
+      for (int r = 2 * r0 + lane; r < 2 * r1; r += 64) xown[b * own + r - 2 * r0] = ld_coh(P.x + (size_t)b * P.d + r);
   }
   uint32_t epoch = A.bar_base;
   bool first = true, have_tok = false;
-  int tok_local = 0;
+  int tok_local[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) tok_local[b] = 0;
   int prev_ph = -3, prev_i = 0;
-  float prev_scale = 1.0f;
+  if (lane < kMaxBatch) scl[lane] = 1.0f;
   PhaseIt id = phase_at(P, A, g0);
   for (; id.g < g1; phase_next(P, A, id)) {
     if (id.ph == -2) continue;
     const int pos = A.pos0 + id.i;
     // outputs of the previous phase; this phase's LDS results start at zero
-    if (!first) w0_store_outputs(P, prev_ph, tab_wg, A.write_logits && prev_i == A.n_tok - 1, prev_scale, out, xown);
+    if (!first) w0_store_outputs<MB>(P, prev_ph, tab_wg, A.write_logits && prev_i == A.n_tok - 1, scl, out, xown);
     if (is_gemv(id.ph)) {
       const int np = rfl(tab_wg[2 * id.ph + 1]) - rfl(tab_wg[2 * id.ph]);
-      for (int t = lane; t < 2 * np; t += 64) out[t] = 0.f;
+      for (int t = lane; t < 2 * np * MB; t += 64) out[t] = 0.f;
     }
     const bool skip_bar = first || (id.ph == PH_QKV && id.l == 0 && have_tok);
     if (!skip_bar) {
@@ -863,7 +968,7 @@ extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident(const Par
     }
     auto wait = [&]() { return skip_bar ? true : w0_wait(P, epoch, A.fenced); };
     // the norm gains do not depend on the barrier: start them first
-    if (norm_phase(id)) w0_dma_vec(gs, norm_gains(P, id), P.d, false);
+    if (norm_phase(id)) w0_dma_vec(gs, norm_gains(P, id), P.d, 4, false);
     bool ok = true;
     if (id.ph == PH_ATTN) {
       switch (P.hd) {
@@ -874,25 +979,48 @@ extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident(const Par
         default: ok = w0_attention<128>(P, id.l, pos, aux, wait); break;
       }
     } else if (id.ph == PH_QKV && id.l == 0) {
-      int tok;
-      if (A.tok_src == TOK_PROMPT) tok = ldg(P.prompt + id.i);
-      else tok = have_tok ? tok_local : ld_coh(P.tok_cur);
-      have_tok = false;
-      tok = tok < 0 ? 0 : (tok >= P.V ? P.V - 1 : tok);
       ok = wait();
-      if (ok) w0_embed(P, tok, xs, xown);
+      if (ok) {
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+          if (b < B) {
+            int tok;
+            if (A.tok_src == TOK_PROMPT) tok = ldg(P.prompt + (size_t)b * A.n_tok + id.i);
+            else tok = have_tok ? tok_local[b] : ld_coh(P.tok_cur + b);
+            tok = tok < 0 ? 0 : (tok >= P.V ? P.V - 1 : tok);
+            w0_embed(P, b, tok, MB == 1 ? xs : stage + (size_t)b * gemv_span(P.d), xown, own);
+          }
+        }
+      }
+      have_tok = false;
     } else if (id.ph == PH_QKV || id.ph == PH_GU || id.ph == PH_LM) {
       ok = wait();
-      if (ok) w0_dma_vec(xs, P.x, P.d, true);
+      if (ok) {
+        if constexpr (MB == 1) {
+          w0_dma_vec(xs, P.x, P.d, 4, true);
+        } else {
+          for (int b = 0; b < B; ++b) w0_dma_vec(stage + (size_t)b * gemv_span(P.d), P.x + (size_t)b * P.d, P.d, 4, true);
+        }
+      }
     } else if (id.ph == PH_DOWN) {
       ok = wait();
-      if (ok) w0_dma_vec(xs, P.act, P.F, true);
+      if (ok) {
+        if constexpr (MB == 1) {
+          w0_dma_vec(xs, P.act, P.F, 4, true);
+        } else {
+          _Float16* xh = reinterpret_cast<_Float16*>(xs);
+          for (int b = 0; b < B; ++b)
+            w0_dma_vec(xh + (size_t)b * gemv_span(P.F), P.act16 + (size_t)b * P.F, P.F, 2, true);
+        }
+      }
     } else if (id.ph == PH_O) {
       ok = wait();
     } else {
       ok = wait();
       if (ok) {
-        tok_local = w0_argmax(P, id.i);
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+          if (b < B) tok_local[b] = w0_argmax(P, id.i, b);
         have_tok = true;
       }
     }
@@ -901,45 +1029,70 @@ extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident(const Par
     first = false;
     __syncthreads();   // S1a
     if (!ok) return;
-    if (norm_phase(id)) apply_gains(xs, gs, P.d, red);
-    if (id.ph == PH_O) merge_attention(P, pos, xs);
-    __syncthreads();   // S1
-    float scale = 1.0f;
     if (norm_phase(id)) {
-      float ss = 0.f;
+      if constexpr (MB == 1) apply_gains(xs, gs, P.d, red);
+      else apply_gains_batch(reinterpret_cast<_Float16*>(xs), stage, gs, P.d, B, red);
+    }
+    if (id.ph == PH_O) merge_attention<MB>(P, pos, xs);
+    __syncthreads();   // S1
+    // this phase's norm scale per sequence, used when its outputs are published
+    if (lane < kMaxBatch) {
+      float s = 1.0f;
+      if (norm_phase(id) && lane < B) {
+        float ss = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) ss += red[w];
-      scale = 1.0f / sqrtf(ss / (float)P.d + P.eps);
+        for (int w = 0; w < kWaves; ++w) ss += red[lane * kWaves + w];
+        s = 1.0f / sqrtf(ss / (float)P.d + P.eps);
+      }
+      scl[lane] = s;
     }
     stamp();
     __syncthreads();   // S2
     stamp();
     prev_ph = id.ph;
     prev_i = id.i;
-    prev_scale = scale;
   }
-  if (!first) w0_store_outputs(P, prev_ph, tab_wg, A.write_logits && prev_i == A.n_tok - 1, prev_scale, out, xown);
+  if (!first) w0_store_outputs<MB>(P, prev_ph, tab_wg, A.write_logits && prev_i == A.n_tok - 1, scl, out, xown);
   wait_vm0();
 }
 
+extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident(const Params* __restrict__ Pp, Launch A) {
+  dec_body<1>(*Pp, A);
+}
+extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident_batch(const Params* __restrict__ Pp, Launch A) {
+  dec_body<kMaxBatch>(*Pp, A);
+}
+
+namespace {
+const void* kernel_for(int batch) {
+  return batch > 1 ? (const void*)dec_resident_batch : (const void*)dec_resident;
+}
+}  // namespace
+
 int kernel_prepare() {
-  return (int)hipFuncSetAttribute((const void*)dec_resident, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  hipError_t e = hipFuncSetAttribute((const void*)dec_resident, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (e != hipSuccess) return (int)e;
+  return (int)hipFuncSetAttribute((const void*)dec_resident_batch, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  kLdsBytes);
 }
 
-int kernel_blocks_per_cu(int* out) {
-  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(out, (const void*)dec_resident, kThreads, kLdsBytes);
+int kernel_blocks_per_cu(int batch, int* out) {
+  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(out, kernel_for(batch), kThreads, kLdsBytes);
 }
 
-int kernel_launch_resident(const Params* P, const Launch& A, int grid, void* stream) {
+int kernel_launch_resident(const Params* P, const Launch& A, int grid, int batch, void* stream) {
   const Params* p = P;
   Launch a = A;
   void* args[] = {&p, &a};
-  return (int)hipLaunchCooperativeKernel((const void*)dec_resident, dim3(grid), dim3(kThreads), args, kLdsBytes,
+  return (int)hipLaunchCooperativeKernel(kernel_for(batch), dim3(grid), dim3(kThreads), args, kLdsBytes,
                                          static_cast<hipStream_t>(stream));
 }
 
-int kernel_launch_plain(const Params* P, const Launch& A, int grid, void* stream) {
-  hipLaunchKernelGGL(dec_resident, dim3(grid), dim3(kThreads), kLdsBytes, static_cast<hipStream_t>(stream), P, A);
+int kernel_launch_plain(const Params* P, const Launch& A, int grid, int batch, void* stream) {
+  if (batch > 1)
+    hipLaunchKernelGGL(dec_resident_batch, dim3(grid), dim3(kThreads), kLdsBytes, static_cast<hipStream_t>(stream), P, A);
+  else
+    hipLaunchKernelGGL(dec_resident, dim3(grid), dim3(kThreads), kLdsBytes, static_cast<hipStream_t>(stream), P, A);
   return (int)hipGetLastError();
 }
 

@@ -45,13 +45,27 @@ def test_exports_every_declared_symbol(lib):
     ("rms_eps", 0.0, B.DEC_ERR_BAD_DESC),
     ("rope_base", 1.0, B.DEC_ERR_BAD_DESC),
     ("flags", 1, B.DEC_ERR_BAD_DESC),
-    ("batch", 8, B.DEC_ERR_UNSUPPORTED),
+    ("batch", 0, B.DEC_ERR_BAD_DESC),
+    ("batch", 9, B.DEC_ERR_UNSUPPORTED),
     ("d_ffn", 8200, B.DEC_ERR_UNSUPPORTED),
 ])
 def test_desc_rules(lib, field, value, code):
     d = desc(**{field: value})
     assert B.check_desc(d) == code
     assert B.last_error()  # reason recorded for handle-less calls
+
+
+def test_batch_rules(lib):
+    # batched decode keeps every sequence's GEMV inputs in LDS: d_model <= 2560,
+    # d_ffn and n_heads*head_dim <= 7680 (padded to 512)
+    for b in (1, 2, 8):
+        assert B.check_desc(desc(batch=b)) == B.DEC_OK, B.last_error()
+    assert B.check_desc(B.ModelDesc.from_shape(synth.shape_for("dense2b"), batch=8)) == B.DEC_OK, B.last_error()
+    assert B.check_desc(desc(batch=2, d_model=3072)) == B.DEC_ERR_UNSUPPORTED
+    assert B.check_desc(desc(batch=2, d_ffn=8192)) == B.DEC_ERR_UNSUPPORTED
+    assert B.check_desc(desc(batch=1, d_model=3072)) == B.DEC_OK
+    # per-sequence buffers grow with the batch
+    assert B.arena_bytes(desc(batch=8), 256) > B.arena_bytes(desc(batch=1), 256)
 
 
 def test_valid_descs_and_arena(lib):
