@@ -280,6 +280,14 @@ const char* dec_last_error(const dec_handle* h);
  *   E        [vocab, d]
  *   W_lm     [lm_vocab, d]
  * Gains are not part of the image (they are uploaded as fp32).
+ * With batch == 1 every matrix is row-major.  With batch > 1 every matrix
+ * except E is stored in tiles of 16 rows x 32 columns (the A operand of the
+ * matrix-core instruction the batched kernel uses): tile (g, j) covers rows
+ * 16g..16g+15 and columns 32j..32j+31, tiles follow each other row-group
+ * first (index g * ceil(cols/32) + j), and inside a tile the 8 elements at
+ * element offset 8*l are row 16g + l%16, columns 32j + 8*(l/16) .. +7, for
+ * l = 0..63.  Rows and columns past the matrix are zero; each matrix region
+ * is ceil(rows/16) * ceil(cols/32) * 512 elements.
  */
 int dec_packed_bytes(const dec_model_desc* desc, size_t* out_bytes);
 int dec_pack(const dec_model_desc* desc, const uint16_t* const* host_tensors,

@@ -81,24 +81,58 @@ int check_desc_impl(const dec_model_desc* d, std::string* err) {
 // ---------------------------------------------------------------------------
 // packed image layout (elements)
 // ---------------------------------------------------------------------------
+// Batch 1: every matrix row-major.  Batch > 1: every GEMV matrix (not the
+// embedding) in tiles of 16 rows x 32 columns, one 1 KB tile per MFMA
+// operand (see tiled_index).
 struct Image {
   size_t off_qkv, off_o, off_gu, off_d, layer_stride, off_E, off_lm, total;
+  bool tiled;
 };
 
 size_t al128(size_t n) { return (n + 127) / 128 * 128; }
 
+// elements a [rows x cols] matrix occupies in the image
+size_t matrix_elems(size_t rows, size_t cols, bool tiled) {
+  if (!tiled) return rows * cols;
+  return ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols) * kTileElems;
+}
+
+// Tiled layout: tile (g, j) covers rows 16g..16g+15 and columns 32j..32j+31
+// and sits at tile index g * ceil(cols/32) + j.  Inside a tile, lane l's 8
+// elements (16 bytes at 16 l) are row 16g + l % 16, columns 32j + 8 (l / 16)
+// .. +7: the A operand of v_mfma_f32_16x16x32_f16 for a wave that loads the
+// tile with one 16-byte load per lane.  Padding rows and columns are zero.
+size_t tiled_index(size_t r, size_t c, size_t cols) {
+  const size_t kt = (cols + kTileCols - 1) / kTileCols;
+  const size_t tile = (r / kTileRows) * kt + c / kTileCols;
+  const size_t lane = (r % kTileRows) + kTileRows * ((c % kTileCols) / 8);
+  return tile * kTileElems + lane * 8 + c % 8;
+}
+
 Image image_layout(const dec_model_desc& d) {
   Image im;
   const size_t D = d.d_model, q = (size_t)d.n_heads * d.head_dim, F = d.d_ffn;
+  const bool t = d.batch > 1;
+  im.tiled = t;
   im.off_qkv = 0;
-  im.off_o = al128(im.off_qkv + 3 * q * D);
-  im.off_gu = al128(im.off_o + D * q);
-  im.off_d = al128(im.off_gu + 2 * F * D);
-  im.layer_stride = al128(im.off_d + D * F);
+  im.off_o = al128(im.off_qkv + matrix_elems(3 * q, D, t));
+  im.off_gu = al128(im.off_o + matrix_elems(D, q, t));
+  im.off_d = al128(im.off_gu + matrix_elems(2 * F, D, t));
+  im.layer_stride = al128(im.off_d + matrix_elems(D, F, t));
   im.off_E = im.layer_stride * d.n_layers;
   im.off_lm = al128(im.off_E + (size_t)d.vocab * D);
-  im.total = al128(im.off_lm + (size_t)d.lm_vocab * D);
+  im.total = al128(im.off_lm + matrix_elems(d.lm_vocab, D, t));
   return im;
+}
+
+// Row `row` (C elements) of a packed matrix with `cols` columns starting at
+// element `base`: copied as it is (row-major) or scattered into tiles.
+void put_row(uint16_t* image, size_t base, size_t row, const uint16_t* src, size_t cols, bool tiled) {
+  if (!tiled) {
+    std::memcpy(image + base + row * cols, src, cols * 2);
+    return;
+  }
+  for (size_t c = 0; c < cols; c += 8) std::memcpy(image + base + tiled_index(row, c, cols), src + c, 16);
 }
 
 // shape of canonical tensor `idx`
@@ -147,7 +181,7 @@ void place_tensor(const dec_model_desc& d, const Image& im, int idx, const uint1
     return;
   }
   if (idx == last) {
-    std::memcpy(image + im.off_lm + row0 * C, src, nrows * C * 2);
+    for (size_t i = 0; i < nrows; ++i) put_row(image, im.off_lm, row0 + i, src + i * C, C, im.tiled);
     return;
   }
   if (idx == last - 1) {
@@ -163,17 +197,16 @@ void place_tensor(const dec_model_desc& d, const Image& im, int idx, const uint1
         gains_out[((size_t)l * 2 + (kind == 5)) * D + row0 + i] = half_to_float(src[i]);
       return;
     case 1: case 2: case 3:  // Wq, Wk, Wv stacked into Wqkv
-      std::memcpy(lay + im.off_qkv + ((kind - 1) * q + row0) * C, src, nrows * C * 2);
+      for (size_t i = 0; i < nrows; ++i) put_row(lay, im.off_qkv, (kind - 1) * q + row0 + i, src + i * C, C, im.tiled);
       return;
     case 4:
-      std::memcpy(lay + im.off_o + row0 * C, src, nrows * C * 2);
+      for (size_t i = 0; i < nrows; ++i) put_row(lay, im.off_o, row0 + i, src + i * C, C, im.tiled);
       return;
     case 6: case 7:          // Wg -> even rows, Wu -> odd rows of Wgu
-      for (size_t i = 0; i < nrows; ++i)
-        std::memcpy(lay + im.off_gu + (2 * (row0 + i) + (kind == 7)) * C, src + i * C, C * 2);
+      for (size_t i = 0; i < nrows; ++i) put_row(lay, im.off_gu, 2 * (row0 + i) + (kind == 7), src + i * C, C, im.tiled);
       return;
     default:
-      std::memcpy(lay + im.off_d + row0 * C, src, nrows * C * 2);
+      for (size_t i = 0; i < nrows; ++i) put_row(lay, im.off_d, row0 + i, src + i * C, C, im.tiled);
       return;
   }
 }
@@ -413,7 +446,7 @@ int upload_weights(dec_handle* h, const dec_weights_src* src) {
     hipError_t e = hipMemcpy(dev_w + (size_t)l * local.layer_stride, stage.data(), local.layer_stride * 2, hipMemcpyHostToDevice);
     if (e != hipSuccess) rc = hip_fail(h, &h->err, e, "hipMemcpy(weights)");
   }
-  // embedding, final gain, LM head: already row-major, copied as they are
+  // embedding, final gain, LM head: row-major ones are copied as they are
   const int last = nt - 1;
   for (int idx : {0, last - 1, last}) {
     if (rc != DEC_OK) break;
@@ -426,7 +459,15 @@ int upload_weights(dec_handle* h, const dec_weights_src* src) {
       continue;
     }
     const size_t off = idx == 0 ? local.off_E : local.off_lm;
-    hipError_t e = hipMemcpy(dev_w + off, t, R * C * 2, hipMemcpyHostToDevice);
+    hipError_t e;
+    if (idx == last && local.tiled) {
+      // tiles: pack into a staging copy of the LM head's region first
+      stage.assign(local.total - local.off_lm, 0);
+      for (size_t r = 0; r < R; ++r) put_row(stage.data(), 0, r, t + r * C, C, true);
+      e = hipMemcpy(dev_w + off, stage.data(), stage.size() * 2, hipMemcpyHostToDevice);
+    } else {
+      e = hipMemcpy(dev_w + off, t, R * C * 2, hipMemcpyHostToDevice);
+    }
     if (e != hipSuccess) rc = hip_fail(h, &h->err, e, "hipMemcpy(embedding/LM head)");
   }
   if (f) std::fclose(f);
@@ -561,10 +602,15 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
     // fixed LDS buffers; the batch kernel keeps kMaxBatch sequences' slots
     auto per_wg = [&](long long n) { return (n + h->grid - 1) / h->grid; };
     const long long q = (long long)desc->n_heads * desc->head_dim;
-    const long long mb = desc->batch > 1 ? kMaxBatch : 1;
-    const long long need_out = mb * std::max({2 * per_wg(3 * q / 2), 2 * per_wg(desc->d_model / 2),
-                                              2 * per_wg(desc->d_ffn), 2 * per_wg(desc->lm_vocab / 2)});
-    if (need_out > kOutFloats || mb * 2 * per_wg(desc->d_model / 2) > kOwnFloats) {
+    const bool tiled = desc->batch > 1;
+    const long long mb = tiled ? kMaxBatch : 1;
+    // rows a workgroup owns in a matrix of `rows` rows: row pairs, or whole 16-row groups
+    auto rows_wg = [&](long long rows) {
+      return tiled ? kTileRows * per_wg((rows + kTileRows - 1) / kTileRows) : 2 * per_wg(rows / 2);
+    };
+    const long long need_out = mb * std::max({rows_wg(3 * q), rows_wg(desc->d_model), rows_wg(2LL * desc->d_ffn),
+                                              rows_wg(desc->lm_vocab)});
+    if (need_out > kOutFloats || mb * rows_wg(desc->d_model) > kOwnFloats) {
       fail(&h->err, DEC_ERR_UNSUPPORTED, "grid %d too small for this model (a workgroup would own %lld outputs)",
            h->grid, need_out);
       return bail(DEC_ERR_UNSUPPORTED);

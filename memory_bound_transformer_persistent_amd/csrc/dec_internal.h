@@ -28,6 +28,12 @@ constexpr int kOwnFloats = 256;             // LDS: a workgroup's rows of the re
 constexpr int kMaxBatch = 8;
 constexpr int kBatchSpanD = 2560;           // padded d_model (input of QKV, GU, LM; staged in fp32 too)
 constexpr int kBatchSpanK = 7680;           // padded d_ffn and n_heads*head_dim
+// The batched kernel multiplies weights by the inputs with MFMA
+// (v_mfma_f32_16x16x32_f16): its weights are packed in 1 KB tiles of 16 rows
+// x 32 columns, and a workgroup owns whole 16-row groups of every matrix.
+constexpr int kTileRows = 16;
+constexpr int kTileCols = 32;
+constexpr int kTileElems = kTileRows * kTileCols;
 constexpr int kLdsBytes = 160 * 1024;       // dynamic LDS per workgroup; > half a CU's 160 KB,
                                             // so exactly one workgroup runs per compute unit
 

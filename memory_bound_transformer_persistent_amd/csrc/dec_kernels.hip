@@ -15,9 +15,10 @@
 // wave instruction), reads its input vector from LDS, accumulates in fp32 and
 // reduces across the wave with DPP.  No MFMA: at one token per step there is
 // no dense contraction to feed it.  With several sequences at the same
-// position (batch), the same pass over the weights serves all of them: the
-// inputs sit in LDS as fp16 and each weight pair meets every sequence's input
-// through v_dot2_f32_f16.
+// position (batch), the same pass over the weights serves all of them and the
+// product is a skinny matrix multiply: the inputs sit in LDS as fp16, the
+// weights are packed as 16 x 32 tiles, and each 1 KB tile is one
+// v_mfma_f32_16x16x32_f16 against eight sequences' inputs.
 //
 // Cross-workgroup data (residual stream, q/k/v, attention partials, SwiGLU
 // output, KV-cache appends, argmax partials) is written with agent-coherent
@@ -53,11 +54,15 @@ constexpr int kStreamers = kWaves - 1;
 // own weight traffic.
 constexpr int kUnitsInFlight = 4;
 constexpr int kBlocksInFlight = 2 * kUnitsInFlight;
+// The batched kernel streams 1 KB weight tiles, one 16-byte load per lane each.
+constexpr int kTilesInFlight = 8;
 constexpr int kTabStride = 12;   // ints per (streamer, phase type) entry of the phase tables
+constexpr int kPlanInts = 16;    // per phase type: count, then up to 2 * kStreamers combine entries
 constexpr int kAuxFloats = 2048;
 
 // LDS map (floats) for a kernel built for up to MB sequences:
-// input region | out | xown | red | scales | si | aux | gains | phase tables.
+// input region | out | xown | red | scales | si | aux | gains | phase tables |
+// partial-output slots | combine plans.
 // MB == 1: the input region is the fp32 vector xs.  MB > 1: it holds the fp16
 // inputs of every sequence side by side (stride = the phase's padded row
 // length) and, for the normed phases, the fp32 residual vectors they come
@@ -69,7 +74,11 @@ struct Lds {
   static constexpr int Out = Region, Own = Out + kOutFloats, Red = Own + kOwnFloats;
   static constexpr int Scl = Red + kWaves * kMaxBatch, Si = Scl + kMaxBatch, Aux = Si + 16;
   static constexpr int Gain = Aux + kAuxFloats, TabWg = Gain + GainN, Tab = TabWg + 16;
-  static constexpr int End = Tab + kStreamers * 6 * kTabStride;
+  // batched kernel: a streamer's partial results for the (at most two)
+  // 16-row output groups it shares with other streamers
+  static constexpr int SlotN = MB == 1 ? 0 : kTileRows * MB;
+  static constexpr int Slot = Tab + kStreamers * 6 * kTabStride, Plan = Slot + kStreamers * 2 * SlotN;
+  static constexpr int End = Plan + (MB == 1 ? 0 : 6 * kPlanInts);
   static_assert(End * 4 <= kLdsBytes, "LDS map exceeds the allocation");
   static_assert(MB == 1 || 3 * kMaxBatch * kBatchSpanD / 2 <= Region, "staged fp32 inputs do not fit");
   static_assert(Gain % 4 == 0 && Region % 4 == 0, "16-byte alignment");
@@ -189,18 +198,6 @@ __device__ __forceinline__ float dot8(u32x4 w, f32x4 xa, f32x4 xb, float acc) {
   acc = __builtin_fmaf((float)h[7], xb[3], acc);
   return acc;
 }
-// 8 fp16 weights times 8 fp16 inputs, fp32 accumulate (v_dot2_f32_f16).  The
-// pairs are taken by value from whole vectors: this compiler's
-// __builtin_bit_cast of a vector element reads element 0.
-__device__ __forceinline__ float dot8h(u32x4 w, u32x4 x, float acc) {
-  const f16x8 a = __builtin_bit_cast(f16x8, w), b = __builtin_bit_cast(f16x8, x);
-  acc = __builtin_amdgcn_fdot2(f16x2{a[0], a[1]}, f16x2{b[0], b[1]}, acc, false);
-  acc = __builtin_amdgcn_fdot2(f16x2{a[2], a[3]}, f16x2{b[2], b[3]}, acc, false);
-  acc = __builtin_amdgcn_fdot2(f16x2{a[4], a[5]}, f16x2{b[4], b[5]}, acc, false);
-  acc = __builtin_amdgcn_fdot2(f16x2{a[6], a[7]}, f16x2{b[6], b[7]}, acc, false);
-  return acc;
-}
-
 __device__ __forceinline__ void split(int n, int g, int G, int& b, int& e) {
   b = (int)((long long)n * g / G);
   e = (int)((long long)n * (g + 1) / G);
@@ -240,10 +237,32 @@ __device__ __forceinline__ GemvWork work_of(const Params& P, int ph, int l) {
   return g;
 }
 
-// Streamer s's unit range [u0, u1) of a phase.
+// Rows and row length of the matrix of GEMV phase type ph.
+__device__ __forceinline__ void phase_shape(const Params& P, int ph, int& rows, int& K) {
+  switch (ph) {
+    case PH_QKV: rows = 3 * P.q; K = P.d; break;
+    case PH_O: rows = P.d; K = P.q; break;
+    case PH_GU: rows = 2 * P.F; K = P.d; break;
+    case PH_DOWN: rows = P.d; K = P.F; break;
+    default: rows = P.Vlm; K = P.d; break;
+  }
+}
+
+// Streamer s's unit range [u0, u1) of a phase: an even split, except that a
+// boundary that would fall inside a row pair which already holds the
+// previous boundary moves to that pair's end.  Then no row pair has more
+// than two contributors, and two ds_add_f32 into a zeroed word give the same
+// bits in either order: the sums do not depend on timing.
 __device__ __forceinline__ void streamer_units(const GemvWork& g, int s, int& u0, int& u1) {
-  const int n = (g.p1 - g.p0) * gemv_npc(g.K);
-  split(n, s - 1, kStreamers, u0, u1);
+  const int npc = gemv_npc(g.K), n = (g.p1 - g.p0) * npc;
+  int prev = 0;
+  for (int k = 1; k <= kStreamers; ++k) {
+    int b = (int)((long long)n * k / kStreamers);
+    if (b < prev) b = prev;
+    if (prev % npc != 0 && b / npc == prev / npc && b % npc != 0) b = min(n, (prev / npc + 1) * npc);
+    if (k == s) { u0 = prev; u1 = b; }
+    prev = b;
+  }
 }
 
 // Phase g of a launch: token i, layer l, phase type ph (-1: argmax, -2: not
@@ -299,6 +318,37 @@ enum TabField { T_LEFT, T_OFF, T_COL, T_NPC, T_ROWB, T_WRAP, T_TAIL, T_T0, T_NBY
 
 __device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Batched kernel: a workgroup owns whole 16-row groups [g0, g1) of each
+// matrix (its row pairs for the publisher: [8 g0, min(8 g1, rows/2))) and its
+// tiles, g0*KT .. g1*KT-1 in the tiled image, are one contiguous byte range
+// that the streamers split evenly.  Per streamer: T_LEFT tiles from byte
+// T_OFF, the first one in the workgroup's row group T_T0 at k-tile T_COL of
+// T_NPC; T_NBYTES bounds the matrix; T_PAD rounds to whole groups.
+__device__ __forceinline__ void fill_tables_tiled(const Params& P, int wave, int* tab_wg, int* tab) {
+  const int lane = threadIdx.x & 63;
+  if (lane >= 6 || lane == PH_ATTN) return;
+  int rows, K;
+  phase_shape(P, lane, rows, K);
+  const int rg = (rows + kTileRows - 1) / kTileRows, kt = (K + kTileCols - 1) / kTileCols;
+  int g0, g1;
+  split(rg, blockIdx.x, gridDim.x, g0, g1);
+  if (wave == 0) {
+    tab_wg[2 * lane] = (kTileRows / 2) * g0;
+    tab_wg[2 * lane + 1] = min((kTileRows / 2) * g1, rows / 2);
+    return;
+  }
+  int u0, u1;
+  split((g1 - g0) * kt, wave - 1, kStreamers, u0, u1);
+  int* e = tab + lane * kTabStride;
+  e[T_LEFT] = u1 - u0;
+  e[T_OFF] = (int)((uint32_t)(g0 * kt + u0) * 1024u);
+  e[T_COL] = u0 % kt;
+  e[T_NPC] = kt;
+  e[T_T0] = u0 / kt;
+  e[T_NBYTES] = (int)((uint32_t)(rg * kt) * 1024u);
+  e[T_PAD] = (kTilesInFlight - (u1 - u0) % kTilesInFlight) % kTilesInFlight;
+}
+
 __device__ __forceinline__ void fill_tables(const Params& P, int wave, int* tab_wg, int* tab) {
   const int lane = threadIdx.x & 63;
   if (lane >= 6 || lane == PH_ATTN) return;
@@ -324,6 +374,82 @@ __device__ __forceinline__ void fill_tables(const Params& P, int wave, int* tab_
   e[T_NBYTES] = (int)((uint32_t)w.rows * rowb);
   // zero-reading units that round the phase up to whole groups of kUnitsInFlight
   e[T_PAD] = (kUnitsInFlight - (u1 - u0) % kUnitsInFlight) % kUnitsInFlight;
+}
+
+// Deterministic partial sums in the batched kernel, where a 16-row group's
+// tiles are usually split over several streamers.  A group that one streamer
+// computes entirely is stored by it directly.  A group several streamers
+// share (only the first or last group of a streamer's range can be shared)
+// is stored by each of them in its own slot, and wave 0 adds the slots in
+// streamer order: the result does not depend on which streamer finished
+// first.  The plan lists, per phase type, the shared (streamer, end) slots in
+// that order; an entry is slot | group << 4 | (first slot of its group) << 28.
+__device__ __forceinline__ bool whole_group(int t, int kt, int u0, int u1) { return t * kt >= u0 && (t + 1) * kt <= u1; }
+
+__device__ __forceinline__ void build_plans(const int* tab_all, int* plan) {
+  const int lane = threadIdx.x & 63;
+  if (lane >= 6 || lane == PH_ATTN) return;
+  int cnt = 0, prev = -1;
+  int* pl = plan + lane * kPlanInts;
+  for (int s = 0; s < kStreamers; ++s) {
+    const int* e = tab_all + (s * 6 + lane) * kTabStride;
+    const int n = e[T_LEFT];
+    if (n <= 0) continue;
+    const int kt = e[T_NPC], t0 = e[T_T0], u0 = t0 * kt + e[T_COL], u1 = u0 + n, t1 = (u1 - 1) / kt;
+    for (int w = 0; w < 2; ++w) {
+      const int t = w == 0 ? t0 : t1;
+      if (w == 1 && t1 == t0) break;
+      if (whole_group(t, kt, u0, u1)) continue;
+      pl[1 + cnt] = (s * 2 + w) | (t << 4) | ((t != prev ? 1 : 0) << 28);
+      prev = t;
+      ++cnt;
+    }
+  }
+  pl[0] = cnt;
+}
+
+// Wave 0, after the streamers have stored a phase's results: out[group] =
+// the sum of its shared slots, added in streamer order.  Lane k holds plan
+// entry k; readlane broadcasts it, so the slot reads do not wait on each other.
+template <int MB>
+__device__ __forceinline__ void w0_combine(int ph, const int* plan, const float* slots, float* out) {
+  constexpr int SN = Lds<MB>::SlotN, NE = 2 * kStreamers;
+  static_assert(SN % 64 == 0, "slot elements are spread over the wave's lanes");
+  const int lane = threadIdx.x & 63;
+  const int* pl = plan + ph * kPlanInts;
+  const int cnt = rfl(pl[0]);
+  if (cnt == 0) return;
+  const int mine = pl[1 + (lane < NE ? lane : 0)];
+#pragma unroll
+  for (int i0 = 0; i0 < SN; i0 += 64) {
+    const int i = i0 + lane;
+    float v[NE];
+#pragma unroll
+    for (int k = 0; k < NE; ++k) {
+      const int ent = __builtin_amdgcn_readlane(mine, k);
+      v[k] = k < cnt ? slots[(ent & 15) * SN + i] : 0.f;
+    }
+    float acc = 0.f;
+    int cur = -1;
+#pragma unroll
+    for (int k = 0; k < NE; ++k) {
+      if (k < cnt) {
+        const int ent = __builtin_amdgcn_readlane(mine, k);
+        if ((ent >> 28) & 1) {
+          if (cur >= 0) out[cur * SN + i] = acc;
+          acc = v[k];
+          cur = (ent >> 4) & 0xFFFFFF;
+        } else {
+          acc += v[k];
+        }
+      }
+    }
+    if (cur >= 0) out[cur * SN + i] = acc;
+  }
+}
+
+__device__ __forceinline__ void lds_add(float* p, float v) {
+  __builtin_amdgcn_ds_faddf((__attribute__((address_space(3))) float*)p, v, 0, 0, false);
 }
 
 __device__ __forceinline__ const uint16_t* gemv_base(const Params& P, int ph, int l) {
@@ -402,9 +528,52 @@ __device__ __forceinline__ void issue_unit(Cursor& cu, uint32_t lane16, u32x4& b
   cu.col = live ? (last_col ? 0u : cu.col + 1u) : cu.col;
 }
 
-__device__ __forceinline__ void lds_add(float* p, float v) {
-  __builtin_amdgcn_ds_faddf((__attribute__((address_space(3))) float*)p, v, 0, 0, false);
+// Tile stream of the batched kernel: a streamer's tiles of a phase are
+// consecutive 1 KB blocks, so its cursor is a byte offset and a count.
+struct TileCursor {
+  PhaseIt it;
+  uint32_t left, pad, off;
+  rsrc_t r;
+};
+__device__ __forceinline__ bool tcursor_take(const Params& P, const int* tab, TileCursor& cu) {
+  if (!is_gemv(cu.it.ph)) return false;
+  const int* e = tab + cu.it.ph * kTabStride;
+  const int left = rfl(e[T_LEFT]);
+  if (left <= 0) return false;
+  cu.left = (uint32_t)left;
+  cu.pad = (uint32_t)rfl(e[T_PAD]);
+  cu.off = (uint32_t)rfl(e[T_OFF]);
+  cu.r = make_rsrc(gemv_base(P, cu.it.ph, cu.it.l), (uint32_t)rfl(e[T_NBYTES]));
+  return true;
 }
+__device__ __forceinline__ void tcursor_start(const Params& P, const Launch& A, int g0, int g1, const int* tab,
+                                              TileCursor& cu) {
+  cu.left = cu.pad = cu.off = 0;
+  cu.r = make_rsrc(P.w, 0);
+  if (g0 >= g1) { cu.it.g = g1; return; }
+  cu.it = phase_at(P, A, g0);
+  while (!tcursor_take(P, tab, cu)) {
+    phase_next(P, A, cu.it);
+    if (cu.it.g >= g1) return;
+  }
+}
+__device__ __forceinline__ void tcursor_next(const Params& P, const Launch& A, int g1, const int* tab,
+                                             TileCursor& cu) {
+  do {
+    phase_next(P, A, cu.it);
+    if (cu.it.g >= g1) return;
+  } while (!tcursor_take(P, tab, cu));
+}
+// Load the cursor's next tile into slot k (16 B per lane); advance.  Past the
+// stream's end the load is out of range (a distinct offset per slot) and reads 0.
+__device__ __forceinline__ void issue_tile(TileCursor& cu, uint32_t lane16, int k, u32x4& b) {
+  const bool live = cu.left > 0;
+  b = ld_nt(cu.r, live ? cu.off + lane16 : kOOB + 16u * (uint32_t)k);
+  cu.left -= live ? 1u : 0u;
+  cu.pad -= (!live && cu.pad > 0) ? 1u : 0u;
+  cu.off += live ? 1024u : 0u;
+}
+
 
 // ---------------------------------------------------------------------------
 // wave 0: grid barrier
@@ -503,14 +672,33 @@ __device__ __forceinline__ void apply_gains_batch(_Float16* xh, const float* st,
   }
 }
 
+// The rows [r0, r1) of the residual stream this workgroup owns: the rows it
+// computes in the O and down phases (row pairs at batch 1, whole 16-row
+// groups in the batched kernel).
+template <int MB>
+__device__ __forceinline__ void own_rows(const Params& P, int& r0, int& r1) {
+  if constexpr (MB == 1) {
+    int p0, p1;
+    split(P.d / 2, blockIdx.x, gridDim.x, p0, p1);
+    r0 = 2 * p0;
+    r1 = 2 * p1;
+  } else {
+    int g0, g1;
+    split((P.d + kTileRows - 1) / kTileRows, blockIdx.x, gridDim.x, g0, g1);
+    r0 = min(P.d, kTileRows * g0);
+    r1 = min(P.d, kTileRows * g1);
+  }
+}
+
 // Layer-0 input of sequence b: x = E[tok] (fp16 -> fp32) into dst (raw, zero
 // past d).  This workgroup's rows of x go to xown (own floats per sequence)
 // and to global x.
+template <int MB>
 __device__ __forceinline__ void w0_embed(const Params& P, int b, int tok, float* dst, float* xown, int own) {
   const int lane = threadIdx.x & 63, d = P.d;
   const _Float16* e = reinterpret_cast<const _Float16*>(P.w + P.off_E + (size_t)tok * d);
   int r0, r1;
-  split(d / 2, blockIdx.x, gridDim.x, r0, r1);
+  own_rows<MB>(P, r0, r1);
   const int span = gemv_span(d);
   for (int i = 8 * lane; i < span; i += 512) {
     f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
@@ -523,8 +711,8 @@ __device__ __forceinline__ void w0_embed(const Params& P, int b, int tok, float*
     *reinterpret_cast<f32x4*>(dst + i + 4) = hi;
   }
   wait_lgkm0();
-  for (int r = 2 * r0 + lane; r < 2 * r1; r += 64) {
-    xown[b * own + r - 2 * r0] = dst[r];
+  for (int r = r0 + lane; r < r1; r += 64) {
+    xown[b * own + r - r0] = dst[r];
     st_coh(P.x + (size_t)b * d + r, dst[r]);
   }
 }
@@ -815,10 +1003,9 @@ __device__ __forceinline__ int w0_argmax(const Params& P, int i, int b) {
 // units (zero-reading units pad it), so unit k of each group always sits in
 // register slot k: the steps below are unrolled over the slots and never
 // copy a register that a load is still filling.
-template <int MB>
 __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, int g0, int g1, const int* tab,
                                               float* xs, float* out, const float* gs, float* red, const int* si) {
-  const int lane = threadIdx.x & 63, B = P.B;
+  const int lane = threadIdx.x & 63;
   const uint32_t lane16 = (uint32_t)lane * 16u;
   Cursor cu;
   cursor_start(P, A, g0, g1, tab, cu);
@@ -830,11 +1017,8 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
     if (id.ph == -2) continue;
     __syncthreads();   // S1a
     if (si[12] == 0) break;
-    if (norm_phase(id)) {
-      if constexpr (MB == 1) apply_gains(xs, gs, P.d, red);
-      else apply_gains_batch(reinterpret_cast<_Float16*>(xs), xs + kMaxBatch * gemv_span(P.d) / 2, gs, P.d, B, red);
-    }
-    if (id.ph == PH_O) merge_attention<MB>(P, A.pos0 + id.i, xs);
+    if (norm_phase(id)) apply_gains(xs, gs, P.d, red);
+    if (id.ph == PH_O) merge_attention<1>(P, A.pos0 + id.i, xs);
     __syncthreads();   // S1
     if (is_gemv(id.ph)) {
       const int* e = tab + id.ph * kTabStride;
@@ -842,9 +1026,7 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
       const int ngroups = (n + rfl(e[T_PAD])) / kUnitsInFlight;
       const int npc = rfl(e[T_NPC]);
       int t = rfl(e[T_T0]), col = rfl(e[T_COL]);
-      float a0[MB], a1[MB];
-#pragma unroll
-      for (int b = 0; b < MB; ++b) a0[b] = a1[b] = 0.f;
+      float a0 = 0.f, a1 = 0.f;
       int u = 0;
       for (int grp = 0; grp < ngroups; ++grp) {
         // the issue side runs one group ahead; phases hold whole groups, so
@@ -854,42 +1036,97 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
         for (int k = 0; k < kUnitsInFlight; ++k) {
           wait_vm<kBlocksInFlight - 2>();
           if (u < n) {
-            if constexpr (MB == 1) {
-              const float* xl = xs + 8 * lane + 512 * col;
-              const f32x4 xa = *reinterpret_cast<const f32x4*>(xl);
-              const f32x4 xb = *reinterpret_cast<const f32x4*>(xl + 4);
-              a0[0] = dot8(buf[2 * k], xa, xb, a0[0]);
-              a1[0] = dot8(buf[2 * k + 1], xa, xb, a1[0]);
-            } else {
-              const int span = 512 * npc;
-              const _Float16* xl = reinterpret_cast<const _Float16*>(xs) + 8 * lane + 512 * col;
-#pragma unroll
-              for (int b = 0; b < MB; ++b) {
-                if (b < B) {
-                  const u32x4 xv = *reinterpret_cast<const u32x4*>(xl + (size_t)b * span);
-                  a0[b] = dot8h(buf[2 * k], xv, a0[b]);
-                  a1[b] = dot8h(buf[2 * k + 1], xv, a1[b]);
-                }
-              }
-            }
+            const float* xl = xs + 8 * lane + 512 * col;
+            const f32x4 xa = *reinterpret_cast<const f32x4*>(xl);
+            const f32x4 xb = *reinterpret_cast<const f32x4*>(xl + 4);
+            a0 = dot8(buf[2 * k], xa, xb, a0);
+            a1 = dot8(buf[2 * k + 1], xa, xb, a1);
             if (col == npc - 1 || u == n - 1) {
-#pragma unroll
-              for (int b = 0; b < MB; ++b) {
-                if (b < B) {
-                  const float y0 = wave_sum(a0[b]), y1 = wave_sum(a1[b]);
-                  if (lane == 0) {
-                    lds_add(out + (2 * t) * MB + b, y0);
-                    lds_add(out + (2 * t + 1) * MB + b, y1);
-                  }
-                  a0[b] = a1[b] = 0.f;
-                }
+              const float y0 = wave_sum(a0), y1 = wave_sum(a1);
+              if (lane == 0) {   // at most two contributors (streamer_units)
+                lds_add(out + 2 * t, y0);
+                lds_add(out + 2 * t + 1, y1);
               }
+              a0 = a1 = 0.f;
               ++t;
             }
             if (++col == npc) col = 0;
           }
           ++u;
           issue_unit(cu, lane16, buf[2 * k], buf[2 * k + 1]);
+        }
+      }
+    }
+    __syncthreads();   // S2
+  }
+  wait_vm0();   // the zero-filled loads past the stream's end
+}
+
+// Streamer role of the batched kernel (waves 1..7): the same walk over the
+// phases, but the stream is 1 KB weight tiles, kTilesInFlight in flight, and
+// each tile is one MFMA.  Lane l supplies the B operand for sequence
+// (l % 16) mod MB at k offset 8 (l / 16): 8 fp16 inputs from LDS.  Columns
+// 8..15 repeat sequences 0..7 and columns of absent sequences hold stale
+// inputs; neither is published.  A 16-row group's fp32 accumulator goes into
+// LDS (ds_add_f32, per sequence) when the group or the streamer's range ends.
+template <int MB>
+__device__ __forceinline__ void streamer_tiles(const Params& P, const Launch& A, int g0, int g1, const int* tab,
+                                               float* xs, float* out, float* slot, const float* gs, float* red,
+                                               const int* si) {
+  static_assert(MB == 8, "the MFMA B operand maps columns to sequences mod 8");
+  const int lane = threadIdx.x & 63, B = P.B;
+  const uint32_t lane16 = (uint32_t)lane * 16u;
+  const int col = lane & 15, kseg = lane >> 4, seq = col & (MB - 1);
+  TileCursor cu;
+  tcursor_start(P, A, g0, g1, tab, cu);
+  u32x4 buf[kTilesInFlight];
+#pragma unroll
+  for (int k = 0; k < kTilesInFlight; ++k) issue_tile(cu, lane16, k, buf[k]);
+  PhaseIt id = phase_at(P, A, g0);
+  for (; id.g < g1; phase_next(P, A, id)) {
+    if (id.ph == -2) continue;
+    __syncthreads();   // S1a
+    if (si[12] == 0) break;
+    if (norm_phase(id))
+      apply_gains_batch(reinterpret_cast<_Float16*>(xs), xs + kMaxBatch * gemv_span(P.d) / 2, gs, P.d, B, red);
+    if (id.ph == PH_O) merge_attention<MB>(P, A.pos0 + id.i, xs);
+    __syncthreads();   // S1
+    if (is_gemv(id.ph)) {
+      const int* e = tab + id.ph * kTabStride;
+      const int n = rfl(e[T_LEFT]);
+      const int ngroups = (n + rfl(e[T_PAD])) / kTilesInFlight;
+      const int kt = rfl(e[T_NPC]);
+      const int t0 = rfl(e[T_T0]), u0 = t0 * kt + rfl(e[T_COL]), u1 = u0 + n;
+      int t = t0, j = rfl(e[T_COL]);
+      const _Float16* xb = reinterpret_cast<const _Float16*>(xs) + seq * gemv_span(phase_k(P, id.ph)) + 8 * kseg;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      int u = 0;
+      for (int grp = 0; grp < ngroups; ++grp) {
+        if (cu.left == 0 && cu.pad == 0 && cu.it.g < g1) tcursor_next(P, A, g1, tab, cu);
+#pragma unroll
+        for (int k = 0; k < kTilesInFlight; ++k) {
+          wait_vm<kTilesInFlight - 1>();
+          if (u < n) {
+            const f16x8 bv = *reinterpret_cast<const f16x8*>(xb + kTileCols * j);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, buf[k]), bv, acc, 0, 0, 0);
+            if (++j == kt || u == n - 1) {
+              if (col < B) {
+                // rows 4 kseg .. 4 kseg + 3 of the group, sequence col
+                float* o = (whole_group(t, kt, u0, u1) ? out + kTileRows * MB * t
+                                                       : slot + (t == t0 ? 0 : kTileRows * MB)) +
+                           4 * kseg * MB + col;
+                const float c0 = acc[0], c1 = acc[1], c2 = acc[2], c3 = acc[3];
+                o[0] = c0;
+                o[MB] = c1;
+                o[2 * MB] = c2;
+                o[3 * MB] = c3;
+              }
+              acc = f32x4{0.f, 0.f, 0.f, 0.f};
+              if (j == kt) { j = 0; ++t; }
+            }
+          }
+          ++u;
+          issue_tile(cu, lane16, k, buf[k]);
         }
       }
     }
@@ -914,7 +1151,10 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   // wave index through readfirstlane: provably uniform, so the role split
   // below is a scalar branch and every per-wave value stays in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  int* tab = reinterpret_cast<int*>(smem + M::Tab) + (wave > 0 ? (wave - 1) * 6 * kTabStride : 0);
+  int* tab_all = reinterpret_cast<int*>(smem + M::Tab);
+  int* tab = tab_all + (wave > 0 ? (wave - 1) * 6 * kTabStride : 0);
+  float* slots = smem + M::Slot;
+  int* plan = reinterpret_cast<int*>(smem + M::Plan);
   const int total = A.n_tok * phases_per_token(P.L);
   const int g0 = A.phase_begin < 0 ? 0 : A.phase_begin;
   const int g1 = A.phase_end < total ? A.phase_end : total;
@@ -922,11 +1162,18 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   // MB > 1: where the normed phases' fp32 inputs are staged (after the fp16 ones)
   float* stage = xs + kMaxBatch * gemv_span(P.d) / 2;
 
-  fill_tables(P, wave, tab_wg, tab);
+  if constexpr (MB == 1) fill_tables(P, wave, tab_wg, tab);
+  else fill_tables_tiled(P, wave, tab_wg, tab);
   wait_lgkm0();
+  __syncthreads();   // every streamer's tables are in LDS
   if (wave > 0) {
-    streamer_role<MB>(P, A, g0, g1, tab, xs, out, gs, red, si);
+    if constexpr (MB == 1) streamer_role(P, A, g0, g1, tab, xs, out, gs, red, si);
+    else streamer_tiles<MB>(P, A, g0, g1, tab, xs, out, slots + (wave - 1) * 2 * M::SlotN, gs, red, si);
     return;
+  }
+  if constexpr (MB > 1) {
+    build_plans(tab_all, plan);
+    wait_lgkm0();
   }
 
   // wave 0: control
@@ -940,9 +1187,9 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   {
     // this workgroup's rows of each sequence's residual stream
     int r0, r1;
-    split(P.d / 2, blockIdx.x, gridDim.x, r0, r1);
+    own_rows<MB>(P, r0, r1);
     for (int b = 0; b < B; ++b)
-      for (int r = 2 * r0 + lane; r < 2 * r1; r += 64) xown[b * own + r - 2 * r0] = ld_coh(P.x + (size_t)b * P.d + r);
+      for (int r = r0 + lane; r < r1; r += 64) xown[b * own + r - r0] = ld_coh(P.x + (size_t)b * P.d + r);
   }
   uint32_t epoch = A.bar_base;
   bool first = true, have_tok = false;
@@ -956,7 +1203,11 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     if (id.ph == -2) continue;
     const int pos = A.pos0 + id.i;
     // outputs of the previous phase; this phase's LDS results start at zero
-    if (!first) w0_store_outputs<MB>(P, prev_ph, tab_wg, A.write_logits && prev_i == A.n_tok - 1, scl, out, xown);
+    if (!first) {
+      if constexpr (MB > 1)
+        if (is_gemv(prev_ph)) w0_combine<MB>(prev_ph, plan, slots, out);
+      w0_store_outputs<MB>(P, prev_ph, tab_wg, A.write_logits && prev_i == A.n_tok - 1, scl, out, xown);
+    }
     if (is_gemv(id.ph)) {
       const int np = rfl(tab_wg[2 * id.ph + 1]) - rfl(tab_wg[2 * id.ph]);
       for (int t = lane; t < 2 * np * MB; t += 64) out[t] = 0.f;
@@ -988,7 +1239,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
             if (A.tok_src == TOK_PROMPT) tok = ldg(P.prompt + (size_t)b * A.n_tok + id.i);
             else tok = have_tok ? tok_local[b] : ld_coh(P.tok_cur + b);
             tok = tok < 0 ? 0 : (tok >= P.V ? P.V - 1 : tok);
-            w0_embed(P, b, tok, MB == 1 ? xs : stage + (size_t)b * gemv_span(P.d), xown, own);
+            w0_embed<MB>(P, b, tok, MB == 1 ? xs : stage + (size_t)b * gemv_span(P.d), xown, own);
           }
         }
       }
@@ -1052,7 +1303,11 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     prev_ph = id.ph;
     prev_i = id.i;
   }
-  if (!first) w0_store_outputs<MB>(P, prev_ph, tab_wg, A.write_logits && prev_i == A.n_tok - 1, scl, out, xown);
+  if (!first) {
+    if constexpr (MB > 1)
+      if (is_gemv(prev_ph)) w0_combine<MB>(prev_ph, plan, slots, out);
+    w0_store_outputs<MB>(P, prev_ph, tab_wg, A.write_logits && prev_i == A.n_tok - 1, scl, out, xown);
+  }
   wait_vm0();
 }
 

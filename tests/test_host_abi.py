@@ -108,6 +108,44 @@ def test_packer_layout_round_trip(lib):
     np.testing.assert_array_equal(img[off_lm: off_lm + s.lm_vocab * D].reshape(s.lm_vocab, D), bits(t[-1]))
 
 
+def _untile(region, rows, cols):
+    """Inverse of the tiled layout documented in dec.h (16 x 32 tiles, lane-major inside)."""
+    rg, kt = -(-rows // 16), -(-cols // 32)
+    t = region[:rg * kt * 512].reshape(rg, kt, 4, 16, 8)        # [g, j, l // 16, l % 16, element]
+    return t.transpose(0, 3, 1, 2, 4).reshape(rg * 16, kt * 32), rg * kt * 512
+
+
+def test_packer_tiled_layout_for_batch(lib):
+    # rows and row lengths that are not multiples of 16 / 32 exercise the zero padding
+    s = TINY.with_(n_layers=2, n_heads=3, head_dim=8, d_ffn=40, vocab=64, lm_vocab=50)
+    t = synth.make_weights(s, seed=4)
+    d = B.ModelDesc.from_shape(s, batch=2)
+    assert B.check_desc(d) == B.DEC_OK, B.last_error()
+    img = B.pack(d, t)
+    assert img.nbytes == B.packed_bytes(d)
+    names = synth.tensor_names(s)
+    bits = lambda a: np.ascontiguousarray(a).view(np.uint16)
+    al = lambda n: (n + 127) // 128 * 128
+    D, q, F = s.d_model, s.qkv_width, s.d_ffn
+    off = 0
+    for l in range(s.n_layers):
+        get = lambda n: bits(t[names.index(f"{n}.{l}")])
+        gu = np.empty((2 * F, D), np.uint16)
+        gu[0::2], gu[1::2] = get("Wg"), get("Wu")
+        for mat in (np.concatenate([get("Wq"), get("Wk"), get("Wv")]), get("Wo"), gu, get("Wd")):
+            R, C = mat.shape
+            full, n = _untile(img[off:], R, C)
+            np.testing.assert_array_equal(full[:R, :C], mat)
+            assert not full[R:].any() and not full[:, C:].any()
+            off = al(off + n)
+    np.testing.assert_array_equal(img[off: off + s.vocab * D].reshape(s.vocab, D), bits(t[0]))   # E stays row-major
+    off = al(off + s.vocab * D)
+    full, n = _untile(img[off:], s.lm_vocab, D)
+    np.testing.assert_array_equal(full[:s.lm_vocab, :D], bits(t[-1]))
+    assert not full[s.lm_vocab:].any()
+    assert off + n <= img.size
+
+
 def test_pack_rejects_wrong_count(lib):
     d = desc()
     t = synth.make_weights(TINY)
