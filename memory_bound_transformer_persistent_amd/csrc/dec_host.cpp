@@ -73,6 +73,7 @@ int check_desc_impl(const dec_model_desc* d, std::string* err) {
   if (big >= (1LL << 31)) return fail(err, DEC_ERR_UNSUPPORTED, "a weight matrix is 2 GiB or larger");
   if (2LL * d->max_ctx * hd >= (1LL << 31)) return fail(err, DEC_ERR_UNSUPPORTED, "KV cache of one head is 2 GiB or larger");
   const int hb = d->batch * d->n_heads;
+  if (hb > kMaxHeads) return fail(err, DEC_ERR_UNSUPPORTED, "batch x n_heads must be <= %d", kMaxHeads);
   if ((long long)hb * max_attn_chunks(d->max_ctx, hb, 1024) > 65536)
     return fail(err, DEC_ERR_UNSUPPORTED, "too many attention partials (batch x n_heads x chunks > 65536)");
   return DEC_OK;
@@ -275,7 +276,7 @@ bool same_shape(const dec_model_desc& a, const dec_model_desc& b) {
 // device arena layout (bytes)
 // ---------------------------------------------------------------------------
 struct Arena {
-  size_t w, gains, rope, kv, x, qkv, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out, prompt, ctl, params, trace, total;
+  size_t w, gains, rope, kv, x, qkv, att_o, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out, prompt, ctl, params, trace, total;
 };
 
 Arena arena_layout(const dec_model_desc& d, int G) {
@@ -292,6 +293,7 @@ Arena arena_layout(const dec_model_desc& d, int G) {
   a.kv = take((size_t)d.n_layers * 2 * hb * d.max_ctx * d.head_dim * 2);
   a.x = take(B * D * 4);
   a.qkv = take(B * 3 * q * 4);
+  a.att_o = take(B * q * 4);
   a.part = take(hb * mc * d.head_dim * 4);
   a.pml = take(hb * mc * 2 * 4);
   a.act = take(B * d.d_ffn * 4);
@@ -680,6 +682,8 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
   P.kv = reinterpret_cast<uint16_t*>(b + h->ar.kv);
   P.x = reinterpret_cast<float*>(b + h->ar.x);
   P.qkv = reinterpret_cast<float*>(b + h->ar.qkv);
+  P.att_o = reinterpret_cast<float*>(b + h->ar.att_o);
+  P.att_o16 = reinterpret_cast<uint16_t*>(b + h->ar.att_o);
   P.part = reinterpret_cast<float*>(b + h->ar.part);
   P.pml = reinterpret_cast<float*>(b + h->ar.pml);
   P.act = reinterpret_cast<float*>(b + h->ar.act);

@@ -67,7 +67,9 @@ struct Params {
   int B;                      // sequences decoded together (batch)
   uint16_t* kv;               // [L][2][B][H][max_ctx][hd] fp16
   float* x;                   // residual stream [B][d]
-  float* qkv;                 // [B][3q]
+  float* qkv;                 // [B][3q]: rotated, scaled q in the first q of each sequence
+  float* att_o;               // attention output [B][q] (batch 1, fp32)
+  uint16_t* att_o16;          // attention output [B][q] (batch > 1, fp16; same memory as att_o)
   float* part;                // attention partial sums [B*H][max_chunks][hd]
   float* pml;                 // attention partial (max, sum) [B*H][max_chunks][2]
   float* act;                 // SwiGLU output [F] (batch 1, fp32)

@@ -718,101 +718,84 @@ __device__ __forceinline__ void w0_embed(const Params& P, int b, int tok, float*
 }
 
 // ---------------------------------------------------------------------------
-// wave 0: attention
+// attention
 // ---------------------------------------------------------------------------
 // Single-query attention of every head of every sequence over positions
 // 0..pos, split into chunks of positions; (sequence-head, chunk) units go
-// round-robin over workgroups.  A lane group of HD/8 lanes holds one
+// round-robin over the workgroups.  The QKV phase has already rotated and
+// scaled q and appended this position's key and value to the cache, so a
+// unit reads q and cached rows only.  A lane group of HD/8 lanes holds one
 // position (16 B of its K and V row per lane); K and V of NPASS*64/(HD/8)
 // positions are loaded together and an online softmax runs across such
-// groups.  The first group's loads are issued before the grid barrier
-// releases (`wait` runs the barrier wait once): cached positions do not
-// depend on this token.  Each unit stores an unnormalised partial (max m, sum
-// of exp l, sum of exp * V) that the O phase merges.
-template <int HD, class Wait>
-__device__ __forceinline__ bool w0_attention(const Params& P, int l, int pos, float* aux, Wait&& wait) {
+// groups.  The first group's rows of earlier positions are loaded before the
+// grid barrier releases (`wait` runs the barrier wait once); the row at pos,
+// written in this token's QKV phase, is read after it.  Each unit stores an
+// unnormalised partial (max m, sum of exp l, sum of exp * V) and counts
+// itself on its head's arrival counter; the unit that arrives last (the
+// counter held C - 1) merges the head's C partials with a running max,
+// o = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c, stores o to att_o and
+// resets the counter.  A single chunk stores o directly.
+template <int HD, int MB, class Wait>
+__device__ __forceinline__ bool attention_units(const Params& P, int l, int pos, int u_first, int u_stride,
+                                                Wait&& wait) {
   constexpr int LP = HD / 8, PPW = 64 / LP;
   constexpr int NPASS = 8;
   constexpr int GRP = PPW * NPASS;       // positions per register group
-  float* qs = aux;                       // [HD] rotated, scaled query
-  float* kn = qs + HD;                   // [HD] new key (fp16-rounded)
-  float* vn = kn + HD;                   // [HD] new value (fp16-rounded)
   const int ctx = pos + 1, H = P.H, HB = P.B * P.H, G = gridDim.x;
   const int C = attn_chunks(ctx, HB, G);
   const int CH = (ctx + C - 1) / C;
   const int lane = threadIdx.x & 63;
   const int sub = lane % LP, pidx = lane / LP;
-  const float scale = 1.0f / sqrtf((float)HD);
   const size_t head_elems = (size_t)P.max_ctx * HD;
   bool waited = false;
-  for (int u = blockIdx.x; u < HB * C; u += G) {
+  for (int u = u_first; u < HB * C; u += u_stride) {
     const int hb = u / C, c = u % C;             // hb = sequence * H + head
     const int seq = hb / H, h = hb - seq * H;
     const int j0 = c * CH;
     const int j1 = min(ctx, j0 + CH);
-    const bool has_new = j0 < ctx && j1 == ctx;
-    uint16_t* kc = P.kv + ((size_t)(l * 2 + 0) * HB + hb) * head_elems;
-    uint16_t* vc = P.kv + ((size_t)(l * 2 + 1) * HB + hb) * head_elems;
+    const uint16_t* kc = P.kv + ((size_t)(l * 2 + 0) * HB + hb) * head_elems;
+    const uint16_t* vc = P.kv + ((size_t)(l * 2 + 1) * HB + hb) * head_elems;
     const rsrc_t rk = make_rsrc(kc, (uint32_t)(head_elems * 2));
     const rsrc_t rv = make_rsrc(vc, (uint32_t)(head_elems * 2));
-    const float* qkv = P.qkv + (size_t)seq * 3 * P.q;
+    const rsrc_t rq = make_rsrc(P.qkv + (size_t)seq * 3 * P.q + h * HD, (uint32_t)(HD * 4));
     float M = -INFINITY, Lsum = 0.f;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    f32x4 qa = {0.f, 0.f, 0.f, 0.f}, qb = {0.f, 0.f, 0.f, 0.f};
     for (int g0 = j0; g0 < j1; g0 += GRP) {
       u32x4 kr[NPASS], vr[NPASS];
+      const bool pre = !waited;   // loads issued before the barrier skip the row at pos
 #pragma unroll
       for (int t = 0; t < NPASS; ++t) {
         const int j = g0 + t * PPW + pidx;
-        const uint32_t off = (j < j1 && j != pos) ? (uint32_t)(j * HD + 8 * sub) * 2u : kOOB;
+        const uint32_t off = (j < j1 && (!pre || j != pos)) ? (uint32_t)(j * HD + 8 * sub) * 2u : kOOB;
         kr[t] = ld_kv(rk, off);
         vr[t] = ld_kv(rv, off);
       }
-      if (!waited) {
+      if (pre) {
         waited = true;
         if (!wait()) return false;
-      }
-      if (g0 == j0) {
-        for (int i = lane; i < HD / 2; i += 64) {
-          const float cs = ldg(P.rope + ((size_t)pos * (HD / 2) + i) * 2);
-          const float sn = ldg(P.rope + ((size_t)pos * (HD / 2) + i) * 2 + 1);
-          const float* qh = qkv + h * HD;
-          const float q0 = ld_coh(qh + 2 * i), q1 = ld_coh(qh + 2 * i + 1);
-          qs[2 * i] = (q0 * cs - q1 * sn) * scale;
-          qs[2 * i + 1] = (q0 * sn + q1 * cs) * scale;
-          if (has_new) {
-            const float* kh = qkv + P.q + h * HD;
-            const float* vh = qkv + 2 * P.q + h * HD;
-            const float k0 = ld_coh(kh + 2 * i), k1 = ld_coh(kh + 2 * i + 1);
-            const _Float16 kr0 = (_Float16)(k0 * cs - k1 * sn), kr1 = (_Float16)(k0 * sn + k1 * cs);
-            const _Float16 vr0 = (_Float16)ld_coh(vh + 2 * i), vr1 = (_Float16)ld_coh(vh + 2 * i + 1);
-            kn[2 * i] = (float)kr0; kn[2 * i + 1] = (float)kr1;
-            vn[2 * i] = (float)vr0; vn[2 * i + 1] = (float)vr1;
-            const uint32_t kb = (uint32_t)__builtin_bit_cast(uint16_t, kr0) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, kr1) << 16);
-            const uint32_t vb = (uint32_t)__builtin_bit_cast(uint16_t, vr0) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, vr1) << 16);
-            st_coh(reinterpret_cast<uint32_t*>(kc + (size_t)pos * HD + 2 * i), kb);
-            st_coh(reinterpret_cast<uint32_t*>(vc + (size_t)pos * HD + 2 * i), vb);
+        if (g0 <= pos && pos < g0 + GRP) {
+          // the row at pos, written before the barrier
+#pragma unroll
+          for (int t = 0; t < NPASS; ++t) {
+            if (g0 + t * PPW + pidx == pos) {
+              const uint32_t off = (uint32_t)(pos * HD + 8 * sub) * 2u;
+              kr[t] = ld_kv(rk, off);
+              vr[t] = ld_kv(rv, off);
+            }
           }
         }
-        wait_lgkm0();   // LDS writes above are visible to this wave's reads below
       }
-      const f32x4 qa = *reinterpret_cast<const f32x4*>(qs + 8 * sub);
-      const f32x4 qb = *reinterpret_cast<const f32x4*>(qs + 8 * sub + 4);
+      if (g0 == j0) {
+        qa = ld_coh4(rq, (uint32_t)(32 * sub));
+        qb = ld_coh4(rq, (uint32_t)(32 * sub + 16));
+      }
       float s[NPASS];
       float mloc = -INFINITY;
 #pragma unroll
       for (int t = 0; t < NPASS; ++t) {
         const int j = g0 + t * PPW + pidx;
-        float dsum;
-        if (j == pos) {
-          const f32x4 ka = *reinterpret_cast<const f32x4*>(kn + 8 * sub);
-          const f32x4 kb = *reinterpret_cast<const f32x4*>(kn + 8 * sub + 4);
-          dsum = ka[0] * qa[0] + ka[1] * qa[1] + ka[2] * qa[2] + ka[3] * qa[3] +
-                 kb[0] * qb[0] + kb[1] * qb[1] + kb[2] * qb[2] + kb[3] * qb[3];
-        } else {
-          dsum = dot8(kr[t], qa, qb, 0.f);
-        }
+        float dsum = dot8(kr[t], qa, qb, 0.f);
         dsum = group_sum<LP>(dsum);
         s[t] = j < j1 ? dsum : -INFINITY;
         mloc = fmaxf(mloc, s[t]);
@@ -827,14 +810,9 @@ __device__ __forceinline__ bool w0_attention(const Params& P, int l, int pos, fl
         const int j = g0 + t * PPW + pidx;
         const float e = j < j1 ? expf(s[t] - Mn) : 0.f;
         lloc += e;
-        if (j == pos) {
+        const f16x8 v = __builtin_bit_cast(f16x8, vr[t]);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(e, vn[8 * sub + q], acc[q]);
-        } else {
-          const f16x8 v = __builtin_bit_cast(f16x8, vr[t]);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(e, (float)v[q], acc[q]);
-        }
+        for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(e, (float)v[q], acc[q]);
       }
       // every lane of a position group holds the same e: count it once
       Lsum = Lsum * alpha + wave_sum(sub == 0 ? lloc : 0.f);
@@ -844,6 +822,18 @@ __device__ __forceinline__ bool w0_attention(const Params& P, int l, int pos, fl
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       for (int off = LP; off < 64; off <<= 1) acc[q] += __shfl_xor(acc[q], off, 64);
+    const size_t o_at = (size_t)seq * P.q + h * HD;
+    if (C == 1) {
+      if (pidx == 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float o = acc[q] / Lsum;
+          if constexpr (MB == 1) st_coh(P.att_o + o_at + 8 * sub + q, o);
+          else st_coh(P.att_o16 + o_at + 8 * sub + q, __builtin_bit_cast(uint16_t, (_Float16)o));
+        }
+      }
+      continue;
+    }
     float* pp = P.part + ((size_t)hb * P.max_chunks + c) * HD;
     float* pm = P.pml + ((size_t)hb * P.max_chunks + c) * 2;
     if (pidx == 0) {
@@ -851,60 +841,54 @@ __device__ __forceinline__ bool w0_attention(const Params& P, int l, int pos, fl
       for (int q = 0; q < 8; ++q) st_coh(pp + 8 * sub + q, acc[q]);
     }
     if (lane == 0) { st_coh(pm, M); st_coh(pm + 1, Lsum); }
+    wait_vm0();   // the partial is visible before the unit counts itself
+    uint32_t old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(P.ctl + kCtlHead0 + hb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = (uint32_t)__builtin_amdgcn_readlane((int)old, 0);
+    if (old != (uint32_t)(C - 1)) continue;
+    // last unit of this head: merge its C partials; lane k owns dims 2k, 2k+1
+    if (lane == 0) st_coh(P.ctl + kCtlHead0 + hb, 0u);
+    const int dd = 2 * lane;
+    const bool act = dd < HD;
+    const float* pbase = P.part + (size_t)hb * P.max_chunks * HD + (act ? dd : 0);
+    const float* mbase = P.pml + (size_t)hb * P.max_chunks * 2;
+    float Mr = -INFINITY, Lr = 0.f, O0 = 0.f, O1 = 0.f;
+    constexpr int CB = 8;
+    for (int cc = 0; cc < C; cc += CB) {
+      float mv[CB], lv[CB], p0v[CB], p1v[CB];
+#pragma unroll
+      for (int t = 0; t < CB; ++t) {
+        const bool in = cc + t < C;
+        mv[t] = in ? ld_coh(mbase + 2 * (cc + t)) : -INFINITY;
+        lv[t] = in ? ld_coh(mbase + 2 * (cc + t) + 1) : 0.f;
+        p0v[t] = in ? ld_coh(pbase + (size_t)(cc + t) * HD) : 0.f;
+        p1v[t] = in ? ld_coh(pbase + (size_t)(cc + t) * HD + 1) : 0.f;
+      }
+#pragma unroll
+      for (int t = 0; t < CB; ++t) {
+        if (mv[t] == -INFINITY) continue;
+        const float Mn = fmaxf(Mr, mv[t]);
+        const float a = Mr == -INFINITY ? 0.f : expf(Mr - Mn);
+        const float bs = expf(mv[t] - Mn);
+        O0 = O0 * a + p0v[t] * bs;
+        O1 = O1 * a + p1v[t] * bs;
+        Lr = Lr * a + lv[t] * bs;
+        Mr = Mn;
+      }
+    }
+    if (act) {
+      if constexpr (MB == 1) {
+        st_coh(P.att_o + o_at + dd, O0 / Lr);
+        st_coh(P.att_o + o_at + dd + 1, O1 / Lr);
+      } else {
+        st_coh(P.att_o16 + o_at + dd, __builtin_bit_cast(uint16_t, (_Float16)(O0 / Lr)));
+        st_coh(P.att_o16 + o_at + dd + 1, __builtin_bit_cast(uint16_t, (_Float16)(O1 / Lr)));
+      }
+    }
   }
   if (!waited) return wait();
   return true;
-}
-
-// All waves: the attention output o of every head of every sequence, merged
-// from the per-chunk partials with a running max:
-// o = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c.  MB == 1: into xs
-// (fp32); MB > 1: into xh[b][0..span(q)) (fp16).
-template <int MB>
-__device__ __forceinline__ void merge_attention(const Params& P, int pos, float* xs) {
-  const int ctx = pos + 1, H = P.H, hd = P.hd, q = P.q, HB = P.B * P.H;
-  const int C = attn_chunks(ctx, HB, gridDim.x);
-  const int span = gemv_span(q);
-  const rsrc_t rp = make_rsrc(P.part, (uint32_t)((size_t)HB * P.max_chunks * hd * 4));
-  constexpr int CB = 8;
-  for (int e4 = threadIdx.x * 4; e4 < P.B * span; e4 += kThreads * 4) {
-    const int b = e4 / span, i = e4 - b * span;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    if (i < q) {
-      const int hb = b * H + i / hd, jj = i % hd;
-      const float* pm = P.pml + (size_t)hb * P.max_chunks * 2;
-      float Mr = -INFINITY, Lr = 0.f;
-      f32x4 Or = {0.f, 0.f, 0.f, 0.f};
-      for (int c0 = 0; c0 < C; c0 += CB) {
-        float mv[CB], lv[CB];
-        f32x4 pv[CB];
-#pragma unroll
-        for (int t = 0; t < CB; ++t) {
-          const bool in = c0 + t < C;
-          mv[t] = in ? ld_coh(pm + 2 * (c0 + t)) : -INFINITY;
-          lv[t] = in ? ld_coh(pm + 2 * (c0 + t) + 1) : 0.f;
-          pv[t] = ld_coh4(rp, in ? (uint32_t)(((size_t)hb * P.max_chunks + c0 + t) * hd + jj) * 4u : kOOB);
-        }
-#pragma unroll
-        for (int t = 0; t < CB; ++t) {
-          if (mv[t] == -INFINITY) continue;
-          const float Mn = fmaxf(Mr, mv[t]);
-          const float a = Mr == -INFINITY ? 0.f : expf(Mr - Mn);
-          const float bs = expf(mv[t] - Mn);
-          Or = Or * a + pv[t] * bs;
-          Lr = Lr * a + lv[t] * bs;
-          Mr = Mn;
-        }
-      }
-      o = Or / Lr;
-    }
-    if constexpr (MB == 1) {
-      *reinterpret_cast<f32x4*>(xs + i) = o;
-    } else {
-      _Float16* xh = reinterpret_cast<_Float16*>(xs);
-      *reinterpret_cast<f16x4*>(xh + (size_t)b * span + i) = f16x4{(_Float16)o[0], (_Float16)o[1], (_Float16)o[2], (_Float16)o[3]};
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -912,18 +896,49 @@ __device__ __forceinline__ void merge_attention(const Params& P, int pos, float*
 // ---------------------------------------------------------------------------
 // out holds the phase's row sums, row-major over sequences: out[row * MB + b].
 // scl[b] is sequence b's norm scale for the phase (1 where there is no norm).
+// QKV rows come in pairs (2i, 2i+1) of one head, which are exactly the pairs
+// the rotary embedding rotates: q is rotated, scaled by 1/sqrt(hd) and
+// stored for attention; k is rotated and v taken as it is, both rounded to
+// fp16 and appended to the KV cache at (layer l, position pos).
 template <int MB>
-__device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, const int* tab_wg, bool want_logits,
-                                                 const float* scl, const float* out, float* xown) {
+__device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l, int pos, const int* tab_wg,
+                                                 bool want_logits, const float* scl, const float* out, float* xown) {
   const int lane = threadIdx.x & 63, B = P.B;
   if (!is_gemv(ph)) return;
   const int p0 = rfl(tab_wg[2 * ph]);
   const int n = rfl(tab_wg[2 * ph + 1]) - p0;
   const int own = kOwnFloats / MB;
   if (ph == PH_QKV) {
-    for (int e = lane; e < 2 * n * MB; e += 64) {
+    const int q = P.q, hd = P.hd, HB = B * P.H;
+    const float qscale = 1.0f / sqrtf((float)hd);
+    const size_t head_elems = (size_t)P.max_ctx * hd;
+    for (int e = lane; e < n * MB; e += 64) {
       const int t = e / MB, b = e - t * MB;
-      if (b < B) st_coh(P.qkv + (size_t)b * 3 * P.q + 2 * p0 + t, out[e] * scl[b]);
+      if (b < B) {
+        const int r = 2 * (p0 + t);                       // even row of Wqkv
+        const int part = r / q, rr = r - part * q;        // 0: q, 1: k, 2: v
+        const int h = rr / hd, i = (rr - h * hd) >> 1;
+        const float y0 = out[2 * t * MB + b] * scl[b], y1 = out[(2 * t + 1) * MB + b] * scl[b];
+        if (part == 2) {
+          const uint32_t vb = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y0) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y1) << 16);
+          uint16_t* vc = P.kv + ((size_t)(l * 2 + 1) * HB + b * P.H + h) * head_elems + (size_t)pos * hd + 2 * i;
+          st_coh(reinterpret_cast<uint32_t*>(vc), vb);
+        } else {
+          const float cs = ldg(P.rope + ((size_t)pos * (hd / 2) + i) * 2);
+          const float sn = ldg(P.rope + ((size_t)pos * (hd / 2) + i) * 2 + 1);
+          const float z0 = y0 * cs - y1 * sn, z1 = y0 * sn + y1 * cs;
+          if (part == 0) {
+            st_coh(P.qkv + (size_t)b * 3 * q + rr, z0 * qscale);
+            st_coh(P.qkv + (size_t)b * 3 * q + rr + 1, z1 * qscale);
+          } else {
+            const uint32_t kb = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)z0) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)z1) << 16);
+            uint16_t* kc = P.kv + ((size_t)(l * 2) * HB + b * P.H + h) * head_elems + (size_t)pos * hd + 2 * i;
+            st_coh(reinterpret_cast<uint32_t*>(kc), kb);
+          }
+        }
+      }
     }
   } else if (ph == PH_O || ph == PH_DOWN) {
     for (int e = lane; e < 2 * n * MB; e += 64) {
@@ -1018,7 +1033,6 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
     __syncthreads();   // S1a
     if (si[12] == 0) break;
     if (norm_phase(id)) apply_gains(xs, gs, P.d, red);
-    if (id.ph == PH_O) merge_attention<1>(P, A.pos0 + id.i, xs);
     __syncthreads();   // S1
     if (is_gemv(id.ph)) {
       const int* e = tab + id.ph * kTabStride;
@@ -1089,7 +1103,6 @@ __device__ __forceinline__ void streamer_tiles(const Params& P, const Launch& A,
     if (si[12] == 0) break;
     if (norm_phase(id))
       apply_gains_batch(reinterpret_cast<_Float16*>(xs), xs + kMaxBatch * gemv_span(P.d) / 2, gs, P.d, B, red);
-    if (id.ph == PH_O) merge_attention<MB>(P, A.pos0 + id.i, xs);
     __syncthreads();   // S1
     if (is_gemv(id.ph)) {
       const int* e = tab + id.ph * kTabStride;
@@ -1196,7 +1209,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   int tok_local[MB];
 #pragma unroll
   for (int b = 0; b < MB; ++b) tok_local[b] = 0;
-  int prev_ph = -3, prev_i = 0;
+  int prev_ph = -3, prev_i = 0, prev_l = 0;
   if (lane < kMaxBatch) scl[lane] = 1.0f;
   PhaseIt id = phase_at(P, A, g0);
   for (; id.g < g1; phase_next(P, A, id)) {
@@ -1206,7 +1219,8 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     if (!first) {
       if constexpr (MB > 1)
         if (is_gemv(prev_ph)) w0_combine<MB>(prev_ph, plan, slots, out);
-      w0_store_outputs<MB>(P, prev_ph, tab_wg, A.write_logits && prev_i == A.n_tok - 1, scl, out, xown);
+      w0_store_outputs<MB>(P, prev_ph, prev_l, A.pos0 + prev_i, tab_wg, A.write_logits && prev_i == A.n_tok - 1, scl,
+                           out, xown);
     }
     if (is_gemv(id.ph)) {
       const int np = rfl(tab_wg[2 * id.ph + 1]) - rfl(tab_wg[2 * id.ph]);
@@ -1222,12 +1236,13 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     if (norm_phase(id)) w0_dma_vec(gs, norm_gains(P, id), P.d, 4, false);
     bool ok = true;
     if (id.ph == PH_ATTN) {
+      const int u0 = blockIdx.x, us = gridDim.x;
       switch (P.hd) {
-        case 8: ok = w0_attention<8>(P, id.l, pos, aux, wait); break;
-        case 16: ok = w0_attention<16>(P, id.l, pos, aux, wait); break;
-        case 32: ok = w0_attention<32>(P, id.l, pos, aux, wait); break;
-        case 64: ok = w0_attention<64>(P, id.l, pos, aux, wait); break;
-        default: ok = w0_attention<128>(P, id.l, pos, aux, wait); break;
+        case 8: ok = attention_units<8, MB>(P, id.l, pos, u0, us, wait); break;
+        case 16: ok = attention_units<16, MB>(P, id.l, pos, u0, us, wait); break;
+        case 32: ok = attention_units<32, MB>(P, id.l, pos, u0, us, wait); break;
+        case 64: ok = attention_units<64, MB>(P, id.l, pos, u0, us, wait); break;
+        default: ok = attention_units<128, MB>(P, id.l, pos, u0, us, wait); break;
       }
     } else if (id.ph == PH_QKV && id.l == 0) {
       ok = wait();
@@ -1266,6 +1281,16 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       }
     } else if (id.ph == PH_O) {
       ok = wait();
+      if (ok) {
+        // the attention output of every head, merged in the attention phase
+        if constexpr (MB == 1) {
+          w0_dma_vec(xs, P.att_o, P.q, 4, true);
+        } else {
+          _Float16* xh = reinterpret_cast<_Float16*>(xs);
+          for (int b = 0; b < B; ++b)
+            w0_dma_vec(xh + (size_t)b * gemv_span(P.q), P.att_o16 + (size_t)b * P.q, P.q, 2, true);
+        }
+      }
     } else {
       ok = wait();
       if (ok) {
@@ -1284,7 +1309,6 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       if constexpr (MB == 1) apply_gains(xs, gs, P.d, red);
       else apply_gains_batch(reinterpret_cast<_Float16*>(xs), stage, gs, P.d, B, red);
     }
-    if (id.ph == PH_O) merge_attention<MB>(P, pos, xs);
     __syncthreads();   // S1
     // this phase's norm scale per sequence, used when its outputs are published
     if (lane < kMaxBatch) {
@@ -1302,11 +1326,13 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     stamp();
     prev_ph = id.ph;
     prev_i = id.i;
+    prev_l = id.l;
   }
   if (!first) {
     if constexpr (MB > 1)
       if (is_gemv(prev_ph)) w0_combine<MB>(prev_ph, plan, slots, out);
-    w0_store_outputs<MB>(P, prev_ph, tab_wg, A.write_logits && prev_i == A.n_tok - 1, scl, out, xown);
+    w0_store_outputs<MB>(P, prev_ph, prev_l, A.pos0 + prev_i, tab_wg, A.write_logits && prev_i == A.n_tok - 1, scl,
+                         out, xown);
   }
   wait_vm0();
 }
