@@ -103,13 +103,16 @@ DEC_HD inline int phases_per_token(int L) { return kPhasesPerLayer * L + 2; }
 
 // Number of attention chunks per head at context length ctx for a grid of G
 // workgroups and H heads (all sequences' heads in a batch): as many as keeps
-// every workgroup busy (at most G/H per head),
-// no chunk shorter than kChunkMin or longer than kChunkMax positions.
+// every wave of every workgroup busy (at most 8 G / H per head), no chunk
+// shorter than kChunkMin positions, and at most kChunkCap chunks (one wave
+// merges a head's partials) unless chunks would exceed kChunkMax positions.
+constexpr int kChunkCap = 32;
 DEC_HD inline int attn_chunks(int ctx, int H, int G) {
   int by_min = (ctx + kChunkMin - 1) / kChunkMin;
   int by_max = (ctx + kChunkMax - 1) / kChunkMax;
-  int fill = G / H > 0 ? G / H : 1;
+  int fill = 8 * G / H > 0 ? 8 * G / H : 1;
   int c = by_min < fill ? by_min : fill;
+  c = c < kChunkCap ? c : kChunkCap;
   return c > by_max ? c : by_max;
 }
 

@@ -729,7 +729,10 @@ __device__ __forceinline__ void w0_embed(const Params& P, int b, int tok, float*
 // positions are loaded together and an online softmax runs across such
 // groups.  The first group's rows of earlier positions are loaded before the
 // grid barrier releases (`wait` runs the barrier wait once); the row at pos,
-// written in this token's QKV phase, is read after it.  Each unit stores an
+// written in this token's QKV phase, is read after it.  All eight waves of a
+// workgroup take units in the attention phase (wave w of workgroup g starts
+// at unit w * G + g); `wait` is where each of them meets the workgroup
+// barrier that follows wave 0's grid barrier.  Each unit stores an
 // unnormalised partial (max m, sum of exp l, sum of exp * V) and counts
 // itself on its head's arrival counter; the unit that arrives last (the
 // counter held C - 1) merges the head's C partials with a running max,
@@ -854,7 +857,7 @@ __device__ __forceinline__ bool attention_units(const Params& P, int l, int pos,
     const float* pbase = P.part + (size_t)hb * P.max_chunks * HD + (act ? dd : 0);
     const float* mbase = P.pml + (size_t)hb * P.max_chunks * 2;
     float Mr = -INFINITY, Lr = 0.f, O0 = 0.f, O1 = 0.f;
-    constexpr int CB = 8;
+    constexpr int CB = 16;
     for (int cc = 0; cc < C; cc += CB) {
       float mv[CB], lv[CB], p0v[CB], p1v[CB];
 #pragma unroll
@@ -889,6 +892,18 @@ __device__ __forceinline__ bool attention_units(const Params& P, int l, int pos,
   }
   if (!waited) return wait();
   return true;
+}
+
+// Attention units of one wave: units u_first, u_first + u_stride, ...
+template <int MB, class Wait>
+__device__ __forceinline__ bool attention_wave(const Params& P, int l, int pos, int u_first, int u_stride, Wait&& wait) {
+  switch (P.hd) {
+    case 8: return attention_units<8, MB>(P, l, pos, u_first, u_stride, wait);
+    case 16: return attention_units<16, MB>(P, l, pos, u_first, u_stride, wait);
+    case 32: return attention_units<32, MB>(P, l, pos, u_first, u_stride, wait);
+    case 64: return attention_units<64, MB>(P, l, pos, u_first, u_stride, wait);
+    default: return attention_units<128, MB>(P, l, pos, u_first, u_stride, wait);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1013,6 +1028,24 @@ __device__ __forceinline__ int w0_argmax(const Params& P, int i, int b) {
 // barrier), S1 (input ready: gains applied or attention merged) and S2
 // (phase outputs in LDS).
 
+// A streamer's attention phase: its units (the first one's cached rows are
+// requested before S1a), then S1 and S2 as in every phase.  False if wave 0
+// reported a failed grid barrier.
+template <int MB>
+__device__ __forceinline__ bool streamer_attention(const Params& P, const Launch& A, const PhaseIt& id, const int* si) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  auto wait_s = [&]() {
+    __syncthreads();   // S1a
+    return si[12] != 0;
+  };
+  if (!attention_wave<MB>(P, id.l, A.pos0 + id.i, wave * gridDim.x + blockIdx.x, kWaves * gridDim.x, wait_s))
+    return false;
+  wait_vm0();   // this wave's stores are complete before wave 0 arrives at the grid barrier
+  __syncthreads();   // S1
+  __syncthreads();   // S2
+  return true;
+}
+
 // Streamer role (waves 1..7): kBlocksInFlight loads always in flight, in
 // stream order.  Every phase is a whole number of groups of kUnitsInFlight
 // units (zero-reading units pad it), so unit k of each group always sits in
@@ -1030,6 +1063,10 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
   PhaseIt id = phase_at(P, A, g0);
   for (; id.g < g1; phase_next(P, A, id)) {
     if (id.ph == -2) continue;
+    if (id.ph == PH_ATTN) {
+      if (!streamer_attention<1>(P, A, id, si)) break;
+      continue;
+    }
     __syncthreads();   // S1a
     if (si[12] == 0) break;
     if (norm_phase(id)) apply_gains(xs, gs, P.d, red);
@@ -1099,6 +1136,10 @@ __device__ __forceinline__ void streamer_tiles(const Params& P, const Launch& A,
   PhaseIt id = phase_at(P, A, g0);
   for (; id.g < g1; phase_next(P, A, id)) {
     if (id.ph == -2) continue;
+    if (id.ph == PH_ATTN) {
+      if (!streamer_attention<MB>(P, A, id, si)) break;
+      continue;
+    }
     __syncthreads();   // S1a
     if (si[12] == 0) break;
     if (norm_phase(id))
@@ -1236,14 +1277,18 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     if (norm_phase(id)) w0_dma_vec(gs, norm_gains(P, id), P.d, 4, false);
     bool ok = true;
     if (id.ph == PH_ATTN) {
-      const int u0 = blockIdx.x, us = gridDim.x;
-      switch (P.hd) {
-        case 8: ok = attention_units<8, MB>(P, id.l, pos, u0, us, wait); break;
-        case 16: ok = attention_units<16, MB>(P, id.l, pos, u0, us, wait); break;
-        case 32: ok = attention_units<32, MB>(P, id.l, pos, u0, us, wait); break;
-        case 64: ok = attention_units<64, MB>(P, id.l, pos, u0, us, wait); break;
-        default: ok = attention_units<128, MB>(P, id.l, pos, u0, us, wait); break;
-      }
+      // the streamers take attention units too: release them (S1a) right
+      // after the grid barrier, then run this wave's own units
+      auto wait_attn = [&]() {
+        const bool r = wait();
+        if (lane == 0) si[12] = r ? 1 : 0;
+        __syncthreads();   // S1a
+        return r;
+      };
+      ok = attention_wave<MB>(P, id.l, pos, blockIdx.x, kWaves * gridDim.x, wait_attn);
+      wait_vm0();   // this wave's stores are complete before the next arrive
+      first = false;
+      if (!ok) return;
     } else if (id.ph == PH_QKV && id.l == 0) {
       ok = wait();
       if (ok) {
@@ -1300,11 +1345,13 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
         have_tok = true;
       }
     }
-    wait_vm0();   // the phase input has landed in LDS
-    if (lane == 0) si[12] = ok ? 1 : 0;
-    first = false;
-    __syncthreads();   // S1a
-    if (!ok) return;
+    if (id.ph != PH_ATTN) {
+      wait_vm0();   // the phase input has landed in LDS
+      if (lane == 0) si[12] = ok ? 1 : 0;
+      first = false;
+      __syncthreads();   // S1a
+      if (!ok) return;
+    }
     if (norm_phase(id)) {
       if constexpr (MB == 1) apply_gains(xs, gs, P.d, red);
       else apply_gains_batch(reinterpret_cast<_Float16*>(xs), stage, gs, P.d, B, red);
