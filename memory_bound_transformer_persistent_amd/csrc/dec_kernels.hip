@@ -997,27 +997,56 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l,
   }
 }
 
-// Greedy token of sequence b = argmax over the workgroups' partials (lowest
-// index on ties).  Every workgroup computes it (it is the next token's
-// input); workgroup 0 publishes it.
-__device__ __forceinline__ int w0_argmax(const Params& P, int i, int b) {
-  const int lane = threadIdx.x & 63, G = gridDim.x;
-  float bvv = -INFINITY;
-  int bii = 0x7fffffff;
-  for (int t = lane; t < G; t += 64) {
-    const float v = ld_coh(P.amax_v + (size_t)b * G + t);
-    const int ix = ld_coh(P.amax_i + (size_t)b * G + t);
-    if (v > bvv || (v == bvv && ix < bii)) { bvv = v; bii = ix; }
+// Greedy token of every sequence = argmax over the workgroups' partials
+// (lowest index on ties).  Every workgroup computes it (it is the next
+// token's input); workgroup 0 publishes it.  All sequences' partials are
+// requested before any is reduced.
+template <int MB>
+__device__ __forceinline__ void w0_argmax(const Params& P, int i, int* tok) {
+  const int lane = threadIdx.x & 63, G = gridDim.x, B = P.B;
+  const rsrc_t rv = make_rsrc(P.amax_v, (uint32_t)(B * G * 4)), ri = make_rsrc(P.amax_i, (uint32_t)(B * G * 4));
+  float bv[MB];
+  int bi[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) { bv[b] = -INFINITY; bi[b] = 0x7fffffff; }
+  constexpr int K = 4;   // partials per lane per sequence and pass
+  for (int t0 = 0; t0 < G; t0 += 64 * K) {
+    float v[MB][K];
+    int ix[MB][K];
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int t = t0 + lane + 64 * k;
+        const uint32_t off = (b < B && t < G) ? (uint32_t)(b * G + t) * 4u : kOOB;
+        v[b][k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, kAuxSc1));
+        ix[b][k] = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, off, 0, kAuxSc1);
+      }
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        if (t0 + lane + 64 * k < G && (v[b][k] > bv[b] || (v[b][k] == bv[b] && ix[b][k] < bi[b]))) {
+          bv[b] = v[b][k];
+          bi[b] = ix[b][k];
+        }
   }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(bvv, off, 64);
-    const int oi = __shfl_xor(bii, off, 64);
-    if (ov > bvv || (ov == bvv && oi < bii)) { bvv = ov; bii = oi; }
+  for (int b = 0; b < MB; ++b) {
+    float bvv = bv[b];
+    int bii = bi[b];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bvv, off, 64);
+      const int oi = __shfl_xor(bii, off, 64);
+      if (ov > bvv || (ov == bvv && oi < bii)) { bvv = ov; bii = oi; }
+    }
+    tok[b] = (bii == 0x7fffffff) ? 0 : bii;
+    if (b < B && blockIdx.x == 0 && lane == 0) {
+      st_coh(P.tok_cur + b, tok[b]);
+      st_coh(P.tok_out + (size_t)i * P.B + b, tok[b]);
+    }
   }
-  const int tok = (bii == 0x7fffffff) ? 0 : bii;
-  if (blockIdx.x == 0 && lane == 0) { st_coh(P.tok_cur + b, tok); st_coh(P.tok_out + (size_t)i * P.B + b, tok); }
-  return tok;
 }
 
 // ---------------------------------------------------------------------------
@@ -1246,7 +1275,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       for (int r = r0 + lane; r < r1; r += 64) xown[b * own + r - r0] = ld_coh(P.x + (size_t)b * P.d + r);
   }
   uint32_t epoch = A.bar_base;
-  bool first = true, have_tok = false;
+  bool first = true, have_tok = false, gains_ready = false;
   int tok_local[MB];
 #pragma unroll
   for (int b = 0; b < MB; ++b) tok_local[b] = 0;
@@ -1273,8 +1302,10 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       w0_arrive(P, A.fenced);
     }
     auto wait = [&]() { return skip_bar ? true : w0_wait(P, epoch, A.fenced); };
-    // the norm gains do not depend on the barrier: start them first
-    if (norm_phase(id)) w0_dma_vec(gs, norm_gains(P, id), P.d, 4, false);
+    // the norm gains do not depend on the barrier: they were prefetched
+    // during the previous normed phase, else start them now
+    if (norm_phase(id) && !gains_ready) w0_dma_vec(gs, norm_gains(P, id), P.d, 4, false);
+    gains_ready = false;
     bool ok = true;
     if (id.ph == PH_ATTN) {
       // the streamers take attention units too: release them (S1a) right
@@ -1339,9 +1370,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     } else {
       ok = wait();
       if (ok) {
-#pragma unroll
-        for (int b = 0; b < MB; ++b)
-          if (b < B) tok_local[b] = w0_argmax(P, id.i, b);
+        w0_argmax<MB>(P, id.i, tok_local);
         have_tok = true;
       }
     }
@@ -1357,6 +1386,18 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       else apply_gains_batch(reinterpret_cast<_Float16*>(xs), stage, gs, P.d, B, red);
     }
     __syncthreads();   // S1
+    if (norm_phase(id)) {
+      // every wave has applied this phase's gains: fetch the next normed
+      // phase's into the same LDS while this GEMV runs
+      PhaseIt nx = id;
+      do {
+        phase_next(P, A, nx);
+      } while (nx.g < g1 && !norm_phase(nx));
+      if (nx.g < g1) {
+        w0_dma_vec(gs, norm_gains(P, nx), P.d, 4, false);
+        gains_ready = true;
+      }
+    }
     // this phase's norm scale per sequence, used when its outputs are published
     if (lane < kMaxBatch) {
       float s = 1.0f;
