@@ -141,6 +141,12 @@ __device__ __forceinline__ int ld_coh(const int* p) {
 __device__ __forceinline__ uint32_t ld_coh(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// The same through the global address space: a global (not flat) load, which
+// counts in vmcnt only, so several can be in flight and waited for in order.
+typedef __attribute__((address_space(1))) uint32_t guint;
+__device__ __forceinline__ uint32_t ld_coh_g(const uint32_t* p) {
+  return __hip_atomic_load((guint*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void st_coh(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -597,24 +603,26 @@ __device__ __forceinline__ bool w0_wait(const Params& P, uint32_t epoch, int fen
   const uint32_t G = gridDim.x;
   const int ng = G < (uint32_t)kGroups ? (int)G : kGroups;
   uint32_t target = 0;
-  const uint32_t* cnt = P.ctl + kCtlGroup0 + 64 * (lane < ng ? lane : 0);
+  // lanes 0..ng-1 watch the group counters and lane kGroups the error word,
+  // all in one load, so each poll costs one round trip
+  const uint32_t* w = lane < ng ? P.ctl + kCtlGroup0 + 64 * lane : (lane == kGroups ? P.ctl + kCtlErr : P.ctl + kCtlGroup0);
   if (lane < ng) target = ((G - (uint32_t)lane + kGroups - 1) / kGroups) * epoch;
   const uint64_t t0 = wall_clock64();
-  bool ok = true;
+  const uint64_t limit = (uint64_t)P.watchdog_ticks;
+  // 0 = released, 1 = a workgroup raised an error, 2 = the watchdog expired
+  int why = 0;
   while (true) {
-    const bool done = lane >= ng || (int)(ld_coh(cnt) - target) >= 0;
-    if (__all(done)) break;
-    if (ld_coh(P.ctl + kCtlErr) != 0u) { ok = false; break; }
-    if (wall_clock64() - t0 > (uint64_t)P.watchdog_ticks) {
-      if (lane == 0) {
-        uint32_t expected = 0u;
-        __hip_atomic_compare_exchange_strong(P.ctl + kCtlErr, &expected, (uint32_t)kDevErrTimeout,
-                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      ok = false;
-      break;
-    }
+    const uint32_t v = ld_coh_g(w);
+    if (__any(lane == kGroups && v != 0u)) { why = 1; break; }
+    if (__all(lane >= ng || (int)(v - target) >= 0)) break;
+    if (wall_clock64() - t0 > limit) { why = 2; break; }
   }
+  if (why == 2 && lane == 0) {
+    uint32_t expected = 0u;
+    __hip_atomic_compare_exchange_strong(P.ctl + kCtlErr, &expected, (uint32_t)kDevErrTimeout, __ATOMIC_RELAXED,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const bool ok = why == 0;
   if (fenced) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return ok;
 }
