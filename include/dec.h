@@ -63,7 +63,8 @@ typedef enum dec_status {
  *   n_heads*head_dim may differ from d_model and must be a multiple of 8;
  *   d_ffn >= 8, a multiple of 8;
  *   1 <= lm_vocab <= vocab, lm_vocab even;
- *   1 <= max_ctx <= 65536; batch >= 1; rms_eps > 0; rope_base > 1; flags == 0.
+ *   1 <= max_ctx <= 65536; batch >= 1; rms_eps > 0; rope_base > 1;
+ *   flags: 0 or DEC_FLAG_BATCHED_PREFILL (batch 1 only).
  * Limits of this build (DEC_ERR_UNSUPPORTED): d_model, n_heads*head_dim and
  * d_ffn <= 8192; batch <= 8; with batch > 1, d_model <= 2560 and d_ffn,
  * n_heads*head_dim <= 7680 after rounding up to a multiple of 512 (every
@@ -77,6 +78,18 @@ typedef enum dec_status {
  * vector (x*g, the attention output, the SwiGLU output) to fp16, where the
  * batch-1 kernel keeps it in fp32.
  */
+/*
+ * DEC_FLAG_BATCHED_PREFILL: dec_prefill runs the prompt 8 positions at a time
+ * through the batched (matrix-core) kernel instead of one position per step
+ * of the decode kernel.  The handle keeps a second, tiled copy of the
+ * weights (see dec_pack) and its per-position buffers hold 8 columns; the
+ * shape limits of batch > 1 apply.  Numerics: each matrix product's input is
+ * rounded to fp16 as in the batched kernel, so the prompt's cache entries and
+ * logits differ from the default prefill's by that rounding.  Decode steps
+ * are unchanged.
+ */
+#define DEC_FLAG_BATCHED_PREFILL 0x2u
+
 typedef struct dec_model_desc {
   int32_t n_layers;
   int32_t d_model;
@@ -90,7 +103,7 @@ typedef struct dec_model_desc {
   int32_t batch;      /* sequences decoded together                    */
   float rms_eps;
   float rope_base;
-  uint32_t flags;     /* reserved, must be 0 */
+  uint32_t flags;     /* 0 or DEC_FLAG_BATCHED_PREFILL */
 } dec_model_desc;
 
 /*

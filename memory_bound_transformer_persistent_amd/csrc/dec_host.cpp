@@ -53,12 +53,14 @@ int check_desc_impl(const dec_model_desc* d, std::string* err) {
   if (d->max_ctx < 1 || d->max_ctx > 65536) return fail(err, DEC_ERR_BAD_DESC, "max_ctx must be in [1, 65536] (got %d)", d->max_ctx);
   if (!(d->rms_eps > 0.f) || !std::isfinite(d->rms_eps)) return fail(err, DEC_ERR_BAD_DESC, "rms_eps must be > 0");
   if (!(d->rope_base > 1.f) || !std::isfinite(d->rope_base)) return fail(err, DEC_ERR_BAD_DESC, "rope_base must be > 1");
-  if (d->flags != 0) return fail(err, DEC_ERR_BAD_DESC, "flags must be 0");
+  if (d->flags & ~DEC_FLAG_BATCHED_PREFILL) return fail(err, DEC_ERR_BAD_DESC, "unknown flags 0x%x", d->flags);
+  const bool bp = (d->flags & DEC_FLAG_BATCHED_PREFILL) != 0;
+  if (bp && d->batch != 1) return fail(err, DEC_ERR_BAD_DESC, "DEC_FLAG_BATCHED_PREFILL is for batch 1");
   if (d->batch < 1) return fail(err, DEC_ERR_BAD_DESC, "batch must be >= 1");
   const long long q = (long long)d->n_heads * hd;
   if (q % 8) return fail(err, DEC_ERR_BAD_DESC, "n_heads*head_dim must be a multiple of 8");
   if (d->batch > kMaxBatch) return fail(err, DEC_ERR_UNSUPPORTED, "batch must be <= %d", kMaxBatch);
-  if (d->batch > 1) {
+  if (d->batch > 1 || bp) {
     auto span = [](long long k) { return (k + 511) / 512 * 512; };
     if (span(d->d_model) > kBatchSpanD || span(d->d_ffn) > kBatchSpanK || span(q) > kBatchSpanK)
       return fail(err, DEC_ERR_UNSUPPORTED,
@@ -72,8 +74,9 @@ int check_desc_impl(const dec_model_desc* d, std::string* err) {
   const long long big = std::max({lm_bytes, 2LL * 3 * q * d->d_model, 2LL * 2 * d->d_ffn * d->d_model});
   if (big >= (1LL << 31)) return fail(err, DEC_ERR_UNSUPPORTED, "a weight matrix is 2 GiB or larger");
   if (2LL * d->max_ctx * hd >= (1LL << 31)) return fail(err, DEC_ERR_UNSUPPORTED, "KV cache of one head is 2 GiB or larger");
-  const int hb = d->batch * d->n_heads;
-  if (hb > kMaxHeads) return fail(err, DEC_ERR_UNSUPPORTED, "batch x n_heads must be <= %d", kMaxHeads);
+  const int hb = (bp ? kMaxBatch : d->batch) * d->n_heads;
+  if (hb > kMaxHeads) return fail(err, DEC_ERR_UNSUPPORTED, "batch (8 with batched prefill) x n_heads must be <= %d",
+                                  kMaxHeads);
   if ((long long)hb * max_attn_chunks(d->max_ctx, hb, 1024) > 65536)
     return fail(err, DEC_ERR_UNSUPPORTED, "too many attention partials (batch x n_heads x chunks > 65536)");
   return DEC_OK;
@@ -276,26 +279,44 @@ bool same_shape(const dec_model_desc& a, const dec_model_desc& b) {
 // device arena layout (bytes)
 // ---------------------------------------------------------------------------
 struct Arena {
-  size_t w, gains, rope, kv, x, qkv, att_o, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out, prompt, ctl, params, trace, total;
+  size_t w, w2, gains, rope, kv, x, qkv, att_o, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out, prompt, ctl,
+      params, params2, trace, total;
 };
+
+bool batched_prefill(const dec_model_desc& d) { return (d.flags & DEC_FLAG_BATCHED_PREFILL) != 0; }
+
+// The description the batched prefill kernel runs with: kMaxBatch columns
+// (consecutive positions of the one sequence) and the tiled weight image.
+dec_model_desc prefill_desc(const dec_model_desc& d) {
+  dec_model_desc p = d;
+  p.batch = kMaxBatch;
+  p.flags = 0;
+  return p;
+}
 
 Arena arena_layout(const dec_model_desc& d, int G) {
   Arena a;
   const Image im = image_layout(d);
-  const size_t D = d.d_model, q = (size_t)d.n_heads * d.head_dim, B = d.batch;
-  const size_t hb = B * d.n_heads;   // attention heads of all sequences
-  const int mc = max_attn_chunks(d.max_ctx, (int)hb, G);
+  const size_t D = d.d_model, q = (size_t)d.n_heads * d.head_dim;
+  const bool bp = batched_prefill(d);
+  // rows of the per-column buffers: sequences, or the batched prefill's columns
+  const size_t B = bp ? (size_t)kMaxBatch : (size_t)d.batch;
+  const size_t hb = B * d.n_heads;   // attention heads of all columns
+  const size_t hkv = (size_t)d.batch * d.n_heads;   // heads with a KV cache
+  const size_t part_rows = std::max(hkv * max_attn_chunks(d.max_ctx, (int)hkv, G),
+                                    hb * max_attn_chunks(d.max_ctx, (int)hb, G));
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
   a.w = take(im.total * 2);
+  a.w2 = bp ? take(image_layout(prefill_desc(d)).total * 2) : 0;
   a.gains = take(((size_t)d.n_layers * 2 + 1) * D * 4);
   a.rope = take((size_t)d.max_ctx * (d.head_dim / 2) * 2 * 4);
-  a.kv = take((size_t)d.n_layers * 2 * hb * d.max_ctx * d.head_dim * 2);
+  a.kv = take((size_t)d.n_layers * 2 * hkv * d.max_ctx * d.head_dim * 2);
   a.x = take(B * D * 4);
   a.qkv = take(B * 3 * q * 4);
   a.att_o = take(B * q * 4);
-  a.part = take(hb * mc * d.head_dim * 4);
-  a.pml = take(hb * mc * 2 * 4);
+  a.part = take(part_rows * d.head_dim * 4);
+  a.pml = take(part_rows * 2 * 4);
   a.act = take(B * d.d_ffn * 4);
   a.logits = take(B * d.lm_vocab * 4);
   a.amax_v = take(B * G * 4);
@@ -305,6 +326,7 @@ Arena arena_layout(const dec_model_desc& d, int G) {
   a.prompt = take((size_t)d.max_ctx * B * 4);
   a.ctl = take(kCtlWords * 4);
   a.params = take(sizeof(Params));
+  a.params2 = take(sizeof(Params));
   a.trace = take((size_t)G * kTraceStride * 8);
   a.total = o;
   return a;
@@ -325,6 +347,7 @@ struct dec_handle {
   Image im;
   Params P;               // host copy
   Params* dP = nullptr;   // device copy read by the kernel
+  Params* dP2 = nullptr;  // device copy for the batched prefill (DEC_FLAG_BATCHED_PREFILL)
   uint32_t debug = 0;
   uint32_t bar_done = 0;   // barriers completed by resident launches (wrapping)
   int pos = 0;
@@ -351,6 +374,7 @@ int launch(dec_handle* h, int pos0, int n_tok, int tok_src, int lm_last_only, in
   A.fenced = 0;
   A.phase_begin = 0;
   A.phase_end = 0x7fffffff;
+  A.pos_end = 0x7fffffff;
   if (h->debug & DEC_DEBUG_MULTILAUNCH) {
     // one ordinary launch per phase: the kernel boundary is the barrier
     const int ppt = phases_per_token(h->desc.n_layers);
@@ -368,6 +392,41 @@ int launch(dec_handle* h, int pos0, int n_tok, int tok_src, int lm_last_only, in
   }
   A.bar_base = h->bar_done;
   HIPCHK(h, &h->err, (hipError_t)kernel_launch_resident(h->dP, A, h->grid, h->desc.batch, h->stream));
+  h->bar_done += launch_barriers(h->desc.n_layers, n_tok, lm_last_only);
+  return DEC_OK;
+}
+
+// The batched prefill: n prompt positions, kMaxBatch per token step of the
+// batched kernel, the LM head and argmax for the last step only.
+int launch_prefill(dec_handle* h, int n, int write_logits) {
+  const int pos0 = 0, n_tok = (n + kMaxBatch - 1) / kMaxBatch, tok_src = TOK_PROMPT, lm_last_only = 1;
+  Launch A;
+  A.pos0 = pos0;
+  A.n_tok = n_tok;
+  A.tok_src = tok_src;
+  A.lm_last_only = lm_last_only;
+  A.write_logits = write_logits;
+  A.fenced = 0;
+  A.phase_begin = 0;
+  A.phase_end = 0x7fffffff;
+  A.pos_end = n;
+  if (h->debug & DEC_DEBUG_MULTILAUNCH) {
+    // one ordinary launch per phase: the kernel boundary is the barrier
+    const int ppt = phases_per_token(h->desc.n_layers);
+    A.bar_base = h->bar_done;
+    for (int i = 0; i < n_tok; ++i) {
+      const bool lm = !lm_last_only || i == n_tok - 1;
+      const int nph = kPhasesPerLayer * h->desc.n_layers + (lm ? 2 : 0);
+      for (int k = 0; k < nph; ++k) {
+        A.phase_begin = i * ppt + k;
+        A.phase_end = A.phase_begin + 1;
+        HIPCHK(h, &h->err, (hipError_t)kernel_launch_plain(h->dP2, A, h->grid, kMaxBatch, h->stream));
+      }
+    }
+    return DEC_OK;
+  }
+  A.bar_base = h->bar_done;
+  HIPCHK(h, &h->err, (hipError_t)kernel_launch_resident(h->dP2, A, h->grid, kMaxBatch, h->stream));
   h->bar_done += launch_barriers(h->desc.n_layers, n_tok, lm_last_only);
   return DEC_OK;
 }
@@ -432,9 +491,18 @@ int upload_weights(dec_handle* h, const dec_weights_src* src) {
   dec_model_desc one = d;
   one.n_layers = 1;
   const Image im1 = image_layout(one);
+  // the batched prefill's tiled copy of every matrix
+  const bool bp = batched_prefill(d);
+  const Image im2 = image_layout(prefill_desc(d));
+  dec_model_desc one2 = prefill_desc(d);
+  one2.n_layers = 1;
+  const Image im12 = image_layout(one2);
+  uint16_t* dev_w2 = reinterpret_cast<uint16_t*>(static_cast<char*>(h->base) + h->ar.w2);
+  std::vector<uint16_t> stage2;
   std::vector<float> g1(3 * (size_t)d.d_model);
   for (int l = 0; l < d.n_layers && rc == DEC_OK; ++l) {
     stage.assign(chunk_elems, 0);
+    if (bp) stage2.assign(im12.layer_stride, 0);
     for (int kind = 0; kind < 9; ++kind) {
       const int idx = 1 + 9 * l + kind;
       const uint16_t* t = fetch(idx, rowbuf);
@@ -442,10 +510,13 @@ int upload_weights(dec_handle* h, const dec_weights_src* src) {
       size_t R, C;
       tensor_shape(d, idx, &R, &C);
       place_tensor(one, im1, 1 + kind, t, 0, R, stage.data(), g1.data());
+      if (bp) place_tensor(one2, im12, 1 + kind, t, 0, R, stage2.data(), g1.data());
     }
     if (rc != DEC_OK) break;
     std::memcpy(gains.data() + (size_t)l * 2 * d.d_model, g1.data(), 2 * (size_t)d.d_model * 4);
     hipError_t e = hipMemcpy(dev_w + (size_t)l * local.layer_stride, stage.data(), local.layer_stride * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess && bp)
+      e = hipMemcpy(dev_w2 + (size_t)l * im2.layer_stride, stage2.data(), im2.layer_stride * 2, hipMemcpyHostToDevice);
     if (e != hipSuccess) rc = hip_fail(h, &h->err, e, "hipMemcpy(weights)");
   }
   // embedding, final gain, LM head: row-major ones are copied as they are
@@ -469,6 +540,16 @@ int upload_weights(dec_handle* h, const dec_weights_src* src) {
       e = hipMemcpy(dev_w + off, stage.data(), stage.size() * 2, hipMemcpyHostToDevice);
     } else {
       e = hipMemcpy(dev_w + off, t, R * C * 2, hipMemcpyHostToDevice);
+    }
+    if (e == hipSuccess && bp) {
+      // the tiled copy: the embedding as it is, the LM head in tiles
+      if (idx == 0) {
+        e = hipMemcpy(dev_w2 + im2.off_E, t, R * C * 2, hipMemcpyHostToDevice);
+      } else {
+        stage.assign(im2.total - im2.off_lm, 0);
+        for (size_t r = 0; r < R; ++r) put_row(stage.data(), 0, r, t + r * C, C, true);
+        e = hipMemcpy(dev_w2 + im2.off_lm, stage.data(), stage.size() * 2, hipMemcpyHostToDevice);
+      }
     }
     if (e != hipSuccess) rc = hip_fail(h, &h->err, e, "hipMemcpy(embedding/LM head)");
   }
@@ -610,9 +691,17 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
     auto rows_wg = [&](long long rows) {
       return tiled ? kTileRows * per_wg((rows + kTileRows - 1) / kTileRows) : 2 * per_wg(rows / 2);
     };
-    const long long need_out = mb * std::max({rows_wg(3 * q), rows_wg(desc->d_model), rows_wg(2LL * desc->d_ffn),
-                                              rows_wg(desc->lm_vocab)});
-    if (need_out > kOutFloats || mb * rows_wg(desc->d_model) > kOwnFloats) {
+    long long need_out = mb * std::max({rows_wg(3 * q), rows_wg(desc->d_model), rows_wg(2LL * desc->d_ffn),
+                                        rows_wg(desc->lm_vocab)});
+    long long need_own = mb * rows_wg(desc->d_model);
+    if (batched_prefill(*desc)) {
+      // the batched prefill runs the tiled kernel with kMaxBatch columns
+      auto rows_t = [&](long long rows) { return kTileRows * per_wg((rows + kTileRows - 1) / kTileRows); };
+      need_out = std::max(need_out, (long long)kMaxBatch * std::max({rows_t(3 * q), rows_t(desc->d_model),
+                                                                      rows_t(2LL * desc->d_ffn), rows_t(desc->lm_vocab)}));
+      need_own = std::max(need_own, (long long)kMaxBatch * rows_t(desc->d_model));
+    }
+    if (need_out > kOutFloats || need_own > kOwnFloats) {
       fail(&h->err, DEC_ERR_UNSUPPORTED, "grid %d too small for this model (a workgroup would own %lld outputs)",
            h->grid, need_out);
       return bail(DEC_ERR_UNSUPPORTED);
@@ -700,9 +789,32 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
   P.trace = (h->debug & DEC_DEBUG_TRACE) ? reinterpret_cast<uint64_t*>(b + h->ar.trace) : nullptr;
   P.trace_stride = kTraceStride;
   h->wall_hz = (double)wall_khz * 1000.0;
+  P.cols_pos = 0;
   h->dP = reinterpret_cast<Params*>(b + h->ar.params);
   e = hipMemcpy(h->dP, &P, sizeof(Params), hipMemcpyHostToDevice);
   if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemcpy(params)"); return bail(DEC_ERR_DEVICE); }
+  if (batched_prefill(*desc)) {
+    // the batched prefill: same buffers and cache, tiled weights, kMaxBatch
+    // columns that are consecutive positions of the sequence
+    const Image im2 = image_layout(prefill_desc(*desc));
+    Params P2 = P;
+    P2.w = reinterpret_cast<const uint16_t*>(b + h->ar.w2);
+    P2.layer_stride = im2.layer_stride;
+    P2.off_qkv = im2.off_qkv; P2.off_o = im2.off_o; P2.off_gu = im2.off_gu; P2.off_d = im2.off_d;
+    P2.off_E = im2.off_E; P2.off_lm = im2.off_lm;
+    P2.B = kMaxBatch;
+    P2.cols_pos = 1;
+    P2.max_chunks = max_attn_chunks(desc->max_ctx, kMaxBatch * desc->n_heads, h->grid);
+    h->dP2 = reinterpret_cast<Params*>(b + h->ar.params2);
+    e = hipMemcpy(h->dP2, &P2, sizeof(Params), hipMemcpyHostToDevice);
+    if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemcpy(params)"); return bail(DEC_ERR_DEVICE); }
+    per_cu = 0;
+    e = (hipError_t)kernel_blocks_per_cu(kMaxBatch, &per_cu);
+    if (e != hipSuccess || per_cu < 1 || h->grid > per_cu * cus) {
+      fail(&h->err, DEC_ERR_UNSUPPORTED, "the batched prefill kernel cannot keep %d workgroups resident", h->grid);
+      return bail(DEC_ERR_UNSUPPORTED);
+    }
+  }
   if (hipDeviceSynchronize() != hipSuccess) { fail(&h->err, DEC_ERR_DEVICE, "device synchronize failed after upload"); return bail(DEC_ERR_DEVICE); }
   *out = h;
   return DEC_OK;
@@ -721,6 +833,22 @@ int dec_prefill(dec_handle* h, const int32_t* tokens, int32_t n, int32_t* out_to
       return fail(&h->err, DEC_ERR_TOKEN_RANGE, "prompt token %lld = %d outside [0, %d)", i, tokens[i], h->desc.vocab);
   HIPCHK(h, &h->err, hipMemcpyAsync(const_cast<int*>(h->P.prompt), tokens, (size_t)n * B * 4, hipMemcpyHostToDevice,
                                     h->stream));
+  if (h->dP2) {
+    // kMaxBatch positions per step; the last step's last live column is position n-1
+    int rc = launch_prefill(h, n, out_logits != nullptr);
+    if (rc) return rc;
+    h->pos = n;
+    h->has_prev_tok = true;
+    rc = check_device_error(h);
+    if (rc) return rc;
+    const int last = (n - 1) % kMaxBatch;
+    const size_t step = (size_t)(n - 1) / kMaxBatch;
+    HIPCHK(h, &h->err, hipMemcpy(out_tok, h->P.tok_out + step * kMaxBatch + last, 4, hipMemcpyDeviceToHost));
+    if (out_logits)
+      HIPCHK(h, &h->err, hipMemcpy(out_logits, h->P.logits + (size_t)last * h->desc.lm_vocab,
+                                   (size_t)h->desc.lm_vocab * 4, hipMemcpyDeviceToHost));
+    return DEC_OK;
+  }
   int rc = launch(h, 0, n, TOK_PROMPT, 1, out_logits != nullptr);
   if (rc) return rc;
   h->pos = n;

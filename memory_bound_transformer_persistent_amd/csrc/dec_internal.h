@@ -64,8 +64,9 @@ struct Params {
   size_t off_E, off_lm;       // element offsets of the embedding and the LM head
   const float* gains;         // [L][2][d] (attn, ffn) then g_final [d]
   const float* rope;          // [max_ctx][hd/2][2] (cos, sin)
-  int B;                      // sequences decoded together (batch)
-  uint16_t* kv;               // [L][2][B][H][max_ctx][hd] fp16
+  int B;                      // columns of the batched kernel: sequences decoded together (batch)
+  int cols_pos;               // 1: the columns are consecutive positions of one sequence (batched prefill)
+  uint16_t* kv;               // [L][2][B][H][max_ctx][hd] fp16 (one sequence when cols_pos)
   float* x;                   // residual stream [B][d]
   float* qkv;                 // [B][3q]: rotated, scaled q in the first q of each sequence
   float* att_o;               // attention output [B][q] (batch 1, fp32)
@@ -97,6 +98,7 @@ struct Launch {
   uint32_t bar_base; // barriers completed before this launch (wrapping)
   int phase_begin;   // run only phases with global index in [phase_begin, phase_end)
   int phase_end;
+  int pos_end;       // positions at or past pos_end are not computed (the ragged last step of a batched prefill)
 };
 
 DEC_HD inline int phases_per_token(int L) { return kPhasesPerLayer * L + 2; }

@@ -209,6 +209,18 @@ __device__ __forceinline__ void split(int n, int g, int G, int& b, int& e) {
   e = (int)((long long)n * (g + 1) / G);
 }
 
+// Columns of the batched kernel.  In a batched decode column b is sequence b
+// and every column is at the token step's position.  In a batched prefill
+// (cols_pos) the columns are kMaxBatch consecutive prompt positions of one
+// sequence: column b of step i is position pos0 + kMaxBatch i + b, and all
+// columns share that sequence's KV cache.
+__device__ __forceinline__ int step_pos(const Params& P, const Launch& A, int i) {
+  return A.pos0 + (P.cols_pos ? kMaxBatch * i : i);
+}
+__device__ __forceinline__ int col_pos(const Params& P, int pos, int b) { return P.cols_pos ? pos + b : pos; }
+__device__ __forceinline__ int kv_seq(const Params& P, int b) { return P.cols_pos ? 0 : b; }
+__device__ __forceinline__ int kv_heads(const Params& P) { return (P.cols_pos ? 1 : P.B) * P.H; }
+
 // ---------------------------------------------------------------------------
 // GEMV work and block streams
 // ---------------------------------------------------------------------------
@@ -747,25 +759,31 @@ __device__ __forceinline__ void w0_embed(const Params& P, int b, int tok, float*
 // o = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c, stores o to att_o and
 // resets the counter.  A single chunk stores o directly.
 template <int HD, int MB, class Wait>
-__device__ __forceinline__ bool attention_units(const Params& P, int l, int pos, int u_first, int u_stride,
-                                                Wait&& wait) {
+__device__ __forceinline__ bool attention_units(const Params& P, int l, int pos, int pos_end, int u_first,
+                                                int u_stride, Wait&& wait) {
   constexpr int LP = HD / 8, PPW = 64 / LP;
   constexpr int NPASS = 8;
   constexpr int GRP = PPW * NPASS;       // positions per register group
-  const int ctx = pos + 1, H = P.H, HB = P.B * P.H, G = gridDim.x;
-  const int C = attn_chunks(ctx, HB, G);
-  const int CH = (ctx + C - 1) / C;
+  // pos: the step's first new position (every column's at a batched
+  // decode); chunks are cut for the last column's context
+  const int H = P.H, HB = P.B * P.H, G = gridDim.x, KH = kv_heads(P);
+  const int ctx_max = col_pos(P, pos, P.B - 1) + 1;
+  const int C = attn_chunks(ctx_max, HB, G);
+  const int CH = (ctx_max + C - 1) / C;
   const int lane = threadIdx.x & 63;
   const int sub = lane % LP, pidx = lane / LP;
   const size_t head_elems = (size_t)P.max_ctx * HD;
   bool waited = false;
   for (int u = u_first; u < HB * C; u += u_stride) {
-    const int hb = u / C, c = u % C;             // hb = sequence * H + head
+    const int hb = u / C, c = u % C;             // hb = column * H + head
     const int seq = hb / H, h = hb - seq * H;
+    const int cpos = col_pos(P, pos, seq);
+    if (cpos >= pos_end) continue;               // a column past the prompt: every unit of it is skipped
     const int j0 = c * CH;
-    const int j1 = min(ctx, j0 + CH);
-    const uint16_t* kc = P.kv + ((size_t)(l * 2 + 0) * HB + hb) * head_elems;
-    const uint16_t* vc = P.kv + ((size_t)(l * 2 + 1) * HB + hb) * head_elems;
+    const int j1 = min(cpos + 1, j0 + CH);
+    const int kh = kv_seq(P, seq) * H + h;
+    const uint16_t* kc = P.kv + ((size_t)(l * 2 + 0) * KH + kh) * head_elems;
+    const uint16_t* vc = P.kv + ((size_t)(l * 2 + 1) * KH + kh) * head_elems;
     const rsrc_t rk = make_rsrc(kc, (uint32_t)(head_elems * 2));
     const rsrc_t rv = make_rsrc(vc, (uint32_t)(head_elems * 2));
     const rsrc_t rq = make_rsrc(P.qkv + (size_t)seq * 3 * P.q + h * HD, (uint32_t)(HD * 4));
@@ -778,19 +796,20 @@ __device__ __forceinline__ bool attention_units(const Params& P, int l, int pos,
 #pragma unroll
       for (int t = 0; t < NPASS; ++t) {
         const int j = g0 + t * PPW + pidx;
-        const uint32_t off = (j < j1 && (!pre || j != pos)) ? (uint32_t)(j * HD + 8 * sub) * 2u : kOOB;
+        const uint32_t off = (j < j1 && (!pre || j < pos)) ? (uint32_t)(j * HD + 8 * sub) * 2u : kOOB;
         kr[t] = ld_kv(rk, off);
         vr[t] = ld_kv(rv, off);
       }
       if (pre) {
         waited = true;
         if (!wait()) return false;
-        if (g0 <= pos && pos < g0 + GRP) {
-          // the row at pos, written before the barrier
+        if (g0 + GRP > pos) {
+          // rows of this step's positions, written before the barrier
 #pragma unroll
           for (int t = 0; t < NPASS; ++t) {
-            if (g0 + t * PPW + pidx == pos) {
-              const uint32_t off = (uint32_t)(pos * HD + 8 * sub) * 2u;
+            const int j = g0 + t * PPW + pidx;
+            if (j >= pos && j < j1) {
+              const uint32_t off = (uint32_t)(j * HD + 8 * sub) * 2u;
               kr[t] = ld_kv(rk, off);
               vr[t] = ld_kv(rv, off);
             }
@@ -904,13 +923,14 @@ __device__ __forceinline__ bool attention_units(const Params& P, int l, int pos,
 
 // Attention units of one wave: units u_first, u_first + u_stride, ...
 template <int MB, class Wait>
-__device__ __forceinline__ bool attention_wave(const Params& P, int l, int pos, int u_first, int u_stride, Wait&& wait) {
+__device__ __forceinline__ bool attention_wave(const Params& P, int l, int pos, int pos_end, int u_first, int u_stride,
+                                               Wait&& wait) {
   switch (P.hd) {
-    case 8: return attention_units<8, MB>(P, l, pos, u_first, u_stride, wait);
-    case 16: return attention_units<16, MB>(P, l, pos, u_first, u_stride, wait);
-    case 32: return attention_units<32, MB>(P, l, pos, u_first, u_stride, wait);
-    case 64: return attention_units<64, MB>(P, l, pos, u_first, u_stride, wait);
-    default: return attention_units<128, MB>(P, l, pos, u_first, u_stride, wait);
+    case 8: return attention_units<8, MB>(P, l, pos, pos_end, u_first, u_stride, wait);
+    case 16: return attention_units<16, MB>(P, l, pos, pos_end, u_first, u_stride, wait);
+    case 32: return attention_units<32, MB>(P, l, pos, pos_end, u_first, u_stride, wait);
+    case 64: return attention_units<64, MB>(P, l, pos, pos_end, u_first, u_stride, wait);
+    default: return attention_units<128, MB>(P, l, pos, pos_end, u_first, u_stride, wait);
   }
 }
 
@@ -924,32 +944,35 @@ __device__ __forceinline__ bool attention_wave(const Params& P, int l, int pos, 
 // stored for attention; k is rotated and v taken as it is, both rounded to
 // fp16 and appended to the KV cache at (layer l, position pos).
 template <int MB>
-__device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l, int pos, const int* tab_wg,
-                                                 bool want_logits, const float* scl, const float* out, float* xown) {
+__device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l, int pos, int pos_end,
+                                                 const int* tab_wg, bool want_logits, const float* scl,
+                                                 const float* out, float* xown) {
   const int lane = threadIdx.x & 63, B = P.B;
   if (!is_gemv(ph)) return;
   const int p0 = rfl(tab_wg[2 * ph]);
   const int n = rfl(tab_wg[2 * ph + 1]) - p0;
   const int own = kOwnFloats / MB;
   if (ph == PH_QKV) {
-    const int q = P.q, hd = P.hd, HB = B * P.H;
+    const int q = P.q, hd = P.hd, KH = kv_heads(P);
     const float qscale = 1.0f / sqrtf((float)hd);
     const size_t head_elems = (size_t)P.max_ctx * hd;
     for (int e = lane; e < n * MB; e += 64) {
       const int t = e / MB, b = e - t * MB;
-      if (b < B) {
+      const int cpos = col_pos(P, pos, b);
+      if (b < B && cpos < pos_end) {
         const int r = 2 * (p0 + t);                       // even row of Wqkv
+        const size_t kvrow = (size_t)(kv_seq(P, b) * P.H) * head_elems + (size_t)cpos * hd;
         const int part = r / q, rr = r - part * q;        // 0: q, 1: k, 2: v
         const int h = rr / hd, i = (rr - h * hd) >> 1;
         const float y0 = out[2 * t * MB + b] * scl[b], y1 = out[(2 * t + 1) * MB + b] * scl[b];
         if (part == 2) {
           const uint32_t vb = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y0) |
                               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y1) << 16);
-          uint16_t* vc = P.kv + ((size_t)(l * 2 + 1) * HB + b * P.H + h) * head_elems + (size_t)pos * hd + 2 * i;
+          uint16_t* vc = P.kv + ((size_t)(l * 2 + 1) * KH + h) * head_elems + kvrow + 2 * i;
           st_coh(reinterpret_cast<uint32_t*>(vc), vb);
         } else {
-          const float cs = ldg(P.rope + ((size_t)pos * (hd / 2) + i) * 2);
-          const float sn = ldg(P.rope + ((size_t)pos * (hd / 2) + i) * 2 + 1);
+          const float cs = ldg(P.rope + ((size_t)cpos * (hd / 2) + i) * 2);
+          const float sn = ldg(P.rope + ((size_t)cpos * (hd / 2) + i) * 2 + 1);
           const float z0 = y0 * cs - y1 * sn, z1 = y0 * sn + y1 * cs;
           if (part == 0) {
             st_coh(P.qkv + (size_t)b * 3 * q + rr, z0 * qscale);
@@ -957,7 +980,7 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l,
           } else {
             const uint32_t kb = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)z0) |
                                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)z1) << 16);
-            uint16_t* kc = P.kv + ((size_t)(l * 2) * HB + b * P.H + h) * head_elems + (size_t)pos * hd + 2 * i;
+            uint16_t* kc = P.kv + ((size_t)(l * 2) * KH + h) * head_elems + kvrow + 2 * i;
             st_coh(reinterpret_cast<uint32_t*>(kc), kb);
           }
         }
@@ -1010,7 +1033,7 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l,
 // token's input); workgroup 0 publishes it.  All sequences' partials are
 // requested before any is reduced.
 template <int MB>
-__device__ __forceinline__ void w0_argmax(const Params& P, int i, int* tok) {
+__device__ __forceinline__ void w0_argmax(const Params& P, int i, int cur_col, int* tok) {
   const int lane = threadIdx.x & 63, G = gridDim.x, B = P.B;
   const rsrc_t rv = make_rsrc(P.amax_v, (uint32_t)(B * G * 4)), ri = make_rsrc(P.amax_i, (uint32_t)(B * G * 4));
   float bv[MB];
@@ -1051,7 +1074,8 @@ __device__ __forceinline__ void w0_argmax(const Params& P, int i, int* tok) {
     }
     tok[b] = (bii == 0x7fffffff) ? 0 : bii;
     if (b < B && blockIdx.x == 0 && lane == 0) {
-      st_coh(P.tok_cur + b, tok[b]);
+      if (cur_col < 0) st_coh(P.tok_cur + b, tok[b]);
+      else if (b == cur_col) st_coh(P.tok_cur, tok[b]);
       st_coh(P.tok_out + (size_t)i * P.B + b, tok[b]);
     }
   }
@@ -1075,7 +1099,8 @@ __device__ __forceinline__ bool streamer_attention(const Params& P, const Launch
     __syncthreads();   // S1a
     return si[12] != 0;
   };
-  if (!attention_wave<MB>(P, id.l, A.pos0 + id.i, wave * gridDim.x + blockIdx.x, kWaves * gridDim.x, wait_s))
+  if (!attention_wave<MB>(P, id.l, step_pos(P, A, id.i), A.pos_end, wave * gridDim.x + blockIdx.x, kWaves * gridDim.x,
+                         wait_s))
     return false;
   wait_vm0();   // this wave's stores are complete before wave 0 arrives at the grid barrier
   __syncthreads();   // S1
@@ -1292,13 +1317,13 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   PhaseIt id = phase_at(P, A, g0);
   for (; id.g < g1; phase_next(P, A, id)) {
     if (id.ph == -2) continue;
-    const int pos = A.pos0 + id.i;
+    const int pos = step_pos(P, A, id.i);
     // outputs of the previous phase; this phase's LDS results start at zero
     if (!first) {
       if constexpr (MB > 1)
         if (is_gemv(prev_ph)) w0_combine<MB>(prev_ph, plan, slots, out);
-      w0_store_outputs<MB>(P, prev_ph, prev_l, A.pos0 + prev_i, tab_wg, A.write_logits && prev_i == A.n_tok - 1, scl,
-                           out, xown);
+      w0_store_outputs<MB>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
+                           A.write_logits && prev_i == A.n_tok - 1, scl, out, xown);
     }
     if (is_gemv(id.ph)) {
       const int np = rfl(tab_wg[2 * id.ph + 1]) - rfl(tab_wg[2 * id.ph]);
@@ -1324,7 +1349,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
         __syncthreads();   // S1a
         return r;
       };
-      ok = attention_wave<MB>(P, id.l, pos, blockIdx.x, kWaves * gridDim.x, wait_attn);
+      ok = attention_wave<MB>(P, id.l, pos, A.pos_end, blockIdx.x, kWaves * gridDim.x, wait_attn);
       wait_vm0();   // this wave's stores are complete before the next arrive
       first = false;
       if (!ok) return;
@@ -1335,7 +1360,10 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
         for (int b = 0; b < MB; ++b) {
           if (b < B) {
             int tok;
-            if (A.tok_src == TOK_PROMPT) tok = ldg(P.prompt + (size_t)b * A.n_tok + id.i);
+            if (A.tok_src == TOK_PROMPT) {
+              if (!P.cols_pos) tok = ldg(P.prompt + (size_t)b * A.n_tok + id.i);
+              else tok = pos + b < A.pos_end ? ldg(P.prompt + (pos + b - A.pos0)) : 0;
+            }
             else tok = have_tok ? tok_local[b] : ld_coh(P.tok_cur + b);
             tok = tok < 0 ? 0 : (tok >= P.V ? P.V - 1 : tok);
             w0_embed<MB>(P, b, tok, MB == 1 ? xs : stage + (size_t)b * gemv_span(P.d), xown, own);
@@ -1378,7 +1406,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     } else {
       ok = wait();
       if (ok) {
-        w0_argmax<MB>(P, id.i, tok_local);
+        w0_argmax<MB>(P, id.i, P.cols_pos ? min(A.pos_end - 1 - pos, B - 1) : -1, tok_local);
         have_tok = true;
       }
     }
@@ -1427,8 +1455,8 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   if (!first) {
     if constexpr (MB > 1)
       if (is_gemv(prev_ph)) w0_combine<MB>(prev_ph, plan, slots, out);
-    w0_store_outputs<MB>(P, prev_ph, prev_l, A.pos0 + prev_i, tab_wg, A.write_logits && prev_i == A.n_tok - 1, scl,
-                         out, xown);
+    w0_store_outputs<MB>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
+                         A.write_logits && prev_i == A.n_tok - 1, scl, out, xown);
   }
   wait_vm0();
 }

@@ -29,8 +29,8 @@ def stream():
     return torch.cuda.Stream(device=0)
 
 
-def make(shape, tensors, stream, batch=1, **kw):
-    return B.Decoder(B.ModelDesc.from_shape(shape, batch=batch), tensors=tensors, device=0,
+def make(shape, tensors, stream, batch=1, flags=0, **kw):
+    return B.Decoder(B.ModelDesc.from_shape(shape, batch=batch, flags=flags), tensors=tensors, device=0,
                      stream=stream.cuda_stream, **kw)
 
 
@@ -502,3 +502,87 @@ def test_dense2b_b8_sampled(stream):
             print(f"seq {b} position {p}: K/V excess/rms {ek.max():.1e} {ev.max():.1e}", flush=True)
             assert ek[0] <= 2e-5 and ev[0] <= 2e-5          # layer 0: exact inputs
             assert ek.max() <= KV_BATCH and ev.max() <= KV_BATCH
+
+
+# ----------------------------------------------------------------------------
+# batched prefill (DEC_FLAG_BATCHED_PREFILL): 8 prompt positions per step of
+# the matrix-core kernel, causal attention over the one sequence's cache.
+# Its matrix-product inputs are rounded to fp16 as in batched decode, so the
+# cache and logit bounds are the batched ones (KV_BATCH, 2e-2).
+# ----------------------------------------------------------------------------
+
+BP = B.DEC_FLAG_BATCHED_PREFILL
+
+
+@pytest.mark.parametrize("n", [1, 8, 21, 128])
+def test_tiny_batched_prefill(stream, n):
+    s = synth.shape_for("tiny")
+    t = synth.make_weights(s, seed=31, gain_jitter=0.1)
+    prompt = synth.make_prompt(s.vocab, n, seed=32 + n)[0]
+    steps = min(6, s.max_ctx - n)
+    fed, ref, ref_pre, _ = O.greedy_decode(s, t, prompt, steps)
+    _, K16, V16, _ = O.prefill_matrix(s, t, prompt)
+    with make(s, t, stream, flags=BP) as d:
+        tok, pre = d.prefill(prompt, want_logits=True)
+        check_logits(pre, ref_pre, f"batched prefill of {n}")
+        if O.top2_margin(ref_pre) > MARGIN:
+            assert tok == O.greedy(ref_pre)
+        assert d.position == n
+        for l in range(s.n_layers):
+            k, v = d.read_kv(l, n)
+            ek, ev = kv_excess(k, K16[l]), kv_excess(v, V16[l])
+            assert ek.max() <= KV_BATCH and ev.max() <= KV_BATCH, (l, ek.max(), ev.max())
+        for i in range(steps):
+            tk, lg = d.step(force_tok=int(fed[i]), want_logits=True)
+            check_logits(lg, ref[i], f"step {i} after batched prefill of {n}")
+            assert tk == int(np.argmax(lg))
+        if n == s.max_ctx:
+            with pytest.raises(B.DecError) as ei:
+                d.step()
+            assert ei.value.code == B.DEC_ERR_CONTEXT_FULL
+
+
+def test_batched_prefill_then_generate_matches_steps(stream):
+    """After a batched prefill the device-side next token feeds decode."""
+    s = synth.shape_for("tiny")
+    t = synth.make_weights(s, seed=33)
+    prompt = synth.make_prompt(s.vocab, 13, seed=34)[0]
+    with make(s, t, stream, flags=BP) as a, make(s, t, stream, flags=BP) as b:
+        ta, _ = a.prefill(prompt)
+        tb, _ = b.prefill(prompt)
+        assert ta == tb
+        ga = a.generate(10)
+        gb = [b.step()[0] for _ in range(10)]
+        assert list(ga) == gb
+
+
+def test_dense2b_batched_prefill_sampled(stream):
+    """The 128-token dense2b prompt through the batched prefill (16 steps of 8).
+
+    The oracle adopts the GPU cache for the positions before the one it
+    checks; its K/V rows and logits at the last prompt position and at the
+    first decode position must match.
+    """
+    w = synth.workload("dense2b")
+    s = w.shape
+    t = synth.workload_weights(w)
+    prompt = synth.make_prompt(s.vocab, w.prompt_len, seed=w.prompt_seed)[0]
+    n = len(prompt)
+    with make(s, t, stream, flags=BP) as d:
+        tok, pre = d.prefill(prompt, want_logits=True)
+        nxt, lg = d.step(force_tok=tok, want_logits=True)
+        kv = [d.read_kv(l, n + 1) for l in range(s.n_layers)]
+    assert nxt == int(np.argmax(lg))
+    K = np.stack([k for k, _ in kv])
+    V = np.stack([v for _, v in kv])
+    od = O.OracleDecoder(s, t)
+    for p, token, got in ((5, int(prompt[5]), None), (n - 1, int(prompt[n - 1]), pre), (n, int(tok), lg)):
+        od.load_cache(K[:, :, :p], V[:, :, :p], p)
+        ref = od.step(token)
+        ek = kv_excess(K[:, :, p], od.Kc[:, :, p])
+        ev = kv_excess(V[:, :, p], od.Vc[:, :, p])
+        print(f"position {p}: K/V excess/rms {ek.max():.1e} {ev.max():.1e}", flush=True)
+        assert ek[0] <= 2e-5 and ev[0] <= 2e-5
+        assert ek.max() <= KV_BATCH and ev.max() <= KV_BATCH
+        if got is not None:
+            check_logits(got, ref, f"position {p}")

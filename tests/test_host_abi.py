@@ -68,6 +68,19 @@ def test_batch_rules(lib):
     assert B.arena_bytes(desc(batch=8), 256) > B.arena_bytes(desc(batch=1), 256)
 
 
+def test_batched_prefill_flag_rules(lib):
+    f = B.DEC_FLAG_BATCHED_PREFILL
+    assert B.check_desc(desc(flags=f)) == B.DEC_OK, B.last_error()
+    assert B.check_desc(desc(flags=f, batch=2)) == B.DEC_ERR_BAD_DESC       # batch-1 handles only
+    assert B.check_desc(desc(flags=f | 1)) == B.DEC_ERR_BAD_DESC            # unknown bit
+    assert B.check_desc(desc(flags=f, d_model=3072)) == B.DEC_ERR_UNSUPPORTED   # inputs must fit in LDS
+    d2 = synth.shape_for("dense2b")
+    plain = B.arena_bytes(B.ModelDesc.from_shape(d2))
+    withf = B.arena_bytes(B.ModelDesc.from_shape(d2, flags=f))
+    # a second, tiled copy of the weights (about 4.6 GB) plus 8-column buffers
+    assert 4.5e9 < withf - plain < 4.8e9
+
+
 def test_valid_descs_and_arena(lib):
     for name in ("tiny", "dense2b", "lane2b"):
         d = B.ModelDesc.from_shape(synth.shape_for(name))
