@@ -88,6 +88,9 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--multilaunch", action="store_true", help="one kernel launch per phase (comparison)")
+    ap.add_argument("--batched-prefill", action="store_true",
+                    help="prefill 8 positions per step on the matrix-core kernel (DEC_FLAG_BATCHED_PREFILL); "
+                         "decode is unchanged")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run plain device-to-device copies of BYTES (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -127,7 +130,9 @@ def main():
 
     stream = torch.cuda.Stream(device=0)
     flags = B.DEC_DEBUG_MULTILAUNCH if args.multilaunch else 0
-    dec = B.Decoder(B.ModelDesc.from_shape(s, batch=nb), tensors=tensors, device=0, stream=stream.cuda_stream,
+    bp = args.batched_prefill and nb == 1
+    dec = B.Decoder(B.ModelDesc.from_shape(s, batch=nb, flags=B.DEC_FLAG_BATCHED_PREFILL if bp else 0),
+                    tensors=tensors, device=0, stream=stream.cuda_stream,
                     debug_flags=flags)
 
     # warm-up: prefill + W steps, then rewind so the timed steps are the workload's positions
@@ -136,7 +141,14 @@ def main():
         dec.step(want_tok=False)
     dec.sync()
     dec.reset()
+    # prefill (time to first token), timed on its own: not part of the metric
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    p0.record(stream)
     first_tok, _ = dec.prefill(prompt)
+    p1.record(stream)
+    p1.synchronize()
+    prefill_ms = p0.elapsed_time(p1)
     pos0 = dec.position
 
     K = args.steps
@@ -200,6 +212,8 @@ def main():
                      "algorithmic_bytes_per_launch": int(bytes_per_launch),
                      "avg_launch_ms": round(avg_launch_s * 1e3, 4)},
         "tokens_per_s_per_request": round(req_tok_s, 2),
+        "prefill": {"tokens": w.prompt_len, "sequences": nb, "ms": round(prefill_ms, 3),
+                    "mode": "batched, 8 positions per step" if bp else "one position per step"},
         "roofline_tokens_per_s": round(roof_tps * nb, 1),
         "roofline_tokens_per_s_per_request": round(roof_tps, 1),
         "hbm_GBps_per_step": round(R.mean_step_bytes(s, pos0, K, nb) * req_tok_s / 1e9, 1),
