@@ -946,13 +946,14 @@ __device__ __forceinline__ bool attention_wave(const Params& P, int l, int pos, 
 template <int MB>
 __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l, int pos, int pos_end,
                                                  const int* tab_wg, bool want_logits, const float* scl,
-                                                 const float* out, float* xown) {
+                                                 const float* out, float* xown, const float* rope_lds) {
   const int lane = threadIdx.x & 63, B = P.B;
   if (!is_gemv(ph)) return;
   const int p0 = rfl(tab_wg[2 * ph]);
   const int n = rfl(tab_wg[2 * ph + 1]) - p0;
   const int own = kOwnFloats / MB;
   if (ph == PH_QKV) {
+    wait_vm0();   // rope_lds: the step's rotary rows (LDS DMA during the QKV GEMV)
     const int q = P.q, hd = P.hd, KH = kv_heads(P);
     const float qscale = 1.0f / sqrtf((float)hd);
     const size_t head_elems = (size_t)P.max_ctx * hd;
@@ -971,8 +972,8 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l,
           uint16_t* vc = P.kv + ((size_t)(l * 2 + 1) * KH + h) * head_elems + kvrow + 2 * i;
           st_coh(reinterpret_cast<uint32_t*>(vc), vb);
         } else {
-          const float cs = ldg(P.rope + ((size_t)cpos * (hd / 2) + i) * 2);
-          const float sn = ldg(P.rope + ((size_t)cpos * (hd / 2) + i) * 2 + 1);
+          const float cs = rope_lds[(cpos - pos) * hd + 2 * i];
+          const float sn = rope_lds[(cpos - pos) * hd + 2 * i + 1];
           const float z0 = y0 * cs - y1 * sn, z1 = y0 * sn + y1 * cs;
           if (part == 0) {
             st_coh(P.qkv + (size_t)b * 3 * q + rr, z0 * qscale);
@@ -1006,23 +1007,37 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l,
       }
     }
   } else if (ph == PH_LM) {
-    for (int b = 0; b < B; ++b) {
-      float best = -INFINITY;
-      int bidx = 0x7fffffff;
-      for (int t = lane; t < 2 * n; t += 64) {
-        const float v = out[t * MB + b] * scl[b];
-        if (v > best) { best = v; bidx = 2 * p0 + t; }
-        if (want_logits) P.logits[(size_t)b * P.Vlm + 2 * p0 + t] = v;
-      }
+    // every sequence's best logit among this workgroup's rows, in one pass
+    float best[MB];
+    int bidx[MB];
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(best, off, 64);
-        const int oi = __shfl_xor(bidx, off, 64);
-        if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
+    for (int b = 0; b < MB; ++b) { best[b] = -INFINITY; bidx[b] = 0x7fffffff; }
+    for (int t = lane; t < 2 * n; t += 64) {
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        if (b < B) {
+          const float v = out[t * MB + b] * scl[b];
+          if (v > best[b]) { best[b] = v; bidx[b] = 2 * p0 + t; }
+          if (want_logits) P.logits[(size_t)b * P.Vlm + 2 * p0 + t] = v;
+        }
       }
-      if (lane == 0) {
-        st_coh(P.amax_v + (size_t)b * gridDim.x + blockIdx.x, best);
-        st_coh(P.amax_i + (size_t)b * gridDim.x + blockIdx.x, bidx);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        const float ov = __shfl_xor(best[b], off, 64);
+        const int oi = __shfl_xor(bidx[b], off, 64);
+        if (ov > best[b] || (ov == best[b] && oi < bidx[b])) { best[b] = ov; bidx[b] = oi; }
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        if (b < B) {
+          st_coh(P.amax_v + (size_t)b * gridDim.x + blockIdx.x, best[b]);
+          st_coh(P.amax_i + (size_t)b * gridDim.x + blockIdx.x, bidx[b]);
+        }
       }
     }
   }
@@ -1323,9 +1338,11 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       if constexpr (MB > 1)
         if (is_gemv(prev_ph)) w0_combine<MB>(prev_ph, plan, slots, out);
       w0_store_outputs<MB>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
-                           A.write_logits && prev_i == A.n_tok - 1, scl, out, xown);
+                           A.write_logits && prev_i == A.n_tok - 1, scl, out, xown, aux);
     }
-    if (is_gemv(id.ph)) {
+    if (MB == 1 && is_gemv(id.ph)) {
+      // the batch-1 streamers add into out (ds_add); the batched kernel's
+      // streamers and combine store every live element
       const int np = rfl(tab_wg[2 * id.ph + 1]) - rfl(tab_wg[2 * id.ph]);
       for (int t = lane; t < 2 * np * MB; t += 64) out[t] = 0.f;
     }
@@ -1422,6 +1439,11 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       else apply_gains_batch(reinterpret_cast<_Float16*>(xs), stage, gs, P.d, B, red);
     }
     __syncthreads();   // S1
+    if (id.ph == PH_QKV) {
+      // the rotary rows of this step's positions, for publishing q and k
+      const int ncols = P.cols_pos ? min(B, P.max_ctx - pos) : 1;
+      w0_dma_vec(aux, P.rope + (size_t)pos * P.hd, ncols * P.hd, 4, false);
+    }
     if (norm_phase(id)) {
       // every wave has applied this phase's gains: fetch the next normed
       // phase's into the same LDS while this GEMV runs
@@ -1456,7 +1478,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     if constexpr (MB > 1)
       if (is_gemv(prev_ph)) w0_combine<MB>(prev_ph, plan, slots, out);
     w0_store_outputs<MB>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
-                         A.write_logits && prev_i == A.n_tok - 1, scl, out, xown);
+                         A.write_logits && prev_i == A.n_tok - 1, scl, out, xown, aux);
   }
   wait_vm0();
 }
