@@ -586,3 +586,39 @@ def test_dense2b_batched_prefill_sampled(stream):
         assert ek.max() <= KV_BATCH and ev.max() <= KV_BATCH
         if got is not None:
             check_logits(got, ref, f"position {p}")
+
+
+# ----------------------------------------------------------------------------
+# other grid sizes: fewer workgroups than barrier groups, odd splits
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("grid", [7, 100])
+def test_tiny_other_grids(stream, grid):
+    s = synth.shape_for("tiny")
+    t = synth.make_weights(s, seed=41, gain_jitter=0.1)
+    prompt = synth.make_prompt(s.vocab, 40, seed=42)[0]
+    teacher_forced(s, t, prompt, 6, stream, grid=grid)
+
+
+def test_tiny_batch_and_batched_prefill_grid_64(stream):
+    s = synth.shape_for("tiny")
+    t = synth.make_weights(s, seed=43)
+    prompts = synth.make_prompt(s.vocab, 11, batch=8, seed=44)
+    refs = [O.greedy_decode(s, t, prompts[b], 3) for b in range(8)]
+    with make(s, t, stream, batch=8, grid=64) as d:
+        _, pre = d.prefill(prompts, want_logits=True)
+        pre = pre.reshape(8, -1)
+        for b in range(8):
+            check_logits(pre[b], refs[b][2], f"grid 64 seq {b} prefill")
+        for i in range(3):
+            ft = np.array([refs[b][0][i] for b in range(8)], dtype=np.int32)
+            _, lg = d.step(force_tok=ft, want_logits=True)
+            lg = lg.reshape(8, -1)
+            for b in range(8):
+                check_logits(lg[b], refs[b][1][i], f"grid 64 seq {b} step {i}")
+    fed, ref, ref_pre, _ = refs[0]
+    with make(s, t, stream, flags=BP, grid=64) as d:
+        _, pre = d.prefill(prompts[0], want_logits=True)
+        check_logits(pre, ref_pre, "grid 64 batched prefill")
+        _, lg = d.step(force_tok=int(fed[0]), want_logits=True)
+        check_logits(lg, ref[0], "grid 64 step after batched prefill")
