@@ -85,7 +85,7 @@ def main():
     ap.add_argument("--mode", choices=["step", "generate"], default="step",
                     help="step: one dec_step launch per token (token fed back on the device); "
                          "generate: all timed steps inside one dec_generate launch")
-    ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--cpu-steps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--multilaunch", action="store_true", help="one kernel launch per phase (comparison)")
     ap.add_argument("--batched-prefill", action="store_true",

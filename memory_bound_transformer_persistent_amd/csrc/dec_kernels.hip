@@ -59,6 +59,11 @@ constexpr int kTilesInFlight = 8;
 constexpr int kTabStride = 12;   // ints per (streamer, phase type) entry of the phase tables
 constexpr int kPlanInts = 16;    // per phase type: count, then up to 2 * kStreamers combine entries
 constexpr int kAuxFloats = 2048;
+// aux LDS: the step's rotary rows from 0 (the batched kernel's 8 positions
+// take up to 1024 floats, batch 1's one position at most 512) and, at batch 1
+// only, the local-attention partials (8 waves x (hd + 2) floats) from kAuxPart
+constexpr int kAuxPart = 512;
+static_assert(kAuxPart + kWaves * (128 + 2) <= kAuxFloats, "aux LDS");
 
 // LDS map (floats) for a kernel built for up to MB sequences:
 // input region | out | xown | red | scales | si | aux | gains | phase tables |
@@ -758,6 +763,86 @@ __device__ __forceinline__ void w0_embed(const Params& P, int b, int tok, float*
 // counter held C - 1) merges the head's C partials with a running max,
 // o = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c, stores o to att_o and
 // resets the counter.  A single chunk stores o directly.
+// Online-softmax partial of one (column, head) over positions [j0, j1): the
+// running max M, the sum of exp Lsum and the unnormalised sum acc of exp * V
+// (dims 8 sub .. 8 sub + 7, summed over the wave's position groups).  The
+// first group's loads of rows before pos go out before `wait` runs (once,
+// `waited` records it); rows from pos on were written in this step and are
+// read after it.  False if the wait reported a failed barrier.
+template <int HD, int MB, class Wait>
+__device__ __forceinline__ bool attend_chunk(const Params& P, rsrc_t rk, rsrc_t rv, rsrc_t rq, int j0, int j1, int pos,
+                                             bool& waited, Wait&& wait, float& M, float& Lsum, float (&acc)[8]) {
+  constexpr int LP = HD / 8, PPW = 64 / LP;
+  constexpr int NPASS = 8;
+  constexpr int GRP = PPW * NPASS;       // positions per register group
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % LP, pidx = lane / LP;
+  f32x4 qa = {0.f, 0.f, 0.f, 0.f}, qb = {0.f, 0.f, 0.f, 0.f};
+  for (int g0 = j0; g0 < j1; g0 += GRP) {
+    u32x4 kr[NPASS], vr[NPASS];
+    const bool pre = !waited;   // loads issued before the barrier skip the row at pos
+#pragma unroll
+    for (int t = 0; t < NPASS; ++t) {
+      const int j = g0 + t * PPW + pidx;
+      const uint32_t off = (j < j1 && (!pre || j < pos)) ? (uint32_t)(j * HD + 8 * sub) * 2u : kOOB;
+      kr[t] = ld_kv(rk, off);
+      vr[t] = ld_kv(rv, off);
+    }
+    if (pre) {
+      waited = true;
+      if (!wait()) return false;
+      if (g0 + GRP > pos) {
+        // rows of this step's positions, written before the barrier
+#pragma unroll
+        for (int t = 0; t < NPASS; ++t) {
+          const int j = g0 + t * PPW + pidx;
+          if (j >= pos && j < j1) {
+            const uint32_t off = (uint32_t)(j * HD + 8 * sub) * 2u;
+            kr[t] = ld_kv(rk, off);
+            vr[t] = ld_kv(rv, off);
+          }
+        }
+      }
+    }
+    if (g0 == j0) {
+      qa = ld_coh4(rq, (uint32_t)(32 * sub));
+      qb = ld_coh4(rq, (uint32_t)(32 * sub + 16));
+    }
+    float s[NPASS];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < NPASS; ++t) {
+      const int j = g0 + t * PPW + pidx;
+      float dsum = dot8(kr[t], qa, qb, 0.f);
+      dsum = group_sum<LP>(dsum);
+      s[t] = j < j1 ? dsum : -INFINITY;
+      mloc = fmaxf(mloc, s[t]);
+    }
+    const float Mn = fmaxf(M, wave_max(mloc));
+    const float alpha = M == -INFINITY ? 0.f : expf(M - Mn);
+    float lloc = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] *= alpha;
+#pragma unroll
+    for (int t = 0; t < NPASS; ++t) {
+      const int j = g0 + t * PPW + pidx;
+      const float e = j < j1 ? expf(s[t] - Mn) : 0.f;
+      lloc += e;
+      const f16x8 v = __builtin_bit_cast(f16x8, vr[t]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(e, (float)v[q], acc[q]);
+    }
+    // every lane of a position group holds the same e: count it once
+    Lsum = Lsum * alpha + wave_sum(sub == 0 ? lloc : 0.f);
+    M = Mn;
+  }
+  // sum over the position groups of the wave: lanes sub, sub+LP, ...
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    for (int off = LP; off < 64; off <<= 1) acc[q] += __shfl_xor(acc[q], off, 64);
+  return true;
+}
+
 template <int HD, int MB, class Wait>
 __device__ __forceinline__ bool attention_units(const Params& P, int l, int pos, int pos_end, int u_first,
                                                 int u_stride, Wait&& wait) {
@@ -789,69 +874,7 @@ __device__ __forceinline__ bool attention_units(const Params& P, int l, int pos,
     const rsrc_t rq = make_rsrc(P.qkv + (size_t)seq * 3 * P.q + h * HD, (uint32_t)(HD * 4));
     float M = -INFINITY, Lsum = 0.f;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    f32x4 qa = {0.f, 0.f, 0.f, 0.f}, qb = {0.f, 0.f, 0.f, 0.f};
-    for (int g0 = j0; g0 < j1; g0 += GRP) {
-      u32x4 kr[NPASS], vr[NPASS];
-      const bool pre = !waited;   // loads issued before the barrier skip the row at pos
-#pragma unroll
-      for (int t = 0; t < NPASS; ++t) {
-        const int j = g0 + t * PPW + pidx;
-        const uint32_t off = (j < j1 && (!pre || j < pos)) ? (uint32_t)(j * HD + 8 * sub) * 2u : kOOB;
-        kr[t] = ld_kv(rk, off);
-        vr[t] = ld_kv(rv, off);
-      }
-      if (pre) {
-        waited = true;
-        if (!wait()) return false;
-        if (g0 + GRP > pos) {
-          // rows of this step's positions, written before the barrier
-#pragma unroll
-          for (int t = 0; t < NPASS; ++t) {
-            const int j = g0 + t * PPW + pidx;
-            if (j >= pos && j < j1) {
-              const uint32_t off = (uint32_t)(j * HD + 8 * sub) * 2u;
-              kr[t] = ld_kv(rk, off);
-              vr[t] = ld_kv(rv, off);
-            }
-          }
-        }
-      }
-      if (g0 == j0) {
-        qa = ld_coh4(rq, (uint32_t)(32 * sub));
-        qb = ld_coh4(rq, (uint32_t)(32 * sub + 16));
-      }
-      float s[NPASS];
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < NPASS; ++t) {
-        const int j = g0 + t * PPW + pidx;
-        float dsum = dot8(kr[t], qa, qb, 0.f);
-        dsum = group_sum<LP>(dsum);
-        s[t] = j < j1 ? dsum : -INFINITY;
-        mloc = fmaxf(mloc, s[t]);
-      }
-      const float Mn = fmaxf(M, wave_max(mloc));
-      const float alpha = M == -INFINITY ? 0.f : expf(M - Mn);
-      float lloc = 0.f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] *= alpha;
-#pragma unroll
-      for (int t = 0; t < NPASS; ++t) {
-        const int j = g0 + t * PPW + pidx;
-        const float e = j < j1 ? expf(s[t] - Mn) : 0.f;
-        lloc += e;
-        const f16x8 v = __builtin_bit_cast(f16x8, vr[t]);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(e, (float)v[q], acc[q]);
-      }
-      // every lane of a position group holds the same e: count it once
-      Lsum = Lsum * alpha + wave_sum(sub == 0 ? lloc : 0.f);
-      M = Mn;
-    }
-    // sum over the position groups of the wave: lanes sub, sub+LP, ...
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      for (int off = LP; off < 64; off <<= 1) acc[q] += __shfl_xor(acc[q], off, 64);
+    if (!attend_chunk<HD, MB>(P, rk, rv, rq, j0, j1, pos, waited, wait, M, Lsum, acc)) return false;
     const size_t o_at = (size_t)seq * P.q + h * HD;
     if (C == 1) {
       if (pidx == 0) {
@@ -919,6 +942,78 @@ __device__ __forceinline__ bool attention_units(const Params& P, int l, int pos,
   }
   if (!waited) return wait();
   return true;
+}
+
+// Batch 1 at short context, with at least as many workgroups as heads: head
+// h runs on workgroup h alone, its eight waves taking eighths of the
+// positions; the partials meet in LDS and wave 0 merges them after S1 (no
+// partials in memory, no arrival counters).
+constexpr int kLocalAttnCtx = 768;
+__device__ __forceinline__ bool attention_is_local(const Params& P, int pos) {
+  return P.B == 1 && !P.cols_pos && P.H <= (int)gridDim.x && pos + 1 <= kLocalAttnCtx;
+}
+
+template <int HD, class Wait>
+__device__ __forceinline__ bool attention_local(const Params& P, int l, int pos, int wave, Wait&& wait, float* part) {
+  constexpr int LP = HD / 8;
+  const int lane = threadIdx.x & 63, sub = lane % LP, pidx = lane / LP;
+  const int h = blockIdx.x, ctx = pos + 1;
+  bool waited = false;
+  float M = -INFINITY, Lsum = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (h < P.H) {
+    const int CH = (ctx + kWaves - 1) / kWaves;
+    const int j0 = min(ctx, wave * CH), j1 = min(ctx, j0 + CH);
+    const size_t head_elems = (size_t)P.max_ctx * HD;
+    const rsrc_t rk = make_rsrc(P.kv + ((size_t)(l * 2 + 0) * P.H + h) * head_elems, (uint32_t)(head_elems * 2));
+    const rsrc_t rv = make_rsrc(P.kv + ((size_t)(l * 2 + 1) * P.H + h) * head_elems, (uint32_t)(head_elems * 2));
+    const rsrc_t rq = make_rsrc(P.qkv + h * HD, (uint32_t)(HD * 4));
+    if (!attend_chunk<HD, 1>(P, rk, rv, rq, j0, j1, pos, waited, wait, M, Lsum, acc)) return false;
+  }
+  if (!waited && !wait()) return false;
+  if (h < P.H) {
+    float* pl = part + wave * (HD + 2);
+    if (pidx == 0) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) pl[8 * sub + q] = acc[q];
+    }
+    if (lane == 0) { pl[HD] = M; pl[HD + 1] = Lsum; }
+  }
+  return true;
+}
+
+template <class Wait>
+__device__ __forceinline__ bool attention_local_wave(const Params& P, int l, int pos, int wave, Wait&& wait, float* part) {
+  switch (P.hd) {
+    case 8: return attention_local<8>(P, l, pos, wave, wait, part);
+    case 16: return attention_local<16>(P, l, pos, wave, wait, part);
+    case 32: return attention_local<32>(P, l, pos, wave, wait, part);
+    case 64: return attention_local<64>(P, l, pos, wave, wait, part);
+    default: return attention_local<128>(P, l, pos, wave, wait, part);
+  }
+}
+
+// Wave 0, after S1: o of this workgroup's head from the eight waves' partials,
+// in wave order (lane k owns dims 2k, 2k+1).
+__device__ __forceinline__ void w0_merge_local(const Params& P, const float* part) {
+  const int lane = threadIdx.x & 63, hd = P.hd, h = blockIdx.x;
+  if (h >= P.H || 2 * lane >= hd) return;
+  float Mx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, part[w * (hd + 2) + hd]);
+  float O0 = 0.f, O1 = 0.f, L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float* pl = part + w * (hd + 2);
+    const float m = pl[hd];
+    if (m == -INFINITY) continue;   // a wave with no positions
+    const float e = expf(m - Mx);
+    O0 = __builtin_fmaf(e, pl[2 * lane], O0);
+    O1 = __builtin_fmaf(e, pl[2 * lane + 1], O1);
+    L = __builtin_fmaf(e, pl[hd + 1], L);
+  }
+  st_coh(P.att_o + h * hd + 2 * lane, O0 / L);
+  st_coh(P.att_o + h * hd + 2 * lane + 1, O1 / L);
 }
 
 // Attention units of one wave: units u_first, u_first + u_stride, ...
@@ -1108,15 +1203,18 @@ __device__ __forceinline__ void w0_argmax(const Params& P, int i, int cur_col, i
 // requested before S1a), then S1 and S2 as in every phase.  False if wave 0
 // reported a failed grid barrier.
 template <int MB>
-__device__ __forceinline__ bool streamer_attention(const Params& P, const Launch& A, const PhaseIt& id, const int* si) {
+__device__ __forceinline__ bool streamer_attention(const Params& P, const Launch& A, const PhaseIt& id, const int* si,
+                                                   float* aux) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   auto wait_s = [&]() {
     __syncthreads();   // S1a
     return si[12] != 0;
   };
-  if (!attention_wave<MB>(P, id.l, step_pos(P, A, id.i), A.pos_end, wave * gridDim.x + blockIdx.x, kWaves * gridDim.x,
-                         wait_s))
-    return false;
+  const int pos = step_pos(P, A, id.i);
+  bool ok;
+  if (MB == 1 && attention_is_local(P, pos)) ok = attention_local_wave(P, id.l, pos, wave, wait_s, aux + kAuxPart);
+  else ok = attention_wave<MB>(P, id.l, pos, A.pos_end, wave * gridDim.x + blockIdx.x, kWaves * gridDim.x, wait_s);
+  if (!ok) return false;
   wait_vm0();   // this wave's stores are complete before wave 0 arrives at the grid barrier
   __syncthreads();   // S1
   __syncthreads();   // S2
@@ -1129,7 +1227,8 @@ __device__ __forceinline__ bool streamer_attention(const Params& P, const Launch
 // register slot k: the steps below are unrolled over the slots and never
 // copy a register that a load is still filling.
 __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, int g0, int g1, const int* tab,
-                                              float* xs, float* out, const float* gs, float* red, const int* si) {
+                                              float* xs, float* out, const float* gs, float* red, const int* si,
+                                              float* aux) {
   const int lane = threadIdx.x & 63;
   const uint32_t lane16 = (uint32_t)lane * 16u;
   Cursor cu;
@@ -1141,7 +1240,7 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
   for (; id.g < g1; phase_next(P, A, id)) {
     if (id.ph == -2) continue;
     if (id.ph == PH_ATTN) {
-      if (!streamer_attention<1>(P, A, id, si)) break;
+      if (!streamer_attention<1>(P, A, id, si, aux)) break;
       continue;
     }
     __syncthreads();   // S1a
@@ -1200,7 +1299,7 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
 template <int MB>
 __device__ __forceinline__ void streamer_tiles(const Params& P, const Launch& A, int g0, int g1, const int* tab,
                                                float* xs, float* out, float* slot, const float* gs, float* red,
-                                               const int* si) {
+                                               const int* si, float* aux) {
   static_assert(MB == 8, "the MFMA B operand maps columns to sequences mod 8");
   const int lane = threadIdx.x & 63, B = P.B;
   const uint32_t lane16 = (uint32_t)lane * 16u;
@@ -1214,7 +1313,7 @@ __device__ __forceinline__ void streamer_tiles(const Params& P, const Launch& A,
   for (; id.g < g1; phase_next(P, A, id)) {
     if (id.ph == -2) continue;
     if (id.ph == PH_ATTN) {
-      if (!streamer_attention<MB>(P, A, id, si)) break;
+      if (!streamer_attention<MB>(P, A, id, si, aux)) break;
       continue;
     }
     __syncthreads();   // S1a
@@ -1298,8 +1397,8 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   wait_lgkm0();
   __syncthreads();   // every streamer's tables are in LDS
   if (wave > 0) {
-    if constexpr (MB == 1) streamer_role(P, A, g0, g1, tab, xs, out, gs, red, si);
-    else streamer_tiles<MB>(P, A, g0, g1, tab, xs, out, slots + (wave - 1) * 2 * M::SlotN, gs, red, si);
+    if constexpr (MB == 1) streamer_role(P, A, g0, g1, tab, xs, out, gs, red, si, aux);
+    else streamer_tiles<MB>(P, A, g0, g1, tab, xs, out, slots + (wave - 1) * 2 * M::SlotN, gs, red, si, aux);
     return;
   }
   if constexpr (MB > 1) {
@@ -1366,7 +1465,8 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
         __syncthreads();   // S1a
         return r;
       };
-      ok = attention_wave<MB>(P, id.l, pos, A.pos_end, blockIdx.x, kWaves * gridDim.x, wait_attn);
+      if (MB == 1 && attention_is_local(P, pos)) ok = attention_local_wave(P, id.l, pos, 0, wait_attn, aux + kAuxPart);
+      else ok = attention_wave<MB>(P, id.l, pos, A.pos_end, blockIdx.x, kWaves * gridDim.x, wait_attn);
       wait_vm0();   // this wave's stores are complete before the next arrive
       first = false;
       if (!ok) return;
@@ -1439,6 +1539,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       else apply_gains_batch(reinterpret_cast<_Float16*>(xs), stage, gs, P.d, B, red);
     }
     __syncthreads();   // S1
+    if (MB == 1 && id.ph == PH_ATTN && attention_is_local(P, pos)) w0_merge_local(P, aux + kAuxPart);
     if (id.ph == PH_QKV) {
       // the rotary rows of this step's positions, for publishing q and k
       const int ncols = P.cols_pos ? min(B, P.max_ctx - pos) : 1;
