@@ -166,6 +166,8 @@ typedef struct dec_weights_src {
  *   watchdog_us: bound on every in-kernel barrier wait; on expiry the kernel
  *                exits and the call returns DEC_ERR_TIMEOUT.  0 = 2,000,000.
  *   grid:        workgroups of the resident kernel; 0 = one per compute unit.
+ *                It must be at least batch x n_heads (8 x n_heads with
+ *                DEC_FLAG_BATCHED_PREFILL), else DEC_ERR_UNSUPPORTED.
  */
 typedef struct dec_init_opts {
   int32_t device;

@@ -681,6 +681,15 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
     return bail(DEC_ERR_UNSUPPORTED);
   }
   {
+    // attention gives every (column, head) pair at least one workgroup
+    const long long pairs = (long long)(batched_prefill(*desc) ? kMaxBatch : desc->batch) * desc->n_heads;
+    if (pairs > h->grid) {
+      fail(&h->err, DEC_ERR_UNSUPPORTED, "grid %d is smaller than the %lld (sequence or position, head) pairs",
+           h->grid, pairs);
+      return bail(DEC_ERR_UNSUPPORTED);
+    }
+  }
+  {
     // per-workgroup GEMV results (every sequence) and residual rows live in
     // fixed LDS buffers; the batch kernel keeps kMaxBatch sequences' slots
     auto per_wg = [&](long long n) { return (n + h->grid - 1) / h->grid; };

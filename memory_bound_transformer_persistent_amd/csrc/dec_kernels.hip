@@ -59,10 +59,11 @@ constexpr int kTilesInFlight = 8;
 constexpr int kTabStride = 12;   // ints per (streamer, phase type) entry of the phase tables
 constexpr int kPlanInts = 16;    // per phase type: count, then up to 2 * kStreamers combine entries
 constexpr int kAuxFloats = 2048;
-// aux LDS: the step's rotary rows from 0 (the batched kernel's 8 positions
-// take up to 1024 floats, batch 1's one position at most 512) and, at batch 1
-// only, the local-attention partials (8 waves x (hd + 2) floats) from kAuxPart
-constexpr int kAuxPart = 512;
+// aux LDS: the step's rotary rows (up to 1024 floats; live from the QKV GEMV
+// to the QKV publication) and, in the attention phase, the eight waves'
+// attention partials (8 x (hd + 2) floats; live from the attention to its
+// merge after S1) share offset 0: their lifetimes do not overlap
+constexpr int kAuxPart = 0;
 static_assert(kAuxPart + kWaves * (128 + 2) <= kAuxFloats, "aux LDS");
 
 // LDS map (floats) for a kernel built for up to MB sequences:
@@ -512,7 +513,10 @@ __device__ __forceinline__ bool cursor_take(const Params& P, const int* tab, Cur
   cu.row_bytes = (uint32_t)rfl(e[T_ROWB]);
   cu.wrap = (uint32_t)rfl(e[T_WRAP]);
   cu.tail = (uint32_t)rfl(e[T_TAIL]);
-  cu.r = make_rsrc(gemv_base(P, cu.it.ph, cu.it.l), (uint32_t)rfl(e[T_NBYTES]));
+  // phase and layer through readfirstlane: the Params fields gemv_base reads
+  // then come from scalar loads, not a vector load that would wait for every
+  // weight load in flight
+  cu.r = make_rsrc(gemv_base(P, rfl(cu.it.ph), rfl(cu.it.l)), (uint32_t)rfl(e[T_NBYTES]));
   return true;
 }
 __device__ __forceinline__ void cursor_start(const Params& P, const Launch& A, int g0, int g1, const int* tab,
@@ -566,7 +570,7 @@ __device__ __forceinline__ bool tcursor_take(const Params& P, const int* tab, Ti
   cu.left = (uint32_t)left;
   cu.pad = (uint32_t)rfl(e[T_PAD]);
   cu.off = (uint32_t)rfl(e[T_OFF]);
-  cu.r = make_rsrc(gemv_base(P, cu.it.ph, cu.it.l), (uint32_t)rfl(e[T_NBYTES]));
+  cu.r = make_rsrc(gemv_base(P, rfl(cu.it.ph), rfl(cu.it.l)), (uint32_t)rfl(e[T_NBYTES]));
   return true;
 }
 __device__ __forceinline__ void tcursor_start(const Params& P, const Launch& A, int g0, int g1, const int* tab,
@@ -745,24 +749,60 @@ __device__ __forceinline__ void w0_embed(const Params& P, int b, int tok, float*
 // ---------------------------------------------------------------------------
 // attention
 // ---------------------------------------------------------------------------
-// Single-query attention of every head of every sequence over positions
-// 0..pos, split into chunks of positions; (sequence-head, chunk) units go
-// round-robin over the workgroups.  The QKV phase has already rotated and
-// scaled q and appended this position's key and value to the cache, so a
-// unit reads q and cached rows only.  A lane group of HD/8 lanes holds one
-// position (16 B of its K and V row per lane); K and V of NPASS*64/(HD/8)
-// positions are loaded together and an online softmax runs across such
-// groups.  The first group's rows of earlier positions are loaded before the
-// grid barrier releases (`wait` runs the barrier wait once); the row at pos,
-// written in this token's QKV phase, is read after it.  All eight waves of a
-// workgroup take units in the attention phase (wave w of workgroup g starts
-// at unit w * G + g); `wait` is where each of them meets the workgroup
-// barrier that follows wave 0's grid barrier.  Each unit stores an
-// unnormalised partial (max m, sum of exp l, sum of exp * V) and counts
-// itself on its head's arrival counter; the unit that arrives last (the
-// counter held C - 1) merges the head's C partials with a running max,
-// o = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c, stores o to att_o and
-// resets the counter.  A single chunk stores o directly.
+// Single-query attention of every (column, head) pair over its positions
+// 0..pos_b.  The QKV phase has already rotated and scaled q and appended this
+// step's keys and values to the cache, so attention reads q and cached rows
+// only.  A pair's positions are cut into chunks; each wave of the pair's
+// workgroups runs an online softmax over one chunk (attend_chunk), the
+// partials (max m, sum of exp l, sum of exp * V) of a workgroup's waves meet
+// in LDS, and the workgroups of a pair meet through memory and an arrival
+// counter: o = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c.
+
+// The last arrival of pair hb (column, head): reset its counter, merge its C
+// partials with a running max and store o at o_at.  Lane k owns dims 2k, 2k+1.
+template <int MB>
+__device__ __forceinline__ void merge_head(const Params& P, int hb, int C, size_t o_at) {
+  const int lane = threadIdx.x & 63, hd = P.hd;
+  if (lane == 0) st_coh(P.ctl + kCtlHead0 + hb, 0u);
+  const int dd = 2 * lane;
+  const bool act = dd < hd;
+  const float* pbase = P.part + (size_t)hb * P.max_chunks * hd + (act ? dd : 0);
+  const float* mbase = P.pml + (size_t)hb * P.max_chunks * 2;
+  float Mr = -INFINITY, Lr = 0.f, O0 = 0.f, O1 = 0.f;
+  constexpr int CB = 8;
+  for (int cc = 0; cc < C; cc += CB) {
+    float mv[CB], lv[CB], p0v[CB], p1v[CB];
+#pragma unroll
+    for (int t = 0; t < CB; ++t) {
+      const bool in = cc + t < C;
+      mv[t] = in ? ld_coh(mbase + 2 * (cc + t)) : -INFINITY;
+      lv[t] = in ? ld_coh(mbase + 2 * (cc + t) + 1) : 0.f;
+      p0v[t] = in ? ld_coh(pbase + (size_t)(cc + t) * hd) : 0.f;
+      p1v[t] = in ? ld_coh(pbase + (size_t)(cc + t) * hd + 1) : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < CB; ++t) {
+      if (mv[t] == -INFINITY) continue;
+      const float Mn = fmaxf(Mr, mv[t]);
+      const float a = Mr == -INFINITY ? 0.f : expf(Mr - Mn);
+      const float bs = expf(mv[t] - Mn);
+      O0 = O0 * a + p0v[t] * bs;
+      O1 = O1 * a + p1v[t] * bs;
+      Lr = Lr * a + lv[t] * bs;
+      Mr = Mn;
+    }
+  }
+  if (act) {
+    if constexpr (MB == 1) {
+      st_coh(P.att_o + o_at + dd, O0 / Lr);
+      st_coh(P.att_o + o_at + dd + 1, O1 / Lr);
+    } else {
+      st_coh(P.att_o16 + o_at + dd, __builtin_bit_cast(uint16_t, (_Float16)(O0 / Lr)));
+      st_coh(P.att_o16 + o_at + dd + 1, __builtin_bit_cast(uint16_t, (_Float16)(O1 / Lr)));
+    }
+  }
+}
+
 // Online-softmax partial of one (column, head) over positions [j0, j1): the
 // running max M, the sum of exp Lsum and the unnormalised sum acc of exp * V
 // (dims 8 sub .. 8 sub + 7, summed over the wave's position groups).  The
@@ -843,135 +883,47 @@ __device__ __forceinline__ bool attend_chunk(const Params& P, rsrc_t rk, rsrc_t 
   return true;
 }
 
-template <int HD, int MB, class Wait>
-__device__ __forceinline__ bool attention_units(const Params& P, int l, int pos, int pos_end, int u_first,
-                                                int u_stride, Wait&& wait) {
-  constexpr int LP = HD / 8, PPW = 64 / LP;
-  constexpr int NPASS = 8;
-  constexpr int GRP = PPW * NPASS;       // positions per register group
-  // pos: the step's first new position (every column's at a batched
-  // decode); chunks are cut for the last column's context
-  const int H = P.H, HB = P.B * P.H, G = gridDim.x, KH = kv_heads(P);
+// Attention by workgroups (the handle guarantees no more (column, head)
+// pairs HB than workgroups).  Pair hb gets W workgroups: workgroup g < HB * W takes
+// pair g / W, and its eight waves take chunks 8 (g mod W) .. 8 (g mod W) + 7
+// of the pair's C = 8 W chunks.  The waves' partials meet in LDS and wave 0
+// merges them after S1.  With W == 1 that is o.  Otherwise the workgroup's
+// partial goes to memory and the last of the pair's W workgroups (arrival
+// counter) merges the W partials.  W grows with the context so that a wave
+// covers about kWavePositions positions.
+constexpr int kWavePositions = 64;
+__device__ __forceinline__ int wg_per_head(const Params& P, int pos) {
+  const int HB = P.B * P.H, G = gridDim.x;   // HB <= G (checked when the handle is made)
   const int ctx_max = col_pos(P, pos, P.B - 1) + 1;
-  const int C = attn_chunks(ctx_max, HB, G);
-  const int CH = (ctx_max + C - 1) / C;
-  const int lane = threadIdx.x & 63;
-  const int sub = lane % LP, pidx = lane / LP;
-  const size_t head_elems = (size_t)P.max_ctx * HD;
-  bool waited = false;
-  for (int u = u_first; u < HB * C; u += u_stride) {
-    const int hb = u / C, c = u % C;             // hb = column * H + head
-    const int seq = hb / H, h = hb - seq * H;
-    const int cpos = col_pos(P, pos, seq);
-    if (cpos >= pos_end) continue;               // a column past the prompt: every unit of it is skipped
-    const int j0 = c * CH;
-    const int j1 = min(cpos + 1, j0 + CH);
-    const int kh = kv_seq(P, seq) * H + h;
-    const uint16_t* kc = P.kv + ((size_t)(l * 2 + 0) * KH + kh) * head_elems;
-    const uint16_t* vc = P.kv + ((size_t)(l * 2 + 1) * KH + kh) * head_elems;
-    const rsrc_t rk = make_rsrc(kc, (uint32_t)(head_elems * 2));
-    const rsrc_t rv = make_rsrc(vc, (uint32_t)(head_elems * 2));
-    const rsrc_t rq = make_rsrc(P.qkv + (size_t)seq * 3 * P.q + h * HD, (uint32_t)(HD * 4));
-    float M = -INFINITY, Lsum = 0.f;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (!attend_chunk<HD, MB>(P, rk, rv, rq, j0, j1, pos, waited, wait, M, Lsum, acc)) return false;
-    const size_t o_at = (size_t)seq * P.q + h * HD;
-    if (C == 1) {
-      if (pidx == 0) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float o = acc[q] / Lsum;
-          if constexpr (MB == 1) st_coh(P.att_o + o_at + 8 * sub + q, o);
-          else st_coh(P.att_o16 + o_at + 8 * sub + q, __builtin_bit_cast(uint16_t, (_Float16)o));
-        }
-      }
-      continue;
-    }
-    float* pp = P.part + ((size_t)hb * P.max_chunks + c) * HD;
-    float* pm = P.pml + ((size_t)hb * P.max_chunks + c) * 2;
-    if (pidx == 0) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) st_coh(pp + 8 * sub + q, acc[q]);
-    }
-    if (lane == 0) { st_coh(pm, M); st_coh(pm + 1, Lsum); }
-    wait_vm0();   // the partial is visible before the unit counts itself
-    uint32_t old = 0;
-    if (lane == 0)
-      old = __hip_atomic_fetch_add(P.ctl + kCtlHead0 + hb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = (uint32_t)__builtin_amdgcn_readlane((int)old, 0);
-    if (old != (uint32_t)(C - 1)) continue;
-    // last unit of this head: merge its C partials; lane k owns dims 2k, 2k+1
-    if (lane == 0) st_coh(P.ctl + kCtlHead0 + hb, 0u);
-    const int dd = 2 * lane;
-    const bool act = dd < HD;
-    const float* pbase = P.part + (size_t)hb * P.max_chunks * HD + (act ? dd : 0);
-    const float* mbase = P.pml + (size_t)hb * P.max_chunks * 2;
-    float Mr = -INFINITY, Lr = 0.f, O0 = 0.f, O1 = 0.f;
-    constexpr int CB = 16;
-    for (int cc = 0; cc < C; cc += CB) {
-      float mv[CB], lv[CB], p0v[CB], p1v[CB];
-#pragma unroll
-      for (int t = 0; t < CB; ++t) {
-        const bool in = cc + t < C;
-        mv[t] = in ? ld_coh(mbase + 2 * (cc + t)) : -INFINITY;
-        lv[t] = in ? ld_coh(mbase + 2 * (cc + t) + 1) : 0.f;
-        p0v[t] = in ? ld_coh(pbase + (size_t)(cc + t) * HD) : 0.f;
-        p1v[t] = in ? ld_coh(pbase + (size_t)(cc + t) * HD + 1) : 0.f;
-      }
-#pragma unroll
-      for (int t = 0; t < CB; ++t) {
-        if (mv[t] == -INFINITY) continue;
-        const float Mn = fmaxf(Mr, mv[t]);
-        const float a = Mr == -INFINITY ? 0.f : expf(Mr - Mn);
-        const float bs = expf(mv[t] - Mn);
-        O0 = O0 * a + p0v[t] * bs;
-        O1 = O1 * a + p1v[t] * bs;
-        Lr = Lr * a + lv[t] * bs;
-        Mr = Mn;
-      }
-    }
-    if (act) {
-      if constexpr (MB == 1) {
-        st_coh(P.att_o + o_at + dd, O0 / Lr);
-        st_coh(P.att_o + o_at + dd + 1, O1 / Lr);
-      } else {
-        st_coh(P.att_o16 + o_at + dd, __builtin_bit_cast(uint16_t, (_Float16)(O0 / Lr)));
-        st_coh(P.att_o16 + o_at + dd + 1, __builtin_bit_cast(uint16_t, (_Float16)(O1 / Lr)));
-      }
-    }
-  }
-  if (!waited) return wait();
-  return true;
+  const int want = (ctx_max + kWaves * kWavePositions - 1) / (kWaves * kWavePositions);
+  return max(1, min(min(want, G / HB), kChunkCap));
 }
 
-// Batch 1 at short context, with at least as many workgroups as heads: head
-// h runs on workgroup h alone, its eight waves taking eighths of the
-// positions; the partials meet in LDS and wave 0 merges them after S1 (no
-// partials in memory, no arrival counters).
-constexpr int kLocalAttnCtx = 768;
-__device__ __forceinline__ bool attention_is_local(const Params& P, int pos) {
-  return P.B == 1 && !P.cols_pos && P.H <= (int)gridDim.x && pos + 1 <= kLocalAttnCtx;
-}
-
-template <int HD, class Wait>
-__device__ __forceinline__ bool attention_local(const Params& P, int l, int pos, int wave, Wait&& wait, float* part) {
+template <int HD, int MB, class Wait>
+__device__ __forceinline__ bool attention_wg(const Params& P, int l, int pos, int pos_end, int wave, int W, Wait&& wait,
+                                             float* part) {
   constexpr int LP = HD / 8;
   const int lane = threadIdx.x & 63, sub = lane % LP, pidx = lane / LP;
-  const int h = blockIdx.x, ctx = pos + 1;
+  const int H = P.H, HB = P.B * P.H, hb = blockIdx.x / W, k = blockIdx.x - hb * W;
+  bool live = hb < HB;
+  const int seq = live ? hb / H : 0, h = hb - seq * H, cpos = col_pos(P, pos, seq);
+  live = live && cpos < pos_end;
   bool waited = false;
   float M = -INFINITY, Lsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (h < P.H) {
-    const int CH = (ctx + kWaves - 1) / kWaves;
-    const int j0 = min(ctx, wave * CH), j1 = min(ctx, j0 + CH);
+  if (live) {
+    const int ctx_max = col_pos(P, pos, P.B - 1) + 1, C = kWaves * W, CH = (ctx_max + C - 1) / C;
+    const int c = k * kWaves + wave;
+    const int j0 = min(cpos + 1, c * CH), j1 = min(cpos + 1, j0 + CH);
     const size_t head_elems = (size_t)P.max_ctx * HD;
-    const rsrc_t rk = make_rsrc(P.kv + ((size_t)(l * 2 + 0) * P.H + h) * head_elems, (uint32_t)(head_elems * 2));
-    const rsrc_t rv = make_rsrc(P.kv + ((size_t)(l * 2 + 1) * P.H + h) * head_elems, (uint32_t)(head_elems * 2));
-    const rsrc_t rq = make_rsrc(P.qkv + h * HD, (uint32_t)(HD * 4));
-    if (!attend_chunk<HD, 1>(P, rk, rv, rq, j0, j1, pos, waited, wait, M, Lsum, acc)) return false;
+    const int KH = kv_heads(P), kh = kv_seq(P, seq) * H + h;
+    const rsrc_t rk = make_rsrc(P.kv + ((size_t)(l * 2 + 0) * KH + kh) * head_elems, (uint32_t)(head_elems * 2));
+    const rsrc_t rv = make_rsrc(P.kv + ((size_t)(l * 2 + 1) * KH + kh) * head_elems, (uint32_t)(head_elems * 2));
+    const rsrc_t rq = make_rsrc(P.qkv + (size_t)seq * 3 * P.q + h * HD, (uint32_t)(HD * 4));
+    if (!attend_chunk<HD, MB>(P, rk, rv, rq, j0, j1, pos, waited, wait, M, Lsum, acc)) return false;
   }
   if (!waited && !wait()) return false;
-  if (h < P.H) {
+  if (live) {
     float* pl = part + wave * (HD + 2);
     if (pidx == 0) {
 #pragma unroll
@@ -982,22 +934,30 @@ __device__ __forceinline__ bool attention_local(const Params& P, int l, int pos,
   return true;
 }
 
-template <class Wait>
-__device__ __forceinline__ bool attention_local_wave(const Params& P, int l, int pos, int wave, Wait&& wait, float* part) {
+template <int MB, class Wait>
+__device__ __forceinline__ bool attention_wg_wave(const Params& P, int l, int pos, int pos_end, int wave, int W,
+                                                  Wait&& wait, float* part) {
   switch (P.hd) {
-    case 8: return attention_local<8>(P, l, pos, wave, wait, part);
-    case 16: return attention_local<16>(P, l, pos, wave, wait, part);
-    case 32: return attention_local<32>(P, l, pos, wave, wait, part);
-    case 64: return attention_local<64>(P, l, pos, wave, wait, part);
-    default: return attention_local<128>(P, l, pos, wave, wait, part);
+    case 8: return attention_wg<8, MB>(P, l, pos, pos_end, wave, W, wait, part);
+    case 16: return attention_wg<16, MB>(P, l, pos, pos_end, wave, W, wait, part);
+    case 32: return attention_wg<32, MB>(P, l, pos, pos_end, wave, W, wait, part);
+    case 64: return attention_wg<64, MB>(P, l, pos, pos_end, wave, W, wait, part);
+    default: return attention_wg<128, MB>(P, l, pos, pos_end, wave, W, wait, part);
   }
 }
 
-// Wave 0, after S1: o of this workgroup's head from the eight waves' partials,
-// in wave order (lane k owns dims 2k, 2k+1).
-__device__ __forceinline__ void w0_merge_local(const Params& P, const float* part) {
-  const int lane = threadIdx.x & 63, hd = P.hd, h = blockIdx.x;
-  if (h >= P.H || 2 * lane >= hd) return;
+// Wave 0, after S1: the workgroup's pair from its eight waves' partials, in
+// wave order (lane k owns dims 2k, 2k+1); then o, or the workgroup's partial
+// and, for the pair's last workgroup, the merge of all W.
+template <int MB>
+__device__ __forceinline__ void w0_merge_wg(const Params& P, int pos, int pos_end, int W, const float* part) {
+  const int lane = threadIdx.x & 63, hd = P.hd, H = P.H, HB = P.B * P.H;
+  const int hb = blockIdx.x / W, k = blockIdx.x - hb * W;
+  if (hb >= HB) return;
+  const int seq = hb / H, h = hb - seq * H;
+  if (col_pos(P, pos, seq) >= pos_end) return;
+  const bool act = 2 * lane < hd;
+  const int dd = act ? 2 * lane : 0;
   float Mx = -INFINITY;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, part[w * (hd + 2) + hd]);
@@ -1008,25 +968,32 @@ __device__ __forceinline__ void w0_merge_local(const Params& P, const float* par
     const float m = pl[hd];
     if (m == -INFINITY) continue;   // a wave with no positions
     const float e = expf(m - Mx);
-    O0 = __builtin_fmaf(e, pl[2 * lane], O0);
-    O1 = __builtin_fmaf(e, pl[2 * lane + 1], O1);
+    O0 = __builtin_fmaf(e, pl[dd], O0);
+    O1 = __builtin_fmaf(e, pl[dd + 1], O1);
     L = __builtin_fmaf(e, pl[hd + 1], L);
   }
-  st_coh(P.att_o + h * hd + 2 * lane, O0 / L);
-  st_coh(P.att_o + h * hd + 2 * lane + 1, O1 / L);
-}
-
-// Attention units of one wave: units u_first, u_first + u_stride, ...
-template <int MB, class Wait>
-__device__ __forceinline__ bool attention_wave(const Params& P, int l, int pos, int pos_end, int u_first, int u_stride,
-                                               Wait&& wait) {
-  switch (P.hd) {
-    case 8: return attention_units<8, MB>(P, l, pos, pos_end, u_first, u_stride, wait);
-    case 16: return attention_units<16, MB>(P, l, pos, pos_end, u_first, u_stride, wait);
-    case 32: return attention_units<32, MB>(P, l, pos, pos_end, u_first, u_stride, wait);
-    case 64: return attention_units<64, MB>(P, l, pos, pos_end, u_first, u_stride, wait);
-    default: return attention_units<128, MB>(P, l, pos, pos_end, u_first, u_stride, wait);
+  const size_t o_at = (size_t)seq * P.q + h * hd;
+  if (W == 1) {
+    if (act) {
+      if constexpr (MB == 1) {
+        st_coh(P.att_o + o_at + dd, O0 / L);
+        st_coh(P.att_o + o_at + dd + 1, O1 / L);
+      } else {
+        st_coh(P.att_o16 + o_at + dd, __builtin_bit_cast(uint16_t, (_Float16)(O0 / L)));
+        st_coh(P.att_o16 + o_at + dd + 1, __builtin_bit_cast(uint16_t, (_Float16)(O1 / L)));
+      }
+    }
+    return;
   }
+  float* pp = P.part + ((size_t)hb * P.max_chunks + k) * hd;
+  float* pm = P.pml + ((size_t)hb * P.max_chunks + k) * 2;
+  if (act) { st_coh(pp + dd, O0); st_coh(pp + dd + 1, O1); }
+  if (lane == 0) { st_coh(pm, Mx); st_coh(pm + 1, L); }
+  wait_vm0();   // the partial is visible before the workgroup counts itself
+  uint32_t old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(P.ctl + kCtlHead0 + hb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = (uint32_t)__builtin_amdgcn_readlane((int)old, 0);
+  if (old == (uint32_t)(W - 1)) merge_head<MB>(P, hb, W, o_at);
 }
 
 // ---------------------------------------------------------------------------
@@ -1150,7 +1117,7 @@ __device__ __forceinline__ void w0_argmax(const Params& P, int i, int cur_col, i
   int bi[MB];
 #pragma unroll
   for (int b = 0; b < MB; ++b) { bv[b] = -INFINITY; bi[b] = 0x7fffffff; }
-  constexpr int K = 4;   // partials per lane per sequence and pass
+  constexpr int K = MB == 1 ? 4 : 2;   // partials per lane per sequence and pass
   for (int t0 = 0; t0 < G; t0 += 64 * K) {
     float v[MB][K];
     int ix[MB][K];
@@ -1212,8 +1179,7 @@ __device__ __forceinline__ bool streamer_attention(const Params& P, const Launch
   };
   const int pos = step_pos(P, A, id.i);
   bool ok;
-  if (MB == 1 && attention_is_local(P, pos)) ok = attention_local_wave(P, id.l, pos, wave, wait_s, aux + kAuxPart);
-  else ok = attention_wave<MB>(P, id.l, pos, A.pos_end, wave * gridDim.x + blockIdx.x, kWaves * gridDim.x, wait_s);
+  ok = attention_wg_wave<MB>(P, id.l, pos, A.pos_end, wave, wg_per_head(P, pos), wait_s, aux + kAuxPart);
   if (!ok) return false;
   wait_vm0();   // this wave's stores are complete before wave 0 arrives at the grid barrier
   __syncthreads();   // S1
@@ -1465,8 +1431,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
         __syncthreads();   // S1a
         return r;
       };
-      if (MB == 1 && attention_is_local(P, pos)) ok = attention_local_wave(P, id.l, pos, 0, wait_attn, aux + kAuxPart);
-      else ok = attention_wave<MB>(P, id.l, pos, A.pos_end, blockIdx.x, kWaves * gridDim.x, wait_attn);
+      ok = attention_wg_wave<MB>(P, id.l, pos, A.pos_end, 0, wg_per_head(P, pos), wait_attn, aux + kAuxPart);
       wait_vm0();   // this wave's stores are complete before the next arrive
       first = false;
       if (!ok) return;
@@ -1539,7 +1504,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       else apply_gains_batch(reinterpret_cast<_Float16*>(xs), stage, gs, P.d, B, red);
     }
     __syncthreads();   // S1
-    if (MB == 1 && id.ph == PH_ATTN && attention_is_local(P, pos)) w0_merge_local(P, aux + kAuxPart);
+    if (id.ph == PH_ATTN) w0_merge_wg<MB>(P, pos, A.pos_end, wg_per_head(P, pos), aux + kAuxPart);
     if (id.ph == PH_QKV) {
       // the rotary rows of this step's positions, for publishing q and k
       const int ncols = P.cols_pos ? min(B, P.max_ctx - pos) : 1;

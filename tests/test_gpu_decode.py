@@ -622,3 +622,13 @@ def test_tiny_batch_and_batched_prefill_grid_64(stream):
         check_logits(pre, ref_pre, "grid 64 batched prefill")
         _, lg = d.step(force_tok=int(fed[0]), want_logits=True)
         check_logits(lg, ref[0], "grid 64 step after batched prefill")
+
+
+def test_grid_smaller_than_head_pairs_is_unsupported(stream):
+    s = synth.shape_for("tiny")
+    t = synth.make_weights(s, seed=45)
+    with pytest.raises(B.DecError) as ei:
+        make(s, t, stream, batch=8, grid=16)      # 8 x 4 pairs > 16 workgroups
+    assert ei.value.code == B.DEC_ERR_UNSUPPORTED
+    with make(s, t, stream, batch=4, grid=16) as d:   # 16 pairs: allowed
+        d.prefill(synth.make_prompt(s.vocab, 5, batch=4, seed=46))
