@@ -434,41 +434,47 @@ __device__ __forceinline__ void build_plans(const int* tab_all, int* plan) {
 
 // Wave 0, after the streamers have stored a phase's results: out[group] =
 // the sum of its shared slots, added in streamer order.  Lane k holds plan
-// entry k; readlane broadcasts it, so the slot reads do not wait on each other.
+// entry k and readlane broadcasts it; every slot read is issued before the
+// first add (entries past the count read slot 0 and count as zero), so the
+// reads overlap, and the adds and stores follow under uniform conditions.
 template <int MB>
 __device__ __forceinline__ void w0_combine(int ph, const int* plan, const float* slots, float* out) {
-  constexpr int SN = Lds<MB>::SlotN, NE = 2 * kStreamers;
+  constexpr int SN = Lds<MB>::SlotN, NE = 2 * kStreamers, PER = SN / 64;
   static_assert(SN % 64 == 0, "slot elements are spread over the wave's lanes");
   const int lane = threadIdx.x & 63;
   const int* pl = plan + ph * kPlanInts;
   const int cnt = rfl(pl[0]);
   if (cnt == 0) return;
   const int mine = pl[1 + (lane < NE ? lane : 0)];
+  int ent[NE];
 #pragma unroll
-  for (int i0 = 0; i0 < SN; i0 += 64) {
-    const int i = i0 + lane;
-    float v[NE];
+  for (int k = 0; k < NE; ++k) ent[k] = k < cnt ? __builtin_amdgcn_readlane(mine, k) : 0;
+  float v[NE][PER];
 #pragma unroll
-    for (int k = 0; k < NE; ++k) {
-      const int ent = __builtin_amdgcn_readlane(mine, k);
-      v[k] = k < cnt ? slots[(ent & 15) * SN + i] : 0.f;
+  for (int k = 0; k < NE; ++k) {
+    const float* sl = slots + (ent[k] & 15) * SN + lane;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) v[k][p] = sl[64 * p];
+  }
+  wait_lgkm0();
+  float acc[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) acc[p] = 0.f;
+#pragma unroll
+  for (int k = 0; k < NE; ++k) {
+    const bool live = k < cnt;
+    const bool first = live && ((ent[k] >> 28) & 1);
+    const bool last = live && (k == cnt - 1 || (k + 1 < NE && ((ent[k + 1] >> 28) & 1)));
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const float x = live ? v[k][p] : 0.f;
+      acc[p] = first ? x : acc[p] + x;
     }
-    float acc = 0.f;
-    int cur = -1;
+    if (last) {
+      const int g = (ent[k] >> 4) & 0xFFFFFF;
 #pragma unroll
-    for (int k = 0; k < NE; ++k) {
-      if (k < cnt) {
-        const int ent = __builtin_amdgcn_readlane(mine, k);
-        if ((ent >> 28) & 1) {
-          if (cur >= 0) out[cur * SN + i] = acc;
-          acc = v[k];
-          cur = (ent >> 4) & 0xFFFFFF;
-        } else {
-          acc += v[k];
-        }
-      }
+      for (int p = 0; p < PER; ++p) out[g * SN + lane + 64 * p] = acc[p];
     }
-    if (cur >= 0) out[cur * SN + i] = acc;
   }
 }
 
