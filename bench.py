@@ -208,7 +208,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s",
                      "frac": round(achieved / peak, 4),
                      "traffic": traffic,
-                     "kernel": "dec_resident_batch" if nb > 1 else "dec_resident",
+                     "kernel": f"dec_resident_{'batch_' if nb > 1 else ''}hd{s.head_dim}",
                      "algorithmic_bytes_per_launch": int(bytes_per_launch),
                      "avg_launch_ms": round(avg_launch_s * 1e3, 4)},
         "tokens_per_s_per_request": round(req_tok_s, 2),

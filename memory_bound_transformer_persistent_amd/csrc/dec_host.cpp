@@ -385,13 +385,13 @@ int launch(dec_handle* h, int pos0, int n_tok, int tok_src, int lm_last_only, in
       for (int k = 0; k < nph; ++k) {
         A.phase_begin = i * ppt + k;
         A.phase_end = A.phase_begin + 1;
-        HIPCHK(h, &h->err, (hipError_t)kernel_launch_plain(h->dP, A, h->grid, h->desc.batch, h->stream));
+        HIPCHK(h, &h->err, (hipError_t)kernel_launch_plain(h->dP, A, h->grid, h->desc.batch, h->desc.head_dim, h->stream));
       }
     }
     return DEC_OK;
   }
   A.bar_base = h->bar_done;
-  HIPCHK(h, &h->err, (hipError_t)kernel_launch_resident(h->dP, A, h->grid, h->desc.batch, h->stream));
+  HIPCHK(h, &h->err, (hipError_t)kernel_launch_resident(h->dP, A, h->grid, h->desc.batch, h->desc.head_dim, h->stream));
   h->bar_done += launch_barriers(h->desc.n_layers, n_tok, lm_last_only);
   return DEC_OK;
 }
@@ -420,13 +420,13 @@ int launch_prefill(dec_handle* h, int n, int write_logits) {
       for (int k = 0; k < nph; ++k) {
         A.phase_begin = i * ppt + k;
         A.phase_end = A.phase_begin + 1;
-        HIPCHK(h, &h->err, (hipError_t)kernel_launch_plain(h->dP2, A, h->grid, kMaxBatch, h->stream));
+        HIPCHK(h, &h->err, (hipError_t)kernel_launch_plain(h->dP2, A, h->grid, kMaxBatch, h->desc.head_dim, h->stream));
       }
     }
     return DEC_OK;
   }
   A.bar_base = h->bar_done;
-  HIPCHK(h, &h->err, (hipError_t)kernel_launch_resident(h->dP2, A, h->grid, kMaxBatch, h->stream));
+  HIPCHK(h, &h->err, (hipError_t)kernel_launch_resident(h->dP2, A, h->grid, kMaxBatch, h->desc.head_dim, h->stream));
   h->bar_done += launch_barriers(h->desc.n_layers, n_tok, lm_last_only);
   return DEC_OK;
 }
@@ -674,7 +674,7 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
   hipError_t e = (hipError_t)kernel_prepare();
   if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipFuncSetAttribute"); return bail(DEC_ERR_DEVICE); }
   int per_cu = 0;
-  e = (hipError_t)kernel_blocks_per_cu(desc->batch, &per_cu);
+  e = (hipError_t)kernel_blocks_per_cu(desc->batch, desc->head_dim, &per_cu);
   if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"); return bail(DEC_ERR_DEVICE); }
   if (per_cu < 1 || h->grid > per_cu * cus) {
     fail(&h->err, DEC_ERR_UNSUPPORTED, "grid %d exceeds co-resident capacity %d x %d", h->grid, per_cu, cus);
@@ -818,7 +818,7 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
     e = hipMemcpy(h->dP2, &P2, sizeof(Params), hipMemcpyHostToDevice);
     if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemcpy(params)"); return bail(DEC_ERR_DEVICE); }
     per_cu = 0;
-    e = (hipError_t)kernel_blocks_per_cu(kMaxBatch, &per_cu);
+    e = (hipError_t)kernel_blocks_per_cu(kMaxBatch, desc->head_dim, &per_cu);
     if (e != hipSuccess || per_cu < 1 || h->grid > per_cu * cus) {
       fail(&h->err, DEC_ERR_UNSUPPORTED, "the batched prefill kernel cannot keep %d workgroups resident", h->grid);
       return bail(DEC_ERR_UNSUPPORTED);

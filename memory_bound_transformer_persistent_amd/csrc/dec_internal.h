@@ -143,11 +143,12 @@ inline uint32_t launch_barriers(int L, int n_tok, int lm_last_only) {
 
 // Launch helpers defined next to the kernel (dec_kernels.hip).  P points to a
 // device copy of the parameters; stream is a hipStream_t; batch selects the
-// kernel built for one sequence or for up to kMaxBatch; each returns a
-// hipError_t value (0 = success).
-int kernel_prepare();                                   // raise the dynamic-LDS limit
-int kernel_blocks_per_cu(int batch, int* out);          // co-resident workgroups per CU
-int kernel_launch_resident(const Params* P, const Launch& A, int grid, int batch, void* stream);  // cooperative
-int kernel_launch_plain(const Params* P, const Launch& A, int grid, int batch, void* stream);     // ordinary
+// kernel built for one sequence or for up to kMaxBatch and hd the one built
+// for that head dimension (8, 16, 32, 64 or 128); each returns a hipError_t
+// value (0 = success; hipErrorInvalidValue for another head dimension).
+int kernel_prepare();                                            // raise the dynamic-LDS limit
+int kernel_blocks_per_cu(int batch, int hd, int* out);           // co-resident workgroups per CU
+int kernel_launch_resident(const Params* P, const Launch& A, int grid, int batch, int hd, void* stream);  // cooperative
+int kernel_launch_plain(const Params* P, const Launch& A, int grid, int batch, int hd, void* stream);     // ordinary
 
 }  // namespace decmono

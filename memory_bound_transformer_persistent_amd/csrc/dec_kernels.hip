@@ -940,17 +940,6 @@ __device__ __forceinline__ bool attention_wg(const Params& P, int l, int pos, in
   return true;
 }
 
-template <int MB, class Wait>
-__device__ __forceinline__ bool attention_wg_wave(const Params& P, int l, int pos, int pos_end, int wave, int W,
-                                                  Wait&& wait, float* part) {
-  switch (P.hd) {
-    case 8: return attention_wg<8, MB>(P, l, pos, pos_end, wave, W, wait, part);
-    case 16: return attention_wg<16, MB>(P, l, pos, pos_end, wave, W, wait, part);
-    case 32: return attention_wg<32, MB>(P, l, pos, pos_end, wave, W, wait, part);
-    case 64: return attention_wg<64, MB>(P, l, pos, pos_end, wave, W, wait, part);
-    default: return attention_wg<128, MB>(P, l, pos, pos_end, wave, W, wait, part);
-  }
-}
 
 // Wave 0, after S1: the workgroup's pair from its eight waves' partials, in
 // wave order (lane k owns dims 2k, 2k+1); then o, or the workgroup's partial
@@ -1175,7 +1164,7 @@ __device__ __forceinline__ void w0_argmax(const Params& P, int i, int cur_col, i
 // A streamer's attention phase: its units (the first one's cached rows are
 // requested before S1a), then S1 and S2 as in every phase.  False if wave 0
 // reported a failed grid barrier.
-template <int MB>
+template <int MB, int HD>
 __device__ __forceinline__ bool streamer_attention(const Params& P, const Launch& A, const PhaseIt& id, const int* si,
                                                    float* aux) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -1185,7 +1174,7 @@ __device__ __forceinline__ bool streamer_attention(const Params& P, const Launch
   };
   const int pos = step_pos(P, A, id.i);
   bool ok;
-  ok = attention_wg_wave<MB>(P, id.l, pos, A.pos_end, wave, wg_per_head(P, pos), wait_s, aux + kAuxPart);
+  ok = attention_wg<HD, MB>(P, id.l, pos, A.pos_end, wave, wg_per_head(P, pos), wait_s, aux + kAuxPart);
   if (!ok) return false;
   wait_vm0();   // this wave's stores are complete before wave 0 arrives at the grid barrier
   __syncthreads();   // S1
@@ -1198,6 +1187,7 @@ __device__ __forceinline__ bool streamer_attention(const Params& P, const Launch
 // units (zero-reading units pad it), so unit k of each group always sits in
 // register slot k: the steps below are unrolled over the slots and never
 // copy a register that a load is still filling.
+template <int HD>
 __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, int g0, int g1, const int* tab,
                                               float* xs, float* out, const float* gs, float* red, const int* si,
                                               float* aux) {
@@ -1212,7 +1202,7 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
   for (; id.g < g1; phase_next(P, A, id)) {
     if (id.ph == -2) continue;
     if (id.ph == PH_ATTN) {
-      if (!streamer_attention<1>(P, A, id, si, aux)) break;
+      if (!streamer_attention<1, HD>(P, A, id, si, aux)) break;
       continue;
     }
     __syncthreads();   // S1a
@@ -1268,7 +1258,7 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
 // 8..15 repeat sequences 0..7 and columns of absent sequences hold stale
 // inputs; neither is published.  A 16-row group's fp32 accumulator goes into
 // LDS (ds_add_f32, per sequence) when the group or the streamer's range ends.
-template <int MB>
+template <int MB, int HD>
 __device__ __forceinline__ void streamer_tiles(const Params& P, const Launch& A, int g0, int g1, const int* tab,
                                                float* xs, float* out, float* slot, const float* gs, float* red,
                                                const int* si, float* aux) {
@@ -1285,7 +1275,7 @@ __device__ __forceinline__ void streamer_tiles(const Params& P, const Launch& A,
   for (; id.g < g1; phase_next(P, A, id)) {
     if (id.ph == -2) continue;
     if (id.ph == PH_ATTN) {
-      if (!streamer_attention<MB>(P, A, id, si, aux)) break;
+      if (!streamer_attention<MB, HD>(P, A, id, si, aux)) break;
       continue;
     }
     __syncthreads();   // S1a
@@ -1337,7 +1327,7 @@ __device__ __forceinline__ void streamer_tiles(const Params& P, const Launch& A,
   wait_vm0();   // the zero-filled loads past the stream's end
 }
 
-template <int MB>
+template <int MB, int HD>
 __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   using M = Lds<MB>;
   extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -1369,8 +1359,8 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   wait_lgkm0();
   __syncthreads();   // every streamer's tables are in LDS
   if (wave > 0) {
-    if constexpr (MB == 1) streamer_role(P, A, g0, g1, tab, xs, out, gs, red, si, aux);
-    else streamer_tiles<MB>(P, A, g0, g1, tab, xs, out, slots + (wave - 1) * 2 * M::SlotN, gs, red, si, aux);
+    if constexpr (MB == 1) streamer_role<HD>(P, A, g0, g1, tab, xs, out, gs, red, si, aux);
+    else streamer_tiles<MB, HD>(P, A, g0, g1, tab, xs, out, slots + (wave - 1) * 2 * M::SlotN, gs, red, si, aux);
     return;
   }
   if constexpr (MB > 1) {
@@ -1437,7 +1427,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
         __syncthreads();   // S1a
         return r;
       };
-      ok = attention_wg_wave<MB>(P, id.l, pos, A.pos_end, 0, wg_per_head(P, pos), wait_attn, aux + kAuxPart);
+      ok = attention_wg<HD, MB>(P, id.l, pos, A.pos_end, 0, wg_per_head(P, pos), wait_attn, aux + kAuxPart);
       wait_vm0();   // this wave's stores are complete before the next arrive
       first = false;
       if (!ok) return;
@@ -1555,44 +1545,71 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   wait_vm0();
 }
 
-extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident(const Params* __restrict__ Pp, Launch A) {
-  dec_body<1>(*Pp, A);
-}
-extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident_batch(const Params* __restrict__ Pp, Launch A) {
-  dec_body<kMaxBatch>(*Pp, A);
-}
+// One kernel per head dimension (the attention code is specialised for it,
+// and a kernel holding one variant is a fraction of the code the instruction
+// cache has to serve): batch 1 and batched, for head_dim 8, 16, 32, 64, 128.
+#define DEC_KERNELS(HD)                                                                                     \
+  extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident_hd##HD(const Params* __restrict__ Pp, \
+                                                                                 Launch A) {                  \
+    dec_body<1, HD>(*Pp, A);                                                                                \
+  }                                                                                                         \
+  extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident_batch_hd##HD(                         \
+      const Params* __restrict__ Pp, Launch A) {                                                            \
+    dec_body<kMaxBatch, HD>(*Pp, A);                                                                        \
+  }
+DEC_KERNELS(8)
+DEC_KERNELS(16)
+DEC_KERNELS(32)
+DEC_KERNELS(64)
+DEC_KERNELS(128)
+#undef DEC_KERNELS
 
 namespace {
-const void* kernel_for(int batch) {
-  return batch > 1 ? (const void*)dec_resident_batch : (const void*)dec_resident;
+// The kernel for a batch size and head dimension; nullptr for an unsupported head dimension.
+const void* kernel_for(int batch, int hd) {
+  const bool b = batch > 1;
+  switch (hd) {
+    case 8: return b ? (const void*)dec_resident_batch_hd8 : (const void*)dec_resident_hd8;
+    case 16: return b ? (const void*)dec_resident_batch_hd16 : (const void*)dec_resident_hd16;
+    case 32: return b ? (const void*)dec_resident_batch_hd32 : (const void*)dec_resident_hd32;
+    case 64: return b ? (const void*)dec_resident_batch_hd64 : (const void*)dec_resident_hd64;
+    case 128: return b ? (const void*)dec_resident_batch_hd128 : (const void*)dec_resident_hd128;
+    default: return nullptr;
+  }
 }
 }  // namespace
 
 int kernel_prepare() {
-  hipError_t e = hipFuncSetAttribute((const void*)dec_resident, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-  if (e != hipSuccess) return (int)e;
-  return (int)hipFuncSetAttribute((const void*)dec_resident_batch, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  kLdsBytes);
+  for (int hd = 8; hd <= 128; hd *= 2)
+    for (int batch = 1; batch <= kMaxBatch; batch += kMaxBatch - 1) {
+      const hipError_t e = hipFuncSetAttribute(kernel_for(batch, hd), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+      if (e != hipSuccess) return (int)e;
+    }
+  return (int)hipSuccess;
 }
 
-int kernel_blocks_per_cu(int batch, int* out) {
-  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(out, kernel_for(batch), kThreads, kLdsBytes);
+int kernel_blocks_per_cu(int batch, int hd, int* out) {
+  const void* k = kernel_for(batch, hd);
+  if (!k) return (int)hipErrorInvalidValue;
+  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(out, k, kThreads, kLdsBytes);
 }
 
-int kernel_launch_resident(const Params* P, const Launch& A, int grid, int batch, void* stream) {
+int kernel_launch_resident(const Params* P, const Launch& A, int grid, int batch, int hd, void* stream) {
+  const void* k = kernel_for(batch, hd);
+  if (!k) return (int)hipErrorInvalidValue;
   const Params* p = P;
   Launch a = A;
   void* args[] = {&p, &a};
-  return (int)hipLaunchCooperativeKernel(kernel_for(batch), dim3(grid), dim3(kThreads), args, kLdsBytes,
-                                         static_cast<hipStream_t>(stream));
+  return (int)hipLaunchCooperativeKernel(k, dim3(grid), dim3(kThreads), args, kLdsBytes, static_cast<hipStream_t>(stream));
 }
 
-int kernel_launch_plain(const Params* P, const Launch& A, int grid, int batch, void* stream) {
-  if (batch > 1)
-    hipLaunchKernelGGL(dec_resident_batch, dim3(grid), dim3(kThreads), kLdsBytes, static_cast<hipStream_t>(stream), P, A);
-  else
-    hipLaunchKernelGGL(dec_resident, dim3(grid), dim3(kThreads), kLdsBytes, static_cast<hipStream_t>(stream), P, A);
-  return (int)hipGetLastError();
+int kernel_launch_plain(const Params* P, const Launch& A, int grid, int batch, int hd, void* stream) {
+  const void* k = kernel_for(batch, hd);
+  if (!k) return (int)hipErrorInvalidValue;
+  const Params* p = P;
+  Launch a = A;
+  void* args[] = {&p, &a};
+  return (int)hipLaunchKernel(k, dim3(grid), dim3(kThreads), args, kLdsBytes, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace decmono
