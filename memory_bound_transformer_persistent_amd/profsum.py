@@ -71,19 +71,22 @@ def trace_summary(d):
             dec = split_decode(v)
             if dec:
                 s = _stats(dec)
-                lines.append(f"{DECODE_KERNEL} single-token decode launches: n={s['n']} mean {s['mean'] / 1e3:.1f} us, "
+                lines.append(f"{k} single-token decode launches: n={s['n']} mean {s['mean'] / 1e3:.1f} us, "
                              f"median {s['median'] / 1e3:.1f} us, min {s['min'] / 1e3:.1f} us, max {s['max'] / 1e3:.1f} us")
     return "\n".join(lines)
 
 
-def counter_values(d, kernel=DECODE_KERNEL):
-    """{counter: [value per dispatch]} for dispatches of `kernel`, plus their durations (ns)."""
+def counter_values(d, kernel=DECODE_KERNEL, names=None):
+    """{counter: [value per dispatch]} for dispatches of `kernel` (a name substring),
+    plus their durations (ns); the matching kernel names are added to `names`."""
     rows = _rows(d, "counter_collection.csv")
     per = {}
     dur = {}
     for r in rows:
         if kernel not in _name(r):
             continue
+        if names is not None:
+            names.add(_name(r))
         key = r.get("Dispatch_Id") or r.get("Correlation_Id")
         c = r.get("Counter_Name")
         per.setdefault(c, {}).setdefault(key, 0.0)
@@ -93,9 +96,9 @@ def counter_values(d, kernel=DECODE_KERNEL):
     return per, dur
 
 
-def decode_counter(d, counter, kernel=DECODE_KERNEL):
+def decode_counter(d, counter, kernel=DECODE_KERNEL, names=None):
     """Median of `counter` over the single-token decode dispatches of `kernel`."""
-    per, dur = counter_values(d, kernel)
+    per, dur = counter_values(d, kernel, names)
     vals = per.get(counter, {})
     if not vals:
         raise SystemExit(f"no {counter} values for {kernel} under {d}")
@@ -122,7 +125,8 @@ def largest_counter(d, counter):
 
 
 def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes, kernel_src, workload="dense2b"):
-    f_kib, nf = decode_counter(fetch_dir, "FETCH_SIZE")
+    names = set()
+    f_kib, nf = decode_counter(fetch_dir, "FETCH_SIZE", names=names)
     w_kib, nw = decode_counter(write_dir, "WRITE_SIZE")
     cf_kib, cname = largest_counter(cfetch_dir, "FETCH_SIZE")
     cw_kib, _ = largest_counter(cwrite_dir, "WRITE_SIZE")
@@ -131,7 +135,7 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes, kernel_src
     hbm = f_kib * 1024.0 * kf + w_kib * 1024.0 * kw
     sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
     return "\n".join([
-        f"kernel = {DECODE_KERNEL}",
+        f"kernel = {', '.join(sorted(names))}",
         f"workload = {workload}",
         f"kernel_sha = {sha}",
         f"decode_dispatches_fetch = {nf}",
