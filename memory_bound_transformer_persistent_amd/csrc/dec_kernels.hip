@@ -681,6 +681,31 @@ __device__ __forceinline__ void w0_dma_vec(void* dst, const void* src, int n, in
   }
 }
 
+// Batched kernel: does phase id take its raw input vectors by LDS DMA (all
+// but the attention, the argmax and layer 0's embedded QKV input)?
+__device__ __forceinline__ bool dma_input(const PhaseIt& id) {
+  return id.ph == PH_GU || id.ph == PH_LM || id.ph == PH_DOWN || id.ph == PH_O || (id.ph == PH_QKV && id.l > 0);
+}
+// Batched kernel, wave w of the workgroup: its share (1 KB chunks w, w + 8,
+// ... over every sequence's vector) of phase id's raw input into LDS: the
+// fp32 residual vectors into the stage of the normed phases, the fp16 SwiGLU
+// or attention outputs into the input region.  Issues only; the caller waits.
+template <int MB>
+__device__ __forceinline__ void dma_input_share(const Params& P, const PhaseIt& id, float* xs, int w) {
+  const int lane = threadIdx.x & 63;
+  const bool normed = id.ph != PH_DOWN && id.ph != PH_O;
+  const int n = normed ? P.d : (id.ph == PH_DOWN ? P.F : P.q), esize = normed ? 4 : 2;
+  const int span_bytes = gemv_span(n) * esize, nch = span_bytes >> 10;
+  char* base = normed ? reinterpret_cast<char*>(xs + kMaxBatch * gemv_span(P.d) / 2) : reinterpret_cast<char*>(xs);
+  for (int k = w; k < P.B * nch; k += kWaves) {
+    const int b = k / nch, c = k - b * nch;
+    const void* src = normed ? (const void*)(P.x + (size_t)b * P.d)
+                             : (const void*)((id.ph == PH_DOWN ? P.act16 + (size_t)b * P.F : P.att_o16 + (size_t)b * P.q));
+    const rsrc_t r = make_rsrc(src, (uint32_t)(n * esize));
+    dma16_coh(r, base + (size_t)b * span_bytes + 1024 * c, (uint32_t)(1024 * c + 16 * lane));
+  }
+}
+
 // MB == 1, all waves: xs[0..n) *= gs[0..n); red[wave] <- this wave's share of sum(x^2).
 __device__ __forceinline__ void apply_gains(float* xs, const float* gs, int n, float* red) {
   float ss = 0.f;
@@ -1285,6 +1310,11 @@ __device__ __forceinline__ void streamer_tiles(const Params& P, const Launch& A,
     }
     __syncthreads();   // S1a
     if (si[12] == 0) break;
+    if (dma_input(id)) {
+      dma_input_share<MB>(P, id, xs, rfl((int)(threadIdx.x >> 6)));
+      wait_vm0();
+    }
+    __syncthreads();   // S1b: the phase input is in LDS
     if (norm_phase(id))
       apply_gains_batch(reinterpret_cast<_Float16*>(xs), xs + kMaxBatch * gemv_span(P.d) / 2, gs, P.d, B, red);
     __syncthreads();   // S1
@@ -1456,36 +1486,17 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       have_tok = false;
     } else if (id.ph == PH_QKV || id.ph == PH_GU || id.ph == PH_LM) {
       ok = wait();
-      if (ok) {
-        if constexpr (MB == 1) {
-          w0_dma_vec(xs, P.x, P.d, 4, true);
-        } else {
-          for (int b = 0; b < B; ++b) w0_dma_vec(stage + (size_t)b * gemv_span(P.d), P.x + (size_t)b * P.d, P.d, 4, true);
-        }
-      }
+      if constexpr (MB == 1)
+        if (ok) w0_dma_vec(xs, P.x, P.d, 4, true);
     } else if (id.ph == PH_DOWN) {
       ok = wait();
-      if (ok) {
-        if constexpr (MB == 1) {
-          w0_dma_vec(xs, P.act, P.F, 4, true);
-        } else {
-          _Float16* xh = reinterpret_cast<_Float16*>(xs);
-          for (int b = 0; b < B; ++b)
-            w0_dma_vec(xh + (size_t)b * gemv_span(P.F), P.act16 + (size_t)b * P.F, P.F, 2, true);
-        }
-      }
+      if constexpr (MB == 1)
+        if (ok) w0_dma_vec(xs, P.act, P.F, 4, true);
     } else if (id.ph == PH_O) {
       ok = wait();
-      if (ok) {
-        // the attention output of every head, merged in the attention phase
-        if constexpr (MB == 1) {
-          w0_dma_vec(xs, P.att_o, P.q, 4, true);
-        } else {
-          _Float16* xh = reinterpret_cast<_Float16*>(xs);
-          for (int b = 0; b < B; ++b)
-            w0_dma_vec(xh + (size_t)b * gemv_span(P.q), P.att_o16 + (size_t)b * P.q, P.q, 2, true);
-        }
-      }
+      // the attention output of every head, merged in the attention phase
+      if constexpr (MB == 1)
+        if (ok) w0_dma_vec(xs, P.att_o, P.q, 4, true);
     } else {
       ok = wait();
       if (ok) {
@@ -1494,11 +1505,19 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       }
     }
     if (id.ph != PH_ATTN) {
-      wait_vm0();   // the phase input has landed in LDS
+      wait_vm0();   // batch 1: the phase input has landed in LDS
       if (lane == 0) si[12] = ok ? 1 : 0;
       first = false;
       __syncthreads();   // S1a
       if (!ok) return;
+      if constexpr (MB > 1) {
+        // batched: every wave lands its share of the inputs of all sequences
+        if (dma_input(id)) {
+          dma_input_share<MB>(P, id, xs, 0);
+          wait_vm0();
+        }
+        __syncthreads();   // S1b
+      }
     }
     if (norm_phase(id)) {
       if constexpr (MB == 1) apply_gains(xs, gs, P.d, red);
