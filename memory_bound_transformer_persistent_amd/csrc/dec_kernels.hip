@@ -854,6 +854,7 @@ __device__ __forceinline__ bool attend_chunk(const Params& P, rsrc_t rk, rsrc_t 
   const int lane = threadIdx.x & 63;
   const int sub = lane % LP, pidx = lane / LP;
   f32x4 qa = {0.f, 0.f, 0.f, 0.f}, qb = {0.f, 0.f, 0.f, 0.f};
+  bool failed = false;
   for (int g0 = j0; g0 < j1; g0 += GRP) {
     u32x4 kr[NPASS], vr[NPASS];
     const bool pre = !waited;   // loads issued before the barrier skip the row at pos
@@ -866,7 +867,10 @@ __device__ __forceinline__ bool attend_chunk(const Params& P, rsrc_t rk, rsrc_t 
     }
     if (pre) {
       waited = true;
-      if (!wait()) return false;
+      // no early return with this group's loads in flight: on the path out,
+      // the compiler would have to assume them pending in the weight loop and
+      // guard its registers with a full vmcnt(0) wait in every group
+      if (!wait()) failed = true;
       if (g0 + GRP > pos) {
         // rows of this step's positions, written before the barrier
 #pragma unroll
@@ -916,7 +920,7 @@ __device__ __forceinline__ bool attend_chunk(const Params& P, rsrc_t rk, rsrc_t 
 #pragma unroll
   for (int q = 0; q < 8; ++q)
     for (int off = LP; off < 64; off <<= 1) acc[q] += __shfl_xor(acc[q], off, 64);
-  return true;
+  return !failed;
 }
 
 // Attention by workgroups (the handle guarantees no more (column, head)
