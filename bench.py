@@ -12,7 +12,9 @@ tokens_per_s_per_request the rate each sequence sees.
 Prints one JSON line.  The roofline object prices the resident decode kernel
 against MI355X's 8 TB/s HBM peak with ALGORITHMIC bytes per launch: every
 weight byte once, one embedding row, the KV-cache rows attention reads at
-that position and the rows it appends.  The cpu_baseline object times the
+that position and the rows it appends.  stream_ceiling is the measured read
+rate of a plain 16-byte non-temporal stream over 2 GiB on the same device
+(dec_stream_ceiling) and the decode rate as a fraction of it.  The cpu_baseline object times the
 CPU oracle (test infrastructure) on a bounded sample of the same workload.
 """
 import argparse
@@ -222,6 +224,10 @@ def main():
                     "note": "2B fp16, batch 1, 8 GPUs each: other hardware, context only"},
     }
     dec.close()
+    # the plain-stream read rate of this device, the practical ceiling under the 8 TB/s peak
+    ceiling = B.stream_ceiling(1 << 31, 5)
+    out["stream_ceiling"] = {"GBps": round(ceiling, 1), "bytes": 1 << 31, "reps": 5, "kernel": "dec_stream_read",
+                             "decode_frac": round(achieved / ceiling, 4)}
     if not args.no_cpu_baseline:
         print("# running the CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(s, tensors, 16, args.cpu_steps)

@@ -276,6 +276,27 @@ int dec_read_trace(dec_handle* h, uint64_t* host, int32_t* out_grid, int32_t* ou
 void dec_free(dec_handle* h);
 
 /*
+ * Measurement aid: the sustained HBM read rate of a plain stream on this
+ * device, the ceiling the decode kernel's weight stream is compared with
+ * (the bandwidth bound of page *標準GPUによるリアルタイムLLM推論：リクエストあ
+ * たり3,000トークン/秒*, section *GPU推論の速度制限要因：メモリ帯域幅*, prices
+ * every byte at the device's bandwidth).  One 512-thread workgroup per
+ * compute unit; each wave reads its own contiguous share of the buffer's
+ * 1 KB blocks with 16-byte non-temporal loads, eight blocks in flight (the
+ * access pattern of the decode kernel's weight streams).
+ *   device:   HIP device ordinal.
+ *   bytes:    buffer size, at least 64 MiB and at most 64 GiB; rounded down
+ *             to a multiple of 1 MiB.  Allocated on the device, filled, read
+ *             once untimed, then `reps` times timed with HIP events, freed.
+ *   reps:     1..100.
+ *   out_gbps: bytes * reps / elapsed / 1e9.
+ * Synchronous.  Returns DEC_ERR_INVALID_ARG for bad arguments, DEC_ERR_OOM if
+ * the buffer cannot be allocated, DEC_ERR_DEVICE for another HIP error.  It
+ * shares the device with any running decode work, so call it when none runs.
+ */
+int dec_stream_ceiling(int32_t device, uint64_t bytes, int32_t reps, double* out_gbps);
+
+/*
  * Last error text of the handle, or of the calling thread's last failed
  * handle-less call (dec_init, dec_check_desc, ...) when h == NULL.  Never NULL.
  */

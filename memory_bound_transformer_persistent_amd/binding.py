@@ -94,6 +94,7 @@ SIGNATURES = {
     "dec_free": (None, [ctypes.c_void_p]),
     "dec_last_error": (ctypes.c_char_p, [ctypes.c_void_p]),
     "dec_read_trace": (ctypes.c_int, [ctypes.c_void_p, _P(ctypes.c_uint64), _i32p, _i32p, _P(ctypes.c_double)]),
+    "dec_stream_ceiling": (ctypes.c_int, [ctypes.c_int32, ctypes.c_uint64, ctypes.c_int32, _P(ctypes.c_double)]),
     "dec_packed_bytes": (ctypes.c_int, [_P(ModelDesc), _P(ctypes.c_size_t)]),
     "dec_pack": (ctypes.c_int, [_P(ModelDesc), _P(_u16p), ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t]),
 }
@@ -162,6 +163,13 @@ def pack(desc, tensors):
     out = np.zeros(packed_bytes(desc) // 2, dtype=np.uint16)
     _check(load().dec_pack(ctypes.byref(desc), ptrs, len(arrs), out.ctypes.data, out.nbytes))
     return out
+
+
+def stream_ceiling(nbytes=1 << 32, reps=5, device=0):
+    """Sustained HBM read rate (GB/s) of a plain 16-byte non-temporal stream (dec_stream_ceiling)."""
+    g = ctypes.c_double()
+    _check(load().dec_stream_ceiling(device, nbytes, reps, ctypes.byref(g)))
+    return g.value
 
 
 def weights_file_check(path):

@@ -948,6 +948,49 @@ int dec_read_kv(dec_handle* h, int32_t layer, int32_t seq, int32_t n_pos, uint16
   return DEC_OK;
 }
 
+int dec_stream_ceiling(int32_t device, uint64_t bytes, int32_t reps, double* out_gbps) {
+  if (!out_gbps) return fail(nullptr, DEC_ERR_INVALID_ARG, "out_gbps is NULL");
+  const uint64_t MiB = 1ull << 20;
+  if (bytes < 64 * MiB || bytes > 64 * 1024 * MiB) return fail(nullptr, DEC_ERR_INVALID_ARG, "bytes must be in [64 MiB, 64 GiB]");
+  if (reps < 1 || reps > 100) return fail(nullptr, DEC_ERR_INVALID_ARG, "reps must be in [1, 100]");
+  bytes = bytes / MiB * MiB;
+  if (hipSetDevice(device) != hipSuccess) return fail(nullptr, DEC_ERR_NO_DEVICE, "hipSetDevice(%d) failed", device);
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1)
+    return fail(nullptr, DEC_ERR_DEVICE, "compute unit count unavailable");
+  const int grid = cus;   // one workgroup per compute unit, as the decode kernel
+  void* buf = nullptr;
+  uint32_t* out = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  int rc = DEC_OK;
+  float ms = 0.f;
+  if (hipMalloc(&buf, bytes) != hipSuccess) {
+    rc = fail(nullptr, DEC_ERR_OOM, "hipMalloc(%llu) failed", (unsigned long long)bytes);
+  } else if (hipMalloc(reinterpret_cast<void**>(&out), (size_t)grid * kThreads * 4) != hipSuccess) {
+    rc = fail(nullptr, DEC_ERR_OOM, "hipMalloc(out) failed");
+  } else {
+    hipError_t e = hipMemset(buf, 0x3c, bytes);
+    if (e == hipSuccess) e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    if (e == hipSuccess) e = (hipError_t)kernel_stream_read(buf, bytes / 16, out, grid);   // untimed pass
+    if (e == hipSuccess) e = hipEventRecord(e0, nullptr);
+    for (int r = 0; r < reps && e == hipSuccess; ++r) e = (hipError_t)kernel_stream_read(buf, bytes / 16, out, grid);
+    if (e == hipSuccess) e = hipEventRecord(e1, nullptr);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+    if (e != hipSuccess) rc = fail(nullptr, DEC_ERR_DEVICE, "stream ceiling run failed: %s", hipGetErrorString(e));
+  }
+  if (e0) hipEventDestroy(e0);
+  if (e1) hipEventDestroy(e1);
+  if (out) hipFree(out);
+  if (buf) hipFree(buf);
+  if (rc == DEC_OK) {
+    if (ms <= 0.f) return fail(nullptr, DEC_ERR_DEVICE, "no elapsed time measured");
+    *out_gbps = (double)bytes * reps / (ms * 1e-3) / 1e9;
+  }
+  return rc;
+}
+
 int dec_read_trace(dec_handle* h, uint64_t* host, int32_t* out_grid, int32_t* out_stride, double* out_hz) {
   if (!h) return fail(nullptr, DEC_ERR_INVALID_ARG, "handle is NULL");
   if (out_grid) *out_grid = h->grid;

@@ -150,5 +150,8 @@ int kernel_prepare();                                            // raise the dy
 int kernel_blocks_per_cu(int batch, int hd, int* out);           // co-resident workgroups per CU
 int kernel_launch_resident(const Params* P, const Launch& A, int grid, int batch, int hd, void* stream);  // cooperative
 int kernel_launch_plain(const Params* P, const Launch& A, int grid, int batch, int hd, void* stream);     // ordinary
+// Stream-ceiling read of n16 16-byte words at src on the null stream; out
+// holds grid * kThreads words.
+int kernel_stream_read(const void* src, uint64_t n16, uint32_t* out, int grid);
 
 }  // namespace decmono

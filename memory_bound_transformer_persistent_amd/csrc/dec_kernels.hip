@@ -1607,6 +1607,34 @@ const void* kernel_for(int batch, int hd) {
 }
 }  // namespace
 
+// Plain streaming read for the stream ceiling: the buffer's 1 KB blocks are
+// split evenly over the grid's waves, and each wave reads its contiguous
+// range with 16-byte non-temporal loads, eight blocks in flight (the access
+// pattern of the decode kernel's weight streams).  Each thread stores the XOR
+// of what it read so no load is dead.  n16 is a multiple of 64.
+extern "C" __global__ __launch_bounds__(kThreads) void dec_stream_read(const u32x4* __restrict__ src, uint64_t n16,
+                                                                       uint32_t* __restrict__ out) {
+  const uint64_t nw = (uint64_t)gridDim.x * kWaves, nblk = n16 / 64;
+  const uint64_t w = (uint64_t)blockIdx.x * kWaves + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const uint64_t b1 = (w + 1) * nblk / nw;
+  uint64_t b = w * nblk / nw;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; b + 8 <= b1; b += 8) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = __builtin_nontemporal_load(src + (b + k) * 64 + lane);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= v[k];
+  }
+  for (; b < b1; ++b) acc ^= __builtin_nontemporal_load(src + b * 64 + lane);
+  out[(uint64_t)blockIdx.x * kThreads + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+int kernel_stream_read(const void* src, uint64_t n16, uint32_t* out, int grid) {
+  hipLaunchKernelGGL(dec_stream_read, dim3(grid), dim3(kThreads), 0, 0, static_cast<const u32x4*>(src), n16, out);
+  return (int)hipGetLastError();
+}
+
 int kernel_prepare() {
   for (int hd = 8; hd <= 128; hd *= 2)
     for (int batch = 1; batch <= kMaxBatch; batch += kMaxBatch - 1) {

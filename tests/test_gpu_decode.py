@@ -632,3 +632,10 @@ def test_grid_smaller_than_head_pairs_is_unsupported(stream):
     assert ei.value.code == B.DEC_ERR_UNSUPPORTED
     with make(s, t, stream, batch=4, grid=16) as d:   # 16 pairs: allowed
         d.prefill(synth.make_prompt(s.vocab, 5, batch=4, seed=46))
+
+
+@pytest.mark.gpu
+def test_stream_ceiling_is_a_plausible_hbm_rate():
+    """The plain-stream probe reads 1 GiB three times at a rate an MI355X can reach (below its 8 TB/s peak)."""
+    g = B.stream_ceiling(1 << 30, 3)
+    assert 1000.0 < g < 8500.0, g

@@ -254,6 +254,15 @@ def test_null_handle_calls(lib):
     assert isinstance(lib.dec_last_error(None), bytes)
 
 
+def test_stream_ceiling_argument_checks(lib):
+    """dec_stream_ceiling rejects bad arguments before it touches a device."""
+    g = ctypes.c_double()
+    assert lib.dec_stream_ceiling(0, 1 << 20, 3, ctypes.byref(g)) == B.DEC_ERR_INVALID_ARG      # below 64 MiB
+    assert lib.dec_stream_ceiling(0, 1 << 40, 3, ctypes.byref(g)) == B.DEC_ERR_INVALID_ARG      # above 64 GiB
+    assert lib.dec_stream_ceiling(0, 1 << 30, 0, ctypes.byref(g)) == B.DEC_ERR_INVALID_ARG      # reps
+    assert lib.dec_stream_ceiling(0, 1 << 30, 3, None) == B.DEC_ERR_INVALID_ARG
+
+
 def test_library_missing_fails_loudly(monkeypatch):
     monkeypatch.setattr(B, "_lib", None)
     monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/libdecmono.so")
