@@ -257,7 +257,17 @@ __device__ __forceinline__ GemvWork work_of(const Params& P, int ph, int l) {
     case PH_LM: g.W = P.w + P.off_lm; g.rows = P.Vlm; g.K = P.d; npairs = P.Vlm / 2; break;
     default: return g;
   }
-  split(npairs, blockIdx.x, gridDim.x, g.p0, g.p1);
+  // batch 1 with few heads (at most 1/32 of the grid, e.g. one lane of a
+  // tensor-parallel split): the workgroups that take attention (the first H)
+  // get no QKV rows, so they reach the attention phase early and its K/V
+  // history loads run while the others finish the QKV GEMV.  With more heads
+  // the others' extra QKV rows cost more than this gains.
+  const int G = gridDim.x, skip = (ph == PH_QKV && P.B == 1 && !P.cols_pos && P.H <= G / 32) ? P.H : 0;
+  if ((int)blockIdx.x < skip) {
+    g.p0 = g.p1 = 0;
+  } else {
+    split(npairs, blockIdx.x - skip, G - skip, g.p0, g.p1);
+  }
   return g;
 }
 
