@@ -68,7 +68,7 @@ static_assert(kAuxPart + kWaves * (128 + 2) <= kAuxFloats, "aux LDS");
 
 // LDS map (floats) for a kernel built for up to MB sequences:
 // input region | out | xown | red | scales | si | aux | gains | phase tables |
-// partial-output slots | combine plans.
+// partial-output slots | combine plans | warm-up sink.
 // MB == 1: the input region is the fp32 vector xs.  MB > 1: it holds the fp16
 // inputs of every sequence side by side (stride = the phase's padded row
 // length) and, for the normed phases, the fp32 residual vectors they come
@@ -84,10 +84,12 @@ struct Lds {
   // 16-row output groups it shares with other streamers
   static constexpr int SlotN = MB == 1 ? 0 : kTileRows * MB;
   static constexpr int Slot = Tab + kStreamers * 6 * kTabStride, Plan = Slot + kStreamers * 2 * SlotN;
-  static constexpr int End = Plan + (MB == 1 ? 0 : 6 * kPlanInts);
+  // batch 1: 1 KB that the attention-phase cache warm-up DMAs land in (never read)
+  static constexpr int Sink = Plan + (MB == 1 ? 0 : 6 * kPlanInts);
+  static constexpr int End = Sink + (MB == 1 ? 256 : 0);
   static_assert(End * 4 <= kLdsBytes, "LDS map exceeds the allocation");
   static_assert(MB == 1 || 3 * kMaxBatch * kBatchSpanD / 2 <= Region, "staged fp32 inputs do not fit");
-  static_assert(Gain % 4 == 0 && Region % 4 == 0, "16-byte alignment");
+  static_assert(Gain % 4 == 0 && Region % 4 == 0 && Sink % 4 == 0, "16-byte alignment");
 };
 
 constexpr int kWaitVm0 = 0x0F70;             // s_waitcnt vmcnt(0), expcnt/lgkmcnt untouched
@@ -1208,15 +1210,33 @@ __device__ __forceinline__ void w0_argmax(const Params& P, int i, int cur_col, i
 // A streamer's attention phase: its units (the first one's cached rows are
 // requested before S1a), then S1 and S2 as in every phase.  False if wave 0
 // reported a failed grid barrier.
+// Cache warm-up in the attention gap: a streamer of a workgroup without a
+// head requests the first GU row pair of its share (10 KB) with ordinary,
+// cache-allocating loads into an LDS sink.  HBM is otherwise idle while the
+// heads' workgroups compute attention, and the GU phase's own streaming loads
+// of those blocks then hit the device-side cache.  More than one row pair
+// per streamer delays these workgroups' arrival at the next barrier.
+__device__ __forceinline__ void warm_gu(const Params& P, const int* tab, int l, float* sink) {
+  const int lane = threadIdx.x & 63;
+  const int* e = tab + PH_GU * kTabStride;
+  if (rfl(e[T_LEFT]) <= 0) return;
+  const rsrc_t r = make_rsrc(gemv_base(P, PH_GU, rfl(l)), (uint32_t)rfl(e[T_NBYTES]));
+  const uint32_t off = (uint32_t)rfl(e[T_OFF]), rowb = (uint32_t)rfl(e[T_ROWB]);
+  for (uint32_t k = 0; k < 2 * rowb / 1024u; ++k) dma16_ld(r, sink, off + 1024u * k + 16u * lane);
+}
+
 template <int MB, int HD>
 __device__ __forceinline__ bool streamer_attention(const Params& P, const Launch& A, const PhaseIt& id, const int* si,
-                                                   float* aux) {
+                                                   float* aux, const int* tab = nullptr, float* sink = nullptr) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   auto wait_s = [&]() {
     __syncthreads();   // S1a
     return si[12] != 0;
   };
   const int pos = step_pos(P, A, id.i);
+  // (not with few heads: their workgroups skip the QKV rows and the gap is short)
+  if constexpr (MB == 1)
+    if (P.H > (int)gridDim.x / 32 && (int)blockIdx.x / wg_per_head(P, pos) >= P.H) warm_gu(P, tab, id.l, sink);
   bool ok;
   ok = attention_wg<HD, MB>(P, id.l, pos, A.pos_end, wave, wg_per_head(P, pos), wait_s, aux + kAuxPart);
   if (!ok) return false;
@@ -1234,7 +1254,7 @@ __device__ __forceinline__ bool streamer_attention(const Params& P, const Launch
 template <int HD>
 __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, int g0, int g1, const int* tab,
                                               float* xs, float* out, const float* gs, float* red, const int* si,
-                                              float* aux) {
+                                              float* aux, float* sink) {
   const int lane = threadIdx.x & 63;
   const uint32_t lane16 = (uint32_t)lane * 16u;
   Cursor cu;
@@ -1246,7 +1266,7 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
   for (; id.g < g1; phase_next(P, A, id)) {
     if (id.ph == -2) continue;
     if (id.ph == PH_ATTN) {
-      if (!streamer_attention<1, HD>(P, A, id, si, aux)) break;
+      if (!streamer_attention<1, HD>(P, A, id, si, aux, tab, sink)) break;
       continue;
     }
     __syncthreads();   // S1a
@@ -1408,7 +1428,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   wait_lgkm0();
   __syncthreads();   // every streamer's tables are in LDS
   if (wave > 0) {
-    if constexpr (MB == 1) streamer_role<HD>(P, A, g0, g1, tab, xs, out, gs, red, si, aux);
+    if constexpr (MB == 1) streamer_role<HD>(P, A, g0, g1, tab, xs, out, gs, red, si, aux, smem + M::Sink);
     else streamer_tiles<MB, HD>(P, A, g0, g1, tab, xs, out, slots + (wave - 1) * 2 * M::SlotN, gs, red, si, aux);
     return;
   }
