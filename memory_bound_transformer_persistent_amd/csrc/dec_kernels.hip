@@ -140,32 +140,43 @@ __device__ __forceinline__ f32x4 ldg4(const float* p) { return *(gf32x4*)p; }
 __device__ __forceinline__ f32x4 ld_coh4(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxSc1));
 }
+// Device-coherent (sc1) loads and stores of data other workgroups exchange,
+// all through the global address space.  A flat access would also count in
+// lgkmcnt, so every later scalar load or LDS read that waits for lgkmcnt
+// would first wait for the store to be acknowledged.  A global access counts
+// in vmcnt only, so several can be in flight and waited for in order.
+typedef __attribute__((address_space(1))) float gfloat_rw;
+typedef __attribute__((address_space(1))) int gint_rw;
+typedef __attribute__((address_space(1))) uint32_t guint;
+typedef __attribute__((address_space(1))) uint16_t gushort;
 __device__ __forceinline__ float ld_coh(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((gfloat_rw*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int ld_coh(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((gint_rw*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t ld_coh(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// The same through the global address space: a global (not flat) load, which
-// counts in vmcnt only, so several can be in flight and waited for in order.
-typedef __attribute__((address_space(1))) uint32_t guint;
-__device__ __forceinline__ uint32_t ld_coh_g(const uint32_t* p) {
   return __hip_atomic_load((guint*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_coh(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((gfloat_rw*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_coh(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((gint_rw*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_coh(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((guint*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_coh(uint16_t* p, uint16_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((gushort*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// plain stores through the global address space (results the host reads)
+typedef __attribute__((address_space(1))) uint64_t gu64;
+__device__ __forceinline__ void st_g(float* p, float v) { *(gfloat_rw*)p = v; }
+__device__ __forceinline__ void st_g(uint64_t* p, uint64_t v) { *(gu64*)p = v; }
+// relaxed device-scope fetch-add, returning the old value
+__device__ __forceinline__ uint32_t atomic_add_coh(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add((guint*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -634,8 +645,7 @@ __device__ __forceinline__ void w0_arrive(const Params& P, int fenced) {
   wait_vm0();
   if ((threadIdx.x & 63) == 0) {
     if (fenced) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint32_t old = __hip_atomic_fetch_add(P.ctl + kCtlGroup0 + 64 * (blockIdx.x % kGroups), 1u,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = atomic_add_coh(P.ctl + kCtlGroup0 + 64 * (blockIdx.x % kGroups), 1u);
     __asm__ volatile("" ::"v"(old));
   }
   // the atomic has landed before the first poll goes out
@@ -656,14 +666,14 @@ __device__ __forceinline__ bool w0_wait(const Params& P, uint32_t epoch, int fen
   // 0 = released, 1 = a workgroup raised an error, 2 = the watchdog expired
   int why = 0;
   while (true) {
-    const uint32_t v = ld_coh_g(w);
+    const uint32_t v = ld_coh(w);
     if (__any(lane == kGroups && v != 0u)) { why = 1; break; }
     if (__all(lane >= ng || (int)(v - target) >= 0)) break;
     if (wall_clock64() - t0 > limit) { why = 2; break; }
   }
   if (why == 2 && lane == 0) {
     uint32_t expected = 0u;
-    __hip_atomic_compare_exchange_strong(P.ctl + kCtlErr, &expected, (uint32_t)kDevErrTimeout, __ATOMIC_RELAXED,
+    __hip_atomic_compare_exchange_strong((guint*)(P.ctl + kCtlErr), &expected, (uint32_t)kDevErrTimeout, __ATOMIC_RELAXED,
                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const bool ok = why == 0;
@@ -1032,7 +1042,7 @@ __device__ __forceinline__ void w0_merge_wg(const Params& P, int pos, int pos_en
   if (lane == 0) { st_coh(pm, Mx); st_coh(pm + 1, L); }
   wait_vm0();   // the partial is visible before the workgroup counts itself
   uint32_t old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(P.ctl + kCtlHead0 + hb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) old = atomic_add_coh(P.ctl + kCtlHead0 + hb, 1u);
   old = (uint32_t)__builtin_amdgcn_readlane((int)old, 0);
   if (old == (uint32_t)(W - 1)) merge_head<MB>(P, hb, W, o_at);
 }
@@ -1121,7 +1131,7 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l,
         if (b < B) {
           const float v = out[t * MB + b] * scl[b];
           if (v > best[b]) { best[b] = v; bidx[b] = 2 * p0 + t; }
-          if (want_logits) P.logits[(size_t)b * P.Vlm + 2 * p0 + t] = v;
+          if (want_logits) st_g(P.logits + (size_t)b * P.Vlm + 2 * p0 + t, v);
         }
       }
     }
@@ -1441,7 +1451,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   uint64_t* trace = P.trace ? P.trace + (size_t)blockIdx.x * P.trace_stride : nullptr;
   int ev = 0;
   auto stamp = [&]() {
-    if (trace && lane == 0 && ev < P.trace_stride) trace[ev] = wall_clock64();
+    if (trace && lane == 0 && ev < P.trace_stride) st_g(trace + ev, wall_clock64());
     ++ev;
   };
   const int own = kOwnFloats / MB;   // xown floats per sequence
