@@ -182,6 +182,15 @@ def main():
         launch_ms = [starts[i].elapsed_time(ends[i]) for i in range(K)]
         bytes_per_launch = R.mean_step_bytes(s, pos0, K, nb)
     avg_launch_s = float(np.mean(launch_ms)) / 1e3
+    # the timed steps in four consecutive segments (step mode): spread of the
+    # rate within the run (later segments are at longer contexts), from the
+    # same per-launch events
+    segs = None
+    if args.mode == "step" and K >= 8:
+        q = K // 4
+        seg_tps = [q * nb / (starts[i * q].elapsed_time(ends[i * q + q - 1]) / 1e3) for i in range(4)]
+        segs = {"n": 4, "steps_each": q, "min": round(min(seg_tps), 2), "median": round(float(np.median(seg_tps)), 2),
+                "max": round(max(seg_tps), 2)}
     req_tok_s = K / (region_ms / 1e3)          # tokens/s of each sequence
     tok_s = req_tok_s * nb                     # whole-job tokens/s
     achieved = bytes_per_launch / avg_launch_s / 1e9
@@ -214,6 +223,7 @@ def main():
                      "algorithmic_bytes_per_launch": int(bytes_per_launch),
                      "avg_launch_ms": round(avg_launch_s * 1e3, 4)},
         "tokens_per_s_per_request": round(req_tok_s, 2),
+        "segments_tokens_per_s": segs,
         "prefill": {"tokens": w.prompt_len, "sequences": nb, "ms": round(prefill_ms, 3),
                     "mode": "batched, 8 positions per step" if bp else "one position per step"},
         "roofline_tokens_per_s": round(roof_tps * nb, 1),
