@@ -15,6 +15,9 @@ FLAGS = [
     "-Wall", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
     # no packed-fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # 64-byte aligned loop heads: the resident kernel's step rate moved by
+    # about 1% with unrelated code changes until its loops were aligned
+    "-falign-loops=64",
     "-fvisibility=hidden",
 ]
 

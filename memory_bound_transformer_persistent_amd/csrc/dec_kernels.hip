@@ -861,6 +861,10 @@ __device__ __forceinline__ void merge_head(const Params& P, int hb, int C, size_
   }
 }
 
+// Passes of a register group in attend_chunk: each pass gives every lane one
+// 16-byte piece of a K row and of a V row (hd / 8 lanes per position).
+constexpr int kAttnPasses = 8;
+
 // Online-softmax partial of one (column, head) over positions [j0, j1): the
 // running max M, the sum of exp Lsum and the unnormalised sum acc of exp * V
 // (dims 8 sub .. 8 sub + 7, summed over the wave's position groups).  The
@@ -871,7 +875,7 @@ template <int HD, int MB, class Wait>
 __device__ __forceinline__ bool attend_chunk(const Params& P, rsrc_t rk, rsrc_t rv, rsrc_t rq, int j0, int j1, int pos,
                                              bool& waited, Wait&& wait, float& M, float& Lsum, float (&acc)[8]) {
   constexpr int LP = HD / 8, PPW = 64 / LP;
-  constexpr int NPASS = 8;
+  constexpr int NPASS = kAttnPasses;
   constexpr int GRP = PPW * NPASS;       // positions per register group
   const int lane = threadIdx.x & 63;
   const int sub = lane % LP, pidx = lane / LP;
@@ -951,13 +955,23 @@ __device__ __forceinline__ bool attend_chunk(const Params& P, rsrc_t rk, rsrc_t 
 // of the pair's C = 8 W chunks.  The waves' partials meet in LDS and wave 0
 // merges them after S1.  With W == 1 that is o.  Otherwise the workgroup's
 // partial goes to memory and the last of the pair's W workgroups (arrival
-// counter) merges the W partials.  W grows with the context so that a wave
-// covers about kWavePositions positions.
-constexpr int kWavePositions = 64;
+// counter) merges the W partials.
+//
+// A wave reads its positions in register groups (attend_chunk: 32
+// positions at head dim 128), and the attention phase lasts about as many
+// group times as the busiest wave has groups; a split over W > 1 workgroups
+// adds a merge through memory that costs about one group.  So: one
+// workgroup (at most two groups per wave) up to 16 groups of positions,
+// beyond that enough workgroups for one group per wave, but at most
+// kMaxWgPerHead: at long contexts the K/V stream is bound by HBM, and more
+// workgroups only add merge work and take workgroups from the GU cache
+// warm-up.
+constexpr int kMaxWgPerHead = 8;
 __device__ __forceinline__ int wg_per_head(const Params& P, int pos) {
   const int HB = P.B * P.H, G = gridDim.x;   // HB <= G (checked when the handle is made)
   const int ctx_max = col_pos(P, pos, P.B - 1) + 1;
-  const int want = (ctx_max + kWaves * kWavePositions - 1) / (kWaves * kWavePositions);
+  const int per_wg = kWaves * (512 / P.hd) * kAttnPasses;   // positions of one group on every wave
+  const int want = ctx_max <= 2 * per_wg ? 1 : min((ctx_max + per_wg - 1) / per_wg, kMaxWgPerHead);
   return max(1, min(min(want, G / HB), kChunkCap));
 }
 
