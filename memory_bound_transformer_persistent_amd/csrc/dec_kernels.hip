@@ -1249,6 +1249,31 @@ __device__ __forceinline__ void warm_gu(const Params& P, const int* tab, int l, 
   for (uint32_t k = 0; k < 2 * rowb / 1024u; ++k) dma16_ld(r, sink, off + 1024u * k + 16u * lane);
 }
 
+// Wave 0 of such a workgroup, once it has arrived at the barrier before O,
+// warms more: for each streamer, the GU blocks just past the row pair the
+// streamer warms itself, up to kW0WarmBlocks of 1 KB, within the streamer's
+// share.  Wave 0 has nothing else in flight there (its first poll simply
+// waits for these loads), so unlike the streamers it can take more without
+// delaying the O phase.  24 blocks per streamer measured best over 128-640
+// positions at d 2560 (16 and 32 were slower; at the shortest contexts the
+// gap is too short for all of them to land).
+constexpr int kW0WarmBlocks = 24;
+__device__ __forceinline__ void w0_warm_gu(const Params& P, const int* tab_all, int l, float* sink) {
+  const int lane = threadIdx.x & 63;
+  const int* e0 = tab_all + PH_GU * kTabStride;
+  const rsrc_t r = make_rsrc(gemv_base(P, PH_GU, rfl(l)), (uint32_t)rfl(e0[T_NBYTES]));
+  for (int s = 0; s < kStreamers; ++s) {
+    const int* e = tab_all + s * 6 * kTabStride + PH_GU * kTabStride;
+    const uint32_t left = (uint32_t)max(rfl(e[T_LEFT]), 0);
+    const uint32_t off = (uint32_t)rfl(e[T_OFF]), rowb = (uint32_t)rfl(e[T_ROWB]);
+    const uint32_t end = off + 2048u * left;   // the streamer's units are about 2 KB each
+    for (uint32_t k = 0; k < (uint32_t)kW0WarmBlocks; ++k) {
+      const uint32_t b = off + 2u * rowb + 1024u * k;
+      if (b + 1024u <= end) dma16_ld(r, sink, b + 16u * lane);
+    }
+  }
+}
+
 template <int MB, int HD>
 __device__ __forceinline__ bool streamer_attention(const Params& P, const Launch& A, const PhaseIt& id, const int* si,
                                                    float* aux, const int* tab = nullptr, float* sink = nullptr) {
@@ -1504,6 +1529,9 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     if (!skip_bar) {
       ++epoch;
       w0_arrive(P, A.fenced);
+      if constexpr (MB == 1)
+        if (id.ph == PH_O && P.H > (int)gridDim.x / 32 && (int)blockIdx.x / wg_per_head(P, pos) >= P.H)
+          w0_warm_gu(P, tab_all, id.l, smem + M::Sink);
     }
     auto wait = [&]() { return skip_bar ? true : w0_wait(P, epoch, A.fenced); };
     // the norm gains do not depend on the barrier: they were prefetched
