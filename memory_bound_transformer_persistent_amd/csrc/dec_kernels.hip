@@ -86,7 +86,7 @@ struct Lds {
   static constexpr int Slot = Tab + kStreamers * 6 * kTabStride, Plan = Slot + kStreamers * 2 * SlotN;
   // batch 1: 1 KB that the attention-phase cache warm-up DMAs land in (never read)
   static constexpr int Sink = Plan + (MB == 1 ? 0 : 6 * kPlanInts);
-  static constexpr int End = Sink + (MB == 1 ? 256 : 0);
+  static constexpr int End = Sink + 256;   // a 1 KB sink for cache warm-up loads
   static_assert(End * 4 <= kLdsBytes, "LDS map exceeds the allocation");
   static_assert(MB == 1 || 3 * kMaxBatch * kBatchSpanD / 2 <= Region, "staged fp32 inputs do not fit");
   static_assert(Gain % 4 == 0 && Region % 4 == 0 && Sink % 4 == 0, "16-byte alignment");
@@ -1274,6 +1274,27 @@ __device__ __forceinline__ void w0_warm_gu(const Params& P, const int* tab_all, 
   }
 }
 
+// The same for the batched kernel (workgroups past the B*H attention pairs):
+// the 1 KB GU tiles past each streamer's first group (in its registers),
+// up to kW0WarmTiles per streamer.  32 measured best at batch 8 (48 was
+// slower).
+constexpr int kW0WarmTiles = 32;
+__device__ __forceinline__ void w0_warm_tiles(const Params& P, const int* tab_all, int l, float* sink) {
+  const int lane = threadIdx.x & 63;
+  const int* e0 = tab_all + PH_GU * kTabStride;
+  const rsrc_t r = make_rsrc(gemv_base(P, PH_GU, rfl(l)), (uint32_t)rfl(e0[T_NBYTES]));
+  for (int s = 0; s < kStreamers; ++s) {
+    const int* e = tab_all + s * 6 * kTabStride + PH_GU * kTabStride;
+    const uint32_t left = (uint32_t)max(rfl(e[T_LEFT]), 0);
+    const uint32_t off = (uint32_t)rfl(e[T_OFF]);
+    const uint32_t end = off + 1024u * left;
+    for (uint32_t k = 0; k < (uint32_t)kW0WarmTiles; ++k) {
+      const uint32_t b = off + 1024u * (kTilesInFlight + k);
+      if (b + 1024u <= end) dma16_ld(r, sink, b + 16u * lane);
+    }
+  }
+}
+
 template <int MB, int HD>
 __device__ __forceinline__ bool streamer_attention(const Params& P, const Launch& A, const PhaseIt& id, const int* si,
                                                    float* aux, const int* tab = nullptr, float* sink = nullptr) {
@@ -1532,6 +1553,9 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       if constexpr (MB == 1)
         if (id.ph == PH_O && P.H > (int)gridDim.x / 32 && (int)blockIdx.x / wg_per_head(P, pos) >= P.H)
           w0_warm_gu(P, tab_all, id.l, smem + M::Sink);
+      if constexpr (MB > 1)
+        if (id.ph == PH_O && !P.cols_pos && (int)blockIdx.x / wg_per_head(P, pos) >= P.B * P.H)
+          w0_warm_tiles(P, tab_all, id.l, smem + M::Sink);
     }
     auto wait = [&]() { return skip_bar ? true : w0_wait(P, epoch, A.fenced); };
     // the norm gains do not depend on the barrier: they were prefetched
