@@ -52,7 +52,7 @@ typedef enum dec_status {
   DEC_ERR_TOKEN_RANGE = -8,   /* token id outside [0, vocab)                         */
   DEC_ERR_DEVICE = -9,        /* a HIP runtime call failed                           */
   DEC_ERR_TIMEOUT = -10,      /* an in-kernel barrier wait passed the watchdog bound */
-  DEC_ERR_UNSUPPORTED = -11   /* valid request this build does not implement         */
+  DEC_ERR_UNSUPPORTED = -11   /* valid request this library does not implement       */
 } dec_status;
 
 /*
@@ -65,7 +65,7 @@ typedef enum dec_status {
  *   1 <= lm_vocab <= vocab, lm_vocab even;
  *   1 <= max_ctx <= 65536; batch >= 1; rms_eps > 0; rope_base > 1;
  *   flags: 0 or DEC_FLAG_BATCHED_PREFILL (batch 1 only).
- * Limits of this build (DEC_ERR_UNSUPPORTED): d_model, n_heads*head_dim and
+ * Limits of this library (DEC_ERR_UNSUPPORTED): d_model, n_heads*head_dim and
  * d_ffn <= 8192; batch <= 8; with batch > 1, d_model <= 2560 and d_ffn,
  * n_heads*head_dim <= 7680 after rounding up to a multiple of 512 (every
  * sequence's matrix-product input is held on chip, in fp16).
