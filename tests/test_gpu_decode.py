@@ -322,6 +322,30 @@ def test_dense2b_real_shape(stream):
     np.testing.assert_array_equal(runs[0], runs[1])
 
 
+def check_kv_row(K, V, od, p, what):
+    """The GPU's fp16 K/V rows at position p (every layer) against the oracle's.
+
+    Layer 0 sees identical inputs: only fp32-vs-fp64 rounding can flip an fp16
+    value, by one spacing.  Deeper layers inherit such flips through attention
+    (the method rounds K/V to fp16 as well); they stay within one spacing plus
+    0.2% of the layer's rms.
+    """
+    n_layers = K.shape[0]
+    for name, g, r in (("K", K[:, :, p], od.Kc[:, :, p]), ("V", V[:, :, p], od.Vc[:, :, p])):
+        g64 = g.astype(np.float64).reshape(n_layers, -1)
+        r64 = r.astype(np.float64).reshape(n_layers, -1)
+        spacing = np.abs(np.spacing(np.maximum(np.abs(g64), np.abs(r64)).astype(np.float16))).astype(np.float64)
+        rms = np.sqrt(np.mean(r64 * r64, axis=1, keepdims=True))
+        excess = (np.abs(g64 - r64) - spacing) / rms    # beyond one fp16 spacing, relative to the layer's rms
+        worst = excess.max(axis=1)
+        same0 = float(np.mean(g64[0] == r64[0]))
+        print(f"{what} {name}: layer 0 {same0:.4f} identical; worst excess/rms per layer "
+              f"{[float(f'{x:.1e}') for x in worst]}", flush=True)
+        assert np.all(excess[0] * rms[0] <= 2e-5), f"{what} {name} layer 0"
+        assert same0 > 0.99, f"{what} {name} layer 0: only {same0} identical"
+        assert np.all(worst <= 2e-3), f"{what} {name}: {worst.max()}"
+
+
 def test_dense2b_long_context_sampled(stream):
     """The long-context workload at full size: a 3968-token prompt, then decode.
 
@@ -331,7 +355,7 @@ def test_dense2b_long_context_sampled(stream):
     positions < p, runs token p, and its K/V rows at p (every layer) must match
     the GPU's, within one fp16 spacing plus the fp32 error carried in.  At the
     last prompt position its logits must match the prefill's, and at position
-    3968 (attention over 3969 positions in 12 chunks per head) the decode
+    3968 (attention over 3969 positions, 8 workgroups per head) the decode
     step's logits.
     """
     w = synth.workload("dense2b_long")
@@ -347,36 +371,64 @@ def test_dense2b_long_context_sampled(stream):
     V = np.stack([v for _, v in kv])
     od = O.OracleDecoder(s, t)
 
-    def check_row(p, what):
-        for name, g, r in (("K", K[:, :, p], od.Kc[:, :, p]), ("V", V[:, :, p], od.Vc[:, :, p])):
-            g64 = g.astype(np.float64).reshape(s.n_layers, -1)
-            r64 = r.astype(np.float64).reshape(s.n_layers, -1)
-            spacing = np.abs(np.spacing(np.maximum(np.abs(g64), np.abs(r64)).astype(np.float16))).astype(np.float64)
-            rms = np.sqrt(np.mean(r64 * r64, axis=1, keepdims=True))
-            excess = (np.abs(g64 - r64) - spacing) / rms    # beyond one fp16 spacing, relative to the layer's rms
-            worst = excess.max(axis=1)
-            same0 = float(np.mean(g64[0] == r64[0]))
-            print(f"{what} {name}: layer 0 {same0:.4f} identical; worst excess/rms per layer "
-                  f"{[float(f'{x:.1e}') for x in worst]}", flush=True)
-            # Layer 0 sees identical inputs: only fp32-vs-fp64 rounding can flip
-            # an fp16 value, by one spacing.  Deeper layers inherit such flips
-            # through attention (the method rounds K/V to fp16 as well); they
-            # stay within one spacing plus 0.2% of the layer's rms.
-            assert np.all(excess[0] * rms[0] <= 2e-5), f"{what} {name} layer 0"
-            assert same0 > 0.99, f"{what} {name} layer 0: only {same0} identical"
-            assert np.all(worst <= 2e-3), f"{what} {name}: {worst.max()}"
-
     for p in (0, 1983, n - 1):
         od.load_cache(K[:, :, :p], V[:, :, :p], p)
         ref = od.step(int(prompt[p]))
-        check_row(p, f"position {p}")
+        check_kv_row(K, V, od, p, f"position {p}")
         if p == n - 1:
             check_logits(pre, ref, "prefill (last prompt position)")
     od.load_cache(K[:, :, :n], V[:, :, :n], n)
     ref = od.step(int(tok))
-    check_row(n, f"decode position {n}")
+    check_kv_row(K, V, od, n, f"decode position {n}")
     check_logits(lg, ref, f"decode step at position {n}")
     assert nxt == int(np.argmax(lg))
+
+
+def test_dense2b_attention_split_over_3_and_4_workgroups(stream):
+    """dense2b at 601-852 positions: each head's attention on 3, then 4 workgroups.
+
+    Up to 512 positions a head's attention runs on one workgroup; past that on
+    enough workgroups that each wave reads one 32-position group (head dim
+    128): 3 workgroups up to 768 positions, 4 up to 1024.  A 700-token prompt
+    is prefilled and decoded for 152 steps.  The oracle adopts the GPU's fp16
+    cache for the positions before each sampled one: the K/V rows at prompt
+    position 600, the prefill's logits at position 699, the decode step's at
+    700 (3 workgroups per head) and a forced step's at position 851 (4).
+    """
+    w = synth.workload("dense2b")
+    s = w.shape
+    t = synth.workload_weights(w)
+    prompt = synth.make_prompt(s.vocab, 700, seed=w.prompt_seed)[0]
+    n = len(prompt)
+    forced = 4242
+    with make(s, t, stream) as d:
+        tok, pre = d.prefill(prompt, want_logits=True)
+        nxt, lg = d.step(force_tok=tok, want_logits=True)          # position n
+        for _ in range(150):
+            d.step(want_tok=False)                                # positions n+1 .. n+150
+        p2 = d.position
+        nxt2, lg2 = d.step(force_tok=forced, want_logits=True)    # position p2
+        kv = [d.read_kv(l, p2 + 1) for l in range(s.n_layers)]
+    assert p2 == n + 151
+    K = np.stack([k for k, _ in kv])
+    V = np.stack([v for _, v in kv])
+    od = O.OracleDecoder(s, t)
+    for p in (600, n - 1):
+        od.load_cache(K[:, :, :p], V[:, :, :p], p)
+        ref = od.step(int(prompt[p]))
+        check_kv_row(K, V, od, p, f"position {p}")
+        if p == n - 1:
+            check_logits(pre, ref, f"prefill (last prompt position {p})")
+    od.load_cache(K[:, :, :n], V[:, :, :n], n)
+    ref = od.step(int(tok))
+    check_kv_row(K, V, od, n, f"decode position {n}")
+    check_logits(lg, ref, f"decode step at position {n}")
+    assert nxt == int(np.argmax(lg))
+    od.load_cache(K[:, :, :p2], V[:, :, :p2], p2)
+    ref2 = od.step(forced)
+    check_kv_row(K, V, od, p2, f"decode position {p2}")
+    check_logits(lg2, ref2, f"forced step at position {p2}")
+    assert nxt2 == int(np.argmax(lg2))
 
 
 # ----------------------------------------------------------------------------
