@@ -57,6 +57,7 @@ constexpr int kBlocksInFlight = 2 * kUnitsInFlight;
 // The batched kernel streams 1 KB weight tiles, one 16-byte load per lane each.
 constexpr int kTilesInFlight = 8;
 constexpr int kTabStride = 12;   // ints per (streamer, phase type) entry of the phase tables
+constexpr int kStreamerTab = 6 * kTabStride;   // one streamer's entries: phase types 0..5
 constexpr int kPlanInts = 16;    // per phase type: count, then up to 2 * kStreamers combine entries
 constexpr int kAuxFloats = 2048;
 // aux LDS: the step's rotary rows (up to 1024 floats; live from the QKV GEMV
@@ -83,7 +84,7 @@ struct Lds {
   // batched kernel: a streamer's partial results for the (at most two)
   // 16-row output groups it shares with other streamers
   static constexpr int SlotN = MB == 1 ? 0 : kTileRows * MB;
-  static constexpr int Slot = Tab + kStreamers * 6 * kTabStride, Plan = Slot + kStreamers * 2 * SlotN;
+  static constexpr int Slot = Tab + kStreamers * kStreamerTab, Plan = Slot + kStreamers * 2 * SlotN;
   // batch 1: 1 KB that the attention-phase cache warm-up DMAs land in (never read)
   static constexpr int Sink = Plan + (MB == 1 ? 0 : 6 * kPlanInts);
   static constexpr int End = Sink + 256;   // a 1 KB sink for cache warm-up loads
@@ -1238,8 +1239,9 @@ __device__ __forceinline__ void w0_argmax(const Params& P, int i, int cur_col, i
 // head requests the first GU row pair of its share (10 KB) with ordinary,
 // cache-allocating loads into an LDS sink.  HBM is otherwise idle while the
 // heads' workgroups compute attention, and the GU phase's own streaming loads
-// of those blocks then hit the device-side cache.  More than one row pair
-// per streamer delays these workgroups' arrival at the next barrier.
+// of those blocks then hit the device-side cache.  A streamer takes no more
+// than one row pair: it issued its O-phase weight loads before these, and
+// its first O-phase wait (in issue order) would also wait for them.
 __device__ __forceinline__ void warm_gu(const Params& P, const int* tab, int l, float* sink) {
   const int lane = threadIdx.x & 63;
   const int* e = tab + PH_GU * kTabStride;
@@ -1263,7 +1265,7 @@ __device__ __forceinline__ void w0_warm_gu(const Params& P, const int* tab_all, 
   const int* e0 = tab_all + PH_GU * kTabStride;
   const rsrc_t r = make_rsrc(gemv_base(P, PH_GU, rfl(l)), (uint32_t)rfl(e0[T_NBYTES]));
   for (int s = 0; s < kStreamers; ++s) {
-    const int* e = tab_all + s * 6 * kTabStride + PH_GU * kTabStride;
+    const int* e = tab_all + s * kStreamerTab + PH_GU * kTabStride;
     const uint32_t left = (uint32_t)max(rfl(e[T_LEFT]), 0);
     const uint32_t off = (uint32_t)rfl(e[T_OFF]), rowb = (uint32_t)rfl(e[T_ROWB]);
     const uint32_t end = off + 2048u * left;   // the streamer's units are about 2 KB each
@@ -1284,7 +1286,7 @@ __device__ __forceinline__ void w0_warm_tiles(const Params& P, const int* tab_al
   const int* e0 = tab_all + PH_GU * kTabStride;
   const rsrc_t r = make_rsrc(gemv_base(P, PH_GU, rfl(l)), (uint32_t)rfl(e0[T_NBYTES]));
   for (int s = 0; s < kStreamers; ++s) {
-    const int* e = tab_all + s * 6 * kTabStride + PH_GU * kTabStride;
+    const int* e = tab_all + s * kStreamerTab + PH_GU * kTabStride;
     const uint32_t left = (uint32_t)max(rfl(e[T_LEFT]), 0);
     const uint32_t off = (uint32_t)rfl(e[T_OFF]);
     const uint32_t end = off + 1024u * left;
@@ -1483,7 +1485,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   // below is a scalar branch and every per-wave value stays in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   int* tab_all = reinterpret_cast<int*>(smem + M::Tab);
-  int* tab = tab_all + (wave > 0 ? (wave - 1) * 6 * kTabStride : 0);
+  int* tab = tab_all + (wave > 0 ? (wave - 1) * kStreamerTab : 0);
   float* slots = smem + M::Slot;
   int* plan = reinterpret_cast<int*>(smem + M::Plan);
   const int total = A.n_tok * phases_per_token(P.L);
