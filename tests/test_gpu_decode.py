@@ -640,6 +640,42 @@ def test_dense2b_batched_prefill_sampled(stream):
             check_logits(got, ref, f"position {p}")
 
 
+
+def test_dense2b_long_batched_prefill_sampled(stream):
+    """The 3968-token long-context prompt through the batched prefill (496 steps of 8).
+
+    Each step's attention runs over up to 3968 positions of the one cache, on
+    one workgroup per (column, head), so every wave reads hundreds of
+    positions.  Sampled as above: the oracle adopts the GPU cache for the
+    positions before the one it checks (early, middle, last prompt position,
+    first decode position).
+    """
+    w = synth.workload("dense2b_long")
+    s = w.shape
+    t = synth.workload_weights(w)
+    prompt = synth.make_prompt(s.vocab, w.prompt_len, seed=w.prompt_seed)[0]
+    n = len(prompt)
+    with make(s, t, stream, flags=BP) as d:
+        tok, pre = d.prefill(prompt, want_logits=True)
+        nxt, lg = d.step(force_tok=tok, want_logits=True)
+        kv = [d.read_kv(l, n + 1) for l in range(s.n_layers)]
+    assert nxt == int(np.argmax(lg))
+    K = np.stack([k for k, _ in kv])
+    V = np.stack([v for _, v in kv])
+    od = O.OracleDecoder(s, t)
+    for p, token, got in ((5, int(prompt[5]), None), (1983, int(prompt[1983]), None),
+                          (n - 1, int(prompt[n - 1]), pre), (n, int(tok), lg)):
+        od.load_cache(K[:, :, :p], V[:, :, :p], p)
+        ref = od.step(token)
+        ek = kv_excess(K[:, :, p], od.Kc[:, :, p])
+        ev = kv_excess(V[:, :, p], od.Vc[:, :, p])
+        print(f"position {p}: K/V excess/rms {ek.max():.1e} {ev.max():.1e}", flush=True)
+        assert ek[0] <= 2e-5 and ev[0] <= 2e-5
+        assert ek.max() <= KV_BATCH and ev.max() <= KV_BATCH
+        if got is not None:
+            check_logits(got, ref, f"position {p}")
+
+
 # ----------------------------------------------------------------------------
 # other grid sizes: fewer workgroups than barrier groups, odd splits
 # ----------------------------------------------------------------------------
