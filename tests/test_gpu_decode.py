@@ -523,9 +523,12 @@ def test_batch_generate_equals_repeated_steps_bitwise(stream):
         assert a.position == b.position == 26
 
 
-def test_dense2b_b8_sampled(stream):
-    """The batch-8 workload at full size: 8 sequences of 256-token prompts, then a step.
+@pytest.mark.parametrize("n", [256, 3968])
+def test_dense2b_b8_sampled(stream, n):
+    """The batch-8 workload at full size: 8 sequences of n-token prompts, then a step.
 
+    256 is the workload's prompt; 3968 runs every (sequence, head) pair's
+    attention on one workgroup over nearly the whole 4096-position cache.
     For two of the sequences the oracle adopts the GPU's fp16 cache for the
     positions before the one it checks, runs that position, and its logits
     (last prompt position and the decode step) and K/V rows must match.
@@ -533,8 +536,7 @@ def test_dense2b_b8_sampled(stream):
     w = synth.workload("dense2b_b8")
     s = w.shape
     t = synth.workload_weights(w)
-    prompts = synth.make_prompt(s.vocab, w.prompt_len, batch=w.batch, seed=w.prompt_seed)
-    n = w.prompt_len
+    prompts = synth.make_prompt(s.vocab, n, batch=w.batch, seed=w.prompt_seed)
     with make(s, t, stream, batch=w.batch) as d:
         tok, pre = d.prefill(prompts, want_logits=True)
         nxt, lg = d.step(force_tok=tok, want_logits=True)
