@@ -384,6 +384,40 @@ def test_dense2b_long_context_sampled(stream):
     assert nxt == int(np.argmax(lg))
 
 
+def test_lane2b_long_context_sampled(stream):
+    """One lane's shape (3 heads) after a 2000-token prompt.
+
+    With few heads the heads' workgroups take no QKV rows, and at 2000
+    positions each head's attention is split over 8 workgroups whose partials
+    the last one merges.  The oracle adopts the GPU's fp16 cache for the
+    positions before each sampled one: the K/V rows at position 1000, the
+    prefill's logits at 1999 and the decode step's at 2000.
+    """
+    w = synth.workload("lane2b")
+    s = w.shape
+    t = synth.workload_weights(w)
+    prompt = synth.make_prompt(s.vocab, 2000, seed=w.prompt_seed)[0]
+    n = len(prompt)
+    with make(s, t, stream) as d:
+        tok, pre = d.prefill(prompt, want_logits=True)
+        nxt, lg = d.step(force_tok=tok, want_logits=True)
+        kv = [d.read_kv(l, n + 1) for l in range(s.n_layers)]
+    K = np.stack([k for k, _ in kv])
+    V = np.stack([v for _, v in kv])
+    od = O.OracleDecoder(s, t)
+    for p in (1000, n - 1):
+        od.load_cache(K[:, :, :p], V[:, :, :p], p)
+        ref = od.step(int(prompt[p]))
+        check_kv_row(K, V, od, p, f"position {p}")
+        if p == n - 1:
+            check_logits(pre, ref, f"prefill (last prompt position {p})")
+    od.load_cache(K[:, :, :n], V[:, :, :n], n)
+    ref = od.step(int(tok))
+    check_kv_row(K, V, od, n, f"decode position {n}")
+    check_logits(lg, ref, f"decode step at position {n}")
+    assert nxt == int(np.argmax(lg))
+
+
 def test_dense2b_attention_split_over_3_and_4_workgroups(stream):
     """dense2b at 601-852 positions: each head's attention on 3, then 4 workgroups.
 
