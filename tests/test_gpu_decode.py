@@ -384,6 +384,31 @@ def test_dense2b_long_context_sampled(stream):
     assert nxt == int(np.argmax(lg))
 
 
+def test_dense2b_generate_across_the_attention_split_equals_steps(stream):
+    """dense2b: 24 tokens in one dec_generate launch equal 24 dec_step calls.
+
+    From a 500-token prompt the launch crosses 512 positions, where each
+    head's attention goes from one workgroup to three; tokens and the whole
+    KV cache must be bitwise equal to the step-by-step run.
+    """
+    w = synth.workload("dense2b")
+    s = w.shape
+    t = synth.workload_weights(w)
+    prompt = synth.make_prompt(s.vocab, 500, seed=w.prompt_seed)[0]
+    with make(s, t, stream) as a, make(s, t, stream) as b:
+        a.prefill(prompt)
+        b.prefill(prompt)
+        ga = a.generate(24)
+        gb = [b.step()[0] for _ in range(24)]
+        assert list(ga) == gb
+        assert a.position == b.position == 524
+        for l in (0, s.n_layers // 2, s.n_layers - 1):
+            ka, va = a.read_kv(l, 524)
+            kb, vb = b.read_kv(l, 524)
+            assert np.array_equal(ka.view(np.uint16), kb.view(np.uint16)), f"K layer {l}"
+            assert np.array_equal(va.view(np.uint16), vb.view(np.uint16)), f"V layer {l}"
+
+
 def test_lane2b_long_context_sampled(stream):
     """One lane's shape (3 heads) after a 2000-token prompt.
 
