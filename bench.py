@@ -14,7 +14,9 @@ against MI355X's 8 TB/s HBM peak with ALGORITHMIC bytes per launch: every
 weight byte once, one embedding row, the KV-cache rows attention reads at
 that position and the rows it appends.  stream_ceiling is the measured read
 rate of a plain 16-byte non-temporal stream over 2 GiB on the same device
-(dec_stream_ceiling) and the decode rate as a fraction of it.  The cpu_baseline object times the
+(dec_stream_ceiling) and the decode rate as a fraction of it.  generate is the
+same positions decoded in one dec_generate launch (not the metric: it shows
+what the per-token launch costs).  The cpu_baseline object times the
 CPU oracle (test infrastructure) on a bounded sample of the same workload.
 """
 import argparse
@@ -233,6 +235,20 @@ def main():
         "context": {"pages_8xMI300X_tokens_per_s": 3000, "pages_8xH200_tokens_per_s": 2100,
                     "note": "2B fp16, batch 1, 8 GPUs each: other hardware, context only"},
     }
+    if args.mode == "step" and not args.multilaunch:
+        # the same positions in one dec_generate launch (context: the step
+        # mode's per-launch cost), after the timed region
+        dec.reset()
+        dec.prefill(prompt)
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        dec.generate(K)
+        g1.record(stream)
+        g1.synchronize()
+        gen_ms = g0.elapsed_time(g1)
+        out["generate"] = {"tokens_per_s": round(K * nb / (gen_ms / 1e3), 2), "ms_per_step": round(gen_ms / K, 4),
+                           "launches": 1}
     dec.close()
     # the plain-stream read rate of this device, the practical ceiling under the 8 TB/s peak
     ceiling = B.stream_ceiling(1 << 31, 5)
