@@ -157,42 +157,40 @@ def main():
 
     K = args.steps
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # HIP events on the decode stream only around the region and at the
+    # boundaries of four segments: an event between every two launches would
+    # add about 5 us per step.  The launches run back to back, so the average
+    # launch duration is the region over K.
+    nseg = 4 if args.mode == "step" and K >= 8 else 1
+    bounds = [K * j // nseg for j in range(nseg + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nseg + 1)]
     t0 = time.perf_counter()
-    ev0.record(stream)
+    evs[0].record(stream)
     if args.mode == "generate":
-        starts[0].record(stream)
         toks = dec.generate(K)
-        ends[0].record(stream)
+        evs[1].record(stream)
     else:
-        for i in range(K):
-            starts[i].record(stream)
-            dec.step(want_tok=False)
-            ends[i].record(stream)
-    ev1.record(stream)
-    ev1.synchronize()
+        for j in range(nseg):
+            for _ in range(bounds[j], bounds[j + 1]):
+                dec.step(want_tok=False)
+            evs[j + 1].record(stream)
+    evs[-1].synchronize()
     dec.sync()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    region_ms = ev0.elapsed_time(ev1)
+    region_ms = evs[0].elapsed_time(evs[-1])
     if args.mode == "generate":
-        launch_ms = [starts[0].elapsed_time(ends[0])]
         bytes_per_launch = sum(R.step_bytes(s, pos0 + i, nb).total for i in range(K))
+        avg_launch_s = region_ms / 1e3
     else:
-        launch_ms = [starts[i].elapsed_time(ends[i]) for i in range(K)]
         bytes_per_launch = R.mean_step_bytes(s, pos0, K, nb)
-    avg_launch_s = float(np.mean(launch_ms)) / 1e3
-    # the timed steps in four consecutive segments (step mode): spread of the
-    # rate within the run (later segments are at longer contexts), from the
-    # same per-launch events
+        avg_launch_s = region_ms / K / 1e3
+    # the rate of each segment (later segments are at longer contexts)
     segs = None
-    if args.mode == "step" and K >= 8:
-        q = K // 4
-        seg_tps = [q * nb / (starts[i * q].elapsed_time(ends[i * q + q - 1]) / 1e3) for i in range(4)]
-        segs = {"n": 4, "steps_each": q, "min": round(min(seg_tps), 2), "median": round(float(np.median(seg_tps)), 2),
-                "max": round(max(seg_tps), 2)}
+    if nseg > 1:
+        seg_tps = [(bounds[j + 1] - bounds[j]) * nb / (evs[j].elapsed_time(evs[j + 1]) / 1e3) for j in range(nseg)]
+        segs = {"n": nseg, "steps_each": K // nseg, "min": round(min(seg_tps), 2),
+                "median": round(float(np.median(seg_tps)), 2), "max": round(max(seg_tps), 2)}
     req_tok_s = K / (region_ms / 1e3)          # tokens/s of each sequence
     tok_s = req_tok_s * nb                     # whole-job tokens/s
     achieved = bytes_per_launch / avg_launch_s / 1e9
