@@ -160,7 +160,7 @@ def test_kv_cache_after_prefill_matches_oracle(stream):
                 # flip an fp16 value; deeper layers also inherit upstream differences
                 same = float(np.mean(diff == 0))
                 print(f"layer {l} {name}: {same:.4f} identical, max diff {diff.max():.2e}")
-                assert same > (0.99 if l == 0 else 0.90), f"layer {l} {name}: {same}"
+                assert same > (0.99 if l == 0 else 0.95), f"layer {l} {name}: {same}"
 
 
 def _idx(shape, name, layer=None):
@@ -299,89 +299,19 @@ def test_weights_file_ingest_matches_host_tensors(stream, tmp_path):
 # real shapes
 # ----------------------------------------------------------------------------
 
-def test_lane2b_real_shape(stream):
-    w = synth.workload("lane2b")
-    t = synth.workload_weights(w)
-    prompt = synth.make_prompt(w.shape.vocab, w.prompt_len, seed=w.prompt_seed)[0]
-    teacher_forced(w.shape, t, prompt, 3, stream)
-
-
-def test_dense2b_real_shape(stream):
+def test_dense2b_run_to_run_bitwise(stream):
+    """Run to run at full size: the partial row sums meet in an order that does
+    not depend on timing (at most two contributors per row pair), so two fresh
+    handles give the same bits."""
     w = synth.workload("dense2b")
     t = synth.workload_weights(w)
     prompt = synth.make_prompt(w.shape.vocab, w.prompt_len, seed=w.prompt_seed)[0]
-    teacher_forced(w.shape, t, prompt, 2, stream)
-    # Run to run at full size: the partial row sums meet in an order that does
-    # not depend on timing (at most two contributors per row pair), so two
-    # fresh handles give the same bits.
     runs = []
     for _ in range(2):
         with make(w.shape, t, stream) as d:
             _, pre = d.prefill(prompt[:24], want_logits=True)
             runs.append(np.concatenate([pre] + [d.step(want_logits=True)[1] for _ in range(2)]))
     np.testing.assert_array_equal(runs[0], runs[1])
-
-
-def check_kv_row(K, V, od, p, what):
-    """The GPU's fp16 K/V rows at position p (every layer) against the oracle's.
-
-    Layer 0 sees identical inputs: only fp32-vs-fp64 rounding can flip an fp16
-    value, by one spacing.  Deeper layers inherit such flips through attention
-    (the method rounds K/V to fp16 as well); they stay within one spacing plus
-    0.2% of the layer's rms.
-    """
-    n_layers = K.shape[0]
-    for name, g, r in (("K", K[:, :, p], od.Kc[:, :, p]), ("V", V[:, :, p], od.Vc[:, :, p])):
-        g64 = g.astype(np.float64).reshape(n_layers, -1)
-        r64 = r.astype(np.float64).reshape(n_layers, -1)
-        spacing = np.abs(np.spacing(np.maximum(np.abs(g64), np.abs(r64)).astype(np.float16))).astype(np.float64)
-        rms = np.sqrt(np.mean(r64 * r64, axis=1, keepdims=True))
-        excess = (np.abs(g64 - r64) - spacing) / rms    # beyond one fp16 spacing, relative to the layer's rms
-        worst = excess.max(axis=1)
-        same0 = float(np.mean(g64[0] == r64[0]))
-        print(f"{what} {name}: layer 0 {same0:.4f} identical; worst excess/rms per layer "
-              f"{[float(f'{x:.1e}') for x in worst]}", flush=True)
-        assert np.all(excess[0] * rms[0] <= 2e-5), f"{what} {name} layer 0"
-        assert same0 > 0.99, f"{what} {name} layer 0: only {same0} identical"
-        assert np.all(worst <= 2e-3), f"{what} {name}: {worst.max()}"
-
-
-def test_dense2b_long_context_sampled(stream):
-    """The long-context workload at full size: a 3968-token prompt, then decode.
-
-    The oracle cannot prefill 3968 tokens of the 2.3B model in test time, so
-    parity is checked on sampled positions, conditioned on the GPU's own fp16
-    cache for the positions before them: the oracle adopts the GPU cache for
-    positions < p, runs token p, and its K/V rows at p (every layer) must match
-    the GPU's, within one fp16 spacing plus the fp32 error carried in.  At the
-    last prompt position its logits must match the prefill's, and at position
-    3968 (attention over 3969 positions, 8 workgroups per head) the decode
-    step's logits.
-    """
-    w = synth.workload("dense2b_long")
-    s = w.shape
-    t = synth.workload_weights(w)
-    prompt = synth.make_prompt(s.vocab, w.prompt_len, seed=w.prompt_seed)[0]
-    n = len(prompt)
-    with make(s, t, stream) as d:
-        tok, pre = d.prefill(prompt, want_logits=True)
-        nxt, lg = d.step(force_tok=tok, want_logits=True)
-        kv = [d.read_kv(l, n + 1) for l in range(s.n_layers)]
-    K = np.stack([k for k, _ in kv])   # [L, H, n+1, hd] fp16
-    V = np.stack([v for _, v in kv])
-    od = O.OracleDecoder(s, t)
-
-    for p in (0, 1983, n - 1):
-        od.load_cache(K[:, :, :p], V[:, :, :p], p)
-        ref = od.step(int(prompt[p]))
-        check_kv_row(K, V, od, p, f"position {p}")
-        if p == n - 1:
-            check_logits(pre, ref, "prefill (last prompt position)")
-    od.load_cache(K[:, :, :n], V[:, :, :n], n)
-    ref = od.step(int(tok))
-    check_kv_row(K, V, od, n, f"decode position {n}")
-    check_logits(lg, ref, f"decode step at position {n}")
-    assert nxt == int(np.argmax(lg))
 
 
 def test_dense2b_generate_across_the_attention_split_equals_steps(stream):
@@ -407,87 +337,6 @@ def test_dense2b_generate_across_the_attention_split_equals_steps(stream):
             kb, vb = b.read_kv(l, 524)
             assert np.array_equal(ka.view(np.uint16), kb.view(np.uint16)), f"K layer {l}"
             assert np.array_equal(va.view(np.uint16), vb.view(np.uint16)), f"V layer {l}"
-
-
-def test_lane2b_long_context_sampled(stream):
-    """One lane's shape (3 heads) after a 2000-token prompt.
-
-    With few heads the heads' workgroups take no QKV rows, and at 2000
-    positions each head's attention is split over 8 workgroups whose partials
-    the last one merges.  The oracle adopts the GPU's fp16 cache for the
-    positions before each sampled one: the K/V rows at position 1000, the
-    prefill's logits at 1999 and the decode step's at 2000.
-    """
-    w = synth.workload("lane2b")
-    s = w.shape
-    t = synth.workload_weights(w)
-    prompt = synth.make_prompt(s.vocab, 2000, seed=w.prompt_seed)[0]
-    n = len(prompt)
-    with make(s, t, stream) as d:
-        tok, pre = d.prefill(prompt, want_logits=True)
-        nxt, lg = d.step(force_tok=tok, want_logits=True)
-        kv = [d.read_kv(l, n + 1) for l in range(s.n_layers)]
-    K = np.stack([k for k, _ in kv])
-    V = np.stack([v for _, v in kv])
-    od = O.OracleDecoder(s, t)
-    for p in (1000, n - 1):
-        od.load_cache(K[:, :, :p], V[:, :, :p], p)
-        ref = od.step(int(prompt[p]))
-        check_kv_row(K, V, od, p, f"position {p}")
-        if p == n - 1:
-            check_logits(pre, ref, f"prefill (last prompt position {p})")
-    od.load_cache(K[:, :, :n], V[:, :, :n], n)
-    ref = od.step(int(tok))
-    check_kv_row(K, V, od, n, f"decode position {n}")
-    check_logits(lg, ref, f"decode step at position {n}")
-    assert nxt == int(np.argmax(lg))
-
-
-def test_dense2b_attention_split_over_3_and_4_workgroups(stream):
-    """dense2b at 601-852 positions: each head's attention on 3, then 4 workgroups.
-
-    Up to 512 positions a head's attention runs on one workgroup; past that on
-    enough workgroups that each wave reads one 32-position group (head dim
-    128): 3 workgroups up to 768 positions, 4 up to 1024.  A 700-token prompt
-    is prefilled and decoded for 152 steps.  The oracle adopts the GPU's fp16
-    cache for the positions before each sampled one: the K/V rows at prompt
-    position 600, the prefill's logits at position 699, the decode step's at
-    700 (3 workgroups per head) and a forced step's at position 851 (4).
-    """
-    w = synth.workload("dense2b")
-    s = w.shape
-    t = synth.workload_weights(w)
-    prompt = synth.make_prompt(s.vocab, 700, seed=w.prompt_seed)[0]
-    n = len(prompt)
-    forced = 4242
-    with make(s, t, stream) as d:
-        tok, pre = d.prefill(prompt, want_logits=True)
-        nxt, lg = d.step(force_tok=tok, want_logits=True)          # position n
-        for _ in range(150):
-            d.step(want_tok=False)                                # positions n+1 .. n+150
-        p2 = d.position
-        nxt2, lg2 = d.step(force_tok=forced, want_logits=True)    # position p2
-        kv = [d.read_kv(l, p2 + 1) for l in range(s.n_layers)]
-    assert p2 == n + 151
-    K = np.stack([k for k, _ in kv])
-    V = np.stack([v for _, v in kv])
-    od = O.OracleDecoder(s, t)
-    for p in (600, n - 1):
-        od.load_cache(K[:, :, :p], V[:, :, :p], p)
-        ref = od.step(int(prompt[p]))
-        check_kv_row(K, V, od, p, f"position {p}")
-        if p == n - 1:
-            check_logits(pre, ref, f"prefill (last prompt position {p})")
-    od.load_cache(K[:, :, :n], V[:, :, :n], n)
-    ref = od.step(int(tok))
-    check_kv_row(K, V, od, n, f"decode position {n}")
-    check_logits(lg, ref, f"decode step at position {n}")
-    assert nxt == int(np.argmax(lg))
-    od.load_cache(K[:, :, :p2], V[:, :, :p2], p2)
-    ref2 = od.step(forced)
-    check_kv_row(K, V, od, p2, f"decode position {p2}")
-    check_logits(lg2, ref2, f"forced step at position {p2}")
-    assert nxt2 == int(np.argmax(lg2))
 
 
 # ----------------------------------------------------------------------------
@@ -582,41 +431,6 @@ def test_batch_generate_equals_repeated_steps_bitwise(stream):
         assert a.position == b.position == 26
 
 
-@pytest.mark.parametrize("n", [256, 3968])
-def test_dense2b_b8_sampled(stream, n):
-    """The batch-8 workload at full size: 8 sequences of n-token prompts, then a step.
-
-    256 is the workload's prompt; 3968 runs every (sequence, head) pair's
-    attention on one workgroup over nearly the whole 4096-position cache.
-    For two of the sequences the oracle adopts the GPU's fp16 cache for the
-    positions before the one it checks, runs that position, and its logits
-    (last prompt position and the decode step) and K/V rows must match.
-    """
-    w = synth.workload("dense2b_b8")
-    s = w.shape
-    t = synth.workload_weights(w)
-    prompts = synth.make_prompt(s.vocab, n, batch=w.batch, seed=w.prompt_seed)
-    with make(s, t, stream, batch=w.batch) as d:
-        tok, pre = d.prefill(prompts, want_logits=True)
-        nxt, lg = d.step(force_tok=tok, want_logits=True)
-        pre, lg = pre.reshape(w.batch, -1), lg.reshape(w.batch, -1)
-        kvs = {b: [d.read_kv(l, n + 1, seq=b) for l in range(s.n_layers)] for b in (0, w.batch - 1)}
-    for b in (0, w.batch - 1):
-        assert nxt[b] == int(np.argmax(lg[b]))
-        K = np.stack([k for k, _ in kvs[b]])
-        V = np.stack([v for _, v in kvs[b]])
-        od = O.OracleDecoder(s, t)
-        for p, ids, got in ((n - 1, prompts[b], pre[b]), (n, None, lg[b])):
-            od.load_cache(K[:, :, :p], V[:, :, :p], p)
-            ref = od.step(int(ids[p]) if ids is not None else int(tok[b]))
-            check_logits(got, ref, f"seq {b} position {p}")
-            ek = kv_excess(K[:, :, p], od.Kc[:, :, p])
-            ev = kv_excess(V[:, :, p], od.Vc[:, :, p])
-            print(f"seq {b} position {p}: K/V excess/rms {ek.max():.1e} {ev.max():.1e}", flush=True)
-            assert ek[0] <= 2e-5 and ev[0] <= 2e-5          # layer 0: exact inputs
-            assert ek.max() <= KV_BATCH and ev.max() <= KV_BATCH
-
-
 # ----------------------------------------------------------------------------
 # batched prefill (DEC_FLAG_BATCHED_PREFILL): 8 prompt positions per step of
 # the matrix-core kernel, causal attention over the one sequence's cache.
@@ -667,74 +481,6 @@ def test_batched_prefill_then_generate_matches_steps(stream):
         ga = a.generate(10)
         gb = [b.step()[0] for _ in range(10)]
         assert list(ga) == gb
-
-
-def test_dense2b_batched_prefill_sampled(stream):
-    """The 128-token dense2b prompt through the batched prefill (16 steps of 8).
-
-    The oracle adopts the GPU cache for the positions before the one it
-    checks; its K/V rows and logits at the last prompt position and at the
-    first decode position must match.
-    """
-    w = synth.workload("dense2b")
-    s = w.shape
-    t = synth.workload_weights(w)
-    prompt = synth.make_prompt(s.vocab, w.prompt_len, seed=w.prompt_seed)[0]
-    n = len(prompt)
-    with make(s, t, stream, flags=BP) as d:
-        tok, pre = d.prefill(prompt, want_logits=True)
-        nxt, lg = d.step(force_tok=tok, want_logits=True)
-        kv = [d.read_kv(l, n + 1) for l in range(s.n_layers)]
-    assert nxt == int(np.argmax(lg))
-    K = np.stack([k for k, _ in kv])
-    V = np.stack([v for _, v in kv])
-    od = O.OracleDecoder(s, t)
-    for p, token, got in ((5, int(prompt[5]), None), (n - 1, int(prompt[n - 1]), pre), (n, int(tok), lg)):
-        od.load_cache(K[:, :, :p], V[:, :, :p], p)
-        ref = od.step(token)
-        ek = kv_excess(K[:, :, p], od.Kc[:, :, p])
-        ev = kv_excess(V[:, :, p], od.Vc[:, :, p])
-        print(f"position {p}: K/V excess/rms {ek.max():.1e} {ev.max():.1e}", flush=True)
-        assert ek[0] <= 2e-5 and ev[0] <= 2e-5
-        assert ek.max() <= KV_BATCH and ev.max() <= KV_BATCH
-        if got is not None:
-            check_logits(got, ref, f"position {p}")
-
-
-
-def test_dense2b_long_batched_prefill_sampled(stream):
-    """The 3968-token long-context prompt through the batched prefill (496 steps of 8).
-
-    Each step's attention runs over up to 3968 positions of the one cache, on
-    one workgroup per (column, head), so every wave reads hundreds of
-    positions.  Sampled as above: the oracle adopts the GPU cache for the
-    positions before the one it checks (early, middle, last prompt position,
-    first decode position).
-    """
-    w = synth.workload("dense2b_long")
-    s = w.shape
-    t = synth.workload_weights(w)
-    prompt = synth.make_prompt(s.vocab, w.prompt_len, seed=w.prompt_seed)[0]
-    n = len(prompt)
-    with make(s, t, stream, flags=BP) as d:
-        tok, pre = d.prefill(prompt, want_logits=True)
-        nxt, lg = d.step(force_tok=tok, want_logits=True)
-        kv = [d.read_kv(l, n + 1) for l in range(s.n_layers)]
-    assert nxt == int(np.argmax(lg))
-    K = np.stack([k for k, _ in kv])
-    V = np.stack([v for _, v in kv])
-    od = O.OracleDecoder(s, t)
-    for p, token, got in ((5, int(prompt[5]), None), (1983, int(prompt[1983]), None),
-                          (n - 1, int(prompt[n - 1]), pre), (n, int(tok), lg)):
-        od.load_cache(K[:, :, :p], V[:, :, :p], p)
-        ref = od.step(token)
-        ek = kv_excess(K[:, :, p], od.Kc[:, :, p])
-        ev = kv_excess(V[:, :, p], od.Vc[:, :, p])
-        print(f"position {p}: K/V excess/rms {ek.max():.1e} {ev.max():.1e}", flush=True)
-        assert ek[0] <= 2e-5 and ev[0] <= 2e-5
-        assert ek.max() <= KV_BATCH and ev.max() <= KV_BATCH
-        if got is not None:
-            check_logits(got, ref, f"position {p}")
 
 
 # ----------------------------------------------------------------------------
