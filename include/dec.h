@@ -18,6 +18,13 @@
  * untied LM head, greedy argmax with the lowest index winning ties) is fixed
  * by the model description below.
  *
+ * Provenance of the calls.  The pages describe a system, not a programming
+ * interface: they name no API.  The calls below are this library's contract
+ * for the decode path (a handle made from a model description and weights;
+ * prefill; one step yielding a token and optionally its logits; reset), and
+ * each call's comment names the passage whose operation it carries out.
+ * Calls that only serve tests or measurement say so.
+ *
  * Conventions
  *  - Every function returns a dec_status (0 = OK, negative = error) unless
  *    stated; on error dec_last_error() describes it.
@@ -26,7 +33,9 @@
  *    optional device arena and stream passed to dec_init.
  *  - A handle is not thread-safe; distinct handles are independent.
  *  - All calls that run GPU work are synchronous with respect to the handle's
- *    stream unless stated (dec_step with out_tok == NULL is asynchronous).
+ *    stream unless stated (dec_step with out_tok == NULL and out_logits ==
+ *    NULL is asynchronous; its input arrays are still read during the call
+ *    only).
  */
 #ifndef DECMONO_DEC_H
 #define DECMONO_DEC_H
@@ -182,19 +191,26 @@ typedef struct dec_init_opts {
 
 typedef struct dec_handle dec_handle;
 
-/* ABI version of the loaded library (DEC_ABI_VERSION it was built with). */
+/* ABI version of the loaded library (DEC_ABI_VERSION it was built with).
+ * Library bookkeeping; no passage of the pages. */
 int32_t dec_abi_version(void);
 
 /*
  * Bytes of device memory a handle for `desc` needs (weights, KV cache,
  * activations and control words), for a caller-provided arena.  Host only;
  * needs no GPU.  grid = workgroups the kernel will use (0 = 256).
+ * Memory planning for the weights and the KV cache the bandwidth bound counts
+ * (page 標準GPUによるリアルタイムLLM推論, section
+ * GPU推論の速度制限要因：メモリ帯域幅).
  */
 int dec_arena_bytes(const dec_model_desc* desc, int32_t grid, size_t* out_bytes);
 
 /*
  * Validate `desc` without touching any device.  DEC_OK or DEC_ERR_BAD_DESC /
- * DEC_ERR_UNSUPPORTED with the reason in dec_last_error(NULL).
+ * DEC_ERR_UNSUPPORTED with the reason in dec_last_error(NULL).  The shape
+ * rules are this library's (the pages give only a 2B-class, 25-layer, fp16
+ * model with a 4096-token context: aether-echoes operator view, section
+ * どう出したか).
  */
 int dec_check_desc(const dec_model_desc* desc);
 
@@ -202,6 +218,9 @@ int dec_check_desc(const dec_model_desc* desc);
  * Read and validate the header and tensor table of a DECW file against the
  * rules above (magic, version, count, dtypes, shapes, offsets, file size).
  * Fills *out_desc from the header.  Host only.  DEC_ERR_WEIGHTS on any defect.
+ * The pages define no weight file; DECW is this library's inference-only
+ * format for fp16 weights with no quantisation (studioglobal.ai article,
+ * section Laneformer 2B: 実証済みの性能).
  */
 int dec_weights_file_check(const char* path, dec_model_desc* out_desc);
 
@@ -210,7 +229,10 @@ int dec_weights_file_check(const char* path, dec_model_desc* out_desc);
  * allocate the KV cache for batch x max_ctx positions and build the rotary
  * table (cos/sin of p * rope_base^(-2i/head_dim), computed in double on the
  * host, stored as fp32).  Position starts at 0.  On failure *out is NULL and
- * dec_last_error(NULL) holds the reason.
+ * dec_last_error(NULL) holds the reason.  The weights are packed once into
+ * the layout the decode kernel streams, the hand-controlled low-level layout
+ * and execution the pages credit for reaching bandwidth speed (page
+ * 標準GPUによるリアルタイムLLM推論, section Kog Inference Engineの特徴とイノベーション).
  */
 int dec_init(const dec_model_desc* desc, const dec_weights_src* weights,
              const dec_init_opts* opts, dec_handle** out);
@@ -222,6 +244,9 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights,
  * cache) and returns the greedy next token of each sequence in out_tok
  * [batch] (host, required) and, if out_logits != NULL, the last position's
  * logits [batch * lm_vocab] (host, fp32).  Position becomes n.
+ * The prompt phase before decoding; its duration is the time to first token,
+ * one of the three speed axes the pages name (page 標準GPUによるリアルタイム
+ * LLM推論, section 単一リクエストLLMデコード速度の重要性).
  */
 int dec_prefill(dec_handle* h, const int32_t* tokens, int32_t n,
                 int32_t* out_tok, float* out_logits);
@@ -229,11 +254,21 @@ int dec_prefill(dec_handle* h, const int32_t* tokens, int32_t n,
 /*
  * One decode step at the current position p.  Input token: force_tok[batch]
  * (host) if non-NULL (teacher forcing), else the previous greedy output kept
- * on the device.  Appends the keys/values of position p, advances to p+1 and
- * produces the greedy token.  out_tok [batch] (host) and out_logits
- * [batch * lm_vocab] (host) are optional; with both NULL the call only
- * enqueues work on the stream and returns without waiting (use dec_sync).
- * DEC_ERR_CONTEXT_FULL if p == max_ctx; DEC_ERR_STATE before any prefill.
+ * on the device.  force_tok is read during the call only: its values travel
+ * in the kernel launch's arguments.  Appends the keys/values of position p,
+ * advances to p+1 and produces the greedy token.  out_tok [batch] (host) and
+ * out_logits [batch * lm_vocab] (host) are optional; with both NULL the call
+ * only enqueues work on the stream and returns without waiting (use dec_sync;
+ * a device error such as DEC_ERR_TIMEOUT then surfaces at the next
+ * synchronous call).  DEC_ERR_CONTEXT_FULL if p == max_ctx; DEC_ERR_STATE
+ * before any prefill; DEC_ERR_TOKEN_RANGE for a forced token outside
+ * [0, vocab).
+ * One step is one pass over every active weight plus the KV cache read, the
+ * quantity the bandwidth bound prices (page 標準GPUによるリアルタイムLLM推論,
+ * section GPU推論の速度制限要因：メモリ帯域幅), with matrix products,
+ * attention, normalisation and sampling in one resident program (same page,
+ * section Kog Inference Engineの特徴とイノベーション); sampling is greedy
+ * (studioglobal.ai article, table under Laneformer 2B: 実証済みの性能).
  */
 int dec_step(dec_handle* h, const int32_t* force_tok, int32_t* out_tok, float* out_logits);
 
@@ -241,22 +276,31 @@ int dec_step(dec_handle* h, const int32_t* force_tok, int32_t* out_tok, float* o
  * n_steps greedy steps inside one kernel launch, each step fed the previous
  * step's token on the device.  Same result as n_steps dec_step calls with
  * force_tok == NULL.  out_toks: host int32 [n_steps * batch] (step-major).
+ * One GPU-resident program for many tokens, without a kernel boundary or host
+ * scheduling between them (page 標準GPUによるリアルタイムLLM推論, section
+ * 標準推論スタックのボトルネックとKogの工夫).
  */
 int dec_generate(dec_handle* h, int32_t n_steps, int32_t* out_toks);
 
-/* Wait for all work enqueued on the handle's stream; reports deferred errors. */
+/* Wait for all work enqueued on the handle's stream; reports deferred errors.
+ * Library bookkeeping; no passage of the pages. */
 int dec_sync(dec_handle* h);
 
-/* Position -> 0.  The cache is logically empty (overwritten, not cleared). */
+/* Position -> 0.  The cache is logically empty (overwritten, not cleared).
+ * Starts a new request on the same weights (the pages' single-request
+ * serving, section 単一リクエストLLMデコード速度の重要性). */
 int dec_reset(dec_handle* h);
 
-/* Current position (number of cached positions), or -1 for a NULL handle. */
+/* Current position (number of cached positions), or -1 for a NULL handle.
+ * Library bookkeeping; no passage of the pages. */
 int32_t dec_position(const dec_handle* h);
 
 /*
  * Copy cached keys and values of positions [0, n_pos) of one layer and one
  * sequence to host memory as fp16 bits, each [n_heads, n_pos, head_dim].
- * Either output may be NULL.  For tests and inspection; synchronous.
+ * Either output may be NULL.  For tests and inspection; synchronous.  The
+ * cache is the KV term of the bandwidth bound (page 標準GPUによるリアルタイム
+ * LLM推論, section GPU推論の速度制限要因：メモリ帯域幅).
  */
 int dec_read_kv(dec_handle* h, int32_t layer, int32_t seq, int32_t n_pos,
                 uint16_t* host_k, uint16_t* host_v);
@@ -269,10 +313,13 @@ int dec_read_kv(dec_handle* h, int32_t layer, int32_t seq, int32_t n_pos,
  * (stamps beyond `stride` are dropped).  *out_grid and *out_stride receive
  * the grid and the stride; *out_hz the clock rate.  host: uint64
  * [grid*stride] or NULL to query the sizes only.  Synchronous.
+ * Measurement aid for finding where the microseconds of a step go (page
+ * 標準GPUによるリアルタイムLLM推論, section Kog Inference Engineの特徴とイノベーション).
  */
 int dec_read_trace(dec_handle* h, uint64_t* host, int32_t* out_grid, int32_t* out_stride, double* out_hz);
 
-/* Release every resource of the handle (not a caller arena or stream). */
+/* Release every resource of the handle (not a caller arena or stream).
+ * Library bookkeeping; no passage of the pages. */
 void dec_free(dec_handle* h);
 
 /*
@@ -299,6 +346,7 @@ int dec_stream_ceiling(int32_t device, uint64_t bytes, int32_t reps, double* out
 /*
  * Last error text of the handle, or of the calling thread's last failed
  * handle-less call (dec_init, dec_check_desc, ...) when h == NULL.  Never NULL.
+ * Library bookkeeping; no passage of the pages.
  */
 const char* dec_last_error(const dec_handle* h);
 
@@ -324,6 +372,8 @@ const char* dec_last_error(const dec_handle* h);
  * element offset 8*l are row 16g + l%16, columns 32j + 8*(l/16) .. +7, for
  * l = 0..63.  Rows and columns past the matrix are zero; each matrix region
  * is ceil(rows/16) * ceil(cols/32) * 512 elements.
+ * The weight pre-pack into the layout the kernel streams (page
+ * 標準GPUによるリアルタイムLLM推論, section Kog Inference Engineの特徴とイノベーション).
  */
 int dec_packed_bytes(const dec_model_desc* desc, size_t* out_bytes);
 int dec_pack(const dec_model_desc* desc, const uint16_t* const* host_tensors,

@@ -224,7 +224,10 @@ class Decoder:
         return self._lib.dec_position(self._h)
 
     def prefill(self, tokens, want_logits=False):
+        """tokens: [batch, n] (or n tokens at batch 1), sequence-major."""
         t = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+        if t.size == 0 or t.size % self.desc.batch:
+            raise ValueError(f"{t.size} prompt tokens do not split into {self.desc.batch} equal sequences")
         n = t.size // self.desc.batch
         out = np.zeros(self.desc.batch, dtype=np.int32)
         lg = np.zeros(self.desc.batch * self.desc.lm_vocab, dtype=np.float32) if want_logits else None
@@ -235,7 +238,9 @@ class Decoder:
     def step(self, force_tok=None, want_tok=True, want_logits=False):
         ft = None
         if force_tok is not None:
-            ft = np.ascontiguousarray(np.atleast_1d(force_tok), dtype=np.int32)
+            ft = np.ascontiguousarray(np.atleast_1d(force_tok), dtype=np.int32).reshape(-1)
+            if ft.size != self.desc.batch:
+                raise ValueError(f"force_tok holds {ft.size} tokens; the batch is {self.desc.batch}")
         out = np.zeros(self.desc.batch, dtype=np.int32) if want_tok else None
         lg = np.zeros(self.desc.batch * self.desc.lm_vocab, dtype=np.float32) if want_logits else None
         self._rc(self._lib.dec_step(self._h, ft.ctypes.data_as(_i32p) if ft is not None else None,

@@ -364,8 +364,16 @@ int hip_fail(dec_handle* h, std::string* err, hipError_t e, const char* what) {
 }
 #define HIPCHK(h, err, call) do { hipError_t e_ = (call); if (e_ != hipSuccess) return hip_fail(h, err, e_, #call); } while (0)
 
-int launch(dec_handle* h, int pos0, int n_tok, int tok_src, int lm_last_only, int write_logits) {
+int launch(dec_handle* h, int pos0, int n_tok, int tok_src, int lm_last_only, int write_logits,
+           const int32_t* force = nullptr) {
   Launch A;
+  std::memset(&A, 0, sizeof A);
+  // forced input tokens travel in the launch arguments, which are copied when
+  // the kernel is enqueued: the caller's array is not read after this call
+  if (force) {
+    A.n_force = 1;
+    for (int b = 0; b < h->desc.batch; ++b) A.force[b] = force[b];
+  }
   A.pos0 = pos0;
   A.n_tok = n_tok;
   A.tok_src = tok_src;
@@ -401,6 +409,7 @@ int launch(dec_handle* h, int pos0, int n_tok, int tok_src, int lm_last_only, in
 int launch_prefill(dec_handle* h, int n, int write_logits) {
   const int pos0 = 0, n_tok = (n + kMaxBatch - 1) / kMaxBatch, tok_src = TOK_PROMPT, lm_last_only = 1;
   Launch A;
+  std::memset(&A, 0, sizeof A);
   A.pos0 = pos0;
   A.n_tok = n_tok;
   A.tok_src = tok_src;
@@ -881,10 +890,8 @@ int dec_step(dec_handle* h, const int32_t* force_tok, int32_t* out_tok, float* o
       if (force_tok[b] < 0 || force_tok[b] >= h->desc.vocab)
         return fail(&h->err, DEC_ERR_TOKEN_RANGE, "token %d of sequence %d outside [0, %d)", force_tok[b], b,
                     h->desc.vocab);
-    HIPCHK(h, &h->err, hipMemcpyAsync(h->P.tok_cur, force_tok, (size_t)h->desc.batch * 4, hipMemcpyHostToDevice,
-                                      h->stream));
   }
-  int rc = launch(h, h->pos, 1, TOK_DEVICE, 0, out_logits != nullptr);
+  int rc = launch(h, h->pos, 1, TOK_DEVICE, 0, out_logits != nullptr, force_tok);
   if (rc) return rc;
   h->pos += 1;
   h->has_prev_tok = true;

@@ -99,6 +99,8 @@ struct Launch {
   int phase_begin;   // run only phases with global index in [phase_begin, phase_end)
   int phase_end;
   int pos_end;       // positions at or past pos_end are not computed (the ragged last step of a batched prefill)
+  int n_force;       // 1: the first token's inputs are force[0..batch) instead of *tok_cur (teacher forcing)
+  int force[kMaxBatch];
 };
 
 DEC_HD inline int phases_per_token(int L) { return kPhasesPerLayer * L + 2; }

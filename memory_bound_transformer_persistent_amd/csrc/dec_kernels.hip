@@ -1589,6 +1589,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
               if (!P.cols_pos) tok = ldg(P.prompt + (size_t)b * A.n_tok + id.i);
               else tok = pos + b < A.pos_end ? ldg(P.prompt + (pos + b - A.pos0)) : 0;
             }
+            else if (A.n_force && id.i == 0) tok = A.force[b];   // teacher forcing: the launch argument
             else tok = have_tok ? tok_local[b] : ld_coh(P.tok_cur + b);
             tok = tok < 0 ? 0 : (tok >= P.V ? P.V - 1 : tok);
             w0_embed<MB>(P, b, tok, MB == 1 ? xs : stage + (size_t)b * gemv_span(P.d), xown, own);
