@@ -238,6 +238,34 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights,
              const dec_init_opts* opts, dec_handle** out);
 
 /*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Creates the
+ * same handle as dec_init, and every other call works on it unchanged, but:
+ *   - opts, opts->arena and opts->stream are required (else
+ *     DEC_ERR_INVALID_ARG).  The arena holds the weights, gains, rotary table
+ *     and KV cache; an arena of dec_arena_bytes() bytes is always large
+ *     enough, and only its leading part is used;
+ *   - the kernels' scratch -- residual stream and the other exchange vectors,
+ *     attention and argmax partials, logits, token buffers, barrier counters,
+ *     the device copies of the parameter block and (DEC_DEBUG_TRACE) the
+ *     trace -- lives in a fixed array inside the library,
+ *     DEC_NOALLOC_SCRATCH_BYTES per device, which that device holds until the
+ *     process exits.  A description whose scratch is larger is rejected with
+ *     DEC_ERR_UNSUPPORTED (the 2.3B shape needs about 1 MiB at batch 1 and
+ *     4 MiB at batch 8; the trace adds 8 MiB at 256 workgroups).
+ * Neither this call nor any later call on the handle allocates device memory
+ * (no hipMalloc, hipFree or allocating library routine).  Init clears the
+ * part of the array it uses: a previous user's contents are never read.  A
+ * device has one array, so one no-allocation handle at a time may use it:
+ * while one is alive, dec_init_noalloc on the same device returns
+ * DEC_ERR_STATE (two handles would race on the shared array); dec_free
+ * releases it.  Other errors as dec_init.
+ */
+#define DEC_NOALLOC_SCRATCH_BYTES (16u << 20)
+int dec_init_noalloc(const dec_model_desc* desc, const dec_weights_src* weights,
+                     const dec_init_opts* opts, dec_handle** out);
+
+/*
  * Prefill: requires position 0 (fresh or after dec_reset), else
  * DEC_ERR_STATE.  tokens: host int32 [batch * n] (sequence-major), 1 <= n <=
  * max_ctx.  Runs positions 0..n-1 (keys/values of every position enter the

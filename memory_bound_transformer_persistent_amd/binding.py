@@ -84,6 +84,7 @@ SIGNATURES = {
     "dec_check_desc": (ctypes.c_int, [_P(ModelDesc)]),
     "dec_weights_file_check": (ctypes.c_int, [ctypes.c_char_p, _P(ModelDesc)]),
     "dec_init": (ctypes.c_int, [_P(ModelDesc), _P(WeightsSrc), _P(InitOpts), _P(ctypes.c_void_p)]),
+    "dec_init_noalloc": (ctypes.c_int, [_P(ModelDesc), _P(WeightsSrc), _P(InitOpts), _P(ctypes.c_void_p)]),
     "dec_prefill": (ctypes.c_int, [ctypes.c_void_p, _i32p, ctypes.c_int32, _i32p, _f32p]),
     "dec_step": (ctypes.c_int, [ctypes.c_void_p, _i32p, _i32p, _f32p]),
     "dec_generate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, _i32p]),
@@ -182,7 +183,9 @@ class Decoder:
     """One handle of the decode library (one device, one stream)."""
 
     def __init__(self, desc, tensors=None, path=None, device=0, stream=None, grid=0,
-                 debug_flags=0, watchdog_us=0, arena=None, arena_bytes=0):
+                 debug_flags=0, watchdog_us=0, arena=None, arena_bytes=0, noalloc=False):
+        """noalloc: dec_init_noalloc (needs arena, arena_bytes and stream; the
+        library allocates no device memory for this handle)."""
         lib = load()
         self.desc = desc
         src = WeightsSrc()
@@ -196,7 +199,8 @@ class Decoder:
         opts = InitOpts(device=device, grid=grid, stream=stream, arena=arena, arena_bytes=arena_bytes,
                         debug_flags=debug_flags, watchdog_us=watchdog_us)
         h = ctypes.c_void_p()
-        rc = lib.dec_init(ctypes.byref(desc), ctypes.byref(src), ctypes.byref(opts), ctypes.byref(h))
+        init = lib.dec_init_noalloc if noalloc else lib.dec_init
+        rc = init(ctypes.byref(desc), ctypes.byref(src), ctypes.byref(opts), ctypes.byref(h))
         del keep
         _check(rc)
         self._h = h

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -343,6 +344,10 @@ struct dec_handle {
   bool own_stream = false;
   void* base = nullptr;
   bool own_arena = false;
+  // device address of the arena's scratch part (offsets from ar.x on): inside
+  // the arena, or the fixed no-allocation array (dec_init_noalloc)
+  char* scr = nullptr;
+  bool noalloc = false;    // holds this device's fixed scratch array
   Arena ar;
   Image im;
   Params P;               // host copy
@@ -357,6 +362,9 @@ struct dec_handle {
 };
 
 namespace {
+
+// Which devices' fixed scratch arrays a live no-allocation handle holds.
+std::atomic<bool> g_scratch_held[kMaxDevices];
 
 int hip_fail(dec_handle* h, std::string* err, hipError_t e, const char* what) {
   if (h) h->broken = true;
@@ -623,7 +631,17 @@ int dec_weights_file_check(const char* path, dec_model_desc* out_desc) {
   return rc;
 }
 
-int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const dec_init_opts* opts, dec_handle** out) {
+}  // extern "C"
+#pragma GCC visibility pop
+
+namespace {
+
+// dec_init and dec_init_noalloc.  noalloc: the caller's arena holds the
+// weights, gains, rotary table and KV cache (the arena's leading part, up to
+// ar.x); the rest of the layout (ar.x .. ) lives in this device's fixed
+// scratch array instead, and no device memory is allocated.
+int init_impl(const dec_model_desc* desc, const dec_weights_src* weights, const dec_init_opts* opts, dec_handle** out,
+              bool noalloc) {
   if (!out) return fail(nullptr, DEC_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   int rc = check_desc_impl(desc, nullptr);
@@ -651,6 +669,11 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
   if (opts) o = *opts;
   if (o.grid < 0 || o.grid > 1024) return fail(nullptr, DEC_ERR_INVALID_ARG, "grid must be in [0, 1024]");
   if (o.watchdog_us < 0) return fail(nullptr, DEC_ERR_INVALID_ARG, "watchdog_us must be >= 0");
+  if (noalloc && (!o.arena || !o.stream))
+    return fail(nullptr, DEC_ERR_INVALID_ARG, "dec_init_noalloc needs a caller arena and a caller stream");
+  if (noalloc && (o.device < 0 || o.device >= kMaxDevices))
+    return fail(nullptr, DEC_ERR_NO_DEVICE, "device %d is past the %d devices the fixed scratch serves", o.device,
+                kMaxDevices);
 
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return fail(nullptr, DEC_ERR_NO_DEVICE, "no HIP device visible");
@@ -734,10 +757,19 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
   }
   h->im = image_layout(*desc);
   h->ar = arena_layout(*desc, h->grid);
+  // the scratch part: everything from the residual stream on (the trace only when asked for)
+  const size_t scratch_end = (h->debug & DEC_DEBUG_TRACE) ? h->ar.total : h->ar.trace;
+  const size_t scratch_bytes = scratch_end - h->ar.x;
+  if (noalloc && scratch_bytes > kNoallocScratchBytes) {
+    fail(&h->err, DEC_ERR_UNSUPPORTED, "this description needs %zu bytes of scratch; the fixed no-allocation array "
+         "holds %zu", scratch_bytes, kNoallocScratchBytes);
+    return bail(DEC_ERR_UNSUPPORTED);
+  }
+  const size_t need = noalloc ? h->ar.x : h->ar.total;
   if (o.arena) {
     if (reinterpret_cast<uintptr_t>(o.arena) % kAlign) { fail(&h->err, DEC_ERR_INVALID_ARG, "arena is not 256-byte aligned"); return bail(DEC_ERR_INVALID_ARG); }
-    if (o.arena_bytes < h->ar.total) {
-      fail(&h->err, DEC_ERR_OOM, "arena of %zu bytes is smaller than the %zu needed", o.arena_bytes, h->ar.total);
+    if (o.arena_bytes < need) {
+      fail(&h->err, DEC_ERR_OOM, "arena of %zu bytes is smaller than the %zu needed", o.arena_bytes, need);
       return bail(DEC_ERR_OOM);
     }
     h->base = o.arena;
@@ -751,9 +783,29 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
     h->own_arena = true;
   }
   char* b = static_cast<char*>(h->base);
-  // zero activations and control words (weights and cache are overwritten)
-  e = hipMemset(b + h->ar.x, 0, h->ar.total - h->ar.x);
-  if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemset"); return bail(DEC_ERR_DEVICE); }
+  if (noalloc) {
+    bool held = false;
+    if (!g_scratch_held[o.device].compare_exchange_strong(held, true)) {
+      fail(&h->err, DEC_ERR_STATE, "another no-allocation handle holds device %d's scratch array", o.device);
+      return bail(DEC_ERR_STATE);
+    }
+    h->noalloc = true;
+    void* p = nullptr;
+    e = (hipError_t)kernel_scratch(o.device, &p);
+    if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipGetSymbolAddress(scratch)"); return bail(DEC_ERR_DEVICE); }
+    h->scr = static_cast<char*>(p);
+    // the array keeps its previous user's contents: clear what this handle uses
+    e = hipMemsetAsync(h->scr, 0, scratch_bytes, h->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+    if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemsetAsync(scratch)"); return bail(DEC_ERR_DEVICE); }
+  } else {
+    h->scr = b + h->ar.x;
+    // zero activations and control words (weights and cache are overwritten)
+    e = hipMemset(h->scr, 0, h->ar.total - h->ar.x);
+    if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemset"); return bail(DEC_ERR_DEVICE); }
+  }
+  // device address of a scratch-part offset of the layout
+  auto sc = [&](size_t off) { return h->scr + (off - h->ar.x); };
   rc = upload_weights(h, weights);
   if (rc) return bail(rc);
   // rotary table: cos/sin(p * base^(-2i/hd)) in double, stored as fp32
@@ -787,28 +839,28 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
   P.rope = reinterpret_cast<const float*>(b + h->ar.rope);
   P.B = desc->batch;
   P.kv = reinterpret_cast<uint16_t*>(b + h->ar.kv);
-  P.x = reinterpret_cast<float*>(b + h->ar.x);
-  P.qkv = reinterpret_cast<float*>(b + h->ar.qkv);
-  P.att_o = reinterpret_cast<float*>(b + h->ar.att_o);
-  P.att_o16 = reinterpret_cast<uint16_t*>(b + h->ar.att_o);
-  P.part = reinterpret_cast<float*>(b + h->ar.part);
-  P.pml = reinterpret_cast<float*>(b + h->ar.pml);
-  P.act = reinterpret_cast<float*>(b + h->ar.act);
-  P.act16 = reinterpret_cast<uint16_t*>(b + h->ar.act);
-  P.logits = reinterpret_cast<float*>(b + h->ar.logits);
-  P.amax_v = reinterpret_cast<float*>(b + h->ar.amax_v);
-  P.amax_i = reinterpret_cast<int*>(b + h->ar.amax_i);
-  P.tok_cur = reinterpret_cast<int*>(b + h->ar.tok_cur);
-  P.tok_out = reinterpret_cast<int*>(b + h->ar.tok_out);
-  P.prompt = reinterpret_cast<const int*>(b + h->ar.prompt);
-  P.ctl = reinterpret_cast<uint32_t*>(b + h->ar.ctl);
+  P.x = reinterpret_cast<float*>(sc(h->ar.x));
+  P.qkv = reinterpret_cast<float*>(sc(h->ar.qkv));
+  P.att_o = reinterpret_cast<float*>(sc(h->ar.att_o));
+  P.att_o16 = reinterpret_cast<uint16_t*>(sc(h->ar.att_o));
+  P.part = reinterpret_cast<float*>(sc(h->ar.part));
+  P.pml = reinterpret_cast<float*>(sc(h->ar.pml));
+  P.act = reinterpret_cast<float*>(sc(h->ar.act));
+  P.act16 = reinterpret_cast<uint16_t*>(sc(h->ar.act));
+  P.logits = reinterpret_cast<float*>(sc(h->ar.logits));
+  P.amax_v = reinterpret_cast<float*>(sc(h->ar.amax_v));
+  P.amax_i = reinterpret_cast<int*>(sc(h->ar.amax_i));
+  P.tok_cur = reinterpret_cast<int*>(sc(h->ar.tok_cur));
+  P.tok_out = reinterpret_cast<int*>(sc(h->ar.tok_out));
+  P.prompt = reinterpret_cast<const int*>(sc(h->ar.prompt));
+  P.ctl = reinterpret_cast<uint32_t*>(sc(h->ar.ctl));
   P.max_chunks = max_attn_chunks(desc->max_ctx, desc->batch * desc->n_heads, h->grid);
   P.watchdog_ticks = (uint32_t)std::min(ticks, 4.0e9);
-  P.trace = (h->debug & DEC_DEBUG_TRACE) ? reinterpret_cast<uint64_t*>(b + h->ar.trace) : nullptr;
+  P.trace = (h->debug & DEC_DEBUG_TRACE) ? reinterpret_cast<uint64_t*>(sc(h->ar.trace)) : nullptr;
   P.trace_stride = kTraceStride;
   h->wall_hz = (double)wall_khz * 1000.0;
   P.cols_pos = 0;
-  h->dP = reinterpret_cast<Params*>(b + h->ar.params);
+  h->dP = reinterpret_cast<Params*>(sc(h->ar.params));
   e = hipMemcpy(h->dP, &P, sizeof(Params), hipMemcpyHostToDevice);
   if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemcpy(params)"); return bail(DEC_ERR_DEVICE); }
   if (batched_prefill(*desc)) {
@@ -823,7 +875,7 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
     P2.B = kMaxBatch;
     P2.cols_pos = 1;
     P2.max_chunks = max_attn_chunks(desc->max_ctx, kMaxBatch * desc->n_heads, h->grid);
-    h->dP2 = reinterpret_cast<Params*>(b + h->ar.params2);
+    h->dP2 = reinterpret_cast<Params*>(sc(h->ar.params2));
     e = hipMemcpy(h->dP2, &P2, sizeof(Params), hipMemcpyHostToDevice);
     if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemcpy(params)"); return bail(DEC_ERR_DEVICE); }
     per_cu = 0;
@@ -836,6 +888,20 @@ int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const d
   if (hipDeviceSynchronize() != hipSuccess) { fail(&h->err, DEC_ERR_DEVICE, "device synchronize failed after upload"); return bail(DEC_ERR_DEVICE); }
   *out = h;
   return DEC_OK;
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+int dec_init(const dec_model_desc* desc, const dec_weights_src* weights, const dec_init_opts* opts, dec_handle** out) {
+  return init_impl(desc, weights, opts, out, false);
+}
+
+int dec_init_noalloc(const dec_model_desc* desc, const dec_weights_src* weights, const dec_init_opts* opts,
+                     dec_handle** out) {
+  return init_impl(desc, weights, opts, out, true);
 }
 
 int dec_prefill(dec_handle* h, const int32_t* tokens, int32_t n, int32_t* out_tok, float* out_logits) {
@@ -1013,6 +1079,7 @@ int dec_read_trace(dec_handle* h, uint64_t* host, int32_t* out_grid, int32_t* ou
 void dec_free(dec_handle* h) {
   if (!h) return;
   if (h->stream) (void)hipStreamSynchronize(h->stream);
+  if (h->noalloc) g_scratch_held[h->device] = false;   // the fixed scratch array is free again
   if (h->own_arena && h->base) (void)hipFree(h->base);
   if (h->own_stream && h->stream) (void)hipStreamDestroy(h->stream);
   delete h;

@@ -37,6 +37,13 @@ constexpr int kTileElems = kTileRows * kTileCols;
 constexpr int kLdsBytes = 160 * 1024;       // dynamic LDS per workgroup; > half a CU's 160 KB,
                                             // so exactly one workgroup runs per compute unit
 
+// The no-allocation handle (dec_init_noalloc) keeps its scratch -- everything
+// in the arena from the residual stream on: exchange vectors, partials,
+// logits, token buffers, control words, parameter blocks, trace -- in a
+// fixed device array of this size, one per device.
+constexpr size_t kNoallocScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+
 // Control words (uint32 index into Params::ctl); each on its own 256-byte line.
 constexpr int kCtlGlobal = 0;               // arrivals of group leaders (cumulative)
 constexpr int kCtlGroup0 = 64;              // group k counter at kCtlGroup0 + 64*k
@@ -155,5 +162,8 @@ int kernel_launch_plain(const Params* P, const Launch& A, int grid, int batch, i
 // Stream-ceiling read of n16 16-byte words at src on the null stream; out
 // holds grid * kThreads words.
 int kernel_stream_read(const void* src, uint64_t n16, uint32_t* out, int grid);
+// Device address of the fixed no-allocation scratch array (kNoallocScratchBytes)
+// on `device`, which must be the current device; looked up once per device.
+int kernel_scratch(int device, void** out);
 
 }  // namespace decmono

@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "dec_internal.h"
 
 namespace decmono {
@@ -1742,6 +1744,31 @@ extern "C" __global__ __launch_bounds__(kThreads) void dec_stream_read(const u32
 int kernel_stream_read(const void* src, uint64_t n16, uint32_t* out, int grid) {
   hipLaunchKernelGGL(dec_stream_read, dim3(grid), dim3(kThreads), 0, 0, static_cast<const u32x4*>(src), n16, out);
   return (int)hipGetLastError();
+}
+
+// Scratch of the no-allocation handle (dec_init_noalloc), for callers that
+// cannot allocate device memory: one fixed array per device that holds a
+// handle's exchange vectors, partial results, barrier counters and parameter
+// blocks, kept until the process ends.  In host code the array's name is not
+// a device address: the runtime is asked for that address once per device
+// (with the device current), and only the pointer it returns is used --
+// inside the parameter block the kernels receive, and for clearing.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+int kernel_scratch(int device, void** out) {
+  static void* addr[kMaxDevices] = {};
+  static std::mutex mu;
+  if (device < 0 || device >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    addr[device] = p;
+  }
+  *out = addr[device];
+  return (int)hipSuccess;
 }
 
 int kernel_prepare() {
