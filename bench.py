@@ -1,23 +1,31 @@
 """Decode benchmark: tokens/s per request at batch 1 on one MI355X.
 
-Workload (default "dense2b"): a 25-layer dense decoder, d_model 2560, 20 heads
-x 128, SwiGLU 6912, vocab 65536, fp16 weights drawn N(0, 0.02) from fixed
-seeds; a 128-token random prompt is prefilled, then the timed region is the
-512 greedy decode steps at positions 128..639.  One step = one decode token
-= one pass over every active weight (the whole hot path).  --workload
-dense2b_b8 decodes 8 independent sequences together (256-token prompts):
-`value` is then the whole-job tokens/s (8 per step) and
-tokens_per_s_per_request the rate each sequence sees.
+Main line (the metric): the dense2b workload -- a 25-layer dense decoder,
+d_model 2560, 20 heads x 128, SwiGLU 6912, vocab 65536, fp16 weights drawn
+N(0, 0.02) from fixed seeds; the 128-token random prompt is prefilled, then
+the timed region is K greedy decode steps (default 512, positions 128..639),
+one dec_step launch per token with the token fed back on the device.  One
+step = one pass over every active weight (the whole hot path).
 
-Prints one JSON line.  The roofline object prices the resident decode kernel
-against MI355X's 8 TB/s HBM peak with ALGORITHMIC bytes per launch: every
-weight byte once, one embedding row, the KV-cache rows attention reads at
-that position and the rows it appends.  stream_ceiling is the measured read
-rate of a plain 16-byte non-temporal stream over 2 GiB on the same device
-(dec_stream_ceiling) and the decode rate as a fraction of it.  generate is the
-same positions decoded in one dec_generate launch (not the metric: it shows
-what the per-token launch costs).  The cpu_baseline object times the
-CPU oracle (test infrastructure) on a bounded sample of the same workload.
+The same JSON line also carries, each measured in this run on its own handle:
+  workloads.lane2b        one lane of an 8-way split (3 heads, FFN 864, an
+                          8192-row LM shard): 128-token prompt + 1024 steps
+  workloads.dense2b_long  a 3968-token prompt through the batched prefill,
+                          then 128 steps to the 4096 cap
+  workloads.dense2b_b8    8 sequences of 256-token prompts, 256 steps together
+                          (value = tokens/s of all 8; per request = of each)
+  ttft                    time to first token of the 128-token prompt: one
+                          position per step (the decode kernel) and batched
+                          (8 positions per step on the matrix-core kernel)
+  generate                the main span in one dec_generate launch
+  stream_ceiling          a plain 16-byte non-temporal read of 2 GiB
+  cpu_baseline            the CPU oracle on a bounded sample of the same steps
+
+Every roofline object prices its kernel against MI355X's 8 TB/s HBM peak with
+ALGORITHMIC bytes per launch (every weight byte once, one embedding row per
+sequence, the KV-cache rows attention reads at that position and the rows it
+appends) divided by the kernel's average launch duration, measured with HIP
+events on the kernel's own stream around back-to-back launches.
 """
 import argparse
 import hashlib
@@ -32,6 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode tokens/s per request (bs=1) and achieved HBM GB/s vs peak, 1 MI355X"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_dec_resident_dense2b.txt")
 KERNEL_SRC = os.path.join(ROOT, "memory_bound_transformer_persistent_amd", "csrc", "dec_kernels.hip")
+EXTRAS = ("lane2b", "dense2b_long", "dense2b_b8")
 
 
 def kernel_hash():
@@ -56,28 +65,135 @@ def read_traffic(workload):
         return None
 
 
-def cpu_baseline(shape, tensors, prompt_len, n_steps):
-    """The oracle, untouched, on a bounded sample: a short prompt then n_steps decode steps."""
-    import numpy as np
-    import oracle as O
-    import synth
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: report the process's CPU count
-        threads = os.cpu_count() or 1
-    prompt = synth.make_prompt(shape.vocab, prompt_len, seed=1)[0]
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: the process's CPU count
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(shape, tensors, prompt, n_steps):
+    """The oracle, untouched, on a bounded sample of the main workload's own steps:
+    the same 128-token prompt (prefilled untimed with the oracle's matrix form),
+    then the first n_steps greedy decode steps at positions 128.. (the oracle's
+    greedy tokens, which equal the GPU's up to near-ties), timed."""
+    import oracle as O
+    n0 = len(prompt)
     lg, K16, V16, _ = O.prefill_matrix(shape, tensors, prompt)
     dec = O.OracleDecoder(shape, tensors)
-    dec.load_cache(K16, V16, prompt_len)
+    dec.load_cache(K16, V16, n0)
     tok = O.greedy(lg[-1])
     t0 = time.perf_counter()
     for _ in range(n_steps):
         tok = O.greedy(dec.step(tok))
     dt = time.perf_counter() - t0
-    return {"value": round(n_steps / dt, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_steps} greedy decode steps of the same model after a {prompt_len}-token prompt "
-                      f"(float64 NumPy oracle; prompt prefill untimed); {dt:.1f} s"}
+    return {"value": round(n_steps / dt, 4), "unit": "tokens/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"{n_steps} greedy decode steps at positions {n0}..{n0 + n_steps - 1} of the main workload "
+                      f"after its {n0}-token prompt (prompt prefilled untimed with the oracle's matrix form); "
+                      f"float64 NumPy oracle, {blas_threads()} BLAS threads; {dt:.1f} s"}
+
+
+class Run:
+    """One handle of one workload, timed on its own stream."""
+
+    def __init__(self, B, R, torch, w, tensors, stream, flags=0, debug=0):
+        self.B, self.R, self.torch, self.w, self.stream = B, R, torch, w, stream
+        self.s, self.nb = w.shape, w.batch
+        import synth
+        self.prompt = synth.make_prompt(self.s.vocab, w.prompt_len, batch=self.nb, seed=w.prompt_seed)
+        self.dec = B.Decoder(B.ModelDesc.from_shape(self.s, batch=self.nb, flags=flags), tensors=tensors, device=0,
+                             stream=stream.cuda_stream, debug_flags=debug)
+
+    def ev(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def warm(self, steps):
+        self.dec.prefill(self.prompt)
+        for _ in range(steps):
+            self.dec.step(want_tok=False)
+        self.dec.sync()
+        self.dec.reset()
+
+    def prefill_ms(self):
+        """Time to first token: the prompt's prefill, HIP events on the handle's stream."""
+        a, b = self.ev(), self.ev()
+        self.torch.cuda.synchronize()
+        a.record(self.stream)
+        self.dec.prefill(self.prompt)
+        b.record(self.stream)
+        b.synchronize()
+        return a.elapsed_time(b)
+
+    def decode(self, K, nseg=4, mode="step"):
+        """K steps from the current position; (region ms, per-segment tokens/s)."""
+        torch, dec = self.torch, self.dec
+        nseg = nseg if mode == "step" and K >= 8 else 1
+        bounds = [K * j // nseg for j in range(nseg + 1)]
+        evs = [self.ev() for _ in range(nseg + 1)]
+        torch.cuda.synchronize()
+        # events only around the region and its segments: an event between
+        # every two launches would add about 5 us per step; the launches run
+        # back to back, so the average launch duration is the region over K
+        evs[0].record(self.stream)
+        if mode == "generate":
+            dec.generate(K)
+            evs[1].record(self.stream)
+        else:
+            for j in range(nseg):
+                for _ in range(bounds[j], bounds[j + 1]):
+                    dec.step(want_tok=False)
+                evs[j + 1].record(self.stream)
+        evs[-1].synchronize()
+        dec.sync()
+        region = evs[0].elapsed_time(evs[-1])
+        segs = [(bounds[j + 1] - bounds[j]) * self.nb / (evs[j].elapsed_time(evs[j + 1]) / 1e3) for j in range(nseg)]
+        return region, segs
+
+    def record(self, pos0, K, region_ms, kernel):
+        R, s, nb = self.R, self.s, self.nb
+        per_launch = R.mean_step_bytes(s, pos0, K, nb)
+        avg_s = region_ms / K / 1e3
+        achieved = per_launch / avg_s / 1e9
+        req = K / (region_ms / 1e3)
+        return {
+            "tokens_per_s": round(req * nb, 2), "tokens_per_s_per_request": round(req, 2),
+            "ms_per_step": round(region_ms / K, 4), "positions": [pos0, pos0 + K - 1], "batch": nb,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": R.MI355X_HBM_PEAK / 1e9,
+                         "unit": "GB/s", "frac": round(achieved / (R.MI355X_HBM_PEAK / 1e9), 4),
+                         "kernel": kernel, "algorithmic_bytes_per_launch": int(per_launch),
+                         "avg_launch_ms": round(avg_s * 1e3, 4)},
+            "roofline_tokens_per_s_per_request": round(R.roofline_tokens_per_s(s, pos0, K, nb), 1),
+        }
+
+    def close(self):
+        self.dec.close()
+
+
+def kernel_name(w):
+    return f"dec_resident_{'batch_' if w.batch > 1 else ''}hd{w.shape.head_dim}"
+
+
+def extra_workload(B, R, torch, name, full_tensors, stream, warmup):
+    """One of the other configurations, at its own prompt and step count."""
+    import synth
+    w = synth.workload(name)
+    tensors = synth.lane_from_full(w.shape, full_tensors) if w.lane else full_tensors
+    bp = name == "dense2b_long"      # the long prompt goes through the batched prefill
+    r = Run(B, R, torch, w, tensors, stream, flags=B.DEC_FLAG_BATCHED_PREFILL if bp else 0)
+    try:
+        r.warm(warmup)
+        pre = r.prefill_ms()
+        pos0 = r.dec.position
+        region, segs = r.decode(w.steps)
+        out = r.record(pos0, w.steps, region, kernel_name(w))
+        out["prefill"] = {"tokens": w.prompt_len, "sequences": w.batch, "ms": round(pre, 3),
+                          "mode": "batched, 8 positions per step" if bp else "one position per step"}
+        out["workload"] = f"{w.name}: {w.description}; prompt {w.prompt_len} + {w.steps} greedy steps, batch {w.batch}"
+        out["segments_tokens_per_s"] = [round(x, 1) for x in segs]
+        return out
+    finally:
+        r.close()
 
 
 def main():
@@ -85,16 +201,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="dense2b")
+    ap.add_argument("--workload", default="dense2b", help="main line's workload (the others run only for dense2b)")
     ap.add_argument("--mode", choices=["step", "generate"], default="step",
                     help="step: one dec_step launch per token (token fed back on the device); "
                          "generate: all timed steps inside one dec_generate launch")
     ap.add_argument("--cpu-steps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="only the main line (profiling runs)")
     ap.add_argument("--multilaunch", action="store_true", help="one kernel launch per phase (comparison)")
     ap.add_argument("--batched-prefill", action="store_true",
-                    help="prefill 8 positions per step on the matrix-core kernel (DEC_FLAG_BATCHED_PREFILL); "
-                         "decode is unchanged")
+                    help="main line: prefill 8 positions per step on the matrix-core kernel; decode is unchanged")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run plain device-to-device copies of BYTES (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -127,70 +243,33 @@ def main():
     if w.prompt_len + max(args.steps, args.warmup) > s.max_ctx:
         sys.exit("prompt + steps exceed the context cap")
     t_gen = time.time()
-    tensors = synth.workload_weights(w)
-    nb = w.batch
-    prompt = synth.make_prompt(s.vocab, w.prompt_len, batch=nb, seed=w.prompt_seed)   # [batch, n]
+    if w.name == "tiny":
+        full, tensors = None, synth.workload_weights(w)
+    else:
+        # every other workload uses the 2.3B model's seeded tensors (a lane slices them)
+        full = synth.make_weights(synth.shape_for("dense2b"), seed=0)
+        tensors = synth.lane_from_full(s, full) if w.lane else full
     print(f"# weights generated in {time.time() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.Stream(device=0)
-    flags = B.DEC_DEBUG_MULTILAUNCH if args.multilaunch else 0
-    bp = args.batched_prefill and nb == 1
-    dec = B.Decoder(B.ModelDesc.from_shape(s, batch=nb, flags=B.DEC_FLAG_BATCHED_PREFILL if bp else 0),
-                    tensors=tensors, device=0, stream=stream.cuda_stream,
-                    debug_flags=flags)
-
+    bp = args.batched_prefill and w.batch == 1
+    flags = B.DEC_FLAG_BATCHED_PREFILL if bp else 0
+    r = Run(B, R, torch, w, tensors, stream, flags=flags,
+            debug=B.DEC_DEBUG_MULTILAUNCH if args.multilaunch else 0)
+    K, nb = args.steps, w.batch
     # warm-up: prefill + W steps, then rewind so the timed steps are the workload's positions
-    dec.prefill(prompt)
-    for _ in range(args.warmup):
-        dec.step(want_tok=False)
-    dec.sync()
-    dec.reset()
-    # prefill (time to first token), timed on its own: not part of the metric
-    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    p0.record(stream)
-    first_tok, _ = dec.prefill(prompt)
-    p1.record(stream)
-    p1.synchronize()
-    prefill_ms = p0.elapsed_time(p1)
-    pos0 = dec.position
-
-    K = args.steps
-    torch.cuda.synchronize()
-    # HIP events on the decode stream only around the region and at the
-    # boundaries of four segments: an event between every two launches would
-    # add about 5 us per step.  The launches run back to back, so the average
-    # launch duration is the region over K.
-    nseg = 4 if args.mode == "step" and K >= 8 else 1
-    bounds = [K * j // nseg for j in range(nseg + 1)]
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nseg + 1)]
+    r.warm(args.warmup)
+    prefill_ms = r.prefill_ms()
+    pos0 = r.dec.position
     t0 = time.perf_counter()
-    evs[0].record(stream)
-    if args.mode == "generate":
-        toks = dec.generate(K)
-        evs[1].record(stream)
-    else:
-        for j in range(nseg):
-            for _ in range(bounds[j], bounds[j + 1]):
-                dec.step(want_tok=False)
-            evs[j + 1].record(stream)
-    evs[-1].synchronize()
-    dec.sync()
-    torch.cuda.synchronize()
+    region_ms, segs = r.decode(K, mode=args.mode)
     wall = time.perf_counter() - t0
-    region_ms = evs[0].elapsed_time(evs[-1])
     if args.mode == "generate":
         bytes_per_launch = sum(R.step_bytes(s, pos0 + i, nb).total for i in range(K))
         avg_launch_s = region_ms / 1e3
     else:
         bytes_per_launch = R.mean_step_bytes(s, pos0, K, nb)
         avg_launch_s = region_ms / K / 1e3
-    # the rate of each segment (later segments are at longer contexts)
-    segs = None
-    if nseg > 1:
-        seg_tps = [(bounds[j + 1] - bounds[j]) * nb / (evs[j].elapsed_time(evs[j + 1]) / 1e3) for j in range(nseg)]
-        segs = {"n": nseg, "steps_each": K // nseg, "min": round(min(seg_tps), 2),
-                "median": round(float(np.median(seg_tps)), 2), "max": round(max(seg_tps), 2)}
     req_tok_s = K / (region_ms / 1e3)          # tokens/s of each sequence
     tok_s = req_tok_s * nb                     # whole-job tokens/s
     achieved = bytes_per_launch / avg_launch_s / 1e9
@@ -219,11 +298,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s",
                      "frac": round(achieved / peak, 4),
                      "traffic": traffic,
-                     "kernel": f"dec_resident_{'batch_' if nb > 1 else ''}hd{s.head_dim}",
+                     "kernel": kernel_name(w),
                      "algorithmic_bytes_per_launch": int(bytes_per_launch),
                      "avg_launch_ms": round(avg_launch_s * 1e3, 4)},
         "tokens_per_s_per_request": round(req_tok_s, 2),
-        "segments_tokens_per_s": segs,
+        "segments_tokens_per_s": None if len(segs) < 2 else {
+            "n": len(segs), "steps_each": K // len(segs), "min": round(min(segs), 2),
+            "median": round(float(np.median(segs)), 2), "max": round(max(segs), 2)},
         "prefill": {"tokens": w.prompt_len, "sequences": nb, "ms": round(prefill_ms, 3),
                     "mode": "batched, 8 positions per step" if bp else "one position per step"},
         "roofline_tokens_per_s": round(roof_tps * nb, 1),
@@ -236,25 +317,36 @@ def main():
     if args.mode == "step" and not args.multilaunch:
         # the same positions in one dec_generate launch (context: the step
         # mode's per-launch cost), after the timed region
-        dec.reset()
-        dec.prefill(prompt)
-        torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g0.record(stream)
-        dec.generate(K)
-        g1.record(stream)
-        g1.synchronize()
-        gen_ms = g0.elapsed_time(g1)
+        r.dec.reset()
+        r.dec.prefill(r.prompt)
+        gen_ms, _ = r.decode(K, mode="generate")
         out["generate"] = {"tokens_per_s": round(K * nb / (gen_ms / 1e3), 2), "ms_per_step": round(gen_ms / K, 4),
                            "launches": 1}
-    dec.close()
+    r.close()
+    if w.name == "dense2b" and not args.no_extras and not args.multilaunch:
+        # time to first token of the 128-token prompt, both prefill paths
+        ttft = {"tokens": w.prompt_len}
+        for key, fl in (("one_position_per_step_ms", 0), ("batched_8_per_step_ms", B.DEC_FLAG_BATCHED_PREFILL)):
+            rt = Run(B, R, torch, w, tensors, stream, flags=fl)
+            rt.warm(0)
+            times = []
+            for _ in range(3):
+                times.append(rt.prefill_ms())
+                rt.dec.reset()
+            ttft[key] = round(min(times), 3)
+            rt.close()
+        out["ttft"] = ttft
+        out["workloads"] = {}
+        for name in EXTRAS:
+            print(f"# measuring {name}", file=sys.stderr, flush=True)
+            out["workloads"][name] = extra_workload(B, R, torch, name, full, stream, 8)
     # the plain-stream read rate of this device, the practical ceiling under the 8 TB/s peak
     ceiling = B.stream_ceiling(1 << 31, 5)
     out["stream_ceiling"] = {"GBps": round(ceiling, 1), "bytes": 1 << 31, "reps": 5, "kernel": "dec_stream_read",
                              "decode_frac": round(achieved / ceiling, 4)}
     if not args.no_cpu_baseline:
         print("# running the CPU oracle baseline", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(s, tensors, 16, args.cpu_steps)
+        out["cpu_baseline"] = cpu_baseline(s, tensors, r.prompt[0], args.cpu_steps)
     print(json.dumps(out), flush=True)
 
 

@@ -112,6 +112,28 @@ def lane_slice_weights(lane_shape: ModelShape, full_shape: ModelShape = DENSE_2B
     return out
 
 
+def lane_from_full(lane_shape: ModelShape, full_tensors, full_shape: ModelShape = DENSE_2B):
+    """Lane 0's tensors sliced from an already drawn full model (the same
+    arrays lane_slice_weights draws, without drawing the full model again)."""
+    q, f = lane_shape.qkv_width, lane_shape.d_ffn
+    out = []
+    for name, t in zip(tensor_names(full_shape), full_tensors):
+        base = name.split(".")[0]
+        if base.startswith("g_"):
+            out.append(np.ones(t.shape, dtype=np.float16))
+        elif base == "E":
+            out.append(t)
+        elif base == "W_lm":
+            out.append(np.ascontiguousarray(t[:lane_shape.lm_vocab]))
+        elif base in ("Wq", "Wk", "Wv", "Wg", "Wu"):
+            out.append(np.ascontiguousarray(t[:q if base in ("Wq", "Wk", "Wv") else f]))
+        elif base in ("Wo", "Wd"):
+            out.append(np.ascontiguousarray(t[:, :q if base == "Wo" else f]))
+        else:
+            raise AssertionError(name)
+    return out
+
+
 def make_prompt(vocab: int, n: int, batch: int = 1, seed: int = 1):
     """Uniform random token ids, int32, shape [batch, n]."""
     rng = np.random.default_rng(seed)

@@ -41,3 +41,17 @@ def test_traffic_only_for_the_same_source_and_workload(tmp_path, monkeypatch):
     assert bench.read_traffic("dense2b") is None             # unreadable figure
     monkeypatch.setattr(bench, "PROFILE_TRAFFIC", str(tmp_path / "missing.txt"))
     assert bench.read_traffic("dense2b") is None
+
+
+def test_lane_slices_of_drawn_tensors_equal_the_lane_draw():
+    # bench.py slices one lane's tensors from the full model it already drew;
+    # they must be the arrays synth's own lane generator draws
+    import numpy as np
+    import synth
+    full = synth.shape_for("tiny")
+    lane = full.with_(n_heads=1, d_ffn=128, lm_vocab=512)
+    a = synth.lane_slice_weights(lane, full, seed=3)
+    b = synth.lane_from_full(lane, synth.make_weights(full, seed=3), full)
+    assert len(a) == len(b)
+    for x, y in zip(a, b):
+        assert x.shape == y.shape and np.array_equal(x, y)
