@@ -15,7 +15,7 @@ namespace decmono {
 
 constexpr int kThreads = 512;               // threads per workgroup (8 wave64)
 constexpr int kWaves = kThreads / 64;
-constexpr int kGroups = 8;                  // barrier groups: workgroup b is in group b % 8
+constexpr int kGroups = 63;                 // barrier groups: workgroup b is in group b % 63 (lane 63 of the poll reads the error word)
 constexpr int kMaxK = 8192;                 // longest GEMV row supported (16 pieces per lane)
 constexpr int kChunkMin = 32;               // shortest attention chunk (positions)
 constexpr int kChunkMax = 2048;

@@ -1256,12 +1256,14 @@ __device__ __forceinline__ void warm_gu(const Params& P, const int* tab, int l, 
 // Wave 0 of such a workgroup, once it has arrived at the barrier before O,
 // warms more: for each streamer, the GU blocks just past the row pair the
 // streamer warms itself, up to kW0WarmBlocks of 1 KB, within the streamer's
-// share.  Wave 0 has nothing else in flight there (its first poll simply
-// waits for these loads), so unlike the streamers it can take more without
-// delaying the O phase.  24 blocks per streamer measured best over 128-640
-// positions at d 2560 (16 and 32 were slower; at the shortest contexts the
-// gap is too short for all of them to land).
-constexpr int kW0WarmBlocks = 24;
+// share.  Wave 0 has nothing else in flight there, but its first poll for the
+// O release waits behind these loads, so they must land within the attention
+// window.  12 blocks per streamer measured best over positions 128-639 at
+// d 2560 with 63 barrier groups: 24 held the O release back by about 3 us,
+// 8 and 10 warmed too little.  With the streamers' own row pair that warms
+// about 33 MB of GU rows per layer over the 236 workgroups without a head,
+// close to the 32 MB of L2, so few warmed rows are evicted and fetched again.
+constexpr int kW0WarmBlocks = 12;
 __device__ __forceinline__ void w0_warm_gu(const Params& P, const int* tab_all, int l, float* sink) {
   const int lane = threadIdx.x & 63;
   const int* e0 = tab_all + PH_GU * kTabStride;
