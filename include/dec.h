@@ -159,6 +159,16 @@ typedef struct dec_weights_src {
                                        "one launch per op" stack, for comparison) */
 #define DEC_DEBUG_TRACE 0x2u        /* record per-phase wall-clock stamps (see
                                        dec_read_trace) */
+#define DEC_DEBUG_FENCED 0x4u       /* also issue agent-scope release and acquire
+                                       fences around every grid barrier; results
+                                       are bitwise those of the default path */
+#define DEC_DEBUG_STRESS 0x8u       /* barrier stress: each workgroup waits a
+                                       pseudo-random 0-2 us before every arrival,
+                                       and every exchange buffer is filled with
+                                       NaN between its last read and its next
+                                       write; results are bitwise those of the
+                                       default path unless a read races a write.
+                                       Not with DEC_DEBUG_MULTILAUNCH. */
 
 /*
  * Init options (NULL = all defaults).

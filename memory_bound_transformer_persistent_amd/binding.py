@@ -28,6 +28,8 @@ DEC_ERR_TIMEOUT = -10
 DEC_ERR_UNSUPPORTED = -11
 DEC_DEBUG_MULTILAUNCH = 0x1
 DEC_DEBUG_TRACE = 0x2
+DEC_DEBUG_FENCED = 0x4
+DEC_DEBUG_STRESS = 0x8
 DEC_FLAG_BATCHED_PREFILL = 0x2
 
 ERR_NAMES = {v: k for k, v in globals().items() if k.startswith("DEC_ERR_")}

@@ -387,7 +387,7 @@ int launch(dec_handle* h, int pos0, int n_tok, int tok_src, int lm_last_only, in
   A.tok_src = tok_src;
   A.lm_last_only = lm_last_only;
   A.write_logits = write_logits;
-  A.fenced = 0;
+  A.fenced = (h->debug & DEC_DEBUG_FENCED) ? 1 : 0;
   A.phase_begin = 0;
   A.phase_end = 0x7fffffff;
   A.pos_end = 0x7fffffff;
@@ -423,7 +423,7 @@ int launch_prefill(dec_handle* h, int n, int write_logits) {
   A.tok_src = tok_src;
   A.lm_last_only = lm_last_only;
   A.write_logits = write_logits;
-  A.fenced = 0;
+  A.fenced = (h->debug & DEC_DEBUG_FENCED) ? 1 : 0;
   A.phase_begin = 0;
   A.phase_end = 0x7fffffff;
   A.pos_end = n;
@@ -669,6 +669,10 @@ int init_impl(const dec_model_desc* desc, const dec_weights_src* weights, const 
   if (opts) o = *opts;
   if (o.grid < 0 || o.grid > 1024) return fail(nullptr, DEC_ERR_INVALID_ARG, "grid must be in [0, 1024]");
   if (o.watchdog_us < 0) return fail(nullptr, DEC_ERR_INVALID_ARG, "watchdog_us must be >= 0");
+  if (o.debug_flags & ~(DEC_DEBUG_MULTILAUNCH | DEC_DEBUG_TRACE | DEC_DEBUG_FENCED | DEC_DEBUG_STRESS))
+    return fail(nullptr, DEC_ERR_INVALID_ARG, "unknown debug flags 0x%x", o.debug_flags);
+  if ((o.debug_flags & DEC_DEBUG_STRESS) && (o.debug_flags & DEC_DEBUG_MULTILAUNCH))
+    return fail(nullptr, DEC_ERR_INVALID_ARG, "DEC_DEBUG_STRESS needs the resident kernel (not DEC_DEBUG_MULTILAUNCH)");
   if (noalloc && (!o.arena || !o.stream))
     return fail(nullptr, DEC_ERR_INVALID_ARG, "dec_init_noalloc needs a caller arena and a caller stream");
   if (noalloc && (o.device < 0 || o.device >= kMaxDevices))
@@ -860,6 +864,7 @@ int init_impl(const dec_model_desc* desc, const dec_weights_src* weights, const 
   P.trace_stride = kTraceStride;
   h->wall_hz = (double)wall_khz * 1000.0;
   P.cols_pos = 0;
+  P.stress = (h->debug & DEC_DEBUG_STRESS) ? 1 : 0;
   h->dP = reinterpret_cast<Params*>(sc(h->ar.params));
   e = hipMemcpy(h->dP, &P, sizeof(Params), hipMemcpyHostToDevice);
   if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemcpy(params)"); return bail(DEC_ERR_DEVICE); }

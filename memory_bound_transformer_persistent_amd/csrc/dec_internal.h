@@ -93,6 +93,7 @@ struct Params {
   uint32_t watchdog_ticks;    // bound on one barrier wait, in wall-clock ticks
   uint64_t* trace;            // optional [G][trace_stride] wall-clock stamps (phase start, phase end, ...)
   int trace_stride;
+  int stress;                 // 1: random delays before every arrival, NaN-poisoned exchange buffers
 };
 
 struct Launch {
@@ -111,6 +112,32 @@ struct Launch {
 };
 
 DEC_HD inline int phases_per_token(int L) { return kPhasesPerLayer * L + 2; }
+
+// GEMV work splits, shared by the kernel and host-side checks.
+// Items [b, e) of n for member g of G: contiguous, in order, sizes within one.
+DEC_HD inline void split_even(int n, int g, int G, int& b, int& e) {
+  b = (int)((long long)n * g / G);
+  e = (int)((long long)n * (g + 1) / G);
+}
+// Piece columns of a GEMV row of K elements: 512 elements (64 lanes x 16 B) each.
+DEC_HD inline int gemv_piece_cols(int K) { return (K + 511) >> 9; }
+// Member s (1..n_members) of a workgroup's n units, where a unit is one piece
+// column of one row pair and a pair's units are consecutive (npc of them):
+// an even split, except that a boundary that would fall inside a row pair
+// which already holds the previous boundary moves to that pair's end.  Then
+// no row pair has more than two contributors, and two ds_add_f32 into a
+// zeroed word give the same bits in either order.
+DEC_HD inline void streamer_range(int n, int npc, int n_members, int s, int& u0, int& u1) {
+  int prev = 0;
+  u0 = u1 = 0;
+  for (int k = 1; k <= n_members; ++k) {
+    int b = (int)((long long)n * k / n_members);
+    if (b < prev) b = prev;
+    if (prev % npc != 0 && b / npc == prev / npc && b % npc != 0) b = (prev / npc + 1) * npc < n ? (prev / npc + 1) * npc : n;
+    if (k == s) { u0 = prev; u1 = b; }
+    prev = b;
+  }
+}
 
 // Number of attention chunks per head at context length ctx for a grid of G
 // workgroups and H heads (all sequences' heads in a batch): as many as keeps

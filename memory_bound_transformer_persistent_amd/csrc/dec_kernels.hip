@@ -226,10 +226,7 @@ __device__ __forceinline__ float dot8(u32x4 w, f32x4 xa, f32x4 xb, float acc) {
   acc = __builtin_fmaf((float)h[7], xb[3], acc);
   return acc;
 }
-__device__ __forceinline__ void split(int n, int g, int G, int& b, int& e) {
-  b = (int)((long long)n * g / G);
-  e = (int)((long long)n * (g + 1) / G);
-}
+__device__ __forceinline__ void split(int n, int g, int G, int& b, int& e) { split_even(n, g, G, b, e); }
 
 // Columns of the batched kernel.  In a batched decode column b is sequence b
 // and every column is at the token step's position.  In a batched prefill
@@ -257,7 +254,7 @@ struct GemvWork {
   int rows, K, p0, p1;
 };
 
-__device__ __forceinline__ int gemv_npc(int K) { return (K + 511) >> 9; }
+__device__ __forceinline__ int gemv_npc(int K) { return gemv_piece_cols(K); }
 // Elements of the input vector a GEMV with row length K reads (zero-padded past K).
 __device__ __forceinline__ int gemv_span(int K) { return 512 * gemv_npc(K); }
 
@@ -298,21 +295,11 @@ __device__ __forceinline__ void phase_shape(const Params& P, int ph, int& rows, 
   }
 }
 
-// Streamer s's unit range [u0, u1) of a phase: an even split, except that a
-// boundary that would fall inside a row pair which already holds the
-// previous boundary moves to that pair's end.  Then no row pair has more
-// than two contributors, and two ds_add_f32 into a zeroed word give the same
-// bits in either order: the sums do not depend on timing.
+// Streamer s's unit range [u0, u1) of a phase (streamer_range: no row pair
+// has more than two contributors, so the partial sums do not depend on timing).
 __device__ __forceinline__ void streamer_units(const GemvWork& g, int s, int& u0, int& u1) {
-  const int npc = gemv_npc(g.K), n = (g.p1 - g.p0) * npc;
-  int prev = 0;
-  for (int k = 1; k <= kStreamers; ++k) {
-    int b = (int)((long long)n * k / kStreamers);
-    if (b < prev) b = prev;
-    if (prev % npc != 0 && b / npc == prev / npc && b % npc != 0) b = min(n, (prev / npc + 1) * npc);
-    if (k == s) { u0 = prev; u1 = b; }
-    prev = b;
-  }
+  const int npc = gemv_npc(g.K);
+  streamer_range((g.p1 - g.p0) * npc, npc, kStreamers, s, u0, u1);
 }
 
 // Phase g of a launch: token i, layer l, phase type ph (-1: argmax, -2: not
@@ -682,6 +669,83 @@ __device__ __forceinline__ bool w0_wait(const Params& P, uint32_t epoch, int fen
   const bool ok = why == 0;
   if (fenced) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return ok;
+}
+
+// ---------------------------------------------------------------------------
+// stress mode (a debug aid for the barrier)
+// ---------------------------------------------------------------------------
+// A workgroup waits a pseudo-random 0 to about 2 us before each arrival, so
+// the order in which workgroups arrive and read each phase's inputs varies
+// from barrier to barrier.  The wait is bounded and wave-uniform.
+__device__ __forceinline__ void stress_delay(uint32_t epoch) {
+  uint32_t h = (blockIdx.x + 1u) * 2654435761u ^ epoch * 0x9E3779B9u;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  const int n = rfl((int)(h % 12u));
+  for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(8);   // 8 x 64 cycles each
+}
+
+// Once the barrier before phase ph (layer l) has released this workgroup,
+// fill with NaN the exchange buffers (or this workgroup's share of them)
+// whose readers have all passed that barrier and whose next writer runs after
+// a later one; none of them is phase ph's own input.  A reader that saw a
+// value before the write meant for it was visible would read NaN (or, for
+// token indices, -1), and the logits or tokens would show it.
+template <int MB>
+__device__ __forceinline__ void w0_poison(const Params& P, int ph, int l, const int* tab_wg) {
+  const int lane = threadIdx.x & 63, G = gridDim.x, B = P.B;
+  const uint32_t nan32 = 0x7FC00000u;
+  const uint16_t nan16 = 0x7E00u;
+  auto share = [&](int n, int& a, int& e) { split(n, blockIdx.x, G, a, e); };
+  int a, e;
+  if (ph == PH_ATTN || ph == PH_DOWN) {
+    // residual rows this workgroup publishes next (in O, resp. DOWN); their
+    // readers, the QKV (resp. GU) input pulls, are behind the barrier
+    int r0, r1;
+    own_rows<MB>(P, r0, r1);
+    for (int b = 0; b < B; ++b)
+      for (int r = r0 + lane; r < r1; r += 64) st_coh(reinterpret_cast<uint32_t*>(P.x + (size_t)b * P.d + r), nan32);
+  }
+  if (ph == PH_QKV) {
+    // this workgroup's SwiGLU outputs, read by the last DOWN input pull; GU publishes them next
+    const int p0 = rfl(tab_wg[2 * PH_GU]), p1 = rfl(tab_wg[2 * PH_GU + 1]);
+    for (int b = 0; b < B; ++b)
+      for (int t = p0 + lane; t < p1; t += 64) {
+        if constexpr (MB == 1) st_coh(reinterpret_cast<uint32_t*>(P.act + t), nan32);
+        else st_coh(P.act16 + (size_t)b * P.F + t, nan16);
+      }
+  }
+  if (ph == PH_O) {
+    // q and the attention partials, read during the attention phase
+    share(B * P.q, a, e);
+    for (int i = a + lane; i < e; i += 64) {
+      const int b = i / P.q;
+      st_coh(reinterpret_cast<uint32_t*>(P.qkv + (size_t)b * 3 * P.q + (i - b * P.q)), nan32);
+    }
+    const int nparts = B * P.H * P.max_chunks;   // the partial slots the attention phase uses
+    share(nparts * P.hd, a, e);
+    for (int i = a + lane; i < e; i += 64) st_coh(reinterpret_cast<uint32_t*>(P.part + i), nan32);
+    share(nparts * 2, a, e);
+    for (int i = a + lane; i < e; i += 64) st_coh(reinterpret_cast<uint32_t*>(P.pml + i), nan32);
+  }
+  if (ph == PH_GU) {
+    // the attention output, read by the O input pull
+    share(B * P.q, a, e);
+    for (int i = a + lane; i < e; i += 64) {
+      if constexpr (MB == 1) st_coh(reinterpret_cast<uint32_t*>(P.att_o + i), nan32);
+      else st_coh(P.att_o16 + i, nan16);
+    }
+  }
+  if (ph == PH_ATTN && l == 0) {
+    // argmax partials, read by the previous token's ARGMAX phase, which no
+    // barrier separates from this token's QKV phase
+    share(B * G, a, e);
+    for (int i = a + lane; i < e; i += 64) {
+      st_coh(reinterpret_cast<uint32_t*>(P.amax_v + i), nan32);
+      st_coh(P.amax_i + i, -1);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1555,6 +1619,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     const bool skip_bar = first || (id.ph == PH_QKV && id.l == 0 && have_tok);
     if (!skip_bar) {
       ++epoch;
+      if (P.stress) stress_delay(epoch);
       w0_arrive(P, A.fenced);
       if constexpr (MB == 1)
         if (id.ph == PH_O && P.H > (int)gridDim.x / 32 && (int)blockIdx.x / wg_per_head(P, pos) >= P.H)
@@ -1641,6 +1706,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       else apply_gains_batch(reinterpret_cast<_Float16*>(xs), stage, gs, P.d, B, red);
     }
     __syncthreads();   // S1
+    if (P.stress) w0_poison<MB>(P, id.ph, id.l, tab_wg);
     if (id.ph == PH_ATTN) w0_merge_wg<MB>(P, pos, A.pos_end, wg_per_head(P, pos), aux + kAuxPart);
     if (id.ph == PH_QKV) {
       // the rotary rows of this step's positions, for publishing q and k

@@ -229,6 +229,15 @@ def test_init_errors_before_any_device_work(lib, good_file, tmp_path):
     with pytest.raises(B.DecError) as e:   # file shapes differ from the description
         B.Decoder(desc(d_ffn=512), path=good_file)
     assert e.value.code == B.DEC_ERR_WEIGHTS
+    with pytest.raises(B.DecError) as e:   # unknown debug flag
+        B.Decoder(desc(), tensors=t, debug_flags=0x100)
+    assert e.value.code == B.DEC_ERR_INVALID_ARG
+    with pytest.raises(B.DecError) as e:   # the stress mode runs on the resident kernel only
+        B.Decoder(desc(), tensors=t, debug_flags=B.DEC_DEBUG_STRESS | B.DEC_DEBUG_MULTILAUNCH)
+    assert e.value.code == B.DEC_ERR_INVALID_ARG
+    with pytest.raises(B.DecError) as e:   # the no-allocation handle needs a caller arena and stream
+        B.Decoder(desc(), tensors=t, noalloc=True)
+    assert e.value.code == B.DEC_ERR_INVALID_ARG
 
 
 def test_init_without_gpu_reports_no_device(lib, good_file):
