@@ -16,7 +16,7 @@ import oracle as O
 import synth
 from fullsize import GOLDEN, Fixture, oracle_sha
 
-NAMES = ("dense2b", "lane2b", "dense2b_long", "dense2b_b8", "dense2b_w4", "lane2b_long")
+NAMES = ("dense2b", "lane2b", "dense2b_long", "dense2b_b8", "dense2b_w4", "lane2b_long", "dense2b_b8_long")
 
 
 @pytest.mark.parametrize("name", NAMES)
