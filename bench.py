@@ -4,8 +4,12 @@ Main line (the metric): the dense2b workload -- a 25-layer dense decoder,
 d_model 2560, 20 heads x 128, SwiGLU 6912, vocab 65536, fp16 weights drawn
 N(0, 0.02) from fixed seeds; the 128-token random prompt is prefilled, then
 the timed region is K greedy decode steps (default 512, positions 128..639),
-one dec_step launch per token with the token fed back on the device.  One
-step = one pass over every active weight (the whole hot path).
+K dec_step calls with the token fed back on the device.  By default they are
+served by the decode server: a resident launch takes each step from a
+host-pinned mailbox, so no kernel boundary falls between tokens (the region is
+4 segments, each one server launch ended by dec_sync); --mode step launches
+the kernel once per token instead.  One step = one pass over every active
+weight (the whole hot path).
 
 The same JSON line also carries, each measured in this run on its own handle:
   workloads.lane2b        one lane of an 8-way split (3 heads, FFN 864, an
@@ -22,10 +26,11 @@ The same JSON line also carries, each measured in this run on its own handle:
   cpu_baseline            the CPU oracle on a bounded sample of the same steps
 
 Every roofline object prices its kernel against MI355X's 8 TB/s HBM peak with
-ALGORITHMIC bytes per launch (every weight byte once, one embedding row per
+ALGORITHMIC bytes per step (every weight byte once, one embedding row per
 sequence, the KV-cache rows attention reads at that position and the rows it
-appends) divided by the kernel's average launch duration, measured with HIP
-events on the kernel's own stream around back-to-back launches.
+appends) divided by the average step duration, measured with HIP events on
+the kernel's own stream around the region (for a server launch of n steps,
+bytes and duration per launch are both n times these).
 """
 import argparse
 import hashlib
@@ -41,6 +46,7 @@ METRIC = "decode tokens/s per request (bs=1) and achieved HBM GB/s vs peak, 1 MI
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_dec_resident_dense2b.txt")
 KERNEL_SRC = os.path.join(ROOT, "memory_bound_transformer_persistent_amd", "csrc", "dec_kernels.hip")
 EXTRAS = ("lane2b", "dense2b_long", "dense2b_b8")
+SERVE_IDLE_US = 200000   # decode server: a launch ends after 0.2 s without a step
 
 
 def kernel_hash():
@@ -97,13 +103,13 @@ def cpu_baseline(shape, tensors, prompt, n_steps):
 class Run:
     """One handle of one workload, timed on its own stream."""
 
-    def __init__(self, B, R, torch, w, tensors, stream, flags=0, debug=0):
+    def __init__(self, B, R, torch, w, tensors, stream, flags=0, debug=0, serve=False):
         self.B, self.R, self.torch, self.w, self.stream = B, R, torch, w, stream
-        self.s, self.nb = w.shape, w.batch
+        self.s, self.nb, self.serve = w.shape, w.batch, serve
         import synth
         self.prompt = synth.make_prompt(self.s.vocab, w.prompt_len, batch=self.nb, seed=w.prompt_seed)
         self.dec = B.Decoder(B.ModelDesc.from_shape(self.s, batch=self.nb, flags=flags), tensors=tensors, device=0,
-                             stream=stream.cuda_stream, debug_flags=debug)
+                             stream=stream.cuda_stream, debug_flags=debug, serve_idle_us=SERVE_IDLE_US if serve else 0)
 
     def ev(self):
         return self.torch.cuda.Event(enable_timing=True)
@@ -126,7 +132,11 @@ class Run:
         return a.elapsed_time(b)
 
     def decode(self, K, nseg=4, mode="step"):
-        """K steps from the current position; (region ms, per-segment tokens/s)."""
+        """K steps from the current position; (region ms, per-segment tokens/s).
+
+        A decode-server handle (serve) runs each segment as one server launch:
+        its steps are posted, then dec_sync ends the launch before the
+        segment's end event, which would otherwise wait behind it."""
         torch, dec = self.torch, self.dec
         nseg = nseg if mode == "step" and K >= 8 else 1
         bounds = [K * j // nseg for j in range(nseg + 1)]
@@ -143,6 +153,8 @@ class Run:
             for j in range(nseg):
                 for _ in range(bounds[j], bounds[j + 1]):
                     dec.step(want_tok=False)
+                if self.serve:
+                    dec.sync()
                 evs[j + 1].record(self.stream)
         evs[-1].synchronize()
         dec.sync()
@@ -174,13 +186,13 @@ def kernel_name(w):
     return f"dec_resident_{'batch_' if w.batch > 1 else ''}hd{w.shape.head_dim}"
 
 
-def extra_workload(B, R, torch, name, full_tensors, stream, warmup):
+def extra_workload(B, R, torch, name, full_tensors, stream, warmup, serve):
     """One of the other configurations, at its own prompt and step count."""
     import synth
     w = synth.workload(name)
     tensors = synth.lane_from_full(w.shape, full_tensors) if w.lane else full_tensors
     bp = name == "dense2b_long"      # the long prompt goes through the batched prefill
-    r = Run(B, R, torch, w, tensors, stream, flags=B.DEC_FLAG_BATCHED_PREFILL if bp else 0)
+    r = Run(B, R, torch, w, tensors, stream, flags=B.DEC_FLAG_BATCHED_PREFILL if bp else 0, serve=serve)
     try:
         r.warm(warmup)
         pre = r.prefill_ms()
@@ -202,8 +214,9 @@ def main():
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="dense2b", help="main line's workload (the others run only for dense2b)")
-    ap.add_argument("--mode", choices=["step", "generate"], default="step",
+    ap.add_argument("--mode", choices=["serve", "step", "generate"], default="serve",
                     help="step: one dec_step launch per token (token fed back on the device); "
+                         "serve: dec_step calls served by the resident decode server (one launch per segment); "
                          "generate: all timed steps inside one dec_generate launch")
     ap.add_argument("--cpu-steps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -254,15 +267,17 @@ def main():
     stream = torch.cuda.Stream(device=0)
     bp = args.batched_prefill and w.batch == 1
     flags = B.DEC_FLAG_BATCHED_PREFILL if bp else 0
+    if args.mode == "serve" and args.multilaunch:
+        sys.exit("--mode serve is one resident launch; not with --multilaunch")
     r = Run(B, R, torch, w, tensors, stream, flags=flags,
-            debug=B.DEC_DEBUG_MULTILAUNCH if args.multilaunch else 0)
+            debug=B.DEC_DEBUG_MULTILAUNCH if args.multilaunch else 0, serve=args.mode == "serve")
     K, nb = args.steps, w.batch
     # warm-up: prefill + W steps, then rewind so the timed steps are the workload's positions
     r.warm(args.warmup)
     prefill_ms = r.prefill_ms()
     pos0 = r.dec.position
     t0 = time.perf_counter()
-    region_ms, segs = r.decode(K, mode=args.mode)
+    region_ms, segs = r.decode(K, mode="generate" if args.mode == "generate" else "step")
     wall = time.perf_counter() - t0
     if args.mode == "generate":
         bytes_per_launch = sum(R.step_bytes(s, pos0 + i, nb).total for i in range(K))
@@ -314,9 +329,9 @@ def main():
         "context": {"pages_8xMI300X_tokens_per_s": 3000, "pages_8xH200_tokens_per_s": 2100,
                     "note": "2B fp16, batch 1, 8 GPUs each: other hardware, context only"},
     }
-    if args.mode == "step" and not args.multilaunch:
-        # the same positions in one dec_generate launch (context: the step
-        # mode's per-launch cost), after the timed region
+    if args.mode != "generate" and not args.multilaunch:
+        # the same positions in one dec_generate launch (context: what the
+        # dec_step calls cost beyond one launch), after the timed region
         r.dec.reset()
         r.dec.prefill(r.prompt)
         gen_ms, _ = r.decode(K, mode="generate")
@@ -339,7 +354,7 @@ def main():
         out["workloads"] = {}
         for name in EXTRAS:
             print(f"# measuring {name}", file=sys.stderr, flush=True)
-            out["workloads"][name] = extra_workload(B, R, torch, name, full, stream, 8)
+            out["workloads"][name] = extra_workload(B, R, torch, name, full, stream, 8, args.mode == "serve")
     # the plain-stream read rate of this device, the practical ceiling under the 8 TB/s peak
     ceiling = B.stream_ceiling(1 << 31, 5)
     out["stream_ceiling"] = {"GBps": round(ceiling, 1), "bytes": 1 << 31, "reps": 5, "kernel": "dec_stream_read",

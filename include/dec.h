@@ -187,6 +187,24 @@ typedef struct dec_weights_src {
  *   grid:        workgroups of the resident kernel; 0 = one per compute unit.
  *                It must be at least batch x n_heads (8 x n_heads with
  *                DEC_FLAG_BATCHED_PREFILL), else DEC_ERR_UNSUPPORTED.
+ *   serve_idle_us: 0 = every dec_step is a kernel launch of its own.  1 ..
+ *                10,000,000 = decode server: one resident launch serves a
+ *                run of dec_step calls, which post their steps to it through
+ *                host-pinned memory (allocated with the handle) instead of
+ *                launching; the launch ends when any other call on the
+ *                handle needs the stream (dec_sync, dec_generate,
+ *                dec_prefill, dec_reset, dec_read_kv, dec_read_trace,
+ *                dec_free), or by itself after serve_idle_us without a step
+ *                (the next dec_step then starts a new one).  While it runs it
+ *                holds every compute unit of the device: other work on the
+ *                handle's stream, and work on other streams that needs a
+ *                compute unit, waits for its end, so call dec_sync before
+ *                such work.  Not with dec_init_noalloc or
+ *                DEC_DEBUG_MULTILAUNCH (DEC_ERR_INVALID_ARG).
+ *                The pages' GPU-resident program that removes kernel
+ *                boundaries and host scheduling between tokens (page
+ *                標準GPUによるリアルタイムLLM推論, section
+ *                標準推論スタックのボトルネックとKogの工夫).
  */
 typedef struct dec_init_opts {
   int32_t device;
@@ -196,7 +214,8 @@ typedef struct dec_init_opts {
   size_t arena_bytes;
   uint32_t debug_flags;
   int32_t watchdog_us;
-  int32_t reserved[6];
+  int32_t serve_idle_us;
+  int32_t reserved[5];
 } dec_init_opts;
 
 typedef struct dec_handle dec_handle;
@@ -298,7 +317,10 @@ int dec_prefill(dec_handle* h, const int32_t* tokens, int32_t n,
  * out_logits [batch * lm_vocab] (host) are optional; with both NULL the call
  * only enqueues work on the stream and returns without waiting (use dec_sync;
  * a device error such as DEC_ERR_TIMEOUT then surfaces at the next
- * synchronous call).  DEC_ERR_CONTEXT_FULL if p == max_ctx; DEC_ERR_STATE
+ * synchronous call).  On a decode-server handle (serve_idle_us > 0) the step
+ * is posted to the running server launch (started if none runs); with both
+ * outputs NULL the call returns once it is posted, waiting only while 64
+ * posted steps are unfinished.  DEC_ERR_CONTEXT_FULL if p == max_ctx; DEC_ERR_STATE
  * before any prefill; DEC_ERR_TOKEN_RANGE for a forced token outside
  * [0, vocab).
  * One step is one pass over every active weight plus the KV cache read, the

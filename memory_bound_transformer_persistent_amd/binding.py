@@ -70,7 +70,7 @@ class WeightsSrc(ctypes.Structure):
 class InitOpts(ctypes.Structure):
     _fields_ = [("device", ctypes.c_int32), ("grid", ctypes.c_int32), ("stream", ctypes.c_void_p),
                 ("arena", ctypes.c_void_p), ("arena_bytes", ctypes.c_size_t), ("debug_flags", ctypes.c_uint32),
-                ("watchdog_us", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6)]
+                ("watchdog_us", ctypes.c_int32), ("serve_idle_us", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
 
 
 _lib = None
@@ -185,9 +185,10 @@ class Decoder:
     """One handle of the decode library (one device, one stream)."""
 
     def __init__(self, desc, tensors=None, path=None, device=0, stream=None, grid=0,
-                 debug_flags=0, watchdog_us=0, arena=None, arena_bytes=0, noalloc=False):
+                 debug_flags=0, watchdog_us=0, arena=None, arena_bytes=0, noalloc=False, serve_idle_us=0):
         """noalloc: dec_init_noalloc (needs arena, arena_bytes and stream; the
-        library allocates no device memory for this handle)."""
+        library allocates no device memory for this handle).  serve_idle_us > 0:
+        decode server (dec_step posts to one resident launch; sync() ends it)."""
         lib = load()
         self.desc = desc
         src = WeightsSrc()
@@ -199,7 +200,7 @@ class Decoder:
         if path is not None:
             src.path = str(path).encode()
         opts = InitOpts(device=device, grid=grid, stream=stream, arena=arena, arena_bytes=arena_bytes,
-                        debug_flags=debug_flags, watchdog_us=watchdog_us)
+                        debug_flags=debug_flags, watchdog_us=watchdog_us, serve_idle_us=serve_idle_us)
         h = ctypes.c_void_p()
         init = lib.dec_init_noalloc if noalloc else lib.dec_init
         rc = init(ctypes.byref(desc), ctypes.byref(src), ctypes.byref(opts), ctypes.byref(h))

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -281,7 +282,7 @@ bool same_shape(const dec_model_desc& a, const dec_model_desc& b) {
 // ---------------------------------------------------------------------------
 struct Arena {
   size_t w, w2, gains, rope, kv, x, qkv, att_o, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out, prompt, ctl,
-      params, params2, trace, total;
+      srv_slot, params, params2, trace, total;
 };
 
 bool batched_prefill(const dec_model_desc& d) { return (d.flags & DEC_FLAG_BATCHED_PREFILL) != 0; }
@@ -326,6 +327,7 @@ Arena arena_layout(const dec_model_desc& d, int G) {
   a.tok_out = take((size_t)d.max_ctx * B * 4);
   a.prompt = take((size_t)d.max_ctx * B * 4);
   a.ctl = take(kCtlWords * 4);
+  a.srv_slot = take((size_t)kSrvSlotWords * 4);
   a.params = take(sizeof(Params));
   a.params2 = take(sizeof(Params));
   a.trace = take((size_t)G * kTraceStride * 8);
@@ -359,6 +361,13 @@ struct dec_handle {
   bool broken = false;     // a launch failed; only dec_reset/dec_free are allowed
   bool has_prev_tok = false;
   double wall_hz = 1e8;
+  // decode server (serve_idle_us > 0)
+  uint32_t srv_idle_ticks = 0;  // 0: off
+  Mailbox* mail = nullptr;      // host-pinned mailbox (host address)
+  float* lg_host = nullptr;     // host-pinned logits [batch * lm_vocab]
+  bool srv_on = false;          // a server launch is enqueued and has not been waited for
+  uint32_t srv_epoch = 0;       // launches so far (tags their request slots)
+  uint32_t srv_posted = 0;      // requests posted to the current launch
 };
 
 namespace {
@@ -446,6 +455,109 @@ int launch_prefill(dec_handle* h, int n, int write_logits) {
   HIPCHK(h, &h->err, (hipError_t)kernel_launch_resident(h->dP2, A, h->grid, kMaxBatch, h->desc.head_dim, h->stream));
   h->bar_done += launch_barriers(h->desc.n_layers, n_tok, lm_last_only);
   return DEC_OK;
+}
+
+// ---------------------------------------------------------------------------
+// decode server: host side of the mailbox protocol
+// ---------------------------------------------------------------------------
+uint32_t mail_load(const uint32_t* p) { return __atomic_load_n(p, __ATOMIC_ACQUIRE); }
+
+// Starts a server launch at the current position.  The previous one has been
+// waited for, so no kernel reads the mailbox while it is reset.
+int srv_start(dec_handle* h) {
+  Mailbox* m = h->mail;
+  __atomic_store_n(&m->done, 0u, __ATOMIC_RELAXED);
+  __atomic_store_n(&m->ctl, 0u, __ATOMIC_SEQ_CST);
+  Launch A;
+  std::memset(&A, 0, sizeof A);
+  A.pos0 = h->pos;
+  A.n_tok = h->desc.max_ctx - h->pos;
+  A.tok_src = TOK_DEVICE;
+  A.fenced = (h->debug & DEC_DEBUG_FENCED) ? 1 : 0;
+  A.phase_begin = 0;
+  A.phase_end = 0x7fffffff;
+  A.pos_end = 0x7fffffff;
+  A.server = 1;
+  A.srv_epoch = ++h->srv_epoch;
+  if (A.srv_epoch == 0) A.srv_epoch = h->srv_epoch = 1;   // 0 would match the zeroed slots
+  A.idle_ticks = h->srv_idle_ticks;
+  A.bar_base = h->bar_done;
+  HIPCHK(h, &h->err, (hipError_t)kernel_launch_resident(h->dP, A, h->grid, h->desc.batch, h->desc.head_dim, h->stream));
+  h->srv_on = true;
+  h->srv_posted = 0;
+  return DEC_OK;
+}
+
+int check_device_error(dec_handle* h);
+
+// Ends the server launch, if one runs: closes the mailbox, waits for the
+// launch and adds the barriers its served requests executed.
+int srv_stop(dec_handle* h) {
+  if (!h->srv_on) return DEC_OK;
+  __atomic_fetch_or(&h->mail->ctl, kMailClosed, __ATOMIC_SEQ_CST);
+  h->srv_on = false;
+  const hipError_t e = hipStreamSynchronize(h->stream);
+  const uint32_t n = mail_load(&h->mail->done);
+  if (n > 0) h->bar_done += launch_barriers(h->desc.n_layers, (int)n, 0);
+  if (e != hipSuccess) return hip_fail(h, &h->err, e, "hipStreamSynchronize(server)");
+  int rc = check_device_error(h);
+  if (rc) return rc;
+  if (n != h->srv_posted) {
+    h->broken = true;
+    return fail(&h->err, DEC_ERR_DEVICE, "server launch ended after %u of %u requests; call dec_reset", n,
+                h->srv_posted);
+  }
+  return DEC_OK;
+}
+
+// Waits until the server launch has completed `n` requests.  The launch ends
+// by itself at the latest after the idle and watchdog bounds, so the stream
+// is checked now and then: a launch that ended short of n reports why.
+int srv_wait(dec_handle* h, uint32_t n) {
+  for (uint32_t spin = 0;; ++spin) {
+    if ((int)(mail_load(&h->mail->done) - n) >= 0) return DEC_OK;
+    if ((spin & 255u) == 255u) {
+      const hipError_t q = hipStreamQuery(h->stream);
+      if (q != hipErrorNotReady) {
+        if ((int)(mail_load(&h->mail->done) - n) >= 0) return DEC_OK;
+        const int rc = srv_stop(h);
+        if (rc) return rc;
+        h->broken = true;
+        return fail(&h->err, DEC_ERR_DEVICE, "server launch ended before request %u completed; call dec_reset", n);
+      }
+    }
+    __builtin_ia32_pause();
+  }
+}
+
+// Posts one step; starts a server launch when none runs or the running one
+// has closed its mailbox for idleness.
+int srv_post(dec_handle* h, int flags, const int32_t* force) {
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    if (!h->srv_on) {
+      int rc = srv_start(h);
+      if (rc) return rc;
+    }
+    Mailbox* m = h->mail;
+    const uint32_t k = h->srv_posted;
+    if (k >= (uint32_t)kMailRing) {
+      // slot k % kMailRing last held request k - kMailRing, which must be complete
+      int rc = srv_wait(h, k - kMailRing + 1);
+      if (rc) return rc;
+    }
+    int32_t* r = m->req[k % kMailRing];
+    r[0] = flags;
+    for (int b = 0; b < h->desc.batch; ++b) r[1 + b] = force ? force[b] : 0;
+    uint32_t expected = k;
+    if (__atomic_compare_exchange_n(&m->ctl, &expected, k + 1, false, __ATOMIC_SEQ_CST, __ATOMIC_SEQ_CST)) {
+      h->srv_posted = k + 1;
+      return DEC_OK;
+    }
+    // the launch closed its mailbox at k (idle): wait for it and start another
+    int rc = srv_stop(h);
+    if (rc) return rc;
+  }
+  return fail(&h->err, DEC_ERR_DEVICE, "a fresh server launch refused a request");
 }
 
 int check_device_error(dec_handle* h) {
@@ -673,6 +785,12 @@ int init_impl(const dec_model_desc* desc, const dec_weights_src* weights, const 
     return fail(nullptr, DEC_ERR_INVALID_ARG, "unknown debug flags 0x%x", o.debug_flags);
   if ((o.debug_flags & DEC_DEBUG_STRESS) && (o.debug_flags & DEC_DEBUG_MULTILAUNCH))
     return fail(nullptr, DEC_ERR_INVALID_ARG, "DEC_DEBUG_STRESS needs the resident kernel (not DEC_DEBUG_MULTILAUNCH)");
+  if (o.serve_idle_us < 0 || o.serve_idle_us > 10000000)
+    return fail(nullptr, DEC_ERR_INVALID_ARG, "serve_idle_us must be in [0, 10000000]");
+  if (o.serve_idle_us > 0 && noalloc)
+    return fail(nullptr, DEC_ERR_INVALID_ARG, "the decode server allocates host-pinned memory: not with dec_init_noalloc");
+  if (o.serve_idle_us > 0 && (o.debug_flags & DEC_DEBUG_MULTILAUNCH))
+    return fail(nullptr, DEC_ERR_INVALID_ARG, "the decode server is one resident launch: not with DEC_DEBUG_MULTILAUNCH");
   if (noalloc && (!o.arena || !o.stream))
     return fail(nullptr, DEC_ERR_INVALID_ARG, "dec_init_noalloc needs a caller arena and a caller stream");
   if (noalloc && (o.device < 0 || o.device >= kMaxDevices))
@@ -865,6 +983,27 @@ int init_impl(const dec_model_desc* desc, const dec_weights_src* weights, const 
   h->wall_hz = (double)wall_khz * 1000.0;
   P.cols_pos = 0;
   P.stress = (h->debug & DEC_DEBUG_STRESS) ? 1 : 0;
+  P.srv_slot = reinterpret_cast<int32_t*>(sc(h->ar.srv_slot));
+  if (o.serve_idle_us > 0) {
+    // decode server: mailbox and logits in host-pinned memory the device maps
+    const unsigned fl = hipHostMallocMapped | hipHostMallocCoherent;
+    void* dm = nullptr;
+    void* dl = nullptr;
+    e = hipHostMalloc(reinterpret_cast<void**>(&h->mail), sizeof(Mailbox), fl);
+    if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&h->lg_host), (size_t)desc->batch * desc->lm_vocab * 4, fl);
+    if (e != hipSuccess) {
+      fail(&h->err, DEC_ERR_OOM, "hipHostMalloc (server mailbox) failed: %s", hipGetErrorString(e));
+      return bail(DEC_ERR_OOM);
+    }
+    std::memset(h->mail, 0, sizeof(Mailbox));
+    e = hipHostGetDevicePointer(&dm, h->mail, 0);
+    if (e == hipSuccess) e = hipHostGetDevicePointer(&dl, h->lg_host, 0);
+    if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipHostGetDevicePointer"); return bail(DEC_ERR_DEVICE); }
+    P.mail = static_cast<Mailbox*>(dm);
+    P.lg_sys = static_cast<float*>(dl);
+    h->srv_idle_ticks = (uint32_t)std::min((double)o.serve_idle_us * wall_khz / 1000.0, 4.0e9);
+    if (h->srv_idle_ticks == 0) h->srv_idle_ticks = 1;
+  }
   h->dP = reinterpret_cast<Params*>(sc(h->ar.params));
   e = hipMemcpy(h->dP, &P, sizeof(Params), hipMemcpyHostToDevice);
   if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemcpy(params)"); return bail(DEC_ERR_DEVICE); }
@@ -915,6 +1054,7 @@ int dec_prefill(dec_handle* h, const int32_t* tokens, int32_t n, int32_t* out_to
   if (h->broken) return fail(&h->err, DEC_ERR_STATE, "handle is in an error state; call dec_reset");
   if (h->pos != 0) return fail(&h->err, DEC_ERR_STATE, "prefill needs position 0 (call dec_reset)");
   if (n < 1) return fail(&h->err, DEC_ERR_INVALID_ARG, "n must be >= 1");
+  if (int rc0 = srv_stop(h)) return rc0;
   if (n > h->desc.max_ctx) return fail(&h->err, DEC_ERR_CONTEXT_FULL, "prompt of %d tokens exceeds max_ctx %d", n, h->desc.max_ctx);
   const int B = h->desc.batch;
   for (long long i = 0; i < (long long)n * B; ++i)
@@ -962,6 +1102,23 @@ int dec_step(dec_handle* h, const int32_t* force_tok, int32_t* out_tok, float* o
         return fail(&h->err, DEC_ERR_TOKEN_RANGE, "token %d of sequence %d outside [0, %d)", force_tok[b], b,
                     h->desc.vocab);
   }
+  if (h->srv_idle_ticks) {
+    // decode server: post the step; wait only for what the caller asked for
+    const int flags = (force_tok ? kReqForce : 0) | (out_logits ? kReqLogits : 0);
+    int rc = srv_post(h, flags, force_tok);
+    if (rc) return rc;
+    h->pos += 1;
+    h->has_prev_tok = true;
+    if (!out_tok && !out_logits) return DEC_OK;
+    const uint32_t k = h->srv_posted - 1;
+    rc = srv_wait(h, k + 1);
+    if (rc) return rc;
+    const size_t B = h->desc.batch;
+    if (out_tok)
+      for (size_t b = 0; b < B; ++b) out_tok[b] = __atomic_load_n(&h->mail->tok[k % kMailRing][b], __ATOMIC_RELAXED);
+    if (out_logits) std::memcpy(out_logits, h->lg_host, B * h->desc.lm_vocab * 4);
+    return DEC_OK;
+  }
   int rc = launch(h, h->pos, 1, TOK_DEVICE, 0, out_logits != nullptr, force_tok);
   if (rc) return rc;
   h->pos += 1;
@@ -978,6 +1135,7 @@ int dec_generate(dec_handle* h, int32_t n_steps, int32_t* out_toks) {
   if (!h->has_prev_tok) return fail(&h->err, DEC_ERR_STATE, "no previous token: prefill first");
   if ((long long)h->pos + n_steps > h->desc.max_ctx)
     return fail(&h->err, DEC_ERR_CONTEXT_FULL, "%d steps from position %d pass max_ctx %d", n_steps, h->pos, h->desc.max_ctx);
+  if (int rc0 = srv_stop(h)) return rc0;
   int rc = launch(h, h->pos, n_steps, TOK_DEVICE, 0, 0);
   if (rc) return rc;
   h->pos += n_steps;
@@ -987,11 +1145,13 @@ int dec_generate(dec_handle* h, int32_t n_steps, int32_t* out_toks) {
 int dec_sync(dec_handle* h) {
   if (!h) return fail(nullptr, DEC_ERR_INVALID_ARG, "handle is NULL");
   if (h->broken) return fail(&h->err, DEC_ERR_STATE, "handle is in an error state; call dec_reset");
+  if (h->srv_on) return srv_stop(h);
   return check_device_error(h);
 }
 
 int dec_reset(dec_handle* h) {
   if (!h) return fail(nullptr, DEC_ERR_INVALID_ARG, "handle is NULL");
+  (void)srv_stop(h);   // an error it reports leaves the handle broken, which the reset clears
   hipError_t e = hipStreamSynchronize(h->stream);
   if (e != hipSuccess) return fail(&h->err, DEC_ERR_DEVICE, "hipStreamSynchronize failed: %s", hipGetErrorString(e));
   if (h->broken) {
@@ -1013,6 +1173,7 @@ int dec_read_kv(dec_handle* h, int32_t layer, int32_t seq, int32_t n_pos, uint16
   const dec_model_desc& d = h->desc;
   if (layer < 0 || layer >= d.n_layers || seq < 0 || seq >= d.batch || n_pos < 0 || n_pos > d.max_ctx)
     return fail(&h->err, DEC_ERR_INVALID_ARG, "layer/seq/n_pos out of range");
+  if (int rc0 = srv_stop(h)) return rc0;
   HIPCHK(h, &h->err, hipStreamSynchronize(h->stream));
   const size_t head = (size_t)d.max_ctx * d.head_dim;
   for (int kind = 0; kind < 2; ++kind) {
@@ -1076,6 +1237,7 @@ int dec_read_trace(dec_handle* h, uint64_t* host, int32_t* out_grid, int32_t* ou
   if (out_hz) *out_hz = h->wall_hz;
   if (!host) return DEC_OK;
   if (!h->P.trace) return fail(&h->err, DEC_ERR_STATE, "handle was created without DEC_DEBUG_TRACE");
+  if (int rc0 = srv_stop(h)) return rc0;
   HIPCHK(h, &h->err, hipStreamSynchronize(h->stream));
   HIPCHK(h, &h->err, hipMemcpy(host, h->P.trace, (size_t)h->grid * kTraceStride * 8, hipMemcpyDeviceToHost));
   return DEC_OK;
@@ -1083,7 +1245,10 @@ int dec_read_trace(dec_handle* h, uint64_t* host, int32_t* out_grid, int32_t* ou
 
 void dec_free(dec_handle* h) {
   if (!h) return;
+  (void)srv_stop(h);
   if (h->stream) (void)hipStreamSynchronize(h->stream);
+  if (h->mail) (void)hipHostFree(h->mail);
+  if (h->lg_host) (void)hipHostFree(h->lg_host);
   if (h->noalloc) g_scratch_held[h->device] = false;   // the fixed scratch array is free again
   if (h->own_arena && h->base) (void)hipFree(h->base);
   if (h->own_stream && h->stream) (void)hipStreamDestroy(h->stream);

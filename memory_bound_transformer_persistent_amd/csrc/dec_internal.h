@@ -62,6 +62,35 @@ enum TokSrc : int { TOK_PROMPT = 0, TOK_DEVICE = 1 };
 // Error codes raised on the device (same values as dec_status).
 constexpr int kDevErrTimeout = -10;
 
+// Decode server: one resident launch serves a run of dec_step calls.  The
+// host posts step k of the launch as request k in a mailbox in host-pinned,
+// coherent memory that the device reads through its own mapping.  Only
+// workgroup 0 reads the mailbox; it copies each request into device slots
+// (kSrvCopies replicas, so polling workgroups spread over memory channels)
+// that the other workgroups read.  `ctl` holds the number of requests posted
+// to the running launch, plus kMailClosed once no request follows: the host
+// sets it to end the launch, and workgroup 0 sets it when no request came for
+// the idle bound.  Both post and close with a compare-and-swap on `ctl`, so a
+// request is either posted before the close or refused by it, for host and
+// device alike.
+constexpr int kMailRing = 64;          // requests in flight at most
+constexpr int kReqWords = 16;          // per request: flags, then the batch's input tokens
+constexpr int kReqForce = 1;           // request flag: the step's input tokens are given
+constexpr int kReqLogits = 2;          // request flag: store the step's logits for the host
+constexpr uint32_t kMailClosed = 0x80000000u;
+constexpr int kSrvCopies = 8;
+struct Mailbox {
+  uint32_t ctl;                        // requests posted | kMailClosed
+  uint32_t pad0[63];
+  uint32_t done;                       // requests completed (their tokens are in tok)
+  uint32_t pad1[63];
+  int32_t req[kMailRing][kReqWords];   // request k in slot k % kMailRing
+  int32_t tok[kMailRing][kMaxBatch];   // greedy tokens of completed request k
+};
+// device slot of request k (words): [0,1] tag, [2] flags, [3 ..] tokens; the
+// tag is (launch epoch << 32) | (k + 1), with kMailClosed when the launch ends at k
+constexpr int kSrvSlotWords = kSrvCopies * kMailRing * kReqWords;
+
 struct Params {
   int L, d, H, hd, F, V, Vlm, max_ctx, q;   // q = H*hd
   float eps;
@@ -94,6 +123,9 @@ struct Params {
   uint64_t* trace;            // optional [G][trace_stride] wall-clock stamps (phase start, phase end, ...)
   int trace_stride;
   int stress;                 // 1: random delays before every arrival, NaN-poisoned exchange buffers
+  Mailbox* mail;              // decode server mailbox (device address of host-pinned memory) or null
+  float* lg_sys;              // decode server logits [B][Vlm] (device address of host-pinned memory) or null
+  int32_t* srv_slot;          // decode server request slots [kSrvCopies][kMailRing][kReqWords]
 };
 
 struct Launch {
@@ -109,6 +141,9 @@ struct Launch {
   int pos_end;       // positions at or past pos_end are not computed (the ragged last step of a batched prefill)
   int n_force;       // 1: the first token's inputs are force[0..batch) instead of *tok_cur (teacher forcing)
   int force[kMaxBatch];
+  int server;        // 1: token i is request i of P.mail; the launch ends where the mailbox closes
+  uint32_t srv_epoch;     // tags this launch's request slots (never 0)
+  uint32_t idle_ticks;    // workgroup 0 closes the mailbox after this long (wall clock) without a request
 };
 
 DEC_HD inline int phases_per_token(int L) { return kPhasesPerLayer * L + 2; }

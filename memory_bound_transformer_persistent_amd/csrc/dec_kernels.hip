@@ -177,6 +177,29 @@ __device__ __forceinline__ void st_coh(uint16_t* p, uint16_t v) {
 typedef __attribute__((address_space(1))) uint64_t gu64;
 __device__ __forceinline__ void st_g(float* p, float v) { *(gfloat_rw*)p = v; }
 __device__ __forceinline__ void st_g(uint64_t* p, uint64_t v) { *(gu64*)p = v; }
+__device__ __forceinline__ uint64_t ld_coh64(const uint64_t* p) {
+  return __hip_atomic_load((gu64*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store((gu64*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// System-scope accesses of host-pinned memory (the decode server's mailbox
+// and logits), through the global address space
+__device__ __forceinline__ int ld_sys(const int* p) {
+  return __hip_atomic_load((gint_rw*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ uint32_t ld_sys(const uint32_t* p) {
+  return __hip_atomic_load((guint*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ void st_sys(int* p, int v) {
+  __hip_atomic_store((gint_rw*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ void st_sys(uint32_t* p, uint32_t v) {
+  __hip_atomic_store((guint*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ void st_sys(float* p, float v) {
+  __hip_atomic_store((gfloat_rw*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 // relaxed device-scope fetch-add, returning the old value
 __device__ __forceinline__ uint32_t atomic_add_coh(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add((guint*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1139,7 +1162,7 @@ __device__ __forceinline__ void w0_merge_wg(const Params& P, int pos, int pos_en
 // fp16 and appended to the KV cache at (layer l, position pos).
 template <int MB>
 __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l, int pos, int pos_end,
-                                                 const int* tab_wg, bool want_logits, const float* scl,
+                                                 const int* tab_wg, int lg_mode, const float* scl,
                                                  const float* out, float* xown, const float* rope_lds) {
   const int lane = threadIdx.x & 63, B = P.B;
   if (!is_gemv(ph)) return;
@@ -1212,7 +1235,10 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l,
         if (b < B) {
           const float v = out[t * MB + b] * scl[b];
           if (v > best[b]) { best[b] = v; bidx[b] = 2 * p0 + t; }
-          if (want_logits) st_g(P.logits + (size_t)b * P.Vlm + 2 * p0 + t, v);
+          // logits: 1 = the device buffer; 2 = the host's pinned buffer (a server
+          // launch keeps running while the host reads them)
+          if (lg_mode == 1) st_g(P.logits + (size_t)b * P.Vlm + 2 * p0 + t, v);
+          else if (lg_mode == 2) st_sys(P.lg_sys + (size_t)b * P.Vlm + 2 * p0 + t, v);
         }
       }
     }
@@ -1288,6 +1314,142 @@ __device__ __forceinline__ void w0_argmax(const Params& P, int i, int cur_col, i
       st_coh(P.tok_out + (size_t)i * P.B + b, tok[b]);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// decode server requests (wave 0)
+// ---------------------------------------------------------------------------
+// A request as wave 0 holds it: state 1 = request k is posted (flags and
+// input tokens below), -1 = the launch ends at k, 0 = not known yet.
+struct Request { int state; int flags; int tok[kMaxBatch]; };
+
+__device__ __forceinline__ uint64_t srv_tag(const Launch& A, uint32_t k, bool end) {
+  return ((uint64_t)A.srv_epoch << 32) | (uint64_t)((k + 1u) | (end ? kMailClosed : 0u));
+}
+
+__device__ __forceinline__ void take_fields(int v, Request& rq) {
+  rq.flags = __builtin_amdgcn_readlane(v, 0);
+#pragma unroll
+  for (int b = 0; b < kMaxBatch; ++b) rq.tok[b] = __builtin_amdgcn_readlane(v, 1 + b);
+}
+
+// Workgroup 0: request k from the host mailbox.  A posted request (ctl counts
+// past k) has its fields in place: the host writes them before it raises
+// ctl, and the field loads issue only after the ctl load has returned.  The
+// request, or the end, is copied to every device slot, fields before tag.
+// With `block`, waits up to the idle bound, then closes the mailbox at k by
+// compare-and-swap; the value that swap leaves (the host's post or the
+// close) decides.  Without `block`, returns 0 when nothing is decided yet.
+__device__ int w0_host_request(const Params& P, const Launch& A, uint32_t k, bool block, Request& rq) {
+  const int lane = threadIdx.x & 63;
+  Mailbox* m = P.mail;
+  const uint64_t t0 = wall_clock64();
+  int state;
+  while (true) {
+    const uint32_t c = (uint32_t)rfl((int)ld_sys(&m->ctl));
+    if ((c & ~kMailClosed) > k) { state = 1; break; }
+    if (c & kMailClosed) { state = -1; break; }
+    if (!block) return 0;
+    const uint64_t waited = wall_clock64() - t0;
+    if (waited > (uint64_t)A.idle_ticks + (uint64_t)P.watchdog_ticks) {
+      // the close did not take (host memory without device atomics): end
+      // with the timeout error rather than spin
+      if (lane == 0) {
+        uint32_t expected = 0u;
+        __hip_atomic_compare_exchange_strong((guint*)(P.ctl + kCtlErr), &expected, (uint32_t)kDevErrTimeout,
+                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      state = -1;
+      break;
+    }
+    if (waited > (uint64_t)A.idle_ticks) {
+      if (lane == 0) {
+        uint32_t expected = c;
+        __hip_atomic_compare_exchange_strong((guint*)&m->ctl, &expected, c | kMailClosed, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+      wait_vm0();
+      continue;
+    }
+    __builtin_amdgcn_s_sleep(4);
+  }
+  const int slot = (int)(k % kMailRing) * kReqWords;
+  if (state > 0) {
+    const int v = lane <= kMaxBatch ? ld_sys(&m->req[0][0] + slot + lane) : 0;
+    take_fields(v, rq);
+    if (lane <= kMaxBatch)
+      for (int c = 0; c < kSrvCopies; ++c) st_coh(P.srv_slot + c * kMailRing * kReqWords + slot + 2 + lane, v);
+  }
+  wait_vm0();   // the fields have landed before any tag
+  if (lane < kSrvCopies)
+    st_coh64(reinterpret_cast<uint64_t*>(P.srv_slot + lane * kMailRing * kReqWords + slot), srv_tag(A, k, state < 0));
+  rq.state = state;
+  return state;
+}
+
+// Every other workgroup: request k from its device slot copy (tag first, then
+// the fields, which workgroup 0 stored before the tag).  With `block`, waits
+// until workgroup 0 has decided; that takes at most the idle bound, so a wait
+// past it plus the watchdog bound, or an error raised by any workgroup, ends
+// the launch here (the watchdog case raising the timeout error).
+__device__ int w0_device_request(const Params& P, const Launch& A, uint32_t k, bool block, Request& rq) {
+  const int lane = threadIdx.x & 63;
+  const int32_t* slot = P.srv_slot + (blockIdx.x % kSrvCopies) * kMailRing * kReqWords + (k % kMailRing) * kReqWords;
+  const uint64_t go = srv_tag(A, k, false), end = srv_tag(A, k, true);
+  const uint64_t t0 = wall_clock64();
+  const uint64_t limit = (uint64_t)A.idle_ticks + (uint64_t)P.watchdog_ticks;
+  int state;
+  while (true) {
+    const uint64_t t = ld_coh64(reinterpret_cast<const uint64_t*>(slot));
+    const uint64_t tu = ((uint64_t)(uint32_t)rfl((int)(t >> 32)) << 32) | (uint32_t)rfl((int)(uint32_t)t);
+    if (tu == go) { state = 1; break; }
+    if (tu == end) { state = -1; break; }
+    if (!block) return 0;
+    if (rfl((int)ld_coh(P.ctl + kCtlErr)) != 0) { state = -1; break; }
+    if (wall_clock64() - t0 > limit) {
+      if (lane == 0) {
+        uint32_t expected = 0u;
+        __hip_atomic_compare_exchange_strong((guint*)(P.ctl + kCtlErr), &expected, (uint32_t)kDevErrTimeout,
+                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      state = -1;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  if (state > 0) take_fields(lane <= kMaxBatch ? ld_coh(slot + 2 + lane) : 0, rq);
+  rq.state = state;
+  return state;
+}
+
+__device__ __forceinline__ int srv_request(const Params& P, const Launch& A, uint32_t k, bool block, Request& rq) {
+  return blockIdx.x == 0 ? w0_host_request(P, A, k, block, rq) : w0_device_request(P, A, k, block, rq);
+}
+
+// Workgroup 0 after request k's greedy tokens: store them for the host now;
+// the completion count follows once they have landed (srv_flush_done), at
+// this wave's next wait for its stores or before it blocks for a request.
+template <int MB>
+__device__ __forceinline__ void srv_post_tokens(const Params& P, uint32_t k, const int* tok, int& done_pending) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int b = 0; b < MB; ++b)
+    if (lane == b && b < P.B) st_sys(&P.mail->tok[k % kMailRing][b], tok[b]);
+  done_pending = (int)k + 1;
+}
+__device__ __forceinline__ void srv_flush_done(const Params& P, int& done_pending) {
+  if (done_pending <= 0) return;
+  wait_vm0();
+  if ((threadIdx.x & 63) == 0) st_sys(&P.mail->done, (uint32_t)done_pending);
+  done_pending = 0;
+}
+
+// where the LM head's logits go for token i: none, the device buffer (the
+// last token of a launch that wants them) or the host (a server request
+// that wants them)
+__device__ __forceinline__ int lg_mode(const Launch& A, int i, bool cur_lg) {
+  if (A.server) return cur_lg ? 2 : 0;
+  return A.write_logits && i == A.n_tok - 1 ? 1 : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -1594,6 +1756,12 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   }
   uint32_t epoch = A.bar_base;
   bool first = true, have_tok = false, gains_ready = false;
+  // server launch: the next request when read ahead, whether the current
+  // token's logits go to the host, and workgroup 0's unpublished completion
+  Request rq;
+  rq.state = 0;
+  bool cur_lg = false;
+  int done_pending = 0;
   int tok_local[MB];
 #pragma unroll
   for (int b = 0; b < MB; ++b) tok_local[b] = 0;
@@ -1608,7 +1776,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       if constexpr (MB > 1)
         if (is_gemv(prev_ph)) w0_combine<MB>(prev_ph, plan, slots, out);
       w0_store_outputs<MB>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
-                           A.write_logits && prev_i == A.n_tok - 1, scl, out, xown, aux);
+                           lg_mode(A, prev_i, cur_lg), scl, out, xown, aux);
     }
     if (MB == 1 && is_gemv(id.ph)) {
       // the batch-1 streamers add into out (ds_add); the batched kernel's
@@ -1621,6 +1789,9 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       ++epoch;
       if (P.stress) stress_delay(epoch);
       w0_arrive(P, A.fenced);
+      // server launch: the previous request's tokens have landed with this
+      // arrival's wait; its completion can go out
+      if (A.server && blockIdx.x == 0) srv_flush_done(P, done_pending);
       if constexpr (MB == 1)
         if (id.ph == PH_O && P.H > (int)gridDim.x / 32 && (int)blockIdx.x / wg_per_head(P, pos) >= P.H)
           w0_warm_gu(P, tab_all, id.l, smem + M::Sink);
@@ -1649,6 +1820,19 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       if (!ok) return;
     } else if (id.ph == PH_QKV && id.l == 0) {
       ok = wait();
+      bool forced = A.n_force && id.i == 0;
+      if (ok && A.server) {
+        // a server launch: token i is request i, or the launch ends here
+        if (rq.state == 0) {
+          if (blockIdx.x == 0) srv_flush_done(P, done_pending);   // the host may be waiting for it
+          srv_request(P, A, (uint32_t)id.i, true, rq);
+        }
+        ok = rq.state > 0;
+        forced = (rq.flags & kReqForce) != 0;
+        cur_lg = (rq.flags & kReqLogits) != 0;
+        rq.state = 0;
+        if (!ok && blockIdx.x == 0) srv_flush_done(P, done_pending);
+      }
       if (ok) {
 #pragma unroll
         for (int b = 0; b < MB; ++b) {
@@ -1658,7 +1842,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
               if (!P.cols_pos) tok = ldg(P.prompt + (size_t)b * A.n_tok + id.i);
               else tok = pos + b < A.pos_end ? ldg(P.prompt + (pos + b - A.pos0)) : 0;
             }
-            else if (A.n_force && id.i == 0) tok = A.force[b];   // teacher forcing: the launch argument
+            else if (forced) tok = A.server ? rq.tok[b] : A.force[b];   // teacher forcing
             else tok = have_tok ? tok_local[b] : ld_coh(P.tok_cur + b);
             tok = tok < 0 ? 0 : (tok >= P.V ? P.V - 1 : tok);
             w0_embed<MB>(P, b, tok, MB == 1 ? xs : stage + (size_t)b * gemv_span(P.d), xown, own);
@@ -1684,6 +1868,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       if (ok) {
         w0_argmax<MB>(P, id.i, P.cols_pos ? min(A.pos_end - 1 - pos, B - 1) : -1, tok_local);
         have_tok = true;
+        if (A.server && blockIdx.x == 0) srv_post_tokens<MB>(P, (uint32_t)id.i, tok_local, done_pending);
       }
     }
     if (id.ph != PH_ATTN) {
@@ -1736,6 +1921,12 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       }
       scl[lane] = s;
     }
+    // server launch: read the next request ahead, while the streamers run --
+    // workgroup 0 from the host early in the token, the others from their
+    // device slot in the LM head, long after workgroup 0 has filled it
+    if (A.server && rq.state == 0 && id.i + 1 < A.n_tok &&
+        ((blockIdx.x == 0 && ((id.ph == PH_GU && id.l == 0) || id.ph == PH_LM)) || (blockIdx.x != 0 && id.ph == PH_LM)))
+      srv_request(P, A, (uint32_t)id.i + 1u, false, rq);
     stamp();
     __syncthreads();   // S2
     stamp();
@@ -1747,8 +1938,9 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     if constexpr (MB > 1)
       if (is_gemv(prev_ph)) w0_combine<MB>(prev_ph, plan, slots, out);
     w0_store_outputs<MB>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
-                         A.write_logits && prev_i == A.n_tok - 1, scl, out, xown, aux);
+                         lg_mode(A, prev_i, cur_lg), scl, out, xown, aux);
   }
+  if (A.server && blockIdx.x == 0) srv_flush_done(P, done_pending);
   wait_vm0();
 }
 

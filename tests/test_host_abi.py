@@ -238,6 +238,14 @@ def test_init_errors_before_any_device_work(lib, good_file, tmp_path):
     with pytest.raises(B.DecError) as e:   # the no-allocation handle needs a caller arena and stream
         B.Decoder(desc(), tensors=t, noalloc=True)
     assert e.value.code == B.DEC_ERR_INVALID_ARG
+    # the decode server: idle bound in [0, 10 s]; one resident launch with
+    # host-pinned memory, so neither with one launch per phase nor without allocation
+    for kw in (dict(serve_idle_us=-1), dict(serve_idle_us=10_000_001),
+               dict(serve_idle_us=1000, debug_flags=B.DEC_DEBUG_MULTILAUNCH),
+               dict(serve_idle_us=1000, noalloc=True)):
+        with pytest.raises(B.DecError) as e:
+            B.Decoder(desc(), tensors=t, **kw)
+        assert e.value.code == B.DEC_ERR_INVALID_ARG, kw
 
 
 def test_init_without_gpu_reports_no_device(lib, good_file):
