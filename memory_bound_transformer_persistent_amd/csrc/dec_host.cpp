@@ -281,8 +281,8 @@ bool same_shape(const dec_model_desc& a, const dec_model_desc& b) {
 // device arena layout (bytes)
 // ---------------------------------------------------------------------------
 struct Arena {
-  size_t w, w2, gains, rope, kv, x, qkv, att_o, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out, prompt, ctl,
-      srv_slot, params, params2, trace, total;
+  size_t w, w2, gains, rope, kv, x, xg16, ssp, qkv, att_o, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out,
+      prompt, ctl, srv_slot, params, params2, trace, total;
 };
 
 bool batched_prefill(const dec_model_desc& d) { return (d.flags & DEC_FLAG_BATCHED_PREFILL) != 0; }
@@ -315,6 +315,8 @@ Arena arena_layout(const dec_model_desc& d, int G) {
   a.rope = take((size_t)d.max_ctx * (d.head_dim / 2) * 2 * 4);
   a.kv = take((size_t)d.n_layers * 2 * hkv * d.max_ctx * d.head_dim * 2);
   a.x = take(B * D * 4);
+  a.xg16 = take(B * D * 2);
+  a.ssp = take((size_t)G * kMaxBatch * 4);
   a.qkv = take(B * 3 * q * 4);
   a.att_o = take(B * q * 4);
   a.part = take(part_rows * d.head_dim * 4);
@@ -962,6 +964,8 @@ int init_impl(const dec_model_desc* desc, const dec_weights_src* weights, const 
   P.B = desc->batch;
   P.kv = reinterpret_cast<uint16_t*>(b + h->ar.kv);
   P.x = reinterpret_cast<float*>(sc(h->ar.x));
+  P.xg16 = reinterpret_cast<uint16_t*>(sc(h->ar.xg16));
+  P.ssp = reinterpret_cast<float*>(sc(h->ar.ssp));
   P.qkv = reinterpret_cast<float*>(sc(h->ar.qkv));
   P.att_o = reinterpret_cast<float*>(sc(h->ar.att_o));
   P.att_o16 = reinterpret_cast<uint16_t*>(sc(h->ar.att_o));

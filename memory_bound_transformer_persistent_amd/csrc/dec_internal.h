@@ -123,6 +123,11 @@ struct Params {
   uint64_t* trace;            // optional [G][trace_stride] wall-clock stamps (phase start, phase end, ...)
   int trace_stride;
   int stress;                 // 1: random delays before every arrival, NaN-poisoned exchange buffers
+  // batched kernel: the normed phases' inputs, published by the O and down
+  // phases: x times the next norm's gains in fp16 [B][d], and each
+  // workgroup's partial sums of x^2 [G][kMaxBatch]
+  uint16_t* xg16;
+  float* ssp;
   Mailbox* mail;              // decode server mailbox (device address of host-pinned memory) or null
   float* lg_sys;              // decode server logits [B][Vlm] (device address of host-pinned memory) or null
   int32_t* srv_slot;          // decode server request slots [kSrvCopies][kMailRing][kReqWords]

@@ -729,6 +729,12 @@ __device__ __forceinline__ void w0_poison(const Params& P, int ph, int l, const 
     own_rows<MB>(P, r0, r1);
     for (int b = 0; b < B; ++b)
       for (int r = r0 + lane; r < r1; r += 64) st_coh(reinterpret_cast<uint32_t*>(P.x + (size_t)b * P.d + r), nan32);
+    if constexpr (MB > 1) {
+      // and the normed inputs published with them
+      for (int b = 0; b < B; ++b)
+        for (int r = r0 + lane; r < r1; r += 64) st_coh(P.xg16 + (size_t)b * P.d + r, nan16);
+      if (lane < MB) st_coh(reinterpret_cast<uint32_t*>(P.ssp + (size_t)blockIdx.x * kMaxBatch + lane), nan32);
+    }
   }
   if (ph == PH_QKV) {
     // this workgroup's SwiGLU outputs, read by the last DOWN input pull; GU publishes them next
@@ -806,16 +812,29 @@ template <int MB>
 __device__ __forceinline__ void dma_input_share(const Params& P, const PhaseIt& id, float* xs, int w) {
   const int lane = threadIdx.x & 63;
   const bool normed = id.ph != PH_DOWN && id.ph != PH_O;
-  const int n = normed ? P.d : (id.ph == PH_DOWN ? P.F : P.q), esize = normed ? 4 : 2;
-  const int span_bytes = gemv_span(n) * esize, nch = span_bytes >> 10;
-  char* base = normed ? reinterpret_cast<char*>(xs + kMaxBatch * gemv_span(P.d) / 2) : reinterpret_cast<char*>(xs);
+  const int n = normed ? P.d : (id.ph == PH_DOWN ? P.F : P.q);
+  const int span_bytes = gemv_span(n) * 2, nch = span_bytes >> 10;
+  char* base = reinterpret_cast<char*>(xs);
   for (int k = w; k < P.B * nch; k += kWaves) {
     const int b = k / nch, c = k - b * nch;
-    const void* src = normed ? (const void*)(P.x + (size_t)b * P.d)
-                             : (const void*)((id.ph == PH_DOWN ? P.act16 + (size_t)b * P.F : P.att_o16 + (size_t)b * P.q));
-    const rsrc_t r = make_rsrc(src, (uint32_t)(n * esize));
+    const uint16_t* src = normed ? P.xg16 + (size_t)b * P.d
+                                 : (id.ph == PH_DOWN ? P.act16 + (size_t)b * P.F : P.att_o16 + (size_t)b * P.q);
+    const rsrc_t r = make_rsrc(src, (uint32_t)(n * 2));
     dma16_coh(r, base + (size_t)b * span_bytes + 1024 * c, (uint32_t)(1024 * c + 16 * lane));
   }
+}
+
+// Batched kernel, wave w, a normed phase whose input was published by the O
+// or down phase: red[b * kWaves + w] <- the sum of workgroups w*8 + j, j +=
+// 64, of their partial sums of x^2 of sequence b (fixed order).
+__device__ __forceinline__ void ss_share(const Params& P, int w, float* red) {
+  const int lane = threadIdx.x & 63, b = lane & (kMaxBatch - 1);
+  float ss = 0.f;
+  for (int g = w * 8 + (lane >> 3); g < (int)gridDim.x; g += 64) ss += ld_coh(P.ssp + (size_t)g * kMaxBatch + b);
+  ss += __shfl_xor(ss, 8, 64);
+  ss += __shfl_xor(ss, 16, 64);
+  ss += __shfl_xor(ss, 32, 64);
+  if (lane < kMaxBatch) red[lane * kWaves + w] = ss;
 }
 
 // MB == 1, all waves: xs[0..n) *= gs[0..n); red[wave] <- this wave's share of sum(x^2).
@@ -1163,7 +1182,8 @@ __device__ __forceinline__ void w0_merge_wg(const Params& P, int pos, int pos_en
 template <int MB>
 __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l, int pos, int pos_end,
                                                  const int* tab_wg, int lg_mode, const float* scl,
-                                                 const float* out, float* xown, const float* rope_lds) {
+                                                 const float* out, float* xown, const float* rope_lds,
+                                                 const float* gs_next) {
   const int lane = threadIdx.x & 63, B = P.B;
   if (!is_gemv(ph)) return;
   const int p0 = rfl(tab_wg[2 * ph]);
@@ -1205,13 +1225,29 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l,
       }
     }
   } else if (ph == PH_O || ph == PH_DOWN) {
+    float ss = 0.f;
     for (int e = lane; e < 2 * n * MB; e += 64) {
       const int t = e / MB, b = e - t * MB;
       if (b < B) {
         const float v = xown[b * own + t] + out[e];
         xown[b * own + t] = v;
         st_coh(P.x + (size_t)b * P.d + 2 * p0 + t, v);
+        if constexpr (MB > 1) {
+          // batched: the next normed phase's input, x times its gains (held in
+          // gs since that phase's gains were fetched), in fp16, and this
+          // workgroup's share of sum(x^2)
+          const _Float16 hv = (_Float16)(v * gs_next[2 * p0 + t]);
+          st_coh(P.xg16 + (size_t)b * P.d + 2 * p0 + t, __builtin_bit_cast(uint16_t, hv));
+          ss += v * v;
+        }
       }
+    }
+    if constexpr (MB > 1) {
+      // lane l holds sequence l % MB's share (64 is a multiple of MB)
+      ss += __shfl_xor(ss, 8, 64);
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      if (lane < MB) st_coh(P.ssp + (size_t)blockIdx.x * kMaxBatch + lane, ss);
     }
   } else if (ph == PH_GU) {
     for (int e = lane; e < n * MB; e += 64) {
@@ -1647,11 +1683,15 @@ __device__ __forceinline__ void streamer_tiles(const Params& P, const Launch& A,
     __syncthreads();   // S1a
     if (si[12] == 0) break;
     if (dma_input(id)) {
-      dma_input_share<MB>(P, id, xs, rfl((int)(threadIdx.x >> 6)));
+      const int w = rfl((int)(threadIdx.x >> 6));
+      dma_input_share<MB>(P, id, xs, w);
+      if (norm_phase(id)) ss_share(P, w, red);
       wait_vm0();
     }
     __syncthreads();   // S1b: the phase input is in LDS
-    if (norm_phase(id))
+    // the embedded layer-0 input: x times the gains here (the others came
+    // multiplied from their producers)
+    if (norm_phase(id) && !dma_input(id))
       apply_gains_batch(reinterpret_cast<_Float16*>(xs), xs + kMaxBatch * gemv_span(P.d) / 2, gs, P.d, B, red);
     __syncthreads();   // S1
     if (is_gemv(id.ph)) {
@@ -1776,7 +1816,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       if constexpr (MB > 1)
         if (is_gemv(prev_ph)) w0_combine<MB>(prev_ph, plan, slots, out);
       w0_store_outputs<MB>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
-                           lg_mode(A, prev_i, cur_lg), scl, out, xown, aux);
+                           lg_mode(A, prev_i, cur_lg), scl, out, xown, aux, gs);
     }
     if (MB == 1 && is_gemv(id.ph)) {
       // the batch-1 streamers add into out (ds_add); the batched kernel's
@@ -1802,8 +1842,20 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     auto wait = [&]() { return skip_bar ? true : w0_wait(P, epoch, A.fenced); };
     // the norm gains do not depend on the barrier: they were prefetched
     // during the previous normed phase, else start them now
-    if (norm_phase(id) && !gains_ready) w0_dma_vec(gs, norm_gains(P, id), P.d, 4, false);
-    gains_ready = false;
+    if (norm_phase(id)) {
+      if (!gains_ready) w0_dma_vec(gs, norm_gains(P, id), P.d, 4, false);
+      gains_ready = false;
+    }
+    if constexpr (MB > 1) {
+      // the O and down outputs are published multiplied by the next norm's
+      // gains; a launch that did not run the normed phase before fetches them
+      if ((id.ph == PH_O || id.ph == PH_DOWN) && !gains_ready) {
+        const float* gn = id.ph == PH_O ? P.gains + ((size_t)id.l * 2 + 1) * P.d
+                                        : P.gains + (size_t)min(2 * (id.l + 1), 2 * P.L) * P.d;
+        w0_dma_vec(gs, gn, P.d, 4, false);
+        gains_ready = true;
+      }
+    }
     bool ok = true;
     if (id.ph == PH_ATTN) {
       // the streamers take attention units too: release them (S1a) right
@@ -1881,6 +1933,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
         // batched: every wave lands its share of the inputs of all sequences
         if (dma_input(id)) {
           dma_input_share<MB>(P, id, xs, 0);
+          if (norm_phase(id)) ss_share(P, 0, red);
           wait_vm0();
         }
         __syncthreads();   // S1b
@@ -1888,7 +1941,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     }
     if (norm_phase(id)) {
       if constexpr (MB == 1) apply_gains(xs, gs, P.d, red);
-      else apply_gains_batch(reinterpret_cast<_Float16*>(xs), stage, gs, P.d, B, red);
+      else if (!dma_input(id)) apply_gains_batch(reinterpret_cast<_Float16*>(xs), stage, gs, P.d, B, red);
     }
     __syncthreads();   // S1
     if (P.stress) w0_poison<MB>(P, id.ph, id.l, tab_wg);
@@ -1938,7 +1991,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     if constexpr (MB > 1)
       if (is_gemv(prev_ph)) w0_combine<MB>(prev_ph, plan, slots, out);
     w0_store_outputs<MB>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
-                         lg_mode(A, prev_i, cur_lg), scl, out, xown, aux);
+                         lg_mode(A, prev_i, cur_lg), scl, out, xown, aux, gs);
   }
   if (A.server && blockIdx.x == 0) srv_flush_done(P, done_pending);
   wait_vm0();
