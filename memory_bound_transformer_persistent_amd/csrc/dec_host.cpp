@@ -323,8 +323,10 @@ Arena arena_layout(const dec_model_desc& d, int G) {
   a.pml = take(part_rows * 2 * 4);
   a.act = take(B * d.d_ffn * 4);
   a.logits = take(B * d.lm_vocab * 4);
-  a.amax_v = take(B * G * 4);
-  a.amax_i = take(B * G * 4);
+  // argmax partials: [G] at batch 1, [G][kMaxBatch] for the batched kernel
+  const size_t Bk = B > 1 ? (size_t)kMaxBatch : 1;
+  a.amax_v = take(Bk * G * 4);
+  a.amax_i = take(Bk * G * 4);
   a.tok_cur = take(B * 4);
   a.tok_out = take((size_t)d.max_ctx * B * 4);
   a.prompt = take((size_t)d.max_ctx * B * 4);

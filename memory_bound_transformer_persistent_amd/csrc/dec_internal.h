@@ -112,8 +112,8 @@ struct Params {
   float* act;                 // SwiGLU output [F] (batch 1, fp32)
   uint16_t* act16;            // SwiGLU output [B][F] (batch > 1, fp16; same memory as act)
   float* logits;              // [B][Vlm]
-  float* amax_v;              // per-workgroup best logit [B][G]
-  int* amax_i;                // per-workgroup best index [B][G]
+  float* amax_v;              // per-workgroup best logit: [G] at batch 1, [G][kMaxBatch] batched
+  int* amax_i;                // its row (lowest on ties), same layout
   int* tok_cur;               // token each sequence's next step consumes [B]
   int* tok_out;               // greedy tokens of a launch [max_ctx][B]
   const int* prompt;          // tokens of a prompt launch [B][n_tok]

@@ -769,7 +769,7 @@ __device__ __forceinline__ void w0_poison(const Params& P, int ph, int l, const 
   if (ph == PH_ATTN && l == 0) {
     // argmax partials, read by the previous token's ARGMAX phase, which no
     // barrier separates from this token's QKV phase
-    share(B * G, a, e);
+    share((MB == 1 ? 1 : kMaxBatch) * G, a, e);
     for (int i = a + lane; i < e; i += 64) {
       st_coh(reinterpret_cast<uint32_t*>(P.amax_v + i), nan32);
       st_coh(P.amax_i + i, -1);
@@ -1259,42 +1259,53 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l,
         else st_coh(P.act16 + (size_t)b * P.F + p0 + t, __builtin_bit_cast(uint16_t, (_Float16)a));
       }
     }
-  } else if (ph == PH_LM) {
-    // every sequence's best logit among this workgroup's rows, in one pass
-    float best[MB];
-    int bidx[MB];
-#pragma unroll
-    for (int b = 0; b < MB; ++b) { best[b] = -INFINITY; bidx[b] = 0x7fffffff; }
+  } else if (ph == PH_LM && MB == 1) {
+    // this workgroup's best logit (lowest row on ties)
+    float best = -INFINITY;
+    int bidx = 0x7fffffff;
     for (int t = lane; t < 2 * n; t += 64) {
-#pragma unroll
-      for (int b = 0; b < MB; ++b) {
-        if (b < B) {
-          const float v = out[t * MB + b] * scl[b];
-          if (v > best[b]) { best[b] = v; bidx[b] = 2 * p0 + t; }
-          // logits: 1 = the device buffer; 2 = the host's pinned buffer (a server
-          // launch keeps running while the host reads them)
-          if (lg_mode == 1) st_g(P.logits + (size_t)b * P.Vlm + 2 * p0 + t, v);
-          else if (lg_mode == 2) st_sys(P.lg_sys + (size_t)b * P.Vlm + 2 * p0 + t, v);
-        }
-      }
+      const float v = out[t] * scl[0];
+      if (v > best) { best = v; bidx = 2 * p0 + t; }
+      // logits: 1 = the device buffer; 2 = the host's pinned buffer (a server
+      // launch keeps running while the host reads them)
+      if (lg_mode == 1) st_g(P.logits + 2 * p0 + t, v);
+      else if (lg_mode == 2) st_sys(P.lg_sys + 2 * p0 + t, v);
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
-#pragma unroll
-      for (int b = 0; b < MB; ++b) {
-        const float ov = __shfl_xor(best[b], off, 64);
-        const int oi = __shfl_xor(bidx[b], off, 64);
-        if (ov > best[b] || (ov == best[b] && oi < bidx[b])) { best[b] = ov; bidx[b] = oi; }
-      }
+      const float ov = __shfl_xor(best, off, 64);
+      const int oi = __shfl_xor(bidx, off, 64);
+      if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
     }
     if (lane == 0) {
-#pragma unroll
-      for (int b = 0; b < MB; ++b) {
-        if (b < B) {
-          st_coh(P.amax_v + (size_t)b * gridDim.x + blockIdx.x, best[b]);
-          st_coh(P.amax_i + (size_t)b * gridDim.x + blockIdx.x, bidx[b]);
-        }
+      st_coh(P.amax_v + blockIdx.x, best);
+      st_coh(P.amax_i + blockIdx.x, bidx);
+    }
+  } else if (ph == PH_LM) {
+    // batched: lane l scans sequence b = l % MB over rows l / MB, l / MB + 8,
+    // ... (consecutive LDS words across the wave), so each sequence's best
+    // is reduced over its 8 lanes only; partials go to [workgroup][kMaxBatch]
+    const int b = lane & (MB - 1);
+    float best = -INFINITY;
+    int bidx = 0x7fffffff;
+    if (b < B) {
+      const float sb = scl[b];
+      for (int t = lane / MB; t < 2 * n; t += 64 / MB) {
+        const float v = out[t * MB + b] * sb;
+        if (v > best) { best = v; bidx = 2 * p0 + t; }
+        if (lg_mode == 1) st_g(P.logits + (size_t)b * P.Vlm + 2 * p0 + t, v);
+        else if (lg_mode == 2) st_sys(P.lg_sys + (size_t)b * P.Vlm + 2 * p0 + t, v);
       }
+    }
+#pragma unroll
+    for (int off = MB; off < 64; off <<= 1) {
+      const float ov = __shfl_xor(best, off, 64);
+      const int oi = __shfl_xor(bidx, off, 64);
+      if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
+    }
+    if (lane < B) {
+      st_coh(P.amax_v + (size_t)blockIdx.x * kMaxBatch + lane, best);
+      st_coh(P.amax_i + (size_t)blockIdx.x * kMaxBatch + lane, bidx);
     }
   }
 }
@@ -1306,44 +1317,72 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l,
 template <int MB>
 __device__ __forceinline__ void w0_argmax(const Params& P, int i, int cur_col, int* tok) {
   const int lane = threadIdx.x & 63, G = gridDim.x, B = P.B;
-  const rsrc_t rv = make_rsrc(P.amax_v, (uint32_t)(B * G * 4)), ri = make_rsrc(P.amax_i, (uint32_t)(B * G * 4));
-  float bv[MB];
-  int bi[MB];
-#pragma unroll
-  for (int b = 0; b < MB; ++b) { bv[b] = -INFINITY; bi[b] = 0x7fffffff; }
-  constexpr int K = MB == 1 ? 4 : 2;   // partials per lane per sequence and pass
-  for (int t0 = 0; t0 < G; t0 += 64 * K) {
-    float v[MB][K];
-    int ix[MB][K];
-#pragma unroll
-    for (int b = 0; b < MB; ++b)
+  auto better = [](float v, int ix, float bv, int bi) { return v > bv || (v == bv && ix < bi); };
+  if constexpr (MB == 1) {
+    const rsrc_t rv = make_rsrc(P.amax_v, (uint32_t)(G * 4)), ri = make_rsrc(P.amax_i, (uint32_t)(G * 4));
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    constexpr int K = 4;   // partials per lane per pass, all requested before any is compared
+    for (int t0 = 0; t0 < G; t0 += 64 * K) {
+      float v[K];
+      int ix[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const int t = t0 + lane + 64 * k;
-        const uint32_t off = (b < B && t < G) ? (uint32_t)(b * G + t) * 4u : kOOB;
-        v[b][k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, kAuxSc1));
-        ix[b][k] = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, off, 0, kAuxSc1);
+        const uint32_t off = t < G ? (uint32_t)t * 4u : kOOB;
+        v[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, kAuxSc1));
+        ix[k] = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, off, 0, kAuxSc1);
       }
 #pragma unroll
-    for (int b = 0; b < MB; ++b)
-#pragma unroll
       for (int k = 0; k < K; ++k)
-        if (t0 + lane + 64 * k < G && (v[b][k] > bv[b] || (v[b][k] == bv[b] && ix[b][k] < bi[b]))) {
-          bv[b] = v[b][k];
-          bi[b] = ix[b][k];
-        }
+        if (t0 + lane + 64 * k < G && better(v[k], ix[k], bv, bi)) { bv = v[k]; bi = ix[k]; }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    tok[0] = (bi == 0x7fffffff) ? 0 : bi;
+  } else {
+    // partials at [workgroup][kMaxBatch]: lane l takes sequence l % MB of
+    // workgroups l / MB + 8 j (consecutive words across the wave), all
+    // requested before any is compared, then the 8 lanes of each sequence
+    // combine theirs
+    const int b = lane & (MB - 1);
+    const uint32_t bytes = (uint32_t)(G * kMaxBatch * 4);
+    const rsrc_t rv = make_rsrc(P.amax_v, bytes), ri = make_rsrc(P.amax_i, bytes);
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    constexpr int J = 32;
+    for (int g0 = 0; g0 < G; g0 += J * (64 / MB)) {
+      float v[J];
+      int ix[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int g = g0 + lane / MB + (64 / MB) * j;
+        const uint32_t off = (b < B && g < G) ? (uint32_t)(g * kMaxBatch + b) * 4u : kOOB;
+        v[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, kAuxSc1));
+        ix[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, off, 0, kAuxSc1);
+      }
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (b < B && g0 + lane / MB + (64 / MB) * j < G && better(v[j], ix[j], bv, bi)) { bv = v[j]; bi = ix[j]; }
+    }
+#pragma unroll
+    for (int off = MB; off < 64; off <<= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+#pragma unroll
+    for (int bb = 0; bb < MB; ++bb) {
+      const int t = __builtin_amdgcn_readlane(bi, bb);
+      tok[bb] = (t == 0x7fffffff) ? 0 : t;
+    }
   }
 #pragma unroll
   for (int b = 0; b < MB; ++b) {
-    float bvv = bv[b];
-    int bii = bi[b];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bvv, off, 64);
-      const int oi = __shfl_xor(bii, off, 64);
-      if (ov > bvv || (ov == bvv && oi < bii)) { bvv = ov; bii = oi; }
-    }
-    tok[b] = (bii == 0x7fffffff) ? 0 : bii;
     if (b < B && blockIdx.x == 0 && lane == 0) {
       if (cur_col < 0) st_coh(P.tok_cur + b, tok[b]);
       else if (b == cur_col) st_coh(P.tok_cur, tok[b]);
