@@ -43,7 +43,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "decode tokens/s per request (bs=1) and achieved HBM GB/s vs peak, 1 MI355X"
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_dec_resident_dense2b.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "memory_bound_transformer_persistent_amd", "csrc", "dec_kernels.hip")
 EXTRAS = ("lane2b", "dense2b_long", "dense2b_b8")
 SERVE_IDLE_US = 200000   # decode server: a launch ends after 0.2 s without a step
@@ -53,13 +53,14 @@ def kernel_hash():
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic(workload):
-    """HBM bytes per launch from the committed PMC summary, if it was taken on
-    this kernel source and this workload."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+def read_traffic(kernel, workload):
+    """HBM bytes per step from the committed PMC summary of this kernel and
+    workload, if it was taken on this kernel source."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
         return None
     rec = {}
-    for line in open(PROFILE_TRAFFIC):
+    for line in open(path):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             rec[k.strip()] = v.strip()
@@ -173,6 +174,7 @@ class Run:
             "ms_per_step": round(region_ms / K, 4), "positions": [pos0, pos0 + K - 1], "batch": nb,
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": R.MI355X_HBM_PEAK / 1e9,
                          "unit": "GB/s", "frac": round(achieved / (R.MI355X_HBM_PEAK / 1e9), 4),
+                         "traffic": read_traffic(kernel, self.w.name),
                          "kernel": kernel, "algorithmic_bytes_per_launch": int(per_launch),
                          "avg_launch_ms": round(avg_s * 1e3, 4)},
             "roofline_tokens_per_s_per_request": round(R.roofline_tokens_per_s(s, pos0, K, nb), 1),
@@ -289,7 +291,8 @@ def main():
     tok_s = req_tok_s * nb                     # whole-job tokens/s
     achieved = bytes_per_launch / avg_launch_s / 1e9
     peak = R.MI355X_HBM_PEAK / 1e9
-    traffic = read_traffic(w.name) if args.mode == "step" and not args.multilaunch else None
+    # per step (counted on single-step launches; a server launch streams the same bytes per step)
+    traffic = read_traffic(kernel_name(w), w.name) if args.mode != "generate" and not args.multilaunch else None
     roof_tps = R.roofline_tokens_per_s(s, pos0, K, nb)   # per request
 
     out = {
@@ -315,7 +318,12 @@ def main():
                      "traffic": traffic,
                      "kernel": kernel_name(w),
                      "algorithmic_bytes_per_launch": int(bytes_per_launch),
-                     "avg_launch_ms": round(avg_launch_s * 1e3, 4)},
+                     "avg_launch_ms": round(avg_launch_s * 1e3, 4),
+                     # a decode-server launch serves several steps: the two
+                     # fields above are then per step, and a launch's duration
+                     # in a kernel trace is steps_per_launch times avg_launch_ms
+                     "steps_per_launch": K if args.mode == "generate" else (K // len(segs) if args.mode == "serve" else 1),
+                     "per": "launch" if args.mode != "serve" else "step"},
         "tokens_per_s_per_request": round(req_tok_s, 2),
         "segments_tokens_per_s": None if len(segs) < 2 else {
             "n": len(segs), "steps_each": K // len(segs), "min": round(min(segs), 2),

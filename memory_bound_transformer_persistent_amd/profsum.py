@@ -8,6 +8,7 @@ for the decode kernel, the same over the single-token decode launches alone
 duration); and, for counter runs, each counter's per-dispatch value.
 
     python -m memory_bound_transformer_persistent_amd.profsum trace DIR
+    python -m memory_bound_transformer_persistent_amd.profsum dispatches DIR
     python -m memory_bound_transformer_persistent_amd.profsum counters DIR [KERNEL]
     python -m memory_bound_transformer_persistent_amd.profsum traffic FETCH_DIR WRITE_DIR \\
         COPY_FETCH_DIR COPY_WRITE_DIR COPY_BYTES KERNEL_SOURCE [WORKLOAD]
@@ -73,6 +74,18 @@ def trace_summary(d):
                 s = _stats(dec)
                 lines.append(f"{k} single-token decode launches: n={s['n']} mean {s['mean'] / 1e3:.1f} us, "
                              f"median {s['median'] / 1e3:.1f} us, min {s['min'] / 1e3:.1f} us, max {s['max'] / 1e3:.1f} us")
+    return "\n".join(lines)
+
+
+def dispatch_list(d):
+    """Every decode-kernel dispatch in start order with its duration: a
+    decode-server launch serves many steps, so its duration is per launch."""
+    rows = [r for r in _rows(d, "kernel_trace.csv") if DECODE_KERNEL in _name(r)]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    t0 = int(rows[0]["Start_Timestamp"]) if rows else 0
+    lines = [f"{'#':>4s} {'kernel':28s} {'start ms':>10s} {'duration us':>12s}"]
+    for i, r in enumerate(rows):
+        lines.append(f"{i:4d} {_name(r)[:28]:28s} {(int(r['Start_Timestamp']) - t0) / 1e6:10.3f} {_dur_ns(r) / 1e3:12.1f}")
     return "\n".join(lines)
 
 
@@ -155,6 +168,8 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes, kernel_src
 def main(argv):
     if len(argv) >= 2 and argv[0] == "trace":
         print(trace_summary(argv[1]))
+    elif len(argv) >= 2 and argv[0] == "dispatches":
+        print(dispatch_list(argv[1]))
     elif len(argv) >= 2 and argv[0] == "counters":
         per, dur = counter_values(argv[1], argv[2] if len(argv) > 2 else DECODE_KERNEL)
         for c, v in per.items():

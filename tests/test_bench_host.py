@@ -1,46 +1,58 @@
 """Host logic of bench.py (no GPU): the HBM-traffic figure it reports.
 
-bench.py reports roofline.traffic from the committed rocprofv3 summary only
-while that summary was taken on the current kernel source and the timed
-workload; otherwise the figure is null.
+bench.py reports roofline.traffic from the committed rocprofv3 summary of
+the timed kernel and workload only while that summary was taken on the
+current kernel source; otherwise the figure is null.
 """
 import os
 
 import bench
 
 
-def _write(tmp_path, sha, workload, value="4368000000"):
-    p = tmp_path / "traffic.txt"
-    p.write_text(f"# summary\nkernel = dec_resident_hd128\nworkload = {workload}\n"
+def _write(d, kernel, workload, sha, value="4368000000"):
+    p = d / f"traffic_{kernel}_{workload}.txt"
+    p.write_text(f"# summary\nkernel = {kernel}\nworkload = {workload}\n"
                  f"kernel_sha = {sha}\nhbm_bytes_per_launch = {value}\n")
     return str(p)
 
 
-def test_committed_traffic_summary_is_read_consistently():
-    # the figure of the committed summary while it matches the kernel source,
-    # else null (a summary taken on an older kernel is never reported)
-    assert os.path.exists(bench.PROFILE_TRAFFIC)
+def _record(path):
     rec = {}
-    for line in open(bench.PROFILE_TRAFFIC):
+    for line in open(path):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             rec[k.strip()] = v.strip()
-    current = rec.get("kernel_sha") == bench.kernel_hash() and rec.get("workload") == "dense2b"
-    expected = float(rec["hbm_bytes_per_launch"]) if current else None
-    assert bench.read_traffic("dense2b") == expected
+    return rec
 
 
-def test_traffic_only_for_the_same_source_and_workload(tmp_path, monkeypatch):
+def test_committed_traffic_summaries_are_read_consistently():
+    # the figure of each committed summary while it matches the kernel source,
+    # else null (a summary taken on an older kernel is never reported)
+    for kernel, workload in (("dec_resident_hd128", "dense2b"), ("dec_resident_batch_hd128", "dense2b_b8")):
+        path = os.path.join(bench.PROFILES, f"traffic_{kernel}_{workload}.txt")
+        assert os.path.exists(path), path
+        rec = _record(path)
+        assert rec["workload"] == workload and rec["kernel"] == kernel
+        current = rec.get("kernel_sha") == bench.kernel_hash()
+        expected = float(rec["hbm_bytes_per_launch"]) if current else None
+        assert bench.read_traffic(kernel, workload) == expected
+
+
+def test_traffic_only_for_the_same_source_kernel_and_workload(tmp_path, monkeypatch):
     sha = bench.kernel_hash()
-    monkeypatch.setattr(bench, "PROFILE_TRAFFIC", _write(tmp_path, sha, "dense2b"))
-    assert bench.read_traffic("dense2b") == 4368000000.0
-    assert bench.read_traffic("dense2b_b8") is None          # another workload
-    monkeypatch.setattr(bench, "PROFILE_TRAFFIC", _write(tmp_path, "0" * 16, "dense2b"))
-    assert bench.read_traffic("dense2b") is None             # another kernel source
-    monkeypatch.setattr(bench, "PROFILE_TRAFFIC", _write(tmp_path, sha, "dense2b", value="n/a"))
-    assert bench.read_traffic("dense2b") is None             # unreadable figure
-    monkeypatch.setattr(bench, "PROFILE_TRAFFIC", str(tmp_path / "missing.txt"))
-    assert bench.read_traffic("dense2b") is None
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    _write(tmp_path, "dec_resident_hd128", "dense2b", sha)
+    assert bench.read_traffic("dec_resident_hd128", "dense2b") == 4368000000.0
+    assert bench.read_traffic("dec_resident_hd128", "dense2b_b8") is None        # another workload
+    assert bench.read_traffic("dec_resident_batch_hd128", "dense2b") is None     # another kernel
+    _write(tmp_path, "dec_resident_hd128", "dense2b", "0" * 16)
+    assert bench.read_traffic("dec_resident_hd128", "dense2b") is None           # another kernel source
+    _write(tmp_path, "dec_resident_hd128", "dense2b", sha, value="n/a")
+    assert bench.read_traffic("dec_resident_hd128", "dense2b") is None           # unreadable figure
+    # a summary whose workload line names another workload than its file name
+    p = tmp_path / "traffic_dec_resident_hd128_lane2b.txt"
+    p.write_text(f"kernel = dec_resident_hd128\nworkload = dense2b\nkernel_sha = {sha}\nhbm_bytes_per_launch = 1\n")
+    assert bench.read_traffic("dec_resident_hd128", "lane2b") is None
 
 
 def test_lane_slices_of_drawn_tensors_equal_the_lane_draw():
