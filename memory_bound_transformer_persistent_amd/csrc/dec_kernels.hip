@@ -691,6 +691,9 @@ __device__ __forceinline__ bool w0_wait(const Params& P, uint32_t epoch, int fen
   }
   const bool ok = why == 0;
   if (fenced) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // no load the caller issues after the release moves above the poll loop
+  // (the loads themselves are device-coherent and issue in program order)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   return ok;
 }
 
