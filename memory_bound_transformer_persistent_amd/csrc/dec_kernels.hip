@@ -200,6 +200,10 @@ __device__ __forceinline__ void st_sys(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void st_sys(float* p, float v) {
   __hip_atomic_store((gfloat_rw*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
+// Paths the decode steps never take unless asked for (decode server, debug
+// modes, errors): marked unlikely so that the hot code is laid out densely
+// (wave 0's serial code is instruction-cache bound; 1% at batch 8).
+#define DEC_COLD(x) __builtin_expect(!!(x), 0)
 // relaxed device-scope fetch-add, returning the old value
 __device__ __forceinline__ uint32_t atomic_add_coh(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add((guint*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -657,7 +661,7 @@ __device__ __forceinline__ void issue_tile(TileCursor& cu, uint32_t lane16, int 
 __device__ __forceinline__ void w0_arrive(const Params& P, int fenced) {
   wait_vm0();
   if ((threadIdx.x & 63) == 0) {
-    if (fenced) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (DEC_COLD(fenced)) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const uint32_t old = atomic_add_coh(P.ctl + kCtlGroup0 + 64 * (blockIdx.x % kGroups), 1u);
     __asm__ volatile("" ::"v"(old));
   }
@@ -690,7 +694,7 @@ __device__ __forceinline__ bool w0_wait(const Params& P, uint32_t epoch, int fen
                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const bool ok = why == 0;
-  if (fenced) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (DEC_COLD(fenced)) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   // no load the caller issues after the release moves above the poll loop
   // (the loads themselves are device-coherent and issue in program order)
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1526,7 +1530,7 @@ __device__ __forceinline__ void srv_flush_done(const Params& P, int& done_pendin
 // last token of a launch that wants them) or the host (a server request
 // that wants them)
 __device__ __forceinline__ int lg_mode(const Launch& A, int i, bool cur_lg) {
-  if (A.server) return cur_lg ? 2 : 0;
+  if (DEC_COLD(A.server)) return cur_lg ? 2 : 0;
   return A.write_logits && i == A.n_tok - 1 ? 1 : 0;
 }
 
@@ -1619,7 +1623,7 @@ __device__ __forceinline__ bool streamer_attention(const Params& P, const Launch
     if (P.H > (int)gridDim.x / 32 && (int)blockIdx.x / wg_per_head(P, pos) >= P.H) warm_gu(P, tab, id.l, sink);
   bool ok;
   ok = attention_wg<HD, MB>(P, id.l, pos, A.pos_end, wave, wg_per_head(P, pos), wait_s, aux + kAuxPart);
-  if (!ok) return false;
+  if (DEC_COLD(!ok)) return false;
   wait_vm0();   // this wave's stores are complete before wave 0 arrives at the grid barrier
   __syncthreads();   // S1
   __syncthreads();   // S2
@@ -1825,7 +1829,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   uint64_t* trace = P.trace ? P.trace + (size_t)blockIdx.x * P.trace_stride : nullptr;
   int ev = 0;
   auto stamp = [&]() {
-    if (trace && lane == 0 && ev < P.trace_stride) st_g(trace + ev, wall_clock64());
+    if (DEC_COLD(trace != nullptr) && lane == 0 && ev < P.trace_stride) st_g(trace + ev, wall_clock64());
     ++ev;
   };
   const int own = kOwnFloats / MB;   // xown floats per sequence
@@ -1869,11 +1873,11 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     const bool skip_bar = first || (id.ph == PH_QKV && id.l == 0 && have_tok);
     if (!skip_bar) {
       ++epoch;
-      if (P.stress) stress_delay(epoch);
+      if (DEC_COLD(P.stress)) stress_delay(epoch);
       w0_arrive(P, A.fenced);
       // server launch: the previous request's tokens have landed with this
       // arrival's wait; its completion can go out
-      if (A.server && blockIdx.x == 0) srv_flush_done(P, done_pending);
+      if (DEC_COLD(A.server) && blockIdx.x == 0) srv_flush_done(P, done_pending);
       if constexpr (MB == 1)
         if (id.ph == PH_O && P.H > (int)gridDim.x / 32 && (int)blockIdx.x / wg_per_head(P, pos) >= P.H)
           w0_warm_gu(P, tab_all, id.l, smem + M::Sink);
@@ -1911,11 +1915,11 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       ok = attention_wg<HD, MB>(P, id.l, pos, A.pos_end, 0, wg_per_head(P, pos), wait_attn, aux + kAuxPart);
       wait_vm0();   // this wave's stores are complete before the next arrive
       first = false;
-      if (!ok) return;
+      if (DEC_COLD(!ok)) return;
     } else if (id.ph == PH_QKV && id.l == 0) {
       ok = wait();
       bool forced = A.n_force && id.i == 0;
-      if (ok && A.server) {
+      if (DEC_COLD(A.server) && ok) {
         // a server launch: token i is request i, or the launch ends here
         if (rq.state == 0) {
           if (blockIdx.x == 0) srv_flush_done(P, done_pending);   // the host may be waiting for it
@@ -1962,7 +1966,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       if (ok) {
         w0_argmax<MB>(P, id.i, P.cols_pos ? min(A.pos_end - 1 - pos, B - 1) : -1, tok_local);
         have_tok = true;
-        if (A.server && blockIdx.x == 0) srv_post_tokens<MB>(P, (uint32_t)id.i, tok_local, done_pending);
+        if (DEC_COLD(A.server) && blockIdx.x == 0) srv_post_tokens<MB>(P, (uint32_t)id.i, tok_local, done_pending);
       }
     }
     if (id.ph != PH_ATTN) {
@@ -1970,7 +1974,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       if (lane == 0) si[12] = ok ? 1 : 0;
       first = false;
       __syncthreads();   // S1a
-      if (!ok) return;
+      if (DEC_COLD(!ok)) return;
       if constexpr (MB > 1) {
         // batched: every wave lands its share of the inputs of all sequences
         if (dma_input(id)) {
@@ -1986,7 +1990,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       else if (!dma_input(id)) apply_gains_batch(reinterpret_cast<_Float16*>(xs), stage, gs, P.d, B, red);
     }
     __syncthreads();   // S1
-    if (P.stress) w0_poison<MB>(P, id.ph, id.l, tab_wg);
+    if (DEC_COLD(P.stress)) w0_poison<MB>(P, id.ph, id.l, tab_wg);
     if (id.ph == PH_ATTN) w0_merge_wg<MB>(P, pos, A.pos_end, wg_per_head(P, pos), aux + kAuxPart);
     if (id.ph == PH_QKV) {
       // the rotary rows of this step's positions, for publishing q and k
@@ -2019,7 +2023,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     // server launch: read the next request ahead, while the streamers run --
     // workgroup 0 from the host early in the token, the others from their
     // device slot in the LM head, long after workgroup 0 has filled it
-    if (A.server && rq.state == 0 && id.i + 1 < A.n_tok &&
+    if (DEC_COLD(A.server) && rq.state == 0 && id.i + 1 < A.n_tok &&
         ((blockIdx.x == 0 && ((id.ph == PH_GU && id.l == 0) || id.ph == PH_LM)) || (blockIdx.x != 0 && id.ph == PH_LM)))
       srv_request(P, A, (uint32_t)id.i + 1u, false, rq);
     stamp();
@@ -2035,7 +2039,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     w0_store_outputs<MB>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
                          lg_mode(A, prev_i, cur_lg), scl, out, xown, aux, gs);
   }
-  if (A.server && blockIdx.x == 0) srv_flush_done(P, done_pending);
+  if (DEC_COLD(A.server) && blockIdx.x == 0) srv_flush_done(P, done_pending);
   wait_vm0();
 }
 
