@@ -60,7 +60,7 @@ constexpr int kBlocksInFlight = 2 * kUnitsInFlight;
 constexpr int kTilesInFlight = 8;
 constexpr int kTabStride = 12;   // ints per (streamer, phase type) entry of the phase tables
 constexpr int kStreamerTab = 6 * kTabStride;   // one streamer's entries: phase types 0..5
-constexpr int kPlanInts = 16;    // per phase type: count, then up to 2 * kStreamers combine entries
+constexpr int kPlanInts = 32;    // per phase type: count, up to 2 * kStreamers combine entries; from 16 on the shared groups
 constexpr int kAuxFloats = 2048;
 // aux LDS: the step's rotary rows (up to 1024 floats; live from the QKV GEMV
 // to the QKV publication) and, in the attention phase, the eight waves'
@@ -444,10 +444,12 @@ __device__ __forceinline__ void fill_tables(const Params& P, int wave, int* tab_
 // tiles are usually split over several streamers.  A group that one streamer
 // computes entirely is stored by it directly.  A group several streamers
 // share (only the first or last group of a streamer's range can be shared)
-// is stored by each of them in its own slot, and wave 0 adds the slots in
-// streamer order: the result does not depend on which streamer finished
-// first.  The plan lists, per phase type, the shared (streamer, end) slots in
-// that order; an entry is slot | group << 4 | (first slot of its group) << 28.
+// is stored by each of them in its own slot, and after the phase all eight
+// waves add the slots in streamer order (combine_all): the result does not
+// depend on which streamer finished first.  The plan lists, per phase type,
+// the shared (streamer, end) slots in that order (an entry is slot | group <<
+// 4 | (first slot of its group) << 28), and from int 16 on the shared groups
+// (output group | first entry << 8 | entry count << 16).
 __device__ __forceinline__ bool whole_group(int t, int kt, int u0, int u1) { return t * kt >= u0 && (t + 1) * kt <= u1; }
 
 __device__ __forceinline__ void build_plans(const int* tab_all, int* plan) {
@@ -470,51 +472,34 @@ __device__ __forceinline__ void build_plans(const int* tab_all, int* plan) {
     }
   }
   pl[0] = cnt;
+  // the shared groups: output group, first entry and entry count of each
+  int* gp = pl + 16;
+  int ng = 0;
+  for (int k = 0; k < cnt; ++k) {
+    const int en = pl[1 + k];
+    if ((en >> 28) & 1) gp[1 + ng++] = ((en >> 4) & 0xFF) | (k << 8) | (1 << 16);
+    else if (ng > 0) gp[ng] += 1 << 16;
+  }
+  gp[0] = ng;
 }
 
-// Wave 0, after the streamers have stored a phase's results: out[group] =
-// the sum of its shared slots, added in streamer order.  Lane k holds plan
-// entry k and readlane broadcasts it; every slot read is issued before the
-// first add (entries past the count read slot 0 and count as zero), so the
-// reads overlap, and the adds and stores follow under uniform conditions.
+// All eight waves, after the streamers have stored a batched phase's results
+// (S2): out[group] = the sum of its shared slots, added in streamer order
+// (the first slot's value, then each later one), one (group, element) per
+// thread.
 template <int MB>
-__device__ __forceinline__ void w0_combine(int ph, const int* plan, const float* slots, float* out) {
-  constexpr int SN = Lds<MB>::SlotN, NE = 2 * kStreamers, PER = SN / 64;
-  static_assert(SN % 64 == 0, "slot elements are spread over the wave's lanes");
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void combine_all(int ph, const int* plan, const float* slots, float* out) {
+  constexpr int SN = Lds<MB>::SlotN;
   const int* pl = plan + ph * kPlanInts;
-  const int cnt = rfl(pl[0]);
-  if (cnt == 0) return;
-  const int mine = pl[1 + (lane < NE ? lane : 0)];
-  int ent[NE];
-#pragma unroll
-  for (int k = 0; k < NE; ++k) ent[k] = k < cnt ? __builtin_amdgcn_readlane(mine, k) : 0;
-  float v[NE][PER];
-#pragma unroll
-  for (int k = 0; k < NE; ++k) {
-    const float* sl = slots + (ent[k] & 15) * SN + lane;
-#pragma unroll
-    for (int p = 0; p < PER; ++p) v[k][p] = sl[64 * p];
-  }
-  wait_lgkm0();
-  float acc[PER];
-#pragma unroll
-  for (int p = 0; p < PER; ++p) acc[p] = 0.f;
-#pragma unroll
-  for (int k = 0; k < NE; ++k) {
-    const bool live = k < cnt;
-    const bool first = live && ((ent[k] >> 28) & 1);
-    const bool last = live && (k == cnt - 1 || (k + 1 < NE && ((ent[k + 1] >> 28) & 1)));
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const float x = live ? v[k][p] : 0.f;
-      acc[p] = first ? x : acc[p] + x;
-    }
-    if (last) {
-      const int g = (ent[k] >> 4) & 0xFFFFFF;
-#pragma unroll
-      for (int p = 0; p < PER; ++p) out[g * SN + lane + 64 * p] = acc[p];
-    }
+  const int* gp = pl + 16;
+  const int n = gp[0] * SN;
+  for (int p = threadIdx.x; p < n; p += kThreads) {
+    const int gi = p / SN, e = p - gi * SN;
+    const int d = gp[1 + gi];
+    const int g = d & 0xFF, e0 = (d >> 8) & 0xFF, ne = d >> 16;
+    float acc = slots[(pl[1 + e0] & 15) * SN + e];
+    for (int k = 1; k < ne; ++k) acc += slots[(pl[1 + e0 + k] & 15) * SN + e];
+    out[g * SN + e] = acc;
   }
 }
 
@@ -1709,7 +1694,7 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
 template <int MB, int HD>
 __device__ __forceinline__ void streamer_tiles(const Params& P, const Launch& A, int g0, int g1, const int* tab,
                                                float* xs, float* out, float* slot, const float* gs, float* red,
-                                               const int* si, float* aux) {
+                                               const int* si, float* aux, const int* plan, const float* slots) {
   static_assert(MB == 8, "the MFMA B operand maps columns to sequences mod 8");
   const int lane = threadIdx.x & 63, B = P.B;
   const uint32_t lane16 = (uint32_t)lane * 16u;
@@ -1780,6 +1765,10 @@ __device__ __forceinline__ void streamer_tiles(const Params& P, const Launch& A,
       }
     }
     __syncthreads();   // S2
+    if (is_gemv(id.ph)) {
+      combine_all<MB>(id.ph, plan, slots, out);
+      __syncthreads();   // S2b
+    }
   }
   wait_vm0();   // the zero-filled loads past the stream's end
 }
@@ -1817,7 +1806,8 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   __syncthreads();   // every streamer's tables are in LDS
   if (wave > 0) {
     if constexpr (MB == 1) streamer_role<HD>(P, A, g0, g1, tab, xs, out, gs, red, si, aux, smem + M::Sink);
-    else streamer_tiles<MB, HD>(P, A, g0, g1, tab, xs, out, slots + (wave - 1) * 2 * M::SlotN, gs, red, si, aux);
+    else streamer_tiles<MB, HD>(P, A, g0, g1, tab, xs, out, slots + (wave - 1) * 2 * M::SlotN, gs, red, si, aux,
+                                plan, slots);
     return;
   }
   if constexpr (MB > 1) {
@@ -1860,7 +1850,10 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     // outputs of the previous phase; this phase's LDS results start at zero
     if (!first) {
       if constexpr (MB > 1)
-        if (is_gemv(prev_ph)) w0_combine<MB>(prev_ph, plan, slots, out);
+        if (is_gemv(prev_ph)) {
+          combine_all<MB>(prev_ph, plan, slots, out);
+          __syncthreads();   // S2b
+        }
       w0_store_outputs<MB>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
                            lg_mode(A, prev_i, cur_lg), scl, out, xown, aux, gs);
     }
@@ -2035,7 +2028,10 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   }
   if (!first) {
     if constexpr (MB > 1)
-      if (is_gemv(prev_ph)) w0_combine<MB>(prev_ph, plan, slots, out);
+      if (is_gemv(prev_ph)) {
+        combine_all<MB>(prev_ph, plan, slots, out);
+        __syncthreads();   // S2b
+      }
     w0_store_outputs<MB>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
                          lg_mode(A, prev_i, cur_lg), scl, out, xown, aux, gs);
   }
