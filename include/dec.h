@@ -73,7 +73,8 @@ typedef enum dec_status {
  *   d_ffn >= 8, a multiple of 8;
  *   1 <= lm_vocab <= vocab, lm_vocab even;
  *   1 <= max_ctx <= 65536; batch >= 1; rms_eps > 0; rope_base > 1;
- *   flags: 0 or DEC_FLAG_BATCHED_PREFILL (batch 1 only).
+ *   flags: 0, DEC_FLAG_BATCHED_PREFILL or DEC_FLAG_MATRIX_PREFILL (batch 1
+ *   only; not both).
  * Limits of this library (DEC_ERR_UNSUPPORTED): d_model, n_heads*head_dim and
  * d_ffn <= 8192; batch <= 8; with batch > 1, d_model <= 2560 and d_ffn,
  * n_heads*head_dim <= 7680 after rounding up to a multiple of 512 (every
@@ -98,6 +99,21 @@ typedef enum dec_status {
  * are unchanged.
  */
 #define DEC_FLAG_BATCHED_PREFILL 0x2u
+/*
+ * DEC_FLAG_MATRIX_PREFILL: dec_prefill runs all prompt positions through
+ * each weight matrix at once, as matrix products on the matrix cores (up to
+ * 2048 positions per pass over the weights), with a tiled causal attention
+ * over the cache; the time to first token is one of the speed figures of
+ * hakusoku.com/story/7519, section 単一リクエストLLMデコード速度の重要性.
+ * Needs head_dim >= 32 and d_model, n_heads*head_dim, d_ffn multiples of 32
+ * (DEC_ERR_UNSUPPORTED otherwise).  The handle's arena holds a workspace of
+ * about min(max_ctx, 2048) x (4 d_model + 2 max(d_model, H hd, d_ffn) +
+ * 2 H hd + 4 max(3 H hd, 2 d_ffn)) bytes plus up to 32 MB of partial sums
+ * (dec_arena_bytes includes it).  Numerics: the products' inputs are rounded
+ * to fp16 as with DEC_FLAG_BATCHED_PREFILL, and so are the rotated queries and
+ * the softmax weights of the attention products.  Decode steps are unchanged.
+ */
+#define DEC_FLAG_MATRIX_PREFILL 0x4u
 
 typedef struct dec_model_desc {
   int32_t n_layers;
@@ -112,7 +128,7 @@ typedef struct dec_model_desc {
   int32_t batch;      /* sequences decoded together                    */
   float rms_eps;
   float rope_base;
-  uint32_t flags;     /* 0 or DEC_FLAG_BATCHED_PREFILL */
+  uint32_t flags;     /* 0, DEC_FLAG_BATCHED_PREFILL or DEC_FLAG_MATRIX_PREFILL */
 } dec_model_desc;
 
 /*

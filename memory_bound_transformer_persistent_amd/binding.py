@@ -31,6 +31,7 @@ DEC_DEBUG_TRACE = 0x2
 DEC_DEBUG_FENCED = 0x4
 DEC_DEBUG_STRESS = 0x8
 DEC_FLAG_BATCHED_PREFILL = 0x2
+DEC_FLAG_MATRIX_PREFILL = 0x4
 
 ERR_NAMES = {v: k for k, v in globals().items() if k.startswith("DEC_ERR_")}
 

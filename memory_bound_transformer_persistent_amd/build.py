@@ -7,7 +7,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdecmono.so")
-SOURCES = ["dec_host.cpp", "dec_kernels.hip"]
+SOURCES = ["dec_host.cpp", "dec_kernels.hip", "dec_matrix.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

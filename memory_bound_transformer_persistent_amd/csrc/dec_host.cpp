@@ -55,12 +55,19 @@ int check_desc_impl(const dec_model_desc* d, std::string* err) {
   if (d->max_ctx < 1 || d->max_ctx > 65536) return fail(err, DEC_ERR_BAD_DESC, "max_ctx must be in [1, 65536] (got %d)", d->max_ctx);
   if (!(d->rms_eps > 0.f) || !std::isfinite(d->rms_eps)) return fail(err, DEC_ERR_BAD_DESC, "rms_eps must be > 0");
   if (!(d->rope_base > 1.f) || !std::isfinite(d->rope_base)) return fail(err, DEC_ERR_BAD_DESC, "rope_base must be > 1");
-  if (d->flags & ~DEC_FLAG_BATCHED_PREFILL) return fail(err, DEC_ERR_BAD_DESC, "unknown flags 0x%x", d->flags);
+  if (d->flags & ~(DEC_FLAG_BATCHED_PREFILL | DEC_FLAG_MATRIX_PREFILL))
+    return fail(err, DEC_ERR_BAD_DESC, "unknown flags 0x%x", d->flags);
   const bool bp = (d->flags & DEC_FLAG_BATCHED_PREFILL) != 0;
+  const bool mp = (d->flags & DEC_FLAG_MATRIX_PREFILL) != 0;
+  if (bp && mp) return fail(err, DEC_ERR_BAD_DESC, "DEC_FLAG_BATCHED_PREFILL and DEC_FLAG_MATRIX_PREFILL exclude each other");
   if (bp && d->batch != 1) return fail(err, DEC_ERR_BAD_DESC, "DEC_FLAG_BATCHED_PREFILL is for batch 1");
+  if (mp && d->batch != 1) return fail(err, DEC_ERR_BAD_DESC, "DEC_FLAG_MATRIX_PREFILL is for batch 1");
   if (d->batch < 1) return fail(err, DEC_ERR_BAD_DESC, "batch must be >= 1");
   const long long q = (long long)d->n_heads * hd;
   if (q % 8) return fail(err, DEC_ERR_BAD_DESC, "n_heads*head_dim must be a multiple of 8");
+  if (mp && (hd < 32 || d->d_model % 32 || q % 32 || d->d_ffn % 32))
+    return fail(err, DEC_ERR_UNSUPPORTED, "DEC_FLAG_MATRIX_PREFILL needs head_dim >= 32 and d_model, "
+                "n_heads*head_dim, d_ffn multiples of 32");
   if (d->batch > kMaxBatch) return fail(err, DEC_ERR_UNSUPPORTED, "batch must be <= %d", kMaxBatch);
   if (d->batch > 1 || bp) {
     auto span = [](long long k) { return (k + 511) / 512 * 512; };
@@ -281,11 +288,21 @@ bool same_shape(const dec_model_desc& a, const dec_model_desc& b) {
 // device arena layout (bytes)
 // ---------------------------------------------------------------------------
 struct Arena {
-  size_t w, w2, gains, rope, kv, x, xg16, ssp, qkv, att_o, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out,
+  size_t w, w2, gains, rope, kv, mp_x, mp_h, mp_q16, mp_c, mp_s, mp_part, x, xg16, ssp, qkv, att_o, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out,
       prompt, ctl, srv_slot, params, params2, trace, total;
 };
 
 bool batched_prefill(const dec_model_desc& d) { return (d.flags & DEC_FLAG_BATCHED_PREFILL) != 0; }
+bool matrix_prefill(const dec_model_desc& d) { return (d.flags & DEC_FLAG_MATRIX_PREFILL) != 0; }
+
+// The matrix prefill's workspace: prompt positions per pass over the
+// weights, and the floats of its split-K partial sums.
+int mp_chunk(const dec_model_desc& d) { return std::min(d.max_ctx, kMpChunk); }
+size_t mp_part_floats(const dec_model_desc& d) {
+  const size_t q = (size_t)d.n_heads * d.head_dim;
+  const size_t widest = std::max({3 * q, 2 * (size_t)d.d_ffn, (size_t)d.d_model});
+  return std::min(kMpPartFloats, 8 * std::max((size_t)mp_chunk(d) * widest, (size_t)d.lm_vocab));
+}
 
 // The description the batched prefill kernel runs with: kMaxBatch columns
 // (consecutive positions of the one sequence) and the tiled weight image.
@@ -314,6 +331,19 @@ Arena arena_layout(const dec_model_desc& d, int G) {
   a.gains = take(((size_t)d.n_layers * 2 + 1) * D * 4);
   a.rope = take((size_t)d.max_ctx * (d.head_dim / 2) * 2 * 4);
   a.kv = take((size_t)d.n_layers * 2 * hkv * d.max_ctx * d.head_dim * 2);
+  // matrix prefill workspace (outside the scratch part: it lives in the
+  // caller's arena for a no-allocation handle)
+  if (matrix_prefill(d)) {
+    const size_t mc = mp_chunk(d), F = d.d_ffn;
+    a.mp_x = take(mc * D * 4);
+    a.mp_h = take(mc * std::max({D, q, F}) * 2);
+    a.mp_q16 = take(mc * q * 2);
+    a.mp_c = take(mc * std::max(3 * q, 2 * F) * 4);
+    a.mp_s = take(mc * 4);
+    a.mp_part = take(mp_part_floats(d) * 4);
+  } else {
+    a.mp_x = a.mp_h = a.mp_q16 = a.mp_c = a.mp_s = a.mp_part = 0;
+  }
   a.x = take(B * D * 4);
   a.xg16 = take(B * D * 2);
   a.ssp = take((size_t)G * kMaxBatch * 4);
@@ -458,6 +488,61 @@ int launch_prefill(dec_handle* h, int n, int write_logits) {
   A.bar_base = h->bar_done;
   HIPCHK(h, &h->err, (hipError_t)kernel_launch_resident(h->dP2, A, h->grid, kMaxBatch, h->desc.head_dim, h->stream));
   h->bar_done += launch_barriers(h->desc.n_layers, n_tok, lm_last_only);
+  return DEC_OK;
+}
+
+// The matrix prefill of n prompt positions (already in P.prompt): chunks of
+// up to kMpChunk positions, each through every layer as matrix products
+// (dec_matrix.hip), then the LM-head row and greedy token of position n-1.
+int launch_matrix_prefill(dec_handle* h, int n) {
+  const dec_model_desc& d = h->desc;
+  const Params& P = h->P;
+  const int D = d.d_model, H = d.n_heads, hd = d.head_dim, q = H * hd, F = d.d_ffn, V = d.lm_vocab;
+  const size_t head_elems = (size_t)d.max_ctx * hd;
+  char* b = static_cast<char*>(h->base);
+  float* x = reinterpret_cast<float*>(b + h->ar.mp_x);
+  uint16_t* hb = reinterpret_cast<uint16_t*>(b + h->ar.mp_h);
+  uint16_t* q16 = reinterpret_cast<uint16_t*>(b + h->ar.mp_q16);
+  float* cb = reinterpret_cast<float*>(b + h->ar.mp_c);
+  float* sb = reinterpret_cast<float*>(b + h->ar.mp_s);
+  float* part = reinterpret_cast<float*>(b + h->ar.mp_part);
+  const size_t part_floats = mp_part_floats(d);
+  void* st = h->stream;
+  auto gemm = [&](const uint16_t* A, int lda, const uint16_t* W, float* C, int ldc, const float* s, int M, int N, int K,
+                  int mode) {
+    MpGemm g;
+    g.A = A; g.lda = lda; g.B = W; g.ldb = K; g.C = C; g.ldc = ldc; g.s = s;
+    g.M = M; g.N = N; g.K = K; g.mode = mode; g.part = part;
+    mp_plan(M, N, K, part_floats, &g.shape, &g.S, &g.kc);
+    return (hipError_t)mp_launch_gemm(g, st);
+  };
+  const int mc = mp_chunk(d);
+  int m = 0;
+  for (int c0 = 0; c0 < n; c0 += mc) {
+    m = std::min(mc, n - c0);
+    HIPCHK(h, &h->err, (hipError_t)mp_launch_embed(P.w + P.off_E, P.prompt + c0, m, D, x, st));
+    for (int l = 0; l < d.n_layers; ++l) {
+      const uint16_t* W = P.w + (size_t)l * P.layer_stride;
+      const float* g_attn = P.gains + (size_t)l * 2 * D;
+      const float* g_ffn = g_attn + D;
+      uint16_t* kc = P.kv + (size_t)l * 2 * H * head_elems;
+      uint16_t* vc = kc + (size_t)H * head_elems;
+      HIPCHK(h, &h->err, (hipError_t)mp_launch_norm(x, g_attn, m, D, d.rms_eps, hb, sb, st));
+      HIPCHK(h, &h->err, gemm(hb, D, W + P.off_qkv, cb, 3 * q, sb, m, 3 * q, D, MP_EP_SCALE));
+      HIPCHK(h, &h->err, (hipError_t)mp_launch_rope_kv(cb, m, q, hd, c0, P.rope, kc, vc, head_elems, q16, st));
+      HIPCHK(h, &h->err, (hipError_t)mp_launch_attention(q16, q, m, c0, H, hd, kc, vc, head_elems, hb, st));
+      HIPCHK(h, &h->err, gemm(hb, q, W + P.off_o, x, D, nullptr, m, D, q, MP_EP_ACCUM));
+      HIPCHK(h, &h->err, (hipError_t)mp_launch_norm(x, g_ffn, m, D, d.rms_eps, hb, sb, st));
+      HIPCHK(h, &h->err, gemm(hb, D, W + P.off_gu, cb, 2 * F, sb, m, 2 * F, D, MP_EP_SCALE));
+      HIPCHK(h, &h->err, (hipError_t)mp_launch_swiglu(cb, m, F, hb, st));
+      HIPCHK(h, &h->err, gemm(hb, F, W + P.off_d, x, D, nullptr, m, D, F, MP_EP_ACCUM));
+    }
+  }
+  // the last position's final norm, LM-head row and greedy token
+  const float* g_final = P.gains + (size_t)d.n_layers * 2 * D;
+  HIPCHK(h, &h->err, (hipError_t)mp_launch_norm(x + (size_t)(m - 1) * D, g_final, 1, D, d.rms_eps, hb, sb, st));
+  HIPCHK(h, &h->err, gemm(hb, D, P.w + P.off_lm, P.logits, V, sb, 1, V, D, MP_EP_SCALE));
+  HIPCHK(h, &h->err, (hipError_t)mp_launch_argmax(P.logits, V, P.tok_out + (n - 1), P.tok_cur, st));
   return DEC_OK;
 }
 
@@ -1068,6 +1153,18 @@ int dec_prefill(dec_handle* h, const int32_t* tokens, int32_t n, int32_t* out_to
       return fail(&h->err, DEC_ERR_TOKEN_RANGE, "prompt token %lld = %d outside [0, %d)", i, tokens[i], h->desc.vocab);
   HIPCHK(h, &h->err, hipMemcpyAsync(const_cast<int*>(h->P.prompt), tokens, (size_t)n * B * 4, hipMemcpyHostToDevice,
                                     h->stream));
+  if (matrix_prefill(h->desc)) {
+    int rc = launch_matrix_prefill(h, n);
+    if (rc) return rc;
+    h->pos = n;
+    h->has_prev_tok = true;
+    rc = check_device_error(h);
+    if (rc) return rc;
+    HIPCHK(h, &h->err, hipMemcpy(out_tok, h->P.tok_out + (n - 1), 4, hipMemcpyDeviceToHost));
+    if (out_logits)
+      HIPCHK(h, &h->err, hipMemcpy(out_logits, h->P.logits, (size_t)h->desc.lm_vocab * 4, hipMemcpyDeviceToHost));
+    return DEC_OK;
+  }
   if (h->dP2) {
     // kMaxBatch positions per step; the last step's last live column is position n-1
     int rc = launch_prefill(h, n, out_logits != nullptr);

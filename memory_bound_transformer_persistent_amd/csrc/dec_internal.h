@@ -1,5 +1,5 @@
 // Internal definitions shared by the host runtime (dec_host.cpp) and the
-// device code (dec_kernels.hip).  Not part of the public ABI.
+// device code (dec_kernels.hip, dec_matrix.hip).  Not part of the public ABI.
 #pragma once
 
 #include <stddef.h>
@@ -216,6 +216,38 @@ inline uint32_t launch_barriers(int L, int n_tok, int lm_last_only) {
   }
   return phases - 1 - skipped;
 }
+
+// Matrix-form prefill (dec_matrix.hip): the prompt's positions as the rows
+// of matrix products on the matrix cores.  A product C = A B^T takes A
+// [M x K] and B [N x K] fp16 with K contiguous and K a multiple of 32.
+enum MpEpilogue : int {
+  MP_EP_SCALE = 0,   // C = s[m] * (A B^T)  (s may be null: no scale)
+  MP_EP_ACCUM = 1,   // C += A B^T
+  MP_EP_PART = 2,    // internal: one K split's partial sums
+};
+constexpr int kMpShapes = 6;           // tile shapes: 128x128, 128x64, 64x64, 64x32, 32x32, 16x64
+constexpr int kMpChunk = 2048;         // prompt positions per pass over the weights
+constexpr size_t kMpPartFloats = size_t(8) << 20;   // split-K partial sums buffer (floats)
+struct MpGemm {
+  const uint16_t* A; int lda;
+  const uint16_t* B; int ldb;
+  float* C; int ldc;
+  const float* s;
+  int M, N, K;
+  int mode;                  // MP_EP_SCALE or MP_EP_ACCUM
+  int shape, S, kc;          // from mp_plan: tile shape, K splits, K elements per split
+  float* part;               // [S][M][N] partial sums when S > 1
+};
+void mp_plan(int M, int N, int K, size_t part_floats, int* shape, int* S, int* kc);
+int mp_launch_embed(const uint16_t* E, const int* tok, int n, int d, float* x, void* stream);
+int mp_launch_norm(const float* x, const float* g, int n, int d, float eps, uint16_t* h, float* s, void* stream);
+int mp_launch_gemm(const MpGemm& g, void* stream);
+int mp_launch_rope_kv(const float* qkv, int n, int q, int hd, int pos0, const float* rope, uint16_t* kc, uint16_t* vc,
+                      size_t head_elems, uint16_t* q16, void* stream);
+int mp_launch_attention(const uint16_t* q16, int q, int n, int pos0, int H, int hd, const uint16_t* kc,
+                        const uint16_t* vc, size_t head_elems, uint16_t* o16, void* stream);
+int mp_launch_swiglu(const float* gu, int n, int F, uint16_t* a, void* stream);
+int mp_launch_argmax(const float* logits, int V, int* tok_out, int* tok_cur, void* stream);
 
 // Launch helpers defined next to the kernel (dec_kernels.hip).  P points to a
 // device copy of the parameters; stream is a hipStream_t; batch selects the

@@ -1,0 +1,474 @@
+// Matrix-form prefill for gfx950: every prompt position goes through each
+// weight matrix in one pass, as matrix products on the matrix cores, instead
+// of one position (or eight) per step of the decode kernel.
+//
+// The prompt phase sets the time to first token, one of the three speed
+// figures the pages list for inference benchmarks beside throughput and
+// per-request decode speed (hakusoku.com/story/7519, section
+// 単一リクエストLLMデコード速度の重要性).  Over a whole prompt the products
+// are dense: n positions times every weight, above the matrix cores' ridge
+// (about 310 flop per HBM byte) once n passes a few hundred, so for long
+// prompts the matrix cores and not HBM bound this path.
+//
+// Per layer, for the prompt positions pos0 .. pos0+n-1 with x their fp32
+// residual rows:
+//   h = fp16(x * g_attn), s = 1/rms(x)                        mp_norm
+//   qkv = s * (h Wqkv^T)                                       mp_gemm
+//   rotary on q and k; k, v (fp16) to the KV cache; q fp16      mp_rope_kv
+//   o = causal softmax(q k^T) v over cache positions, fp16      mp_attention
+//   x += o Wo^T                                                 mp_gemm (accumulate)
+//   h = fp16(x * g_ffn), s = 1/rms(x);  gu = s * (h Wgu^T)      mp_norm, mp_gemm
+//   a = fp16(silu(gate) * up)                                   mp_swiglu
+//   x += a Wd^T                                                 mp_gemm (accumulate)
+// then the final norm of the prompt's last position, its LM-head row and
+// the argmax.  Matrix-product inputs are rounded to fp16 as in the batched
+// decode kernel; q and the softmax weights are also rounded to fp16 for the
+// attention products.  Every sum has a fixed order (split-K partials too), so
+// results do not depend on timing.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "dec_internal.h"
+
+namespace decmono {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4m __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc;
+
+constexpr uint32_t kOutOfRange = 0x80000000u;   // a buffer offset past every record: reads 0
+
+__device__ __forceinline__ rsrc make_res(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes >= 0x7fffffffull ? 0x7fffffffu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ f16x8 ld8(rsrc r, uint32_t off) {
+  return __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float wave_sum64(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// x[m][:] = E[tok[m]] in fp32 (tokens were range-checked by the host).  One
+// workgroup per position.
+__global__ __launch_bounds__(256) void mp_embed(const uint16_t* __restrict__ E, const int* __restrict__ tok, int d,
+                                                float* __restrict__ x) {
+  const int m = blockIdx.x;
+  const _Float16* e = reinterpret_cast<const _Float16*>(E) + (size_t)tok[m] * d;
+  for (int i = threadIdx.x; i < d; i += 256) x[(size_t)m * d + i] = (float)e[i];
+}
+
+// h[m] = fp16(x[m] * g) and s[m] = 1 / sqrt(mean(x[m]^2) + eps).  One
+// workgroup per row; the sum of squares is added per thread in index order,
+// then over the wave, then over the four waves in order.
+__global__ __launch_bounds__(256) void mp_norm(const float* __restrict__ x, const float* __restrict__ g, int d,
+                                               float eps, uint16_t* __restrict__ h, float* __restrict__ s) {
+  __shared__ float part[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const float* xr = x + (size_t)m * d;
+  _Float16* hr = reinterpret_cast<_Float16*>(h) + (size_t)m * d;
+  float ss = 0.f;
+  for (int i = tid; i < d; i += 256) {
+    const float v = xr[i];
+    ss += v * v;
+    hr[i] = (_Float16)(v * g[i]);
+  }
+  ss = wave_sum64(ss);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  if (tid == 0) s[m] = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d + eps);
+}
+
+// C[M x N] from A [M x K] and B [N x K], both fp16 with K contiguous (row
+// strides lda, ldb; K a multiple of 32): C = A B^T through the epilogue
+// (MpEpilogue).  Four waves per workgroup in a WR x (4/WR) arrangement, each
+// computing a (16 WM) x (16 WN) block as WM x WN products of
+// v_mfma_f32_16x16x32_f16.  Operand layout of that instruction: lane l holds
+// row l % 16 and the 8 K-elements 8 (l / 16) .. +7 of a 32-wide K step (a
+// row of A for the A operand, a row of B -- a column of C -- for the B
+// operand); the result is lane l's rows 4 (l / 16) .. +3 at column l % 16.
+// Each lane loads its operands straight from the K-contiguous rows, 16 bytes
+// per load, one K step ahead of the products; rows past M or N read as zero.
+// Split z (blockIdx.z) covers K elements [z kc, min(K, (z+1) kc)).
+template <int WM, int WN, int WR>
+__global__ __launch_bounds__(256) void mp_gemm(const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ B,
+                                               int ldb, float* __restrict__ C, int ldc, const float* __restrict__ s,
+                                               int M, int N, int K, int kc, int mode) {
+  constexpr int WC = 4 / WR;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave / WC, wc = wave % WC;
+  const int m0 = blockIdx.y * (16 * WM * WR) + wr * 16 * WM, n0 = blockIdx.x * (16 * WN * WC) + wc * 16 * WN;
+  const int kb = blockIdx.z * kc, ke = min(K, kb + kc);
+  const rsrc ra = make_res(A, (uint64_t)M * lda * 2), rb = make_res(B, (uint64_t)N * ldb * 2);
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  uint32_t offa[WM], offb[WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+    const int m = m0 + 16 * i + r16;
+    offa[i] = m < M ? (uint32_t)((size_t)m * lda + kb + kq) * 2u : kOutOfRange;
+  }
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    const int n = n0 + 16 * j + r16;
+    offb[j] = n < N ? (uint32_t)((size_t)n * ldb + kb + kq) * 2u : kOutOfRange;
+  }
+  f32x4m acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = f32x4m{0.f, 0.f, 0.f, 0.f};
+  f16x8 a[WM], b[WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i) a[i] = ld8(ra, offa[i]);
+#pragma unroll
+  for (int j = 0; j < WN; ++j) b[j] = ld8(rb, offb[j]);
+  for (int k = kb; k < ke; k += 32) {
+    f16x8 an[WM], bn[WN];
+    const bool more = k + 32 < ke;
+    const uint32_t step = (uint32_t)(k + 32 - kb) * 2u;
+#pragma unroll
+    for (int i = 0; i < WM; ++i) an[i] = ld8(ra, more && offa[i] != kOutOfRange ? offa[i] + step : kOutOfRange);
+#pragma unroll
+    for (int j = 0; j < WN; ++j) bn[j] = ld8(rb, more && offb[j] != kOutOfRange ? offb[j] + step : kOutOfRange);
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < WM; ++i) a[i] = an[i];
+#pragma unroll
+    for (int j = 0; j < WN; ++j) b[j] = bn[j];
+  }
+  float* Cz = mode == MP_EP_PART ? C + (size_t)blockIdx.z * M * ldc : C;
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + 16 * i + (lane >> 4) * 4 + r;
+      if (m >= M) continue;
+      const float sc = (mode == MP_EP_SCALE && s) ? s[m] : 1.0f;
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const int n = n0 + 16 * j + r16;
+        if (n >= N) continue;
+        float* c = Cz + (size_t)m * ldc + n;
+        const float v = acc[i][j][r];
+        if (mode == MP_EP_ACCUM) *c = *c + v;
+        else *c = v * sc;
+      }
+    }
+  }
+}
+
+// The epilogue of a split-K product: the S partial slices [S][M][N] added in
+// slice order, then scaled by s[m] (MP_EP_SCALE) or added to C (MP_EP_ACCUM).
+__global__ __launch_bounds__(256) void mp_splitk_sum(const float* __restrict__ part, int S, int M, int N,
+                                                     float* __restrict__ C, int ldc, const float* __restrict__ s,
+                                                     int mode) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)M * N) return;
+  const int m = (int)(i / N), n = (int)(i - (size_t)m * N);
+  float v = part[i];
+  for (int z = 1; z < S; ++z) v += part[(size_t)z * M * N + i];
+  float* c = C + (size_t)m * ldc + n;
+  if (mode == MP_EP_ACCUM) *c = *c + v;
+  else *c = v * (s ? s[m] : 1.0f);
+}
+
+// Rotary embedding and cache append for positions pos0 .. pos0+n-1 of one
+// layer: qkv [n x 3q] (fp32); q rotated and scaled by 1/sqrt(hd) to q16
+// [n x q] (fp16); k rotated, and v as it is, to the fp16 KV cache
+// ([H][max_ctx][hd], head_elems = max_ctx hd apart).  Pairs (2i, 2i+1) of a
+// head turn by the angle in the cos/sin table row of the position.
+__global__ __launch_bounds__(256) void mp_rope_kv(const float* __restrict__ qkv, int q, int hd, int pos0,
+                                                  const float* __restrict__ rope, uint16_t* __restrict__ kc,
+                                                  uint16_t* __restrict__ vc, size_t head_elems,
+                                                  uint16_t* __restrict__ q16) {
+  const int m = blockIdx.x, pos = pos0 + m;
+  const float* row = qkv + (size_t)m * 3 * q;
+  const float qscale = 1.0f / sqrtf((float)hd);
+  const float* rt = rope + (size_t)pos * hd;
+  for (int p = threadIdx.x; p < 3 * q / 2; p += 256) {
+    const int r = 2 * p, part = r / q, rr = r - part * q, h = rr / hd, i = (rr - h * hd) >> 1;
+    const float y0 = row[r], y1 = row[r + 1];
+    if (part == 2) {
+      _Float16* v = reinterpret_cast<_Float16*>(vc) + (size_t)h * head_elems + (size_t)pos * hd + 2 * i;
+      v[0] = (_Float16)y0;
+      v[1] = (_Float16)y1;
+      continue;
+    }
+    const float cs = rt[2 * i], sn = rt[2 * i + 1];
+    const float z0 = __builtin_fmaf(y0, cs, -(y1 * sn)), z1 = __builtin_fmaf(y0, sn, y1 * cs);
+    if (part == 0) {
+      _Float16* o = reinterpret_cast<_Float16*>(q16) + (size_t)m * q + rr;
+      o[0] = (_Float16)(z0 * qscale);
+      o[1] = (_Float16)(z1 * qscale);
+    } else {
+      _Float16* k = reinterpret_cast<_Float16*>(kc) + (size_t)h * head_elems + (size_t)pos * hd + 2 * i;
+      k[0] = (_Float16)z0;
+      k[1] = (_Float16)z1;
+    }
+  }
+}
+
+// Causal attention of queries pos0 .. pos0+n-1 of one head (blockIdx.y)
+// over cache positions 0 .. pos0+n-1, 16 queries per wave.  For each block of
+// 32 keys at or below the wave's last query: scores S = q k^T on the matrix
+// cores (two 16 x 16 tiles, hd/32 products each), a running max and sum per
+// query row (online softmax), P = exp(S - max) rounded to fp16 and o += P v
+// on the matrix cores.  P moves through LDS from the result layout (query
+// 4 (l/16) + r, key l % 16) to the A-operand layout (query l % 16, keys
+// 8 (l/16) .. +7); the value block is staged transposed (dimension-major,
+// rows padded) so each lane's B operand is 16 contiguous bytes.  Finally
+// o = o / sum, fp16, to o16 [n x q].
+template <int HD>
+__global__ __launch_bounds__(64) void mp_attention(const uint16_t* __restrict__ q16, int q, int n, int pos0,
+                                                   const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+                                                   size_t head_elems, uint16_t* __restrict__ o16) {
+  constexpr int VT = 32 + 8;   // padded key stride of the transposed value block (fp16)
+  __shared__ _Float16 vt[HD * VT];
+  __shared__ float pbuf[16 * 33];
+  const int lane = threadIdx.x, h = blockIdx.y, m0 = blockIdx.x * 16;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8, rq = (lane >> 4) * 4;
+  const int n_keys = pos0 + n;
+  const _Float16* kh = reinterpret_cast<const _Float16*>(kc) + (size_t)h * head_elems;
+  const _Float16* vh = reinterpret_cast<const _Float16*>(vc) + (size_t)h * head_elems;
+  const rsrc rk = make_res(kh, (uint64_t)n_keys * HD * 2), rqr = make_res(q16, (uint64_t)n * q * 2);
+  // this lane's query-row operands for the hd/32 K steps of the score products
+  f16x8 qa[HD / 32];
+#pragma unroll
+  for (int c = 0; c < HD / 32; ++c) {
+    const int m = m0 + r16;
+    qa[c] = ld8(rqr, m < n ? (uint32_t)((size_t)m * q + (size_t)h * HD + 32 * c + kq) * 2u : kOutOfRange);
+  }
+  f32x4m acc[HD / 16];
+#pragma unroll
+  for (int t = 0; t < HD / 16; ++t) acc[t] = f32x4m{0.f, 0.f, 0.f, 0.f};
+  float mrow[4], lrow[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    mrow[r] = -INFINITY;
+    lrow[r] = 0.f;
+  }
+  const int last = pos0 + min(m0 + 15, n - 1);   // position of the wave's last query
+  for (int j0 = 0; j0 <= last; j0 += 32) {
+    // scores of keys j0 + l%16 and j0 + 16 + l%16 against this lane's 4 query rows
+    f32x4m s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < HD / 32; ++c) {
+      const int ja = j0 + r16, jb = j0 + 16 + r16;
+      const f16x8 ka = ld8(rk, ja < n_keys ? (uint32_t)(ja * HD + 32 * c + kq) * 2u : kOutOfRange);
+      const f16x8 kb = ld8(rk, jb < n_keys ? (uint32_t)(jb * HD + 32 * c + kq) * 2u : kOutOfRange);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[c], ka, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[c], kb, s1, 0, 0, 0);
+    }
+    // stage this block's values transposed: vt[dim][key] (keys past the cache read 0)
+    __syncthreads();
+    for (int e = lane; e < 32 * (HD / 8); e += 64) {
+      const int key = e / (HD / 8), d8 = (e - key * (HD / 8)) * 8;
+      const int j = j0 + key;
+      f16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (j < n_keys) v = *reinterpret_cast<const f16x8*>(vh + (size_t)j * HD + d8);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) vt[(d8 + t) * VT + key] = v[t];
+    }
+    // online softmax over the 32 keys of each query row
+    float p0[4], p1[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qi = pos0 + m0 + rq + r;
+      const float a = (j0 + r16 <= qi) ? s0[r] : -INFINITY;
+      const float b = (j0 + 16 + r16 <= qi) ? s1[r] : -INFINITY;
+      float mx = fmaxf(a, b);
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+      // key 0 is at or below every query, so the max is finite from the first block on
+      const float mn = fmaxf(mrow[r], mx);
+      const float alpha = expf(mrow[r] - mn);
+      const float e0 = expf(a - mn), e1 = expf(b - mn);
+      float rs = e0 + e1;
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) rs += __shfl_xor(rs, off, 64);
+      lrow[r] = lrow[r] * alpha + rs;
+      mrow[r] = mn;
+      p0[r] = e0;
+      p1[r] = e1;
+#pragma unroll
+      for (int t = 0; t < HD / 16; ++t) acc[t][r] *= alpha;
+    }
+    // P to the A-operand layout through LDS (rounded to fp16 there)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pbuf[(rq + r) * 33 + r16] = p0[r];
+      pbuf[(rq + r) * 33 + 16 + r16] = p1[r];
+    }
+    __syncthreads();
+    f16x8 pa;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) pa[t] = (_Float16)pbuf[r16 * 33 + kq + t];
+#pragma unroll
+    for (int t = 0; t < HD / 16; ++t) {
+      const f16x8 vb = *reinterpret_cast<const f16x8*>(&vt[(16 * t + r16) * VT + kq]);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, acc[t], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = m0 + rq + r;
+    if (m >= n) continue;
+    const float inv = 1.0f / lrow[r];
+    _Float16* orow = reinterpret_cast<_Float16*>(o16) + (size_t)m * q + (size_t)h * HD;
+#pragma unroll
+    for (int t = 0; t < HD / 16; ++t) orow[16 * t + r16] = (_Float16)(acc[t][r] * inv);
+  }
+}
+
+// a[m][i] = fp16(silu(gu[m][2i]) * gu[m][2i+1]): gate and up rows are
+// interleaved in the packed weights, so they are adjacent columns here.
+__global__ __launch_bounds__(256) void mp_swiglu(const float* __restrict__ gu, int F, uint16_t* __restrict__ a) {
+  const int m = blockIdx.x;
+  const float* r = gu + (size_t)m * 2 * F;
+  _Float16* o = reinterpret_cast<_Float16*>(a) + (size_t)m * F;
+  for (int i = threadIdx.x; i < F; i += 256) {
+    const float g = r[2 * i], u = r[2 * i + 1];
+    o[i] = (_Float16)(g / (1.0f + expf(-g)) * u);
+  }
+}
+
+// The greedy token of one logits row (lowest index on ties): one workgroup,
+// each thread over a strided share in index order, then a fixed-order tree.
+__global__ __launch_bounds__(1024) void mp_argmax(const float* __restrict__ logits, int V, int* __restrict__ tok_out,
+                                                  int* __restrict__ tok_cur) {
+  __shared__ float bv[1024];
+  __shared__ int bi[1024];
+  const int tid = threadIdx.x;
+  float best = -INFINITY;
+  int idx = 0x7fffffff;
+  for (int i = tid; i < V; i += 1024) {
+    const float v = logits[i];
+    if (v > best) {
+      best = v;
+      idx = i;
+    }
+  }
+  bv[tid] = best;
+  bi[tid] = idx;
+  __syncthreads();
+  for (int w = 512; w >= 1; w >>= 1) {
+    if (tid < w) {
+      const float ov = bv[tid + w];
+      const int oi = bi[tid + w];
+      if (ov > bv[tid] || (ov == bv[tid] && oi < bi[tid])) {
+        bv[tid] = ov;
+        bi[tid] = oi;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const int t = bi[0] == 0x7fffffff ? 0 : bi[0];
+    *tok_out = t;
+    *tok_cur = t;
+  }
+}
+
+constexpr int kShapeBM[kMpShapes] = {128, 128, 64, 64, 32, 16};
+constexpr int kShapeBN[kMpShapes] = {128, 64, 64, 32, 32, 64};
+
+template <int WM, int WN, int WR>
+void gemm_as(const MpGemm& g, dim3 grid, hipStream_t st) {
+  const bool split = g.S > 1;
+  hipLaunchKernelGGL((mp_gemm<WM, WN, WR>), grid, dim3(256), 0, st, g.A, g.lda, g.B, g.ldb, split ? g.part : g.C,
+                     split ? g.N : g.ldc, g.s, g.M, g.N, g.K, g.kc, split ? (int)MP_EP_PART : g.mode);
+}
+
+}  // namespace
+
+// Tile shape and K split of a product: the largest tile that still gives
+// every compute unit two workgroups; failing that the smallest tile, with
+// the K range split (up to 8 ways, each split 4 K steps or more, partials
+// within part_floats) until it does.
+void mp_plan(int M, int N, int K, size_t part_floats, int* shape, int* S, int* kc) {
+  const long long want = 512;
+  auto count = [&](int t) {
+    return (long long)((M + kShapeBM[t] - 1) / kShapeBM[t]) * ((N + kShapeBN[t] - 1) / kShapeBN[t]);
+  };
+  int pick = -1;
+  if (M <= 16) {
+    pick = kMpShapes - 1;
+  } else {
+    for (int t = 0; t < kMpShapes - 1 && pick < 0; ++t)
+      if (count(t) >= want) pick = t;
+    if (pick < 0) pick = kMpShapes - 2;
+  }
+  int s = 1;
+  const long long c = count(pick);
+  while (s < 8 && c * s < want && K / (32 * 2 * s) >= 4 && (size_t)(2 * s) * M * N <= part_floats) s *= 2;
+  const int steps = (K / 32 + s - 1) / s;   // K steps per split
+  *shape = pick;
+  *S = (K / 32 + steps - 1) / steps;
+  *kc = steps * 32;
+}
+
+// Host-side launches of the matrix prefill (each returns a hipError_t value).
+int mp_launch_embed(const uint16_t* E, const int* tok, int n, int d, float* x, void* stream) {
+  hipLaunchKernelGGL(mp_embed, dim3(n), dim3(256), 0, (hipStream_t)stream, E, tok, d, x);
+  return (int)hipGetLastError();
+}
+int mp_launch_norm(const float* x, const float* g, int n, int d, float eps, uint16_t* h, float* s, void* stream) {
+  hipLaunchKernelGGL(mp_norm, dim3(n), dim3(256), 0, (hipStream_t)stream, x, g, d, eps, h, s);
+  return (int)hipGetLastError();
+}
+int mp_launch_gemm(const MpGemm& g, void* stream) {
+  if (g.K < 32 || g.K % 32 || g.M < 1 || g.N < 1 || g.shape < 0 || g.shape >= kMpShapes || g.S < 1 || g.kc < 32 ||
+      g.kc % 32 || (long long)g.S * g.kc < g.K || (long long)(g.S - 1) * g.kc >= g.K || (g.S > 1 && !g.part))
+    return (int)hipErrorInvalidValue;
+  const dim3 grid((g.N + kShapeBN[g.shape] - 1) / kShapeBN[g.shape], (g.M + kShapeBM[g.shape] - 1) / kShapeBM[g.shape],
+                  g.S);
+  const hipStream_t st = (hipStream_t)stream;
+  switch (g.shape) {
+    case 0: gemm_as<4, 4, 2>(g, grid, st); break;
+    case 1: gemm_as<4, 2, 2>(g, grid, st); break;
+    case 2: gemm_as<2, 2, 2>(g, grid, st); break;
+    case 3: gemm_as<2, 1, 2>(g, grid, st); break;
+    case 4: gemm_as<1, 1, 2>(g, grid, st); break;
+    default: gemm_as<1, 1, 1>(g, grid, st); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g.S == 1) return (int)e;
+  const size_t total = (size_t)g.M * g.N;
+  hipLaunchKernelGGL(mp_splitk_sum, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, g.part, g.S, g.M, g.N,
+                     g.C, g.ldc, g.s, g.mode);
+  return (int)hipGetLastError();
+}
+int mp_launch_rope_kv(const float* qkv, int n, int q, int hd, int pos0, const float* rope, uint16_t* kc, uint16_t* vc,
+                      size_t head_elems, uint16_t* q16, void* stream) {
+  hipLaunchKernelGGL(mp_rope_kv, dim3(n), dim3(256), 0, (hipStream_t)stream, qkv, q, hd, pos0, rope, kc, vc,
+                     head_elems, q16);
+  return (int)hipGetLastError();
+}
+int mp_launch_attention(const uint16_t* q16, int q, int n, int pos0, int H, int hd, const uint16_t* kc,
+                        const uint16_t* vc, size_t head_elems, uint16_t* o16, void* stream) {
+  const dim3 grid((n + 15) / 16, H);
+  const hipStream_t st = (hipStream_t)stream;
+  switch (hd) {
+    case 32: hipLaunchKernelGGL(mp_attention<32>, grid, dim3(64), 0, st, q16, q, n, pos0, kc, vc, head_elems, o16); break;
+    case 64: hipLaunchKernelGGL(mp_attention<64>, grid, dim3(64), 0, st, q16, q, n, pos0, kc, vc, head_elems, o16); break;
+    case 128: hipLaunchKernelGGL(mp_attention<128>, grid, dim3(64), 0, st, q16, q, n, pos0, kc, vc, head_elems, o16); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+int mp_launch_swiglu(const float* gu, int n, int F, uint16_t* a, void* stream) {
+  hipLaunchKernelGGL(mp_swiglu, dim3(n), dim3(256), 0, (hipStream_t)stream, gu, F, a);
+  return (int)hipGetLastError();
+}
+int mp_launch_argmax(const float* logits, int V, int* tok_out, int* tok_cur, void* stream) {
+  hipLaunchKernelGGL(mp_argmax, dim3(1), dim3(1024), 0, (hipStream_t)stream, logits, V, tok_out, tok_cur);
+  return (int)hipGetLastError();
+}
+
+}  // namespace decmono

@@ -484,6 +484,92 @@ def test_batched_prefill_then_generate_matches_steps(stream):
 
 
 # ----------------------------------------------------------------------------
+# matrix prefill (DEC_FLAG_MATRIX_PREFILL): every prompt position as a row of
+# matrix products on the matrix cores, causal attention on the matrix cores.
+# The products' inputs, the rotated queries and the softmax weights are fp16,
+# so the cache bound is the batched one (KV_BATCH); logits keep the 2e-2 bound.
+# Tiny shapes run every product with split K (partials summed in order); the
+# full-size tests run the unsplit tiles.
+# ----------------------------------------------------------------------------
+
+MP = B.DEC_FLAG_MATRIX_PREFILL
+
+
+def check_prefill_kv(d, s, K16, V16, n, what):
+    for l in range(s.n_layers):
+        k, v = d.read_kv(l, n)
+        ek, ev = kv_excess(k, K16[l]), kv_excess(v, V16[l])
+        print(f"{what} layer {l}: cache excess k {ek.max():.2e} v {ev.max():.2e}", flush=True)
+        assert ek.max() <= KV_BATCH and ev.max() <= KV_BATCH, (l, ek.max(), ev.max())
+
+
+@pytest.mark.parametrize("n", [1, 2, 15, 16, 17, 33, 100, 128])
+def test_tiny_matrix_prefill(stream, n):
+    s = synth.shape_for("tiny")
+    t = synth.make_weights(s, seed=35, gain_jitter=0.1)
+    prompt = synth.make_prompt(s.vocab, n, seed=36 + n)[0]
+    steps = min(6, s.max_ctx - n)
+    fed, ref, ref_pre, _ = O.greedy_decode(s, t, prompt, steps)
+    _, K16, V16, _ = O.prefill_matrix(s, t, prompt)
+    with make(s, t, stream, flags=MP) as d:
+        tok, pre = d.prefill(prompt, want_logits=True)
+        check_logits(pre, ref_pre, f"matrix prefill of {n}")
+        assert tok == int(np.argmax(pre))
+        assert d.position == n
+        check_prefill_kv(d, s, K16, V16, n, f"matrix prefill of {n}")
+        for i in range(steps):
+            tk, lg = d.step(force_tok=int(fed[i]), want_logits=True)
+            check_logits(lg, ref[i], f"step {i} after matrix prefill of {n}")
+            assert tk == int(np.argmax(lg))
+        if n == s.max_ctx:
+            with pytest.raises(B.DecError) as ei:
+                d.step()
+            assert ei.value.code == B.DEC_ERR_CONTEXT_FULL
+
+
+def test_matrix_prefill_then_generate_matches_steps(stream):
+    """After a matrix prefill the device-side next token feeds decode; a reset
+    handle prefills again to the same tokens (no state kept between prompts)."""
+    s = synth.shape_for("tiny")
+    t = synth.make_weights(s, seed=37)
+    prompt = synth.make_prompt(s.vocab, 19, seed=38)[0]
+    other = synth.make_prompt(s.vocab, 40, seed=39)[0]
+    with make(s, t, stream, flags=MP) as a, make(s, t, stream, flags=MP) as b:
+        ta, pa = a.prefill(prompt, want_logits=True)
+        b.prefill(other)
+        b.generate(5)
+        b.reset()
+        tb, pb = b.prefill(prompt, want_logits=True)
+        assert ta == tb
+        np.testing.assert_array_equal(pa, pb)
+        ga = a.generate(10)
+        gb = [b.step()[0] for _ in range(10)]
+        assert list(ga) == gb
+
+
+def test_matrix_prefill_spans_two_chunks(stream):
+    """2100 prompt positions: 2048 in the first pass over the weights and 52 in
+    the second, whose attention reads the first pass's cache entries."""
+    n = 2100
+    s = synth.shape_for("tiny").with_(max_ctx=2112)
+    t = synth.make_weights(s, seed=47, gain_jitter=0.1)
+    prompt = synth.make_prompt(s.vocab, n, seed=48)[0]
+    lg, K16, V16, _ = O.prefill_matrix(s, t, prompt)
+    ref = O.OracleDecoder(s, t)
+    ref.load_cache(K16, V16, n)
+    with make(s, t, stream, flags=MP) as d:
+        tok, pre = d.prefill(prompt, want_logits=True)
+        check_logits(pre, lg[-1], f"matrix prefill of {n}")
+        check_prefill_kv(d, s, K16, V16, n, f"matrix prefill of {n}")
+        nxt = O.greedy(lg[-1])
+        for i in range(3):
+            want = ref.step(nxt)
+            _, got = d.step(force_tok=int(nxt), want_logits=True)
+            check_logits(got, want, f"step {i} after matrix prefill of {n}")
+            nxt = O.greedy(want)
+
+
+# ----------------------------------------------------------------------------
 # other grid sizes: fewer workgroups than barrier groups, odd splits
 # ----------------------------------------------------------------------------
 

@@ -13,8 +13,9 @@ pinned to the oracle by tests/test_fullsize_fixtures.py).  Tolerances:
     deeper layers inherit fp32-versus-float64 differences from every layer
     below and every earlier position, and stay within one spacing plus 2e-3
     of the layer's rms;
-  * K/V rows, batched kernel (batch 8, batched prefill): its matrix-product
-    inputs are rounded to fp16, so 1e-2 of the rms (the batched bound).
+  * K/V rows, batched kernel (batch 8, batched prefill) and matrix prefill:
+    matrix-product inputs are rounded to fp16, so 1e-2 of the rms (the
+    batched bound).
 """
 import numpy as np
 import pytest
@@ -28,6 +29,7 @@ pytestmark = pytest.mark.gpu
 KV_B1 = 2e-3
 KV_BATCH = 1e-2
 BP = B.DEC_FLAG_BATCHED_PREFILL
+MP = B.DEC_FLAG_MATRIX_PREFILL
 
 
 @pytest.fixture(scope="module")
@@ -158,6 +160,26 @@ def test_dense2b_batched_prefill_teacher_forced(stream):
     """The metric's prompt through the batched prefill, then the 512 forced steps."""
     fx = Fixture("dense2b")
     run_teacher_forced(fx, stream, "dense2b batched prefill 128 + 512", flags=BP, kv_bound=KV_BATCH)
+
+
+def test_dense2b_matrix_prefill_teacher_forced(stream):
+    """The metric's 128-token prompt as the rows of matrix products, then 64 forced steps."""
+    run_teacher_forced(Fixture("dense2b"), stream, "dense2b matrix prefill 128 + 64", flags=MP, kv_bound=KV_BATCH,
+                       steps=64)
+
+
+def test_dense2b_long_matrix_prefill_teacher_forced(stream):
+    """The 3968-token prompt in two passes over the weights (2048 + 1920 positions),
+    then the 128 forced steps to the 4096 cap."""
+    run_teacher_forced(Fixture("dense2b_long"), stream, "dense2b_long matrix prefill 3968 + 128", flags=MP,
+                       kv_bound=KV_BATCH)
+
+
+def test_lane2b_matrix_prefill_teacher_forced(stream):
+    """One lane's shape through the matrix prefill: 384-wide Q/K/V and a 1728-row
+    gate/up product leave ragged column tiles."""
+    run_teacher_forced(Fixture("lane2b"), stream, "lane2b matrix prefill 128 + 64", flags=MP, kv_bound=KV_BATCH,
+                       steps=64)
 
 
 def test_dense2b_b8_teacher_forced(stream):

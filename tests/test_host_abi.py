@@ -81,6 +81,29 @@ def test_batched_prefill_flag_rules(lib):
     assert 4.5e9 < withf - plain < 4.8e9
 
 
+def test_matrix_prefill_flag_rules(lib):
+    f = B.DEC_FLAG_MATRIX_PREFILL
+    assert B.check_desc(desc(flags=f)) == B.DEC_OK, B.last_error()
+    assert B.check_desc(desc(flags=f, batch=2)) == B.DEC_ERR_BAD_DESC       # batch-1 handles only
+    assert B.check_desc(desc(flags=f | B.DEC_FLAG_BATCHED_PREFILL)) == B.DEC_ERR_BAD_DESC   # one prefill form
+    assert B.check_desc(desc(flags=f | 1)) == B.DEC_ERR_BAD_DESC            # unknown bit
+    # matrix-product K dimensions and head_dim in whole 32-wide K steps
+    assert B.check_desc(desc(flags=f, head_dim=16)) == B.DEC_ERR_UNSUPPORTED
+    assert B.check_desc(desc(flags=f, d_model=264)) == B.DEC_ERR_UNSUPPORTED
+    assert B.check_desc(desc(flags=f, d_ffn=1000)) == B.DEC_ERR_UNSUPPORTED
+    assert B.check_desc(desc(head_dim=16)) == B.DEC_OK                     # no flag: no such limit
+    for name in ("dense2b", "lane2b"):
+        assert B.check_desc(B.ModelDesc.from_shape(synth.shape_for(name), flags=f)) == B.DEC_OK, B.last_error()
+    d2 = synth.shape_for("dense2b")
+    plain = B.arena_bytes(B.ModelDesc.from_shape(d2))
+    withf = B.arena_bytes(B.ModelDesc.from_shape(d2, flags=f))
+    # workspace for 2048 positions (per position: fp32 residual 10 KB, fp16 product input
+    # 13.8 KB, fp16 q 5 KB, fp32 product 55.3 KB, one scale), about 172 MB, plus 32 MB of
+    # split-K partial sums
+    per_pos = 4 * 2560 + 2 * 6912 + 2 * 2560 + 4 * 13824 + 4
+    assert 2048 * per_pos + 32 * 2**20 <= withf - plain < 2048 * per_pos + 32 * 2**20 + 4096
+
+
 def test_valid_descs_and_arena(lib):
     for name in ("tiny", "dense2b", "lane2b"):
         d = B.ModelDesc.from_shape(synth.shape_for(name))
