@@ -915,6 +915,7 @@ int init_impl(const dec_model_desc* desc, const dec_weights_src* weights, const 
     return bail(DEC_ERR_UNSUPPORTED);
   }
   hipError_t e = (hipError_t)kernel_prepare();
+  if (e == hipSuccess && matrix_prefill(*desc)) e = (hipError_t)mp_prepare();
   if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipFuncSetAttribute"); return bail(DEC_ERR_DEVICE); }
   int per_cu = 0;
   e = (hipError_t)kernel_blocks_per_cu(desc->batch, desc->head_dim, &per_cu);

@@ -225,7 +225,7 @@ enum MpEpilogue : int {
   MP_EP_ACCUM = 1,   // C += A B^T
   MP_EP_PART = 2,    // internal: one K split's partial sums
 };
-constexpr int kMpShapes = 6;           // tile shapes: 128x128, 128x64, 64x64, 64x32, 32x32, 16x64
+constexpr int kMpShapes = 6;           // tile shapes: 128x128, 128x64 (register-staged), 64x64, 128x64, 64x32 (LDS DMA), 16x64
 constexpr int kMpChunk = 2048;         // prompt positions per pass over the weights
 constexpr size_t kMpPartFloats = size_t(8) << 20;   // split-K partial sums buffer (floats)
 struct MpGemm {
@@ -238,6 +238,7 @@ struct MpGemm {
   int shape, S, kc;          // from mp_plan: tile shape, K splits, K elements per split
   float* part;               // [S][M][N] partial sums when S > 1
 };
+int mp_prepare();
 void mp_plan(int M, int N, int K, size_t part_floats, int* shape, int* S, int* kc);
 int mp_launch_embed(const uint16_t* E, const int* tok, int n, int d, float* x, void* stream);
 int mp_launch_norm(const float* x, const float* g, int n, int d, float eps, uint16_t* h, float* s, void* stream);

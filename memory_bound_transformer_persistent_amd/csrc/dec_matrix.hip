@@ -37,6 +37,7 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4m __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc;
+typedef __attribute__((address_space(3))) void lds_ptr;
 
 constexpr uint32_t kOutOfRange = 0x80000000u;   // a buffer offset past every record: reads 0
 
@@ -46,6 +47,34 @@ __device__ __forceinline__ rsrc make_res(const void* base, uint64_t bytes) {
 }
 __device__ __forceinline__ f16x8 ld8(rsrc r, uint32_t off) {
   return __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// s_waitcnt vmcnt(N): at most N of this wave's vector-memory loads (LDS DMA
+// included) still pending; they complete in issue order
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ void wait_lgkm0() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt/expcnt untouched
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Wait until at most `later` K tiles' DMAs (PER loads each) are pending.
+template <int PER, int NS>
+__device__ __forceinline__ void wait_tiles(int later) {
+  static_assert(PER * (NS - 2) < 64, "vmcnt is 6 bits");
+  switch (later) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<PER * (NS >= 3)>(); break;
+    case 2: wait_vmcnt<PER * 2 * (NS >= 4)>(); break;
+    case 3: wait_vmcnt<PER * 3 * (NS >= 5)>(); break;
+    case 4: wait_vmcnt<PER * 4 * (NS >= 6)>(); break;
+    case 5: wait_vmcnt<PER * 5 * (NS >= 7)>(); break;
+    default: wait_vmcnt<PER * 6 * (NS >= 8)>(); break;
+  }
 }
 __device__ __forceinline__ float wave_sum64(float v) {
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -153,6 +182,232 @@ __global__ __launch_bounds__(256) void mp_gemm(const uint16_t* __restrict__ A, i
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
         const int n = n0 + 16 * j + r16;
+        if (n >= N) continue;
+        float* c = Cz + (size_t)m * ldc + n;
+        const float v = acc[i][j][r];
+        if (mode == MP_EP_ACCUM) *c = *c + v;
+        else *c = v * sc;
+      }
+    }
+  }
+}
+
+// One wave's share of K tile t of an LDS-staged product: PER 1 KB operand
+// blocks (block wave + 4 j) into stage t % NS, one 16-byte LDS DMA per lane.
+// roff is the lane's row offset at the split's first K element (kOutOfRange
+// for rows past the matrix), kst the block's K step within the tile.
+template <int PER, int NS, int STAGE>
+__device__ __forceinline__ void dma_tile(char* lds, int t, int wave, int lane, rsrc ra, rsrc rb, const uint32_t* roff,
+                                         const int* kst, const bool* isa, int kb, int ke) {
+  char* st = lds + (t % NS) * STAGE;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int k0 = t * 64 + kst[j] * 32;   // from kb
+    const uint32_t off = (roff[j] != kOutOfRange && kb + k0 < ke) ? roff[j] + (uint32_t)k0 * 2u : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(isa[j] ? ra : rb, (lds_ptr*)(st + (wave + 4 * j) * 1024), 16, off, 0, 0,
+                                             0);
+  }
+}
+
+// The same product with both operands staged in LDS, for 17 to 128 rows
+// (the weight-streaming products): BM x BN tiles, K in 64-wide tiles, NS
+// tiles in flight.  A tile's
+// operands land in LDS as 1 KB blocks already in the MFMA operand layout:
+// block (r, s) holds rows 16 r .. +15 and K step s (32 wide) of the tile,
+// lane l's 16 bytes at 16 l being row l % 16, K elements 8 (l / 16) .. +7.
+// Each block is one 16-byte-per-lane LDS DMA of one wave
+// (buffer_load ... lds), so the operand reads are linear ds_read_b128 with no
+// bank conflicts and no register staging.  The four waves split the tile
+// 2 x 2, each computing (BM/2) x (BN/2) with v_mfma_f32_16x16x32_f16.  Rows
+// past M or N and K steps past the split's end load nothing useful (offsets
+// past the buffer); their products are skipped or land in rows and columns
+// that are not stored.
+template <int BM, int BN, int NS>
+__global__ __launch_bounds__(256) void mp_gemm_lds(const uint16_t* __restrict__ A, int lda,
+                                                   const uint16_t* __restrict__ B, int ldb, float* __restrict__ C,
+                                                   int ldc, const float* __restrict__ s, int M, int N, int K, int kc,
+                                                   int mode) {
+  constexpr int WM = BM / 32, WN = BN / 32;          // 16 x 16 blocks per wave
+  constexpr int ABLK = BM / 16 * 2, BBLK = BN / 16 * 2;
+  constexpr int NBLK = ABLK + BBLK, PER = NBLK / 4;  // DMA blocks per tile, per wave
+  constexpr int STAGE = NBLK * 1024;
+  static_assert(NBLK % 4 == 0, "blocks split evenly over the waves");
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  // the wave index in a scalar register: buffer descriptors and LDS bases chosen by it stay scalar
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int mb = blockIdx.y * BM, nb = blockIdx.x * BN;
+  const int kb = blockIdx.z * kc, ke = min(K, kb + kc);
+  const int ntiles = (ke - kb + 63) / 64;
+  const rsrc ra = make_res(A, (uint64_t)M * lda * 2), rb = make_res(B, (uint64_t)N * ldb * 2);
+  // this wave's DMA blocks: b = wave + 4 j; the lane's row offset (bytes, at K = kb) and K step
+  uint32_t roff[PER];
+  int kst[PER];
+  bool isa[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int b = wave + 4 * j;
+    isa[j] = b < ABLK;
+    const int bb = isa[j] ? b : b - ABLK;
+    kst[j] = bb & 1;
+    const int row = (isa[j] ? mb : nb) + (bb >> 1) * 16 + (lane & 15);
+    const int lim = isa[j] ? M : N;
+    const int ld = isa[j] ? lda : ldb;
+    roff[j] = row < lim ? (uint32_t)((size_t)row * ld + kb + (lane >> 4) * 8) * 2u : kOutOfRange;
+  }
+  f32x4m acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = f32x4m{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < ntiles) dma_tile<PER, NS, STAGE>(lds, t, wave, lane, ra, rb, roff, kst, isa, kb, ke);
+  for (int t = 0; t < ntiles; ++t) {
+    // this wave's blocks of tile t have landed once at most the later tiles' DMAs are pending
+    // Every wave's blocks of tile t are in LDS and tile t-1's stage is free
+    // once all waves pass: each waits for its own DMAs of tile t (later
+    // tiles' stay in flight) and its LDS reads, then the plain s_barrier.
+    // (__syncthreads would also drain every pending DMA.)
+    wait_tiles<PER, NS>(min(NS - 2, ntiles - 1 - t));
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (t + NS - 1 < ntiles) dma_tile<PER, NS, STAGE>(lds, t + NS - 1, wave, lane, ra, rb, roff, kst, isa, kb, ke);
+    const char* as = lds + (t % NS) * STAGE;
+    const char* bs = as + ABLK * 1024;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (kb + t * 64 + ks * 32 >= ke) break;
+      f16x8 a[WM], b[WN];
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+        a[i] = *reinterpret_cast<const f16x8*>(as + ((wr * WM + i) * 2 + ks) * 1024 + 16 * lane);
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+        b[j] = *reinterpret_cast<const f16x8*>(bs + ((wc * WN + j) * 2 + ks) * 1024 + 16 * lane);
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  float* Cz = mode == MP_EP_PART ? C + (size_t)blockIdx.z * M * ldc : C;
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = mb + (wr * WM + i) * 16 + (lane >> 4) * 4 + r;
+      if (m >= M) continue;
+      const float sc = (mode == MP_EP_SCALE && s) ? s[m] : 1.0f;
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const int n = nb + (wc * WN + j) * 16 + (lane & 15);
+        if (n >= N) continue;
+        float* c = Cz + (size_t)m * ldc + n;
+        const float v = acc[i][j][r];
+        if (mode == MP_EP_ACCUM) *c = *c + v;
+        else *c = v * sc;
+      }
+    }
+  }
+}
+
+// The same LDS operand-block layout, staged through registers instead of LDS
+// DMA: each thread loads its 16-byte pieces of K tile t+1 into registers
+// while the tile t products run, then writes them to the other of two LDS
+// stages.  On gfx950 this runs faster than the DMA form for the large tiles
+// (the plain ds_write_b128 path drains faster than 16-byte LDS DMA), while the
+// DMA form's deeper pipelines suit the few-row, weight-streaming products.
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void mp_gemm_rs(const uint16_t* __restrict__ A, int lda,
+                                                  const uint16_t* __restrict__ B, int ldb, float* __restrict__ C,
+                                                  int ldc, const float* __restrict__ s, int M, int N, int K, int kc,
+                                                  int mode) {
+  constexpr int WM = BM / 32, WN = BN / 32;
+  constexpr int ABLK = BM / 16 * 2, BBLK = BN / 16 * 2;
+  constexpr int NBLK = ABLK + BBLK, PER = NBLK / 4, STAGE = NBLK * 1024;
+  static_assert(NBLK % 4 == 0, "blocks split evenly over the waves");
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int mb = blockIdx.y * BM, nb = blockIdx.x * BN;
+  const int kb = blockIdx.z * kc, ke = min(K, kb + kc);
+  const int ntiles = (ke - kb + 63) / 64;
+  const rsrc ra = make_res(A, (uint64_t)M * lda * 2), rb = make_res(B, (uint64_t)N * ldb * 2);
+  uint32_t roff[PER];
+  int kst[PER];
+  bool isa[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int b = wave + 4 * j;
+    isa[j] = b < ABLK;
+    const int bb = isa[j] ? b : b - ABLK;
+    kst[j] = bb & 1;
+    const int row = (isa[j] ? mb : nb) + (bb >> 1) * 16 + (lane & 15);
+    const int lim = isa[j] ? M : N;
+    const int ld = isa[j] ? lda : ldb;
+    roff[j] = row < lim ? (uint32_t)((size_t)row * ld + kb + (lane >> 4) * 8) * 2u : kOutOfRange;
+  }
+  f16x8 reg[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int k0 = kst[j] * 32;
+    reg[j] = ld8(isa[j] ? ra : rb, (roff[j] != kOutOfRange && kb + k0 < ke) ? roff[j] + (uint32_t)k0 * 2u : kOutOfRange);
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) *reinterpret_cast<f16x8*>(lds + (wave + 4 * j) * 1024 + 16 * lane) = reg[j];
+  __syncthreads();
+  f32x4m acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = f32x4m{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < ntiles; ++t) {
+    const bool next = t + 1 < ntiles;
+    if (next) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int k0 = (t + 1) * 64 + kst[j] * 32;
+        reg[j] = ld8(isa[j] ? ra : rb,
+                     (roff[j] != kOutOfRange && kb + k0 < ke) ? roff[j] + (uint32_t)k0 * 2u : kOutOfRange);
+      }
+    }
+    const char* as = lds + (t & 1) * STAGE;
+    const char* bs = as + ABLK * 1024;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (kb + t * 64 + ks * 32 >= ke) break;
+      f16x8 a[WM], b[WN];
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+        a[i] = *reinterpret_cast<const f16x8*>(as + ((wr * WM + i) * 2 + ks) * 1024 + 16 * lane);
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+        b[j] = *reinterpret_cast<const f16x8*>(bs + ((wc * WN + j) * 2 + ks) * 1024 + 16 * lane);
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (next) {
+      char* st = lds + ((t + 1) & 1) * STAGE;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) *reinterpret_cast<f16x8*>(st + (wave + 4 * j) * 1024 + 16 * lane) = reg[j];
+    }
+    __syncthreads();   // tile t+1 is in LDS; tile t's stage may be overwritten
+  }
+  float* Cz = mode == MP_EP_PART ? C + (size_t)blockIdx.z * M * ldc : C;
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = mb + (wr * WM + i) * 16 + (lane >> 4) * 4 + r;
+      if (m >= M) continue;
+      const float sc = (mode == MP_EP_SCALE && s) ? s[m] : 1.0f;
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const int n = nb + (wc * WN + j) * 16 + (lane & 15);
         if (n >= N) continue;
         float* c = Cz + (size_t)m * ldc + n;
         const float v = acc[i][j][r];
@@ -375,8 +630,43 @@ __global__ __launch_bounds__(1024) void mp_argmax(const float* __restrict__ logi
   }
 }
 
-constexpr int kShapeBM[kMpShapes] = {128, 128, 64, 64, 32, 16};
-constexpr int kShapeBN[kMpShapes] = {128, 64, 64, 32, 32, 64};
+// Tile shapes (index = MpGemm::shape): register-staged 128 x 128 and
+// 128 x 64 tiles for many rows; LDS-DMA 64 x 64, 128 x 64 and 64 x 32 tiles
+// with four K tiles in flight for up to 128 rows, where the product streams
+// the weights; the register-direct 16 x 64 tile for one to 16 rows.
+constexpr int kShapeBM[kMpShapes] = {128, 128, 64, 128, 64, 16};
+constexpr int kShapeBN[kMpShapes] = {128, 64, 64, 64, 32, 64};
+
+template <int BM, int BN, int NS>
+constexpr int lds_bytes() { return NS * (BM / 16 * 2 + BN / 16 * 2) * 1024; }
+
+template <int BM, int BN, int NS>
+hipError_t prepare_lds() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&mp_gemm_lds<BM, BN, NS>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes<BM, BN, NS>());
+}
+template <int BM, int BN>
+hipError_t prepare_rs() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&mp_gemm_rs<BM, BN>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes<BM, BN, 2>());
+}
+
+template <int BM, int BN, int NS>
+void gemm_lds_as(const MpGemm& g, dim3 grid, hipStream_t st) {
+  const bool split = g.S > 1;
+  constexpr int lds = lds_bytes<BM, BN, NS>();
+  hipLaunchKernelGGL((mp_gemm_lds<BM, BN, NS>), grid, dim3(256), lds, st, g.A, g.lda, g.B, g.ldb,
+                     split ? g.part : g.C, split ? g.N : g.ldc, g.s, g.M, g.N, g.K, g.kc,
+                     split ? (int)MP_EP_PART : g.mode);
+}
+
+template <int BM, int BN>
+void gemm_rs_as(const MpGemm& g, dim3 grid, hipStream_t st) {
+  const bool split = g.S > 1;
+  constexpr int lds = lds_bytes<BM, BN, 2>();
+  hipLaunchKernelGGL((mp_gemm_rs<BM, BN>), grid, dim3(256), lds, st, g.A, g.lda, g.B, g.ldb, split ? g.part : g.C,
+                     split ? g.N : g.ldc, g.s, g.M, g.N, g.K, g.kc, split ? (int)MP_EP_PART : g.mode);
+}
 
 template <int WM, int WN, int WR>
 void gemm_as(const MpGemm& g, dim3 grid, hipStream_t st) {
@@ -387,26 +677,33 @@ void gemm_as(const MpGemm& g, dim3 grid, hipStream_t st) {
 
 }  // namespace
 
-// Tile shape and K split of a product: the largest tile that still gives
-// every compute unit two workgroups; failing that the smallest tile, with
-// the K range split (up to 8 ways, each split 4 K steps or more, partials
-// within part_floats) until it does.
+// Raise the dynamic-LDS limit of the LDS-staged products (once per process).
+int mp_prepare() {
+  hipError_t e = prepare_rs<128, 128>();
+  if (e == hipSuccess) e = prepare_rs<128, 64>();
+  if (e == hipSuccess) e = prepare_lds<64, 64, 4>();
+  if (e == hipSuccess) e = prepare_lds<128, 64, 4>();
+  if (e == hipSuccess) e = prepare_lds<64, 32, 4>();
+  return (int)e;
+}
+
+// Tile shape and K split of a product.  One to 16 rows: the register-direct
+// tile.  Up to 512 rows: 64 x 64 LDS-DMA tiles (128 x 64 for the widest
+// products above 64 rows).  More rows: the register-staged 128 x 128 tile.
+// Then the K range is split (up to 8 ways, each split 4 K steps or more,
+// partials within part_floats) until about 200 workgroups run.  The choices
+// follow timings of the dense2b products on MI355X at 1 to 3968 rows.
 void mp_plan(int M, int N, int K, size_t part_floats, int* shape, int* S, int* kc) {
-  const long long want = 512;
   auto count = [&](int t) {
     return (long long)((M + kShapeBM[t] - 1) / kShapeBM[t]) * ((N + kShapeBN[t] - 1) / kShapeBN[t]);
   };
-  int pick = -1;
-  if (M <= 16) {
-    pick = kMpShapes - 1;
-  } else {
-    for (int t = 0; t < kMpShapes - 1 && pick < 0; ++t)
-      if (count(t) >= want) pick = t;
-    if (pick < 0) pick = kMpShapes - 2;
-  }
+  int pick;
+  if (M <= 16) pick = 5;
+  else if (M <= 512) pick = (M > 64 && N >= 8192) ? 3 : 2;
+  else pick = 0;
   int s = 1;
   const long long c = count(pick);
-  while (s < 8 && c * s < want && K / (32 * 2 * s) >= 4 && (size_t)(2 * s) * M * N <= part_floats) s *= 2;
+  while (s < 8 && c * s < 200 && K / (32 * 2 * s) >= 4 && (size_t)(2 * s) * M * N <= part_floats) s *= 2;
   const int steps = (K / 32 + s - 1) / s;   // K steps per split
   *shape = pick;
   *S = (K / 32 + steps - 1) / steps;
@@ -430,11 +727,11 @@ int mp_launch_gemm(const MpGemm& g, void* stream) {
                   g.S);
   const hipStream_t st = (hipStream_t)stream;
   switch (g.shape) {
-    case 0: gemm_as<4, 4, 2>(g, grid, st); break;
-    case 1: gemm_as<4, 2, 2>(g, grid, st); break;
-    case 2: gemm_as<2, 2, 2>(g, grid, st); break;
-    case 3: gemm_as<2, 1, 2>(g, grid, st); break;
-    case 4: gemm_as<1, 1, 2>(g, grid, st); break;
+    case 0: gemm_rs_as<128, 128>(g, grid, st); break;
+    case 1: gemm_rs_as<128, 64>(g, grid, st); break;
+    case 2: gemm_lds_as<64, 64, 4>(g, grid, st); break;
+    case 3: gemm_lds_as<128, 64, 4>(g, grid, st); break;
+    case 4: gemm_lds_as<64, 32, 4>(g, grid, st); break;
     default: gemm_as<1, 1, 1>(g, grid, st); break;
   }
   hipError_t e = hipGetLastError();
