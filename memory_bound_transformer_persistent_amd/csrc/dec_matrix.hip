@@ -469,115 +469,136 @@ __global__ __launch_bounds__(256) void mp_rope_kv(const float* __restrict__ qkv,
   }
 }
 
+// DT consecutive fp16 values (DT = 2, 4 or 8) through a buffer descriptor.
+template <int DT>
+struct HalfRow;
+template <>
+struct HalfRow<8> {
+  typedef _Float16 T __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ T load(rsrc r, uint32_t off) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+};
+template <>
+struct HalfRow<4> {
+  typedef _Float16 T __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ T load(rsrc r, uint32_t off) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  }
+};
+template <>
+struct HalfRow<2> {
+  typedef _Float16 T __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ T load(rsrc r, uint32_t off) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  }
+};
+
 // Causal attention of queries pos0 .. pos0+n-1 of one head (blockIdx.y)
-// over cache positions 0 .. pos0+n-1, 16 queries per wave.  For each block of
-// 32 keys at or below the wave's last query: scores S = q k^T on the matrix
-// cores (two 16 x 16 tiles, hd/32 products each), a running max and sum per
-// query row (online softmax), P = exp(S - max) rounded to fp16 and o += P v
-// on the matrix cores.  P moves through LDS from the result layout (query
-// 4 (l/16) + r, key l % 16) to the A-operand layout (query l % 16, keys
-// 8 (l/16) .. +7); the value block is staged transposed (dimension-major,
-// rows padded) so each lane's B operand is 16 contiguous bytes.  Finally
-// o = o / sum, fp16, to o16 [n x q].
+// over cache positions 0 .. pos0+n-1.  Four waves per workgroup, 16 queries
+// per wave, no LDS: everything is computed transposed so that each lane owns
+// one query.  For each block of 32 keys at or below the wave's last query:
+//   scores S^T = K q^T on the matrix cores (A operand: key rows of the cache,
+//   B operand: the wave's query rows), two 16-key tiles; lane l gets query
+//   l % 16 against keys 4 (l/16) + r and 16 + 4 (l/16) + r, r = 0..3;
+//   online softmax per lane (its 8 keys, then the 3 other lanes of the query);
+//   O^T += V^T P^T on the matrix cores, where P^T is the lane's 8 weights in
+//   fp16 as they stand (the products' K index of lane group g is keys
+//   4g .. 4g+3 and 16 + 4g .. +3), and V^T's operand is built in registers:
+//   lane l loads the HD/16 consecutive dims (l%16) HD/16 .. +HD/16-1 of each of
+//   those 8 keys and transposes the 8 x HD/16 block, so output block t holds
+//   dims c HD/16 + t for c = 0..15.
+// Lane l then holds HD/16 consecutive dims per result row: o = o / sum, fp16,
+// to o16 [n x q].  Query blocks run heaviest (latest) first.
 template <int HD>
-__global__ __launch_bounds__(64) void mp_attention(const uint16_t* __restrict__ q16, int q, int n, int pos0,
-                                                   const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-                                                   size_t head_elems, uint16_t* __restrict__ o16) {
-  constexpr int VT = 32 + 8;   // padded key stride of the transposed value block (fp16)
-  __shared__ _Float16 vt[HD * VT];
-  __shared__ float pbuf[16 * 33];
-  const int lane = threadIdx.x, h = blockIdx.y, m0 = blockIdx.x * 16;
-  const int r16 = lane & 15, kq = (lane >> 4) * 8, rq = (lane >> 4) * 4;
+__global__ __launch_bounds__(256) void mp_attention(const uint16_t* __restrict__ q16, int q, int n, int pos0,
+                                                    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+                                                    size_t head_elems, uint16_t* __restrict__ o16) {
+  constexpr int DT = HD / 16;   // dims per lane per output row; output blocks of 16 dims
+  typedef HalfRow<DT> Row;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = blockIdx.y, nqb = (n + 63) / 64;
+  const int m0 = (nqb - 1 - (int)blockIdx.x) * 64 + wave * 16;
+  if (m0 >= n) return;   // the wave has no query (no barriers in this kernel)
+  const int c = lane & 15, g = lane >> 4;
   const int n_keys = pos0 + n;
   const _Float16* kh = reinterpret_cast<const _Float16*>(kc) + (size_t)h * head_elems;
   const _Float16* vh = reinterpret_cast<const _Float16*>(vc) + (size_t)h * head_elems;
-  const rsrc rk = make_res(kh, (uint64_t)n_keys * HD * 2), rqr = make_res(q16, (uint64_t)n * q * 2);
-  // this lane's query-row operands for the hd/32 K steps of the score products
-  f16x8 qa[HD / 32];
+  const rsrc rk = make_res(kh, (uint64_t)n_keys * HD * 2), rv = make_res(vh, (uint64_t)n_keys * HD * 2);
+  const rsrc rq = make_res(q16, (uint64_t)n * q * 2);
+  // B operand of the score products: this lane's query row, dims 32 cc + 8 g .. +7
+  f16x8 qb[HD / 32];
 #pragma unroll
-  for (int c = 0; c < HD / 32; ++c) {
-    const int m = m0 + r16;
-    qa[c] = ld8(rqr, m < n ? (uint32_t)((size_t)m * q + (size_t)h * HD + 32 * c + kq) * 2u : kOutOfRange);
-  }
-  f32x4m acc[HD / 16];
+  for (int cc = 0; cc < HD / 32; ++cc)
+    qb[cc] = ld8(rq, m0 + c < n ? (uint32_t)((size_t)(m0 + c) * q + (size_t)h * HD + 32 * cc + 8 * g) * 2u : kOutOfRange);
+  f32x4m acc[DT];
 #pragma unroll
-  for (int t = 0; t < HD / 16; ++t) acc[t] = f32x4m{0.f, 0.f, 0.f, 0.f};
-  float mrow[4], lrow[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    mrow[r] = -INFINITY;
-    lrow[r] = 0.f;
-  }
-  const int last = pos0 + min(m0 + 15, n - 1);   // position of the wave's last query
+  for (int t = 0; t < DT; ++t) acc[t] = f32x4m{0.f, 0.f, 0.f, 0.f};
+  float mrow = -INFINITY, lsum = 0.f;
+  const int qi = pos0 + m0 + c;                    // this lane's query position
+  const int last = pos0 + min(m0 + 15, n - 1);     // the wave's last query position
   for (int j0 = 0; j0 <= last; j0 += 32) {
-    // scores of keys j0 + l%16 and j0 + 16 + l%16 against this lane's 4 query rows
+    // the 8 keys of this lane group: j0 + 4g + i (i < 4) and j0 + 16 + 4g + i - 4
+    typename Row::T vrow[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = j0 + (i < 4 ? 4 * g + i : 16 + 4 * g + i - 4);
+      vrow[i] = Row::load(rv, key < n_keys ? (uint32_t)(key * HD + c * DT) * 2u : kOutOfRange);
+    }
     f32x4m s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < HD / 32; ++c) {
-      const int ja = j0 + r16, jb = j0 + 16 + r16;
-      const f16x8 ka = ld8(rk, ja < n_keys ? (uint32_t)(ja * HD + 32 * c + kq) * 2u : kOutOfRange);
-      const f16x8 kb = ld8(rk, jb < n_keys ? (uint32_t)(jb * HD + 32 * c + kq) * 2u : kOutOfRange);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[c], ka, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[c], kb, s1, 0, 0, 0);
+    for (int cc = 0; cc < HD / 32; ++cc) {
+      const int ja = j0 + c, jb = j0 + 16 + c;
+      const f16x8 ka = ld8(rk, ja < n_keys ? (uint32_t)(ja * HD + 32 * cc + 8 * g) * 2u : kOutOfRange);
+      const f16x8 kb = ld8(rk, jb < n_keys ? (uint32_t)(jb * HD + 32 * cc + 8 * g) * 2u : kOutOfRange);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[cc], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, qb[cc], s1, 0, 0, 0);
     }
-    // stage this block's values transposed: vt[dim][key] (keys past the cache read 0)
-    __syncthreads();
-    for (int e = lane; e < 32 * (HD / 8); e += 64) {
-      const int key = e / (HD / 8), d8 = (e - key * (HD / 8)) * 8;
-      const int j = j0 + key;
-      f16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (j < n_keys) v = *reinterpret_cast<const f16x8*>(vh + (size_t)j * HD + d8);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) vt[(d8 + t) * VT + key] = v[t];
-    }
-    // online softmax over the 32 keys of each query row
-    float p0[4], p1[4];
+    // online softmax of the lane's query over the 32 keys
+    float p[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int qi = pos0 + m0 + rq + r;
-      const float a = (j0 + r16 <= qi) ? s0[r] : -INFINITY;
-      const float b = (j0 + 16 + r16 <= qi) ? s1[r] : -INFINITY;
-      float mx = fmaxf(a, b);
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-      // key 0 is at or below every query, so the max is finite from the first block on
-      const float mn = fmaxf(mrow[r], mx);
-      const float alpha = expf(mrow[r] - mn);
-      const float e0 = expf(a - mn), e1 = expf(b - mn);
-      float rs = e0 + e1;
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) rs += __shfl_xor(rs, off, 64);
-      lrow[r] = lrow[r] * alpha + rs;
-      mrow[r] = mn;
-      p0[r] = e0;
-      p1[r] = e1;
-#pragma unroll
-      for (int t = 0; t < HD / 16; ++t) acc[t][r] *= alpha;
+      p[r] = (j0 + 4 * g + r <= qi) ? s0[r] : -INFINITY;
+      p[4 + r] = (j0 + 16 + 4 * g + r <= qi) ? s1[r] : -INFINITY;
     }
-    // P to the A-operand layout through LDS (rounded to fp16 there)
+    float mx = p[0];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pbuf[(rq + r) * 33 + r16] = p0[r];
-      pbuf[(rq + r) * 33 + 16 + r16] = p1[r];
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, p[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // key 0 is at or below every query, so the max is finite from the first block on
+    const float mn = fmaxf(mrow, mx);
+    const float alpha = expf(mrow - mn);
+    f16x8 pb;
+    float rs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float e = expf(p[i] - mn);
+      rs += e;
+      pb[i] = (_Float16)e;
     }
-    __syncthreads();
-    f16x8 pa;
+    rs += __shfl_xor(rs, 16, 64);
+    rs += __shfl_xor(rs, 32, 64);
+    lsum = lsum * alpha + rs;
+    mrow = mn;
+    // O^T += V^T P^T, output block t = dims c DT + t
 #pragma unroll
-    for (int t = 0; t < 8; ++t) pa[t] = (_Float16)pbuf[r16 * 33 + kq + t];
+    for (int t = 0; t < DT; ++t) {
+      f16x8 va;
 #pragma unroll
-    for (int t = 0; t < HD / 16; ++t) {
-      const f16x8 vb = *reinterpret_cast<const f16x8*>(&vt[(16 * t + r16) * VT + kq]);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, acc[t], 0, 0, 0);
+      for (int i = 0; i < 8; ++i) va[i] = vrow[i][t];
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[t] * alpha, 0, 0, 0);
     }
   }
+  if (m0 + c >= n) return;
+  const float inv = 1.0f / lsum;
+  _Float16* orow = reinterpret_cast<_Float16*>(o16) + (size_t)(m0 + c) * q + (size_t)h * HD;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int m = m0 + rq + r;
-    if (m >= n) continue;
-    const float inv = 1.0f / lrow[r];
-    _Float16* orow = reinterpret_cast<_Float16*>(o16) + (size_t)m * q + (size_t)h * HD;
+    typename Row::T o;
 #pragma unroll
-    for (int t = 0; t < HD / 16; ++t) orow[16 * t + r16] = (_Float16)(acc[t][r] * inv);
+    for (int t = 0; t < DT; ++t) o[t] = (_Float16)(acc[t][r] * inv);
+    *reinterpret_cast<typename Row::T*>(orow + (4 * g + r) * DT) = o;
   }
 }
 
@@ -749,12 +770,12 @@ int mp_launch_rope_kv(const float* qkv, int n, int q, int hd, int pos0, const fl
 }
 int mp_launch_attention(const uint16_t* q16, int q, int n, int pos0, int H, int hd, const uint16_t* kc,
                         const uint16_t* vc, size_t head_elems, uint16_t* o16, void* stream) {
-  const dim3 grid((n + 15) / 16, H);
+  const dim3 grid((n + 63) / 64, H);
   const hipStream_t st = (hipStream_t)stream;
   switch (hd) {
-    case 32: hipLaunchKernelGGL(mp_attention<32>, grid, dim3(64), 0, st, q16, q, n, pos0, kc, vc, head_elems, o16); break;
-    case 64: hipLaunchKernelGGL(mp_attention<64>, grid, dim3(64), 0, st, q16, q, n, pos0, kc, vc, head_elems, o16); break;
-    case 128: hipLaunchKernelGGL(mp_attention<128>, grid, dim3(64), 0, st, q16, q, n, pos0, kc, vc, head_elems, o16); break;
+    case 32: hipLaunchKernelGGL(mp_attention<32>, grid, dim3(256), 0, st, q16, q, n, pos0, kc, vc, head_elems, o16); break;
+    case 64: hipLaunchKernelGGL(mp_attention<64>, grid, dim3(256), 0, st, q16, q, n, pos0, kc, vc, head_elems, o16); break;
+    case 128: hipLaunchKernelGGL(mp_attention<128>, grid, dim3(256), 0, st, q16, q, n, pos0, kc, vc, head_elems, o16); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
