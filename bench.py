@@ -14,13 +14,17 @@ weight (the whole hot path).
 The same JSON line also carries, each measured in this run on its own handle:
   workloads.lane2b        one lane of an 8-way split (3 heads, FFN 864, an
                           8192-row LM shard): 128-token prompt + 1024 steps
-  workloads.dense2b_long  a 3968-token prompt through the batched prefill,
+  workloads.dense2b_long  a 3968-token prompt through the matrix prefill,
                           then 128 steps to the 4096 cap
   workloads.dense2b_b8    8 sequences of 256-token prompts, 256 steps together
                           (value = tokens/s of all 8; per request = of each)
   ttft                    time to first token of the 128-token prompt: one
-                          position per step (the decode kernel) and batched
-                          (8 positions per step on the matrix-core kernel)
+                          position per step (the decode kernel), batched (8
+                          positions per step on the matrix-core kernel) and
+                          matrix (every position as a row of the products);
+                          ttft.long: the 3968-token prompt, batched and matrix,
+                          with the matrix prefill's flop rate against the
+                          2.5 PFLOP/s fp16 peak
   generate                the main span in one dec_generate launch
   stream_ceiling          a plain 16-byte non-temporal read of 2 GiB
   cpu_baseline            the CPU oracle on a bounded sample of the same steps
@@ -193,8 +197,8 @@ def extra_workload(B, R, torch, name, full_tensors, stream, warmup, serve):
     import synth
     w = synth.workload(name)
     tensors = synth.lane_from_full(w.shape, full_tensors) if w.lane else full_tensors
-    bp = name == "dense2b_long"      # the long prompt goes through the batched prefill
-    r = Run(B, R, torch, w, tensors, stream, flags=B.DEC_FLAG_BATCHED_PREFILL if bp else 0, serve=serve)
+    mp = name == "dense2b_long"      # the long prompt goes through the matrix prefill
+    r = Run(B, R, torch, w, tensors, stream, flags=B.DEC_FLAG_MATRIX_PREFILL if mp else 0, serve=serve)
     try:
         r.warm(warmup)
         pre = r.prefill_ms()
@@ -202,7 +206,7 @@ def extra_workload(B, R, torch, name, full_tensors, stream, warmup, serve):
         region, segs = r.decode(w.steps)
         out = r.record(pos0, w.steps, region, kernel_name(w))
         out["prefill"] = {"tokens": w.prompt_len, "sequences": w.batch, "ms": round(pre, 3),
-                          "mode": "batched, 8 positions per step" if bp else "one position per step"}
+                          "mode": "matrix, all positions per product" if mp else "one position per step"}
         out["workload"] = f"{w.name}: {w.description}; prompt {w.prompt_len} + {w.steps} greedy steps, batch {w.batch}"
         out["segments_tokens_per_s"] = [round(x, 1) for x in segs]
         return out
@@ -347,17 +351,33 @@ def main():
                            "launches": 1}
     r.close()
     if w.name == "dense2b" and not args.no_extras and not args.multilaunch:
-        # time to first token of the 128-token prompt, both prefill paths
-        ttft = {"tokens": w.prompt_len}
-        for key, fl in (("one_position_per_step_ms", 0), ("batched_8_per_step_ms", B.DEC_FLAG_BATCHED_PREFILL)):
-            rt = Run(B, R, torch, w, tensors, stream, flags=fl)
+        # time to first token of the 128-token prompt, every prefill path, and
+        # of the 3968-token prompt through the two matrix-core paths
+        def ttft_ms(wl, fl, reps):
+            rt = Run(B, R, torch, wl, tensors, stream, flags=fl)
             rt.warm(0)
             times = []
-            for _ in range(3):
+            for _ in range(reps):
                 times.append(rt.prefill_ms())
                 rt.dec.reset()
-            ttft[key] = round(min(times), 3)
             rt.close()
+            return min(times)
+        ttft = {"tokens": w.prompt_len}
+        for key, fl in (("one_position_per_step_ms", 0), ("batched_8_per_step_ms", B.DEC_FLAG_BATCHED_PREFILL),
+                        ("matrix_ms", B.DEC_FLAG_MATRIX_PREFILL)):
+            ttft[key] = round(ttft_ms(w, fl, 3), 3)
+        wl = synth.workload("dense2b_long")
+        long_mp = ttft_ms(wl, B.DEC_FLAG_MATRIX_PREFILL, 3)
+        fl_long = R.prefill_flops(wl.shape, wl.prompt_len)
+        achieved_tf = fl_long / (long_mp / 1e3) / 1e12
+        ttft["long"] = {"tokens": wl.prompt_len, "matrix_ms": round(long_mp, 2),
+                        "batched_8_per_step_ms": round(ttft_ms(wl, B.DEC_FLAG_BATCHED_PREFILL, 1), 1),
+                        "roofline": {"bound": "mfma", "achieved": round(achieved_tf, 1),
+                                     "peak": R.MI355X_FP16_PEAK / 1e12, "unit": "TFLOP/s",
+                                     "frac": round(achieved_tf * 1e12 / R.MI355X_FP16_PEAK, 4),
+                                     "flops": fl_long, "kernels": "whole prefill (products, attention, "
+                                                                  "norms, rotary, SwiGLU, LM row)"}}
+        ttft["matrix_tflops_128"] = round(R.prefill_flops(s, w.prompt_len) / (ttft["matrix_ms"] / 1e3) / 1e12, 1)
         out["ttft"] = ttft
         out["workloads"] = {}
         for name in EXTRAS:

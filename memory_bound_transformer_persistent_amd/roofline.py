@@ -11,6 +11,7 @@ is from the same page, section 標準推論スタックのボトルネックとK
 from dataclasses import dataclass
 
 MI355X_HBM_PEAK = 8.0e12   # bytes/s, published HBM3E peak of one MI355X
+MI355X_FP16_PEAK = 2.5e15  # flop/s, published dense fp16 matrix peak of one MI355X
 
 
 def bound_tokens_per_s(bw_bytes_per_s, weight_bytes, kv_bytes=0.0, beta=1.0):
@@ -72,3 +73,16 @@ def roofline_tokens_per_s(shape, first_pos: int, n_steps: int, batch: int = 1,
                           bw=MI355X_HBM_PEAK) -> float:
     """Per-request tokens/s bound over a run of n_steps starting at first_pos."""
     return bw / mean_step_bytes(shape, first_pos, n_steps, batch)
+
+
+def prefill_flops(shape, n: int) -> int:
+    """Algorithmic flops of a whole-prompt prefill of n positions (one sequence).
+
+    Every position goes through every layer's matrices (2 flops per weight),
+    causal attention scores and weighted sums for query i over keys 0..i
+    (2 hd flops each, twice), and the LM head for the last position only.
+    """
+    d, q, f = shape.d_model, shape.n_heads * shape.head_dim, shape.d_ffn
+    mats = 3 * q * d + d * q + 2 * f * d + d * f
+    attn = 2 * shape.n_heads * shape.head_dim * n * (n + 1)     # sum over i of 2 * 2 hd (i + 1)
+    return shape.n_layers * (2 * n * mats + attn) + 2 * shape.lm_vocab * d

@@ -67,3 +67,22 @@ def test_lane_slices_of_drawn_tensors_equal_the_lane_draw():
     assert len(a) == len(b)
     for x, y in zip(a, b):
         assert x.shape == y.shape and np.array_equal(x, y)
+
+
+def test_prefill_flops_counts_every_product_once():
+    """The matrix prefill's algorithmic flops, against an explicit count over
+    positions, heads and keys on a small shape."""
+    import synth
+    from memory_bound_transformer_persistent_amd import roofline as R
+    s = synth.shape_for("tiny")
+    d, q, f = s.d_model, s.n_heads * s.head_dim, s.d_ffn
+    for n in (1, 2, 7):
+        count = 0
+        for _ in range(s.n_layers):
+            for i in range(n):
+                count += 2 * (3 * q * d) + 2 * (d * q) + 2 * (2 * f * d) + 2 * (d * f)   # the four products
+                for _h in range(s.n_heads):
+                    for _j in range(i + 1):
+                        count += 2 * s.head_dim + 2 * s.head_dim                   # q.k and p v
+        count += 2 * s.lm_vocab * d                                                 # the last row's logits
+        assert R.prefill_flops(s, n) == count
