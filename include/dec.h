@@ -107,9 +107,9 @@ typedef enum dec_status {
  * hakusoku.com/story/7519, section 単一リクエストLLMデコード速度の重要性.
  * Needs head_dim >= 32 and d_model, n_heads*head_dim, d_ffn multiples of 32
  * (DEC_ERR_UNSUPPORTED otherwise).  The handle's arena holds a workspace of
- * about min(max_ctx, 2048) x (4 d_model + 2 max(d_model, H hd, d_ffn) +
- * 2 H hd + 4 max(3 H hd, 2 d_ffn)) bytes plus up to 32 MB of partial sums
- * (dec_arena_bytes includes it).  Numerics: the products' inputs are rounded
+ * about min(max_ctx, 2048) x (4 d_model + 2 max(d_model, H hd) + 2 H hd +
+ * 2 d_ffn + 4) bytes plus up to 32 MB of partial sums (dec_arena_bytes
+ * includes it).  Numerics: the products' inputs are rounded
  * to fp16 as with DEC_FLAG_BATCHED_PREFILL, and so are the rotated queries and
  * the softmax weights of the attention products.  Decode steps are unchanged.
  */

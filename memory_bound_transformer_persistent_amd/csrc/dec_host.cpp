@@ -288,7 +288,7 @@ bool same_shape(const dec_model_desc& a, const dec_model_desc& b) {
 // device arena layout (bytes)
 // ---------------------------------------------------------------------------
 struct Arena {
-  size_t w, w2, gains, rope, kv, mp_x, mp_h, mp_q16, mp_c, mp_s, mp_part, x, xg16, ssp, qkv, att_o, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out,
+  size_t w, w2, gains, rope, kv, mp_x, mp_h, mp_q16, mp_a, mp_s, mp_part, x, xg16, ssp, qkv, att_o, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out,
       prompt, ctl, srv_slot, params, params2, trace, total;
 };
 
@@ -336,13 +336,13 @@ Arena arena_layout(const dec_model_desc& d, int G) {
   if (matrix_prefill(d)) {
     const size_t mc = mp_chunk(d), F = d.d_ffn;
     a.mp_x = take(mc * D * 4);
-    a.mp_h = take(mc * std::max({D, q, F}) * 2);
+    a.mp_h = take(mc * std::max(D, q) * 2);    // normed rows, then the attention output
     a.mp_q16 = take(mc * q * 2);
-    a.mp_c = take(mc * std::max(3 * q, 2 * F) * 4);
+    a.mp_a = take(mc * F * 2);                   // SwiGLU output (written while the gate/up product reads mp_h)
     a.mp_s = take(mc * 4);
     a.mp_part = take(mp_part_floats(d) * 4);
   } else {
-    a.mp_x = a.mp_h = a.mp_q16 = a.mp_c = a.mp_s = a.mp_part = 0;
+    a.mp_x = a.mp_h = a.mp_q16 = a.mp_a = a.mp_s = a.mp_part = 0;
   }
   a.x = take(B * D * 4);
   a.xg16 = take(B * D * 2);
@@ -503,18 +503,23 @@ int launch_matrix_prefill(dec_handle* h, int n) {
   float* x = reinterpret_cast<float*>(b + h->ar.mp_x);
   uint16_t* hb = reinterpret_cast<uint16_t*>(b + h->ar.mp_h);
   uint16_t* q16 = reinterpret_cast<uint16_t*>(b + h->ar.mp_q16);
-  float* cb = reinterpret_cast<float*>(b + h->ar.mp_c);
+  uint16_t* ab = reinterpret_cast<uint16_t*>(b + h->ar.mp_a);
   float* sb = reinterpret_cast<float*>(b + h->ar.mp_s);
   float* part = reinterpret_cast<float*>(b + h->ar.mp_part);
   const size_t part_floats = mp_part_floats(d);
   void* st = h->stream;
-  auto gemm = [&](const uint16_t* A, int lda, const uint16_t* W, float* C, int ldc, const float* s, int M, int N, int K,
-                  int mode) {
+  auto gemm = [&](const uint16_t* A, int lda, const uint16_t* W, int M, int N, int K, const MpEpi& e) {
     MpGemm g;
-    g.A = A; g.lda = lda; g.B = W; g.ldb = K; g.C = C; g.ldc = ldc; g.s = s;
-    g.M = M; g.N = N; g.K = K; g.mode = mode; g.part = part;
+    g.A = A; g.lda = lda; g.B = W; g.ldb = K;
+    g.M = M; g.N = N; g.K = K; g.epi = e; g.part = part;
     mp_plan(M, N, K, part_floats, &g.shape, &g.S, &g.kc);
     return (hipError_t)mp_launch_gemm(g, st);
+  };
+  auto epi = [&](int mode, float* C, int ldc, const float* s) {
+    MpEpi e;
+    std::memset(&e, 0, sizeof e);
+    e.mode = mode; e.C = C; e.ldc = ldc; e.s = s;
+    return e;
   };
   const int mc = mp_chunk(d);
   int m = 0;
@@ -527,21 +532,26 @@ int launch_matrix_prefill(dec_handle* h, int n) {
       const float* g_ffn = g_attn + D;
       uint16_t* kc = P.kv + (size_t)l * 2 * H * head_elems;
       uint16_t* vc = kc + (size_t)H * head_elems;
+      // QKV product; its epilogue rotates q and k, appends k and v to the cache, writes fp16 q
+      MpEpi rope = epi(MP_EP_ROPE, nullptr, 0, sb);
+      rope.H = q16; rope.ldh = q; rope.rope = P.rope; rope.kc = kc; rope.vc = vc; rope.head_elems = head_elems;
+      rope.pos0 = c0; rope.q = q; rope.hd = hd;
       HIPCHK(h, &h->err, (hipError_t)mp_launch_norm(x, g_attn, m, D, d.rms_eps, hb, sb, st));
-      HIPCHK(h, &h->err, gemm(hb, D, W + P.off_qkv, cb, 3 * q, sb, m, 3 * q, D, MP_EP_SCALE));
-      HIPCHK(h, &h->err, (hipError_t)mp_launch_rope_kv(cb, m, q, hd, c0, P.rope, kc, vc, head_elems, q16, st));
+      HIPCHK(h, &h->err, gemm(hb, D, W + P.off_qkv, m, 3 * q, D, rope));
       HIPCHK(h, &h->err, (hipError_t)mp_launch_attention(q16, q, m, c0, H, hd, kc, vc, head_elems, hb, st));
-      HIPCHK(h, &h->err, gemm(hb, q, W + P.off_o, x, D, nullptr, m, D, q, MP_EP_ACCUM));
+      HIPCHK(h, &h->err, gemm(hb, q, W + P.off_o, m, D, q, epi(MP_EP_ACCUM, x, D, nullptr)));
+      // gate/up product; its epilogue writes the fp16 SwiGLU output
+      MpEpi swiglu = epi(MP_EP_SWIGLU, nullptr, 0, sb);
+      swiglu.H = ab; swiglu.ldh = F;
       HIPCHK(h, &h->err, (hipError_t)mp_launch_norm(x, g_ffn, m, D, d.rms_eps, hb, sb, st));
-      HIPCHK(h, &h->err, gemm(hb, D, W + P.off_gu, cb, 2 * F, sb, m, 2 * F, D, MP_EP_SCALE));
-      HIPCHK(h, &h->err, (hipError_t)mp_launch_swiglu(cb, m, F, hb, st));
-      HIPCHK(h, &h->err, gemm(hb, F, W + P.off_d, x, D, nullptr, m, D, F, MP_EP_ACCUM));
+      HIPCHK(h, &h->err, gemm(hb, D, W + P.off_gu, m, 2 * F, D, swiglu));
+      HIPCHK(h, &h->err, gemm(ab, F, W + P.off_d, m, D, F, epi(MP_EP_ACCUM, x, D, nullptr)));
     }
   }
   // the last position's final norm, LM-head row and greedy token
   const float* g_final = P.gains + (size_t)d.n_layers * 2 * D;
   HIPCHK(h, &h->err, (hipError_t)mp_launch_norm(x + (size_t)(m - 1) * D, g_final, 1, D, d.rms_eps, hb, sb, st));
-  HIPCHK(h, &h->err, gemm(hb, D, P.w + P.off_lm, P.logits, V, sb, 1, V, D, MP_EP_SCALE));
+  HIPCHK(h, &h->err, gemm(hb, D, P.w + P.off_lm, 1, V, D, epi(MP_EP_SCALE, P.logits, V, sb)));
   HIPCHK(h, &h->err, (hipError_t)mp_launch_argmax(P.logits, V, P.tok_out + (n - 1), P.tok_cur, st));
   return DEC_OK;
 }

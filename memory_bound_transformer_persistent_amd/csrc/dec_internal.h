@@ -223,7 +223,20 @@ inline uint32_t launch_barriers(int L, int n_tok, int lm_last_only) {
 enum MpEpilogue : int {
   MP_EP_SCALE = 0,   // C = s[m] * (A B^T)  (s may be null: no scale)
   MP_EP_ACCUM = 1,   // C += A B^T
-  MP_EP_PART = 2,    // internal: one K split's partial sums
+  MP_EP_PART = 2,    // internal: one K split's partial sums, [S][M][N]
+  MP_EP_SWIGLU = 3,  // H[m][n/2] = fp16(silu(g) * u), g, u = s[m] (A B^T) at columns n, n+1 (n even)
+  MP_EP_ROPE = 4,    // columns [q | k | v] of s[m] (A B^T): q, k rotated (q also times 1/sqrt(hd)),
+                     // q to H (fp16 [M][ldh]), k and v to the fp16 cache at position pos0 + m
+};
+struct MpEpi {
+  int mode;
+  float* C; int ldc;           // SCALE, ACCUM, PART
+  const float* s;              // row scales (SCALE, SWIGLU, ROPE; null: 1)
+  uint16_t* H; int ldh;        // SWIGLU, ROPE: fp16 output rows
+  const float* rope;           // ROPE: cos/sin table [max_ctx][hd/2][2]
+  uint16_t* kc; uint16_t* vc;  // ROPE: the layer's K and V cache, [H][max_ctx][hd] each
+  size_t head_elems;           // ROPE: max_ctx hd
+  int pos0, q, hd;             // ROPE: position of row 0, H hd, head_dim
 };
 constexpr int kMpShapes = 6;           // tile shapes: 128x128, 128x64 (register-staged), 64x64, 128x64, 64x32 (LDS DMA), 16x64
 constexpr int kMpChunk = 2048;         // prompt positions per pass over the weights
@@ -231,10 +244,8 @@ constexpr size_t kMpPartFloats = size_t(8) << 20;   // split-K partial sums buff
 struct MpGemm {
   const uint16_t* A; int lda;
   const uint16_t* B; int ldb;
-  float* C; int ldc;
-  const float* s;
   int M, N, K;
-  int mode;                  // MP_EP_SCALE or MP_EP_ACCUM
+  MpEpi epi;                 // what becomes of each result (N even for the pair modes)
   int shape, S, kc;          // from mp_plan: tile shape, K splits, K elements per split
   float* part;               // [S][M][N] partial sums when S > 1
 };
@@ -243,11 +254,8 @@ void mp_plan(int M, int N, int K, size_t part_floats, int* shape, int* S, int* k
 int mp_launch_embed(const uint16_t* E, const int* tok, int n, int d, float* x, void* stream);
 int mp_launch_norm(const float* x, const float* g, int n, int d, float eps, uint16_t* h, float* s, void* stream);
 int mp_launch_gemm(const MpGemm& g, void* stream);
-int mp_launch_rope_kv(const float* qkv, int n, int q, int hd, int pos0, const float* rope, uint16_t* kc, uint16_t* vc,
-                      size_t head_elems, uint16_t* q16, void* stream);
 int mp_launch_attention(const uint16_t* q16, int q, int n, int pos0, int H, int hd, const uint16_t* kc,
                         const uint16_t* vc, size_t head_elems, uint16_t* o16, void* stream);
-int mp_launch_swiglu(const float* gu, int n, int F, uint16_t* a, void* stream);
 int mp_launch_argmax(const float* logits, int V, int* tok_out, int* tok_cur, void* stream);
 
 // Launch helpers defined next to the kernel (dec_kernels.hip).  P points to a

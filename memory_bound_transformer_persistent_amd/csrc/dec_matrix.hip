@@ -13,12 +13,12 @@
 // Per layer, for the prompt positions pos0 .. pos0+n-1 with x their fp32
 // residual rows:
 //   h = fp16(x * g_attn), s = 1/rms(x)                        mp_norm
-//   qkv = s * (h Wqkv^T)                                       mp_gemm
-//   rotary on q and k; k, v (fp16) to the KV cache; q fp16      mp_rope_kv
+//   qkv = s * (h Wqkv^T); in its epilogue rotary on q and k,
+//     k, v (fp16) to the KV cache, q (fp16) to q16               mp_gemm (ROPE)
 //   o = causal softmax(q k^T) v over cache positions, fp16      mp_attention
 //   x += o Wo^T                                                 mp_gemm (accumulate)
-//   h = fp16(x * g_ffn), s = 1/rms(x);  gu = s * (h Wgu^T)      mp_norm, mp_gemm
-//   a = fp16(silu(gate) * up)                                   mp_swiglu
+//   h = fp16(x * g_ffn), s = 1/rms(x)                         mp_norm
+//   a = fp16(silu(gate) * up), gate, up = s * (h Wgu^T)        mp_gemm (SWIGLU)
 //   x += a Wd^T                                                 mp_gemm (accumulate)
 // then the final norm of the prompt's last position, its LM-head row and
 // the argmax.  Matrix-product inputs are rounded to fp16 as in the batched
@@ -111,6 +111,71 @@ __global__ __launch_bounds__(256) void mp_norm(const float* __restrict__ x, cons
   if (tid == 0) s[m] = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d + eps);
 }
 
+// Epilogue of one result pair (columns n, n+1; n even) for the pair modes:
+// v0, v1 are the scaled results.
+__device__ __forceinline__ void pair_store(const MpEpi& e, int m, int n, float v0, float v1) {
+  if (e.mode == MP_EP_SWIGLU) {
+    reinterpret_cast<_Float16*>(e.H)[(size_t)m * e.ldh + (n >> 1)] = (_Float16)(v0 / (1.0f + expf(-v0)) * v1);
+    return;
+  }
+  // rotary embedding and cache append: pairs (2i, 2i+1) of a head turn by the
+  // angle in the cos/sin table row of the position
+  const int part = n / e.q, rr = n - part * e.q, h = rr / e.hd, d = rr - h * e.hd, pos = e.pos0 + m;
+  const size_t at = (size_t)h * e.head_elems + (size_t)pos * e.hd + d;
+  if (part == 2) {
+    reinterpret_cast<_Float16*>(e.vc)[at] = (_Float16)v0;
+    reinterpret_cast<_Float16*>(e.vc)[at + 1] = (_Float16)v1;
+    return;
+  }
+  const float* rt = e.rope + (size_t)pos * e.hd + d;
+  const float cs = rt[0], sn = rt[1];
+  const float z0 = __builtin_fmaf(v0, cs, -(v1 * sn)), z1 = __builtin_fmaf(v0, sn, v1 * cs);
+  if (part == 0) {
+    const float qscale = 1.0f / sqrtf((float)e.hd);
+    _Float16* o = reinterpret_cast<_Float16*>(e.H) + (size_t)m * e.ldh + rr;
+    o[0] = (_Float16)(z0 * qscale);
+    o[1] = (_Float16)(z1 * qscale);
+  } else {
+    reinterpret_cast<_Float16*>(e.kc)[at] = (_Float16)z0;
+    reinterpret_cast<_Float16*>(e.kc)[at + 1] = (_Float16)z1;
+  }
+}
+
+// The epilogue of one wave's WM x WN result blocks: element (i, j, r) is row
+// mrow + 16 i + 4 (lane / 16) + r and column ncol + 16 j + lane % 16.  Pair
+// modes take the partner column from the neighbouring lane (every lane
+// shuffles, then the even lanes store).
+template <int WM, int WN>
+__device__ __forceinline__ void wave_epilogue(const MpEpi& e, const f32x4m (&acc)[WM][WN], int mrow, int ncol, int M,
+                                              int N, int lane) {
+  const bool pair = e.mode == MP_EP_SWIGLU || e.mode == MP_EP_ROPE;
+  float* Cz = e.mode == MP_EP_PART ? e.C + (size_t)blockIdx.z * M * N : e.C;
+  const int ldc = e.mode == MP_EP_PART ? N : e.ldc;
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = mrow + 16 * i + (lane >> 4) * 4 + r;
+      const bool mok = m < M;
+      const float sc = (e.mode != MP_EP_ACCUM && e.mode != MP_EP_PART && e.s && mok) ? e.s[m] : 1.0f;
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const int n = ncol + 16 * j + (lane & 15);
+        const float v = acc[i][j][r] * sc;
+        if (pair) {
+          const float w = __shfl_xor(v, 1, 64);
+          if (mok && n < N && !(n & 1)) pair_store(e, m, n, v, w);
+          continue;
+        }
+        if (!mok || n >= N) continue;
+        float* c = Cz + (size_t)m * ldc + n;
+        if (e.mode == MP_EP_ACCUM) *c = *c + v;
+        else *c = v;
+      }
+    }
+  }
+}
+
 // C[M x N] from A [M x K] and B [N x K], both fp16 with K contiguous (row
 // strides lda, ldb; K a multiple of 32): C = A B^T through the epilogue
 // (MpEpilogue).  Four waves per workgroup in a WR x (4/WR) arrangement, each
@@ -124,8 +189,7 @@ __global__ __launch_bounds__(256) void mp_norm(const float* __restrict__ x, cons
 // Split z (blockIdx.z) covers K elements [z kc, min(K, (z+1) kc)).
 template <int WM, int WN, int WR>
 __global__ __launch_bounds__(256) void mp_gemm(const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ B,
-                                               int ldb, float* __restrict__ C, int ldc, const float* __restrict__ s,
-                                               int M, int N, int K, int kc, int mode) {
+                                               int ldb, int M, int N, int K, int kc, MpEpi e) {
   constexpr int WC = 4 / WR;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave / WC, wc = wave % WC;
@@ -171,25 +235,7 @@ __global__ __launch_bounds__(256) void mp_gemm(const uint16_t* __restrict__ A, i
 #pragma unroll
     for (int j = 0; j < WN; ++j) b[j] = bn[j];
   }
-  float* Cz = mode == MP_EP_PART ? C + (size_t)blockIdx.z * M * ldc : C;
-#pragma unroll
-  for (int i = 0; i < WM; ++i) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 16 * i + (lane >> 4) * 4 + r;
-      if (m >= M) continue;
-      const float sc = (mode == MP_EP_SCALE && s) ? s[m] : 1.0f;
-#pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        const int n = n0 + 16 * j + r16;
-        if (n >= N) continue;
-        float* c = Cz + (size_t)m * ldc + n;
-        const float v = acc[i][j][r];
-        if (mode == MP_EP_ACCUM) *c = *c + v;
-        else *c = v * sc;
-      }
-    }
-  }
+  wave_epilogue<WM, WN>(e, acc, m0, n0, M, N, lane);
 }
 
 // One wave's share of K tile t of an LDS-staged product: PER 1 KB operand
@@ -224,9 +270,8 @@ __device__ __forceinline__ void dma_tile(char* lds, int t, int wave, int lane, r
 // that are not stored.
 template <int BM, int BN, int NS>
 __global__ __launch_bounds__(256) void mp_gemm_lds(const uint16_t* __restrict__ A, int lda,
-                                                   const uint16_t* __restrict__ B, int ldb, float* __restrict__ C,
-                                                   int ldc, const float* __restrict__ s, int M, int N, int K, int kc,
-                                                   int mode) {
+                                                   const uint16_t* __restrict__ B, int ldb, int M, int N, int K, int kc,
+                                                   MpEpi e) {
   constexpr int WM = BM / 32, WN = BN / 32;          // 16 x 16 blocks per wave
   constexpr int ABLK = BM / 16 * 2, BBLK = BN / 16 * 2;
   constexpr int NBLK = ABLK + BBLK, PER = NBLK / 4;  // DMA blocks per tile, per wave
@@ -292,40 +337,23 @@ __global__ __launch_bounds__(256) void mp_gemm_lds(const uint16_t* __restrict__ 
         for (int j = 0; j < WN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   }
-  float* Cz = mode == MP_EP_PART ? C + (size_t)blockIdx.z * M * ldc : C;
-#pragma unroll
-  for (int i = 0; i < WM; ++i) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = mb + (wr * WM + i) * 16 + (lane >> 4) * 4 + r;
-      if (m >= M) continue;
-      const float sc = (mode == MP_EP_SCALE && s) ? s[m] : 1.0f;
-#pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        const int n = nb + (wc * WN + j) * 16 + (lane & 15);
-        if (n >= N) continue;
-        float* c = Cz + (size_t)m * ldc + n;
-        const float v = acc[i][j][r];
-        if (mode == MP_EP_ACCUM) *c = *c + v;
-        else *c = v * sc;
-      }
-    }
-  }
+  wave_epilogue<WM, WN>(e, acc, mb + wr * WM * 16, nb + wc * WN * 16, M, N, lane);
 }
 
 // The same LDS operand-block layout, staged through registers instead of LDS
-// DMA: each thread loads its 16-byte pieces of K tile t+1 into registers
-// while the tile t products run, then writes them to the other of two LDS
-// stages.  On gfx950 this runs faster than the DMA form for the large tiles
-// (the plain ds_write_b128 path drains faster than 16-byte LDS DMA), while the
-// DMA form's deeper pipelines suit the few-row, weight-streaming products.
-template <int BM, int BN>
-__global__ __launch_bounds__(256) void mp_gemm_rs(const uint16_t* __restrict__ A, int lda,
-                                                  const uint16_t* __restrict__ B, int ldb, float* __restrict__ C,
-                                                  int ldc, const float* __restrict__ s, int M, int N, int K, int kc,
-                                                  int mode) {
+// DMA: each thread loads its 16-byte pieces of K tile t+1 (32 KS wide) into
+// registers while the tile t products run, then writes them to the other of
+// two LDS stages.  For the large tiles this measured faster on MI355X than
+// the DMA form, best with 32-wide K tiles and three workgroups per compute
+// unit (KS = 1, OCC = 3); the DMA form's deeper pipelines suit the few-row,
+// weight-streaming products.
+template <int BM, int BN, int KS = 2, int OCC = 1>
+__global__ __launch_bounds__(256, OCC) void mp_gemm_rs(const uint16_t* __restrict__ A, int lda,
+                                                       const uint16_t* __restrict__ B, int ldb, int M, int N, int K,
+                                                       int kc, MpEpi e) {
   constexpr int WM = BM / 32, WN = BN / 32;
-  constexpr int ABLK = BM / 16 * 2, BBLK = BN / 16 * 2;
+  constexpr int KT = 32 * KS;                         // K elements per tile
+  constexpr int ABLK = BM / 16 * KS, BBLK = BN / 16 * KS;
   constexpr int NBLK = ABLK + BBLK, PER = NBLK / 4, STAGE = NBLK * 1024;
   static_assert(NBLK % 4 == 0, "blocks split evenly over the waves");
   extern __shared__ __attribute__((aligned(1024))) char lds[];
@@ -333,7 +361,7 @@ __global__ __launch_bounds__(256) void mp_gemm_rs(const uint16_t* __restrict__ A
   const int wr = wave >> 1, wc = wave & 1;
   const int mb = blockIdx.y * BM, nb = blockIdx.x * BN;
   const int kb = blockIdx.z * kc, ke = min(K, kb + kc);
-  const int ntiles = (ke - kb + 63) / 64;
+  const int ntiles = (ke - kb + KT - 1) / KT;
   const rsrc ra = make_res(A, (uint64_t)M * lda * 2), rb = make_res(B, (uint64_t)N * ldb * 2);
   uint32_t roff[PER];
   int kst[PER];
@@ -343,8 +371,8 @@ __global__ __launch_bounds__(256) void mp_gemm_rs(const uint16_t* __restrict__ A
     const int b = wave + 4 * j;
     isa[j] = b < ABLK;
     const int bb = isa[j] ? b : b - ABLK;
-    kst[j] = bb & 1;
-    const int row = (isa[j] ? mb : nb) + (bb >> 1) * 16 + (lane & 15);
+    kst[j] = bb % KS;
+    const int row = (isa[j] ? mb : nb) + (bb / KS) * 16 + (lane & 15);
     const int lim = isa[j] ? M : N;
     const int ld = isa[j] ? lda : ldb;
     roff[j] = row < lim ? (uint32_t)((size_t)row * ld + kb + (lane >> 4) * 8) * 2u : kOutOfRange;
@@ -368,7 +396,7 @@ __global__ __launch_bounds__(256) void mp_gemm_rs(const uint16_t* __restrict__ A
     if (next) {
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
-        const int k0 = (t + 1) * 64 + kst[j] * 32;
+        const int k0 = (t + 1) * KT + kst[j] * 32;
         reg[j] = ld8(isa[j] ? ra : rb,
                      (roff[j] != kOutOfRange && kb + k0 < ke) ? roff[j] + (uint32_t)k0 * 2u : kOutOfRange);
       }
@@ -376,15 +404,15 @@ __global__ __launch_bounds__(256) void mp_gemm_rs(const uint16_t* __restrict__ A
     const char* as = lds + (t & 1) * STAGE;
     const char* bs = as + ABLK * 1024;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (kb + t * 64 + ks * 32 >= ke) break;
+    for (int ks = 0; ks < KS; ++ks) {
+      if (kb + t * KT + ks * 32 >= ke) break;
       f16x8 a[WM], b[WN];
 #pragma unroll
       for (int i = 0; i < WM; ++i)
-        a[i] = *reinterpret_cast<const f16x8*>(as + ((wr * WM + i) * 2 + ks) * 1024 + 16 * lane);
+        a[i] = *reinterpret_cast<const f16x8*>(as + ((wr * WM + i) * KS + ks) * 1024 + 16 * lane);
 #pragma unroll
       for (int j = 0; j < WN; ++j)
-        b[j] = *reinterpret_cast<const f16x8*>(bs + ((wc * WN + j) * 2 + ks) * 1024 + 16 * lane);
+        b[j] = *reinterpret_cast<const f16x8*>(bs + ((wc * WN + j) * KS + ks) * 1024 + 16 * lane);
 #pragma unroll
       for (int i = 0; i < WM; ++i)
 #pragma unroll
@@ -397,76 +425,31 @@ __global__ __launch_bounds__(256) void mp_gemm_rs(const uint16_t* __restrict__ A
     }
     __syncthreads();   // tile t+1 is in LDS; tile t's stage may be overwritten
   }
-  float* Cz = mode == MP_EP_PART ? C + (size_t)blockIdx.z * M * ldc : C;
-#pragma unroll
-  for (int i = 0; i < WM; ++i) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = mb + (wr * WM + i) * 16 + (lane >> 4) * 4 + r;
-      if (m >= M) continue;
-      const float sc = (mode == MP_EP_SCALE && s) ? s[m] : 1.0f;
-#pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        const int n = nb + (wc * WN + j) * 16 + (lane & 15);
-        if (n >= N) continue;
-        float* c = Cz + (size_t)m * ldc + n;
-        const float v = acc[i][j][r];
-        if (mode == MP_EP_ACCUM) *c = *c + v;
-        else *c = v * sc;
-      }
-    }
-  }
+  wave_epilogue<WM, WN>(e, acc, mb + wr * WM * 16, nb + wc * WN * 16, M, N, lane);
 }
 
 // The epilogue of a split-K product: the S partial slices [S][M][N] added in
-// slice order, then scaled by s[m] (MP_EP_SCALE) or added to C (MP_EP_ACCUM).
-__global__ __launch_bounds__(256) void mp_splitk_sum(const float* __restrict__ part, int S, int M, int N,
-                                                     float* __restrict__ C, int ldc, const float* __restrict__ s,
-                                                     int mode) {
+// slice order, then through the product's epilogue (one thread per result,
+// or per column pair in the pair modes).
+__global__ __launch_bounds__(256) void mp_splitk_sum(const float* __restrict__ part, int S, int M, int N, MpEpi e) {
+  const bool pair = e.mode == MP_EP_SWIGLU || e.mode == MP_EP_ROPE;
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (size_t)M * N) return;
-  const int m = (int)(i / N), n = (int)(i - (size_t)m * N);
-  float v = part[i];
-  for (int z = 1; z < S; ++z) v += part[(size_t)z * M * N + i];
-  float* c = C + (size_t)m * ldc + n;
-  if (mode == MP_EP_ACCUM) *c = *c + v;
-  else *c = v * (s ? s[m] : 1.0f);
-}
-
-// Rotary embedding and cache append for positions pos0 .. pos0+n-1 of one
-// layer: qkv [n x 3q] (fp32); q rotated and scaled by 1/sqrt(hd) to q16
-// [n x q] (fp16); k rotated, and v as it is, to the fp16 KV cache
-// ([H][max_ctx][hd], head_elems = max_ctx hd apart).  Pairs (2i, 2i+1) of a
-// head turn by the angle in the cos/sin table row of the position.
-__global__ __launch_bounds__(256) void mp_rope_kv(const float* __restrict__ qkv, int q, int hd, int pos0,
-                                                  const float* __restrict__ rope, uint16_t* __restrict__ kc,
-                                                  uint16_t* __restrict__ vc, size_t head_elems,
-                                                  uint16_t* __restrict__ q16) {
-  const int m = blockIdx.x, pos = pos0 + m;
-  const float* row = qkv + (size_t)m * 3 * q;
-  const float qscale = 1.0f / sqrtf((float)hd);
-  const float* rt = rope + (size_t)pos * hd;
-  for (int p = threadIdx.x; p < 3 * q / 2; p += 256) {
-    const int r = 2 * p, part = r / q, rr = r - part * q, h = rr / hd, i = (rr - h * hd) >> 1;
-    const float y0 = row[r], y1 = row[r + 1];
-    if (part == 2) {
-      _Float16* v = reinterpret_cast<_Float16*>(vc) + (size_t)h * head_elems + (size_t)pos * hd + 2 * i;
-      v[0] = (_Float16)y0;
-      v[1] = (_Float16)y1;
-      continue;
-    }
-    const float cs = rt[2 * i], sn = rt[2 * i + 1];
-    const float z0 = __builtin_fmaf(y0, cs, -(y1 * sn)), z1 = __builtin_fmaf(y0, sn, y1 * cs);
-    if (part == 0) {
-      _Float16* o = reinterpret_cast<_Float16*>(q16) + (size_t)m * q + rr;
-      o[0] = (_Float16)(z0 * qscale);
-      o[1] = (_Float16)(z1 * qscale);
-    } else {
-      _Float16* k = reinterpret_cast<_Float16*>(kc) + (size_t)h * head_elems + (size_t)pos * hd + 2 * i;
-      k[0] = (_Float16)z0;
-      k[1] = (_Float16)z1;
-    }
+  const size_t cols = pair ? (size_t)N / 2 : (size_t)N;
+  if (i >= (size_t)M * cols) return;
+  const int m = (int)(i / cols), n = (int)(i - (size_t)m * cols) * (pair ? 2 : 1);
+  const size_t at = (size_t)m * N + n;
+  float v0 = part[at], v1 = pair ? part[at + 1] : 0.f;
+  for (int z = 1; z < S; ++z) {
+    v0 += part[(size_t)z * M * N + at];
+    if (pair) v1 += part[(size_t)z * M * N + at + 1];
   }
+  if (e.mode == MP_EP_ACCUM) {
+    e.C[(size_t)m * e.ldc + n] += v0;
+    return;
+  }
+  const float sc = e.s ? e.s[m] : 1.0f;
+  if (pair) pair_store(e, m, n, v0 * sc, v1 * sc);
+  else e.C[(size_t)m * e.ldc + n] = v0 * sc;
 }
 
 // DT consecutive fp16 values (DT = 2, 4 or 8) through a buffer descriptor.
@@ -602,18 +585,6 @@ __global__ __launch_bounds__(256) void mp_attention(const uint16_t* __restrict__
   }
 }
 
-// a[m][i] = fp16(silu(gu[m][2i]) * gu[m][2i+1]): gate and up rows are
-// interleaved in the packed weights, so they are adjacent columns here.
-__global__ __launch_bounds__(256) void mp_swiglu(const float* __restrict__ gu, int F, uint16_t* __restrict__ a) {
-  const int m = blockIdx.x;
-  const float* r = gu + (size_t)m * 2 * F;
-  _Float16* o = reinterpret_cast<_Float16*>(a) + (size_t)m * F;
-  for (int i = threadIdx.x; i < F; i += 256) {
-    const float g = r[2 * i], u = r[2 * i + 1];
-    o[i] = (_Float16)(g / (1.0f + expf(-g)) * u);
-  }
-}
-
 // The greedy token of one logits row (lowest index on ties): one workgroup,
 // each thread over a strided share in index order, then a fixed-order tree.
 __global__ __launch_bounds__(1024) void mp_argmax(const float* __restrict__ logits, int V, int* __restrict__ tok_out,
@@ -666,34 +637,32 @@ hipError_t prepare_lds() {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&mp_gemm_lds<BM, BN, NS>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes<BM, BN, NS>());
 }
+// register-staged tiles: 32-wide K tiles in two LDS stages, three workgroups per compute unit
+template <int BM, int BN>
+constexpr int rs_lds_bytes() { return 2 * (BM / 16 + BN / 16) * 1024; }
 template <int BM, int BN>
 hipError_t prepare_rs() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&mp_gemm_rs<BM, BN>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes<BM, BN, 2>());
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&mp_gemm_rs<BM, BN, 1, 3>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, rs_lds_bytes<BM, BN>());
 }
 
 template <int BM, int BN, int NS>
-void gemm_lds_as(const MpGemm& g, dim3 grid, hipStream_t st) {
-  const bool split = g.S > 1;
+void gemm_lds_as(const MpGemm& g, const MpEpi& e, dim3 grid, hipStream_t st) {
   constexpr int lds = lds_bytes<BM, BN, NS>();
-  hipLaunchKernelGGL((mp_gemm_lds<BM, BN, NS>), grid, dim3(256), lds, st, g.A, g.lda, g.B, g.ldb,
-                     split ? g.part : g.C, split ? g.N : g.ldc, g.s, g.M, g.N, g.K, g.kc,
-                     split ? (int)MP_EP_PART : g.mode);
+  hipLaunchKernelGGL((mp_gemm_lds<BM, BN, NS>), grid, dim3(256), lds, st, g.A, g.lda, g.B, g.ldb, g.M, g.N, g.K,
+                     g.kc, e);
 }
 
 template <int BM, int BN>
-void gemm_rs_as(const MpGemm& g, dim3 grid, hipStream_t st) {
-  const bool split = g.S > 1;
-  constexpr int lds = lds_bytes<BM, BN, 2>();
-  hipLaunchKernelGGL((mp_gemm_rs<BM, BN>), grid, dim3(256), lds, st, g.A, g.lda, g.B, g.ldb, split ? g.part : g.C,
-                     split ? g.N : g.ldc, g.s, g.M, g.N, g.K, g.kc, split ? (int)MP_EP_PART : g.mode);
+void gemm_rs_as(const MpGemm& g, const MpEpi& e, dim3 grid, hipStream_t st) {
+  constexpr int lds = rs_lds_bytes<BM, BN>();
+  hipLaunchKernelGGL((mp_gemm_rs<BM, BN, 1, 3>), grid, dim3(256), lds, st, g.A, g.lda, g.B, g.ldb, g.M, g.N, g.K,
+                     g.kc, e);
 }
 
 template <int WM, int WN, int WR>
-void gemm_as(const MpGemm& g, dim3 grid, hipStream_t st) {
-  const bool split = g.S > 1;
-  hipLaunchKernelGGL((mp_gemm<WM, WN, WR>), grid, dim3(256), 0, st, g.A, g.lda, g.B, g.ldb, split ? g.part : g.C,
-                     split ? g.N : g.ldc, g.s, g.M, g.N, g.K, g.kc, split ? (int)MP_EP_PART : g.mode);
+void gemm_as(const MpGemm& g, const MpEpi& e, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((mp_gemm<WM, WN, WR>), grid, dim3(256), 0, st, g.A, g.lda, g.B, g.ldb, g.M, g.N, g.K, g.kc, e);
 }
 
 }  // namespace
@@ -741,31 +710,33 @@ int mp_launch_norm(const float* x, const float* g, int n, int d, float eps, uint
   return (int)hipGetLastError();
 }
 int mp_launch_gemm(const MpGemm& g, void* stream) {
+  const bool pair = g.epi.mode == MP_EP_SWIGLU || g.epi.mode == MP_EP_ROPE;
   if (g.K < 32 || g.K % 32 || g.M < 1 || g.N < 1 || g.shape < 0 || g.shape >= kMpShapes || g.S < 1 || g.kc < 32 ||
-      g.kc % 32 || (long long)g.S * g.kc < g.K || (long long)(g.S - 1) * g.kc >= g.K || (g.S > 1 && !g.part))
+      g.kc % 32 || (long long)g.S * g.kc < g.K || (long long)(g.S - 1) * g.kc >= g.K || (g.S > 1 && !g.part) ||
+      g.epi.mode < MP_EP_SCALE || g.epi.mode > MP_EP_ROPE || g.epi.mode == MP_EP_PART || (pair && g.N % 2) ||
+      (g.epi.mode == MP_EP_ROPE && (g.N != 3 * g.epi.q || g.epi.q % g.epi.hd || g.epi.hd % 2)))
     return (int)hipErrorInvalidValue;
   const dim3 grid((g.N + kShapeBN[g.shape] - 1) / kShapeBN[g.shape], (g.M + kShapeBM[g.shape] - 1) / kShapeBM[g.shape],
                   g.S);
   const hipStream_t st = (hipStream_t)stream;
-  switch (g.shape) {
-    case 0: gemm_rs_as<128, 128>(g, grid, st); break;
-    case 1: gemm_rs_as<128, 64>(g, grid, st); break;
-    case 2: gemm_lds_as<64, 64, 4>(g, grid, st); break;
-    case 3: gemm_lds_as<128, 64, 4>(g, grid, st); break;
-    case 4: gemm_lds_as<64, 32, 4>(g, grid, st); break;
-    default: gemm_as<1, 1, 1>(g, grid, st); break;
+  MpEpi e = g.epi;
+  if (g.S > 1) {   // the product writes its partial sums; the sum kernel applies the epilogue
+    e.mode = MP_EP_PART;
+    e.C = g.part;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || g.S == 1) return (int)e;
-  const size_t total = (size_t)g.M * g.N;
+  switch (g.shape) {
+    case 0: gemm_rs_as<128, 128>(g, e, grid, st); break;
+    case 1: gemm_rs_as<128, 64>(g, e, grid, st); break;
+    case 2: gemm_lds_as<64, 64, 4>(g, e, grid, st); break;
+    case 3: gemm_lds_as<128, 64, 4>(g, e, grid, st); break;
+    case 4: gemm_lds_as<64, 32, 4>(g, e, grid, st); break;
+    default: gemm_as<1, 1, 1>(g, e, grid, st); break;
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || g.S == 1) return (int)err;
+  const size_t total = (size_t)g.M * (pair ? g.N / 2 : g.N);
   hipLaunchKernelGGL(mp_splitk_sum, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, g.part, g.S, g.M, g.N,
-                     g.C, g.ldc, g.s, g.mode);
-  return (int)hipGetLastError();
-}
-int mp_launch_rope_kv(const float* qkv, int n, int q, int hd, int pos0, const float* rope, uint16_t* kc, uint16_t* vc,
-                      size_t head_elems, uint16_t* q16, void* stream) {
-  hipLaunchKernelGGL(mp_rope_kv, dim3(n), dim3(256), 0, (hipStream_t)stream, qkv, q, hd, pos0, rope, kc, vc,
-                     head_elems, q16);
+                     g.epi);
   return (int)hipGetLastError();
 }
 int mp_launch_attention(const uint16_t* q16, int q, int n, int pos0, int H, int hd, const uint16_t* kc,
@@ -778,10 +749,6 @@ int mp_launch_attention(const uint16_t* q16, int q, int n, int pos0, int H, int 
     case 128: hipLaunchKernelGGL(mp_attention<128>, grid, dim3(256), 0, st, q16, q, n, pos0, kc, vc, head_elems, o16); break;
     default: return (int)hipErrorInvalidValue;
   }
-  return (int)hipGetLastError();
-}
-int mp_launch_swiglu(const float* gu, int n, int F, uint16_t* a, void* stream) {
-  hipLaunchKernelGGL(mp_swiglu, dim3(n), dim3(256), 0, (hipStream_t)stream, gu, F, a);
   return (int)hipGetLastError();
 }
 int mp_launch_argmax(const float* logits, int V, int* tok_out, int* tok_cur, void* stream) {

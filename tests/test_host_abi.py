@@ -98,9 +98,9 @@ def test_matrix_prefill_flag_rules(lib):
     plain = B.arena_bytes(B.ModelDesc.from_shape(d2))
     withf = B.arena_bytes(B.ModelDesc.from_shape(d2, flags=f))
     # workspace for 2048 positions (per position: fp32 residual 10 KB, fp16 product input
-    # 13.8 KB, fp16 q 5 KB, fp32 product 55.3 KB, one scale), about 172 MB, plus 32 MB of
+    # 5 KB, fp16 q 5 KB, fp16 SwiGLU output 13.8 KB, one scale), about 70 MB, plus 32 MB of
     # split-K partial sums
-    per_pos = 4 * 2560 + 2 * 6912 + 2 * 2560 + 4 * 13824 + 4
+    per_pos = 4 * 2560 + 2 * 2560 + 2 * 2560 + 2 * 6912 + 4
     assert 2048 * per_pos + 32 * 2**20 <= withf - plain < 2048 * per_pos + 32 * 2**20 + 4096
 
 
