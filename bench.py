@@ -214,6 +214,37 @@ def extra_workload(B, R, torch, name, full_tensors, stream, warmup, serve):
         r.close()
 
 
+def measure_ttft(B, R, torch, synth, w, tensors, stream):
+    """Time to first token of the workload's prompt through every prefill path,
+    and of the 3968-token prompt through the two matrix-core paths."""
+    def ttft_ms(wl, fl, reps):
+        rt = Run(B, R, torch, wl, tensors, stream, flags=fl)
+        rt.warm(0)
+        times = []
+        for _ in range(reps):
+            times.append(rt.prefill_ms())
+            rt.dec.reset()
+        rt.close()
+        return min(times)
+    ttft = {"tokens": w.prompt_len}
+    for key, fl in (("one_position_per_step_ms", 0), ("batched_8_per_step_ms", B.DEC_FLAG_BATCHED_PREFILL),
+                    ("matrix_ms", B.DEC_FLAG_MATRIX_PREFILL)):
+        ttft[key] = round(ttft_ms(w, fl, 3), 3)
+    wl = synth.workload("dense2b_long")
+    long_mp = ttft_ms(wl, B.DEC_FLAG_MATRIX_PREFILL, 3)
+    fl_long = R.prefill_flops(wl.shape, wl.prompt_len)
+    achieved_tf = fl_long / (long_mp / 1e3) / 1e12
+    ttft["long"] = {"tokens": wl.prompt_len, "matrix_ms": round(long_mp, 2),
+                    "batched_8_per_step_ms": round(ttft_ms(wl, B.DEC_FLAG_BATCHED_PREFILL, 1), 1),
+                    "roofline": {"bound": "mfma", "achieved": round(achieved_tf, 1),
+                                 "peak": R.MI355X_FP16_PEAK / 1e12, "unit": "TFLOP/s",
+                                 "frac": round(achieved_tf * 1e12 / R.MI355X_FP16_PEAK, 4),
+                                 "flops": fl_long, "kernels": "whole prefill (products, attention, "
+                                                              "norms, rotary, SwiGLU, LM row)"}}
+    ttft["matrix_tflops_128"] = round(R.prefill_flops(w.shape, w.prompt_len) / (ttft["matrix_ms"] / 1e3) / 1e12, 1)
+    return ttft
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,6 +261,8 @@ def main():
     ap.add_argument("--multilaunch", action="store_true", help="one kernel launch per phase (comparison)")
     ap.add_argument("--batched-prefill", action="store_true",
                     help="main line: prefill 8 positions per step on the matrix-core kernel; decode is unchanged")
+    ap.add_argument("--ttft-only", action="store_true",
+                    help="only the time-to-first-token measurements of dense2b (prefill profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run plain device-to-device copies of BYTES (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -271,6 +304,11 @@ def main():
     print(f"# weights generated in {time.time() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.Stream(device=0)
+    if args.ttft_only:
+        if w.name != "dense2b":
+            sys.exit("--ttft-only measures the dense2b prompts")
+        print(json.dumps({"ttft": measure_ttft(B, R, torch, synth, w, tensors, stream)}), flush=True)
+        return
     bp = args.batched_prefill and w.batch == 1
     flags = B.DEC_FLAG_BATCHED_PREFILL if bp else 0
     if args.mode == "serve" and args.multilaunch:
@@ -351,34 +389,7 @@ def main():
                            "launches": 1}
     r.close()
     if w.name == "dense2b" and not args.no_extras and not args.multilaunch:
-        # time to first token of the 128-token prompt, every prefill path, and
-        # of the 3968-token prompt through the two matrix-core paths
-        def ttft_ms(wl, fl, reps):
-            rt = Run(B, R, torch, wl, tensors, stream, flags=fl)
-            rt.warm(0)
-            times = []
-            for _ in range(reps):
-                times.append(rt.prefill_ms())
-                rt.dec.reset()
-            rt.close()
-            return min(times)
-        ttft = {"tokens": w.prompt_len}
-        for key, fl in (("one_position_per_step_ms", 0), ("batched_8_per_step_ms", B.DEC_FLAG_BATCHED_PREFILL),
-                        ("matrix_ms", B.DEC_FLAG_MATRIX_PREFILL)):
-            ttft[key] = round(ttft_ms(w, fl, 3), 3)
-        wl = synth.workload("dense2b_long")
-        long_mp = ttft_ms(wl, B.DEC_FLAG_MATRIX_PREFILL, 3)
-        fl_long = R.prefill_flops(wl.shape, wl.prompt_len)
-        achieved_tf = fl_long / (long_mp / 1e3) / 1e12
-        ttft["long"] = {"tokens": wl.prompt_len, "matrix_ms": round(long_mp, 2),
-                        "batched_8_per_step_ms": round(ttft_ms(wl, B.DEC_FLAG_BATCHED_PREFILL, 1), 1),
-                        "roofline": {"bound": "mfma", "achieved": round(achieved_tf, 1),
-                                     "peak": R.MI355X_FP16_PEAK / 1e12, "unit": "TFLOP/s",
-                                     "frac": round(achieved_tf * 1e12 / R.MI355X_FP16_PEAK, 4),
-                                     "flops": fl_long, "kernels": "whole prefill (products, attention, "
-                                                                  "norms, rotary, SwiGLU, LM row)"}}
-        ttft["matrix_tflops_128"] = round(R.prefill_flops(s, w.prompt_len) / (ttft["matrix_ms"] / 1e3) / 1e12, 1)
-        out["ttft"] = ttft
+        out["ttft"] = measure_ttft(B, R, torch, synth, w, tensors, stream)
         out["workloads"] = {}
         for name in EXTRAS:
             print(f"# measuring {name}", file=sys.stderr, flush=True)
