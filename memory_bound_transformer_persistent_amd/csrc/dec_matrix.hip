@@ -428,6 +428,141 @@ __global__ __launch_bounds__(256, OCC) void mp_gemm_rs(const uint16_t* __restric
   wave_epilogue<WM, WN>(e, acc, mb + wr * WM * 16, nb + wc * WN * 16, M, N, lane);
 }
 
+typedef float f32x16m __attribute__((ext_vector_type(16)));
+
+// The epilogue of one v_mfma_f32_32x32x16_f16 result block: element x is row
+// mrow + 8 (x / 4) + 4 (lane / 32) + x % 4 and column ncol + lane % 32.  (One
+// block per call keeps every index of the accumulators constant after
+// unrolling, so they stay in registers.)
+__device__ __forceinline__ void block_epilogue32(const MpEpi& e, float* Cz, int ldc, f32x16m v16, int mrow, int ncol,
+                                                 int M, int N, int lane) {
+  const bool pair = e.mode == MP_EP_SWIGLU || e.mode == MP_EP_ROPE;
+  const int n = ncol + (lane & 31);
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    const int m = mrow + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
+    const bool mok = m < M;
+    const float sc = (e.mode != MP_EP_ACCUM && e.mode != MP_EP_PART && e.s && mok) ? e.s[m] : 1.0f;
+    const float v = v16[x] * sc;
+    if (pair) {
+      const float w = __shfl_xor(v, 1, 64);
+      if (mok && n < N && !(n & 1)) pair_store(e, m, n, v, w);
+      continue;
+    }
+    if (!mok || n >= N) continue;
+    float* c = Cz + (size_t)m * ldc + n;
+    if (e.mode == MP_EP_ACCUM) *c = *c + v;
+    else *c = v;
+  }
+}
+
+// Every block of a wave's WM x WN accumulators, block I = i WN + j by
+// compile-time recursion (plain loops here were left rolled by the compiler,
+// which then kept the accumulators in scratch memory).
+template <int I, int WM, int WN>
+__device__ __forceinline__ void epilogue_blocks32(const MpEpi& e, float* Cz, int ldc, const f32x16m (&acc)[WM][WN],
+                                                  int mrow, int ncol, int M, int N, int lane) {
+  if constexpr (I < WM * WN) {
+    block_epilogue32(e, Cz, ldc, acc[I / WN][I % WN], mrow + 32 * (I / WN), ncol + 32 * (I % WN), M, N, lane);
+    epilogue_blocks32<I + 1, WM, WN>(e, Cz, ldc, acc, mrow, ncol, M, N, lane);
+  }
+}
+
+// Large products: 256 x 128 tiles, four waves of 128 x 64 computed with
+// v_mfma_f32_32x32x16_f16 (4 x 2 blocks of 32 x 32 per wave), 32-wide K tiles
+// staged through registers into two LDS stages.  In LDS a 1 KB block holds
+// rows 32 r .. +31 and one 16-wide K step: lane l's 16 bytes at 16 l are row
+// l % 32, K elements 8 (l / 32) .. +7, the instruction's operand layout.  The
+// global loads take each row's 64 bytes of a K tile as four 16-byte pieces;
+// thread t loads piece (t / 16) % 4 of row t % 16 + 16 (t / 64) (+ 64 i), so
+// the 16 lanes of each LDS write phase land on 16 consecutive rows of one
+// block: no bank conflicts.  The larger wave tile reads 24 bytes of LDS per
+// thousand flops against 32 for the 64 x 64 wave tile.
+template <int OCC>
+__global__ __launch_bounds__(256, OCC) void mp_gemm_big(const uint16_t* __restrict__ A, int lda,
+                                                        const uint16_t* __restrict__ B, int ldb, int M, int N, int K,
+                                                        int kc, MpEpi e) {
+  constexpr int BM = 256, BN = 128, WM = 4, WN = 2;
+  constexpr int ABLK = BM / 32 * 2, BBLK = BN / 32 * 2, STAGE = (ABLK + BBLK) * 1024;
+  constexpr int LA = BM / 64, LB = BN / 64;   // 16-byte global loads per thread per K tile
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int mb = blockIdx.y * BM, nb = blockIdx.x * BN;
+  const int kb = blockIdx.z * kc, ke = min(K, kb + kc);
+  const int ntiles = (ke - kb) / 32;   // K, kc and so ke - kb are multiples of 32
+  const rsrc ra = make_res(A, (uint64_t)M * lda * 2), rb = make_res(B, (uint64_t)N * ldb * 2);
+  const int t = threadIdx.x, r0 = (t & 15) + 16 * (t >> 6), pc = (t >> 4) & 3;
+  uint32_t aoff[LA], boff[LB];
+  int aw[LA], bw[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int r = r0 + 64 * i, row = mb + r;
+    aoff[i] = row < M ? (uint32_t)((size_t)row * lda + kb + 8 * pc) * 2u : kOutOfRange;
+    aw[i] = ((r >> 5) * 2 + (pc >> 1)) * 1024 + ((r & 31) + 32 * (pc & 1)) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int r = r0 + 64 * i, row = nb + r;
+    boff[i] = row < N ? (uint32_t)((size_t)row * ldb + kb + 8 * pc) * 2u : kOutOfRange;
+    bw[i] = ABLK * 1024 + ((r >> 5) * 2 + (pc >> 1)) * 1024 + ((r & 31) + 32 * (pc & 1)) * 16;
+  }
+  f16x8 ga[LA], gb[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) ga[i] = ld8(ra, aoff[i]);
+#pragma unroll
+  for (int i = 0; i < LB; ++i) gb[i] = ld8(rb, boff[i]);
+#pragma unroll
+  for (int i = 0; i < LA; ++i) *reinterpret_cast<f16x8*>(lds + aw[i]) = ga[i];
+#pragma unroll
+  for (int i = 0; i < LB; ++i) *reinterpret_cast<f16x8*>(lds + bw[i]) = gb[i];
+  __syncthreads();
+  f32x16m acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) acc[i][j][x] = 0.f;
+  for (int tt = 0; tt < ntiles; ++tt) {
+    const bool next = tt + 1 < ntiles;
+    if (next) {
+      const uint32_t step = (uint32_t)(tt + 1) * 64u;   // 32 halves per K tile
+#pragma unroll
+      for (int i = 0; i < LA; ++i) ga[i] = ld8(ra, aoff[i] != kOutOfRange ? aoff[i] + step : kOutOfRange);
+#pragma unroll
+      for (int i = 0; i < LB; ++i) gb[i] = ld8(rb, boff[i] != kOutOfRange ? boff[i] + step : kOutOfRange);
+    }
+    const char* as = lds + (tt & 1) * STAGE;
+    const char* bs = as + ABLK * 1024;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      f16x8 a[WM], b[WN];
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+        a[i] = *reinterpret_cast<const f16x8*>(as + ((wr * WM + i) * 2 + ks) * 1024 + 16 * lane);
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+        b[j] = *reinterpret_cast<const f16x8*>(bs + ((wc * WN + j) * 2 + ks) * 1024 + 16 * lane);
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (next) {
+      char* st = lds + ((tt + 1) & 1) * STAGE;
+#pragma unroll
+      for (int i = 0; i < LA; ++i) *reinterpret_cast<f16x8*>(st + aw[i]) = ga[i];
+#pragma unroll
+      for (int i = 0; i < LB; ++i) *reinterpret_cast<f16x8*>(st + bw[i]) = gb[i];
+    }
+    __syncthreads();   // tile tt+1 is in LDS; tile tt's stage may be overwritten
+  }
+  float* Cz = e.mode == MP_EP_PART ? e.C + (size_t)blockIdx.z * M * N : e.C;
+  const int ldc = e.mode == MP_EP_PART ? N : e.ldc;
+  epilogue_blocks32<0, WM, WN>(e, Cz, ldc, acc, mb + wr * 128, nb + wc * 64, M, N, lane);
+}
+
 // The epilogue of a split-K product: the S partial slices [S][M][N] added in
 // slice order, then through the product's epilogue (one thread per result,
 // or per column pair in the pair modes).
@@ -493,15 +628,16 @@ struct HalfRow<2> {
 //   dims c HD/16 + t for c = 0..15.
 // Lane l then holds HD/16 consecutive dims per result row: o = o / sum, fp16,
 // to o16 [n x q].  Query blocks run heaviest (latest) first.
-template <int HD>
-__global__ __launch_bounds__(256) void mp_attention(const uint16_t* __restrict__ q16, int q, int n, int pos0,
+template <int HD, int QG>
+__global__ __launch_bounds__(256, 2) void mp_attention(const uint16_t* __restrict__ q16, int q, int n, int pos0,
                                                     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
                                                     size_t head_elems, uint16_t* __restrict__ o16) {
-  constexpr int DT = HD / 16;   // dims per lane per output row; output blocks of 16 dims
+  constexpr int DT = HD / 16;        // dims per lane per output row; output blocks of 16 dims
+  constexpr int WQ = 16 * QG;        // queries per wave: QG groups of 16 share every K/V load
   typedef HalfRow<DT> Row;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = blockIdx.y, nqb = (n + 63) / 64;
-  const int m0 = (nqb - 1 - (int)blockIdx.x) * 64 + wave * 16;
+  const int h = blockIdx.y, nqb = (n + 4 * WQ - 1) / (4 * WQ);
+  const int m0 = (nqb - 1 - (int)blockIdx.x) * 4 * WQ + wave * WQ;
   if (m0 >= n) return;   // the wave has no query (no barriers in this kernel)
   const int c = lane & 15, g = lane >> 4;
   const int n_keys = pos0 + n;
@@ -509,17 +645,25 @@ __global__ __launch_bounds__(256) void mp_attention(const uint16_t* __restrict__
   const _Float16* vh = reinterpret_cast<const _Float16*>(vc) + (size_t)h * head_elems;
   const rsrc rk = make_res(kh, (uint64_t)n_keys * HD * 2), rv = make_res(vh, (uint64_t)n_keys * HD * 2);
   const rsrc rq = make_res(q16, (uint64_t)n * q * 2);
-  // B operand of the score products: this lane's query row, dims 32 cc + 8 g .. +7
-  f16x8 qb[HD / 32];
+  // B operands of the score products: this lane's query row of each group, dims 32 cc + 8 g .. +7
+  f16x8 qb[QG][HD / 32];
 #pragma unroll
-  for (int cc = 0; cc < HD / 32; ++cc)
-    qb[cc] = ld8(rq, m0 + c < n ? (uint32_t)((size_t)(m0 + c) * q + (size_t)h * HD + 32 * cc + 8 * g) * 2u : kOutOfRange);
-  f32x4m acc[DT];
+  for (int u = 0; u < QG; ++u) {
+    const int m = m0 + 16 * u + c;
 #pragma unroll
-  for (int t = 0; t < DT; ++t) acc[t] = f32x4m{0.f, 0.f, 0.f, 0.f};
-  float mrow = -INFINITY, lsum = 0.f;
-  const int qi = pos0 + m0 + c;                    // this lane's query position
-  const int last = pos0 + min(m0 + 15, n - 1);     // the wave's last query position
+    for (int cc = 0; cc < HD / 32; ++cc)
+      qb[u][cc] = ld8(rq, m < n ? (uint32_t)((size_t)m * q + (size_t)h * HD + 32 * cc + 8 * g) * 2u : kOutOfRange);
+  }
+  f32x4m acc[QG][DT];
+  float mrow[QG], lsum[QG];
+#pragma unroll
+  for (int u = 0; u < QG; ++u) {
+    mrow[u] = -INFINITY;
+    lsum[u] = 0.f;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) acc[u][t] = f32x4m{0.f, 0.f, 0.f, 0.f};
+  }
+  const int last = pos0 + min(m0 + WQ - 1, n - 1);   // the wave's last query position
   for (int j0 = 0; j0 <= last; j0 += 32) {
     // the 8 keys of this lane group: j0 + 4g + i (i < 4) and j0 + 16 + 4g + i - 4
     typename Row::T vrow[8];
@@ -528,60 +672,76 @@ __global__ __launch_bounds__(256) void mp_attention(const uint16_t* __restrict__
       const int key = j0 + (i < 4 ? 4 * g + i : 16 + 4 * g + i - 4);
       vrow[i] = Row::load(rv, key < n_keys ? (uint32_t)(key * HD + c * DT) * 2u : kOutOfRange);
     }
-    f32x4m s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    f16x8 ka[HD / 32], kb[HD / 32];
 #pragma unroll
     for (int cc = 0; cc < HD / 32; ++cc) {
       const int ja = j0 + c, jb = j0 + 16 + c;
-      const f16x8 ka = ld8(rk, ja < n_keys ? (uint32_t)(ja * HD + 32 * cc + 8 * g) * 2u : kOutOfRange);
-      const f16x8 kb = ld8(rk, jb < n_keys ? (uint32_t)(jb * HD + 32 * cc + 8 * g) * 2u : kOutOfRange);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[cc], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, qb[cc], s1, 0, 0, 0);
+      ka[cc] = ld8(rk, ja < n_keys ? (uint32_t)(ja * HD + 32 * cc + 8 * g) * 2u : kOutOfRange);
+      kb[cc] = ld8(rk, jb < n_keys ? (uint32_t)(jb * HD + 32 * cc + 8 * g) * 2u : kOutOfRange);
     }
-    // online softmax of the lane's query over the 32 keys
-    float p[8];
+    // V^T operands, output block t = dims c DT + t (shared by the query groups)
+    f16x8 va[DT];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[r] = (j0 + 4 * g + r <= qi) ? s0[r] : -INFINITY;
-      p[4 + r] = (j0 + 16 + 4 * g + r <= qi) ? s1[r] : -INFINITY;
-    }
-    float mx = p[0];
+    for (int t = 0; t < DT; ++t)
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, p[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // key 0 is at or below every query, so the max is finite from the first block on
-    const float mn = fmaxf(mrow, mx);
-    const float alpha = expf(mrow - mn);
-    f16x8 pb;
-    float rs = 0.f;
+      for (int i = 0; i < 8; ++i) va[t][i] = vrow[i][t];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float e = expf(p[i] - mn);
-      rs += e;
-      pb[i] = (_Float16)e;
-    }
-    rs += __shfl_xor(rs, 16, 64);
-    rs += __shfl_xor(rs, 32, 64);
-    lsum = lsum * alpha + rs;
-    mrow = mn;
-    // O^T += V^T P^T, output block t = dims c DT + t
+    for (int u = 0; u < QG; ++u) {
+      if (j0 > pos0 + m0 + 16 * u + 15) continue;   // every key of the block is past this group (wave-uniform)
+      // scores S^T = K q^T: s0[r] for key j0 + 4g + r, s1[r] for key j0 + 16 + 4g + r
+      f32x4m s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      f16x8 va;
+      for (int cc = 0; cc < HD / 32; ++cc) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[cc], qb[u][cc], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[cc], qb[u][cc], s1, 0, 0, 0);
+      }
+      // online softmax of the lane's query over the 32 keys
+      const int qi = pos0 + m0 + 16 * u + c;
+      float p[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) va[i] = vrow[i][t];
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[t] * alpha, 0, 0, 0);
+      for (int r = 0; r < 4; ++r) {
+        p[r] = (j0 + 4 * g + r <= qi) ? s0[r] : -INFINITY;
+        p[4 + r] = (j0 + 16 + 4 * g + r <= qi) ? s1[r] : -INFINITY;
+      }
+      float mx = p[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, p[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // key 0 is at or below every query, so the max is finite from the first block on
+      const float mn = fmaxf(mrow[u], mx);
+      const float alpha = expf(mrow[u] - mn);
+      f16x8 pb;
+      float rs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float ev = expf(p[i] - mn);
+        rs += ev;
+        pb[i] = (_Float16)ev;
+      }
+      rs += __shfl_xor(rs, 16, 64);
+      rs += __shfl_xor(rs, 32, 64);
+      lsum[u] = lsum[u] * alpha + rs;
+      mrow[u] = mn;
+      // O^T += V^T P^T
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+        acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[t], pb, acc[u][t] * alpha, 0, 0, 0);
     }
   }
-  if (m0 + c >= n) return;
-  const float inv = 1.0f / lsum;
-  _Float16* orow = reinterpret_cast<_Float16*>(o16) + (size_t)(m0 + c) * q + (size_t)h * HD;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    typename Row::T o;
+  for (int u = 0; u < QG; ++u) {
+    const int m = m0 + 16 * u + c;
+    if (m >= n) continue;
+    const float inv = 1.0f / lsum[u];
+    _Float16* orow = reinterpret_cast<_Float16*>(o16) + (size_t)m * q + (size_t)h * HD;
 #pragma unroll
-    for (int t = 0; t < DT; ++t) o[t] = (_Float16)(acc[t][r] * inv);
-    *reinterpret_cast<typename Row::T*>(orow + (4 * g + r) * DT) = o;
+    for (int r = 0; r < 4; ++r) {
+      typename Row::T o;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) o[t] = (_Float16)(acc[u][t][r] * inv);
+      *reinterpret_cast<typename Row::T*>(orow + (4 * g + r) * DT) = o;
+    }
   }
 }
 
@@ -741,12 +901,13 @@ int mp_launch_gemm(const MpGemm& g, void* stream) {
 }
 int mp_launch_attention(const uint16_t* q16, int q, int n, int pos0, int H, int hd, const uint16_t* kc,
                         const uint16_t* vc, size_t head_elems, uint16_t* o16, void* stream) {
-  const dim3 grid((n + 63) / 64, H);
+  constexpr int QG = 2;   // query groups of 16 per wave
+  const dim3 grid((n + 64 * QG - 1) / (64 * QG), H);
   const hipStream_t st = (hipStream_t)stream;
   switch (hd) {
-    case 32: hipLaunchKernelGGL(mp_attention<32>, grid, dim3(256), 0, st, q16, q, n, pos0, kc, vc, head_elems, o16); break;
-    case 64: hipLaunchKernelGGL(mp_attention<64>, grid, dim3(256), 0, st, q16, q, n, pos0, kc, vc, head_elems, o16); break;
-    case 128: hipLaunchKernelGGL(mp_attention<128>, grid, dim3(256), 0, st, q16, q, n, pos0, kc, vc, head_elems, o16); break;
+    case 32: hipLaunchKernelGGL((mp_attention<32, QG>), grid, dim3(256), 0, st, q16, q, n, pos0, kc, vc, head_elems, o16); break;
+    case 64: hipLaunchKernelGGL((mp_attention<64, QG>), grid, dim3(256), 0, st, q16, q, n, pos0, kc, vc, head_elems, o16); break;
+    case 128: hipLaunchKernelGGL((mp_attention<128, QG>), grid, dim3(256), 0, st, q16, q, n, pos0, kc, vc, head_elems, o16); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
