@@ -428,141 +428,6 @@ __global__ __launch_bounds__(256, OCC) void mp_gemm_rs(const uint16_t* __restric
   wave_epilogue<WM, WN>(e, acc, mb + wr * WM * 16, nb + wc * WN * 16, M, N, lane);
 }
 
-typedef float f32x16m __attribute__((ext_vector_type(16)));
-
-// The epilogue of one v_mfma_f32_32x32x16_f16 result block: element x is row
-// mrow + 8 (x / 4) + 4 (lane / 32) + x % 4 and column ncol + lane % 32.  (One
-// block per call keeps every index of the accumulators constant after
-// unrolling, so they stay in registers.)
-__device__ __forceinline__ void block_epilogue32(const MpEpi& e, float* Cz, int ldc, f32x16m v16, int mrow, int ncol,
-                                                 int M, int N, int lane) {
-  const bool pair = e.mode == MP_EP_SWIGLU || e.mode == MP_EP_ROPE;
-  const int n = ncol + (lane & 31);
-#pragma unroll
-  for (int x = 0; x < 16; ++x) {
-    const int m = mrow + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
-    const bool mok = m < M;
-    const float sc = (e.mode != MP_EP_ACCUM && e.mode != MP_EP_PART && e.s && mok) ? e.s[m] : 1.0f;
-    const float v = v16[x] * sc;
-    if (pair) {
-      const float w = __shfl_xor(v, 1, 64);
-      if (mok && n < N && !(n & 1)) pair_store(e, m, n, v, w);
-      continue;
-    }
-    if (!mok || n >= N) continue;
-    float* c = Cz + (size_t)m * ldc + n;
-    if (e.mode == MP_EP_ACCUM) *c = *c + v;
-    else *c = v;
-  }
-}
-
-// Every block of a wave's WM x WN accumulators, block I = i WN + j by
-// compile-time recursion (plain loops here were left rolled by the compiler,
-// which then kept the accumulators in scratch memory).
-template <int I, int WM, int WN>
-__device__ __forceinline__ void epilogue_blocks32(const MpEpi& e, float* Cz, int ldc, const f32x16m (&acc)[WM][WN],
-                                                  int mrow, int ncol, int M, int N, int lane) {
-  if constexpr (I < WM * WN) {
-    block_epilogue32(e, Cz, ldc, acc[I / WN][I % WN], mrow + 32 * (I / WN), ncol + 32 * (I % WN), M, N, lane);
-    epilogue_blocks32<I + 1, WM, WN>(e, Cz, ldc, acc, mrow, ncol, M, N, lane);
-  }
-}
-
-// Large products: 256 x 128 tiles, four waves of 128 x 64 computed with
-// v_mfma_f32_32x32x16_f16 (4 x 2 blocks of 32 x 32 per wave), 32-wide K tiles
-// staged through registers into two LDS stages.  In LDS a 1 KB block holds
-// rows 32 r .. +31 and one 16-wide K step: lane l's 16 bytes at 16 l are row
-// l % 32, K elements 8 (l / 32) .. +7, the instruction's operand layout.  The
-// global loads take each row's 64 bytes of a K tile as four 16-byte pieces;
-// thread t loads piece (t / 16) % 4 of row t % 16 + 16 (t / 64) (+ 64 i), so
-// the 16 lanes of each LDS write phase land on 16 consecutive rows of one
-// block: no bank conflicts.  The larger wave tile reads 24 bytes of LDS per
-// thousand flops against 32 for the 64 x 64 wave tile.
-template <int OCC>
-__global__ __launch_bounds__(256, OCC) void mp_gemm_big(const uint16_t* __restrict__ A, int lda,
-                                                        const uint16_t* __restrict__ B, int ldb, int M, int N, int K,
-                                                        int kc, MpEpi e) {
-  constexpr int BM = 256, BN = 128, WM = 4, WN = 2;
-  constexpr int ABLK = BM / 32 * 2, BBLK = BN / 32 * 2, STAGE = (ABLK + BBLK) * 1024;
-  constexpr int LA = BM / 64, LB = BN / 64;   // 16-byte global loads per thread per K tile
-  extern __shared__ __attribute__((aligned(1024))) char lds[];
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wr = wave >> 1, wc = wave & 1;
-  const int mb = blockIdx.y * BM, nb = blockIdx.x * BN;
-  const int kb = blockIdx.z * kc, ke = min(K, kb + kc);
-  const int ntiles = (ke - kb) / 32;   // K, kc and so ke - kb are multiples of 32
-  const rsrc ra = make_res(A, (uint64_t)M * lda * 2), rb = make_res(B, (uint64_t)N * ldb * 2);
-  const int t = threadIdx.x, r0 = (t & 15) + 16 * (t >> 6), pc = (t >> 4) & 3;
-  uint32_t aoff[LA], boff[LB];
-  int aw[LA], bw[LB];
-#pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    const int r = r0 + 64 * i, row = mb + r;
-    aoff[i] = row < M ? (uint32_t)((size_t)row * lda + kb + 8 * pc) * 2u : kOutOfRange;
-    aw[i] = ((r >> 5) * 2 + (pc >> 1)) * 1024 + ((r & 31) + 32 * (pc & 1)) * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    const int r = r0 + 64 * i, row = nb + r;
-    boff[i] = row < N ? (uint32_t)((size_t)row * ldb + kb + 8 * pc) * 2u : kOutOfRange;
-    bw[i] = ABLK * 1024 + ((r >> 5) * 2 + (pc >> 1)) * 1024 + ((r & 31) + 32 * (pc & 1)) * 16;
-  }
-  f16x8 ga[LA], gb[LB];
-#pragma unroll
-  for (int i = 0; i < LA; ++i) ga[i] = ld8(ra, aoff[i]);
-#pragma unroll
-  for (int i = 0; i < LB; ++i) gb[i] = ld8(rb, boff[i]);
-#pragma unroll
-  for (int i = 0; i < LA; ++i) *reinterpret_cast<f16x8*>(lds + aw[i]) = ga[i];
-#pragma unroll
-  for (int i = 0; i < LB; ++i) *reinterpret_cast<f16x8*>(lds + bw[i]) = gb[i];
-  __syncthreads();
-  f32x16m acc[WM][WN];
-#pragma unroll
-  for (int i = 0; i < WM; ++i)
-#pragma unroll
-    for (int j = 0; j < WN; ++j)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) acc[i][j][x] = 0.f;
-  for (int tt = 0; tt < ntiles; ++tt) {
-    const bool next = tt + 1 < ntiles;
-    if (next) {
-      const uint32_t step = (uint32_t)(tt + 1) * 64u;   // 32 halves per K tile
-#pragma unroll
-      for (int i = 0; i < LA; ++i) ga[i] = ld8(ra, aoff[i] != kOutOfRange ? aoff[i] + step : kOutOfRange);
-#pragma unroll
-      for (int i = 0; i < LB; ++i) gb[i] = ld8(rb, boff[i] != kOutOfRange ? boff[i] + step : kOutOfRange);
-    }
-    const char* as = lds + (tt & 1) * STAGE;
-    const char* bs = as + ABLK * 1024;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      f16x8 a[WM], b[WN];
-#pragma unroll
-      for (int i = 0; i < WM; ++i)
-        a[i] = *reinterpret_cast<const f16x8*>(as + ((wr * WM + i) * 2 + ks) * 1024 + 16 * lane);
-#pragma unroll
-      for (int j = 0; j < WN; ++j)
-        b[j] = *reinterpret_cast<const f16x8*>(bs + ((wc * WN + j) * 2 + ks) * 1024 + 16 * lane);
-#pragma unroll
-      for (int i = 0; i < WM; ++i)
-#pragma unroll
-        for (int j = 0; j < WN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (next) {
-      char* st = lds + ((tt + 1) & 1) * STAGE;
-#pragma unroll
-      for (int i = 0; i < LA; ++i) *reinterpret_cast<f16x8*>(st + aw[i]) = ga[i];
-#pragma unroll
-      for (int i = 0; i < LB; ++i) *reinterpret_cast<f16x8*>(st + bw[i]) = gb[i];
-    }
-    __syncthreads();   // tile tt+1 is in LDS; tile tt's stage may be overwritten
-  }
-  float* Cz = e.mode == MP_EP_PART ? e.C + (size_t)blockIdx.z * M * N : e.C;
-  const int ldc = e.mode == MP_EP_PART ? N : e.ldc;
-  epilogue_blocks32<0, WM, WN>(e, Cz, ldc, acc, mb + wr * 128, nb + wc * 64, M, N, lane);
-}
-
 // The epilogue of a split-K product: the S partial slices [S][M][N] added in
 // slice order, then through the product's epilogue (one thread per result,
 // or per column pair in the pair modes).
