@@ -32,10 +32,10 @@ def stream():
     return torch.cuda.Stream(device=0)
 
 
-def run(shape, tensors, prompt, script, batch=1, stream=None, serve=0, **kw):
+def run(shape, tensors, prompt, script, batch=1, stream=None, serve=0, flags=0, **kw):
     """Apply `script` to a fresh handle; returns every output in order."""
     out = []
-    dec = B.Decoder(B.ModelDesc.from_shape(shape, batch=batch), tensors=tensors, device=0,
+    dec = B.Decoder(B.ModelDesc.from_shape(shape, batch=batch, flags=flags), tensors=tensors, device=0,
                     stream=None if stream is None else stream.cuda_stream, serve_idle_us=serve, **kw)
     try:
         out.append(dec.prefill(prompt, want_logits=True))
@@ -78,9 +78,9 @@ def same(a, b, what=""):
             np.testing.assert_array_equal(np.asarray(x), np.asarray(y), err_msg=f"{what} output {i}")
 
 
-def compare(shape, tensors, prompt, script, stream, batch=1, serve=IDLE_US):
-    ref = run(shape, tensors, prompt, script, batch=batch, stream=stream)
-    got = run(shape, tensors, prompt, script, batch=batch, serve=serve)
+def compare(shape, tensors, prompt, script, stream, batch=1, serve=IDLE_US, flags=0):
+    ref = run(shape, tensors, prompt, script, batch=batch, stream=stream, flags=flags)
+    got = run(shape, tensors, prompt, script, batch=batch, serve=serve, flags=flags)
     same(ref, got, "server vs one launch per step")
     return got
 
@@ -100,6 +100,19 @@ def test_server_steps_bitwise(stream):
         script.append(("step", force, i % 2 == 0, i % 3 == 0))
     script += [("kv", l) for l in range(s.n_layers)]
     compare(s, t, prompt, script, stream)
+
+
+def test_server_after_matrix_prefill(stream):
+    """The matrix prefill (its own kernels on the handle's stream) hands its
+    cache and next token to the decode server as to a per-step launch; a
+    reset and a second matrix prefill follow a running server launch."""
+    s, t = tiny()
+    prompt = synth.make_prompt(s.vocab, 23, seed=6)[0]
+    other = synth.make_prompt(s.vocab, 9, seed=7)[0]
+    script = [("step", None, True, i % 4 == 0) for i in range(12)]
+    script += [("restart", other)] + [("step", None, True, True) for _ in range(6)]
+    script += [("kv", l) for l in range(s.n_layers)]
+    compare(s, t, prompt, script, stream, flags=B.DEC_FLAG_MATRIX_PREFILL)
 
 
 def test_server_async_steps_past_the_ring(stream):

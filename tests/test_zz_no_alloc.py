@@ -58,6 +58,27 @@ def test_noalloc_equals_dec_init_on_two_calls_in_a_row(stream):
               flush=True)
 
 
+def test_noalloc_matrix_prefill_equals_dec_init(stream):
+    """With DEC_FLAG_MATRIX_PREFILL the prefill's workspace sits in the caller's
+    arena; two handles in a row, the second with a smaller prompt, equal
+    dec_init bitwise."""
+    s = synth.shape_for("tiny")
+    t = synth.make_weights(s, seed=55, gain_jitter=0.1)
+    desc = B.ModelDesc.from_shape(s, flags=B.DEC_FLAG_MATRIX_PREFILL)
+    arena, n = arena_for(desc)
+    for plen, steps, gen in ((70, 8, 6), (12, 3, 2)):
+        prompt = synth.make_prompt(s.vocab, plen, seed=56 + plen)[0]
+        with B.Decoder(desc, tensors=t, stream=stream.cuda_stream) as ref:
+            want = run(ref, prompt, steps, gen)
+        with B.Decoder(desc, tensors=t, stream=stream.cuda_stream, arena=arena.data_ptr(), arena_bytes=n,
+                       noalloc=True) as d:
+            got = run(d, prompt, steps, gen)
+        np.testing.assert_array_equal(got[0], want[0])
+        np.testing.assert_array_equal(got[1], want[1])
+        print(f"matrix prefill {plen} + {steps} steps + {gen} generated: no-allocation handle equals dec_init bitwise",
+              flush=True)
+
+
 def test_noalloc_batch8_and_dense2b_equal_dec_init(stream):
     # batch 8 on the tiny shape (batched kernel, larger scratch) ...
     s = synth.shape_for("tiny")
