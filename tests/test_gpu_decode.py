@@ -547,6 +547,25 @@ def test_matrix_prefill_then_generate_matches_steps(stream):
         assert list(ga) == gb
 
 
+@pytest.mark.parametrize("hd,H", [(32, 8), (128, 2)])
+def test_matrix_prefill_other_head_dims(stream, hd, H):
+    """The attention kernel is built per head dimension: 32 and 128 as well as
+    tiny's 64, with the same 256-wide Q/K/V."""
+    s = synth.shape_for("tiny").with_(head_dim=hd, n_heads=H)
+    t = synth.make_weights(s, seed=61 + hd, gain_jitter=0.1)
+    n = 45
+    prompt = synth.make_prompt(s.vocab, n, seed=62 + hd)[0]
+    fed, ref, ref_pre, _ = O.greedy_decode(s, t, prompt, 3)
+    _, K16, V16, _ = O.prefill_matrix(s, t, prompt)
+    with make(s, t, stream, flags=MP) as d:
+        tok, pre = d.prefill(prompt, want_logits=True)
+        check_logits(pre, ref_pre, f"matrix prefill, head dim {hd}")
+        check_prefill_kv(d, s, K16, V16, n, f"matrix prefill, head dim {hd}")
+        for i in range(3):
+            _, lg = d.step(force_tok=int(fed[i]), want_logits=True)
+            check_logits(lg, ref[i], f"step {i} after matrix prefill, head dim {hd}")
+
+
 def test_matrix_prefill_spans_two_chunks(stream):
     """2100 prompt positions: 2048 in the first pass over the weights and 52 in
     the second, whose attention reads the first pass's cache entries."""
