@@ -91,19 +91,26 @@ __global__ __launch_bounds__(256) void mp_embed(const uint16_t* __restrict__ E, 
 }
 
 // h[m] = fp16(x[m] * g) and s[m] = 1 / sqrt(mean(x[m]^2) + eps).  One
-// workgroup per row; the sum of squares is added per thread in index order,
+// workgroup per row, four consecutive elements per thread and access (d is a
+// multiple of 32); the sum of squares is added per thread in index order,
 // then over the wave, then over the four waves in order.
 __global__ __launch_bounds__(256) void mp_norm(const float* __restrict__ x, const float* __restrict__ g, int d,
                                                float eps, uint16_t* __restrict__ h, float* __restrict__ s) {
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
   __shared__ float part[4];
   const int m = blockIdx.x, tid = threadIdx.x;
-  const float* xr = x + (size_t)m * d;
-  _Float16* hr = reinterpret_cast<_Float16*>(h) + (size_t)m * d;
+  const f32x4v* xr = reinterpret_cast<const f32x4v*>(x + (size_t)m * d);
+  const f32x4v* gr = reinterpret_cast<const f32x4v*>(g);
+  f16x4* hr = reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(h) + (size_t)m * d);
   float ss = 0.f;
-  for (int i = tid; i < d; i += 256) {
-    const float v = xr[i];
-    ss += v * v;
-    hr[i] = (_Float16)(v * g[i]);
+  for (int i = tid; i < d / 4; i += 256) {
+    const f32x4v v = xr[i], gg = gr[i];
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    f16x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = (_Float16)(v[k] * gg[k]);
+    hr[i] = o;
   }
   ss = wave_sum64(ss);
   if ((tid & 63) == 0) part[tid >> 6] = ss;
