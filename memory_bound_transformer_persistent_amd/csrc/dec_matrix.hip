@@ -714,8 +714,8 @@ int mp_prepare() {
 // the widest and the deepest products).  More rows: the register-staged
 // 128 x 128 tile.  Then the K range is split (up to 8 ways, each split 4 K
 // steps or more, partials within part_floats) until about 150 workgroups
-// run.  The choices follow timings of the dense2b products on MI355X at 1 to
-// 3968 rows.
+// run (200 for the register-staged tile).  The choices follow timings of the
+// dense2b products on MI355X at 1 to 3968 rows.
 void mp_plan(int M, int N, int K, size_t part_floats, int* shape, int* S, int* kc) {
   auto count = [&](int t) {
     return (long long)((M + kShapeBM[t] - 1) / kShapeBM[t]) * ((N + kShapeBN[t] - 1) / kShapeBN[t]);
@@ -726,7 +726,8 @@ void mp_plan(int M, int N, int K, size_t part_floats, int* shape, int* S, int* k
   else pick = 0;
   int s = 1;
   const long long c = count(pick);
-  while (s < 8 && c * s < 150 && K / (32 * 2 * s) >= 4 && (size_t)(2 * s) * M * N <= part_floats) s *= 2;
+  const long long want = M <= 512 ? 150 : 200;
+  while (s < 8 && c * s < want && K / (32 * 2 * s) >= 4 && (size_t)(2 * s) * M * N <= part_floats) s *= 2;
   const int steps = (K / 32 + s - 1) / s;   // K steps per split
   *shape = pick;
   *S = (K / 32 + steps - 1) / steps;
