@@ -55,3 +55,57 @@ def format_summary(out, total):
                      f"{v['span']:9.2f} {v['span'] * v['count']:11.1f}")
     lines.append(f"launch total {total:.1f} us")
     return "\n".join(lines)
+
+
+def main(argv):
+    """python -m memory_bound_transformer_persistent_amd.trace [WORKLOAD] [STEPS]
+
+    Per-phase summary of single-step decode launches with DEC_DEBUG_TRACE:
+    the workload's prompt is prefilled, then STEPS launches of one token each
+    are traced and their summaries averaged (the stamps add a few
+    microseconds per launch, so the totals sit slightly above untraced steps).
+    """
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import torch
+    import synth
+    from memory_bound_transformer_persistent_amd import binding as B
+
+    name = argv[0] if argv else "dense2b"
+    steps = int(argv[1]) if len(argv) > 1 else 16
+    w = synth.workload(name)
+    s = w.shape
+    tensors = synth.workload_weights(w)
+    prompt = synth.make_prompt(s.vocab, w.prompt_len, batch=w.batch, seed=w.prompt_seed)
+    stream = torch.cuda.Stream(device=0)
+    sums, total = None, 0.0
+    with B.Decoder(B.ModelDesc.from_shape(s, batch=w.batch), tensors=tensors, device=0, stream=stream.cuda_stream,
+                   debug_flags=B.DEC_DEBUG_TRACE) as dec:
+        dec.prefill(prompt)
+        for _ in range(4):
+            dec.step()
+        pos0 = dec.position
+        for _ in range(steps):
+            dec.step()
+            stamps, hz = dec.read_trace()
+            out, tot = summarize(stamps, hz, s.n_layers)
+            total += tot / steps
+            if sums is None:
+                sums = {k: dict(v) for k, v in out.items()}
+                for v in sums.values():
+                    for f in ("work", "slowest", "barrier", "span"):
+                        v[f] /= steps
+            else:
+                for k, v in out.items():
+                    for f in ("work", "slowest", "barrier", "span"):
+                        sums[k][f] += v[f] / steps
+    print(f"{name}: {steps} traced single-step launches at positions {pos0}..{pos0 + steps - 1}, "
+          f"batch {w.batch}; per phase kind, mean over layers and launches (us)")
+    print(format_summary(sums, total))
+    return 0
+
+
+if __name__ == "__main__":
+    import sys
+    sys.exit(main(sys.argv[1:]))
