@@ -6,8 +6,10 @@ same arrays from it and compute from them independently.
 """
 from .shapes import ModelShape, Workload, WORKLOADS, shape_for, workload
 from .gen import (tensor_names, tensor_shapes, make_weights, make_prompt,
-                  lane_slice_weights, lane_from_full, workload_weights, N_TENSORS_PER_LAYER)
+                  lane_slice_weights, lane_from_full, workload_weights, N_TENSORS_PER_LAYER,
+                  layer_tensors)
 
 __all__ = ["ModelShape", "Workload", "WORKLOADS", "shape_for", "workload",
            "tensor_names", "tensor_shapes", "make_weights", "make_prompt",
-           "lane_slice_weights", "lane_from_full", "workload_weights", "N_TENSORS_PER_LAYER"]
+           "lane_slice_weights", "lane_from_full", "workload_weights", "N_TENSORS_PER_LAYER",
+           "layer_tensors"]

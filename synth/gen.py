@@ -11,6 +11,19 @@ Canonical tensor order (also the order of the C ABI's host tensor list):
              Wo [d, H*hd], g_ffn [d], Wg [F, d], Wu [F, d], Wd [d, F]
   g_final [d], W_lm [lm_vocab, d]
 All matrices are stored [out, in], row-major.
+
+Mixture-of-experts shapes (n_experts E > 0, expert width F = d_ffn) replace
+Wg, Wu, Wd by a router and E experts per layer:
+  per layer: g_attn, Wq, Wk, Wv, Wo, g_ffn, Wr [E, d] (fp16),
+             Wg8 [E*F, d] (uint8 FP8 E4M3 codes), sg [E*F] (float32 row scales),
+             Wu8 [E*F, d], su [E*F], Wd8 [E*d, F], sd [E*d]
+Expert e owns rows e*F .. e*F+F-1 of Wg8/Wu8 and rows e*d .. e*d+d-1 of Wd8.
+The expert weights are drawn as codes, never as values: sign and mantissa
+bits uniform, the exponent field from a fixed 16-entry table that roughly
+follows the magnitudes of a standard normal (1/16 of the codes subnormal,
+none with the all-ones exponent, so no NaN and no value above 3.75), and
+every row's scale is 0.01 * (0.75 + 0.5 u), u uniform.  The router is drawn
+like the other fp16 matrices.
 """
 import os
 from concurrent.futures import ThreadPoolExecutor
@@ -23,25 +36,48 @@ _THREADS = min(16, os.cpu_count() or 1)
 
 LAYER_TENSORS = ("g_attn", "Wq", "Wk", "Wv", "Wo", "g_ffn", "Wg", "Wu", "Wd")
 N_TENSORS_PER_LAYER = len(LAYER_TENSORS)
+MOE_LAYER_TENSORS = ("g_attn", "Wq", "Wk", "Wv", "Wo", "g_ffn", "Wr", "Wg8", "sg", "Wu8", "su", "Wd8", "sd")
+
+# exponent field of a drawn FP8 code, indexed by 4 random bits
+_EXP_FIELD = np.array([8, 7, 7, 7, 7, 6, 6, 6, 6, 6, 5, 5, 5, 4, 3, 0], dtype=np.uint8)
+
+
+def layer_tensors(shape: ModelShape):
+    return MOE_LAYER_TENSORS if shape.moe else LAYER_TENSORS
 
 
 def tensor_names(shape: ModelShape):
     names = ["E"]
     for l in range(shape.n_layers):
-        names += [f"{t}.{l}" for t in LAYER_TENSORS]
+        names += [f"{t}.{l}" for t in layer_tensors(shape)]
     names += ["g_final", "W_lm"]
     return names
 
 
 def tensor_shapes(shape: ModelShape):
-    d, q, f = shape.d_model, shape.qkv_width, shape.d_ffn
+    d, q, f, E = shape.d_model, shape.qkv_width, shape.d_ffn, shape.n_experts
     per = {"g_attn": (d,), "Wq": (q, d), "Wk": (q, d), "Wv": (q, d), "Wo": (d, q),
-           "g_ffn": (d,), "Wg": (f, d), "Wu": (f, d), "Wd": (d, f)}
+           "g_ffn": (d,), "Wg": (f, d), "Wu": (f, d), "Wd": (d, f),
+           "Wr": (E, d), "Wg8": (E * f, d), "sg": (E * f,), "Wu8": (E * f, d), "su": (E * f,),
+           "Wd8": (E * d, f), "sd": (E * d,)}
     shapes = [(shape.vocab, d)]
     for _ in range(shape.n_layers):
-        shapes += [per[t] for t in LAYER_TENSORS]
+        shapes += [per[t] for t in layer_tensors(shape)]
     shapes += [(d,), (shape.lm_vocab, d)]
     return shapes
+
+
+def _draw_codes(shp, seed, index):
+    """FP8 E4M3 codes (uint8): sign and mantissa bits uniform, exponent field from _EXP_FIELD."""
+    rng = np.random.default_rng([seed, index])
+    u = rng.integers(0, 256, size=shp, dtype=np.uint8)
+    e = _EXP_FIELD[rng.integers(0, 16, size=shp, dtype=np.uint8)]
+    return (u & np.uint8(0x87)) | (e << np.uint8(3))
+
+
+def _draw_scales(shp, seed, index):
+    rng = np.random.default_rng([seed, index])
+    return (0.01 * (0.75 + 0.5 * rng.random(shp))).astype(np.float32)
 
 
 def _draw(shp, seed, index, scale=0.02):
@@ -64,6 +100,11 @@ def make_weights(shape: ModelShape, seed: int = 0, gain_jitter: float = 0.0):
                 rng = np.random.default_rng([seed, idx, 7])
                 return (1.0 + gain_jitter * rng.standard_normal(shp)).astype(np.float16)
             return np.ones(shp, dtype=np.float16)
+        base = name.split(".")[0]
+        if base in ("Wg8", "Wu8", "Wd8"):
+            return _draw_codes(shp, seed, idx)
+        if base in ("sg", "su", "sd"):
+            return _draw_scales(shp, seed, idx)
         return _draw(shp, seed, idx)
 
     items = list(enumerate(zip(tensor_names(shape), tensor_shapes(shape))))

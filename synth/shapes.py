@@ -22,10 +22,19 @@ class ModelShape:
     max_ctx: int
     rms_eps: float = 1e-5
     rope_base: float = 10000.0
+    # mixture of experts: n_experts > 0 replaces every layer's MLP by
+    # n_experts SwiGLU experts of width d_ffn with FP8 (E4M3) weights, of
+    # which a router picks top_k per token
+    n_experts: int = 0
+    top_k: int = 0
 
     @property
     def qkv_width(self) -> int:
         return self.n_heads * self.head_dim
+
+    @property
+    def moe(self) -> bool:
+        return self.n_experts > 0
 
     def with_(self, **kw) -> "ModelShape":
         return replace(self, **kw)
@@ -51,6 +60,11 @@ DENSE_2B = ModelShape(n_layers=25, d_model=2560, n_heads=20, head_dim=128,
 # One lane of an 8-way tensor-parallel split of DENSE_2B: 3 of the 20 heads,
 # 864 of the 6912 FFN columns and an 8192-row vocabulary shard of the LM head.
 LANE_2B = DENSE_2B.with_(n_heads=3, d_ffn=864, lm_vocab=8192)
+# dense2b's attention, embedding and LM head with a mixture-of-experts MLP:
+# 32 experts of width 1728 in FP8, 4 active per token, so the active MLP is
+# dense2b's 6912 columns at half the bytes.
+MOE_2B = DENSE_2B.with_(d_ffn=1728, n_experts=32, top_k=4)
+TINY_MOE = TINY.with_(d_ffn=256, n_experts=8, top_k=2)
 
 WORKLOADS = {
     "tiny": Workload("tiny", TINY, prompt_len=16, steps=32, batch=1,
@@ -61,6 +75,8 @@ WORKLOADS = {
                        description="one 8-way TP lane of dense2b: 3 heads, ffn 864, 8192-row LM shard"),
     "dense2b_long": Workload("dense2b_long", DENSE_2B, prompt_len=3968, steps=128, batch=1,
                              description="dense2b from a 3968-token prompt to the 4096 cap"),
+    "moe2b": Workload("moe2b", MOE_2B, prompt_len=128, steps=512, batch=1,
+                      description="dense2b attention with 32 FP8 experts of width 1728, top-4 routing"),
     "dense2b_b8": Workload("dense2b_b8", DENSE_2B, prompt_len=256, steps=256, batch=8,
                            description="dense2b, 8 sequences of 256 prompt tokens decoded together"),
 }
