@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DEC_ABI_VERSION 1
+#define DEC_ABI_VERSION 2
 
 typedef enum dec_status {
   DEC_OK = 0,
@@ -80,6 +80,27 @@ typedef enum dec_status {
  * n_heads*head_dim <= 7680 after rounding up to a multiple of 512 (every
  * sequence's matrix-product input is held on chip, in fp16).
  * Shapes of the weight tensors follow from it (see dec_weights_src).
+ *
+ * Mixture of experts (n_experts > 0).  Every layer's MLP is then n_experts
+ * SwiGLU experts of width d_ffn whose matrices are FP8 E4M3 codes with one
+ * float32 scale per output row; a bias-free fp16 router [n_experts, d_model]
+ * applied to the same normed vector picks the top_k experts with the largest
+ * logits (the lower expert index first on equal logits), and their outputs
+ * are added with the softmax of those top_k logits as weights.  This is the
+ * pages' next milestone, large mixture-of-experts models read at their
+ * active-parameter size with FP8 expert weights (page
+ * 標準GPUによるリアルタイムLLM推論, section Hackerたちの意見; page
+ * 「ソフトウェア・ファースト」戦略でGPUの限界を突破…, section
+ * 今後のマイルストーンと課題).  Rules (DEC_ERR_BAD_DESC otherwise):
+ * n_experts == 0 and top_k == 0 for a dense model; else 2 <= n_experts <= 64,
+ * n_experts even, 1 <= top_k <= min(n_experts, 8).  Limits
+ * (DEC_ERR_UNSUPPORTED): batch 1, flags 0, d_model and d_ffn multiples of
+ * 16, top_k * d_ffn <= 7168, each layer's expert matrices under 2 GiB of
+ * codes; weights from host tensors only (not a DECW file), not with
+ * dec_init_noalloc, dec_pack or DEC_DEBUG_MULTILAUNCH.  Numerics: the
+ * router's top_k choice is made on fp32 logits; a choice between two
+ * experts whose logits differ by less than the accumulated rounding can
+ * differ from an exact evaluation's (see dec_read_routes).
  *
  * Batch.  batch > 1 decodes that many independent sequences in lockstep (same
  * position, one pass over the weights per step serves all of them); each has
@@ -129,6 +150,8 @@ typedef struct dec_model_desc {
   float rms_eps;
   float rope_base;
   uint32_t flags;     /* 0, DEC_FLAG_BATCHED_PREFILL or DEC_FLAG_MATRIX_PREFILL */
+  int32_t n_experts;  /* 0: dense MLP; else experts per layer (mixture of experts) */
+  int32_t top_k;      /* experts each token uses (mixture of experts), else 0 */
 } dec_model_desc;
 
 /*
@@ -142,6 +165,18 @@ typedef struct dec_model_desc {
  *   g_final [d], W_lm [lm_vocab, d]
  * so n_tensors == 1 + 9*n_layers + 2.  The caller owns the buffers; they are
  * read during dec_init only.
+ *
+ * Mixture of experts (n_experts = E > 0, expert width F = d_ffn): the layer's
+ * Wg, Wu, Wd are replaced by seven tensors, so n_tensors == 1 + 13*n_layers
+ * + 2, and each pointer's bytes are read as the tensor's own element type:
+ *   for each layer: g_attn, Wq, Wk, Wv, Wo, g_ffn (fp16 as above),
+ *                   Wr  [E, d]      fp16 router,
+ *                   Wg8 [E*F, d]    uint8 E4M3 codes,  sg [E*F] float32 row scales,
+ *                   Wu8 [E*F, d]    uint8 E4M3 codes,  su [E*F] float32,
+ *                   Wd8 [E*d, F]    uint8 E4M3 codes,  sd [E*d] float32
+ * Expert e owns rows e*F .. e*F+F-1 of Wg8/Wu8 (and of sg/su) and rows
+ * e*d .. e*d+d-1 of Wd8 (and of sd); its matrix element is
+ * value(code) * scale of the element's row.
  *
  * path: a DECW weight file (format below).  Its description must equal the
  * one passed to dec_init in every shape field.
@@ -380,6 +415,18 @@ int32_t dec_position(const dec_handle* h);
  */
 int dec_read_kv(dec_handle* h, int32_t layer, int32_t seq, int32_t n_pos,
                 uint16_t* host_k, uint16_t* host_v);
+
+/*
+ * Mixture-of-experts models: the experts the router chose at positions
+ * [pos0, pos0 + n_pos), copied to host as int32 [n_pos][n_layers][top_k]
+ * (largest logit first).  Every step and prefill records its positions'
+ * choices; a position not yet computed reads as -1.  DEC_ERR_STATE for a
+ * dense model.  For tests and inspection (a choice between experts whose
+ * logits nearly tie can legitimately differ from an exact evaluation's);
+ * synchronous.  The routing the pages' mixture-of-experts projection
+ * assumes (page 標準GPUによるリアルタイムLLM推論, section Hackerたちの意見).
+ */
+int dec_read_routes(dec_handle* h, int32_t pos0, int32_t n_pos, int32_t* out_routes);
 
 /*
  * Phase trace of the most recent launch (handle created with DEC_DEBUG_TRACE).

@@ -51,14 +51,15 @@ class ModelDesc(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("d_ffn", ctypes.c_int32),
                 ("vocab", ctypes.c_int32), ("lm_vocab", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
                 ("batch", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32)]
 
     @classmethod
     def from_shape(cls, s, batch=1, **override):
         """From any object with the model-shape attributes."""
         kw = dict(n_layers=s.n_layers, d_model=s.d_model, n_heads=s.n_heads, n_kv_heads=s.n_heads,
                   head_dim=s.head_dim, d_ffn=s.d_ffn, vocab=s.vocab, lm_vocab=s.lm_vocab,
-                  max_ctx=s.max_ctx, batch=batch, rms_eps=s.rms_eps, rope_base=s.rope_base, flags=0)
+                  max_ctx=s.max_ctx, batch=batch, rms_eps=s.rms_eps, rope_base=s.rope_base, flags=0,
+                  n_experts=getattr(s, "n_experts", 0), top_k=getattr(s, "top_k", 0))
         kw.update(override)
         return cls(**kw)
 
@@ -95,6 +96,7 @@ SIGNATURES = {
     "dec_reset": (ctypes.c_int, [ctypes.c_void_p]),
     "dec_position": (ctypes.c_int32, [ctypes.c_void_p]),
     "dec_read_kv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _u16p, _u16p]),
+    "dec_read_routes": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, _i32p]),
     "dec_free": (None, [ctypes.c_void_p]),
     "dec_last_error": (ctypes.c_char_p, [ctypes.c_void_p]),
     "dec_read_trace": (ctypes.c_int, [ctypes.c_void_p, _P(ctypes.c_uint64), _i32p, _i32p, _P(ctypes.c_double)]),
@@ -137,10 +139,13 @@ def _check(rc, handle=None):
 
 
 def _tensor_ptrs(tensors):
+    """float16 tensors; a mixture of experts' expert codes are uint8 and
+    their row scales float32 (the library reads each pointer as its tensor's
+    own element type)."""
     arrs = [np.ascontiguousarray(t) for t in tensors]
     for a in arrs:
-        if a.dtype != np.float16:
-            raise TypeError("weights must be float16 arrays")
+        if a.dtype not in (np.float16, np.uint8, np.float32):
+            raise TypeError("weights must be float16 arrays (expert codes uint8, their scales float32)")
     ptrs = (_u16p * len(arrs))(*[a.ctypes.data_as(_u16p) for a in arrs])
     return arrs, ptrs
 
@@ -275,6 +280,13 @@ class Decoder:
         out = np.zeros((g.value, st.value), dtype=np.uint64)
         self._rc(self._lib.dec_read_trace(self._h, out.ctypes.data_as(_P(ctypes.c_uint64)), None, None, None))
         return out, hz.value
+
+    def read_routes(self, pos0, n_pos):
+        """Mixture of experts: the experts chosen at positions [pos0, pos0 + n_pos),
+        int32 [n_pos, n_layers, top_k] (-1 where not computed)."""
+        out = np.zeros((n_pos, self.desc.n_layers, self.desc.top_k), dtype=np.int32)
+        self._rc(self._lib.dec_read_routes(self._h, pos0, n_pos, out.ctypes.data_as(_i32p)))
+        return out
 
     def read_kv(self, layer, n_pos, seq=0):
         H, hd = self.desc.n_heads, self.desc.head_dim

@@ -37,7 +37,13 @@ int fail(std::string* where, int code, const char* fmt, ...) {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t n, size_t a = kAlign) { return (n + a - 1) / a * a; }
 
-int n_tensors_for(const dec_model_desc& d) { return 1 + 9 * d.n_layers + 2; }
+bool moe(const dec_model_desc& d) { return d.n_experts > 0; }
+// canonical tensors per layer: dense 9; mixture of experts 13 (the MLP's
+// three matrices become the router, three code matrices and their scales)
+int per_layer(const dec_model_desc& d) { return moe(d) ? 13 : 9; }
+int n_tensors_for(const dec_model_desc& d) { return 1 + per_layer(d) * d.n_layers + 2; }
+// which resident kernel runs the model: its batch, or the mixture-of-experts one
+int kernel_kind(const dec_model_desc& d) { return moe(d) ? kMoeKernel : d.batch; }
 
 int check_desc_impl(const dec_model_desc* d, std::string* err) {
   if (!d) return fail(err, DEC_ERR_INVALID_ARG, "model description is NULL");
@@ -63,6 +69,22 @@ int check_desc_impl(const dec_model_desc* d, std::string* err) {
   if (bp && d->batch != 1) return fail(err, DEC_ERR_BAD_DESC, "DEC_FLAG_BATCHED_PREFILL is for batch 1");
   if (mp && d->batch != 1) return fail(err, DEC_ERR_BAD_DESC, "DEC_FLAG_MATRIX_PREFILL is for batch 1");
   if (d->batch < 1) return fail(err, DEC_ERR_BAD_DESC, "batch must be >= 1");
+  if (d->n_experts == 0) {
+    if (d->top_k != 0) return fail(err, DEC_ERR_BAD_DESC, "top_k must be 0 for a dense model (got %d)", d->top_k);
+  } else {
+    if (d->n_experts < 2 || d->n_experts > kMoeMaxExperts || d->n_experts % 2)
+      return fail(err, DEC_ERR_BAD_DESC, "n_experts must be 0 or even and in [2, %d] (got %d)", kMoeMaxExperts, d->n_experts);
+    if (d->top_k < 1 || d->top_k > std::min(d->n_experts, kMoeMaxTopK))
+      return fail(err, DEC_ERR_BAD_DESC, "top_k must be in [1, min(n_experts, %d)] (got %d)", kMoeMaxTopK, d->top_k);
+    if (d->batch != 1 || d->flags)
+      return fail(err, DEC_ERR_UNSUPPORTED, "a mixture-of-experts model runs at batch 1 with flags 0");
+    if (d->d_model % 16 || d->d_ffn % 16)
+      return fail(err, DEC_ERR_UNSUPPORTED, "a mixture-of-experts model needs d_model and d_ffn multiples of 16");
+    if ((long long)d->top_k * d->d_ffn > kMaxK - 1024)
+      return fail(err, DEC_ERR_UNSUPPORTED, "top_k * d_ffn must be <= %d", kMaxK - 1024);
+    if ((long long)d->n_experts * 2 * d->d_ffn * d->d_model >= (1LL << 31))
+      return fail(err, DEC_ERR_UNSUPPORTED, "a layer's expert codes must be under 2 GiB");
+  }
   const long long q = (long long)d->n_heads * hd;
   if (q % 8) return fail(err, DEC_ERR_BAD_DESC, "n_heads*head_dim must be a multiple of 8");
   if (mp && (hd < 32 || d->d_model % 32 || q % 32 || d->d_ffn % 32))
@@ -97,9 +119,16 @@ int check_desc_impl(const dec_model_desc* d, std::string* err) {
 // Batch 1: every matrix row-major.  Batch > 1: every GEMV matrix (not the
 // embedding) in tiles of 16 rows x 32 columns, one 1 KB tile per MFMA
 // operand (see tiled_index).
+// Mixture of experts: the fp16 image holds the router where the dense
+// model's Wgu is (off_gu, [E, d]) and no Wd; the experts live in an image of
+// their own (bytes): per layer Wgu8 [E][F][2][d] (gate row j and up row j of
+// expert e at rows 2(eF + j), 2(eF + j) + 1), then Wd8 [E][d][F]; and their
+// row scales (floats): per layer [E][F][2] (gate, up), then [E][d].
 struct Image {
   size_t off_qkv, off_o, off_gu, off_d, layer_stride, off_E, off_lm, total;
   bool tiled;
+  size_t e8_d, e8_stride, e8_total;     // expert codes (bytes)
+  size_t sc_d, sc_stride, sc_total;     // expert row scales (floats)
 };
 
 size_t al128(size_t n) { return (n + 127) / 128 * 128; }
@@ -130,8 +159,21 @@ Image image_layout(const dec_model_desc& d) {
   im.off_qkv = 0;
   im.off_o = al128(im.off_qkv + matrix_elems(3 * q, D, t));
   im.off_gu = al128(im.off_o + matrix_elems(D, q, t));
-  im.off_d = al128(im.off_gu + matrix_elems(2 * F, D, t));
-  im.layer_stride = al128(im.off_d + matrix_elems(D, F, t));
+  im.e8_d = im.e8_stride = im.e8_total = im.sc_d = im.sc_stride = im.sc_total = 0;
+  if (moe(d)) {
+    const size_t E = d.n_experts;
+    im.off_d = al128(im.off_gu + E * D);
+    im.layer_stride = im.off_d;
+    im.e8_d = align_up(E * 2 * F * D);
+    im.e8_stride = align_up(im.e8_d + E * D * F);
+    im.e8_total = im.e8_stride * d.n_layers;
+    im.sc_d = E * F * 2;
+    im.sc_stride = align_up(im.sc_d + E * D, 64);
+    im.sc_total = im.sc_stride * d.n_layers;
+  } else {
+    im.off_d = al128(im.off_gu + matrix_elems(2 * F, D, t));
+    im.layer_stride = al128(im.off_d + matrix_elems(D, F, t));
+  }
   im.off_E = im.layer_stride * d.n_layers;
   im.off_lm = al128(im.off_E + (size_t)d.vocab * D);
   im.total = al128(im.off_lm + matrix_elems(d.lm_vocab, D, t));
@@ -155,6 +197,19 @@ void tensor_shape(const dec_model_desc& d, int idx, size_t* r, size_t* c) {
   if (idx == 0) { *r = d.vocab; *c = D; return; }
   if (idx == last) { *r = d.lm_vocab; *c = D; return; }
   if (idx == last - 1) { *r = D; *c = 1; return; }
+  if (moe(d)) {
+    const size_t E = d.n_experts;
+    switch ((idx - 1) % 13) {
+      case 0: case 5: *r = D; *c = 1; return;            // gains
+      case 1: case 2: case 3: *r = q; *c = D; return;     // Wq, Wk, Wv
+      case 4: *r = D; *c = q; return;                     // Wo
+      case 6: *r = E; *c = D; return;                     // Wr
+      case 7: case 9: *r = E * F; *c = D; return;         // Wg8, Wu8
+      case 8: case 10: *r = E * F; *c = 1; return;        // sg, su
+      case 11: *r = E * D; *c = F; return;                // Wd8
+      default: *r = E * D; *c = 1; return;                // sd
+    }
+  }
   switch ((idx - 1) % 9) {
     case 0: case 5: *r = D; *c = 1; return;            // gains
     case 1: case 2: case 3: *r = q; *c = D; return;     // Wq, Wk, Wv
@@ -164,10 +219,12 @@ void tensor_shape(const dec_model_desc& d, int idx, size_t* r, size_t* c) {
   }
 }
 
-// Place canonical tensor idx (fp16 bits, row-major) into the packed image;
-// gains go to gains_out (fp32) instead.  Rows may be passed in slices.
+// Place canonical tensor idx (row-major) into the packed image; gains go to
+// gains_out (fp32) instead, expert codes to image8 and their scales to
+// scales (a mixture of experts).  Rows may be passed in slices.
 void place_tensor(const dec_model_desc& d, const Image& im, int idx, const uint16_t* src,
-                  size_t row0, size_t nrows, uint16_t* image, float* gains_out) {
+                  size_t row0, size_t nrows, uint16_t* image, float* gains_out, uint8_t* image8 = nullptr,
+                  float* scales = nullptr) {
   size_t R, C;
   tensor_shape(d, idx, &R, &C);
   const size_t D = d.d_model, q = (size_t)d.n_heads * d.head_dim;
@@ -201,8 +258,27 @@ void place_tensor(const dec_model_desc& d, const Image& im, int idx, const uint1
     for (size_t i = 0; i < nrows; ++i) gains_out[(size_t)d.n_layers * 2 * D + row0 + i] = half_to_float(src[i]);
     return;
   }
-  const int l = (idx - 1) / 9, kind = (idx - 1) % 9;
+  const int per = per_layer(d);
+  const int l = (idx - 1) / per, kind = (idx - 1) % per;
   uint16_t* lay = image + (size_t)l * im.layer_stride;
+  if (moe(d) && kind >= 6) {
+    const size_t F = d.d_ffn;
+    const uint8_t* s8 = reinterpret_cast<const uint8_t*>(src);
+    const float* sf = reinterpret_cast<const float*>(src);
+    uint8_t* lay8 = image8 + (size_t)l * im.e8_stride;
+    float* lsc = scales + (size_t)l * im.sc_stride;
+    for (size_t i = 0; i < nrows; ++i) {
+      const size_t r = row0 + i;
+      switch (kind) {
+        case 6: put_row(lay, im.off_gu, r, src + i * C, C, false); break;   // router
+        case 7: case 9: std::memcpy(lay8 + (2 * r + (kind == 9)) * D, s8 + i * C, C); break;
+        case 8: case 10: lsc[2 * r + (kind == 10)] = sf[i]; break;
+        case 11: std::memcpy(lay8 + im.e8_d + r * F, s8 + i * C, C); break;
+        default: lsc[im.sc_d + r] = sf[i]; break;
+      }
+    }
+    return;
+  }
   switch (kind) {
     case 0:
     case 5:
@@ -281,14 +357,15 @@ int read_file_header(FILE* f, dec_model_desc* out, std::vector<FileEntry>* entri
 
 bool same_shape(const dec_model_desc& a, const dec_model_desc& b) {
   return a.n_layers == b.n_layers && a.d_model == b.d_model && a.n_heads == b.n_heads && a.n_kv_heads == b.n_kv_heads &&
-         a.head_dim == b.head_dim && a.d_ffn == b.d_ffn && a.vocab == b.vocab && a.lm_vocab == b.lm_vocab;
+         a.head_dim == b.head_dim && a.d_ffn == b.d_ffn && a.vocab == b.vocab && a.lm_vocab == b.lm_vocab &&
+         a.n_experts == b.n_experts && a.top_k == b.top_k;
 }
 
 // ---------------------------------------------------------------------------
 // device arena layout (bytes)
 // ---------------------------------------------------------------------------
 struct Arena {
-  size_t w, w2, gains, rope, kv, mp_x, mp_h, mp_q16, mp_a, mp_s, mp_part, x, xg16, ssp, qkv, att_o, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out,
+  size_t w, w2, w8, esc, routes, gains, rope, kv, mp_x, mp_h, mp_q16, mp_a, mp_s, mp_part, x, xg16, ssp, qkv, att_o, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out,
       prompt, ctl, srv_slot, params, params2, trace, total;
 };
 
@@ -328,6 +405,10 @@ Arena arena_layout(const dec_model_desc& d, int G) {
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
   a.w = take(im.total * 2);
   a.w2 = bp ? take(image_layout(prefill_desc(d)).total * 2) : 0;
+  // mixture of experts: expert codes, their row scales, the routing record
+  a.w8 = moe(d) ? take(im.e8_total) : 0;
+  a.esc = moe(d) ? take(im.sc_total * 4) : 0;
+  a.routes = moe(d) ? take((size_t)d.max_ctx * d.n_layers * d.top_k * 4) : 0;
   a.gains = take(((size_t)d.n_layers * 2 + 1) * D * 4);
   a.rope = take((size_t)d.max_ctx * (d.head_dim / 2) * 2 * 4);
   a.kv = take((size_t)d.n_layers * 2 * hkv * d.max_ctx * d.head_dim * 2);
@@ -351,7 +432,8 @@ Arena arena_layout(const dec_model_desc& d, int G) {
   a.att_o = take(B * q * 4);
   a.part = take(part_rows * d.head_dim * 4);
   a.pml = take(part_rows * 2 * 4);
-  a.act = take(B * d.d_ffn * 4);
+  // the MLP's hidden vector: d_ffn, or top_k experts' d_ffn each
+  a.act = take(B * d.d_ffn * (moe(d) ? d.top_k : 1) * 4);
   a.logits = take(B * d.lm_vocab * 4);
   // argmax partials: [G] at batch 1, [G][kMaxBatch] for the batched kernel
   const size_t Bk = B > 1 ? (size_t)kMaxBatch : 1;
@@ -444,13 +526,13 @@ int launch(dec_handle* h, int pos0, int n_tok, int tok_src, int lm_last_only, in
       for (int k = 0; k < nph; ++k) {
         A.phase_begin = i * ppt + k;
         A.phase_end = A.phase_begin + 1;
-        HIPCHK(h, &h->err, (hipError_t)kernel_launch_plain(h->dP, A, h->grid, h->desc.batch, h->desc.head_dim, h->stream));
+        HIPCHK(h, &h->err, (hipError_t)kernel_launch_plain(h->dP, A, h->grid, kernel_kind(h->desc), h->desc.head_dim, h->stream));
       }
     }
     return DEC_OK;
   }
   A.bar_base = h->bar_done;
-  HIPCHK(h, &h->err, (hipError_t)kernel_launch_resident(h->dP, A, h->grid, h->desc.batch, h->desc.head_dim, h->stream));
+  HIPCHK(h, &h->err, (hipError_t)kernel_launch_resident(h->dP, A, h->grid, kernel_kind(h->desc), h->desc.head_dim, h->stream));
   h->bar_done += launch_barriers(h->desc.n_layers, n_tok, lm_last_only);
   return DEC_OK;
 }
@@ -581,7 +663,7 @@ int srv_start(dec_handle* h) {
   if (A.srv_epoch == 0) A.srv_epoch = h->srv_epoch = 1;   // 0 would match the zeroed slots
   A.idle_ticks = h->srv_idle_ticks;
   A.bar_base = h->bar_done;
-  HIPCHK(h, &h->err, (hipError_t)kernel_launch_resident(h->dP, A, h->grid, h->desc.batch, h->desc.head_dim, h->stream));
+  HIPCHK(h, &h->err, (hipError_t)kernel_launch_resident(h->dP, A, h->grid, kernel_kind(h->desc), h->desc.head_dim, h->stream));
   h->srv_on = true;
   h->srv_posted = 0;
   return DEC_OK;
@@ -728,16 +810,22 @@ int upload_weights(dec_handle* h, const dec_weights_src* src) {
   uint16_t* dev_w2 = reinterpret_cast<uint16_t*>(static_cast<char*>(h->base) + h->ar.w2);
   std::vector<uint16_t> stage2;
   std::vector<float> g1(3 * (size_t)d.d_model);
+  // mixture of experts: one layer's expert codes and scales
+  std::vector<uint8_t> stage8(im1.e8_stride);
+  std::vector<float> stagesc(im1.sc_stride);
+  char* dev_w8 = static_cast<char*>(h->base) + h->ar.w8;
+  char* dev_sc = static_cast<char*>(h->base) + h->ar.esc;
+  const int per = per_layer(d);
   for (int l = 0; l < d.n_layers && rc == DEC_OK; ++l) {
     stage.assign(chunk_elems, 0);
     if (bp) stage2.assign(im12.layer_stride, 0);
-    for (int kind = 0; kind < 9; ++kind) {
-      const int idx = 1 + 9 * l + kind;
+    for (int kind = 0; kind < per; ++kind) {
+      const int idx = 1 + per * l + kind;
       const uint16_t* t = fetch(idx, rowbuf);
       if (!t) { rc = fail(&h->err, DEC_ERR_WEIGHTS, "cannot read tensor %d from the weight file", idx); break; }
       size_t R, C;
       tensor_shape(d, idx, &R, &C);
-      place_tensor(one, im1, 1 + kind, t, 0, R, stage.data(), g1.data());
+      place_tensor(one, im1, 1 + kind, t, 0, R, stage.data(), g1.data(), stage8.data(), stagesc.data());
       if (bp) place_tensor(one2, im12, 1 + kind, t, 0, R, stage2.data(), g1.data());
     }
     if (rc != DEC_OK) break;
@@ -745,6 +833,11 @@ int upload_weights(dec_handle* h, const dec_weights_src* src) {
     hipError_t e = hipMemcpy(dev_w + (size_t)l * local.layer_stride, stage.data(), local.layer_stride * 2, hipMemcpyHostToDevice);
     if (e == hipSuccess && bp)
       e = hipMemcpy(dev_w2 + (size_t)l * im2.layer_stride, stage2.data(), im2.layer_stride * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess && moe(d)) {
+      e = hipMemcpy(dev_w8 + (size_t)l * local.e8_stride, stage8.data(), local.e8_stride, hipMemcpyHostToDevice);
+      if (e == hipSuccess)
+        e = hipMemcpy(dev_sc + (size_t)l * local.sc_stride * 4, stagesc.data(), local.sc_stride * 4, hipMemcpyHostToDevice);
+    }
     if (e != hipSuccess) rc = hip_fail(h, &h->err, e, "hipMemcpy(weights)");
   }
   // embedding, final gain, LM head: row-major ones are copied as they are
@@ -809,6 +902,7 @@ int dec_packed_bytes(const dec_model_desc* desc, size_t* out_bytes) {
   if (!out_bytes) return fail(nullptr, DEC_ERR_INVALID_ARG, "out_bytes is NULL");
   int rc = check_desc_impl(desc, nullptr);
   if (rc) return rc;
+  if (moe(*desc)) return fail(nullptr, DEC_ERR_UNSUPPORTED, "the packed fp16 image is for dense models");
   *out_bytes = image_layout(*desc).total * 2;
   return DEC_OK;
 }
@@ -816,6 +910,7 @@ int dec_packed_bytes(const dec_model_desc* desc, size_t* out_bytes) {
 int dec_pack(const dec_model_desc* desc, const uint16_t* const* host_tensors, int32_t n_tensors, void* dst, size_t dst_bytes) {
   int rc = check_desc_impl(desc, nullptr);
   if (rc) return rc;
+  if (moe(*desc)) return fail(nullptr, DEC_ERR_UNSUPPORTED, "the packed fp16 image is for dense models");
   if (!host_tensors || !dst) return fail(nullptr, DEC_ERR_INVALID_ARG, "NULL tensor list or destination");
   if (n_tensors != n_tensors_for(*desc))
     return fail(nullptr, DEC_ERR_WEIGHTS, "expected %d tensors, got %d", n_tensors_for(*desc), n_tensors);
@@ -860,6 +955,10 @@ int init_impl(const dec_model_desc* desc, const dec_weights_src* weights, const 
   if (!weights) return fail(nullptr, DEC_ERR_INVALID_ARG, "weights is NULL");
   if ((weights->path == nullptr) == (weights->host_tensors == nullptr))
     return fail(nullptr, DEC_ERR_INVALID_ARG, "exactly one of weights->path and weights->host_tensors must be set");
+  if (moe(*desc) && weights->path)
+    return fail(nullptr, DEC_ERR_UNSUPPORTED, "a mixture-of-experts model comes from host tensors, not a DECW file");
+  if (moe(*desc) && noalloc)
+    return fail(nullptr, DEC_ERR_UNSUPPORTED, "a mixture-of-experts model is not served by dec_init_noalloc");
   if (weights->host_tensors) {
     if (weights->n_tensors != n_tensors_for(*desc))
       return fail(nullptr, DEC_ERR_WEIGHTS, "expected %d tensors, got %d", n_tensors_for(*desc), weights->n_tensors);
@@ -882,6 +981,9 @@ int init_impl(const dec_model_desc* desc, const dec_weights_src* weights, const 
   if (o.watchdog_us < 0) return fail(nullptr, DEC_ERR_INVALID_ARG, "watchdog_us must be >= 0");
   if (o.debug_flags & ~(DEC_DEBUG_MULTILAUNCH | DEC_DEBUG_TRACE | DEC_DEBUG_FENCED | DEC_DEBUG_STRESS))
     return fail(nullptr, DEC_ERR_INVALID_ARG, "unknown debug flags 0x%x", o.debug_flags);
+  if (moe(*desc) && (o.debug_flags & DEC_DEBUG_MULTILAUNCH))
+    return fail(nullptr, DEC_ERR_UNSUPPORTED, "a mixture-of-experts model keeps its routing on chip between phases: "
+                "not with DEC_DEBUG_MULTILAUNCH");
   if ((o.debug_flags & DEC_DEBUG_STRESS) && (o.debug_flags & DEC_DEBUG_MULTILAUNCH))
     return fail(nullptr, DEC_ERR_INVALID_ARG, "DEC_DEBUG_STRESS needs the resident kernel (not DEC_DEBUG_MULTILAUNCH)");
   if (o.serve_idle_us < 0 || o.serve_idle_us > 10000000)
@@ -928,7 +1030,7 @@ int init_impl(const dec_model_desc* desc, const dec_weights_src* weights, const 
   if (e == hipSuccess && matrix_prefill(*desc)) e = (hipError_t)mp_prepare();
   if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipFuncSetAttribute"); return bail(DEC_ERR_DEVICE); }
   int per_cu = 0;
-  e = (hipError_t)kernel_blocks_per_cu(desc->batch, desc->head_dim, &per_cu);
+  e = (hipError_t)kernel_blocks_per_cu(kernel_kind(*desc), desc->head_dim, &per_cu);
   if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"); return bail(DEC_ERR_DEVICE); }
   if (per_cu < 1 || h->grid > per_cu * cus) {
     fail(&h->err, DEC_ERR_UNSUPPORTED, "grid %d exceeds co-resident capacity %d x %d", h->grid, per_cu, cus);
@@ -956,6 +1058,21 @@ int init_impl(const dec_model_desc* desc, const dec_weights_src* weights, const 
     };
     long long need_out = mb * std::max({rows_wg(3 * q), rows_wg(desc->d_model), rows_wg(2LL * desc->d_ffn),
                                         rows_wg(desc->lm_vocab)});
+    if (moe(*desc)) {
+      // the router's logits, then the workgroup's gate/up row pairs of its
+      // expert slot (every slot has at least h->grid / top_k workgroups)
+      if (h->grid < desc->top_k) {
+        fail(&h->err, DEC_ERR_UNSUPPORTED, "grid %d is smaller than top_k", h->grid);
+        return bail(DEC_ERR_UNSUPPORTED);
+      }
+      const long long wg_slot = h->grid / desc->top_k;
+      need_out = std::max(need_out, (long long)kMoeOutPairs + 2 * ((desc->d_ffn + wg_slot - 1) / wg_slot));
+      if ((long long)desc->top_k * rows_wg(desc->d_model) > kMoeScaleFloats) {
+        fail(&h->err, DEC_ERR_UNSUPPORTED, "grid %d too small for this model (a workgroup would stage %lld down-row "
+             "scales)", h->grid, (long long)desc->top_k * rows_wg(desc->d_model));
+        return bail(DEC_ERR_UNSUPPORTED);
+      }
+    }
     long long need_own = mb * rows_wg(desc->d_model);
     if (batched_prefill(*desc)) {
       // the batched prefill runs the tiled kernel with kMaxBatch columns
@@ -1051,6 +1168,17 @@ int init_impl(const dec_model_desc* desc, const dec_weights_src* weights, const 
   const double ticks = wd_us * wall_khz / 1000.0;
   Params& P = h->P;
   P.L = desc->n_layers; P.d = desc->d_model; P.H = desc->n_heads; P.hd = desc->head_dim; P.F = desc->d_ffn;
+  P.E = desc->n_experts; P.topk = desc->top_k; P.Fe = desc->d_ffn;
+  if (moe(*desc)) {
+    P.F = desc->top_k * desc->d_ffn;   // the down product's input: every chosen expert's hidden vector
+    P.w8 = reinterpret_cast<const uint8_t*>(b + h->ar.w8);
+    P.e8_stride = h->im.e8_stride; P.e8_d = h->im.e8_d;
+    P.esc = reinterpret_cast<const float*>(b + h->ar.esc);
+    P.sc_stride = h->im.sc_stride; P.sc_d = h->im.sc_d;
+    P.routes = reinterpret_cast<int32_t*>(b + h->ar.routes);
+    e = hipMemset(P.routes, 0xFF, (size_t)desc->max_ctx * desc->n_layers * desc->top_k * 4);
+    if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemset(routes)"); return bail(DEC_ERR_DEVICE); }
+  }
   P.V = desc->vocab; P.Vlm = desc->lm_vocab; P.max_ctx = desc->max_ctx; P.q = desc->n_heads * desc->head_dim;
   P.eps = desc->rms_eps;
   P.w = reinterpret_cast<const uint16_t*>(b + h->ar.w);
@@ -1275,6 +1403,10 @@ int dec_reset(dec_handle* h) {
     h->bar_done = 0;
     h->broken = false;
   }
+  if (moe(h->desc)) {
+    e = hipMemset(h->P.routes, 0xFF, (size_t)h->desc.max_ctx * h->desc.n_layers * h->desc.top_k * 4);
+    if (e != hipSuccess) return fail(&h->err, DEC_ERR_DEVICE, "hipMemset(routes) failed: %s", hipGetErrorString(e));
+  }
   h->pos = 0;
   h->has_prev_tok = false;
   return DEC_OK;
@@ -1298,6 +1430,21 @@ int dec_read_kv(dec_handle* h, int32_t layer, int32_t seq, int32_t n_pos, uint16
       HIPCHK(h, &h->err, hipMemcpy(dst + (size_t)hh * n_pos * d.head_dim, src, (size_t)n_pos * d.head_dim * 2, hipMemcpyDeviceToHost));
     }
   }
+  return DEC_OK;
+}
+
+int dec_read_routes(dec_handle* h, int32_t pos0, int32_t n_pos, int32_t* out_routes) {
+  if (!h) return fail(nullptr, DEC_ERR_INVALID_ARG, "handle is NULL");
+  const dec_model_desc& d = h->desc;
+  if (!moe(d)) return fail(&h->err, DEC_ERR_STATE, "a dense model has no routing");
+  if (pos0 < 0 || n_pos < 0 || (long long)pos0 + n_pos > d.max_ctx || (n_pos > 0 && !out_routes))
+    return fail(&h->err, DEC_ERR_INVALID_ARG, "positions [%d, %d) outside [0, max_ctx) or NULL output", pos0, pos0 + n_pos);
+  if (int rc0 = srv_stop(h)) return rc0;
+  HIPCHK(h, &h->err, hipStreamSynchronize(h->stream));
+  const size_t per_pos = (size_t)d.n_layers * d.top_k;
+  if (n_pos > 0)
+    HIPCHK(h, &h->err, hipMemcpy(out_routes, h->P.routes + (size_t)pos0 * per_pos, (size_t)n_pos * per_pos * 4,
+                                 hipMemcpyDeviceToHost));
   return DEC_OK;
 }
 

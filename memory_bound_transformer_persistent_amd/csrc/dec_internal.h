@@ -26,6 +26,14 @@ constexpr int kOwnFloats = 256;             // LDS: a workgroup's rows of the re
 // inputs of every sequence sit in LDS as fp16, side by side, so one pass over
 // the weights serves all of them.  Limits that keep them in LDS:
 constexpr int kMaxBatch = 8;
+// mixture of experts: limits, the kernel-kind value of the batch-1
+// mixture-of-experts kernel, and where a workgroup's gate/up results start
+// in its LDS result buffer (the router's logits come first)
+constexpr int kMoeMaxExperts = 64;
+constexpr int kMoeMaxTopK = 8;
+constexpr int kMoeKernel = 0;
+constexpr int kMoeOutPairs = 64;
+constexpr int kMoeScaleFloats = 512;   // LDS for the down phase's row scales of every chosen expert
 constexpr int kBatchSpanD = 2560;           // padded d_model (input of QKV, GU, LM; staged in fp32 too)
 constexpr int kBatchSpanK = 7680;           // padded d_ffn and n_heads*head_dim
 // The batched kernel multiplies weights by the inputs with MFMA
@@ -131,6 +139,13 @@ struct Params {
   Mailbox* mail;              // decode server mailbox (device address of host-pinned memory) or null
   float* lg_sys;              // decode server logits [B][Vlm] (device address of host-pinned memory) or null
   int32_t* srv_slot;          // decode server request slots [kSrvCopies][kMailRing][kReqWords]
+  // mixture of experts (E > 0; F above is then topk * Fe, the down product's input)
+  int E, topk, Fe;            // experts per layer, experts per token, expert width
+  const uint8_t* w8;          // expert codes (E4M3): per layer Wgu8 [E][Fe][2][d], then Wd8 [E][d][Fe] at e8_d
+  size_t e8_stride, e8_d;     // bytes between layers; offset of Wd8 inside a layer
+  const float* esc;           // expert row scales: per layer [E][Fe][2] (gate, up), then [E][d] at sc_d
+  size_t sc_stride, sc_d;     // floats between layers; offset of the down scales inside a layer
+  int32_t* routes;            // chosen experts [max_ctx][L][topk]
 };
 
 struct Launch {
@@ -263,10 +278,12 @@ int mp_launch_argmax(const float* logits, int V, int* tok_out, int* tok_cur, voi
 // kernel built for one sequence or for up to kMaxBatch and hd the one built
 // for that head dimension (8, 16, 32, 64 or 128); each returns a hipError_t
 // value (0 = success; hipErrorInvalidValue for another head dimension).
+// `kind` picks the resident kernel: the batch it is built for (1, or up to
+// kMaxBatch for the batched one) or kMoeKernel (batch 1, mixture of experts)
 int kernel_prepare();                                            // raise the dynamic-LDS limit
-int kernel_blocks_per_cu(int batch, int hd, int* out);           // co-resident workgroups per CU
-int kernel_launch_resident(const Params* P, const Launch& A, int grid, int batch, int hd, void* stream);  // cooperative
-int kernel_launch_plain(const Params* P, const Launch& A, int grid, int batch, int hd, void* stream);     // ordinary
+int kernel_blocks_per_cu(int kind, int hd, int* out);            // co-resident workgroups per CU
+int kernel_launch_resident(const Params* P, const Launch& A, int grid, int kind, int hd, void* stream);  // cooperative
+int kernel_launch_plain(const Params* P, const Launch& A, int grid, int kind, int hd, void* stream);     // ordinary
 // Stream-ceiling read of n16 16-byte words at src on the null stream; out
 // holds grid * kThreads words.
 int kernel_stream_read(const void* src, uint64_t n16, uint32_t* out, int grid);

@@ -68,6 +68,13 @@ constexpr int kAuxFloats = 2048;
 // merge after S1) share offset 0: their lifetimes do not overlap
 constexpr int kAuxPart = 0;
 static_assert(kAuxPart + kWaves * (128 + 2) <= kAuxFloats, "aux LDS");
+// a mixture of experts' routing of the current layer, 16 words per wave
+// from kAuxRoute (past the rotary rows and the attention partials): the
+// top_k experts (ints), then their weights from word 8.  Each wave forms its
+// own copy in the GU phase; wave 0's is read until the down phase.
+constexpr int kAuxRoute = 1280;
+static_assert(kAuxRoute >= 1024 && kAuxRoute >= kAuxPart + kWaves * (128 + 2) && kAuxRoute + 16 * kWaves <= 1536,
+              "aux LDS");
 
 // LDS map (floats) for a kernel built for up to MB sequences:
 // input region | out | xown | red | scales | si | aux | gains | phase tables |
@@ -297,6 +304,14 @@ __device__ __forceinline__ GemvWork work_of(const Params& P, int ph, int l) {
     case PH_LM: g.W = P.w + P.off_lm; g.rows = P.Vlm; g.K = P.d; npairs = P.Vlm / 2; break;
     default: return g;
   }
+  if (P.E > 0 && ph == PH_GU) {
+    // mixture of experts: the GU phase's ordinary stream is the router
+    // [E, d], all of it in every workgroup (the experts follow it)
+    g.rows = P.E;
+    g.p0 = 0;
+    g.p1 = P.E / 2;
+    return g;
+  }
   // batch 1 with few heads (at most 1/32 of the grid, e.g. one lane of a
   // tensor-parallel split): the workgroups that take attention (the first H)
   // get no QKV rows, so they reach the attention phase early and its K/V
@@ -379,6 +394,9 @@ __device__ __forceinline__ int phase_k(const Params& P, int ph) {
 // into LDS (no divisions on the phase path).  Per type ph: the workgroup's
 // pairs [p0, p1) (kept by wave 0) and, per streamer, its share of units.
 enum TabField { T_LEFT, T_OFF, T_COL, T_NPC, T_ROWB, T_WRAP, T_TAIL, T_T0, T_NBYTES, T_PAD };
+// wave 0's table: (p0, p1) per phase type in ints 0..11; a mixture of
+// experts' slot, q0, q1 (moe_slot) from int kTabMoeSlot on
+constexpr int kTabMoeSlot = 12;
 
 __device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -413,15 +431,31 @@ __device__ __forceinline__ void fill_tables_tiled(const Params& P, int wave, int
   e[T_PAD] = (kTilesInFlight - (u1 - u0) % kTilesInFlight) % kTilesInFlight;
 }
 
+// Mixture of experts: the expert slot of workgroup b (slot floor(b top_k /
+// G), so every slot has G / top_k workgroups or one more) and its gate/up row
+// pairs [q0, q1) of the slot's expert (an even split of Fe over the slot's
+// workgroups).
+__device__ __forceinline__ void moe_slot(const Params& P, int b, int G, int& slot, int& q0, int& q1) {
+  slot = (int)((long long)b * P.topk / G);
+  const int first = (int)(((long long)slot * G + P.topk - 1) / P.topk);
+  const int next = (int)(((long long)(slot + 1) * G + P.topk - 1) / P.topk);
+  split(P.Fe, b - first, next - first, q0, q1);
+}
+
 __device__ __forceinline__ void fill_tables(const Params& P, int wave, int* tab_wg, int* tab) {
   const int lane = threadIdx.x & 63;
   if (lane >= 6 || lane == PH_ATTN) return;
-  const GemvWork w = work_of(P, lane, 0);
+  GemvWork w = work_of(P, lane, 0);
   if (wave == 0) {
     tab_wg[2 * lane] = w.p0;
     tab_wg[2 * lane + 1] = w.p1;
+    if (P.E > 0 && lane == 0) moe_slot(P, blockIdx.x, gridDim.x, tab_wg[kTabMoeSlot], tab_wg[kTabMoeSlot + 1],
+                                       tab_wg[kTabMoeSlot + 2]);
     return;
   }
+  // mixture of experts: the down phase's rows are streamed once the routing
+  // is known (moe_stream), not by the cursor
+  if (P.E > 0 && lane == PH_DOWN) w.p1 = w.p0;
   int u0, u1;
   streamer_units(w, wave, u0, u1);
   const uint32_t npc = (uint32_t)gemv_npc(w.K), rowb = (uint32_t)w.K * 2u;
@@ -729,8 +763,12 @@ __device__ __forceinline__ void w0_poison(const Params& P, int ph, int l, const 
     }
   }
   if (ph == PH_QKV) {
-    // this workgroup's SwiGLU outputs, read by the last DOWN input pull; GU publishes them next
-    const int p0 = rfl(tab_wg[2 * PH_GU]), p1 = rfl(tab_wg[2 * PH_GU + 1]);
+    // this workgroup's SwiGLU outputs, read by the last DOWN input pull; GU
+    // publishes them next (a mixture of experts: its slot's part)
+    const bool moe = MB == 1 && P.E > 0;
+    const int base = moe ? rfl(tab_wg[kTabMoeSlot]) * P.Fe : 0;
+    const int p0 = base + rfl(tab_wg[moe ? kTabMoeSlot + 1 : 2 * PH_GU]);
+    const int p1 = base + rfl(tab_wg[moe ? kTabMoeSlot + 2 : 2 * PH_GU + 1]);
     for (int b = 0; b < B; ++b)
       for (int t = p0 + lane; t < p1; t += 64) {
         if constexpr (MB == 1) st_coh(reinterpret_cast<uint32_t*>(P.act + t), nan32);
@@ -780,10 +818,11 @@ __device__ __forceinline__ void w0_poison(const Params& P, int ph, int l, const 
 
 // dst[0..gemv_span(n) elements of esize bytes) <- src[0..n) by LDS DMA
 // (coherent when coh; zero past n).  Issues only; the caller waits.
-__device__ __forceinline__ void w0_dma_vec(void* dst, const void* src, int n, int esize, bool coh) {
+// extra: that many more elements of zero fill past n (rounded up to 512)
+__device__ __forceinline__ void w0_dma_vec(void* dst, const void* src, int n, int esize, bool coh, int extra = 0) {
   const int lane = threadIdx.x & 63;
   const rsrc_t r = make_rsrc(src, (uint32_t)(n * esize));
-  const int span_bytes = gemv_span(n) * esize;
+  const int span_bytes = gemv_span(n + extra) * esize;
   for (int o = 0; o < span_bytes; o += 1024) {
     void* base = static_cast<char*>(dst) + o;
     if (coh) dma16_coh(r, base, (uint32_t)(o + 16 * lane));
@@ -1171,13 +1210,29 @@ __device__ __forceinline__ void w0_merge_wg(const Params& P, int pos, int pos_en
 // the rotary embedding rotates: q is rotated, scaled by 1/sqrt(hd) and
 // stored for attention; k is rotated and v taken as it is, both rounded to
 // fp16 and appended to the KV cache at (layer l, position pos).
-template <int MB>
+template <int MB, bool MOE = false>
 __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l, int pos, int pos_end,
                                                  const int* tab_wg, int lg_mode, const float* scl,
                                                  const float* out, float* xown, const float* rope_lds,
                                                  const float* gs_next) {
   const int lane = threadIdx.x & 63, B = P.B;
   if (!is_gemv(ph)) return;
+  if (MOE && ph == PH_GU) {
+    // mixture of experts: this workgroup's row pairs j of its slot's expert
+    // e, silu(gate) * up with the row scales, times the expert's routing
+    // weight, into the slot's part of the hidden vector
+    const int slot = rfl(tab_wg[kTabMoeSlot]), q0 = rfl(tab_wg[kTabMoeSlot + 1]), nq = rfl(tab_wg[kTabMoeSlot + 2]) - q0;
+    // the routing wave 0 kept in LDS (aux, which rope_lds points at)
+    const int e = reinterpret_cast<const int*>(rope_lds)[kAuxRoute + slot];
+    const float w = rope_lds[kAuxRoute + kMoeMaxTopK + slot];
+    const float* sc = P.esc + (size_t)l * P.sc_stride + (size_t)2 * ((size_t)e * P.Fe + q0);
+    for (int t = lane; t < nq; t += 64) {
+      const float gt = out[kMoeOutPairs + 2 * t] * scl[0] * ldg(sc + 2 * t);
+      const float up = out[kMoeOutPairs + 2 * t + 1] * scl[0] * ldg(sc + 2 * t + 1);
+      st_coh(P.act + (size_t)slot * P.Fe + q0 + t, gt / (1.0f + expf(-gt)) * up * w);
+    }
+    return;
+  }
   const int p0 = rfl(tab_wg[2 * ph]);
   const int n = rfl(tab_wg[2 * ph + 1]) - p0;
   const int own = kOwnFloats / MB;
@@ -1605,7 +1660,8 @@ __device__ __forceinline__ bool streamer_attention(const Params& P, const Launch
   const int pos = step_pos(P, A, id.i);
   // (not with few heads: their workgroups skip the QKV rows and the gap is short)
   if constexpr (MB == 1)
-    if (P.H > (int)gridDim.x / 32 && (int)blockIdx.x / wg_per_head(P, pos) >= P.H) warm_gu(P, tab, id.l, sink);
+    if (P.E == 0 && P.H > (int)gridDim.x / 32 && (int)blockIdx.x / wg_per_head(P, pos) >= P.H)
+      warm_gu(P, tab, id.l, sink);
   bool ok;
   ok = attention_wg<HD, MB>(P, id.l, pos, A.pos_end, wave, wg_per_head(P, pos), wait_s, aux + kAuxPart);
   if (DEC_COLD(!ok)) return false;
@@ -1615,15 +1671,180 @@ __device__ __forceinline__ bool streamer_attention(const Params& P, const Launch
   return true;
 }
 
+// ---------------------------------------------------------------------------
+// mixture of experts (batch 1)
+// ---------------------------------------------------------------------------
+// A layer's MLP is top_k of E SwiGLU experts whose rows are FP8 E4M3 codes
+// with one fp32 scale each: at batch 1 only the chosen experts' bytes are
+// read, which is what makes large mixture-of-experts models fast at batch 1
+// (page 標準GPUによるリアルタイムLLM推論, section Hackerたちの意見; page
+// 「ソフトウェア・ファースト」戦略でGPUの限界を突破…, section 今後のマイルストーンと課題).
+// The GU phase's ordinary weight stream is the fp16 router [E, d], all of it
+// in every workgroup, so its first blocks are prefetched across the barrier
+// like any phase's.  Then every wave takes the top_k experts from the
+// router's logits in LDS (moe_route), and the streamers read the chosen
+// experts' rows (moe_stream): in GU the workgroups form top_k slots that
+// split their expert's gate/up row pairs; in DOWN each workgroup keeps its
+// dense share of the d output rows and reads, per row pair, the top_k
+// experts' rows in turn.  Expert loads start once the routing is known, so
+// they are not prefetched across the barrier.
+
+// 16 E4M3 codes of each of two rows (one 16-byte load per row) times the
+// same 16 fp32 inputs; fp32 accumulate.  The hardware conversion decodes
+// OCP E4M3 exactly.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void dot16_e4m3x2(u32x4 w0, u32x4 w1, const float* x, float& a0, float& a1) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 xv = *reinterpret_cast<const f32x4*>(x + 4 * i);
+    const uint32_t c0 = w0[i], c1 = w1[i];
+    const f32x2 l0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c0, false), h0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c0, true);
+    const f32x2 l1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c1, false), h1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c1, true);
+    const float x0 = xv[0], x1 = xv[1], x2 = xv[2], x3 = xv[3];
+    a0 = __builtin_fmaf(l0[0], x0, a0);
+    a0 = __builtin_fmaf(l0[1], x1, a0);
+    a0 = __builtin_fmaf(h0[0], x2, a0);
+    a0 = __builtin_fmaf(h0[1], x3, a0);
+    a1 = __builtin_fmaf(l1[0], x0, a1);
+    a1 = __builtin_fmaf(l1[1], x1, a1);
+    a1 = __builtin_fmaf(h1[0], x2, a1);
+    a1 = __builtin_fmaf(h1[1], x3, a1);
+  }
+}
+
+// Every wave, into its routing words rt (LDS, 16 per wave): the top_k
+// experts of the router's row sums out[0, E) -- times the phase's norm
+// scale, formed here from the waves' shares of sum(x^2) in the order wave 0
+// forms it -- largest logit first, the lower index first on equal logits,
+// then from word 8 their weights, the softmax of the chosen logits.
+__device__ __forceinline__ void moe_route(const Params& P, const float* out, const float* red, float* rt) {
+  const int lane = threadIdx.x & 63;
+  float ss = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) ss += red[w];
+  const float scale = 1.0f / sqrtf(ss / (float)P.d + P.eps);
+  float v = lane < P.E ? out[lane] * scale : -INFINITY;
+  float mine = 0.f;   // lane s: the s-th chosen logit
+  for (int s = 0; s < P.topk; ++s) {
+    float best = v;
+    int bi = lane;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(best, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+    }
+    bi = min(max(rfl(bi), 0), P.E - 1);
+    if (lane == s) {
+      reinterpret_cast<int*>(rt)[s] = bi;
+      mine = best;
+    }
+    if (lane == bi) v = -INFINITY;
+  }
+  const float top = readlane(mine, 0);
+  const float ex = lane < P.topk ? expf(mine - top) : 0.f;
+  const float den = wave_sum(ex);
+  if (lane < P.topk) rt[kMoeMaxTopK + lane] = ex / den;
+}
+
+// LDS of the down phase's row scales: [slot][2 np] for the workgroup's np
+// output row pairs (wave 0 fills it with the phase input; aux floats from
+// kAuxMoe on, past the rotary rows and the attention partials)
+constexpr int kAuxMoe = 1536;
+static_assert(kAuxMoe + kMoeScaleFloats <= kAuxFloats, "aux LDS");
+
+// Streamer s's share of a routed phase -- GU: gate/up row pairs [q0, q1) of
+// the slot's expert; DOWN: every chosen expert's rows of the workgroup's
+// output pairs -- with kUnitsInFlight units (a 1 KB piece of each of a row
+// pair's two rows) in flight in its own registers.  Row sums go to out by
+// ds_add, at most two contributors per row pair (streamer_range).  A down
+// row's sum over one expert is scaled by that row's scale before the next
+// expert's is added.
+template <bool DOWN>
+__device__ __forceinline__ void moe_stream(const Params& P, int l, int s, const int* tab_wg, int eslot,
+                                           const float* aux, const float* xs, float* out) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t lane16 = (uint32_t)lane * 16u;
+  const int d = P.d, Fe = P.Fe;
+  const int p0 = rfl(tab_wg[DOWN ? 2 * PH_DOWN : kTabMoeSlot + 1]);
+  const int p1 = rfl(tab_wg[DOWN ? 2 * PH_DOWN + 1 : kTabMoeSlot + 2]);
+  // DOWN: the layer's experts (wave 0's routing words) and the row scales
+  // wave 0 staged with the phase input
+  const int* sel = reinterpret_cast<const int*>(aux) + kAuxRoute;
+  const float* sc_lds = aux + kAuxMoe;
+  const int K = DOWN ? Fe : d;                            // a row's codes inside one expert
+  const int npc = (K + 1023) >> 10;                       // 1 KB pieces per expert row
+  const int tail = (K - 1024 * (npc - 1)) >> 4;           // lanes with codes in the last piece
+  const int nsl = DOWN ? P.topk : 1;                      // experts per row pair
+  const int per = nsl * npc;
+  int u0, u1;
+  streamer_range((p1 - p0) * per, per, kStreamers, s, u0, u1);
+  const int n = u1 - u0;
+  if (n <= 0) return;
+  const rsrc_t r = make_rsrc(P.w8 + (size_t)rfl(l) * P.e8_stride, (uint32_t)P.e8_stride);
+  const uint32_t row_bytes = (uint32_t)K;
+  // issue and consume cursors: row pair t (from p0), expert segment sl, piece c
+  int it = u0 / per, isl = (u0 - it * per) / npc, ic = u0 - it * per - isl * npc;
+  int ct = it, csl = isl, cc = ic;
+  u32x4 b[2 * kUnitsInFlight];
+#define MOE_ISSUE(k)                                                                                          \
+  {                                                                                                           \
+    const bool live = issued < n;                                                                             \
+    const int e = DOWN ? rfl(sel[isl]) : eslot;                                                               \
+    const uint32_t row0 = DOWN ? (uint32_t)P.e8_d + (uint32_t)(e * d + 2 * (p0 + it)) * row_bytes              \
+                               : (uint32_t)((e * Fe + p0 + it) * 2) * row_bytes;                              \
+    const bool ok = live && (ic + 1 < npc || lane < tail);                                                    \
+    const uint32_t o = row0 + 1024u * (uint32_t)ic + lane16;                                                  \
+    b[2 * (k)] = ld_nt(r, ok ? o : kOOB);                                                                     \
+    b[2 * (k) + 1] = ld_nt(r, ok ? o + row_bytes : kOOB + 16u);                                               \
+    ++issued;                                                                                                 \
+    if (++ic == npc) { ic = 0; if (++isl == nsl) { isl = 0; ++it; } }                                         \
+  }
+  int issued = 0;
+#pragma unroll
+  for (int k = 0; k < kUnitsInFlight; ++k) MOE_ISSUE(k)
+  float a0 = 0.f, a1 = 0.f, s0 = 0.f, s1 = 0.f;
+  const int ngroups = (n + kUnitsInFlight - 1) / kUnitsInFlight;
+  const int np = p1 - p0;
+  for (int grp = 0; grp < ngroups; ++grp) {
+#pragma unroll
+    for (int k = 0; k < kUnitsInFlight; ++k) {
+      wait_vm<kBlocksInFlight - 2>();
+      const int j = grp * kUnitsInFlight + k;
+      if (j < n) {
+        dot16_e4m3x2(b[2 * k], b[2 * k + 1], xs + (DOWN ? csl * Fe : 0) + 1024 * cc + 16 * lane, a0, a1);
+        const bool last = j == n - 1, seg_end = cc + 1 == npc;
+        if (DOWN && (seg_end || last)) {
+          s0 = __builtin_fmaf(a0, sc_lds[csl * 2 * np + 2 * ct], s0);
+          s1 = __builtin_fmaf(a1, sc_lds[csl * 2 * np + 2 * ct + 1], s1);
+          a0 = a1 = 0.f;
+        }
+        if ((seg_end && csl + 1 == nsl) || last) {
+          const float y0 = wave_sum(DOWN ? s0 : a0), y1 = wave_sum(DOWN ? s1 : a1);
+          if (lane == 0) {
+            lds_add(out + (DOWN ? 0 : kMoeOutPairs) + 2 * ct, y0);
+            lds_add(out + (DOWN ? 0 : kMoeOutPairs) + 2 * ct + 1, y1);
+          }
+          a0 = a1 = s0 = s1 = 0.f;
+        }
+        if (++cc == npc) { cc = 0; if (++csl == nsl) { csl = 0; ++ct; } }
+      }
+      MOE_ISSUE(k)
+    }
+  }
+#undef MOE_ISSUE
+  wait_vm0();   // the zero-reading loads past the share's end
+}
+
 // Streamer role (waves 1..7): kBlocksInFlight loads always in flight, in
 // stream order.  Every phase is a whole number of groups of kUnitsInFlight
 // units (zero-reading units pad it), so unit k of each group always sits in
 // register slot k: the steps below are unrolled over the slots and never
 // copy a register that a load is still filling.
-template <int HD>
+template <int HD, bool MOE>
 __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, int g0, int g1, const int* tab,
                                               float* xs, float* out, const float* gs, float* red, const int* si,
-                                              float* aux, float* sink) {
+                                              float* aux, float* sink, const int* tab_wg) {
   const int lane = threadIdx.x & 63;
   const uint32_t lane16 = (uint32_t)lane * 16u;
   Cursor cu;
@@ -1677,6 +1898,18 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
           ++u;
           issue_unit(cu, lane16, buf[2 * k], buf[2 * k + 1]);
         }
+      }
+    }
+    if constexpr (MOE) {
+      if (id.ph == PH_GU) {
+        __syncthreads();   // SR: the router's logits are in out[0, E)
+        const int w = rfl((int)(threadIdx.x >> 6));
+        float* rt = aux + kAuxRoute + 16 * w;
+        moe_route(P, out, red, rt);
+        moe_stream<false>(P, id.l, w, tab_wg, rfl(reinterpret_cast<const int*>(rt)[rfl(tab_wg[kTabMoeSlot])]), aux,
+                          xs, out);
+      } else if (id.ph == PH_DOWN) {
+        moe_stream<true>(P, id.l, rfl((int)(threadIdx.x >> 6)), tab_wg, 0, aux, xs, out);
       }
     }
     __syncthreads();   // S2
@@ -1773,7 +2006,7 @@ __device__ __forceinline__ void streamer_tiles(const Params& P, const Launch& A,
   wait_vm0();   // the zero-filled loads past the stream's end
 }
 
-template <int MB, int HD>
+template <int MB, int HD, bool MOE = false>
 __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   using M = Lds<MB>;
   extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -1805,7 +2038,8 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   wait_lgkm0();
   __syncthreads();   // every streamer's tables are in LDS
   if (wave > 0) {
-    if constexpr (MB == 1) streamer_role<HD>(P, A, g0, g1, tab, xs, out, gs, red, si, aux, smem + M::Sink);
+    if constexpr (MB == 1)
+      streamer_role<HD, MOE>(P, A, g0, g1, tab, xs, out, gs, red, si, aux, smem + M::Sink, tab_wg);
     else streamer_tiles<MB, HD>(P, A, g0, g1, tab, xs, out, slots + (wave - 1) * 2 * M::SlotN, gs, red, si, aux,
                                 plan, slots);
     return;
@@ -1854,14 +2088,19 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
           combine_all<MB>(prev_ph, plan, slots, out);
           __syncthreads();   // S2b
         }
-      w0_store_outputs<MB>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
-                           lg_mode(A, prev_i, cur_lg), scl, out, xown, aux, gs);
+      w0_store_outputs<MB, MOE>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
+                                lg_mode(A, prev_i, cur_lg), scl, out, xown, aux, gs);
     }
     if (MB == 1 && is_gemv(id.ph)) {
       // the batch-1 streamers add into out (ds_add); the batched kernel's
       // streamers and combine store every live element
       const int np = rfl(tab_wg[2 * id.ph + 1]) - rfl(tab_wg[2 * id.ph]);
       for (int t = lane; t < 2 * np * MB; t += 64) out[t] = 0.f;
+      if (MOE && id.ph == PH_GU) {
+        // and the expert's gate/up row pairs after the router's logits
+        const int nq = rfl(tab_wg[kTabMoeSlot + 2]) - rfl(tab_wg[kTabMoeSlot + 1]);
+        for (int t = lane; t < 2 * nq; t += 64) out[kMoeOutPairs + t] = 0.f;
+      }
     }
     const bool skip_bar = first || (id.ph == PH_QKV && id.l == 0 && have_tok);
     if (!skip_bar) {
@@ -1871,7 +2110,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       // server launch: the previous request's tokens have landed with this
       // arrival's wait; its completion can go out
       if (DEC_COLD(A.server) && blockIdx.x == 0) srv_flush_done(P, done_pending);
-      if constexpr (MB == 1)
+      if constexpr (MB == 1 && !MOE)
         if (id.ph == PH_O && P.H > (int)gridDim.x / 32 && (int)blockIdx.x / wg_per_head(P, pos) >= P.H)
           w0_warm_gu(P, tab_all, id.l, smem + M::Sink);
       if constexpr (MB > 1)
@@ -1943,12 +2182,24 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       have_tok = false;
     } else if (id.ph == PH_QKV || id.ph == PH_GU || id.ph == PH_LM) {
       ok = wait();
+      // (mixture of experts: zeros up to the next 1 KB piece of E4M3 codes)
       if constexpr (MB == 1)
-        if (ok) w0_dma_vec(xs, P.x, P.d, 4, true);
+        if (ok) w0_dma_vec(xs, P.x, P.d, 4, true, MOE ? 512 : 0);
     } else if (id.ph == PH_DOWN) {
       ok = wait();
       if constexpr (MB == 1)
-        if (ok) w0_dma_vec(xs, P.act, P.F, 4, true);
+        if (ok) w0_dma_vec(xs, P.act, P.F, 4, true, MOE ? 1024 : 0);
+      if constexpr (MOE) {
+        // the row scales of this workgroup's output pairs in every chosen
+        // expert, [slot][2 np], for the streamers
+        const int r0 = 2 * rfl(tab_wg[2 * PH_DOWN]), nr = 2 * rfl(tab_wg[2 * PH_DOWN + 1]) - r0;
+        const float* sd = P.esc + (size_t)id.l * P.sc_stride + P.sc_d;
+        const int* route = reinterpret_cast<const int*>(aux) + kAuxRoute;
+        for (int i = lane; i < P.topk * nr; i += 64) {
+          const int k = i / nr;
+          aux[kAuxMoe + i] = ldg(sd + (size_t)route[k] * P.d + r0 + (i - k * nr));
+        }
+      }
     } else if (id.ph == PH_O) {
       ok = wait();
       // the attention output of every head, merged in the attention phase
@@ -2013,6 +2264,16 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       }
       scl[lane] = s;
     }
+    if constexpr (MOE) {
+      if (id.ph == PH_GU) {
+        __syncthreads();   // SR: the router's logits are in out[0, E)
+        // wave 0's routing words stay in LDS for the publication and the
+        // down phase; workgroup 0 records the routing of the step's position
+        moe_route(P, out, red, aux + kAuxRoute);
+        if (blockIdx.x == 0 && lane < P.topk)
+          st_coh(P.routes + ((size_t)pos * P.L + id.l) * P.topk + lane, reinterpret_cast<const int*>(aux)[kAuxRoute + lane]);
+      }
+    }
     // server launch: read the next request ahead, while the streamers run --
     // workgroup 0 from the host early in the token, the others from their
     // device slot in the LM head, long after workgroup 0 has filled it
@@ -2032,8 +2293,8 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
         combine_all<MB>(prev_ph, plan, slots, out);
         __syncthreads();   // S2b
       }
-    w0_store_outputs<MB>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
-                         lg_mode(A, prev_i, cur_lg), scl, out, xown, aux, gs);
+    w0_store_outputs<MB, MOE>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
+                              lg_mode(A, prev_i, cur_lg), scl, out, xown, aux, gs);
   }
   if (DEC_COLD(A.server) && blockIdx.x == 0) srv_flush_done(P, done_pending);
   wait_vm0();
@@ -2050,6 +2311,10 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
   extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident_batch_hd##HD(                         \
       const Params* __restrict__ Pp, Launch A) {                                                            \
     dec_body<kMaxBatch, HD>(*Pp, A);                                                                        \
+  }                                                                                                         \
+  extern "C" __global__ __launch_bounds__(kThreads, 1) void dec_resident_moe_hd##HD(                           \
+      const Params* __restrict__ Pp, Launch A) {                                                            \
+    dec_body<1, HD, true>(*Pp, A);                                                                          \
   }
 DEC_KERNELS(8)
 DEC_KERNELS(16)
@@ -2060,8 +2325,18 @@ DEC_KERNELS(128)
 
 namespace {
 // The kernel for a batch size and head dimension; nullptr for an unsupported head dimension.
-const void* kernel_for(int batch, int hd) {
-  const bool b = batch > 1;
+const void* kernel_for(int kind, int hd) {
+  const bool b = kind > 1;
+  if (kind == kMoeKernel) {
+    switch (hd) {
+      case 8: return (const void*)dec_resident_moe_hd8;
+      case 16: return (const void*)dec_resident_moe_hd16;
+      case 32: return (const void*)dec_resident_moe_hd32;
+      case 64: return (const void*)dec_resident_moe_hd64;
+      case 128: return (const void*)dec_resident_moe_hd128;
+      default: return nullptr;
+    }
+  }
   switch (hd) {
     case 8: return b ? (const void*)dec_resident_batch_hd8 : (const void*)dec_resident_hd8;
     case 16: return b ? (const void*)dec_resident_batch_hd16 : (const void*)dec_resident_hd16;
@@ -2128,21 +2403,21 @@ int kernel_scratch(int device, void** out) {
 
 int kernel_prepare() {
   for (int hd = 8; hd <= 128; hd *= 2)
-    for (int batch = 1; batch <= kMaxBatch; batch += kMaxBatch - 1) {
-      const hipError_t e = hipFuncSetAttribute(kernel_for(batch, hd), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    for (int kind : {1, kMaxBatch, kMoeKernel}) {
+      const hipError_t e = hipFuncSetAttribute(kernel_for(kind, hd), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
       if (e != hipSuccess) return (int)e;
     }
   return (int)hipSuccess;
 }
 
-int kernel_blocks_per_cu(int batch, int hd, int* out) {
-  const void* k = kernel_for(batch, hd);
+int kernel_blocks_per_cu(int kind, int hd, int* out) {
+  const void* k = kernel_for(kind, hd);
   if (!k) return (int)hipErrorInvalidValue;
   return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(out, k, kThreads, kLdsBytes);
 }
 
-int kernel_launch_resident(const Params* P, const Launch& A, int grid, int batch, int hd, void* stream) {
-  const void* k = kernel_for(batch, hd);
+int kernel_launch_resident(const Params* P, const Launch& A, int grid, int kind, int hd, void* stream) {
+  const void* k = kernel_for(kind, hd);
   if (!k) return (int)hipErrorInvalidValue;
   const Params* p = P;
   Launch a = A;
@@ -2150,8 +2425,8 @@ int kernel_launch_resident(const Params* P, const Launch& A, int grid, int batch
   return (int)hipLaunchCooperativeKernel(k, dim3(grid), dim3(kThreads), args, kLdsBytes, static_cast<hipStream_t>(stream));
 }
 
-int kernel_launch_plain(const Params* P, const Launch& A, int grid, int batch, int hd, void* stream) {
-  const void* k = kernel_for(batch, hd);
+int kernel_launch_plain(const Params* P, const Launch& A, int grid, int kind, int hd, void* stream) {
+  const void* k = kernel_for(kind, hd);
   if (!k) return (int)hipErrorInvalidValue;
   const Params* p = P;
   Launch a = A;

@@ -142,7 +142,9 @@ def moe_ffn(w, l, xn, k, force=None):
 class OracleMoEDecoder:
     """Token-at-a-time MoE decoder with an fp16 KV cache, batch 1.
 
-    After each step: last_routes [L, k], last_weights [L, k], last_margins [L].
+    After each step: last_routes [L, k] (the experts used), last_weights
+    [L, k], last_margins [L] and last_natural [L, k] (the router's own choice,
+    which differs from last_routes only where routes were forced).
     """
 
     def __init__(self, shape, tensors):
@@ -167,7 +169,7 @@ class OracleMoEDecoder:
             raise ValueError("token out of range")
         H, hd, k = s.n_heads, s.head_dim, s.top_k
         x = f64(w.E[int(tok)])
-        routes, wts, margins = [], [], []
+        routes, wts, margins, natural = [], [], [], []
         for l, lw in enumerate(w.layers):
             xn = rmsnorm(x, lw["g_attn"], s.rms_eps)
             q = (f64(lw["Wq"]) @ xn).reshape(H, hd)
@@ -183,14 +185,16 @@ class OracleMoEDecoder:
             x = x + f64(lw["Wo"]) @ o.reshape(H * hd)
             xn = rmsnorm(x, lw["g_ffn"], s.rms_eps)
             force = None if force_routes is None else force_routes[l]
-            y, sel, ws, margin, _ = moe_ffn(w, l, xn, k, force)
+            y, sel, ws, margin, r = moe_ffn(w, l, xn, k, force)
             x = x + y
             routes.append(sel)
             wts.append(ws)
             margins.append(margin)
+            natural.append(route(r, k)[0])
         self.last_routes = np.array(routes)
         self.last_weights = np.array(wts)
         self.last_margins = np.array(margins)
+        self.last_natural = np.array(natural)
         self.pos = p + 1
         return f64(w.W_lm) @ rmsnorm(x, w.g_final, s.rms_eps)
 

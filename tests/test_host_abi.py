@@ -5,6 +5,8 @@ No compute calls: these run without a GPU.
 import ctypes
 import os
 
+import re
+
 import numpy as np
 import pytest
 
@@ -29,7 +31,8 @@ def test_exports_every_declared_symbol(lib):
     assert len(names) >= 15
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.dec_abi_version() == 1
+    want = int(re.search(r"#define DEC_ABI_VERSION (\d+)", open(B.HEADER).read()).group(1))
+    assert lib.dec_abi_version() == want == 2
     assert set(names) == set(B.SIGNATURES)
 
 
@@ -102,6 +105,31 @@ def test_matrix_prefill_flag_rules(lib):
     # split-K partial sums
     per_pos = 4 * 2560 + 2 * 2560 + 2 * 2560 + 2 * 6912 + 4
     assert 2048 * per_pos + 32 * 2**20 <= withf - plain < 2048 * per_pos + 32 * 2**20 + 4096
+
+
+def test_moe_desc_rules(lib):
+    m = synth.shape_for("moe2b")
+    ok = B.ModelDesc.from_shape(m)
+    assert (ok.n_experts, ok.top_k) == (32, 4)
+    assert B.check_desc(ok) == B.DEC_OK, B.last_error()
+    assert B.check_desc(desc(top_k=2)) == B.DEC_ERR_BAD_DESC                       # dense with top_k
+    tiny = synth.shape_for("tiny")
+    for E, k in ((1, 1), (7, 2), (66, 2), (8, 0), (8, 9), (4, 5), (16, 9)):
+        assert B.check_desc(B.ModelDesc.from_shape(tiny, n_experts=E, top_k=k, d_ffn=256)) == B.DEC_ERR_BAD_DESC, (E, k)
+    for kw in (dict(batch=2), dict(flags=B.DEC_FLAG_MATRIX_PREFILL), dict(flags=B.DEC_FLAG_BATCHED_PREFILL),
+               dict(d_ffn=264), dict(d_model=264), dict(d_ffn=2048)):   # 4 x 2048 > 7168
+        assert B.check_desc(B.ModelDesc.from_shape(m, **kw)) == B.DEC_ERR_UNSUPPORTED, kw
+    assert B.check_desc(B.ModelDesc.from_shape(m, d_ffn=1792)) == B.DEC_OK       # 4 x 1792 = 7168
+    with pytest.raises(B.DecError, match="UNSUPPORTED"):
+        B.packed_bytes(ok)
+    # the arena holds the dense parts, the experts' codes and row scales and
+    # the routing record on top of what a dense model of the same attention needs
+    dense = B.arena_bytes(B.ModelDesc.from_shape(synth.shape_for("dense2b")))
+    moe = B.arena_bytes(ok)
+    L, d, F, E, k, C = 25, 2560, 1728, 32, 4, 4096
+    fp16_mlp = L * (3 * 6912 * d) * 2                     # dense2b's gate, up and down
+    experts = L * (E * 3 * F * d + 4 * E * (2 * F + d)) + C * L * k * 4 + L * E * d * 2
+    assert abs((moe - dense) - (experts - fp16_mlp)) < 2e6, (moe - dense, experts - fp16_mlp)
 
 
 def test_valid_descs_and_arena(lib):
