@@ -18,6 +18,10 @@ The same JSON line also carries, each measured in this run on its own handle:
                           then 128 steps to the 4096 cap
   workloads.dense2b_b8    8 sequences of 256-token prompts, 256 steps together
                           (value = tokens/s of all 8; per request = of each)
+  workloads.moe2b         dense2b's attention with a mixture-of-experts MLP:
+                          32 experts of width 1728 in FP8 E4M3, top-4 routing
+                          inside the resident kernel; 128-token prompt + 512
+                          steps (its roofline counts the active experts only)
   ttft                    time to first token of the 128-token prompt: one
                           position per step (the decode kernel), batched (8
                           positions per step on the matrix-core kernel) and
@@ -49,7 +53,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode tokens/s per request (bs=1) and achieved HBM GB/s vs peak, 1 MI355X"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "memory_bound_transformer_persistent_amd", "csrc", "dec_kernels.hip")
-EXTRAS = ("lane2b", "dense2b_long", "dense2b_b8")
+EXTRAS = ("lane2b", "dense2b_long", "dense2b_b8", "moe2b")
 SERVE_IDLE_US = 200000   # decode server: a launch ends after 0.2 s without a step
 
 
@@ -91,9 +95,14 @@ def cpu_baseline(shape, tensors, prompt, n_steps):
     greedy tokens, which equal the GPU's up to near-ties), timed."""
     import oracle as O
     n0 = len(prompt)
-    lg, K16, V16, _ = O.prefill_matrix(shape, tensors, prompt)
-    dec = O.OracleDecoder(shape, tensors)
-    dec.load_cache(K16, V16, n0)
+    if shape.moe:
+        lg, K16, V16, _, _ = O.prefill_matrix_moe(shape, tensors, prompt)
+        dec = O.OracleMoEDecoder(shape, tensors)
+        dec.Kc[:, :, :n0], dec.Vc[:, :, :n0], dec.pos = K16, V16, n0
+    else:
+        lg, K16, V16, _ = O.prefill_matrix(shape, tensors, prompt)
+        dec = O.OracleDecoder(shape, tensors)
+        dec.load_cache(K16, V16, n0)
     tok = O.greedy(lg[-1])
     t0 = time.perf_counter()
     for _ in range(n_steps):
@@ -189,14 +198,18 @@ class Run:
 
 
 def kernel_name(w):
-    return f"dec_resident_{'batch_' if w.batch > 1 else ''}hd{w.shape.head_dim}"
+    kind = "batch_" if w.batch > 1 else ("moe_" if w.shape.moe else "")
+    return f"dec_resident_{kind}hd{w.shape.head_dim}"
 
 
 def extra_workload(B, R, torch, name, full_tensors, stream, warmup, serve):
     """One of the other configurations, at its own prompt and step count."""
     import synth
     w = synth.workload(name)
-    tensors = synth.lane_from_full(w.shape, full_tensors) if w.lane else full_tensors
+    if w.shape.moe:
+        tensors = synth.workload_weights(w)      # its own seeded draw: router, expert codes and scales
+    else:
+        tensors = synth.lane_from_full(w.shape, full_tensors) if w.lane else full_tensors
     mp = name == "dense2b_long"      # the long prompt goes through the matrix prefill
     r = Run(B, R, torch, w, tensors, stream, flags=B.DEC_FLAG_MATRIX_PREFILL if mp else 0, serve=serve)
     try:
@@ -208,6 +221,8 @@ def extra_workload(B, R, torch, name, full_tensors, stream, warmup, serve):
         out["prefill"] = {"tokens": w.prompt_len, "sequences": w.batch, "ms": round(pre, 3),
                           "mode": "matrix, all positions per product" if mp else "one position per step"}
         out["workload"] = f"{w.name}: {w.description}; prompt {w.prompt_len} + {w.steps} greedy steps, batch {w.batch}"
+        if w.shape.moe:
+            out["active_bytes_per_step"] = int(R.mean_step_bytes(w.shape, pos0, w.steps, w.batch))
         out["segments_tokens_per_s"] = [round(x, 1) for x in segs]
         return out
     finally:
@@ -295,7 +310,7 @@ def main():
     if w.prompt_len + max(args.steps, args.warmup) > s.max_ctx:
         sys.exit("prompt + steps exceed the context cap")
     t_gen = time.time()
-    if w.name == "tiny":
+    if w.name == "tiny" or s.moe:
         full, tensors = None, synth.workload_weights(w)
     else:
         # every other workload uses the 2.3B model's seeded tensors (a lane slices them)

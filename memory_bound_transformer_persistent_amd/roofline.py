@@ -37,7 +37,15 @@ class StepBytes:
 
 
 def layer_weight_bytes(shape) -> int:
+    """Weight bytes one token reads in one layer.  A mixture of experts reads
+    its fp16 router and only the top_k chosen experts: one byte per E4M3 code
+    and a 4-byte scale per row (page 標準GPUによるリアルタイムLLM推論, section
+    Hackerたちの意見: batch-1 speed follows the active parameters)."""
     d, q, f = shape.d_model, shape.n_heads * shape.head_dim, shape.d_ffn
+    if getattr(shape, "n_experts", 0):
+        k = shape.top_k
+        fp16 = 3 * q * d + d * q + shape.n_experts * d
+        return 2 * (fp16 + 2 * d) + k * (3 * f * d) + 4 * k * (2 * f + d)
     mats = 3 * q * d + d * q + 2 * f * d + d * f
     return 2 * (mats + 2 * d)            # fp16 matrices + the two norm gains
 

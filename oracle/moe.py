@@ -203,12 +203,16 @@ class OracleMoEDecoder:
 # whole-prompt matrix form
 # ----------------------------------------------------------------------------
 
-def prefill_matrix_moe(shape, tensors, tokens):
+def prefill_matrix_moe(shape, tensors, tokens, force_routes=None, progress=None):
     """All prompt positions at once (explicit causal mask, experts applied
     to the rows routed to them).
 
     Returns (logits [n, lm_vocab], K16 [L, H, n, hd], V16 [L, H, n, hd],
-    routes [n, L, k], margins [n, L]).
+    routes [n, L, k], margins [n, L]): the router's own choice at every
+    position and layer and its gap between the k-th and (k+1)-th logit.
+    force_routes [n, L, k], if given, are the experts used instead (the
+    returned routes stay the router's own choice, so the two can be
+    compared); progress(l), if given, is called after each layer.
     """
     s = shape
     w = MoEWeights(shape, tensors)
@@ -242,6 +246,9 @@ def prefill_matrix_moe(shape, tensors, tokens):
         for i in range(n):
             sel, ws, margins[i, l] = route(R[i], k)
             routes[i, l] = sel
+            if force_routes is not None:
+                sel = np.asarray(force_routes[i][l], dtype=np.int64)
+                ws = softmax(R[i, sel])
             wts[i, sel] = ws
         Y = np.zeros_like(X)
         for e in range(s.n_experts):
@@ -254,6 +261,8 @@ def prefill_matrix_moe(shape, tensors, tokens):
         X = X + Y
         Ks.append(K16.transpose(1, 0, 2))
         Vs.append(V16.transpose(1, 0, 2))
+        if progress is not None:
+            progress(l)
     logits = rmsnorm(X, w.g_final, s.rms_eps) @ f64(w.W_lm).T
     return logits, np.stack(Ks).astype(np.float16), np.stack(Vs).astype(np.float16), routes, margins
 

@@ -27,6 +27,9 @@ Stored per fixture (npz, float32 values of float64 results):
   kv_layers, kv_pos            where K/V rows are stored
   kv_K, kv_V  [batch, layers, H, positions, hd] fp16 cache rows
   greedy_*    (dense2b only)   the oracle's free-running greedy decode
+  routes      [n, L, k]        (mixture of experts) the experts the oracle's
+                               router chose at every position and layer
+  route_gap   [n, L]           its gap between the k-th and (k+1)-th logit there
 
 Usage: python tests/golden/make_fullsize.py [name ...]   (default: all)
 """
@@ -46,6 +49,7 @@ import oracle as O  # noqa: E402
 import synth  # noqa: E402
 
 ORACLE_SRC = os.path.join(ROOT, "oracle", "decoder.py")
+MOE_SRC = os.path.join(ROOT, "oracle", "moe.py")
 N_SAMPLES = 1024
 FORCED_SEED = 7          # seed of the forced decode tokens (the prompt uses the workload's prompt seed)
 SAMPLE_SEED = 12345      # seed of the sampled logit indices
@@ -84,12 +88,15 @@ FIXTURES = {
     # over nearly the whole 4096-position cache
     "dense2b_b8_long": dict(workload="dense2b_b8", prompt_len=3968, steps=8, every=1,
                             extra=[], kv_layers=[0, 12, 24], kv_pos=[0, 1983, 3967, 3975], kv_seqs=[0, 7]),
+    # dense2b's attention with 32 FP8 experts, top-4: 128 + 64
+    "moe2b": dict(workload="moe2b", prompt_len=128, steps=64, every=4, extra=[127, 128, 129, 190, 191],
+                  kv_layers=[0, 1, 12, 24], kv_pos=[0, 5, 127, 128, 191]),
 }
 GREEDY_STEPS = 16        # dense2b: free-running greedy steps after the 128-token prompt
 
 
-def oracle_sha():
-    return hashlib.sha256(open(ORACLE_SRC, "rb").read()).hexdigest()[:16]
+def oracle_sha(path=ORACLE_SRC):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
 def forced_tokens(vocab, steps, batch):
@@ -128,8 +135,13 @@ def make(name):
     samp_val = np.zeros((nb, len(samp_pos), len(samp_idx)), np.float32)
     kv_K = np.zeros((len(kv_seqs), len(kv_layers), s.n_heads, len(kv_pos), s.head_dim), np.float16)
     kv_V = np.zeros_like(kv_K)
+    extra = {}
     for b in range(nb):
-        logits, K16, V16, _ = O.prefill_matrix(s, tensors, tokens[b])
+        if s.moe:
+            logits, K16, V16, routes, gaps = O.prefill_matrix_moe(s, tensors, tokens[b])
+            extra = dict(routes=routes.astype(np.int8), route_gap=gaps.astype(np.float32))
+        else:
+            logits, K16, V16, _ = O.prefill_matrix(s, tensors, tokens[b])
         ti, tv = top2(logits[pos])
         top_idx[b], top_val[b] = ti, tv.astype(np.float32)
         samp_val[b] = logits[samp_pos][:, samp_idx].astype(np.float32)
@@ -140,7 +152,7 @@ def make(name):
         print(f"{name}: sequence {b} done ({time.time() - t0:.0f} s)", flush=True)
     out = dict(tokens=tokens, pos=pos, top_idx=top_idx, top_val=top_val, samp_idx=samp_idx,
                samp_pos=samp_pos, samp_val=samp_val, kv_layers=kv_layers, kv_pos=kv_pos,
-               kv_seqs=np.array(kv_seqs, dtype=np.int32), kv_K=kv_K, kv_V=kv_V)
+               kv_seqs=np.array(kv_seqs, dtype=np.int32), kv_K=kv_K, kv_V=kv_V, **extra)
     if name == "dense2b":
         # free-running greedy decode of the oracle from the same prompt
         fed, lg, pre, nxt = O.greedy_decode(s, tensors, prompt[0], GREEDY_STEPS)
@@ -151,6 +163,8 @@ def make(name):
     meta = dict(fixture=name, workload=w.name, prompt_len=n0, steps=steps, batch=nb,
                 weight_seed=w.weight_seed, prompt_seed=w.prompt_seed, forced_seed=FORCED_SEED,
                 sample_seed=SAMPLE_SEED, oracle_sha=oracle_sha(), script="tests/golden/make_fullsize.py")
+    if s.moe:
+        meta["moe_sha"] = oracle_sha(MOE_SRC)
     out["meta"] = np.array(json.dumps(meta))
     path = os.path.join(HERE, f"fullsize_{name}.npz")
     np.savez_compressed(path, **out)

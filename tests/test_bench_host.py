@@ -86,3 +86,21 @@ def test_prefill_flops_counts_every_product_once():
                         count += 2 * s.head_dim + 2 * s.head_dim                   # q.k and p v
         count += 2 * s.lm_vocab * d                                                 # the last row's logits
         assert R.prefill_flops(s, n) == count
+
+
+def test_moe_step_bytes_count_the_active_experts_only():
+    import synth
+    from memory_bound_transformer_persistent_amd import roofline as R
+    m = synth.shape_for("moe2b")
+    d, F, E, k = 2560, 1728, 32, 4
+    attn = 2 * (4 * 2560 * 2560)
+    want = attn + 2 * E * d + 2 * 2 * d + k * 3 * F * d + 4 * k * (2 * F + d)
+    assert R.layer_weight_bytes(m) == want
+    # the same attention with dense2b's fp16 MLP reads 2 x 3 x 6912 x 2560 bytes more per
+    # layer, the FP8 experts 4 x 3 x 1728 x 2560 (plus their scales and the router)
+    dense = R.layer_weight_bytes(synth.shape_for("dense2b"))
+    assert dense - want == 2 * 3 * 6912 * d - (k * 3 * F * d + 4 * k * (2 * F + d) + 2 * E * d)
+    # every other term of a step is the dense model's
+    sb, sd = R.step_bytes(m, 200), R.step_bytes(synth.shape_for("dense2b"), 200)
+    assert sb.kv_read == sd.kv_read and sb.act == sd.act
+    assert sd.weights - sb.weights == 25 * (dense - want)

@@ -16,7 +16,7 @@ import oracle as O
 import synth
 from fullsize import GOLDEN, Fixture, oracle_sha
 
-NAMES = ("dense2b", "lane2b", "dense2b_long", "dense2b_b8", "dense2b_w4", "lane2b_long", "dense2b_b8_long")
+NAMES = ("dense2b", "lane2b", "dense2b_long", "dense2b_b8", "dense2b_w4", "lane2b_long", "dense2b_b8_long", "moe2b")
 
 
 @pytest.mark.parametrize("name", NAMES)
@@ -83,3 +83,18 @@ def test_fixture_script_uses_only_the_oracle_and_the_generators():
         elif isinstance(node, ast.ImportFrom):
             mods.add((node.module or "").split(".")[0])
     assert mods <= {"hashlib", "json", "os", "sys", "time", "numpy", "oracle", "synth"}, mods
+
+
+def test_moe2b_fixture_is_from_the_current_moe_oracle():
+    import hashlib
+    fx = Fixture("moe2b")
+    src = os.path.join(os.path.dirname(GOLDEN), "..", "oracle", "moe.py")
+    assert fx.meta["moe_sha"] == hashlib.sha256(open(src, "rb").read()).hexdigest()[:16], \
+        "oracle/moe.py changed: rerun tests/golden/make_fullsize.py moe2b"
+    s = fx.shape
+    n = fx.n0 + fx.steps
+    assert fx.routes.shape == (n, s.n_layers, s.top_k) and fx.route_gap.shape == (n, s.n_layers)
+    assert fx.routes.min() >= 0 and fx.routes.max() < s.n_experts
+    # k distinct experts per position and layer, and a non-negative gap to the next
+    assert all(len(set(r)) == s.top_k for r in fx.routes.reshape(-1, s.top_k))
+    assert fx.route_gap.min() >= 0.0

@@ -46,7 +46,7 @@ _TENSORS = {}
 def tensors_for(fx):
     """The workload's seeded weights (kept for the module: the 2.3B tensors take seconds to draw)."""
     name = fx.workload.name
-    key = "lane2b" if fx.workload.lane else "dense2b"
+    key = "lane2b" if fx.workload.lane else ("moe2b" if fx.shape.moe else "dense2b")
     if key not in _TENSORS:
         _TENSORS.clear()
         _TENSORS[key] = synth.workload_weights(fx.workload)
@@ -207,3 +207,74 @@ def test_dense2b_b8_after_3968_token_prompts(stream):
     """Batch 8 after 3968-token prompts: each (sequence, head) pair on one workgroup
     over nearly the whole 4096-position cache; 8 forced steps."""
     run_teacher_forced(Fixture("dense2b_b8_long"), stream, "dense2b_b8 8 x (3968 + 8)", kv_bound=KV_BATCH)
+
+
+ROUTE_TIE = 5e-3
+
+
+def test_moe2b_teacher_forced(stream):
+    """dense2b's attention with 32 FP8 experts, top-4: 128-token prompt, 64 forced steps.
+
+    The router's choice is an integer decided by floating point: where the
+    oracle's gap between its 4th and 5th logit is below ROUTE_TIE, either
+    choice is correct.  Two comparisons:
+      * against the fixture (the oracle from the seeds alone): the routes at
+        every position up to the first such near-tie where the library took
+        the other expert, and the K/V rows before it;
+      * against the oracle run here on the fixture's tokens, which takes the
+        router's own choice wherever it is not a near-tie and the library's
+        choice at near-ties (each one checked to be a near-tie): the logits of
+        every position 127..191 and the K/V rows at the fixture's positions.
+    """
+    import oracle as O
+    fx = Fixture("moe2b")
+    n0, steps, L = fx.n0, fx.steps, fx.shape.n_layers
+    n = n0 + steps
+    t = Tracker(fx, "moe2b 128 + 64")
+    logits = {}
+    with make(fx, stream) as d:
+        tok, pre = d.prefill(fx.prompt, want_logits=True)
+        logits[n0 - 1] = (pre, tok)
+        for i in range(steps):
+            tk, lg = d.step(force_tok=int(fx.forced(i)[0]), want_logits=True)
+            logits[n0 + i] = (lg, tk)
+        routes = d.read_routes(0, n)
+        kv = {int(l): d.read_kv(int(l), n) for l in fx.kv_layers}
+        split = n
+        for p in range(n):
+            diff = [l for l in range(L) if set(routes[p, l]) != set(fx.routes[p, l])]
+            if diff:
+                l = diff[0]
+                assert fx.route_gap[p, l] < ROUTE_TIE, \
+                    f"position {p} layer {l}: {list(routes[p, l])} vs {list(fx.routes[p, l])}, gap {fx.route_gap[p, l]}"
+                split = p
+                break
+        check_kv(d, fx, "moe2b against the fixture", KV_B1, upto=split)
+    print(f"moe2b: routes equal to the fixture's at the first {split} of {n} positions", flush=True)
+    # the oracle on the same tokens, following the library at near-ties
+    lg, K16, V16, own, gap = O.prefill_matrix_moe(fx.shape, tensors_for(fx), fx.tokens[0], force_routes=routes,
+                                                  progress=lambda l: print(f"oracle layer {l} done", flush=True))
+    followed = 0
+    for p in range(n):
+        for l in range(L):
+            if set(own[p, l]) != set(routes[p, l]):
+                assert gap[p, l] < ROUTE_TIE, \
+                    f"position {p} layer {l}: library {list(routes[p, l])}, oracle {list(own[p, l])}, gap {gap[p, l]}"
+                followed += 1
+    worst = 0.0
+    for p, (g, tk) in sorted(logits.items()):
+        err = float(np.max(np.abs(g.astype(np.float64) - lg[p])))
+        assert err <= 2e-2, f"position {p}: {err}"
+        if O.top2_margin(lg[p]) > 0.05:
+            assert int(tk) == O.greedy(lg[p]), p
+        worst = max(worst, err)
+    kv_worst = 0.0
+    for li, layer in enumerate(fx.kv_layers):
+        k, v = kv[int(layer)]
+        for got, want in ((k, K16[layer]), (v, V16[layer])):
+            ex = kv_excess(got[:, fx.kv_pos].transpose(1, 0, 2), want[:, fx.kv_pos].transpose(1, 0, 2))
+            assert ex.max() <= KV_B1, f"layer {layer}: {ex.max()}"
+            kv_worst = max(kv_worst, float(ex.max()))
+    print(f"moe2b 128 + 64: logits at {len(logits)} positions, max |gpu - oracle| = {worst:.3e} (bound 2e-2); "
+          f"K/V worst excess {kv_worst:.2e} of the rms; {followed} near-tie routing choices "
+          f"(of {n * L}) followed", flush=True)

@@ -235,3 +235,19 @@ def test_greedy_decode_moe_feeds_its_argmax():
     for i in range(1, 4):
         assert fed[i] == O.greedy(outs[i - 1])
     assert routes.shape == (9, TINY_MOE.n_layers, TINY_MOE.top_k) and margins.shape == (9, TINY_MOE.n_layers)
+
+
+def test_matrix_prefill_with_forced_routes_equals_forced_steps():
+    t = synth.make_weights(TINY_MOE, seed=28, gain_jitter=0.1)
+    toks = synth.make_prompt(TINY_MOE.vocab, 6, seed=7)[0]
+    rng = np.random.default_rng(3)
+    force = np.array([[rng.choice(TINY_MOE.n_experts, TINY_MOE.top_k, replace=False)
+                       for _ in range(TINY_MOE.n_layers)] for _ in range(6)])
+    lg, K16, V16, routes, gaps = O.prefill_matrix_moe(TINY_MOE, t, toks, force_routes=force)
+    dec = O.OracleMoEDecoder(TINY_MOE, t)
+    for i, tok in enumerate(toks):
+        li = dec.step(int(tok), force_routes=[list(r) for r in force[i]])
+        np.testing.assert_allclose(li, lg[i], rtol=1e-10, atol=1e-11)
+        # the returned routes are the router's own choice on the forced path
+        np.testing.assert_array_equal(dec.last_natural, routes[i])
+    np.testing.assert_array_equal(dec.Kc[:, :, :6], K16)
