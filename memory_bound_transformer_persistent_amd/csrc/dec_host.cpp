@@ -365,7 +365,7 @@ bool same_shape(const dec_model_desc& a, const dec_model_desc& b) {
 // device arena layout (bytes)
 // ---------------------------------------------------------------------------
 struct Arena {
-  size_t w, w2, w8, esc, routes, gains, rope, kv, mp_x, mp_h, mp_q16, mp_a, mp_s, mp_part, x, xg16, ssp, qkv, att_o, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out,
+  size_t w, w2, w8, esc, routes, rpart, gains, rope, kv, mp_x, mp_h, mp_q16, mp_a, mp_s, mp_part, x, xg16, ssp, qkv, att_o, part, pml, act, logits, amax_v, amax_i, tok_cur, tok_out,
       prompt, ctl, srv_slot, params, params2, trace, total;
 };
 
@@ -393,6 +393,7 @@ dec_model_desc prefill_desc(const dec_model_desc& d) {
 Arena arena_layout(const dec_model_desc& d, int G) {
   Arena a;
   const Image im = image_layout(d);
+  a.rpart = 0;
   const size_t D = d.d_model, q = (size_t)d.n_heads * d.head_dim;
   const bool bp = batched_prefill(d);
   // rows of the per-column buffers: sequences, or the batched prefill's columns
@@ -434,6 +435,7 @@ Arena arena_layout(const dec_model_desc& d, int G) {
   a.pml = take(part_rows * 2 * 4);
   // the MLP's hidden vector: d_ffn, or top_k experts' d_ffn each
   a.act = take(B * d.d_ffn * (moe(d) ? d.top_k : 1) * 4);
+  if (moe(d)) a.rpart = take((size_t)G * kMoeMaxExperts * 4);
   a.logits = take(B * d.lm_vocab * 4);
   // argmax partials: [G] at batch 1, [G][kMaxBatch] for the batched kernel
   const size_t Bk = B > 1 ? (size_t)kMaxBatch : 1;
@@ -1067,6 +1069,11 @@ int init_impl(const dec_model_desc* desc, const dec_weights_src* weights, const 
       }
       const long long wg_slot = h->grid / desc->top_k;
       need_out = std::max(need_out, (long long)kMoeOutPairs + 2 * ((desc->d_ffn + wg_slot - 1) / wg_slot));
+      if ((long long)desc->n_experts * rows_wg(desc->d_model) > kMoeWrElems) {
+        fail(&h->err, DEC_ERR_UNSUPPORTED, "grid %d too small for this model (a workgroup would stage %lld router "
+             "weights)", h->grid, (long long)desc->n_experts * rows_wg(desc->d_model));
+        return bail(DEC_ERR_UNSUPPORTED);
+      }
       if ((long long)desc->top_k * rows_wg(desc->d_model) > kMoeScaleFloats) {
         fail(&h->err, DEC_ERR_UNSUPPORTED, "grid %d too small for this model (a workgroup would stage %lld down-row "
              "scales)", h->grid, (long long)desc->top_k * rows_wg(desc->d_model));
@@ -1176,6 +1183,7 @@ int init_impl(const dec_model_desc* desc, const dec_weights_src* weights, const 
     P.esc = reinterpret_cast<const float*>(b + h->ar.esc);
     P.sc_stride = h->im.sc_stride; P.sc_d = h->im.sc_d;
     P.routes = reinterpret_cast<int32_t*>(b + h->ar.routes);
+    P.rpart = reinterpret_cast<float*>(sc(h->ar.rpart));
     e = hipMemset(P.routes, 0xFF, (size_t)desc->max_ctx * desc->n_layers * desc->top_k * 4);
     if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemset(routes)"); return bail(DEC_ERR_DEVICE); }
   }

@@ -34,6 +34,7 @@ constexpr int kMoeMaxTopK = 8;
 constexpr int kMoeKernel = 0;
 constexpr int kMoeOutPairs = 64;
 constexpr int kMoeScaleFloats = 512;   // LDS for the down phase's row scales of every chosen expert
+constexpr int kMoeWrElems = 768;       // LDS fp16 elements for the router's columns of a workgroup's residual rows
 constexpr int kBatchSpanD = 2560;           // padded d_model (input of QKV, GU, LM; staged in fp32 too)
 constexpr int kBatchSpanK = 7680;           // padded d_ffn and n_heads*head_dim
 // The batched kernel multiplies weights by the inputs with MFMA
@@ -146,6 +147,7 @@ struct Params {
   const float* esc;           // expert row scales: per layer [E][Fe][2] (gate, up), then [E][d] at sc_d
   size_t sc_stride, sc_d;     // floats between layers; offset of the down scales inside a layer
   int32_t* routes;            // chosen experts [max_ctx][L][topk]
+  float* rpart;               // router logits' partial sums over each workgroup's rows [G][kMoeMaxExperts]
 };
 
 struct Launch {

@@ -68,10 +68,15 @@ constexpr int kAuxFloats = 2048;
 // merge after S1) share offset 0: their lifetimes do not overlap
 constexpr int kAuxPart = 0;
 static_assert(kAuxPart + kWaves * (128 + 2) <= kAuxFloats, "aux LDS");
-// a mixture of experts' routing of the current layer, 16 words per wave
-// from kAuxRoute (past the rotary rows and the attention partials): the
-// top_k experts (ints), then their weights from word 8.  Each wave forms its
-// own copy in the GU phase; wave 0's is read until the down phase.
+// Mixture of experts, in aux LDS the rotary rows and the attention partials
+// leave free from the O phase to the down phase:
+//   kAuxRouter  the router logits' sums over each wave's workgroups [8][64] (GU)
+//   kAuxRoute   the layer's routing, 16 words per wave: the top_k experts
+//               (ints), then their weights from word 8.  Each wave forms its
+//               own copy in the GU phase; wave 0's is read until the down phase.
+//   kAuxMoe     the down phase's row scales (kMoeScaleFloats)
+constexpr int kAuxRouter = 0;
+static_assert(kAuxRouter + kWaves * kMoeMaxExperts <= 1280, "aux LDS");
 constexpr int kAuxRoute = 1280;
 static_assert(kAuxRoute >= 1024 && kAuxRoute >= kAuxPart + kWaves * (128 + 2) && kAuxRoute + 16 * kWaves <= 1536,
               "aux LDS");
@@ -96,7 +101,10 @@ struct Lds {
   static constexpr int Slot = Tab + kStreamers * kStreamerTab, Plan = Slot + kStreamers * 2 * SlotN;
   // batch 1: 1 KB that the attention-phase cache warm-up DMAs land in (never read)
   static constexpr int Sink = Plan + (MB == 1 ? 0 : 6 * kPlanInts);
-  static constexpr int End = Sink + 256;   // a 1 KB sink for cache warm-up loads
+  // mixture of experts: the router's columns of the workgroup's residual
+  // rows, fp16 [E][rows] (LDS DMA in the QKV phase, read by the O publication)
+  static constexpr int MoeWr = Sink + 256;
+  static constexpr int End = MoeWr + kMoeWrElems / 2;
   static_assert(End * 4 <= kLdsBytes, "LDS map exceeds the allocation");
   static_assert(MB == 1 || 3 * kMaxBatch * kBatchSpanD / 2 <= Region, "staged fp32 inputs do not fit");
   static_assert(Gain % 4 == 0 && Region % 4 == 0 && Sink % 4 == 0, "16-byte alignment");
@@ -305,11 +313,9 @@ __device__ __forceinline__ GemvWork work_of(const Params& P, int ph, int l) {
     default: return g;
   }
   if (P.E > 0 && ph == PH_GU) {
-    // mixture of experts: the GU phase's ordinary stream is the router
-    // [E, d], all of it in every workgroup (the experts follow it)
-    g.rows = P.E;
-    g.p0 = 0;
-    g.p1 = P.E / 2;
+    // mixture of experts: the GU phase streams only the chosen experts
+    // (moe_stream), nothing through the ordinary stream
+    g.p0 = g.p1 = 0;
     return g;
   }
   // batch 1 with few heads (at most 1/32 of the grid, e.g. one lane of a
@@ -788,6 +794,11 @@ __device__ __forceinline__ void w0_poison(const Params& P, int ph, int l, const 
     share(nparts * 2, a, e);
     for (int i = a + lane; i < e; i += 64) st_coh(reinterpret_cast<uint32_t*>(P.pml + i), nan32);
   }
+  if (MB == 1 && P.E > 0 && ph == PH_DOWN && lane < P.E) {
+    // mixture of experts: this workgroup's router-logit shares, read by every
+    // workgroup's GU phase (behind the barrier); the next O publication writes them
+    st_coh(reinterpret_cast<uint32_t*>(P.rpart + (size_t)blockIdx.x * kMoeMaxExperts + lane), nan32);
+  }
   if (ph == PH_GU) {
     // the attention output, read by the O input pull
     share(B * P.q, a, e);
@@ -1214,7 +1225,7 @@ template <int MB, bool MOE = false>
 __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l, int pos, int pos_end,
                                                  const int* tab_wg, int lg_mode, const float* scl,
                                                  const float* out, float* xown, const float* rope_lds,
-                                                 const float* gs_next) {
+                                                 const float* gs_next, const uint16_t* moe_wr = nullptr) {
   const int lane = threadIdx.x & 63, B = P.B;
   if (!is_gemv(ph)) return;
   if (MOE && ph == PH_GU) {
@@ -1288,6 +1299,16 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l,
           ss += v * v;
         }
       }
+    }
+    if (MOE && ph == PH_O && lane < P.E) {
+      // mixture of experts: this workgroup's share of each router logit,
+      // sum over its rows r of router[e][r] * g[r] * x[r] (g: the FFN norm's
+      // gains, in gs since the QKV phase fetched them; the router columns
+      // staged in the O phase)
+      float acc = 0.f;
+      const _Float16* wr = reinterpret_cast<const _Float16*>(moe_wr) + lane * 2 * n;
+      for (int t = 0; t < 2 * n; ++t) acc = __builtin_fmaf((float)wr[t], gs_next[2 * p0 + t] * xown[t], acc);
+      st_coh(P.rpart + (size_t)blockIdx.x * kMoeMaxExperts + lane, acc);
     }
     if constexpr (MB > 1) {
       // lane l holds sequence l % MB's share (64 is a multiple of MB)
@@ -1712,18 +1733,49 @@ __device__ __forceinline__ void dot16_e4m3x2(u32x4 w0, u32x4 w1, const float* x,
   }
 }
 
+// The router's logits are sums over the residual rows: every workgroup's O
+// publication adds its own rows' share, router[e][r] * g[r] * x[r] for the
+// FFN norm's gains g, into P.rpart[workgroup][e].  After the barrier each
+// wave w sums the shares of workgroups w, w + 8, ... in that order
+// (moe_router_sums, into LDS), and every wave adds the eight sums in wave
+// order: the same bits in every wave and every workgroup.
+__device__ __forceinline__ void moe_router_sums(const Params& P, float* rs) {
+  const int lane = threadIdx.x & 63, w = rfl((int)(threadIdx.x >> 6)), G = gridDim.x;
+  // 32 shares per lane requested before any is added (one round trip for a
+  // grid of up to 256 workgroups), added in workgroup order
+  constexpr int kChunk = 32;
+  float acc = 0.f;
+  if (lane < P.E) {
+    for (int g0 = w; g0 < G; g0 += kChunk * kWaves) {
+      float v[kChunk];
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) {
+        const int g = g0 + kWaves * k;
+        v[k] = g < G ? ld_coh(P.rpart + (size_t)g * kMoeMaxExperts + lane) : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) acc += v[k];
+    }
+  }
+  rs[w * kMoeMaxExperts + lane] = acc;
+}
+
 // Every wave, into its routing words rt (LDS, 16 per wave): the top_k
-// experts of the router's row sums out[0, E) -- times the phase's norm
-// scale, formed here from the waves' shares of sum(x^2) in the order wave 0
-// forms it -- largest logit first, the lower index first on equal logits,
-// then from word 8 their weights, the softmax of the chosen logits.
-__device__ __forceinline__ void moe_route(const Params& P, const float* out, const float* red, float* rt) {
+// experts of the router's logits (the sums rs of moe_router_sums, times the
+// phase's norm scale, formed here from the waves' shares of sum(x^2) in the
+// order wave 0 forms it) -- largest logit first, the lower index first on
+// equal logits -- then from word 8 their weights, the softmax of the chosen
+// logits.
+__device__ __forceinline__ void moe_route(const Params& P, const float* rs, const float* red, float* rt) {
   const int lane = threadIdx.x & 63;
   float ss = 0.f;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) ss += red[w];
   const float scale = 1.0f / sqrtf(ss / (float)P.d + P.eps);
-  float v = lane < P.E ? out[lane] * scale : -INFINITY;
+  float sum = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) sum += rs[w * kMoeMaxExperts + lane];
+  float v = lane < P.E ? sum * scale : -INFINITY;
   float mine = 0.f;   // lane s: the s-th chosen logit
   for (int s = 0; s < P.topk; ++s) {
     float best = v;
@@ -1755,71 +1807,98 @@ static_assert(kAuxMoe + kMoeScaleFloats <= kAuxFloats, "aux LDS");
 
 // Streamer s's share of a routed phase -- GU: gate/up row pairs [q0, q1) of
 // the slot's expert; DOWN: every chosen expert's rows of the workgroup's
-// output pairs -- with kUnitsInFlight units (a 1 KB piece of each of a row
-// pair's two rows) in flight in its own registers.  Row sums go to out by
-// ds_add, at most two contributors per row pair (streamer_range).  A down
-// row's sum over one expert is scaled by that row's scale before the next
-// expert's is added.
+// output pairs.  A unit is a 1 KB piece of each of a row pair's two rows.
+struct MoeGeo {
+  int p0, np, npc, tail, nsl, per, u0, n;
+};
 template <bool DOWN>
-__device__ __forceinline__ void moe_stream(const Params& P, int l, int s, const int* tab_wg, int eslot,
-                                           const float* aux, const float* xs, float* out) {
+__device__ __forceinline__ MoeGeo moe_geo(const Params& P, int s, const int* tab_wg) {
+  MoeGeo g;
+  g.p0 = rfl(tab_wg[DOWN ? 2 * PH_DOWN : kTabMoeSlot + 1]);
+  g.np = rfl(tab_wg[DOWN ? 2 * PH_DOWN + 1 : kTabMoeSlot + 2]) - g.p0;
+  const int K = DOWN ? P.Fe : P.d;                      // a row's codes inside one expert
+  g.npc = (K + 1023) >> 10;                             // 1 KB pieces per expert row
+  g.tail = (K - 1024 * (g.npc - 1)) >> 4;               // lanes with codes in the last piece
+  g.nsl = DOWN ? P.topk : 1;                            // experts per row pair
+  g.per = g.nsl * g.npc;
+  int u1;
+  streamer_range(g.np * g.per, g.per, kStreamers, s, g.u0, u1);
+  g.n = u1 - g.u0;
+  return g;
+}
+
+// Issue cursor over a streamer's units: row pair t (from p0), expert segment
+// sl, piece c; units past the share read zeros (out-of-range offsets), so the
+// loads in flight never change in number.
+struct MoeCur {
+  int t, sl, c, issued;
+};
+__device__ __forceinline__ MoeCur moe_cursor(const MoeGeo& g, int u) {
+  MoeCur c;
+  c.t = u / g.per;
+  c.sl = (u - c.t * g.per) / g.npc;
+  c.c = u - c.t * g.per - c.sl * g.npc;
+  c.issued = 0;
+  return c;
+}
+template <bool DOWN>
+__device__ __forceinline__ void moe_issue(const Params& P, const MoeGeo& g, rsrc_t r, const int* sel, int eslot,
+                                          MoeCur& c, u32x4& b0, u32x4& b1) {
   const int lane = threadIdx.x & 63;
-  const uint32_t lane16 = (uint32_t)lane * 16u;
-  const int d = P.d, Fe = P.Fe;
-  const int p0 = rfl(tab_wg[DOWN ? 2 * PH_DOWN : kTabMoeSlot + 1]);
-  const int p1 = rfl(tab_wg[DOWN ? 2 * PH_DOWN + 1 : kTabMoeSlot + 2]);
-  // DOWN: the layer's experts (wave 0's routing words) and the row scales
-  // wave 0 staged with the phase input
-  const int* sel = reinterpret_cast<const int*>(aux) + kAuxRoute;
-  const float* sc_lds = aux + kAuxMoe;
-  const int K = DOWN ? Fe : d;                            // a row's codes inside one expert
-  const int npc = (K + 1023) >> 10;                       // 1 KB pieces per expert row
-  const int tail = (K - 1024 * (npc - 1)) >> 4;           // lanes with codes in the last piece
-  const int nsl = DOWN ? P.topk : 1;                      // experts per row pair
-  const int per = nsl * npc;
-  int u0, u1;
-  streamer_range((p1 - p0) * per, per, kStreamers, s, u0, u1);
-  const int n = u1 - u0;
-  if (n <= 0) return;
-  const rsrc_t r = make_rsrc(P.w8 + (size_t)rfl(l) * P.e8_stride, (uint32_t)P.e8_stride);
-  const uint32_t row_bytes = (uint32_t)K;
-  // issue and consume cursors: row pair t (from p0), expert segment sl, piece c
-  int it = u0 / per, isl = (u0 - it * per) / npc, ic = u0 - it * per - isl * npc;
-  int ct = it, csl = isl, cc = ic;
-  u32x4 b[2 * kUnitsInFlight];
-#define MOE_ISSUE(k)                                                                                          \
-  {                                                                                                           \
-    const bool live = issued < n;                                                                             \
-    const int e = DOWN ? rfl(sel[isl]) : eslot;                                                               \
-    const uint32_t row0 = DOWN ? (uint32_t)P.e8_d + (uint32_t)(e * d + 2 * (p0 + it)) * row_bytes              \
-                               : (uint32_t)((e * Fe + p0 + it) * 2) * row_bytes;                              \
-    const bool ok = live && (ic + 1 < npc || lane < tail);                                                    \
-    const uint32_t o = row0 + 1024u * (uint32_t)ic + lane16;                                                  \
-    b[2 * (k)] = ld_nt(r, ok ? o : kOOB);                                                                     \
-    b[2 * (k) + 1] = ld_nt(r, ok ? o + row_bytes : kOOB + 16u);                                               \
-    ++issued;                                                                                                 \
-    if (++ic == npc) { ic = 0; if (++isl == nsl) { isl = 0; ++it; } }                                         \
+  const uint32_t row_bytes = (uint32_t)(DOWN ? P.Fe : P.d);
+  const int e = DOWN ? rfl(sel[c.sl]) : eslot;
+  const uint32_t row0 = DOWN ? (uint32_t)P.e8_d + (uint32_t)(e * P.d + 2 * (g.p0 + c.t)) * row_bytes
+                             : (uint32_t)((e * P.Fe + g.p0 + c.t) * 2) * row_bytes;
+  const bool ok = c.issued < g.n && (c.c + 1 < g.npc || lane < g.tail);
+  const uint32_t o = row0 + 1024u * (uint32_t)c.c + (uint32_t)lane * 16u;
+  b0 = ld_nt(r, ok ? o : kOOB);
+  b1 = ld_nt(r, ok ? o + row_bytes : kOOB + 16u);   // distinct: always two loads
+  ++c.issued;
+  if (++c.c == g.npc) {
+    c.c = 0;
+    if (++c.sl == g.nsl) { c.sl = 0; ++c.t; }
   }
-  int issued = 0;
+}
+
+// Streams the share with kUnitsInFlight units in flight in b.  Row sums go
+// to out by ds_add, at most two contributors per row pair
+// (streamer_range).  A down row's sum over one expert is scaled by that
+// row's scale before the next expert's is added.  sel: this wave's routing
+// words.  (Issuing the down phase's first units at the end of the GU stream,
+// across the barrier, made the step slower: the early finishers' loads took
+// bandwidth from the GU phase's last workgroups.)
+template <bool DOWN>
+__device__ __forceinline__ void moe_stream(const Params& P, int l, int s, const int* tab_wg, const int* sel,
+                                           int eslot, const float* sc_lds, const float* xs, float* out,
+                                           u32x4 (&b)[2 * kUnitsInFlight]) {
+  const int lane = threadIdx.x & 63;
+  const MoeGeo g = moe_geo<DOWN>(P, s, tab_wg);
+  const rsrc_t r = make_rsrc(P.w8 + (size_t)rfl(l) * P.e8_stride, (uint32_t)P.e8_stride);
+  MoeCur ic = moe_cursor(g, g.u0);
 #pragma unroll
-  for (int k = 0; k < kUnitsInFlight; ++k) MOE_ISSUE(k)
+  for (int k = 0; k < kUnitsInFlight; ++k) moe_issue<DOWN>(P, g, r, sel, eslot, ic, b[2 * k], b[2 * k + 1]);
+  int ct = ic.t, csl = 0, cc = 0;
+  {
+    const MoeCur c0 = moe_cursor(g, g.u0);
+    ct = c0.t; csl = c0.sl; cc = c0.c;
+  }
   float a0 = 0.f, a1 = 0.f, s0 = 0.f, s1 = 0.f;
+  const int n = g.n;
   const int ngroups = (n + kUnitsInFlight - 1) / kUnitsInFlight;
-  const int np = p1 - p0;
   for (int grp = 0; grp < ngroups; ++grp) {
 #pragma unroll
     for (int k = 0; k < kUnitsInFlight; ++k) {
       wait_vm<kBlocksInFlight - 2>();
       const int j = grp * kUnitsInFlight + k;
       if (j < n) {
-        dot16_e4m3x2(b[2 * k], b[2 * k + 1], xs + (DOWN ? csl * Fe : 0) + 1024 * cc + 16 * lane, a0, a1);
-        const bool last = j == n - 1, seg_end = cc + 1 == npc;
+        dot16_e4m3x2(b[2 * k], b[2 * k + 1], xs + (DOWN ? csl * P.Fe : 0) + 1024 * cc + 16 * lane, a0, a1);
+        const bool last = j == n - 1, seg_end = cc + 1 == g.npc;
         if (DOWN && (seg_end || last)) {
-          s0 = __builtin_fmaf(a0, sc_lds[csl * 2 * np + 2 * ct], s0);
-          s1 = __builtin_fmaf(a1, sc_lds[csl * 2 * np + 2 * ct + 1], s1);
+          s0 = __builtin_fmaf(a0, sc_lds[csl * 2 * g.np + 2 * ct], s0);
+          s1 = __builtin_fmaf(a1, sc_lds[csl * 2 * g.np + 2 * ct + 1], s1);
           a0 = a1 = 0.f;
         }
-        if ((seg_end && csl + 1 == nsl) || last) {
+        if ((seg_end && csl + 1 == g.nsl) || last) {
           const float y0 = wave_sum(DOWN ? s0 : a0), y1 = wave_sum(DOWN ? s1 : a1);
           if (lane == 0) {
             lds_add(out + (DOWN ? 0 : kMoeOutPairs) + 2 * ct, y0);
@@ -1827,12 +1906,11 @@ __device__ __forceinline__ void moe_stream(const Params& P, int l, int s, const 
           }
           a0 = a1 = s0 = s1 = 0.f;
         }
-        if (++cc == npc) { cc = 0; if (++csl == nsl) { csl = 0; ++ct; } }
+        if (++cc == g.npc) { cc = 0; if (++csl == g.nsl) { csl = 0; ++ct; } }
       }
-      MOE_ISSUE(k)
+      moe_issue<DOWN>(P, g, r, sel, eslot, ic, b[2 * k], b[2 * k + 1]);
     }
   }
-#undef MOE_ISSUE
   wait_vm0();   // the zero-reading loads past the share's end
 }
 
@@ -1849,6 +1927,7 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
   const uint32_t lane16 = (uint32_t)lane * 16u;
   Cursor cu;
   cursor_start(P, A, g0, g1, tab, cu);
+  u32x4 mb[2 * kUnitsInFlight];   // mixture of experts: the routed phases' loads
   u32x4 buf[kBlocksInFlight];
 #pragma unroll
   for (int k = 0; k < kUnitsInFlight; ++k) issue_unit(cu, lane16, buf[2 * k], buf[2 * k + 1]);
@@ -1902,14 +1981,17 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
     }
     if constexpr (MOE) {
       if (id.ph == PH_GU) {
-        __syncthreads();   // SR: the router's logits are in out[0, E)
+        moe_router_sums(P, aux + kAuxRouter);
+        __syncthreads();   // SR: every wave's share of the router logits is in LDS
         const int w = rfl((int)(threadIdx.x >> 6));
         float* rt = aux + kAuxRoute + 16 * w;
-        moe_route(P, out, red, rt);
-        moe_stream<false>(P, id.l, w, tab_wg, rfl(reinterpret_cast<const int*>(rt)[rfl(tab_wg[kTabMoeSlot])]), aux,
-                          xs, out);
+        moe_route(P, aux + kAuxRouter, red, rt);
+        const int* sel = reinterpret_cast<const int*>(rt);
+        moe_stream<false>(P, id.l, w, tab_wg, sel, rfl(sel[rfl(tab_wg[kTabMoeSlot])]), nullptr, xs, out, mb);
       } else if (id.ph == PH_DOWN) {
-        moe_stream<true>(P, id.l, rfl((int)(threadIdx.x >> 6)), tab_wg, 0, aux, xs, out);
+        const int w = rfl((int)(threadIdx.x >> 6));
+        moe_stream<true>(P, id.l, w, tab_wg, reinterpret_cast<const int*>(aux) + kAuxRoute + 16 * w, 0,
+                         aux + kAuxMoe, xs, out, mb);
       }
     }
     __syncthreads();   // S2
@@ -2089,7 +2171,8 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
           __syncthreads();   // S2b
         }
       w0_store_outputs<MB, MOE>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
-                                lg_mode(A, prev_i, cur_lg), scl, out, xown, aux, gs);
+                                lg_mode(A, prev_i, cur_lg), scl, out, xown, aux, gs,
+                                reinterpret_cast<const uint16_t*>(smem + M::MoeWr));
     }
     if (MB == 1 && is_gemv(id.ph)) {
       // the batch-1 streamers add into out (ds_add); the batched kernel's
@@ -2189,17 +2272,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       ok = wait();
       if constexpr (MB == 1)
         if (ok) w0_dma_vec(xs, P.act, P.F, 4, true, MOE ? 1024 : 0);
-      if constexpr (MOE) {
-        // the row scales of this workgroup's output pairs in every chosen
-        // expert, [slot][2 np], for the streamers
-        const int r0 = 2 * rfl(tab_wg[2 * PH_DOWN]), nr = 2 * rfl(tab_wg[2 * PH_DOWN + 1]) - r0;
-        const float* sd = P.esc + (size_t)id.l * P.sc_stride + P.sc_d;
-        const int* route = reinterpret_cast<const int*>(aux) + kAuxRoute;
-        for (int i = lane; i < P.topk * nr; i += 64) {
-          const int k = i / nr;
-          aux[kAuxMoe + i] = ldg(sd + (size_t)route[k] * P.d + r0 + (i - k * nr));
-        }
-      }
+
     } else if (id.ph == PH_O) {
       ok = wait();
       // the attention output of every head, merged in the attention phase
@@ -2240,6 +2313,19 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
       // the rotary rows of this step's positions, for publishing q and k
       const int ncols = P.cols_pos ? min(B, P.max_ctx - pos) : 1;
       w0_dma_vec(aux, P.rope + (size_t)pos * P.hd, ncols * P.hd, 4, false);
+      if constexpr (MOE) {
+        // the router's columns of this workgroup's residual rows for the O
+        // publication's router-logit shares, [E][rows] in fp16 pairs: dword
+        // e * np + j holds rows r0 + 2j, r0 + 2j + 1 of expert e (landed with
+        // the rotary rows, which the QKV publication waits for)
+        const int r0 = 2 * rfl(tab_wg[2 * PH_O]), np = rfl(tab_wg[2 * PH_O + 1]) - rfl(tab_wg[2 * PH_O]);
+        const rsrc_t r = make_rsrc(P.w + (size_t)id.l * P.layer_stride + P.off_gu, (uint32_t)(P.E * P.d * 2));
+        for (int i0 = 0; i0 < P.E * np; i0 += 64) {
+          const int i = i0 + lane, e = i / max(np, 1);
+          const uint32_t off = i < P.E * np ? (uint32_t)(e * P.d + r0 + 2 * (i - e * np)) * 2u : kOOB;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(smem + M::MoeWr + i0), 4, off, 0, 0, 0);
+        }
+      }
     }
     if (norm_phase(id)) {
       // every wave has applied this phase's gains: fetch the next normed
@@ -2266,12 +2352,23 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     }
     if constexpr (MOE) {
       if (id.ph == PH_GU) {
-        __syncthreads();   // SR: the router's logits are in out[0, E)
+        moe_router_sums(P, aux + kAuxRouter);
+        __syncthreads();   // SR: every wave's share of the router logits is in LDS
         // wave 0's routing words stay in LDS for the publication and the
         // down phase; workgroup 0 records the routing of the step's position
-        moe_route(P, out, red, aux + kAuxRoute);
+        moe_route(P, aux + kAuxRouter, red, aux + kAuxRoute);
+        const int* route = reinterpret_cast<const int*>(aux) + kAuxRoute;
         if (blockIdx.x == 0 && lane < P.topk)
-          st_coh(P.routes + ((size_t)pos * P.L + id.l) * P.topk + lane, reinterpret_cast<const int*>(aux)[kAuxRoute + lane]);
+          st_coh(P.routes + ((size_t)pos * P.L + id.l) * P.topk + lane, route[lane]);
+        // the row scales of this workgroup's down-phase output pairs in every
+        // chosen expert, [slot][2 np], for the down phase's streamers (they
+        // land while the experts' gate/up rows stream)
+        const int r0 = 2 * rfl(tab_wg[2 * PH_DOWN]), nr = 2 * rfl(tab_wg[2 * PH_DOWN + 1]) - r0;
+        const float* sd = P.esc + (size_t)id.l * P.sc_stride + P.sc_d;
+        for (int i = lane; i < P.topk * nr; i += 64) {
+          const int k = i / nr;
+          aux[kAuxMoe + i] = ldg(sd + (size_t)route[k] * P.d + r0 + (i - k * nr));
+        }
       }
     }
     // server launch: read the next request ahead, while the streamers run --
@@ -2294,7 +2391,8 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
         __syncthreads();   // S2b
       }
     w0_store_outputs<MB, MOE>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
-                              lg_mode(A, prev_i, cur_lg), scl, out, xown, aux, gs);
+                              lg_mode(A, prev_i, cur_lg), scl, out, xown, aux, gs,
+                              reinterpret_cast<const uint16_t*>(smem + M::MoeWr));
   }
   if (DEC_COLD(A.server) && blockIdx.x == 0) srv_flush_done(P, done_pending);
   wait_vm0();
