@@ -1737,31 +1737,34 @@ __device__ __forceinline__ void dot16_e4m3x2(u32x4 w0, u32x4 w1, const float* x,
 // publication adds its own rows' share, router[e][r] * g[r] * x[r] for the
 // FFN norm's gains g, into P.rpart[workgroup][e].  After the barrier each
 // wave w sums the shares of workgroups w, w + 8, ... in that order
-// (moe_router_sums, into LDS), and every wave adds the eight sums in wave
-// order: the same bits in every wave and every workgroup.
-__device__ __forceinline__ void moe_router_sums(const Params& P, float* rs) {
+// (moe_router_issue / moe_router_finish, into LDS), and every wave adds the
+// eight sums in wave order: the same bits in every wave and every workgroup.
+// Split in two so that the shares' loads are in flight while the wave
+// applies the norm gains: moe_router_issue requests the first 32 shares of
+// this wave's workgroups (all of them for a grid of up to 256),
+// moe_router_finish adds them (and any further ones) in workgroup order and
+// stores the wave's sum.
+constexpr int kRouterChunk = 32;
+__device__ __forceinline__ void moe_router_issue(const Params& P, float (&v)[kRouterChunk]) {
   const int lane = threadIdx.x & 63, w = rfl((int)(threadIdx.x >> 6)), G = gridDim.x;
-  // 32 shares per lane requested before any is added (one round trip for a
-  // grid of up to 256 workgroups), added in workgroup order
-  constexpr int kChunk = 32;
-  float acc = 0.f;
-  if (lane < P.E) {
-    for (int g0 = w; g0 < G; g0 += kChunk * kWaves) {
-      float v[kChunk];
 #pragma unroll
-      for (int k = 0; k < kChunk; ++k) {
-        const int g = g0 + kWaves * k;
-        v[k] = g < G ? ld_coh(P.rpart + (size_t)g * kMoeMaxExperts + lane) : 0.f;
-      }
-#pragma unroll
-      for (int k = 0; k < kChunk; ++k) acc += v[k];
-    }
+  for (int k = 0; k < kRouterChunk; ++k) {
+    const int g = w + kWaves * k;
+    v[k] = (lane < P.E && g < G) ? ld_coh(P.rpart + (size_t)g * kMoeMaxExperts + lane) : 0.f;
   }
+}
+__device__ __forceinline__ void moe_router_finish(const Params& P, const float (&v)[kRouterChunk], float* rs) {
+  const int lane = threadIdx.x & 63, w = rfl((int)(threadIdx.x >> 6)), G = gridDim.x;
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < kRouterChunk; ++k) acc += v[k];
+  if (lane < P.E)
+    for (int g = w + kWaves * kRouterChunk; g < G; g += kWaves) acc += ld_coh(P.rpart + (size_t)g * kMoeMaxExperts + lane);
   rs[w * kMoeMaxExperts + lane] = acc;
 }
 
 // Every wave, into its routing words rt (LDS, 16 per wave): the top_k
-// experts of the router's logits (the sums rs of moe_router_sums, times the
+// experts of the router's logits (the sums rs of moe_router_finish, times the
 // phase's norm scale, formed here from the waves' shares of sum(x^2) in the
 // order wave 0 forms it) -- largest logit first, the lower index first on
 // equal logits -- then from word 8 their weights, the softmax of the chosen
@@ -1778,15 +1781,10 @@ __device__ __forceinline__ void moe_route(const Params& P, const float* rs, cons
   float v = lane < P.E ? sum * scale : -INFINITY;
   float mine = 0.f;   // lane s: the s-th chosen logit
   for (int s = 0; s < P.topk; ++s) {
-    float best = v;
-    int bi = lane;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(best, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-    }
-    bi = min(max(rfl(bi), 0), P.E - 1);
+    // the largest remaining logit (DPP maximum), at its lowest lane (ballot)
+    const float best = wave_max(v);
+    const uint64_t hit = __ballot(v == best);
+    const int bi = min(hit ? (int)__builtin_ctzll(hit) : 0, P.E - 1);
     if (lane == s) {
       reinterpret_cast<int*>(rt)[s] = bi;
       mine = best;
@@ -1864,9 +1862,9 @@ __device__ __forceinline__ void moe_issue(const Params& P, const MoeGeo& g, rsrc
 // to out by ds_add, at most two contributors per row pair
 // (streamer_range).  A down row's sum over one expert is scaled by that
 // row's scale before the next expert's is added.  sel: this wave's routing
-// words.  (Issuing the down phase's first units at the end of the GU stream,
-// across the barrier, made the step slower: the early finishers' loads took
-// bandwidth from the GU phase's last workgroups.)
+// words.  (Issuing the down phase's first units ahead, at the end of the GU
+// stream or before the down phase's barrier, made the step slower: 1.35 and
+// 1.22 against 1.16 ms traced on moe2b.)
 template <bool DOWN>
 __device__ __forceinline__ void moe_stream(const Params& P, int l, int s, const int* tab_wg, const int* sel,
                                            int eslot, const float* sc_lds, const float* xs, float* out,
@@ -1940,7 +1938,10 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
     }
     __syncthreads();   // S1a
     if (si[12] == 0) break;
+    float rv[kRouterChunk];   // mixture of experts, GU: the router-logit shares in flight
+    if (MOE && id.ph == PH_GU) moe_router_issue(P, rv);
     if (norm_phase(id)) apply_gains(xs, gs, P.d, red);
+    if (MOE && id.ph == PH_GU) moe_router_finish(P, rv, aux + kAuxRouter);
     __syncthreads();   // S1
     if (is_gemv(id.ph)) {
       const int* e = tab + id.ph * kTabStride;
@@ -1981,8 +1982,7 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
     }
     if constexpr (MOE) {
       if (id.ph == PH_GU) {
-        moe_router_sums(P, aux + kAuxRouter);
-        __syncthreads();   // SR: every wave's share of the router logits is in LDS
+        // (S1 above: every wave's sum of the router-logit shares is in LDS)
         const int w = rfl((int)(threadIdx.x >> 6));
         float* rt = aux + kAuxRoute + 16 * w;
         moe_route(P, aux + kAuxRouter, red, rt);
@@ -2302,10 +2302,13 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
         __syncthreads();   // S1b
       }
     }
+    float rv[kRouterChunk];   // mixture of experts, GU: the router-logit shares in flight
+    if (MOE && id.ph == PH_GU) moe_router_issue(P, rv);
     if (norm_phase(id)) {
       if constexpr (MB == 1) apply_gains(xs, gs, P.d, red);
       else if (!dma_input(id)) apply_gains_batch(reinterpret_cast<_Float16*>(xs), stage, gs, P.d, B, red);
     }
+    if (MOE && id.ph == PH_GU) moe_router_finish(P, rv, aux + kAuxRouter);
     __syncthreads();   // S1
     if (DEC_COLD(P.stress)) w0_poison<MB>(P, id.ph, id.l, tab_wg);
     if (id.ph == PH_ATTN) w0_merge_wg<MB>(P, pos, A.pos_end, wg_per_head(P, pos), aux + kAuxPart);
@@ -2352,8 +2355,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
     }
     if constexpr (MOE) {
       if (id.ph == PH_GU) {
-        moe_router_sums(P, aux + kAuxRouter);
-        __syncthreads();   // SR: every wave's share of the router logits is in LDS
+        // (S1 above: every wave's sum of the router-logit shares is in LDS)
         // wave 0's routing words stay in LDS for the publication and the
         // down phase; workgroup 0 records the routing of the step's position
         moe_route(P, aux + kAuxRouter, red, aux + kAuxRoute);
