@@ -24,6 +24,10 @@ The pages fix no router or expert detail; the readings taken here:
     format: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, exponent
     field 0 subnormal, S.1111.111 NaN, no infinities) with one float32 scale
     per output row: W[r, c] = value(code[r, c]) * scale[r];
+  * or, with the MXFP4 format, OCP microscaling blocks: FP4 E2M1 codes (1
+    sign, 2 exponent bits with bias 1, 1 mantissa bit, exponent field 0
+    subnormal) two to a byte, element 2i in the low nibble, and one E8M0
+    scale (2^(s - 127), 0xFF NaN) per 32 consecutive elements of a row;
   * no shared expert, no expert bias, no capacity limit (one token).
 Attention, norms, rotary embedding, KV cache and LM head are those of the
 dense reference decoder (oracle.decoder).  Arithmetic is float64.
@@ -67,6 +71,45 @@ def dequant(codes, scales):
 
 
 # ----------------------------------------------------------------------------
+# MXFP4: E2M1 elements, E8M0 block scales
+# ----------------------------------------------------------------------------
+
+MX_BLOCK = 32
+
+
+def e2m1_value(nibble):
+    """The value of one E2M1 code (an int 0..15)."""
+    n = int(nibble)
+    sign = -1.0 if n & 8 else 1.0
+    e = (n >> 1) & 3
+    m = n & 1
+    if e == 0:
+        return sign * 0.5 * m
+    return sign * (1.0 + 0.5 * m) * 2.0 ** (e - 1)
+
+
+def e8m0_value(byte):
+    """The value of one E8M0 scale (an int 0..255): 2^(byte - 127), 0xFF NaN."""
+    b = int(byte)
+    return float("nan") if b == 0xFF else 2.0 ** (b - 127)
+
+
+E2M1_TABLE = np.array([e2m1_value(n) for n in range(16)], dtype=np.float64)
+E8M0_TABLE = np.array([e8m0_value(b) for b in range(256)], dtype=np.float64)
+
+
+def mx_dequant(codes, scales):
+    """W [R, K] (float64) from packed codes [R, K/2] (element 2i in the low
+    nibble of byte i) and E8M0 scales [R, K/32]."""
+    c = np.asarray(codes, dtype=np.uint8)
+    vals = np.empty((c.shape[0], 2 * c.shape[1]))
+    vals[:, 0::2] = E2M1_TABLE[c & 0x0F]
+    vals[:, 1::2] = E2M1_TABLE[c >> 4]
+    sc = E8M0_TABLE[np.asarray(scales, dtype=np.uint8)]
+    return vals * np.repeat(sc, MX_BLOCK, axis=1)
+
+
+# ----------------------------------------------------------------------------
 # router and experts
 # ----------------------------------------------------------------------------
 
@@ -105,9 +148,10 @@ class MoEWeights:
         """Expert e of layer l as float64 (Wg [F, d], Wu [F, d], Wd [d, F])."""
         lw = self.layers[l]
         F, d = self.shape.d_ffn, self.shape.d_model
-        g = dequant(lw["Wg8"][e * F:(e + 1) * F], lw["sg"][e * F:(e + 1) * F])
-        u = dequant(lw["Wu8"][e * F:(e + 1) * F], lw["su"][e * F:(e + 1) * F])
-        dn = dequant(lw["Wd8"][e * d:(e + 1) * d], lw["sd"][e * d:(e + 1) * d])
+        deq = mx_dequant if getattr(self.shape, "mxfp4", False) else dequant
+        g = deq(lw["Wg8"][e * F:(e + 1) * F], lw["sg"][e * F:(e + 1) * F])
+        u = deq(lw["Wu8"][e * F:(e + 1) * F], lw["su"][e * F:(e + 1) * F])
+        dn = deq(lw["Wd8"][e * d:(e + 1) * d], lw["sd"][e * d:(e + 1) * d])
         return g, u, dn
 
 

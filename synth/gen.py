@@ -24,6 +24,11 @@ follows the magnitudes of a standard normal (1/16 of the codes subnormal,
 none with the all-ones exponent, so no NaN and no value above 3.75), and
 every row's scale is 0.01 * (0.75 + 0.5 u), u uniform.  The router is drawn
 like the other fp16 matrices.
+
+MXFP4 experts (shape.mxfp4) fill the same slots with OCP microscaling
+blocks: Wg8 / Wu8 [E*F, d/2] and Wd8 [E*d, F/2] hold two E2M1 codes per
+byte (uniform random bytes), sg / su [E*F, d/32] and sd [E*d, F/32] one E8M0
+scale per 32 weights of a row (118, 119 or 120 uniformly, i.e. 2^-9 .. 2^-7).
 """
 import os
 from concurrent.futures import ThreadPoolExecutor
@@ -60,6 +65,9 @@ def tensor_shapes(shape: ModelShape):
            "g_ffn": (d,), "Wg": (f, d), "Wu": (f, d), "Wd": (d, f),
            "Wr": (E, d), "Wg8": (E * f, d), "sg": (E * f,), "Wu8": (E * f, d), "su": (E * f,),
            "Wd8": (E * d, f), "sd": (E * d,)}
+    if getattr(shape, "mxfp4", False):
+        per.update({"Wg8": (E * f, d // 2), "sg": (E * f, d // 32), "Wu8": (E * f, d // 2), "su": (E * f, d // 32),
+                    "Wd8": (E * d, f // 2), "sd": (E * d, f // 32)})
     shapes = [(shape.vocab, d)]
     for _ in range(shape.n_layers):
         shapes += [per[t] for t in layer_tensors(shape)]
@@ -73,6 +81,16 @@ def _draw_codes(shp, seed, index):
     u = rng.integers(0, 256, size=shp, dtype=np.uint8)
     e = _EXP_FIELD[rng.integers(0, 16, size=shp, dtype=np.uint8)]
     return (u & np.uint8(0x87)) | (e << np.uint8(3))
+
+
+def _draw_mx_codes(shp, seed, index):
+    """Two E2M1 codes per byte, every byte value equally likely."""
+    return np.random.default_rng([seed, index]).integers(0, 256, size=shp, dtype=np.uint8)
+
+
+def _draw_mx_scales(shp, seed, index):
+    """E8M0 block scales 118, 119 or 120."""
+    return np.random.default_rng([seed, index]).integers(118, 121, size=shp, dtype=np.uint8)
 
 
 def _draw_scales(shp, seed, index):
@@ -101,10 +119,11 @@ def make_weights(shape: ModelShape, seed: int = 0, gain_jitter: float = 0.0):
                 return (1.0 + gain_jitter * rng.standard_normal(shp)).astype(np.float16)
             return np.ones(shp, dtype=np.float16)
         base = name.split(".")[0]
+        mx = getattr(shape, "mxfp4", False)
         if base in ("Wg8", "Wu8", "Wd8"):
-            return _draw_codes(shp, seed, idx)
+            return _draw_mx_codes(shp, seed, idx) if mx else _draw_codes(shp, seed, idx)
         if base in ("sg", "su", "sd"):
-            return _draw_scales(shp, seed, idx)
+            return _draw_mx_scales(shp, seed, idx) if mx else _draw_scales(shp, seed, idx)
         return _draw(shp, seed, idx)
 
     items = list(enumerate(zip(tensor_names(shape), tensor_shapes(shape))))

@@ -27,6 +27,9 @@ class ModelShape:
     # which a router picks top_k per token
     n_experts: int = 0
     top_k: int = 0
+    # expert weights as OCP MXFP4 blocks (E2M1 pairs, an E8M0 scale per 32)
+    # instead of E4M3 codes with a float32 scale per row
+    mxfp4: bool = False
 
     @property
     def qkv_width(self) -> int:
@@ -65,6 +68,8 @@ LANE_2B = DENSE_2B.with_(n_heads=3, d_ffn=864, lm_vocab=8192)
 # dense2b's 6912 columns at half the bytes.
 MOE_2B = DENSE_2B.with_(d_ffn=1728, n_experts=32, top_k=4)
 TINY_MOE = TINY.with_(d_ffn=256, n_experts=8, top_k=2)
+# the same experts in MXFP4
+MOE_2B_MX = MOE_2B.with_(mxfp4=True)
 
 WORKLOADS = {
     "tiny": Workload("tiny", TINY, prompt_len=16, steps=32, batch=1,
@@ -77,6 +82,8 @@ WORKLOADS = {
                              description="dense2b from a 3968-token prompt to the 4096 cap"),
     "moe2b": Workload("moe2b", MOE_2B, prompt_len=128, steps=512, batch=1,
                       description="dense2b attention with 32 FP8 experts of width 1728, top-4 routing"),
+    "moe2b_mx": Workload("moe2b_mx", MOE_2B_MX, prompt_len=128, steps=512, batch=1,
+                         description="moe2b with MXFP4 experts (E2M1 pairs, an E8M0 scale per 32 weights)"),
     "dense2b_b8": Workload("dense2b_b8", DENSE_2B, prompt_len=256, steps=256, batch=8,
                            description="dense2b, 8 sequences of 256 prompt tokens decoded together"),
 }

@@ -251,3 +251,84 @@ def test_matrix_prefill_with_forced_routes_equals_forced_steps():
         # the returned routes are the router's own choice on the forced path
         np.testing.assert_array_equal(dec.last_natural, routes[i])
     np.testing.assert_array_equal(dec.Kc[:, :, :6], K16)
+
+
+# ----------------------------------------------------------------------------
+# MXFP4 (OCP microscaling: E2M1 elements, an E8M0 scale per 32)
+# ----------------------------------------------------------------------------
+
+TINY_MX = TINY_MOE.with_(mxfp4=True)
+
+
+def test_e2m1_values_are_the_format_table():
+    # the eight magnitudes the OCP MX specification lists for E2M1, then the
+    # same with the sign bit set (negative zero included)
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert [O.e2m1_value(n) for n in range(8)] == mags
+    assert [O.e2m1_value(n | 8) for n in range(8)] == [-m for m in mags]
+    assert math.copysign(1.0, O.e2m1_value(8)) == -1.0
+
+
+def test_e2m1_through_e4m3_bit_placement():
+    # a second route: an E2M1 code's bits placed in an E4M3 code (exponent
+    # field + 6, the mantissa bit at the top of the mantissa) give the same
+    # value for every normal code; the subnormal one is 0.5 = E4M3 0x30
+    for n in range(16):
+        e, m, s = (n >> 1) & 3, n & 1, (n >> 3) & 1
+        if e == 0:
+            code = (s << 7) | (0x30 if m else 0)
+        else:
+            code = (s << 7) | ((e + 6) << 3) | (m << 2)
+        assert O.e4m3_value(code) == O.e2m1_value(n), n
+
+
+def test_e8m0_matches_torch_float8_e8m0fnu():
+    b = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(b).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = np.array([O.e8m0_value(x) for x in range(256)])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    # torch reads code 0 as 2^-127 as the format defines; every code's value
+    assert np.array_equal(got[:255], ref[:255])
+    assert O.e8m0_value(127) == 1.0 and O.e8m0_value(120) == 2.0 ** -7
+
+
+def test_mx_dequant_nibble_order_and_block_scales():
+    # row 0: bytes 0x21 -> elements 0.5 (low nibble 1), 1.0 (high nibble 2);
+    # block 0 (elements 0..31) scaled by 2^1, block 1 (32..63) by 2^-2
+    codes = np.zeros((1, 32), dtype=np.uint8)
+    codes[0, 0] = 0x21
+    codes[0, 16] = 0xF7          # elements 32, 33: 6.0 and -6.0
+    scales = np.array([[128, 125]], dtype=np.uint8)
+    w = O.mx_dequant(codes, scales)
+    assert w.shape == (1, 64)
+    assert w[0, 0] == 1.0 and w[0, 1] == 2.0 and w[0, 32] == 1.5 and w[0, 33] == -1.5
+    assert np.count_nonzero(w) == 4
+
+
+def test_single_mx_expert_equals_dense_decoder():
+    # MXFP4 values with these scales are exact in fp16
+    shp = TINY_MX.with_(n_experts=1, top_k=1)
+    t = synth.make_weights(shp, seed=31, gain_jitter=0.1)
+    dshape = shp.with_(n_experts=0, top_k=0, mxfp4=False)
+    names = synth.tensor_names(shp)
+    dense = []
+    for i, (name, x) in enumerate(zip(names, t)):
+        base = name.split(".")[0]
+        if base in ("Wg8", "Wu8", "Wd8"):
+            sc = t[i + 1]
+            dense.append(O.mx_dequant(x, sc).astype(np.float16))
+        elif base not in ("sg", "su", "sd", "Wr"):
+            dense.append(x)
+    a, b = O.OracleMoEDecoder(shp, t), O.OracleDecoder(dshape, dense)
+    for tok in (3, 900, 17):
+        np.testing.assert_allclose(a.step(tok), b.step(tok), rtol=1e-12, atol=1e-12)
+
+
+def test_mx_model_step_and_matrix_forms_agree():
+    t = synth.make_weights(TINY_MX, seed=32, gain_jitter=0.1)
+    toks = synth.make_prompt(TINY_MX.vocab, 7, seed=8)[0]
+    lg, K16, V16, routes, gaps = O.prefill_matrix_moe(TINY_MX, t, toks)
+    dec = O.OracleMoEDecoder(TINY_MX, t)
+    for i, tok in enumerate(toks):
+        np.testing.assert_allclose(dec.step(int(tok)), lg[i], rtol=1e-10, atol=1e-11)
+        np.testing.assert_array_equal(dec.last_routes, routes[i])
