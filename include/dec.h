@@ -94,8 +94,8 @@ typedef enum dec_status {
  * 今後のマイルストーンと課題).  Rules (DEC_ERR_BAD_DESC otherwise):
  * n_experts == 0 and top_k == 0 for a dense model; else 2 <= n_experts <= 64,
  * n_experts even, 1 <= top_k <= min(n_experts, 8).  Limits
- * (DEC_ERR_UNSUPPORTED): batch 1, flags 0, d_model and d_ffn multiples of
- * 16, top_k * d_ffn <= 7168, each layer's expert matrices under 2 GiB of
+ * (DEC_ERR_UNSUPPORTED): batch 1, flags 0 or DEC_FLAG_EXPERTS_MXFP4, d_model
+ * and d_ffn multiples of 16 (32 with MXFP4), top_k * d_ffn <= 7168, each layer's expert matrices under 2 GiB of
  * codes; weights from host tensors only (not a DECW file), not with
  * dec_init_noalloc, dec_pack or DEC_DEBUG_MULTILAUNCH.  Numerics: the
  * router's top_k choice is made on fp32 logits; a choice between two
@@ -135,6 +135,17 @@ typedef enum dec_status {
  * the softmax weights of the attention products.  Decode steps are unchanged.
  */
 #define DEC_FLAG_MATRIX_PREFILL 0x4u
+/*
+ * DEC_FLAG_EXPERTS_MXFP4 (mixture of experts only): the expert matrices are
+ * OCP microscaling MXFP4 blocks instead of E4M3 codes with row scales --
+ * FP4 E2M1 codes two to a byte (element 2i in the low nibble) and one E8M0
+ * scale, 2^(s - 127), per 32 consecutive weights of a row: the pages' FP4
+ * expert format (page 標準GPUによるリアルタイムLLM推論, section Hackerたちの意見).
+ * Needs d_model and d_ffn multiples of 32.  Tensors (see dec_weights_src):
+ * Wg8, Wu8 [E*F, d/2] and Wd8 [E*d, F/2] uint8 code pairs; sg, su
+ * [E*F, d/32] and sd [E*d, F/32] uint8 scales.
+ */
+#define DEC_FLAG_EXPERTS_MXFP4 0x8u
 
 typedef struct dec_model_desc {
   int32_t n_layers;
@@ -149,7 +160,7 @@ typedef struct dec_model_desc {
   int32_t batch;      /* sequences decoded together                    */
   float rms_eps;
   float rope_base;
-  uint32_t flags;     /* 0, DEC_FLAG_BATCHED_PREFILL or DEC_FLAG_MATRIX_PREFILL */
+  uint32_t flags;     /* 0, DEC_FLAG_BATCHED_PREFILL, DEC_FLAG_MATRIX_PREFILL or (experts) DEC_FLAG_EXPERTS_MXFP4 */
   int32_t n_experts;  /* 0: dense MLP; else experts per layer (mixture of experts) */
   int32_t top_k;      /* experts each token uses (mixture of experts), else 0 */
 } dec_model_desc;

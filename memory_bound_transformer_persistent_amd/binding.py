@@ -32,6 +32,7 @@ DEC_DEBUG_FENCED = 0x4
 DEC_DEBUG_STRESS = 0x8
 DEC_FLAG_BATCHED_PREFILL = 0x2
 DEC_FLAG_MATRIX_PREFILL = 0x4
+DEC_FLAG_EXPERTS_MXFP4 = 0x8
 
 ERR_NAMES = {v: k for k, v in globals().items() if k.startswith("DEC_ERR_")}
 
@@ -58,7 +59,8 @@ class ModelDesc(ctypes.Structure):
         """From any object with the model-shape attributes."""
         kw = dict(n_layers=s.n_layers, d_model=s.d_model, n_heads=s.n_heads, n_kv_heads=s.n_heads,
                   head_dim=s.head_dim, d_ffn=s.d_ffn, vocab=s.vocab, lm_vocab=s.lm_vocab,
-                  max_ctx=s.max_ctx, batch=batch, rms_eps=s.rms_eps, rope_base=s.rope_base, flags=0,
+                  max_ctx=s.max_ctx, batch=batch, rms_eps=s.rms_eps, rope_base=s.rope_base,
+                  flags=DEC_FLAG_EXPERTS_MXFP4 if getattr(s, "mxfp4", False) else 0,
                   n_experts=getattr(s, "n_experts", 0), top_k=getattr(s, "top_k", 0))
         kw.update(override)
         return cls(**kw)

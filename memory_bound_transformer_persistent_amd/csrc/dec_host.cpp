@@ -38,6 +38,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t n, size_t a = kAlign) { return (n + a - 1) / a * a; }
 
 bool moe(const dec_model_desc& d) { return d.n_experts > 0; }
+bool mxfp4(const dec_model_desc& d) { return moe(d) && (d.flags & DEC_FLAG_EXPERTS_MXFP4) != 0; }
 // canonical tensors per layer: dense 9; mixture of experts 13 (the MLP's
 // three matrices become the router, three code matrices and their scales)
 int per_layer(const dec_model_desc& d) { return moe(d) ? 13 : 9; }
@@ -61,8 +62,10 @@ int check_desc_impl(const dec_model_desc* d, std::string* err) {
   if (d->max_ctx < 1 || d->max_ctx > 65536) return fail(err, DEC_ERR_BAD_DESC, "max_ctx must be in [1, 65536] (got %d)", d->max_ctx);
   if (!(d->rms_eps > 0.f) || !std::isfinite(d->rms_eps)) return fail(err, DEC_ERR_BAD_DESC, "rms_eps must be > 0");
   if (!(d->rope_base > 1.f) || !std::isfinite(d->rope_base)) return fail(err, DEC_ERR_BAD_DESC, "rope_base must be > 1");
-  if (d->flags & ~(DEC_FLAG_BATCHED_PREFILL | DEC_FLAG_MATRIX_PREFILL))
+  if (d->flags & ~(DEC_FLAG_BATCHED_PREFILL | DEC_FLAG_MATRIX_PREFILL | DEC_FLAG_EXPERTS_MXFP4))
     return fail(err, DEC_ERR_BAD_DESC, "unknown flags 0x%x", d->flags);
+  if ((d->flags & DEC_FLAG_EXPERTS_MXFP4) && d->n_experts == 0)
+    return fail(err, DEC_ERR_BAD_DESC, "DEC_FLAG_EXPERTS_MXFP4 is for a mixture of experts");
   const bool bp = (d->flags & DEC_FLAG_BATCHED_PREFILL) != 0;
   const bool mp = (d->flags & DEC_FLAG_MATRIX_PREFILL) != 0;
   if (bp && mp) return fail(err, DEC_ERR_BAD_DESC, "DEC_FLAG_BATCHED_PREFILL and DEC_FLAG_MATRIX_PREFILL exclude each other");
@@ -76,10 +79,13 @@ int check_desc_impl(const dec_model_desc* d, std::string* err) {
       return fail(err, DEC_ERR_BAD_DESC, "n_experts must be 0 or even and in [2, %d] (got %d)", kMoeMaxExperts, d->n_experts);
     if (d->top_k < 1 || d->top_k > std::min(d->n_experts, kMoeMaxTopK))
       return fail(err, DEC_ERR_BAD_DESC, "top_k must be in [1, min(n_experts, %d)] (got %d)", kMoeMaxTopK, d->top_k);
-    if (d->batch != 1 || d->flags)
-      return fail(err, DEC_ERR_UNSUPPORTED, "a mixture-of-experts model runs at batch 1 with flags 0");
+    if (d->batch != 1 || (d->flags & ~DEC_FLAG_EXPERTS_MXFP4))
+      return fail(err, DEC_ERR_UNSUPPORTED, "a mixture-of-experts model runs at batch 1 with flags 0 or "
+                  "DEC_FLAG_EXPERTS_MXFP4");
     if (d->d_model % 16 || d->d_ffn % 16)
       return fail(err, DEC_ERR_UNSUPPORTED, "a mixture-of-experts model needs d_model and d_ffn multiples of 16");
+    if ((d->flags & DEC_FLAG_EXPERTS_MXFP4) && (d->d_model % 32 || d->d_ffn % 32))
+      return fail(err, DEC_ERR_UNSUPPORTED, "MXFP4 experts need d_model and d_ffn multiples of 32");
     if ((long long)d->top_k * d->d_ffn > kMaxK - 1024)
       return fail(err, DEC_ERR_UNSUPPORTED, "top_k * d_ffn must be <= %d", kMaxK - 1024);
     if ((long long)d->n_experts * 2 * d->d_ffn * d->d_model >= (1LL << 31))
@@ -128,7 +134,7 @@ struct Image {
   size_t off_qkv, off_o, off_gu, off_d, layer_stride, off_E, off_lm, total;
   bool tiled;
   size_t e8_d, e8_stride, e8_total;     // expert codes (bytes)
-  size_t sc_d, sc_stride, sc_total;     // expert row scales (floats)
+  size_t sc_d, sc_stride, sc_total;     // expert row scales (floats), or MXFP4 block scales (bytes)
 };
 
 size_t al128(size_t n) { return (n + 127) / 128 * 128; }
@@ -164,11 +170,19 @@ Image image_layout(const dec_model_desc& d) {
     const size_t E = d.n_experts;
     im.off_d = al128(im.off_gu + E * D);
     im.layer_stride = im.off_d;
-    im.e8_d = align_up(E * 2 * F * D);
-    im.e8_stride = align_up(im.e8_d + E * D * F);
+    if (mxfp4(d)) {
+      // E2M1 pairs: half a byte per weight; E8M0 scales: a byte per 32 weights
+      im.e8_d = align_up(E * F * D);
+      im.e8_stride = align_up(im.e8_d + E * D * F / 2);
+      im.sc_d = E * F * 2 * (D / 32);
+      im.sc_stride = align_up(im.sc_d + E * D * (F / 32));
+    } else {
+      im.e8_d = align_up(E * 2 * F * D);
+      im.e8_stride = align_up(im.e8_d + E * D * F);
+      im.sc_d = E * F * 2;
+      im.sc_stride = align_up(im.sc_d + E * D, 64);
+    }
     im.e8_total = im.e8_stride * d.n_layers;
-    im.sc_d = E * F * 2;
-    im.sc_stride = align_up(im.sc_d + E * D, 64);
     im.sc_total = im.sc_stride * d.n_layers;
   } else {
     im.off_d = al128(im.off_gu + matrix_elems(2 * F, D, t));
@@ -199,15 +213,16 @@ void tensor_shape(const dec_model_desc& d, int idx, size_t* r, size_t* c) {
   if (idx == last - 1) { *r = D; *c = 1; return; }
   if (moe(d)) {
     const size_t E = d.n_experts;
+    const bool mx = mxfp4(d);
     switch ((idx - 1) % 13) {
       case 0: case 5: *r = D; *c = 1; return;            // gains
       case 1: case 2: case 3: *r = q; *c = D; return;     // Wq, Wk, Wv
       case 4: *r = D; *c = q; return;                     // Wo
       case 6: *r = E; *c = D; return;                     // Wr
-      case 7: case 9: *r = E * F; *c = D; return;         // Wg8, Wu8
-      case 8: case 10: *r = E * F; *c = 1; return;        // sg, su
-      case 11: *r = E * D; *c = F; return;                // Wd8
-      default: *r = E * D; *c = 1; return;                // sd
+      case 7: case 9: *r = E * F; *c = mx ? D / 2 : D; return;     // Wg8, Wu8 (MXFP4: code pairs)
+      case 8: case 10: *r = E * F; *c = mx ? D / 32 : 1; return;   // sg, su (MXFP4: block scales)
+      case 11: *r = E * D; *c = mx ? F / 2 : F; return;            // Wd8
+      default: *r = E * D; *c = mx ? F / 32 : 1; return;           // sd
     }
   }
   switch ((idx - 1) % 9) {
@@ -267,14 +282,23 @@ void place_tensor(const dec_model_desc& d, const Image& im, int idx, const uint1
     const float* sf = reinterpret_cast<const float*>(src);
     uint8_t* lay8 = image8 + (size_t)l * im.e8_stride;
     float* lsc = scales + (size_t)l * im.sc_stride;
+    // MXFP4: the scale image holds bytes (E8M0), C of them per row
+    uint8_t* lsx = reinterpret_cast<uint8_t*>(scales) + (size_t)l * im.sc_stride;
+    const bool mx = mxfp4(d);
     for (size_t i = 0; i < nrows; ++i) {
       const size_t r = row0 + i;
       switch (kind) {
         case 6: put_row(lay, im.off_gu, r, src + i * C, C, false); break;   // router
-        case 7: case 9: std::memcpy(lay8 + (2 * r + (kind == 9)) * D, s8 + i * C, C); break;
-        case 8: case 10: lsc[2 * r + (kind == 10)] = sf[i]; break;
-        case 11: std::memcpy(lay8 + im.e8_d + r * F, s8 + i * C, C); break;
-        default: lsc[im.sc_d + r] = sf[i]; break;
+        case 7: case 9: std::memcpy(lay8 + (2 * r + (kind == 9)) * C, s8 + i * C, C); break;
+        case 8: case 10:
+          if (mx) std::memcpy(lsx + (2 * r + (kind == 10)) * C, s8 + i * C, C);
+          else lsc[2 * r + (kind == 10)] = sf[i];
+          break;
+        case 11: std::memcpy(lay8 + im.e8_d + r * C, s8 + i * C, C); break;
+        default:
+          if (mx) std::memcpy(lsx + im.sc_d + r * C, s8 + i * C, C);
+          else lsc[im.sc_d + r] = sf[i];
+          break;
       }
     }
     return;
@@ -408,7 +432,7 @@ Arena arena_layout(const dec_model_desc& d, int G) {
   a.w2 = bp ? take(image_layout(prefill_desc(d)).total * 2) : 0;
   // mixture of experts: expert codes, their row scales, the routing record
   a.w8 = moe(d) ? take(im.e8_total) : 0;
-  a.esc = moe(d) ? take(im.sc_total * 4) : 0;
+  a.esc = moe(d) ? take(im.sc_total * (mxfp4(d) ? 1 : 4)) : 0;
   a.routes = moe(d) ? take((size_t)d.max_ctx * d.n_layers * d.top_k * 4) : 0;
   a.gains = take(((size_t)d.n_layers * 2 + 1) * D * 4);
   a.rope = take((size_t)d.max_ctx * (d.head_dim / 2) * 2 * 4);
@@ -814,7 +838,8 @@ int upload_weights(dec_handle* h, const dec_weights_src* src) {
   std::vector<float> g1(3 * (size_t)d.d_model);
   // mixture of experts: one layer's expert codes and scales
   std::vector<uint8_t> stage8(im1.e8_stride);
-  std::vector<float> stagesc(im1.sc_stride);
+  std::vector<float> stagesc(im1.sc_stride);   // (MXFP4: sc_stride bytes in the first quarter)
+  const size_t sc_bytes = mxfp4(d) ? local.sc_stride : local.sc_stride * 4;
   char* dev_w8 = static_cast<char*>(h->base) + h->ar.w8;
   char* dev_sc = static_cast<char*>(h->base) + h->ar.esc;
   const int per = per_layer(d);
@@ -838,7 +863,7 @@ int upload_weights(dec_handle* h, const dec_weights_src* src) {
     if (e == hipSuccess && moe(d)) {
       e = hipMemcpy(dev_w8 + (size_t)l * local.e8_stride, stage8.data(), local.e8_stride, hipMemcpyHostToDevice);
       if (e == hipSuccess)
-        e = hipMemcpy(dev_sc + (size_t)l * local.sc_stride * 4, stagesc.data(), local.sc_stride * 4, hipMemcpyHostToDevice);
+        e = hipMemcpy(dev_sc + (size_t)l * sc_bytes, stagesc.data(), sc_bytes, hipMemcpyHostToDevice);
     }
     if (e != hipSuccess) rc = hip_fail(h, &h->err, e, "hipMemcpy(weights)");
   }
@@ -1184,6 +1209,10 @@ int init_impl(const dec_model_desc* desc, const dec_weights_src* weights, const 
     P.sc_stride = h->im.sc_stride; P.sc_d = h->im.sc_d;
     P.routes = reinterpret_cast<int32_t*>(b + h->ar.routes);
     P.rpart = reinterpret_cast<float*>(sc(h->ar.rpart));
+    P.mx = mxfp4(*desc) ? 1 : 0;
+    P.xsc = reinterpret_cast<const uint8_t*>(b + h->ar.esc);
+    P.xsc_stride = h->im.sc_stride;
+    P.xsc_d = h->im.sc_d;
     e = hipMemset(P.routes, 0xFF, (size_t)desc->max_ctx * desc->n_layers * desc->top_k * 4);
     if (e != hipSuccess) { hip_fail(h, &h->err, e, "hipMemset(routes)"); return bail(DEC_ERR_DEVICE); }
   }

@@ -147,6 +147,9 @@ struct Params {
   const float* esc;           // expert row scales: per layer [E][Fe][2] (gate, up), then [E][d] at sc_d
   size_t sc_stride, sc_d;     // floats between layers; offset of the down scales inside a layer
   int32_t* routes;            // chosen experts [max_ctx][L][topk]
+  int mx;                     // 1: MXFP4 experts (w8 holds E2M1 pairs; xsc the E8M0 block scales)
+  const uint8_t* xsc;         // MXFP4 scales: per layer Wgu [E][Fe][2][d/32], then Wd [E][d][Fe/32] at xsc_d
+  size_t xsc_stride, xsc_d;   // bytes between layers; offset of the down scales inside a layer
   float* rpart;               // router logits' partial sums over each workgroup's rows [G][kMoeMaxExperts]
 };
 

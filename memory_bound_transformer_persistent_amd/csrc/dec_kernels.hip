@@ -1238,8 +1238,9 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l,
     const float w = rope_lds[kAuxRoute + kMoeMaxTopK + slot];
     const float* sc = P.esc + (size_t)l * P.sc_stride + (size_t)2 * ((size_t)e * P.Fe + q0);
     for (int t = lane; t < nq; t += 64) {
-      const float gt = out[kMoeOutPairs + 2 * t] * scl[0] * ldg(sc + 2 * t);
-      const float up = out[kMoeOutPairs + 2 * t + 1] * scl[0] * ldg(sc + 2 * t + 1);
+      // (MXFP4 rows have no row scale: their block scales were applied in the dot)
+      const float gt = out[kMoeOutPairs + 2 * t] * scl[0] * (P.mx ? 1.0f : ldg(sc + 2 * t));
+      const float up = out[kMoeOutPairs + 2 * t + 1] * scl[0] * (P.mx ? 1.0f : ldg(sc + 2 * t + 1));
       st_coh(P.act + (size_t)slot * P.Fe + q0 + t, gt / (1.0f + expf(-gt)) * up * w);
     }
     return;
@@ -1763,6 +1764,49 @@ __device__ __forceinline__ void moe_router_finish(const Params& P, const float (
   rs[w * kMoeMaxExperts + lane] = acc;
 }
 
+// 32 MXFP4 weights of each of two rows (a 16-byte load per row: one block)
+// times the same 32 fp32 inputs; fp32 accumulate.  v_cvt_scalef32_pk_f32_fp4
+// turns one byte into its two E2M1 values (low nibble first) times the
+// block's scale.
+__device__ __forceinline__ float e8m0_float(uint32_t s) {
+  // 2^(s - 127): the exponent field of an fp32, 2^-127 as a subnormal, 0xFF NaN
+  return __builtin_bit_cast(float, s == 0u ? 0x00400000u : (s == 255u ? 0x7FC00000u : s << 23));
+}
+__device__ __forceinline__ void dot32_mxfp4x2(u32x4 w0, u32x4 w1, float s0, float s1, const float* x, float& a0,
+                                              float& a1) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 xa = *reinterpret_cast<const f32x4*>(x + 8 * i);
+    const f32x4 xb = *reinterpret_cast<const f32x4*>(x + 8 * i + 4);
+    const uint32_t c0 = w0[i], c1 = w1[i];
+    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c0, s0, 0);
+    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c0, s0, 1);
+    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c0, s0, 2);
+    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c0, s0, 3);
+    const f32x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c1, s1, 0);
+    const f32x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c1, s1, 1);
+    const f32x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c1, s1, 2);
+    const f32x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c1, s1, 3);
+    const float x0 = xa[0], x1 = xa[1], x2 = xa[2], x3 = xa[3], x4 = xb[0], x5 = xb[1], x6 = xb[2], x7 = xb[3];
+    a0 = __builtin_fmaf(p0[0], x0, a0);
+    a0 = __builtin_fmaf(p0[1], x1, a0);
+    a0 = __builtin_fmaf(p1[0], x2, a0);
+    a0 = __builtin_fmaf(p1[1], x3, a0);
+    a0 = __builtin_fmaf(p2[0], x4, a0);
+    a0 = __builtin_fmaf(p2[1], x5, a0);
+    a0 = __builtin_fmaf(p3[0], x6, a0);
+    a0 = __builtin_fmaf(p3[1], x7, a0);
+    a1 = __builtin_fmaf(q0[0], x0, a1);
+    a1 = __builtin_fmaf(q0[1], x1, a1);
+    a1 = __builtin_fmaf(q1[0], x2, a1);
+    a1 = __builtin_fmaf(q1[1], x3, a1);
+    a1 = __builtin_fmaf(q2[0], x4, a1);
+    a1 = __builtin_fmaf(q2[1], x5, a1);
+    a1 = __builtin_fmaf(q3[0], x6, a1);
+    a1 = __builtin_fmaf(q3[1], x7, a1);
+  }
+}
+
 // Every wave, into its routing words rt (LDS, 16 per wave): the top_k
 // experts of the router's logits (the sums rs of moe_router_finish, times the
 // phase's norm scale, formed here from the waves' shares of sum(x^2) in the
@@ -1809,12 +1853,12 @@ static_assert(kAuxMoe + kMoeScaleFloats <= kAuxFloats, "aux LDS");
 struct MoeGeo {
   int p0, np, npc, tail, nsl, per, u0, n;
 };
-template <bool DOWN>
+template <bool DOWN, bool MX>
 __device__ __forceinline__ MoeGeo moe_geo(const Params& P, int s, const int* tab_wg) {
   MoeGeo g;
   g.p0 = rfl(tab_wg[DOWN ? 2 * PH_DOWN : kTabMoeSlot + 1]);
   g.np = rfl(tab_wg[DOWN ? 2 * PH_DOWN + 1 : kTabMoeSlot + 2]) - g.p0;
-  const int K = DOWN ? P.Fe : P.d;                      // a row's codes inside one expert
+  const int K = (DOWN ? P.Fe : P.d) / (MX ? 2 : 1);     // a row's bytes inside one expert
   g.npc = (K + 1023) >> 10;                             // 1 KB pieces per expert row
   g.tail = (K - 1024 * (g.npc - 1)) >> 4;               // lanes with codes in the last piece
   g.nsl = DOWN ? P.topk : 1;                            // experts per row pair
@@ -1839,18 +1883,27 @@ __device__ __forceinline__ MoeCur moe_cursor(const MoeGeo& g, int u) {
   c.issued = 0;
   return c;
 }
-template <bool DOWN>
-__device__ __forceinline__ void moe_issue(const Params& P, const MoeGeo& g, rsrc_t r, const int* sel, int eslot,
-                                          MoeCur& c, u32x4& b0, u32x4& b1) {
+// MXFP4: a lane's 16 bytes of a row are one 32-weight block, whose E8M0
+// scale is one byte of the scale image (rs; 2 per unit, in s0 and s1).
+template <bool DOWN, bool MX>
+__device__ __forceinline__ void moe_issue(const Params& P, const MoeGeo& g, rsrc_t r, rsrc_t rs, const int* sel,
+                                          int eslot, MoeCur& c, u32x4& b0, u32x4& b1, uint32_t& s0,
+                                          uint32_t& s1) {
   const int lane = threadIdx.x & 63;
-  const uint32_t row_bytes = (uint32_t)(DOWN ? P.Fe : P.d);
+  const uint32_t row_bytes = (uint32_t)((DOWN ? P.Fe : P.d) / (MX ? 2 : 1));
   const int e = DOWN ? rfl(sel[c.sl]) : eslot;
-  const uint32_t row0 = DOWN ? (uint32_t)P.e8_d + (uint32_t)(e * P.d + 2 * (g.p0 + c.t)) * row_bytes
-                             : (uint32_t)((e * P.Fe + g.p0 + c.t) * 2) * row_bytes;
+  const uint32_t row = DOWN ? (uint32_t)(e * P.d + 2 * (g.p0 + c.t)) : (uint32_t)((e * P.Fe + g.p0 + c.t) * 2);
+  const uint32_t row0 = (DOWN ? (uint32_t)P.e8_d : 0u) + row * row_bytes;
   const bool ok = c.issued < g.n && (c.c + 1 < g.npc || lane < g.tail);
   const uint32_t o = row0 + 1024u * (uint32_t)c.c + (uint32_t)lane * 16u;
   b0 = ld_nt(r, ok ? o : kOOB);
   b1 = ld_nt(r, ok ? o + row_bytes : kOOB + 16u);   // distinct: always two loads
+  if (MX) {
+    const uint32_t blocks = row_bytes / 16u;   // scales per row
+    const uint32_t so = (DOWN ? (uint32_t)P.xsc_d : 0u) + row * blocks + 64u * (uint32_t)c.c + (uint32_t)lane;
+    s0 = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? so : kOOB, 0, 0);
+    s1 = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? so + blocks : kOOB + 16u, 0, 0);
+  }
   ++c.issued;
   if (++c.c == g.npc) {
     c.c = 0;
@@ -1865,16 +1918,19 @@ __device__ __forceinline__ void moe_issue(const Params& P, const MoeGeo& g, rsrc
 // words.  (Issuing the down phase's first units ahead, at the end of the GU
 // stream or before the down phase's barrier, made the step slower: 1.35 and
 // 1.22 against 1.16 ms traced on moe2b.)
-template <bool DOWN>
+template <bool DOWN, bool MX>
 __device__ __forceinline__ void moe_stream(const Params& P, int l, int s, const int* tab_wg, const int* sel,
                                            int eslot, const float* sc_lds, const float* xs, float* out,
                                            u32x4 (&b)[2 * kUnitsInFlight]) {
   const int lane = threadIdx.x & 63;
-  const MoeGeo g = moe_geo<DOWN>(P, s, tab_wg);
+  const MoeGeo g = moe_geo<DOWN, MX>(P, s, tab_wg);
   const rsrc_t r = make_rsrc(P.w8 + (size_t)rfl(l) * P.e8_stride, (uint32_t)P.e8_stride);
+  const rsrc_t rs = make_rsrc(P.xsc + (size_t)rfl(l) * P.xsc_stride, MX ? (uint32_t)P.xsc_stride : 0u);
+  uint32_t bs[2 * kUnitsInFlight];   // MXFP4: the units' block scales
   MoeCur ic = moe_cursor(g, g.u0);
 #pragma unroll
-  for (int k = 0; k < kUnitsInFlight; ++k) moe_issue<DOWN>(P, g, r, sel, eslot, ic, b[2 * k], b[2 * k + 1]);
+  for (int k = 0; k < kUnitsInFlight; ++k)
+    moe_issue<DOWN, MX>(P, g, r, rs, sel, eslot, ic, b[2 * k], b[2 * k + 1], bs[2 * k], bs[2 * k + 1]);
   int ct = ic.t, csl = 0, cc = 0;
   {
     const MoeCur c0 = moe_cursor(g, g.u0);
@@ -1886,12 +1942,25 @@ __device__ __forceinline__ void moe_stream(const Params& P, int l, int s, const 
   for (int grp = 0; grp < ngroups; ++grp) {
 #pragma unroll
     for (int k = 0; k < kUnitsInFlight; ++k) {
-      wait_vm<kBlocksInFlight - 2>();
+      // (MXFP4: four loads per unit -- codes, then scales -- all in issue order)
+      wait_vm<(MX ? 2 : 1) * kBlocksInFlight - (MX ? 4 : 2)>();
       const int j = grp * kUnitsInFlight + k;
       if (j < n) {
-        dot16_e4m3x2(b[2 * k], b[2 * k + 1], xs + (DOWN ? csl * P.Fe : 0) + 1024 * cc + 16 * lane, a0, a1);
+        if (MX) {
+          // a lane's 32 weights of the piece; lanes past the row's end skip
+          if (cc + 1 < g.npc || lane < g.tail)
+            dot32_mxfp4x2(b[2 * k], b[2 * k + 1], e8m0_float(bs[2 * k]), e8m0_float(bs[2 * k + 1]),
+                          xs + (DOWN ? csl * P.Fe : 0) + 2048 * cc + 32 * lane, a0, a1);
+        } else {
+          dot16_e4m3x2(b[2 * k], b[2 * k + 1], xs + (DOWN ? csl * P.Fe : 0) + 1024 * cc + 16 * lane, a0, a1);
+        }
         const bool last = j == n - 1, seg_end = cc + 1 == g.npc;
-        if (DOWN && (seg_end || last)) {
+        if (DOWN && MX && (seg_end || last)) {
+          s0 += a0;   // MXFP4: the block scales are applied already
+          s1 += a1;
+          a0 = a1 = 0.f;
+        }
+        if (DOWN && !MX && (seg_end || last)) {
           s0 = __builtin_fmaf(a0, sc_lds[csl * 2 * g.np + 2 * ct], s0);
           s1 = __builtin_fmaf(a1, sc_lds[csl * 2 * g.np + 2 * ct + 1], s1);
           a0 = a1 = 0.f;
@@ -1906,7 +1975,7 @@ __device__ __forceinline__ void moe_stream(const Params& P, int l, int s, const 
         }
         if (++cc == g.npc) { cc = 0; if (++csl == g.nsl) { csl = 0; ++ct; } }
       }
-      moe_issue<DOWN>(P, g, r, sel, eslot, ic, b[2 * k], b[2 * k + 1]);
+      moe_issue<DOWN, MX>(P, g, r, rs, sel, eslot, ic, b[2 * k], b[2 * k + 1], bs[2 * k], bs[2 * k + 1]);
     }
   }
   wait_vm0();   // the zero-reading loads past the share's end
@@ -1987,11 +2056,14 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
         float* rt = aux + kAuxRoute + 16 * w;
         moe_route(P, aux + kAuxRouter, red, rt);
         const int* sel = reinterpret_cast<const int*>(rt);
-        moe_stream<false>(P, id.l, w, tab_wg, sel, rfl(sel[rfl(tab_wg[kTabMoeSlot])]), nullptr, xs, out, mb);
+        const int eslot = rfl(sel[rfl(tab_wg[kTabMoeSlot])]);
+        if (P.mx) moe_stream<false, true>(P, id.l, w, tab_wg, sel, eslot, nullptr, xs, out, mb);
+        else moe_stream<false, false>(P, id.l, w, tab_wg, sel, eslot, nullptr, xs, out, mb);
       } else if (id.ph == PH_DOWN) {
         const int w = rfl((int)(threadIdx.x >> 6));
-        moe_stream<true>(P, id.l, w, tab_wg, reinterpret_cast<const int*>(aux) + kAuxRoute + 16 * w, 0,
-                         aux + kAuxMoe, xs, out, mb);
+        const int* sel = reinterpret_cast<const int*>(aux) + kAuxRoute + 16 * w;
+        if (P.mx) moe_stream<true, true>(P, id.l, w, tab_wg, sel, 0, aux + kAuxMoe, xs, out, mb);
+        else moe_stream<true, false>(P, id.l, w, tab_wg, sel, 0, aux + kAuxMoe, xs, out, mb);
       }
     }
     __syncthreads();   // S2
@@ -2367,7 +2439,7 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
         // land while the experts' gate/up rows stream)
         const int r0 = 2 * rfl(tab_wg[2 * PH_DOWN]), nr = 2 * rfl(tab_wg[2 * PH_DOWN + 1]) - r0;
         const float* sd = P.esc + (size_t)id.l * P.sc_stride + P.sc_d;
-        for (int i = lane; i < P.topk * nr; i += 64) {
+        for (int i = lane; i < (P.mx ? 0 : P.topk * nr); i += 64) {
           const int k = i / nr;
           aux[kAuxMoe + i] = ldg(sd + (size_t)route[k] * P.d + r0 + (i - k * nr));
         }

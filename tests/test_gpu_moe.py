@@ -169,3 +169,36 @@ def test_moe_rejections(stream):
                                                                         seed=52), stream) as dense:
         with pytest.raises(B.DecError, match="STATE"):
             dense.read_routes(0, 1)
+
+
+# ----------------------------------------------------------------------------
+# MXFP4 experts (DEC_FLAG_EXPERTS_MXFP4)
+# ----------------------------------------------------------------------------
+
+def test_moe_mxfp4_tiny_teacher_forced(stream):
+    s = TINY_MOE.with_(mxfp4=True)
+    t = synth.make_weights(s, seed=61, gain_jitter=0.1)
+    prompt = synth.make_prompt(s.vocab, 16, seed=62)[0]
+    worst, forced = moe_teacher_forced(s, t, prompt, 16, stream)
+    assert forced == 0
+
+
+def test_moe_mxfp4_ragged_pieces(stream):
+    # d 384 and expert width 160: rows of 192 and 80 bytes of code pairs end
+    # inside a 1 KB piece (12 and 5 lanes); expert width 2080 (second test):
+    # down rows of a full piece plus one lane
+    s = synth.shape_for("tiny").with_(n_layers=3, d_model=384, n_heads=6, head_dim=64, d_ffn=160,
+                                      n_experts=10, top_k=3, max_ctx=64, mxfp4=True)
+    t = synth.make_weights(s, seed=63, gain_jitter=0.1)
+    moe_teacher_forced(s, t, synth.make_prompt(s.vocab, 9, seed=64)[0], 8, stream)
+    s2 = synth.shape_for("tiny").with_(n_layers=2, d_ffn=2080, n_experts=4, top_k=2, max_ctx=48, mxfp4=True)
+    t2 = synth.make_weights(s2, seed=65)
+    moe_teacher_forced(s2, t2, synth.make_prompt(s2.vocab, 6, seed=66)[0], 6, stream)
+
+
+def test_moe_mxfp4_rules(stream):
+    s = TINY_MOE.with_(mxfp4=True)
+    assert B.check_desc(B.ModelDesc.from_shape(s)) == B.DEC_OK
+    assert B.check_desc(B.ModelDesc.from_shape(s, d_ffn=272)) == B.DEC_ERR_UNSUPPORTED      # not a multiple of 32
+    dense = synth.shape_for("tiny")
+    assert B.check_desc(B.ModelDesc.from_shape(dense, flags=B.DEC_FLAG_EXPERTS_MXFP4)) == B.DEC_ERR_BAD_DESC
