@@ -22,6 +22,8 @@ The same JSON line also carries, each measured in this run on its own handle:
                           32 experts of width 1728 in FP8 E4M3, top-4 routing
                           inside the resident kernel; 128-token prompt + 512
                           steps (its roofline counts the active experts only)
+  workloads.moe2b_mx      the same with MXFP4 experts (E2M1 pairs, an E8M0
+                          scale per 32 weights)
   ttft                    time to first token of the 128-token prompt: one
                           position per step (the decode kernel), batched (8
                           positions per step on the matrix-core kernel) and
@@ -53,7 +55,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode tokens/s per request (bs=1) and achieved HBM GB/s vs peak, 1 MI355X"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "memory_bound_transformer_persistent_amd", "csrc", "dec_kernels.hip")
-EXTRAS = ("lane2b", "dense2b_long", "dense2b_b8", "moe2b")
+EXTRAS = ("lane2b", "dense2b_long", "dense2b_b8", "moe2b", "moe2b_mx")
 SERVE_IDLE_US = 200000   # decode server: a launch ends after 0.2 s without a step
 
 
@@ -122,8 +124,10 @@ class Run:
         self.s, self.nb, self.serve = w.shape, w.batch, serve
         import synth
         self.prompt = synth.make_prompt(self.s.vocab, w.prompt_len, batch=self.nb, seed=w.prompt_seed)
-        self.dec = B.Decoder(B.ModelDesc.from_shape(self.s, batch=self.nb, flags=flags), tensors=tensors, device=0,
-                             stream=stream.cuda_stream, debug_flags=debug, serve_idle_us=SERVE_IDLE_US if serve else 0)
+        desc = B.ModelDesc.from_shape(self.s, batch=self.nb)
+        desc.flags |= flags      # keep the shape's own flags (MXFP4 experts)
+        self.dec = B.Decoder(desc, tensors=tensors, device=0, stream=stream.cuda_stream, debug_flags=debug,
+                             serve_idle_us=SERVE_IDLE_US if serve else 0)
 
     def ev(self):
         return self.torch.cuda.Event(enable_timing=True)

@@ -63,6 +63,9 @@ class ModelDesc(ctypes.Structure):
                   flags=DEC_FLAG_EXPERTS_MXFP4 if getattr(s, "mxfp4", False) else 0,
                   n_experts=getattr(s, "n_experts", 0), top_k=getattr(s, "top_k", 0))
         kw.update(override)
+        if getattr(s, "mxfp4", False):
+            # the experts' tensors have MXFP4 shapes whatever other flags are asked for
+            kw["flags"] |= DEC_FLAG_EXPERTS_MXFP4
         return cls(**kw)
 
 

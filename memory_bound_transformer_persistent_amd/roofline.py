@@ -45,6 +45,9 @@ def layer_weight_bytes(shape) -> int:
     if getattr(shape, "n_experts", 0):
         k = shape.top_k
         fp16 = 3 * q * d + d * q + shape.n_experts * d
+        if getattr(shape, "mxfp4", False):
+            # MXFP4: half a byte per weight and a 1-byte scale per 32 weights
+            return 2 * (fp16 + 2 * d) + k * (3 * f * d) // 2 + k * (3 * f * d) // 32
         return 2 * (fp16 + 2 * d) + k * (3 * f * d) + 4 * k * (2 * f + d)
     mats = 3 * q * d + d * q + 2 * f * d + d * f
     return 2 * (mats + 2 * d)            # fp16 matrices + the two norm gains

@@ -91,6 +91,9 @@ FIXTURES = {
     # dense2b's attention with 32 FP8 experts, top-4: 128 + 64
     "moe2b": dict(workload="moe2b", prompt_len=128, steps=64, every=4, extra=[127, 128, 129, 190, 191],
                   kv_layers=[0, 1, 12, 24], kv_pos=[0, 5, 127, 128, 191]),
+    # the same with MXFP4 experts
+    "moe2b_mx": dict(workload="moe2b_mx", prompt_len=128, steps=64, every=4, extra=[127, 128, 129, 190, 191],
+                     kv_layers=[0, 1, 12, 24], kv_pos=[0, 5, 127, 128, 191]),
 }
 GREEDY_STEPS = 16        # dense2b: free-running greedy steps after the 128-token prompt
 

@@ -104,3 +104,13 @@ def test_moe_step_bytes_count_the_active_experts_only():
     sb, sd = R.step_bytes(m, 200), R.step_bytes(synth.shape_for("dense2b"), 200)
     assert sb.kv_read == sd.kv_read and sb.act == sd.act
     assert sd.weights - sb.weights == 25 * (dense - want)
+
+
+def test_mxfp4_experts_count_half_a_byte_per_weight_and_their_block_scales():
+    import synth
+    from memory_bound_transformer_persistent_amd import roofline as R
+    e4 = R.layer_weight_bytes(synth.shape_for("moe2b"))
+    mx = R.layer_weight_bytes(synth.shape_for("moe2b_mx"))
+    k, F, d = 4, 1728, 2560
+    codes = k * 3 * F * d
+    assert e4 - mx == (codes + 4 * k * (2 * F + d)) - (codes // 2 + codes // 32)

@@ -16,7 +16,7 @@ import oracle as O
 import synth
 from fullsize import GOLDEN, Fixture, oracle_sha
 
-NAMES = ("dense2b", "lane2b", "dense2b_long", "dense2b_b8", "dense2b_w4", "lane2b_long", "dense2b_b8_long", "moe2b")
+NAMES = ("dense2b", "lane2b", "dense2b_long", "dense2b_b8", "dense2b_w4", "lane2b_long", "dense2b_b8_long", "moe2b", "moe2b_mx")
 
 
 @pytest.mark.parametrize("name", NAMES)
@@ -85,12 +85,13 @@ def test_fixture_script_uses_only_the_oracle_and_the_generators():
     assert mods <= {"hashlib", "json", "os", "sys", "time", "numpy", "oracle", "synth"}, mods
 
 
-def test_moe2b_fixture_is_from_the_current_moe_oracle():
+@pytest.mark.parametrize("name", ["moe2b", "moe2b_mx"])
+def test_moe2b_fixture_is_from_the_current_moe_oracle(name):
     import hashlib
-    fx = Fixture("moe2b")
+    fx = Fixture(name)
     src = os.path.join(os.path.dirname(GOLDEN), "..", "oracle", "moe.py")
     assert fx.meta["moe_sha"] == hashlib.sha256(open(src, "rb").read()).hexdigest()[:16], \
-        "oracle/moe.py changed: rerun tests/golden/make_fullsize.py moe2b"
+        f"oracle/moe.py changed: rerun tests/golden/make_fullsize.py {name}"
     s = fx.shape
     n = fx.n0 + fx.steps
     assert fx.routes.shape == (n, s.n_layers, s.top_k) and fx.route_gap.shape == (n, s.n_layers)

@@ -46,7 +46,7 @@ _TENSORS = {}
 def tensors_for(fx):
     """The workload's seeded weights (kept for the module: the 2.3B tensors take seconds to draw)."""
     name = fx.workload.name
-    key = "lane2b" if fx.workload.lane else ("moe2b" if fx.shape.moe else "dense2b")
+    key = "lane2b" if fx.workload.lane else (name if fx.shape.moe else "dense2b")
     if key not in _TENSORS:
         _TENSORS.clear()
         _TENSORS[key] = synth.workload_weights(fx.workload)
@@ -55,8 +55,9 @@ def tensors_for(fx):
 
 
 def make(fx, stream, flags=0):
-    return B.Decoder(B.ModelDesc.from_shape(fx.shape, batch=fx.batch, flags=flags), tensors=tensors_for(fx),
-                     device=0, stream=stream.cuda_stream)
+    d = B.ModelDesc.from_shape(fx.shape, batch=fx.batch)
+    d.flags |= flags          # keep the shape's own flags (MXFP4 experts)
+    return B.Decoder(d, tensors=tensors_for(fx), device=0, stream=stream.cuda_stream)
 
 
 def check_kv(dec, fx, what, bound, upto=None):
@@ -212,8 +213,10 @@ def test_dense2b_b8_after_3968_token_prompts(stream):
 ROUTE_TIE = 5e-3
 
 
-def test_moe2b_teacher_forced(stream):
-    """dense2b's attention with 32 FP8 experts, top-4: 128-token prompt, 64 forced steps.
+@pytest.mark.parametrize("name", ["moe2b", "moe2b_mx"])
+def test_moe2b_teacher_forced(stream, name):
+    """dense2b's attention with 32 experts (FP8 E4M3, or MXFP4 for moe2b_mx),
+    top-4: 128-token prompt, 64 forced steps.
 
     The router's choice is an integer decided by floating point: where the
     oracle's gap between its 4th and 5th logit is below ROUTE_TIE, either
@@ -227,10 +230,10 @@ def test_moe2b_teacher_forced(stream):
         every position 127..191 and the K/V rows at the fixture's positions.
     """
     import oracle as O
-    fx = Fixture("moe2b")
+    fx = Fixture(name)
     n0, steps, L = fx.n0, fx.steps, fx.shape.n_layers
     n = n0 + steps
-    t = Tracker(fx, "moe2b 128 + 64")
+    t = Tracker(fx, f"{name} 128 + 64")
     logits = {}
     with make(fx, stream) as d:
         tok, pre = d.prefill(fx.prompt, want_logits=True)
@@ -249,8 +252,8 @@ def test_moe2b_teacher_forced(stream):
                     f"position {p} layer {l}: {list(routes[p, l])} vs {list(fx.routes[p, l])}, gap {fx.route_gap[p, l]}"
                 split = p
                 break
-        check_kv(d, fx, "moe2b against the fixture", KV_B1, upto=split)
-    print(f"moe2b: routes equal to the fixture's at the first {split} of {n} positions", flush=True)
+        check_kv(d, fx, f"{name} against the fixture", KV_B1, upto=split)
+    print(f"{name}: routes equal to the fixture's at the first {split} of {n} positions", flush=True)
     # the oracle on the same tokens, following the library at near-ties
     lg, K16, V16, own, gap = O.prefill_matrix_moe(fx.shape, tensors_for(fx), fx.tokens[0], force_routes=routes,
                                                   progress=lambda l: print(f"oracle layer {l} done", flush=True))
@@ -275,6 +278,6 @@ def test_moe2b_teacher_forced(stream):
             ex = kv_excess(got[:, fx.kv_pos].transpose(1, 0, 2), want[:, fx.kv_pos].transpose(1, 0, 2))
             assert ex.max() <= KV_B1, f"layer {layer}: {ex.max()}"
             kv_worst = max(kv_worst, float(ex.max()))
-    print(f"moe2b 128 + 64: logits at {len(logits)} positions, max |gpu - oracle| = {worst:.3e} (bound 2e-2); "
+    print(f"{name} 128 + 64: logits at {len(logits)} positions, max |gpu - oracle| = {worst:.3e} (bound 2e-2); "
           f"K/V worst excess {kv_worst:.2e} of the rms; {followed} near-tie routing choices "
           f"(of {n * L}) followed", flush=True)
