@@ -1911,7 +1911,11 @@ __device__ __forceinline__ void moe_issue(const Params& P, const MoeGeo& g, rsrc
   }
 }
 
-// Streams the share with kUnitsInFlight units in flight in b.  Row sums go
+// Units a streamer keeps in flight in the routed phases.  Traced moe2b steps
+// (E4M3 / MXFP4): 2 units 1.172 / 1.158 ms, 3 units 1.151 / 1.167 ms, 4 units
+// 1.165 / 1.177 ms, 8 units 1.240 / 1.243 ms.
+constexpr int kMoeUnits = 3;
+// Streams the share with kMoeUnits units in flight in b.  Row sums go
 // to out by ds_add, at most two contributors per row pair
 // (streamer_range).  A down row's sum over one expert is scaled by that
 // row's scale before the next expert's is added.  sel: this wave's routing
@@ -1921,15 +1925,15 @@ __device__ __forceinline__ void moe_issue(const Params& P, const MoeGeo& g, rsrc
 template <bool DOWN, bool MX>
 __device__ __forceinline__ void moe_stream(const Params& P, int l, int s, const int* tab_wg, const int* sel,
                                            int eslot, const float* sc_lds, const float* xs, float* out,
-                                           u32x4 (&b)[2 * kUnitsInFlight]) {
+                                           u32x4 (&b)[2 * kMoeUnits]) {
   const int lane = threadIdx.x & 63;
   const MoeGeo g = moe_geo<DOWN, MX>(P, s, tab_wg);
   const rsrc_t r = make_rsrc(P.w8 + (size_t)rfl(l) * P.e8_stride, (uint32_t)P.e8_stride);
   const rsrc_t rs = make_rsrc(P.xsc + (size_t)rfl(l) * P.xsc_stride, MX ? (uint32_t)P.xsc_stride : 0u);
-  uint32_t bs[2 * kUnitsInFlight];   // MXFP4: the units' block scales
+  uint32_t bs[2 * kMoeUnits];   // MXFP4: the units' block scales
   MoeCur ic = moe_cursor(g, g.u0);
 #pragma unroll
-  for (int k = 0; k < kUnitsInFlight; ++k)
+  for (int k = 0; k < kMoeUnits; ++k)
     moe_issue<DOWN, MX>(P, g, r, rs, sel, eslot, ic, b[2 * k], b[2 * k + 1], bs[2 * k], bs[2 * k + 1]);
   int ct = ic.t, csl = 0, cc = 0;
   {
@@ -1938,13 +1942,13 @@ __device__ __forceinline__ void moe_stream(const Params& P, int l, int s, const 
   }
   float a0 = 0.f, a1 = 0.f, s0 = 0.f, s1 = 0.f;
   const int n = g.n;
-  const int ngroups = (n + kUnitsInFlight - 1) / kUnitsInFlight;
+  const int ngroups = (n + kMoeUnits - 1) / kMoeUnits;
   for (int grp = 0; grp < ngroups; ++grp) {
 #pragma unroll
-    for (int k = 0; k < kUnitsInFlight; ++k) {
+    for (int k = 0; k < kMoeUnits; ++k) {
       // (MXFP4: four loads per unit -- codes, then scales -- all in issue order)
-      wait_vm<(MX ? 2 : 1) * kBlocksInFlight - (MX ? 4 : 2)>();
-      const int j = grp * kUnitsInFlight + k;
+      wait_vm<(MX ? 2 : 1) * (2 * kMoeUnits) - (MX ? 4 : 2)>();
+      const int j = grp * kMoeUnits + k;
       if (j < n) {
         if (MX) {
           // a lane's 32 weights of the piece; lanes past the row's end skip
@@ -1994,7 +1998,7 @@ __device__ __forceinline__ void streamer_role(const Params& P, const Launch& A, 
   const uint32_t lane16 = (uint32_t)lane * 16u;
   Cursor cu;
   cursor_start(P, A, g0, g1, tab, cu);
-  u32x4 mb[2 * kUnitsInFlight];   // mixture of experts: the routed phases' loads
+  u32x4 mb[2 * kMoeUnits];   // mixture of experts: the routed phases' loads
   u32x4 buf[kBlocksInFlight];
 #pragma unroll
   for (int k = 0; k < kUnitsInFlight; ++k) issue_unit(cu, lane16, buf[2 * k], buf[2 * k + 1]);
