@@ -283,6 +283,23 @@ def test_watchdog_timeout_is_an_error_not_a_hang(stream):
         check_logits(lg, O.prefill_matrix(s, t, prompt)[0][-1], "after timeout")
 
 
+def test_asynchronous_step_timeout_surfaces_at_sync(stream):
+    """dec_step with neither outputs returns before the step has run; a
+    watchdog expiry in it is reported by the next call that waits (dec_sync)."""
+    s = synth.shape_for("tiny")
+    t = synth.make_weights(s, seed=0)
+    with make(s, t, stream, watchdog_us=1) as d:
+        tok, lg = d.step(force_tok=1, want_tok=False)       # asynchronous: nothing to wait for
+        assert tok is None and lg is None
+        with pytest.raises(B.DecError) as e:
+            d.sync()
+        assert e.value.code == B.DEC_ERR_TIMEOUT
+        with pytest.raises(B.DecError) as e:
+            d.step(force_tok=1)
+        assert e.value.code == B.DEC_ERR_STATE
+        d.reset()
+
+
 def test_weights_file_ingest_matches_host_tensors(stream, tmp_path):
     from memory_bound_transformer_persistent_amd import weights_file as WF
     s = synth.shape_for("tiny")
