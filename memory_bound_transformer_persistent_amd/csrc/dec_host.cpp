@@ -451,14 +451,15 @@ Arena arena_layout(const dec_model_desc& d, int G) {
     a.mp_x = a.mp_h = a.mp_q16 = a.mp_a = a.mp_s = a.mp_part = 0;
   }
   a.x = take(B * D * 4);
-  a.xg16 = take(B * D * 2);
+  a.xg16 = take((size_t)kMaxBatch * D * 2);   // blocks of 8 rows x kMaxBatch sequences
   a.ssp = take((size_t)G * kMaxBatch * 4);
   a.qkv = take(B * 3 * q * 4);
   a.att_o = take(B * q * 4);
   a.part = take(part_rows * d.head_dim * 4);
   a.pml = take(part_rows * 2 * 4);
-  // the MLP's hidden vector: d_ffn, or top_k experts' d_ffn each
-  a.act = take(B * d.d_ffn * (moe(d) ? d.top_k : 1) * 4);
+  // the MLP's hidden vector: d_ffn, or top_k experts' d_ffn each (batched:
+  // fp16 in blocks of 8 rows x kMaxBatch sequences, whatever the batch)
+  a.act = take(std::max(B * d.d_ffn * (moe(d) ? d.top_k : 1) * 4, (size_t)kMaxBatch * d.d_ffn * 2));
   if (moe(d)) a.rpart = take((size_t)G * kMoeMaxExperts * 4);
   a.logits = take(B * d.lm_vocab * 4);
   // argmax partials: [G] at batch 1, [G][kMaxBatch] for the batched kernel

@@ -119,7 +119,7 @@ struct Params {
   float* part;                // attention partial sums [B*H][max_chunks][hd]
   float* pml;                 // attention partial (max, sum) [B*H][max_chunks][2]
   float* act;                 // SwiGLU output [F] (batch 1, fp32)
-  uint16_t* act16;            // SwiGLU output [B][F] (batch > 1, fp16; same memory as act)
+  uint16_t* act16;            // SwiGLU output (batch > 1, fp16 in 8-row blocks, see blk8; same memory as act)
   float* logits;              // [B][Vlm]
   float* amax_v;              // per-workgroup best logit: [G] at batch 1, [G][kMaxBatch] batched
   int* amax_i;                // its row (lowest on ties), same layout
@@ -133,8 +133,8 @@ struct Params {
   int trace_stride;
   int stress;                 // 1: random delays before every arrival, NaN-poisoned exchange buffers
   // batched kernel: the normed phases' inputs, published by the O and down
-  // phases: x times the next norm's gains in fp16 [B][d], and each
-  // workgroup's partial sums of x^2 [G][kMaxBatch]
+  // phases: x times the next norm's gains in fp16 (8-row blocks, see blk8),
+  // and each workgroup's partial sums of x^2 [G][kMaxBatch]
   uint16_t* xg16;
   float* ssp;
   Mailbox* mail;              // decode server mailbox (device address of host-pinned memory) or null

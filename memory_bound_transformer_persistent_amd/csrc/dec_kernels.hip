@@ -299,6 +299,13 @@ struct GemvWork {
 __device__ __forceinline__ int gemv_npc(int K) { return gemv_piece_cols(K); }
 // Elements of the input vector a GEMV with row length K reads (zero-padded past K).
 __device__ __forceinline__ int gemv_span(int K) { return 512 * gemv_npc(K); }
+// Batched kernel: element (sequence b, row r) of the fp16 exchange vectors
+// that several workgroups write and every workgroup pulls (the normed inputs
+// and the SwiGLU output).  Blocks of 8 rows x kMaxBatch sequences are one
+// 128-byte line each: a workgroup owns whole 16-row groups, so every line has
+// one writer, and a publication store of 8 rows of all sequences fills one
+// line.  Lines written by several workgroups took about twice as long to pull.
+__device__ __forceinline__ size_t blk8(int b, int r) { return (size_t)(r >> 3) * (8 * kMaxBatch) + b * 8 + (r & 7); }
 
 __device__ __forceinline__ GemvWork work_of(const Params& P, int ph, int l) {
   GemvWork g{nullptr, 0, 0, 0, 0};
@@ -764,7 +771,7 @@ __device__ __forceinline__ void w0_poison(const Params& P, int ph, int l, const 
     if constexpr (MB > 1) {
       // and the normed inputs published with them
       for (int b = 0; b < B; ++b)
-        for (int r = r0 + lane; r < r1; r += 64) st_coh(P.xg16 + (size_t)b * P.d + r, nan16);
+        for (int r = r0 + lane; r < r1; r += 64) st_coh(P.xg16 + blk8(b, r), nan16);
       if (lane < MB) st_coh(reinterpret_cast<uint32_t*>(P.ssp + (size_t)blockIdx.x * kMaxBatch + lane), nan32);
     }
   }
@@ -778,7 +785,7 @@ __device__ __forceinline__ void w0_poison(const Params& P, int ph, int l, const 
     for (int b = 0; b < B; ++b)
       for (int t = p0 + lane; t < p1; t += 64) {
         if constexpr (MB == 1) st_coh(reinterpret_cast<uint32_t*>(P.act + t), nan32);
-        else st_coh(P.act16 + (size_t)b * P.F + t, nan16);
+        else st_coh(P.act16 + blk8(b, t), nan16);
       }
   }
   if (ph == PH_O) {
@@ -847,23 +854,32 @@ __device__ __forceinline__ bool dma_input(const PhaseIt& id) {
   return id.ph == PH_GU || id.ph == PH_LM || id.ph == PH_DOWN || id.ph == PH_O || (id.ph == PH_QKV && id.l > 0);
 }
 // Batched kernel, wave w of the workgroup: its share (1 KB chunks w, w + 8,
-// ... over every sequence's vector) of phase id's raw input into LDS: the
-// fp32 residual vectors into the stage of the normed phases, the fp16 SwiGLU
-// or attention outputs into the input region.  Issues only; the caller waits.
+// ...) of phase id's fp16 input into the input region, in 8-row blocks as
+// blk8 lays them out (so that a lane's MFMA B operand, 8 consecutive columns
+// of one sequence, is 16 contiguous bytes), zero past row n: the normed
+// phases' x times gains and the SwiGLU output are copied as they are; the
+// attention output, [B][q] in memory, is gathered (each load still reads 8
+// whole 128-byte runs).  Issues only; the caller waits.
 template <int MB>
 __device__ __forceinline__ void dma_input_share(const Params& P, const PhaseIt& id, float* xs, int w) {
   const int lane = threadIdx.x & 63;
   const bool normed = id.ph != PH_DOWN && id.ph != PH_O;
   const int n = normed ? P.d : (id.ph == PH_DOWN ? P.F : P.q);
-  const int span_bytes = gemv_span(n) * 2, nch = span_bytes >> 10;
+  // 1 KB chunk c holds rows 64c .. 64c + 63 of every sequence (n is a
+  // multiple of 8, so a lane's 16 bytes are all in range or all past it)
+  const int nch = gemv_span(n) * 2 * kMaxBatch >> 10;
   char* base = reinterpret_cast<char*>(xs);
-  for (int k = w; k < P.B * nch; k += kWaves) {
-    const int b = k / nch, c = k - b * nch;
-    const uint16_t* src = normed ? P.xg16 + (size_t)b * P.d
-                                 : (id.ph == PH_DOWN ? P.act16 + (size_t)b * P.F : P.att_o16 + (size_t)b * P.q);
-    const rsrc_t r = make_rsrc(src, (uint32_t)(n * 2));
-    dma16_coh(r, base + (size_t)b * span_bytes + 1024 * c, (uint32_t)(1024 * c + 16 * lane));
+  if (id.ph == PH_O) {
+    const rsrc_t r = make_rsrc(P.att_o16, (uint32_t)(P.B * n * 2));
+    const int b = lane & (kMaxBatch - 1);
+    for (int c = w; c < nch; c += kWaves) {
+      const int row = 64 * c + 8 * (lane >> 3);
+      dma16_coh(r, base + 1024 * c, b < P.B && row < n ? (uint32_t)((b * n + row) * 2) : kOOB);
+    }
+    return;
   }
+  const rsrc_t r = make_rsrc(normed ? P.xg16 : P.act16, (uint32_t)(n * 2 * kMaxBatch));
+  for (int c = w; c < nch; c += kWaves) dma16_coh(r, base + 1024 * c, (uint32_t)(1024 * c + 16 * lane));
 }
 
 // Batched kernel, wave w, a normed phase whose input was published by the O
@@ -903,7 +919,8 @@ __device__ __forceinline__ void apply_gains_batch(_Float16* xh, const float* st,
       const f32x4 v = *reinterpret_cast<const f32x4*>(st + (size_t)b * span + i);
       ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
       const f32x4 y = v * *reinterpret_cast<const f32x4*>(gs + i);
-      *reinterpret_cast<f16x4*>(xh + (size_t)b * span + i) = f16x4{(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
+      // 8-row blocks as the pulled inputs (blk8); i is a multiple of 4
+      *reinterpret_cast<f16x4*>(xh + blk8(b, i)) = f16x4{(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
     }
     ss = wave_sum(ss);
     if ((threadIdx.x & 63) == 0) red[b * kWaves + (threadIdx.x >> 6)] = ss;
@@ -1296,7 +1313,7 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l,
           // gs since that phase's gains were fetched), in fp16, and this
           // workgroup's share of sum(x^2)
           const _Float16 hv = (_Float16)(v * gs_next[2 * p0 + t]);
-          st_coh(P.xg16 + (size_t)b * P.d + 2 * p0 + t, __builtin_bit_cast(uint16_t, hv));
+          st_coh(P.xg16 + blk8(b, 2 * p0 + t), __builtin_bit_cast(uint16_t, hv));
           ss += v * v;
         }
       }
@@ -1325,7 +1342,7 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l,
         const float gt = out[2 * t * MB + b] * scl[b], up = out[(2 * t + 1) * MB + b] * scl[b];
         const float a = gt / (1.0f + expf(-gt)) * up;
         if constexpr (MB == 1) st_coh(P.act + p0 + t, a);
-        else st_coh(P.act16 + (size_t)b * P.F + p0 + t, __builtin_bit_cast(uint16_t, (_Float16)a));
+        else st_coh(P.act16 + blk8(b, p0 + t), __builtin_bit_cast(uint16_t, (_Float16)a));
       }
     }
   } else if (ph == PH_LM && MB == 1) {
@@ -2123,7 +2140,8 @@ __device__ __forceinline__ void streamer_tiles(const Params& P, const Launch& A,
       const int kt = rfl(e[T_NPC]);
       const int t0 = rfl(e[T_T0]), u0 = t0 * kt + rfl(e[T_COL]), u1 = u0 + n;
       int t = t0, j = rfl(e[T_COL]);
-      const _Float16* xb = reinterpret_cast<const _Float16*>(xs) + seq * gemv_span(phase_k(P, id.ph)) + 8 * kseg;
+      // columns 32 j + 8 kseg .. + 7 of sequence seq (8-row blocks, blk8)
+      const _Float16* xb = reinterpret_cast<const _Float16*>(xs) + blk8(seq, 8 * kseg);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       int u = 0;
       for (int grp = 0; grp < ngroups; ++grp) {
@@ -2132,7 +2150,7 @@ __device__ __forceinline__ void streamer_tiles(const Params& P, const Launch& A,
         for (int k = 0; k < kTilesInFlight; ++k) {
           wait_vm<kTilesInFlight - 1>();
           if (u < n) {
-            const f16x8 bv = *reinterpret_cast<const f16x8*>(xb + kTileCols * j);
+            const f16x8 bv = *reinterpret_cast<const f16x8*>(xb + kTileCols * kMaxBatch * j);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, buf[k]), bv, acc, 0, 0, 0);
             if (++j == kt || u == n - 1) {
               if (col < B) {
