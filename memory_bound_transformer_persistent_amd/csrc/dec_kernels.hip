@@ -188,6 +188,11 @@ __device__ __forceinline__ void st_coh(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void st_coh(uint16_t* p, uint16_t v) {
   __hip_atomic_store((gushort*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16 bytes per lane at byte offset off of buffer r, with the same
+// device-scope (sc1) policy as st_coh
+__device__ __forceinline__ void st_coh16(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kAuxSc1);
+}
 // plain stores through the global address space (results the host reads)
 typedef __attribute__((address_space(1))) uint64_t gu64;
 __device__ __forceinline__ void st_g(float* p, float v) { *(gfloat_rw*)p = v; }
@@ -1242,7 +1247,8 @@ template <int MB, bool MOE = false>
 __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l, int pos, int pos_end,
                                                  const int* tab_wg, int lg_mode, const float* scl,
                                                  const float* out, float* xown, const float* rope_lds,
-                                                 const float* gs_next, const uint16_t* moe_wr = nullptr) {
+                                                 const float* gs_next, const uint16_t* moe_wr = nullptr,
+                                                 bool store_x = true) {
   const int lane = threadIdx.x & 63, B = P.B;
   if (!is_gemv(ph)) return;
   if (MOE && ph == PH_GU) {
@@ -1302,19 +1308,41 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l,
     }
   } else if (ph == PH_O || ph == PH_DOWN) {
     float ss = 0.f;
-    for (int e = lane; e < 2 * n * MB; e += 64) {
-      const int t = e / MB, b = e - t * MB;
-      if (b < B) {
-        const float v = xown[b * own + t] + out[e];
-        xown[b * own + t] = v;
-        st_coh(P.x + (size_t)b * P.d + 2 * p0 + t, v);
-        if constexpr (MB > 1) {
-          // batched: the next normed phase's input, x times its gains (held in
-          // gs since that phase's gains were fetched), in fp16, and this
-          // workgroup's share of sum(x^2)
-          const _Float16 hv = (_Float16)(v * gs_next[2 * p0 + t]);
-          st_coh(P.xg16 + blk8(b, 2 * p0 + t), __builtin_bit_cast(uint16_t, hv));
-          ss += v * v;
+    if constexpr (MB == 1) {
+      for (int t = lane; t < 2 * n; t += 64) {
+        const float v = xown[t] + out[t];
+        xown[t] = v;
+        st_coh(P.x + 2 * p0 + t, v);
+      }
+    } else {
+      // batched: the next normed phase's input, x times its gains (held in
+      // gs since that phase's gains were fetched), in fp16, and this
+      // workgroup's share of sum(x^2).  Lane: sequence b = lane % 8, 8-row
+      // blocks k = lane / 8, + 8, ... (the workgroup's 2n rows are a multiple
+      // of 8), each one 16-byte store.  x itself is stored only when the
+      // launch ends here (store_x): the next token starts from its embedding,
+      // and within a launch only this workgroup reads its rows (xown).
+      const int b = lane & (MB - 1);
+      const rsrc_t rx = make_rsrc(P.x, (uint32_t)(B * P.d * 4));
+      const rsrc_t rg = make_rsrc(P.xg16, (uint32_t)(kMaxBatch * P.d * 2));
+      for (int k = lane >> 3; k < (2 * n) >> 3; k += 8) {
+        if (b < B) {
+          float v[8];
+          f16x8 h;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int t = 8 * k + i;
+            v[i] = xown[b * own + t] + out[t * MB + b];
+            xown[b * own + t] = v[i];
+            h[i] = (_Float16)(v[i] * gs_next[2 * p0 + t]);
+            ss += v[i] * v[i];
+          }
+          const int r = 2 * p0 + 8 * k;
+          st_coh16(rg, (uint32_t)(blk8(b, r) * 2), __builtin_bit_cast(u32x4, h));
+          if (store_x) {
+            st_coh16(rx, (uint32_t)(((size_t)b * P.d + r) * 4), __builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]}));
+            st_coh16(rx, (uint32_t)(((size_t)b * P.d + r + 4) * 4), __builtin_bit_cast(u32x4, f32x4{v[4], v[5], v[6], v[7]}));
+          }
         }
       }
     }
@@ -1335,14 +1363,30 @@ __device__ __forceinline__ void w0_store_outputs(const Params& P, int ph, int l,
       ss += __shfl_xor(ss, 32, 64);
       if (lane < MB) st_coh(P.ssp + (size_t)blockIdx.x * kMaxBatch + lane, ss);
     }
+  } else if (ph == PH_GU && MB > 1) {
+    // batched: lane: sequence b = lane % 8, outputs 8k .. 8k + 7 for blocks
+    // k = lane / 8, + 8, ... (n is a multiple of 8), one 16-byte store each
+    const int b = lane & (MB - 1);
+    const rsrc_t ra = make_rsrc(P.act16, (uint32_t)(kMaxBatch * P.F * 2));
+    for (int k = lane >> 3; k < n >> 3; k += 8) {
+      if (b < B) {
+        f16x8 h;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int t = 8 * k + i;
+          const float gt = out[2 * t * MB + b] * scl[b], up = out[(2 * t + 1) * MB + b] * scl[b];
+          h[i] = (_Float16)(gt / (1.0f + expf(-gt)) * up);
+        }
+        st_coh16(ra, (uint32_t)(blk8(b, p0 + 8 * k) * 2), __builtin_bit_cast(u32x4, h));
+      }
+    }
   } else if (ph == PH_GU) {
     for (int e = lane; e < n * MB; e += 64) {
       const int t = e / MB, b = e - t * MB;
       if (b < B) {
         const float gt = out[2 * t * MB + b] * scl[b], up = out[(2 * t + 1) * MB + b] * scl[b];
         const float a = gt / (1.0f + expf(-gt)) * up;
-        if constexpr (MB == 1) st_coh(P.act + p0 + t, a);
-        else st_coh(P.act16 + blk8(b, p0 + t), __builtin_bit_cast(uint16_t, (_Float16)a));
+        st_coh(P.act + p0 + t, a);
       }
     }
   } else if (ph == PH_LM && MB == 1) {
@@ -2264,9 +2308,10 @@ __device__ __forceinline__ void dec_body(const Params& P, const Launch& A) {
           combine_all<MB>(prev_ph, plan, slots, out);
           __syncthreads();   // S2b
         }
+      // (the batched kernel stores the residual only where a launch ends)
       w0_store_outputs<MB, MOE>(P, prev_ph, prev_l, step_pos(P, A, prev_i), A.pos_end, tab_wg,
                                 lg_mode(A, prev_i, cur_lg), scl, out, xown, aux, gs,
-                                reinterpret_cast<const uint16_t*>(smem + M::MoeWr));
+                                reinterpret_cast<const uint16_t*>(smem + M::MoeWr), MB == 1);
     }
     if (MB == 1 && is_gemv(id.ph)) {
       // the batch-1 streamers add into out (ds_add); the batched kernel's
