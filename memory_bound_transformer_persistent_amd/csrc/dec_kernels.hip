@@ -108,6 +108,7 @@ struct Lds {
   static_assert(End * 4 <= kLdsBytes, "LDS map exceeds the allocation");
   static_assert(MB == 1 || 3 * kMaxBatch * kBatchSpanD / 2 <= Region, "staged fp32 inputs do not fit");
   static_assert(Gain % 4 == 0 && Region % 4 == 0 && Sink % 4 == 0, "16-byte alignment");
+  static_assert(Plan % 2 == 0 && kPlanInts % 2 == 0, "8-byte plan words (combine_all)");
 };
 
 constexpr int kWaitVm0 = 0x0F70;             // s_waitcnt vmcnt(0), expcnt/lgkmcnt untouched
@@ -500,8 +501,10 @@ __device__ __forceinline__ void fill_tables(const Params& P, int wave, int* tab_
 // waves add the slots in streamer order (combine_all): the result does not
 // depend on which streamer finished first.  The plan lists, per phase type,
 // the shared (streamer, end) slots in that order (an entry is slot | group <<
-// 4 | (first slot of its group) << 28), and from int 16 on the shared groups
-// (output group | first entry << 8 | entry count << 16).
+// 4 | (first slot of its group) << 28), and from int 16 on the count of
+// shared groups, then from int 18 two ints per shared group: output group |
+// slot count << 8, and its slots, 4 bits each in streamer order (a group has
+// at most one slot per streamer, so at most kStreamers).
 __device__ __forceinline__ bool whole_group(int t, int kt, int u0, int u1) { return t * kt >= u0 && (t + 1) * kt <= u1; }
 
 __device__ __forceinline__ void build_plans(const int* tab_all, int* plan) {
@@ -524,13 +527,20 @@ __device__ __forceinline__ void build_plans(const int* tab_all, int* plan) {
     }
   }
   pl[0] = cnt;
-  // the shared groups: output group, first entry and entry count of each
+  // the shared groups: output group, slot count and slot list of each
   int* gp = pl + 16;
   int ng = 0;
   for (int k = 0; k < cnt; ++k) {
     const int en = pl[1 + k];
-    if ((en >> 28) & 1) gp[1 + ng++] = ((en >> 4) & 0xFF) | (k << 8) | (1 << 16);
-    else if (ng > 0) gp[ng] += 1 << 16;
+    if ((en >> 28) & 1) {
+      gp[2 + 2 * ng] = ((en >> 4) & 0xFF) | (1 << 8);
+      gp[3 + 2 * ng] = en & 15;
+      ++ng;
+    } else if (ng > 0) {
+      const int c = gp[2 * ng] >> 8;
+      gp[2 * ng] += 1 << 8;
+      gp[2 * ng + 1] |= (en & 15) << (4 * c);
+    }
   }
   gp[0] = ng;
 }
@@ -542,15 +552,20 @@ __device__ __forceinline__ void build_plans(const int* tab_all, int* plan) {
 template <int MB>
 __device__ __forceinline__ void combine_all(int ph, const int* plan, const float* slots, float* out) {
   constexpr int SN = Lds<MB>::SlotN;
-  const int* pl = plan + ph * kPlanInts;
-  const int* gp = pl + 16;
+  const int* gp = plan + ph * kPlanInts + 16;
   const int n = gp[0] * SN;
   for (int p = threadIdx.x; p < n; p += kThreads) {
     const int gi = p / SN, e = p - gi * SN;
-    const int d = gp[1 + gi];
-    const int g = d & 0xFF, e0 = (d >> 8) & 0xFF, ne = d >> 16;
-    float acc = slots[(pl[1 + e0] & 15) * SN + e];
-    for (int k = 1; k < ne; ++k) acc += slots[(pl[1 + e0 + k] & 15) * SN + e];
+    // one read for the group's slots, then all its slot reads at once
+    const int2 d = *reinterpret_cast<const int2*>(gp + 2 + 2 * gi);
+    const int g = d.x & 0xFF, ne = d.x >> 8;
+    float v[kStreamers];
+#pragma unroll
+    for (int k = 0; k < kStreamers; ++k) v[k] = k < ne ? slots[((d.y >> (4 * k)) & 15) * SN + e] : 0.f;
+    float acc = v[0];
+#pragma unroll
+    for (int k = 1; k < kStreamers; ++k)
+      if (k < ne) acc += v[k];
     out[g * SN + e] = acc;
   }
 }
