@@ -179,6 +179,16 @@ DEC_HD inline void split_even(int n, int g, int G, int& b, int& e) {
   b = (int)((long long)n * g / G);
   e = (int)((long long)n * (g + 1) / G);
 }
+// The batched kernel's 16-row groups of a GEMV over G workgroups, contiguous
+// and in order, where the n mod G workgroups with one group more are the last
+// ones: attention pairs go to the first workgroups, and the ones past them
+// warm their gate/up tiles in the cache during attention, which hides the
+// extra group there.
+DEC_HD inline void split_tail(int n, int g, int G, int& b, int& e) {
+  const int base = n / G, lo = G - n % G;   // workgroups [lo, G) take base + 1
+  b = g < lo ? g * base : lo * base + (g - lo) * (base + 1);
+  e = b + (g < lo ? base : base + 1);
+}
 // Piece columns of a GEMV row of K elements: 512 elements (64 lanes x 16 B) each.
 DEC_HD inline int gemv_piece_cols(int K) { return (K + 511) >> 9; }
 // Member s (1..n_members) of a workgroup's n units, where a unit is one piece

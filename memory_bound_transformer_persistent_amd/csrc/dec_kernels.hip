@@ -432,7 +432,7 @@ __device__ __forceinline__ void fill_tables_tiled(const Params& P, int wave, int
   phase_shape(P, lane, rows, K);
   const int rg = (rows + kTileRows - 1) / kTileRows, kt = (K + kTileCols - 1) / kTileCols;
   int g0, g1;
-  split(rg, blockIdx.x, gridDim.x, g0, g1);
+  split_tail(rg, blockIdx.x, gridDim.x, g0, g1);
   if (wave == 0) {
     tab_wg[2 * lane] = (kTileRows / 2) * g0;
     tab_wg[2 * lane + 1] = min((kTileRows / 2) * g1, rows / 2);
@@ -959,7 +959,7 @@ __device__ __forceinline__ void own_rows(const Params& P, int& r0, int& r1) {
     r1 = 2 * p1;
   } else {
     int g0, g1;
-    split((P.d + kTileRows - 1) / kTileRows, blockIdx.x, gridDim.x, g0, g1);
+    split_tail((P.d + kTileRows - 1) / kTileRows, blockIdx.x, gridDim.x, g0, g1);
     r0 = min(P.d, kTileRows * g0);
     r1 = min(P.d, kTileRows * g1);
   }

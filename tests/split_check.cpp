@@ -1,6 +1,8 @@
 // Host driver for the kernel's GEMV work splits (dec_internal.h), for
 // tests/test_splits.py.  Reads "npairs K G skip" lines from stdin and prints,
-// per workgroup g, its row pairs [p0, p1) and each streamer's unit range.
+// per workgroup g, its row pairs [p0, p1) and each streamer's unit range.  A
+// line with skip -1 asks for the batched kernel's split of npairs 16-row
+// groups instead: per workgroup, its groups [b, e).
 #include <cstdio>
 
 #include "dec_internal.h"
@@ -11,6 +13,15 @@ int main() {
   int npairs, K, G, skip;
   const int kStreamers = kWaves - 1;
   while (std::scanf("%d %d %d %d", &npairs, &K, &G, &skip) == 4) {
+    if (skip == -1) {
+      for (int g = 0; g < G; ++g) {
+        int b, e;
+        split_tail(npairs, g, G, b, e);
+        std::printf("%d %d %d\n", g, b, e);
+      }
+      std::printf("end\n");
+      continue;
+    }
     const int npc = gemv_piece_cols(K);
     for (int g = 0; g < G; ++g) {
       int p0 = 0, p1 = 0;

@@ -9,6 +9,8 @@ boundary moves to that pair's end, so that no row pair is summed by more than
 two waves (two additions into a zeroed word commute bitwise).  The split code
 itself (dec_internal.h) is compiled here for the host with g++ and driven over
 every GEMV phase of every supported workload shape and several grid sizes.
+The batched kernel instead gives every workgroup whole 16-row groups, the
+larger shares to the last workgroups; that split is checked the same way.
 """
 import os
 import subprocess
@@ -109,3 +111,40 @@ def test_splits_match_the_model_and_cover_every_unit_once(driver):
             assert max(contrib, default=0) <= 2, (what, g)
         assert covered == npairs, what
         assert max(sizes) - min(sizes) <= 1, what
+
+
+def model_groups(n, G, g):
+    """Batched kernel: contiguous, in order, sizes n // G or one more, the
+    larger ones last (the workgroups past the attention pairs)."""
+    sizes = [n // G + (1 if k >= G - n % G else 0) for k in range(G)]
+    b = sum(sizes[:g])
+    return b, b + sizes[g]
+
+
+def test_batched_group_split(driver):
+    """The 16-row groups of every batched GEMV phase (and a few odd counts)
+    over several grids: the model above, every group once."""
+    counts = set()
+    for wl in ("tiny", "dense2b"):
+        s = synth.shape_for(wl)
+        q = s.n_heads * s.head_dim
+        for rows in (3 * q, s.d_model, 2 * s.d_ffn, s.lm_vocab):
+            counts.add((rows + 15) // 16)
+    counts |= {1, 5, 255, 256, 257, 864}
+    cases = [(n, G) for n in sorted(counts) for G in (7, 64, 100, 256)]
+    inp = "".join(f"{n} 0 {G} -1\n" for n, G in cases)
+    out = subprocess.run([driver], input=inp, capture_output=True, text=True, check=True).stdout
+    blocks = [b.strip().splitlines() for b in out.split("end\n")[:-1]]
+    assert len(blocks) == len(cases)
+    for (n, G), rows in zip(cases, blocks):
+        assert len(rows) == G
+        prev = 0
+        for line in rows:
+            g, b, e = (int(x) for x in line.split())
+            assert (b, e) == model_groups(n, G, g), (n, G, g)
+            assert b == prev
+            prev = e
+        assert prev == n
+    # dense2b at batch 8: the 96 extra gate/up groups go to workgroups 160-255,
+    # the ones past the 160 (sequence, head) attention pairs
+    assert [model_groups(864, 256, g)[1] - model_groups(864, 256, g)[0] for g in (0, 159, 160, 255)] == [3, 3, 4, 4]
