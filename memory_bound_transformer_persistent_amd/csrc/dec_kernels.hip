@@ -1728,9 +1728,10 @@ __device__ __forceinline__ void w0_warm_gu(const Params& P, const int* tab_all, 
 
 // The same for the batched kernel (workgroups past the B*H attention pairs):
 // the 1 KB GU tiles past each streamer's first group (in its registers),
-// up to kW0WarmTiles per streamer.  32 measured best at batch 8 (48 was
-// slower).
-constexpr int kW0WarmTiles = 32;
+// up to kW0WarmTiles per streamer.  At batch 8, with these workgroups
+// holding the extra gate/up group (split_tail): 16, 24, 32, 40 and 48 tiles
+// gave 1.471, 1.452, 1.458, 1.519 and 1.540 ms per step.
+constexpr int kW0WarmTiles = 24;
 __device__ __forceinline__ void w0_warm_tiles(const Params& P, const int* tab_all, int l, float* sink) {
   const int lane = threadIdx.x & 63;
   const int* e0 = tab_all + PH_GU * kTabStride;
