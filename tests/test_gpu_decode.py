@@ -382,9 +382,15 @@ def kv_excess(g, r):
     return ((np.abs(g64 - r64) - spacing) / rms).max(axis=1)
 
 
-@pytest.mark.parametrize("nb", [8, 3])
-def test_tiny_batch_teacher_forced(stream, nb):
-    s = synth.shape_for("tiny")
+# d_model 200 and 5 x 8 heads: the O, down and QKV outputs end in a 16-row
+# group holding 8 rows (one 8-row block of the exchange vectors); d_ffn 136;
+# an LM head of 4090 rows ends inside a group
+RAGGED_BATCH = synth.shape_for("tiny").with_(d_model=200, n_heads=5, head_dim=8, d_ffn=136, lm_vocab=4090)
+
+
+@pytest.mark.parametrize("nb,ragged", [(8, False), (3, False), (5, True)])
+def test_tiny_batch_teacher_forced(stream, nb, ragged):
+    s = RAGGED_BATCH if ragged else synth.shape_for("tiny")
     t = synth.make_weights(s, seed=21, gain_jitter=0.1)
     n, steps = 16, 12
     prompts = synth.make_prompt(s.vocab, n, batch=nb, seed=22)
