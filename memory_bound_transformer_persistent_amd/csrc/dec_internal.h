@@ -112,7 +112,7 @@ struct Params {
   int B;                      // columns of the batched kernel: sequences decoded together (batch)
   int cols_pos;               // 1: the columns are consecutive positions of one sequence (batched prefill)
   uint16_t* kv;               // [L][2][B][H][max_ctx][hd] fp16 (one sequence when cols_pos)
-  float* x;                   // residual stream [B][d]
+  float* x;                   // residual stream [B][d] (the batched kernel keeps its rows in LDS and stores them here only where a launch ends)
   float* qkv;                 // [B][3q]: rotated, scaled q in the first q of each sequence
   float* att_o;               // attention output [B][q] (batch 1, fp32)
   uint16_t* att_o16;          // attention output [B][q] (batch > 1, fp16; same memory as att_o)
